@@ -1,0 +1,244 @@
+"""NumPy front end of the fp64 CPU oracle (csa_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the CPU-baseline leg of
+the benchmark may import this module; the product path never does.  It shares no
+code with the HIP library and imports nothing from it.
+
+Arrays follow the layouts in csa_oracle.h.  Stored tensors are numpy arrays of
+dtype float32 (binary32) or uint16 (bfloat16 bit patterns); every result is fp64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "csa_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libcsa_oracle.so")
+
+SUMMARY, EXACT_MASS = 0, 1
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (fp64, no FMA contraction, OpenMP over pairs)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
+             _SRC, "-o", tmp, "-lm"],
+            cwd=_HERE,
+        )
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int),
+        ("n_q_heads", ctypes.c_int),
+        ("n_kv_heads", ctypes.c_int),
+        ("head_dim", ctypes.c_int),
+        ("n_tokens", ctypes.c_int),
+        ("block_size", ctypes.c_int),
+        ("dtype", ctypes.c_int),
+        ("scale", ctypes.c_double),
+    ]
+
+
+@dataclass(frozen=True)
+class Shape:
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    n_tokens: int
+    block_size: int
+    dtype: str  # "f32" or "bf16"
+    scale: float = 0.0  # 0 means 1/sqrt(head_dim)
+
+    @property
+    def n_blocks(self) -> int:
+        return -(-self.n_tokens // self.block_size)
+
+    @property
+    def group(self) -> int:
+        return self.n_q_heads // self.n_kv_heads
+
+    def c(self) -> _Shape:
+        return _Shape(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim, self.n_tokens,
+                      self.block_size, 0 if self.dtype == "f32" else 1, float(self.scale))
+
+    @property
+    def np_dtype(self):
+        return np.float32 if self.dtype == "f32" else np.uint16
+
+
+_lib = None
+_lib_override = None
+
+
+def use_library(path):
+    """Load the oracle from another build of csa_oracle.c (None restores the default).
+    Used by the mutation tests, which build copies with planted mistakes."""
+    global _lib, _lib_override
+    _lib, _lib_override = None, path
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        lib = ctypes.CDLL(_lib_override or build())
+        P, I, D = ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_double)
+        SP = ctypes.POINTER(_Shape)
+        lib.oracle_kv_summary_build.argtypes = [SP, P, P, P, P]
+        lib.oracle_block_logits.argtypes = [SP, I, P, P, P]
+        lib.oracle_group_score.argtypes = [SP, P, P]
+        lib.oracle_topk.argtypes = [I, I, I, P, P, P]
+        lib.oracle_attend.argtypes = [SP, P, P, P, P, P, P, I, P, P, I, I, P, P]
+        lib.oracle_dense.argtypes = [SP, P, P, P, P, P]
+        lib.oracle_block_mass.argtypes = [SP, P, P, P, P, P]
+        lib.oracle_round_bf16.argtypes = [ctypes.c_double]
+        lib.oracle_round_bf16.restype = ctypes.c_uint16
+        for f in ("oracle_kv_summary_build", "oracle_block_logits", "oracle_group_score",
+                  "oracle_topk", "oracle_attend", "oracle_dense", "oracle_block_mass"):
+            getattr(lib, f).restype = I
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _stored(shape: Shape, a, dims):
+    a = np.ascontiguousarray(a)
+    if a.dtype != shape.np_dtype:
+        raise TypeError(f"expected {shape.np_dtype} array, got {a.dtype}")
+    if tuple(a.shape) != tuple(dims):
+        raise ValueError(f"expected shape {dims}, got {a.shape}")
+    return a
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what}: invalid argument")
+
+
+def kv_summary_build(shape: Shape, K, V):
+    """Mean key and mean value of every block, rounded once to the storage dtype."""
+    kv = (shape.batch, shape.n_kv_heads, shape.n_tokens, shape.head_dim)
+    sm = (shape.batch, shape.n_kv_heads, shape.n_blocks, shape.head_dim)
+    K, V = _stored(shape, K, kv), _stored(shape, V, kv)
+    Kbar = np.empty(sm, shape.np_dtype)
+    Vbar = np.empty(sm, shape.np_dtype)
+    _check(_load().oracle_kv_summary_build(ctypes.byref(shape.c()), _ptr(K), _ptr(V), _ptr(Kbar), _ptr(Vbar)),
+           "kv_summary_build")
+    return Kbar, Vbar
+
+
+def block_logits(shape: Shape, mode: int, q, keys):
+    """Per-query-head block logits [B, Hq, nb]: first-order summary score or exact ln m_b."""
+    rows = shape.n_blocks if mode == SUMMARY else shape.n_tokens
+    q = _stored(shape, q, (shape.batch, shape.n_q_heads, shape.head_dim))
+    keys = _stored(shape, keys, (shape.batch, shape.n_kv_heads, rows, shape.head_dim))
+    out = np.empty((shape.batch, shape.n_q_heads, shape.n_blocks), np.float64)
+    _check(_load().oracle_block_logits(ctypes.byref(shape.c()), mode, _ptr(q), _ptr(keys), _ptr(out)),
+           "block_logits")
+    return out
+
+
+def group_score(shape: Shape, logits):
+    """Group block score [B, Hkv, nb] (log of the sum of per-head normalised masses for G > 1)."""
+    logits = np.ascontiguousarray(logits, np.float64)
+    assert logits.shape == (shape.batch, shape.n_q_heads, shape.n_blocks)
+    out = np.empty((shape.batch, shape.n_kv_heads, shape.n_blocks), np.float64)
+    _check(_load().oracle_group_score(ctypes.byref(shape.c()), _ptr(logits), _ptr(out)), "group_score")
+    return out
+
+
+def block_score(shape: Shape, mode: int, q, keys):
+    return group_score(shape, block_logits(shape, mode, q, keys))
+
+
+def topk_select(scores, k: int):
+    """Top-k of each row of a 2-D (or [B, Hkv, nb]) score array.
+
+    Returns (sel, margin): sel [..., min(k, nb)] int32 ascending, margin [...] fp64
+    = score_(k) - score_(k+1) in (score desc, index asc) order (inf if all kept)."""
+    scores = np.ascontiguousarray(scores, np.float64)
+    lead, nb = scores.shape[:-1], scores.shape[-1]
+    rows = int(np.prod(lead)) if lead else 1
+    kk = min(k, nb)
+    sel = np.empty(lead + (kk,), np.int32)
+    margin = np.empty(lead, np.float64)
+    _check(_load().oracle_topk(rows, nb, k, _ptr(scores), _ptr(sel), _ptr(margin)), "topk")
+    return sel, margin
+
+
+def sparse_decode_attn(shape: Shape, q, K, V, Kbar, Vbar, sel, proxies: bool,
+                       tok_idx=None, tok_logw=None):
+    """Attention over exact tokens of the kept blocks, weighted tokens and proxies."""
+    kv = (shape.batch, shape.n_kv_heads, shape.n_tokens, shape.head_dim)
+    q = _stored(shape, q, (shape.batch, shape.n_q_heads, shape.head_dim))
+    K, V = _stored(shape, K, kv), _stored(shape, V, kv)
+    if proxies:
+        sm = (shape.batch, shape.n_kv_heads, shape.n_blocks, shape.head_dim)
+        Kbar, Vbar = _stored(shape, Kbar, sm), _stored(shape, Vbar, sm)
+    else:
+        Kbar = Vbar = None
+    sel = np.ascontiguousarray(sel, np.int32)
+    k = sel.shape[-1]
+    assert sel.shape == (shape.batch, shape.n_kv_heads, k)
+    m = 0
+    if tok_idx is not None:
+        tok_idx = np.ascontiguousarray(tok_idx, np.int32)
+        tok_logw = np.ascontiguousarray(tok_logw, np.float32)
+        m = tok_idx.shape[-1]
+        assert tok_idx.shape == tok_logw.shape == (shape.batch, shape.n_kv_heads, m)
+    out = np.empty((shape.batch, shape.n_q_heads, shape.head_dim), np.float64)
+    lse = np.empty((shape.batch, shape.n_q_heads), np.float64)
+    _check(_load().oracle_attend(ctypes.byref(shape.c()), _ptr(q), _ptr(K), _ptr(V), _ptr(Kbar), _ptr(Vbar),
+                                 _ptr(sel), k, _ptr(tok_idx), _ptr(tok_logw), m, 1 if proxies else 0,
+                                 _ptr(out), _ptr(lse)), "attend")
+    return out, lse
+
+
+def dense_decode_attn(shape: Shape, q, K, V):
+    kv = (shape.batch, shape.n_kv_heads, shape.n_tokens, shape.head_dim)
+    q = _stored(shape, q, (shape.batch, shape.n_q_heads, shape.head_dim))
+    K, V = _stored(shape, K, kv), _stored(shape, V, kv)
+    out = np.empty((shape.batch, shape.n_q_heads, shape.head_dim), np.float64)
+    lse = np.empty((shape.batch, shape.n_q_heads), np.float64)
+    _check(_load().oracle_dense(ctypes.byref(shape.c()), _ptr(q), _ptr(K), _ptr(V), _ptr(out), _ptr(lse)),
+           "dense")
+    return out, lse
+
+
+def block_mass(shape: Shape, q, K, V, centroids: bool = False):
+    """Exact ln m_b per query head [B, Hq, nb] and optionally the attention-weighted
+    block centroids [B, Hq, nb, d]."""
+    kv = (shape.batch, shape.n_kv_heads, shape.n_tokens, shape.head_dim)
+    q = _stored(shape, q, (shape.batch, shape.n_q_heads, shape.head_dim))
+    K, V = _stored(shape, K, kv), _stored(shape, V, kv)
+    ln_m = np.empty((shape.batch, shape.n_q_heads, shape.n_blocks), np.float64)
+    cen = np.empty((shape.batch, shape.n_q_heads, shape.n_blocks, shape.head_dim), np.float64) if centroids else None
+    _check(_load().oracle_block_mass(ctypes.byref(shape.c()), _ptr(q), _ptr(K), _ptr(V), _ptr(ln_m), _ptr(cen)),
+           "block_mass")
+    return (ln_m, cen) if centroids else ln_m
+
+
+def round_bf16(x: float) -> int:
+    """The oracle's fp64 -> bfloat16 rounding (bit pattern)."""
+    return int(_load().oracle_round_bf16(float(x)))
+
+
+def widen(shape_or_dtype, a):
+    """Stored array -> fp64 (exact)."""
+    dt = shape_or_dtype.dtype if isinstance(shape_or_dtype, Shape) else shape_or_dtype
+    if dt == "f32":
+        return np.asarray(a, np.float32).astype(np.float64)
+    return (np.asarray(a, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)

@@ -1,0 +1,84 @@
+"""The pins are strong enough: each plausible mistake planted in a copy of the oracle's C
+source (a dropped term, a wrong sign, a wrong operand or index, a wrong tie rule) makes at
+least one pin of test_oracle_pins fail.  The mutants are built on the CPU into a temporary
+directory; the real oracle is untouched and restored afterwards."""
+import os
+import subprocess
+
+import pytest
+
+import test_oracle_pins as P
+from oracle import oracle as O
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "csa_oracle.c")
+
+MUTANTS = {
+    "summary score without ln c_b": ("keys, kv_off(s, b, j, nb, blk)) + log((double)c);",
+                                     "keys, kv_off(s, b, j, nb, blk));"),
+    "proxy logit without ln count": ("Kbar, off) + log((double)block_count(s, blk));", "Kbar, off);"),
+    "group score not normalised per head": ("first[(size_t)g * nb + blk] - lse_h[g];",
+                                            "first[(size_t)g * nb + blk];"),
+    "ties to the higher index": ("return (a->index > b->index) - (a->index < b->index);",
+                                 "return (a->index < b->index) - (a->index > b->index);"),
+    "ragged block divided by L": ("sk / c);", "sk / s->block_size);"),
+    "value summary taken from keys": ("sv += elem(V, s->dtype", "sv += elem(K, s->dtype"),
+    "logit scale 1/d": ("1.0 / sqrt((double)s->head_dim)", "1.0 / (double)s->head_dim"),
+    "log-weight subtracted": ("+ (double)tok_logw[", "- (double)tok_logw["),
+    "output not normalised": ("out[t] /= denom;", "out[t] /= 1.0;"),
+    "query head on the wrong KV head": ("j = h / G;", "j = h % s->n_kv_heads;"),
+    "lse without the maximum": ("*lse = mx + log(denom);", "*lse = log(denom);"),
+    "exact mass as the maximum logit": ("    return mx + log(sum);", "    return mx + 0.0 * log(sum);"),
+}
+
+BATTERY = [
+    (P.test_summaries_are_exact_means_rounded_once, ("f32", 1000, 16)),
+    (P.test_summaries_are_exact_means_rounded_once, ("bf16", 200, 64)),
+    (P.test_dense_matches_library_attention, ("f32",)),
+    (P.test_dense_closed_form_identical_keys, ()),
+    (P.test_keeping_all_blocks_equals_dense, ("bf16", 3, 1000, 64)),
+    (P.test_block_size_one_makes_proxies_exact, (3,)),
+    (P.test_equal_logit_tail_proxy_is_exact, ()),
+    (P.test_proxy_logit_is_mean_logit_plus_log_count, ()),
+    (P.test_mha_selection_is_top_k_by_exact_mass, (12,)),
+    (P.test_group_score_is_sum_of_normalised_masses, ()),
+    (P.test_topk_ties_go_to_lower_index, ()),
+    (P.test_jensen_mean_logit_bound, ()),
+    (P.test_mixture_and_renormalised_error_identities, ()),
+    (P.test_worked_example_from_the_page, ()),
+    (P.test_integer_weights_equal_multiplicities, ()),
+]
+
+
+def _failures():
+    failed = []
+    for fn, args in BATTERY:
+        try:
+            fn(*args)
+        except (AssertionError, ValueError):
+            failed.append(fn.__name__)
+    return failed
+
+
+def test_unmutated_oracle_passes_the_battery():
+    O.use_library(None)
+    assert _failures() == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    count = src.count(old)
+    assert count >= 1, f"mutation site for {name!r} not found"
+    mutant_c = tmp_path / "mutant.c"
+    mutant_c.write_text(src.replace(old, new))
+    (tmp_path / "csa_oracle.h").write_text(open(SRC[:-2] + ".h").read())
+    lib = tmp_path / "libmutant.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
+                           str(mutant_c), "-o", str(lib), "-lm"])
+    O.use_library(str(lib))
+    try:
+        failed = _failures()
+    finally:
+        O.use_library(None)
+    assert failed, f"no pin caught the mutant {name!r}"

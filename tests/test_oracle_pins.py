@@ -1,0 +1,484 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each test names the passage it follows.  Page titles:
+  [OA]    "OpenAttention reads 1% of the KV cache -- Count-aware tail proxy"
+  [COBS]  "COBS: Cumulant Order Block Sparse Attention"
+  [WC]    "WildCat: Near-Linear Attention in Theory and Practice"
+  [QOC]   "Query-Oblivious Coresets for Softmax Attention"
+None of these tests needs a GPU.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import brute
+from coreset_softmax_attention_amd import workloads as W
+from oracle import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def store(x, dtype):
+    x = np.asarray(x)
+    return x.astype(np.float32) if dtype == "f32" else W.to_bf16_bits(x.astype(np.float32))
+
+
+def rand_case(seed, B, Hq, Hkv, d, n, dtype, qscale=1.0):
+    rng = np.random.default_rng(seed)
+    q = store(qscale * rng.standard_normal((B, Hq, d)), dtype)
+    K = store(rng.standard_normal((B, Hkv, n, d)), dtype)
+    V = store(rng.standard_normal((B, Hkv, n, d)), dtype)
+    return q, K, V
+
+
+def rel_err(a, b):
+    """Per output row ||a - b||_inf / ||b||_inf, maximum over rows."""
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    num = np.abs(a - b).reshape(-1, a.shape[-1]).max(axis=1)
+    den = np.abs(b).reshape(-1, b.shape[-1]).max(axis=1)
+    return float((num / den).max())
+
+
+def nested(a, dtype):
+    return O.widen(dtype, a).tolist()
+
+
+# ---------------------------------------------------------------------------
+# storage rounding and summaries
+# ---------------------------------------------------------------------------
+
+def test_round_bf16_matches_exact_rational_rounding():
+    rng = np.random.default_rng(1)
+    xs = list(rng.standard_normal(2000) * 10.0 ** rng.integers(-40, 38, 2000))
+    # exact ties between neighbouring bf16 values, both parities, and extremes
+    for base in (1.0, 1.0078125, -3.0, 2.0 ** -126, 2.0 ** -130, 1.5 * 2.0 ** 100):
+        xs += [base * (1 + 2.0 ** -8), base * (1 + 3 * 2.0 ** -8), base * (1 + 2.0 ** -8 + 2.0 ** -40)]
+    xs += [2.0 ** -134, 3 * 2.0 ** -135, 2.0 ** -140, -(2.0 ** -140), 3.3e38, 3.4e38, -1e39]
+    for x in xs:
+        assert O.round_bf16(x) == brute.round_to_bf16_bits(Fraction(x)), x
+    assert O.round_bf16(0.0) == 0x0000 and O.round_bf16(-0.0) == 0x8000  # signed zeros kept
+
+
+def test_generator_bf16_rounding_is_round_to_nearest_even():
+    rng = np.random.default_rng(2)
+    x = (rng.standard_normal(3000) * 10.0 ** rng.integers(-30, 30, 3000)).astype(np.float32)
+    x = np.concatenate([x, np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8)], np.float32)])
+    got = W.to_bf16_bits(x)
+    for xi, g in zip(x, got):
+        assert int(g) == brute.round_to_bf16_bits(Fraction(float(xi)))
+
+
+@pytest.mark.parametrize("dtype,n,L", [("bf16", 1024, 64), ("f32", 1000, 16), ("bf16", 200, 64)])
+def test_summaries_are_exact_means_rounded_once(dtype, n, L):
+    """Mean key / mean value per block ([OA] 'Skipping reviews...': the proxy value is the mean
+    of the values it replaces; [COBS] Eq. (18): the first-order summary is the mean key),
+    checked against an exact rational mean rounded by an independent routine."""
+    if dtype == "bf16" and n == 1024:
+        w = W.scaled_down(W.WORKLOADS["llama3_8b_layer_b1"], n_tokens=1024, n_kv_heads=1)
+        data = W.generate(w)
+        K, V = data["K"], data["V"]
+        shp = O.Shape(1, w.n_q_heads, 1, 128, n, L, dtype)
+    else:
+        _, K, V = rand_case(3, 1, 1, 1, 16, n, dtype)
+        shp = O.Shape(1, 1, 1, 16, n, L, dtype)
+    Kbar, Vbar = O.kv_summary_build(shp, K, V)
+    Kw, Vw = nested(K, dtype)[0][0], nested(V, dtype)[0][0]
+    nb = shp.n_blocks
+    check = range(nb) if nb <= 20 else list(range(3)) + [nb - 1]
+    for b in check:
+        rows = range(b * L, min(n, (b + 1) * L))
+        for src, bar in ((Kw, Kbar), (Vw, Vbar)):
+            exact = brute.mean_rows([src[i] for i in rows], dtype)
+            got = O.widen(dtype, bar[0, 0, b]).tolist()
+            assert got == exact, (b, dtype)
+
+
+def test_block_size_one_summary_is_the_key_itself():
+    """A block of one token: the mean is the token (no rounding happens)."""
+    q, K, V = rand_case(4, 1, 2, 2, 64, 50, "bf16")
+    Kbar, Vbar = O.kv_summary_build(O.Shape(1, 2, 2, 64, 50, 1, "bf16"), K, V)
+    assert np.array_equal(Kbar, K) and np.array_equal(Vbar, V)
+
+
+# ---------------------------------------------------------------------------
+# dense attention
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_dense_matches_library_attention(dtype):
+    """Dense softmax attention equals torch's scaled_dot_product_attention in fp64 (GQA heads
+    expanded), and lse equals torch.logsumexp of the scaled logits."""
+    B, Hq, Hkv, d, n = 2, 6, 2, 64, 300
+    q, K, V = rand_case(5, B, Hq, Hkv, d, n, dtype, qscale=2.0)
+    out, lse = O.dense_decode_attn(O.Shape(B, Hq, Hkv, d, n, 16, dtype), q, K, V)
+    qt = torch.from_numpy(O.widen(dtype, q))[:, :, None, :]
+    Kt = torch.from_numpy(O.widen(dtype, K)).repeat_interleave(Hq // Hkv, dim=1)
+    Vt = torch.from_numpy(O.widen(dtype, V)).repeat_interleave(Hq // Hkv, dim=1)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, Kt, Vt)[:, :, 0, :].numpy()
+    ref_lse = torch.logsumexp((qt @ Kt.transpose(-1, -2))[:, :, 0, :] / math.sqrt(d), dim=-1).numpy()
+    assert rel_err(out, ref) < 1e-12
+    assert np.abs(lse - ref_lse).max() < 1e-12
+
+
+def test_dense_closed_form_identical_keys():
+    """All keys equal: every weight is 1/n, so out = mean(V) and lse = s + ln n."""
+    d, n = 64, 777
+    rng = np.random.default_rng(6)
+    q = store(rng.standard_normal((1, 1, d)), "f32")
+    K = np.repeat(store(rng.standard_normal((1, 1, 1, d)), "f32"), n, axis=2)
+    V = store(rng.standard_normal((1, 1, n, d)), "f32")
+    out, lse = O.dense_decode_attn(O.Shape(1, 1, 1, d, n, 16, "f32"), q, K, V)
+    s = float(np.dot(q[0, 0].astype(np.float64), K[0, 0, 0].astype(np.float64))) / 8.0
+    assert rel_err(out[0, 0], V[0, 0].astype(np.float64).mean(axis=0)) < 1e-13
+    assert abs(lse[0, 0] - (s + math.log(n))) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# the sparse path: special cases that must reduce to dense
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,G,n,L", [("f32", 1, 1024, 16), ("bf16", 4, 640, 64), ("bf16", 3, 1000, 64)])
+def test_keeping_all_blocks_equals_dense(dtype, G, n, L):
+    """[COBS] discard-and-renormalise with no dropped block (tau = 0) is the dense output."""
+    Hkv = 2
+    shp = O.Shape(2, G * Hkv, Hkv, 64, n, L, dtype)
+    q, K, V = rand_case(7, 2, G * Hkv, Hkv, 64, n, dtype, qscale=2.0)
+    Kbar, Vbar = O.kv_summary_build(shp, K, V)
+    sel = np.tile(np.arange(shp.n_blocks, dtype=np.int32), (2, Hkv, 1))
+    ref, ref_lse = O.dense_decode_attn(shp, q, K, V)
+    for proxies in (False, True):
+        out, lse = O.sparse_decode_attn(shp, q, K, V, Kbar, Vbar, sel, proxies)
+        assert rel_err(out, ref) < 1e-13
+        assert np.abs(lse - ref_lse).max() < 1e-12
+
+
+@pytest.mark.parametrize("k", [0, 3, 40])
+def test_block_size_one_makes_proxies_exact(k):
+    """L = 1: each proxy is its own token (mean key = key, ln 1 = 0), so the output equals
+    dense for every k."""
+    n, d = 97, 64
+    shp = O.Shape(1, 4, 2, d, n, 1, "bf16")
+    q, K, V = rand_case(8, 1, 4, 2, d, n, "bf16", qscale=2.0)
+    Kbar, Vbar = O.kv_summary_build(shp, K, V)
+    sel = np.stack([np.sort(np.random.default_rng(9 + j).choice(n, k, replace=False)) for j in range(2)])
+    sel = sel.astype(np.int32).reshape(1, 2, k)
+    out, lse = O.sparse_decode_attn(shp, q, K, V, Kbar, Vbar, sel, True)
+    ref, ref_lse = O.dense_decode_attn(shp, q, K, V)
+    assert rel_err(out, ref) < 1e-13
+    assert np.abs(lse - ref_lse).max() < 1e-12
+
+
+def _equal_logit_tail_case(equal_tail=True):
+    """q is zero on half of its coordinates; every key of an unread block is a shared k0 on q's
+    support plus noise only where q is zero, so all tail logits are equal.  Keys and values are
+    small dyadic numbers so block means are exact in binary32."""
+    d, n, L = 64, 256, 16
+    rng = np.random.default_rng(10)
+    q = np.zeros((1, 1, d))
+    q[0, 0, : d // 2] = rng.integers(-8, 9, d // 2) / 4
+    K = rng.integers(-8, 9, (1, 1, n, d)) / 4
+    V = rng.integers(-8, 9, (1, 1, n, d)) / 4
+    sel = np.array([[[2, 7]]], np.int32)
+    k0 = rng.integers(-8, 9, d // 2) / 4
+    for b in range(n // L):
+        if b not in (2, 7) and equal_tail:
+            K[0, 0, b * L:(b + 1) * L, : d // 2] = k0
+    shp = O.Shape(1, 1, 1, d, n, L, "f32")
+    return shp, store(q, "f32"), store(K, "f32"), store(V, "f32"), sel
+
+
+def test_equal_logit_tail_proxy_is_exact():
+    """[OA] 'Skipping reviews...': the proxy reproduces the tail's attention weight exactly
+    when every tail token has the same logit."""
+    shp, q, K, V, sel = _equal_logit_tail_case(True)
+    Kbar, Vbar = O.kv_summary_build(shp, K, V)
+    out, lse = O.sparse_decode_attn(shp, q, K, V, Kbar, Vbar, sel, True)
+    ref, ref_lse = O.dense_decode_attn(shp, q, K, V)
+    assert rel_err(out, ref) < 1e-13 and abs(lse - ref_lse).max() < 1e-12
+    # the same construction without the equal tail is visibly not exact
+    shp, q, K, V, sel = _equal_logit_tail_case(False)
+    Kbar, Vbar = O.kv_summary_build(shp, K, V)
+    out, _ = O.sparse_decode_attn(shp, q, K, V, Kbar, Vbar, sel, True)
+    ref, _ = O.dense_decode_attn(shp, q, K, V)
+    assert rel_err(out, ref) > 1e-3
+
+
+def test_proxy_logit_is_mean_logit_plus_log_count():
+    """[OA]: the proxy's logit is the mean logit of the tokens it replaces plus ln(count);
+    by linearity this is q . (mean key) / sqrt(d) + ln c ([COBS] Eq. (18) with a_b = ln L).
+    Ragged last block included (n = 248, L = 16: the last block has 8 tokens, so its mean
+    stays exact too)."""
+    d, n, L = 64, 248, 16
+    rng = np.random.default_rng(11)
+    q = store(rng.integers(-8, 9, (1, 2, d)) / 4, "f32")
+    K = store(rng.integers(-8, 9, (1, 1, n, d)) / 4, "f32")  # dyadic: block means exact
+    shp = O.Shape(1, 2, 1, d, n, L, "f32")
+    Kbar, _ = O.kv_summary_build(shp, K, K)
+    got = O.block_logits(shp, O.SUMMARY, q, Kbar)
+    Kw = K[0, 0].astype(np.float64)
+    for h in range(2):
+        s = Kw @ q[0, h].astype(np.float64) / 8.0
+        for b in range(shp.n_blocks):
+            tok = s[b * L:(b + 1) * L]
+            assert abs(got[0, h, b] - (tok.mean() + math.log(len(tok)))) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# block scores and selection
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", [12, 13, 14])
+def test_mha_selection_is_top_k_by_exact_mass(seed):
+    """[COBS] Eq. (5) with G = 1: minimising the bound keeps the top-k blocks by mass m_b.
+    Exhaustive search over all k-subsets maximising the exact sum of m_b (Python-computed
+    masses, exact rational sums) must pick the oracle's set."""
+    n, L, d, k = 192, 16, 64, 4
+    shp = O.Shape(1, 2, 2, d, n, L, "bf16")
+    q, K, V = rand_case(seed, 1, 2, 2, d, n, "bf16", qscale=3.0)
+    score = O.block_score(shp, O.EXACT_MASS, q, K)
+    sel, margin = O.topk_select(score, k)
+    Kw, qw = O.widen("bf16", K), O.widen("bf16", q)
+    for j in range(2):
+        s = Kw[0, j] @ qw[0, j] / math.sqrt(d)
+        masses = [math.fsum(math.exp(x) for x in s[b * L:(b + 1) * L]) for b in range(shp.n_blocks)]
+        assert list(sel[0, j]) == brute.best_subset(masses, k)
+        # the score itself is ln m_b
+        assert np.allclose(score[0, j], np.log(masses), rtol=0, atol=1e-12)
+
+
+def test_group_score_is_sum_of_normalised_masses():
+    """[COBS] Eq. (5): the GQA score of a block is the sum over the group of m_b^(g) / Z^(g);
+    the oracle returns its logarithm.  Summed over blocks the normalised masses give G."""
+    n, L, d, G = 300, 32, 64, 3
+    shp = O.Shape(2, 2 * G, 2, d, n, L, "f32")
+    q, K, V = rand_case(15, 2, 2 * G, 2, d, n, "f32", qscale=2.0)
+    score = O.block_score(shp, O.EXACT_MASS, q, K)
+    Kw, qw = O.widen("f32", K), O.widen("f32", q)
+    for b in range(2):
+        for j in range(2):
+            logits = []
+            for g in range(G):
+                s = Kw[b, j] @ qw[b, j * G + g] / math.sqrt(d)
+                logits.append([brute.lse(list(s[i * L:(i + 1) * L])) for i in range(shp.n_blocks)])
+            assert np.allclose(score[b, j], brute.group_scores(logits), rtol=0, atol=1e-12)
+            assert abs(math.fsum(np.exp(score[b, j])) - G) < 1e-12
+
+
+def test_group_selection_is_best_additive_subset():
+    """Ranking by an additive per-block score ([COBS] Eq. (5)) keeps the k-subset with the
+    largest total score (exhaustive check, G = 4, summary score)."""
+    n, L, d, k = 12 * 16, 16, 64, 3
+    shp = O.Shape(1, 8, 2, d, n, L, "bf16")
+    q, K, V = rand_case(16, 1, 8, 2, d, n, "bf16", qscale=2.0)
+    Kbar, _ = O.kv_summary_build(shp, K, V)
+    score = O.block_score(shp, O.SUMMARY, q, Kbar)
+    sel, _ = O.topk_select(score, k)
+    for j in range(2):
+        # maximise the sum of the (positive) normalised masses, i.e. of exp(score)
+        assert list(sel[0, j]) == brute.best_subset([math.exp(x) for x in score[0, j]], k)
+
+
+def test_topk_ties_go_to_lower_index():
+    """Equal scores (including +0 and -0) are broken by the lower block index; k >= nb keeps
+    every block; k = 0 keeps none."""
+    s = np.array([[1.0, 3.0, 3.0, -0.0, 0.0, 3.0, 0.0, -2.0, 1.0, 1.0]])
+    for k in range(0, 12):
+        sel, margin = O.topk_select(s, k)
+        assert list(sel[0]) == brute.best_subset(list(s[0]), k), k
+    sel, _ = O.topk_select(s, 4)
+    assert list(sel[0]) == [0, 1, 2, 5]
+
+
+def test_summary_score_equals_exact_mass_for_single_token_blocks():
+    """With L = 1 the first-order score (mean key, ln 1 = 0) is the exact log-mass."""
+    n, d = 120, 64
+    shp = O.Shape(1, 4, 2, d, n, 1, "bf16")
+    q, K, V = rand_case(17, 1, 4, 2, d, n, "bf16", qscale=2.0)
+    Kbar, _ = O.kv_summary_build(shp, K, V)
+    a = O.block_logits(shp, O.SUMMARY, q, Kbar)
+    b = O.block_logits(shp, O.EXACT_MASS, q, K)
+    assert np.abs(a - b).max() < 1e-13
+
+
+def test_jensen_mean_logit_bound():
+    """c_b exp(mean_i s_i) <= m_b = sum_i exp(s_i), equality iff the block's logits are equal
+    (the Jensen step of [QOC] Lemma 3.5 and the exactness condition of [OA])."""
+    n, L, d = 256, 16, 64
+    shp = O.Shape(1, 1, 1, d, n, L, "f32")
+    q, K, V = rand_case(18, 1, 1, 1, d, n, "f32", qscale=2.0)
+    K[0, 0, 0:L] = K[0, 0, 0]  # block 0: all logits equal
+    ln_m = O.block_mass(shp, q, K, V)[0, 0]
+    s = K[0, 0].astype(np.float64) @ q[0, 0].astype(np.float64) / 8.0
+    for b in range(shp.n_blocks):
+        lower = math.log(L) + s[b * L:(b + 1) * L].mean()
+        if b == 0:
+            assert abs(ln_m[b] - lower) < 1e-13
+        else:
+            assert lower < ln_m[b]
+
+
+def test_mixture_and_renormalised_error_identities():
+    """[COBS] around Eqs. (1)-(3): dense output = sum_b P_b v^c_b with P_b = m_b / Z and v^c_b
+    the attention-weighted block centroid; keeping a set S and renormalising gives
+    out_S - out = 1/(1 - tau) sum_{b not in S} P_b (out - v^c_b), tau the dropped mass."""
+    n, L, d = 320, 32, 64
+    shp = O.Shape(1, 2, 1, d, n, L, "f32")
+    q, K, V = rand_case(19, 1, 2, 1, d, n, "f32", qscale=2.0)
+    ln_m, cen = O.block_mass(shp, q, K, V, centroids=True)
+    out, _ = O.dense_decode_attn(shp, q, K, V)
+    S = [1, 4, 5, 8]
+    out_S, _ = O.sparse_decode_attn(shp, q, K, V, None, None, np.array([[S]], np.int32), False)
+    for h in range(2):
+        P = np.exp(ln_m[0, h] - np.logaddexp.reduce(ln_m[0, h]))
+        assert abs(P.sum() - 1) < 1e-14
+        assert rel_err(P @ cen[0, h], out[0, h]) < 1e-13
+        drop = [b for b in range(shp.n_blocks) if b not in S]
+        tau = P[drop].sum()
+        pred = (P[drop][:, None] * (out[0, h][None, :] - cen[0, h, drop])).sum(axis=0) / (1 - tau)
+        assert np.abs((out_S[0, h] - out[0, h]) - pred).max() < 1e-13
+
+
+def test_worked_example_from_the_page():
+    """[OA] 'A worked example with named numbers': 10,000 tokens, the 100 exact tokens hold
+    60 % of the mass and the 9,900-token tail 40 % with (stipulated) similar logits.
+    Discarding the tail inflates the exact tokens by 1/0.60 ~ 1.67x; one count-aware proxy
+    keeps the tail's 40 % so the exact tokens stay at 60 %."""
+    g = json.load(open(os.path.join(GOLDEN, "worked_example.json")))
+    n, L, d = g["n_tokens"], g["exact_tokens"], 64
+    gap = math.log(g["exact_mass_share"] / g["exact_tokens"] / (g["tail_mass_share"] / g["tail_tokens"]))
+    q = np.zeros((1, 1, d), np.float32)
+    q[0, 0, 0] = 8.0  # with scale 1/8 the logit is K[..., 0]
+    K = np.zeros((1, 1, n, d), np.float32)
+    K[0, 0, :L, 0] = gap  # the 100 top tokens; tail logits are 0
+    V = np.zeros((1, 1, n, d), np.float32)
+    V[0, 0, :L, 0] = 1.0  # out[0] = weight on exact tokens
+    V[0, 0, L:, 1] = 1.0  # out[1] = weight on the tail
+    shp = O.Shape(1, 1, 1, d, n, L, "f32")
+    Kbar, Vbar = O.kv_summary_build(shp, K, V)
+    sel = np.array([[[0]]], np.int32)
+    dense, _ = O.dense_decode_attn(shp, q, K, V)
+    prox, _ = O.sparse_decode_attn(shp, q, K, V, Kbar, Vbar, sel, True)
+    disc, _ = O.sparse_decode_attn(shp, q, K, V, None, None, sel, False)
+    assert abs(dense[0, 0, 0] - g["exact_mass_share"]) < 1e-6
+    assert abs(dense[0, 0, 1] - g["tail_mass_share"]) < 1e-6
+    assert abs(prox[0, 0, 0] - g["proxy_exact_share"]) < 1e-6
+    assert abs(prox[0, 0, 1] - g["proxy_tail_share"]) < 1e-6
+    assert np.abs(prox - dense).max() < 1e-12
+    assert abs(disc[0, 0, 0] - 1.0) < 1e-12 and disc[0, 0, 1] == 0.0
+    inflation = disc[0, 0, 0] / dense[0, 0, 0]
+    assert round(inflation, g["discard_inflation_printed_digits"]) == g["discard_inflation"]
+
+
+def test_integer_weights_equal_multiplicities():
+    """[WC] Abstract: attention over a weighted subset, out = sum w e^s v / sum w e^s.  With
+    integer weights this is dense attention over the multiset that repeats token i w_i times."""
+    n, d = 150, 64
+    rng = np.random.default_rng(20)
+    shp = O.Shape(1, 2, 1, d, n, 16, "f32")
+    q, K, V = rand_case(21, 1, 2, 1, d, n, "f32", qscale=2.0)
+    idx = np.sort(rng.choice(n, 40, replace=False)).astype(np.int32)
+    wts = rng.integers(1, 4, 40)
+    logw = np.log(wts).astype(np.float32)
+    out, lse = O.sparse_decode_attn(shp, q, K, V, None, None, np.zeros((1, 1, 0), np.int32), False,
+                                    idx.reshape(1, 1, -1), logw.reshape(1, 1, -1))
+    rep = np.repeat(idx, wts)
+    shp2 = O.Shape(1, 2, 1, d, len(rep), 16, "f32")
+    ref, ref_lse = O.dense_decode_attn(shp2, q, K[:, :, rep], V[:, :, rep])
+    # ln w rounded to binary32 perturbs each weight by < 2^-24 relative
+    assert rel_err(out, ref) < 1e-6 and np.abs(lse - ref_lse).max() < 1e-6
+
+
+def test_full_coreset_with_unit_weights_is_dense():
+    """Every token once with w = 1 (and nothing else) is dense attention."""
+    n, d = 200, 64
+    shp = O.Shape(2, 4, 2, d, n, 16, "bf16")
+    q, K, V = rand_case(22, 2, 4, 2, d, n, "bf16", qscale=2.0)
+    idx = np.tile(np.arange(n, dtype=np.int32), (2, 2, 1))
+    out, lse = O.sparse_decode_attn(shp, q, K, V, None, None, np.zeros((2, 2, 0), np.int32), False,
+                                    idx, np.zeros_like(idx, dtype=np.float32))
+    ref, ref_lse = O.dense_decode_attn(shp, q, K, V)
+    assert rel_err(out, ref) < 1e-13 and np.abs(lse - ref_lse).max() < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# independent brute force on tiny inputs
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,G,mode,proxies,n,L,k,m", [
+    ("f32", 1, "summary", True, 100, 16, 2, 0),
+    ("bf16", 2, "summary", True, 130, 16, 3, 5),
+    ("bf16", 3, "exact_mass", False, 96, 16, 2, 0),
+    ("f32", 2, "exact_mass", True, 75, 8, 4, 3),
+    ("bf16", 1, "exact_mass", False, 64, 64, 1, 0),
+])
+def test_oracle_agrees_with_brute_force(dtype, G, mode, proxies, n, L, k, m):
+    """The whole path against the separately written pure-Python version (exact rational
+    block means, exhaustive subset search), with ragged last blocks and weighted tokens."""
+    B, Hkv, d = 2, 2, 16
+    seed = hash((dtype, G, mode, n)) % 1000
+    q, K, V = rand_case(seed, B, G * Hkv, Hkv, d, n, dtype, qscale=2.0)
+    shp = O.Shape(B, G * Hkv, Hkv, d, n, L, dtype)
+    rng = np.random.default_rng(seed + 1)
+    tok_idx = rng.integers(0, n, (B, Hkv, m)).astype(np.int32)
+    tok_logw = rng.standard_normal((B, Hkv, m)).astype(np.float32)
+    Kbar, Vbar = O.kv_summary_build(shp, K, V)
+    md = O.SUMMARY if mode == "summary" else O.EXACT_MASS
+    score = O.block_score(shp, md, q, Kbar if mode == "summary" else K)
+    sel, _ = O.topk_select(score, k)
+    out, lse = O.sparse_decode_attn(shp, q, K, V, Kbar, Vbar, sel, proxies,
+                                    tok_idx if m else None, tok_logw if m else None)
+    tok = [[list(zip(tok_idx[b, j].tolist(), tok_logw[b, j].astype(np.float64).tolist()))
+            for j in range(Hkv)] for b in range(B)] if m else None
+    ref = brute.pipeline(nested(q, dtype), nested(K, dtype), nested(V, dtype), L, k, mode, proxies, dtype,
+                         tok=tok)
+    assert O.widen(dtype, Kbar).tolist() == ref["Kbar"]
+    assert O.widen(dtype, Vbar).tolist() == ref["Vbar"]
+    assert np.abs(score - np.array(ref["score"])).max() < 1e-12
+    assert sel.tolist() == ref["sel"]
+    assert rel_err(out, np.array(ref["out"])) < 1e-12
+    assert np.abs(lse - np.array(ref["lse"])).max() < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# argument handling and the input recipes
+# ---------------------------------------------------------------------------
+
+def test_oracle_rejects_an_empty_virtual_token_set():
+    shp = O.Shape(1, 1, 1, 16, 64, 16, "f32")
+    q, K, V = rand_case(23, 1, 1, 1, 16, 64, "f32")
+    with pytest.raises(ValueError):
+        O.sparse_decode_attn(shp, q, K, V, None, None, np.zeros((1, 1, 0), np.int32), False)
+
+
+def test_generator_is_deterministic_and_stream_independent():
+    w = W.scaled_down(W.WORKLOADS["weighted_coreset_128k"], batch=3, n_tokens=4096)
+    w = w.with_(coreset=64)
+    a = W.generate(w)
+    b = W.generate(w, batches=[2, 0])
+    for key in a:
+        assert np.array_equal(a[key][[2, 0]], b[key]), key
+    c = W.generate(w, threads=1)
+    for key in a:
+        assert np.array_equal(a[key], c[key]), key
+    assert np.all((a["tok_idx"] >= 0) & (a["tok_idx"] < w.n_tokens))
+    for bj in a["tok_idx"].reshape(-1, 64):
+        assert len(set(bj.tolist())) == 64  # without replacement
+    tot = np.exp(a["tok_logw"].astype(np.float64)).sum(axis=-1)
+    assert np.allclose(tot, w.n_tokens, rtol=1e-5)
+
+
+def test_heavy_hitters_are_planted():
+    """tiny_f32_d64: eight key rows are 3 q/|q| plus small noise (logit ~ 3|q|/sqrt(d))."""
+    w = W.WORKLOADS["tiny_f32_d64"]
+    data = W.generate(w)
+    q = data["q"][0, 0].astype(np.float64)
+    K = data["K"][0, 0].astype(np.float64)
+    cos = K @ q / np.linalg.norm(K, axis=1) / np.linalg.norm(q)
+    assert (cos > 0.9).sum() == 8
+    hh = np.nonzero(cos > 0.9)[0]
+    assert np.allclose(np.linalg.norm(K[hh], axis=1), 3.0, atol=0.5)
