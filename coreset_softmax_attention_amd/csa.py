@@ -1,0 +1,232 @@
+"""Thin Python binding of libcsa.so (the C-ABI in include/csa.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  torch supplies device memory and the current HIP stream.  The same
+names as the C entry points are exported.  If the library has not been built,
+loading fails loudly; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so")
+
+CSA_OK, CSA_ERR_INVALID_ARG, CSA_ERR_UNSUPPORTED, CSA_ERR_WORKSPACE, CSA_ERR_HIP = 0, -1, -2, -3, -4
+CSA_F32, CSA_BF16 = 0, 1
+CSA_SCORE_SUMMARY, CSA_SCORE_EXACT_MASS = 0, 1
+CSA_PROXY_NONE, CSA_PROXY_COMPLEMENT = 0, 1
+CSA_WS_BLOCK_SCORE_SUMMARY, CSA_WS_BLOCK_SCORE_EXACT_MASS = 0, 1
+CSA_WS_SPARSE_DECODE_ATTN, CSA_WS_DENSE_DECODE_ATTN = 2, 3
+
+MODES = {"summary": CSA_SCORE_SUMMARY, "exact_mass": CSA_SCORE_EXACT_MASS}
+
+
+class CsaError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: {detail} (status {status})")
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("n_tokens", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("dtype", ctypes.c_int),
+        ("scale", ctypes.c_float),
+    ]
+
+    @property
+    def n_blocks(self) -> int:
+        L = min(self.block_size, self.n_tokens)
+        return -(-self.n_tokens // L)
+
+
+_lib = None
+_P, _I32, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+_SIGS = {
+    "kv_summary_build": [ctypes.POINTER(Shape), _P, _P, _P, _P, _P],
+    "block_score": [ctypes.POINTER(Shape), ctypes.c_int, _P, _P, _P, _P, _SZ, _P],
+    "topk_select": [_I32, _I32, _I32, _P, _P, _P],
+    "sparse_decode_attn": [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _I32, _P, _P, _I32, ctypes.c_int,
+                           _P, _P, _P, _SZ, _P],
+    "dense_decode_attn": [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _SZ, _P],
+}
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """Load libcsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                               "`python -m coreset_softmax_attention_amd.build_lib` (or __graft_entry__.build())")
+        L = ctypes.CDLL(_LIB_PATH)
+        for name, args in _SIGS.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        L.csa_workspace_size.argtypes = [ctypes.POINTER(Shape), ctypes.c_int, _I32, _I32]
+        L.csa_workspace_size.restype = _SZ
+        L.csa_status_str.argtypes = [ctypes.c_int]
+        L.csa_status_str.restype = ctypes.c_char_p
+        L.csa_last_error.argtypes = []
+        L.csa_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, where: str):
+    if rc != CSA_OK:
+        raise CsaError(rc, where, lib().csa_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return CSA_F32
+    if t.dtype == torch.bfloat16:
+        return CSA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("tensors must be on the GPU")
+            if not t.is_contiguous():
+                raise ValueError("tensors must be contiguous")
+    return ts[0].device
+
+
+def make_shape(q: torch.Tensor, K: torch.Tensor, block_size: int, scale: float = 0.0) -> Shape:
+    """Shape of q [B, Hq, d] against a cache K [B, Hkv, n, d]."""
+    B, Hq, d = q.shape
+    B2, Hkv, n, d2 = K.shape
+    if B != B2 or d != d2:
+        raise ValueError(f"q {tuple(q.shape)} does not match K {tuple(K.shape)}")
+    if q.dtype != K.dtype:
+        raise TypeError("q and K must have the same dtype")
+    return Shape(B, Hq, Hkv, d, n, block_size, _dtype_code(K), float(scale))
+
+
+def workspace_size(shape: Shape, entry: int, k: int = 0, m: int = 0) -> int:
+    return int(lib().csa_workspace_size(ctypes.byref(shape), entry, k, m))
+
+
+def _workspace(shape: Shape, entry: int, k: int, m: int, ws, device):
+    need = workspace_size(shape, entry, k, m)
+    if need == 0:
+        return None, 0
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def kv_summary_build(K: torch.Tensor, V: torch.Tensor, block_size: int, Kbar=None, Vbar=None):
+    """Mean key and mean value of every block: Kbar, Vbar [B, Hkv, nb, d]."""
+    dev = _dev(K, V, Kbar, Vbar)
+    B, Hkv, n, d = K.shape
+    shape = Shape(B, Hkv, Hkv, d, n, block_size, _dtype_code(K), 0.0)
+    nb = shape.n_blocks
+    Kbar = torch.empty((B, Hkv, nb, d), dtype=K.dtype, device=dev) if Kbar is None else Kbar
+    Vbar = torch.empty((B, Hkv, nb, d), dtype=K.dtype, device=dev) if Vbar is None else Vbar
+    _check(lib().kv_summary_build(ctypes.byref(shape), _ptr(K), _ptr(V), _ptr(Kbar), _ptr(Vbar), _stream(dev)),
+           "kv_summary_build")
+    return Kbar, Vbar
+
+
+def block_score(q: torch.Tensor, keys: torch.Tensor, mode: str, block_size: int, n_tokens: int | None = None,
+                scale: float = 0.0, scores=None, ws=None):
+    """Block scores [B, Hkv, nb].  keys = Kbar (mode 'summary') or K (mode 'exact_mass');
+    n_tokens is needed in summary mode (the cache length the summaries describe)."""
+    dev = _dev(q, keys, scores)
+    B, Hq, d = q.shape
+    Hkv = keys.shape[1]
+    if mode == "summary":
+        if n_tokens is None:
+            raise ValueError("summary mode needs n_tokens")
+        n = n_tokens
+    else:
+        n = keys.shape[2]
+    shape = Shape(B, Hq, Hkv, d, n, block_size, _dtype_code(q), float(scale))
+    nb = shape.n_blocks
+    if mode == "summary" and keys.shape[2] != nb:
+        raise ValueError(f"Kbar has {keys.shape[2]} rows, expected {nb}")
+    scores = torch.empty((B, Hkv, nb), dtype=torch.float32, device=dev) if scores is None else scores
+    entry = CSA_WS_BLOCK_SCORE_SUMMARY if mode == "summary" else CSA_WS_BLOCK_SCORE_EXACT_MASS
+    ws, wsb = _workspace(shape, entry, 0, 0, ws, dev)
+    _check(lib().block_score(ctypes.byref(shape), MODES[mode], _ptr(q), _ptr(keys), _ptr(scores), _ptr(ws), wsb,
+                             _stream(dev)), "block_score")
+    return scores
+
+
+def topk_select(scores: torch.Tensor, k: int, sel=None):
+    """Top-k block indices per row (ascending), ties to the lower index: [..., min(k, nb)] int32."""
+    dev = _dev(scores, sel)
+    nb = scores.shape[-1]
+    rows = scores.numel() // nb
+    kk = min(k, nb)
+    sel = torch.empty(scores.shape[:-1] + (kk,), dtype=torch.int32, device=dev) if sel is None else sel
+    _check(lib().topk_select(rows, nb, k, _ptr(scores), _ptr(sel), _stream(dev)), "topk_select")
+    return sel
+
+
+def sparse_decode_attn(q, K, V, Kbar, Vbar, sel, block_size: int, proxies: bool = True, tok_idx=None,
+                       tok_logw=None, scale: float = 0.0, out=None, lse=None, ws=None):
+    """Attention over exact tokens of sel, optional weighted tokens and count-aware proxies.
+    Returns (out [B, Hq, d] float32, lse [B, Hq] float32)."""
+    dev = _dev(q, K, V, Kbar, Vbar, sel, tok_idx, tok_logw)
+    shape = make_shape(q, K, block_size, scale)
+    k = sel.shape[-1] if sel is not None else 0
+    m = tok_idx.shape[-1] if tok_idx is not None else 0
+    B, Hq, d = q.shape
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev) if out is None else out
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if lse is None else lse
+    ws, wsb = _workspace(shape, CSA_WS_SPARSE_DECODE_ATTN, k, m, ws, dev)
+    _check(lib().sparse_decode_attn(ctypes.byref(shape), _ptr(q), _ptr(K), _ptr(V), _ptr(Kbar), _ptr(Vbar),
+                                    _ptr(sel), k, _ptr(tok_idx), _ptr(tok_logw), m,
+                                    CSA_PROXY_COMPLEMENT if proxies else CSA_PROXY_NONE, _ptr(out), _ptr(lse),
+                                    _ptr(ws), wsb, _stream(dev)), "sparse_decode_attn")
+    return out, lse
+
+
+def dense_decode_attn(q, K, V, scale: float = 0.0, out=None, lse=None, ws=None):
+    """Softmax attention over every token: (out [B, Hq, d], lse [B, Hq])."""
+    dev = _dev(q, K, V)
+    shape = make_shape(q, K, K.shape[2], scale)
+    B, Hq, d = q.shape
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev) if out is None else out
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if lse is None else lse
+    ws, wsb = _workspace(shape, CSA_WS_DENSE_DECODE_ATTN, 0, 0, ws, dev)
+    _check(lib().dense_decode_attn(ctypes.byref(shape), _ptr(q), _ptr(K), _ptr(V), _ptr(out), _ptr(lse), _ptr(ws),
+                                   wsb, _stream(dev)), "dense_decode_attn")
+    return out, lse
+
+
+def to_device(a, device="cuda"):
+    """numpy array from the workload generator -> torch tensor on the GPU
+    (uint16 bfloat16 patterns become torch.bfloat16)."""
+    import numpy as np
+
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(a).to(device)

@@ -1,0 +1,226 @@
+// api.hip -- the C-ABI entry points of libcsa: argument validation on the host,
+// workspace sizing, and dispatch to the kernel launchers.  Every check runs
+// before any HIP call, so invalid calls launch nothing and touch no output.
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "../../include/csa.h"
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int code, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* where)
+{
+    return fail(CSA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+constexpr long long kMaxRows = 1ll << 31;
+
+// Validate a shape and derive the launch dimensions.
+int make_dims(const csa_shape* sh, csa::Dims* d)
+{
+    if (!sh) return fail(CSA_ERR_INVALID_ARG, "shape is NULL");
+    if (sh->batch < 1 || sh->n_q_heads < 1 || sh->n_kv_heads < 1 || sh->head_dim < 1 || sh->n_tokens < 1 ||
+        sh->block_size < 1)
+        return fail(CSA_ERR_INVALID_ARG, "shape has a non-positive size (B=%d Hq=%d Hkv=%d d=%d n=%d L=%d)",
+                    sh->batch, sh->n_q_heads, sh->n_kv_heads, sh->head_dim, sh->n_tokens, sh->block_size);
+    if (sh->n_q_heads % sh->n_kv_heads != 0)
+        return fail(CSA_ERR_INVALID_ARG, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)", sh->n_q_heads,
+                    sh->n_kv_heads);
+    if (sh->dtype != CSA_F32 && sh->dtype != CSA_BF16)
+        return fail(CSA_ERR_INVALID_ARG, "unknown dtype %d", (int)sh->dtype);
+    if (!isfinite(sh->scale)) return fail(CSA_ERR_INVALID_ARG, "scale is not finite");
+    if (sh->head_dim != 64 && sh->head_dim != 128)
+        return fail(CSA_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", sh->head_dim);
+    if (sh->n_tokens > (1 << 30)) return fail(CSA_ERR_UNSUPPORTED, "n_tokens %d above 2^30", sh->n_tokens);
+    const int G = sh->n_q_heads / sh->n_kv_heads;
+    if (G > 64) return fail(CSA_ERR_UNSUPPORTED, "group size %d above 64", G);
+    d->B = sh->batch;
+    d->Hq = sh->n_q_heads;
+    d->Hkv = sh->n_kv_heads;
+    d->G = G;
+    d->d = sh->head_dim;
+    d->n = sh->n_tokens;
+    d->L = sh->block_size < sh->n_tokens ? sh->block_size : sh->n_tokens;  // one ragged block if L >= n
+    d->nb = (sh->n_tokens + d->L - 1) / d->L;
+    d->dtype = sh->dtype == CSA_F32 ? csa::DT_F32 : csa::DT_BF16;
+    d->scale = sh->scale != 0.0f ? sh->scale : (float)(1.0 / sqrt((double)sh->head_dim));
+    d->ln_L = (float)log((double)d->L);
+    d->ln_last = (float)log((double)(sh->n_tokens - (d->nb - 1) * d->L));
+    return CSA_OK;
+}
+
+int check_ws(size_t need, const void* ws, size_t ws_bytes)
+{
+    if (need == 0) return CSA_OK;
+    if (!ws) return fail(CSA_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
+    if (ws_bytes < need) return fail(CSA_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", need, ws_bytes);
+    if (!aligned16(ws)) return fail(CSA_ERR_WORKSPACE, "workspace is not 16-byte aligned");
+    return CSA_OK;
+}
+
+size_t block_score_ws(const csa::Dims& d)
+{
+    return d.G > 1 ? (size_t)d.B * d.Hq * d.nb * sizeof(float) : 0;
+}
+
+int attn_rows_ok(const csa::Dims& d, long long k, long long m, int proxies, int dense)
+{
+    const long long rows = (dense ? (long long)d.n : k * d.L) + m + (proxies ? d.nb : 0);
+    if (rows >= kMaxRows) return fail(CSA_ERR_UNSUPPORTED, "virtual-token list of %lld rows above 2^31", rows);
+    return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kv_summary_build(const csa_shape* shape, const void* K, const void* V, void* Kbar, void* Vbar, hipStream_t stream)
+{
+    csa::Dims d;
+    if (int rc = make_dims(shape, &d)) return rc;
+    if (!K || !V || !Kbar || !Vbar) return fail(CSA_ERR_INVALID_ARG, "kv_summary_build: NULL tensor pointer");
+    if (!aligned16(K) || !aligned16(V) || !aligned16(Kbar) || !aligned16(Vbar))
+        return fail(CSA_ERR_INVALID_ARG, "kv_summary_build: tensors must be 16-byte aligned");
+    const hipError_t e = csa::launch_summary(d, K, V, Kbar, Vbar, stream);
+    return e == hipSuccess ? CSA_OK : hip_fail(e, "kv_summary_build");
+}
+
+int block_score(const csa_shape* shape, csa_score_mode mode, const void* q, const void* keys, float* scores, void* ws,
+                size_t ws_bytes, hipStream_t stream)
+{
+    csa::Dims d;
+    if (int rc = make_dims(shape, &d)) return rc;
+    if (mode != CSA_SCORE_SUMMARY && mode != CSA_SCORE_EXACT_MASS)
+        return fail(CSA_ERR_INVALID_ARG, "block_score: unknown mode %d", (int)mode);
+    if (!q || !keys || !scores) return fail(CSA_ERR_INVALID_ARG, "block_score: NULL tensor pointer");
+    if (!aligned16(q) || !aligned16(keys) || !aligned4(scores))
+        return fail(CSA_ERR_INVALID_ARG, "block_score: misaligned tensor");
+    if (int rc = check_ws(block_score_ws(d), ws, ws_bytes)) return rc;
+    float* dst = d.G == 1 ? scores : static_cast<float*>(ws);
+    hipError_t e = mode == CSA_SCORE_SUMMARY ? csa::launch_block_logits_summary(d, q, keys, dst, stream)
+                                             : csa::launch_block_logits_exact(d, q, keys, dst, stream);
+    if (e != hipSuccess) return hip_fail(e, "block_score");
+    if (d.G > 1) {
+        e = csa::launch_group_score(d, dst, scores, stream);
+        if (e != hipSuccess) return hip_fail(e, "block_score (group score)");
+    }
+    return CSA_OK;
+}
+
+int topk_select(int32_t rows, int32_t nb, int32_t k, const float* scores, int32_t* sel, hipStream_t stream)
+{
+    if (rows < 0 || nb < 1 || k < 0)
+        return fail(CSA_ERR_INVALID_ARG, "topk_select: rows=%d nb=%d k=%d", rows, nb, k);
+    if (rows == 0 || k == 0) return CSA_OK;
+    if (!scores || !sel) return fail(CSA_ERR_INVALID_ARG, "topk_select: NULL pointer");
+    if (!aligned4(scores) || !aligned4(sel)) return fail(CSA_ERR_INVALID_ARG, "topk_select: misaligned pointer");
+    const hipError_t e = csa::launch_topk(rows, nb, k, scores, sel, stream);
+    return e == hipSuccess ? CSA_OK : hip_fail(e, "topk_select");
+}
+
+int sparse_decode_attn(const csa_shape* shape, const void* q, const void* K, const void* V, const void* Kbar,
+                       const void* Vbar, const int32_t* sel, int32_t k, const int32_t* tok_idx,
+                       const float* tok_logw, int32_t m, csa_proxy_mode proxy_mode, float* out, float* lse,
+                       void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    csa::Dims d;
+    if (int rc = make_dims(shape, &d)) return rc;
+    if (proxy_mode != CSA_PROXY_NONE && proxy_mode != CSA_PROXY_COMPLEMENT)
+        return fail(CSA_ERR_INVALID_ARG, "sparse_decode_attn: unknown proxy mode %d", (int)proxy_mode);
+    const int proxies = proxy_mode == CSA_PROXY_COMPLEMENT;
+    if (k < 0 || k > d.nb) return fail(CSA_ERR_INVALID_ARG, "sparse_decode_attn: k=%d outside [0, %d]", k, d.nb);
+    if (m < 0) return fail(CSA_ERR_INVALID_ARG, "sparse_decode_attn: m=%d is negative", m);
+    if (k == 0 && m == 0 && !proxies)
+        return fail(CSA_ERR_INVALID_ARG, "sparse_decode_attn: empty virtual-token set (k = 0, m = 0, no proxies)");
+    if (!q || !K || !V || !out) return fail(CSA_ERR_INVALID_ARG, "sparse_decode_attn: NULL tensor pointer");
+    if (k > 0 && !sel) return fail(CSA_ERR_INVALID_ARG, "sparse_decode_attn: sel is NULL with k=%d", k);
+    if (m > 0 && (!tok_idx || !tok_logw))
+        return fail(CSA_ERR_INVALID_ARG, "sparse_decode_attn: weighted tokens missing with m=%d", m);
+    if (proxies && (!Kbar || !Vbar)) return fail(CSA_ERR_INVALID_ARG, "sparse_decode_attn: proxies need Kbar, Vbar");
+    if (!aligned16(q) || !aligned16(K) || !aligned16(V) || (proxies && (!aligned16(Kbar) || !aligned16(Vbar))) ||
+        !aligned4(out) || (lse && !aligned4(lse)) || (sel && !aligned4(sel)) || (tok_idx && !aligned4(tok_idx)) ||
+        (tok_logw && !aligned4(tok_logw)))
+        return fail(CSA_ERR_INVALID_ARG, "sparse_decode_attn: misaligned pointer");
+    if (int rc = attn_rows_ok(d, k, m, proxies, 0)) return rc;
+    const csa::AttnPlan plan = csa::plan_attention(d, k, m, proxies, 0);
+    if (int rc = check_ws(plan.ws_bytes, ws, ws_bytes)) return rc;
+    csa::AttnInputs in{q, K, V, Kbar, Vbar, sel, k, tok_idx, tok_logw, m, proxies, 0, out, lse};
+    const hipError_t e = csa::launch_attention(d, plan, in, ws, stream);
+    return e == hipSuccess ? CSA_OK : hip_fail(e, "sparse_decode_attn");
+}
+
+int dense_decode_attn(const csa_shape* shape, const void* q, const void* K, const void* V, float* out, float* lse,
+                      void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    csa::Dims d;
+    if (int rc = make_dims(shape, &d)) return rc;
+    if (!q || !K || !V || !out) return fail(CSA_ERR_INVALID_ARG, "dense_decode_attn: NULL tensor pointer");
+    if (!aligned16(q) || !aligned16(K) || !aligned16(V) || !aligned4(out) || (lse && !aligned4(lse)))
+        return fail(CSA_ERR_INVALID_ARG, "dense_decode_attn: misaligned pointer");
+    if (int rc = attn_rows_ok(d, 0, 0, 0, 1)) return rc;
+    const csa::AttnPlan plan = csa::plan_attention(d, 0, 0, 0, 1);
+    if (int rc = check_ws(plan.ws_bytes, ws, ws_bytes)) return rc;
+    csa::AttnInputs in{q, K, V, nullptr, nullptr, nullptr, 0, nullptr, nullptr, 0, 0, 1, out, lse};
+    const hipError_t e = csa::launch_attention(d, plan, in, ws, stream);
+    return e == hipSuccess ? CSA_OK : hip_fail(e, "dense_decode_attn");
+}
+
+size_t csa_workspace_size(const csa_shape* shape, csa_entry entry, int32_t k, int32_t m)
+{
+    csa::Dims d;
+    if (make_dims(shape, &d) != CSA_OK) return 0;
+    switch (entry) {
+    case CSA_WS_BLOCK_SCORE_SUMMARY:
+    case CSA_WS_BLOCK_SCORE_EXACT_MASS: return block_score_ws(d);
+    case CSA_WS_SPARSE_DECODE_ATTN: {
+        if (k < 0 || k > d.nb || m < 0) {
+            fail(CSA_ERR_INVALID_ARG, "csa_workspace_size: k=%d or m=%d out of range", k, m);
+            return 0;
+        }
+        if (attn_rows_ok(d, k, m, 1, 0) != CSA_OK) return 0;
+        // proxies change the row count; size for the larger of the two plans
+        const size_t a = csa::plan_attention(d, k, m, 1, 0).ws_bytes;
+        const size_t b = csa::plan_attention(d, k, m, 0, 0).ws_bytes;
+        return a > b ? a : b;
+    }
+    case CSA_WS_DENSE_DECODE_ATTN:
+        if (attn_rows_ok(d, 0, 0, 0, 1) != CSA_OK) return 0;
+        return csa::plan_attention(d, 0, 0, 0, 1).ws_bytes;
+    }
+    fail(CSA_ERR_INVALID_ARG, "csa_workspace_size: unknown entry %d", (int)entry);
+    return 0;
+}
+
+const char* csa_status_str(int status)
+{
+    switch (status) {
+    case CSA_OK: return "ok";
+    case CSA_ERR_INVALID_ARG: return "invalid argument";
+    case CSA_ERR_UNSUPPORTED: return "unsupported";
+    case CSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case CSA_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+    }
+}
+
+const char* csa_last_error(void) { return g_last_error; }
+
+}  // extern "C"

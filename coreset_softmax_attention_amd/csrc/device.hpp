@@ -1,0 +1,140 @@
+// device.hpp -- device helpers shared by the gfx950 kernels of libcsa.
+//
+// Row layout used by every kernel: a row of d elements is read as 16-byte
+// chunks, one chunk per lane, so a row occupies LPR = d * elem_bytes / 16
+// consecutive lanes of a 64-wide wavefront and one wave-wide load instruction
+// covers 64 / LPR whole rows (fully coalesced).  Dot products are reduced over
+// the LPR lanes of a row with DPP lane permutes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa {
+
+enum : int { DT_F32 = 0, DT_BF16 = 1 };
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+template <int DT>
+struct Elem;
+template <>
+struct Elem<DT_F32> {
+    static constexpr int bytes = 4;
+    static constexpr int per16 = 4;  // elements per 16-byte chunk
+};
+template <>
+struct Elem<DT_BF16> {
+    static constexpr int bytes = 2;
+    static constexpr int per16 = 8;
+};
+
+// Geometry of a row of D elements of type DT in a 64-lane wavefront.
+template <int DT, int D>
+struct RowGeom {
+    static constexpr int row_bytes = D * Elem<DT>::bytes;
+    static constexpr int lpr = row_bytes / 16;  // lanes per row
+    static constexpr int rpw = 64 / lpr;        // rows per wave-wide load
+    static constexpr int epl = Elem<DT>::per16; // elements per lane
+    static_assert(lpr >= 8 && lpr <= 32 && (lpr & (lpr - 1)) == 0, "unsupported row width");
+};
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Nontemporal 16-byte load: data read once, do not keep it in the caches.
+__device__ __forceinline__ uint4 ld16_nt(const void* p)
+{
+    const uint4* q = reinterpret_cast<const uint4*>(p);
+    uint4 r;
+    r.x = __builtin_nontemporal_load(&reinterpret_cast<const uint32_t*>(q)[0]);
+    r.y = __builtin_nontemporal_load(&reinterpret_cast<const uint32_t*>(q)[1]);
+    r.z = __builtin_nontemporal_load(&reinterpret_cast<const uint32_t*>(q)[2]);
+    r.w = __builtin_nontemporal_load(&reinterpret_cast<const uint32_t*>(q)[3]);
+    return r;
+}
+
+// 16 bytes -> per16 floats.  A bfloat16 is the upper half of a binary32.
+template <int DT>
+__device__ __forceinline__ void unpack(const uint4& r, float* f)
+{
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+    if constexpr (DT == DT_F32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(w[i]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = __uint_as_float(w[i] << 16);
+            f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+}
+
+// DPP lane permutes (gfx9 encodings).
+enum : int {
+    DPP_QUAD_1032 = 0xB1,     // quad_perm [1,0,3,2]
+    DPP_QUAD_2301 = 0x4E,     // quad_perm [2,3,0,1]
+    DPP_ROW_MIRROR = 0x140,   // lane i <-> 15 - i within 16 lanes
+    DPP_ROW_HMIRROR = 0x141,  // lane i <-> 7 - i within 8 lanes
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __builtin_amdgcn_update_dpp(0.0f, v, CTRL, 0xf, 0xf, false);
+}
+
+// Sum over aligned groups of W lanes (W = 8, 16 or 32); every lane of the group
+// receives the group's sum.
+template <int W>
+__device__ __forceinline__ float group_sum(float v)
+{
+    v += dpp<DPP_QUAD_1032>(v);
+    v += dpp<DPP_QUAD_2301>(v);
+    v += dpp<DPP_ROW_HMIRROR>(v);
+    if constexpr (W >= 16) v += dpp<DPP_ROW_MIRROR>(v);
+    if constexpr (W >= 32) v += __shfl_xor(v, 16);
+    return v;
+}
+
+template <int W>
+__device__ __forceinline__ float group_max(float v)
+{
+    v = fmaxf(v, dpp<DPP_QUAD_1032>(v));
+    v = fmaxf(v, dpp<DPP_QUAD_2301>(v));
+    v = fmaxf(v, dpp<DPP_ROW_HMIRROR>(v));
+    if constexpr (W >= 16) v = fmaxf(v, dpp<DPP_ROW_MIRROR>(v));
+    if constexpr (W >= 32) v = fmaxf(v, __shfl_xor(v, 16));
+    return v;
+}
+
+// 2^x with 2^-inf = 0.
+__device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Scale factor 2^(m_old - m_new) of an online-softmax state, 0 for an empty state.
+__device__ __forceinline__ float rescale(float m_old, float m_new)
+{
+    return m_old == kNegInf ? 0.0f : exp2_(m_old - m_new);
+}
+
+// fp64 -> bfloat16 bit pattern, round to nearest with ties to even, in one step.
+__device__ __forceinline__ uint16_t bf16_from_f64(double x)
+{
+    const uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
+    const uint16_t sign = static_cast<uint16_t>((u >> 48) & 0x8000u);
+    const uint64_t mag = u & 0x7fffffffffffffffull;
+    if (mag > 0x7ff0000000000000ull) return 0x7fc0;  // NaN
+    if ((mag >> 52) >= 897) {                        // |x| >= 2^-126: a normal bfloat16
+        // keep 7 of the 52 fraction bits; add half an ulp minus one, plus the kept lsb
+        const uint64_t r = (mag + 0x00000fffffffffffull + ((mag >> 45) & 1u)) >> 45;
+        const uint64_t b = r - (static_cast<uint64_t>(1023 - 127) << 7);  // rebias exponent
+        return b >= 0x7f80u ? static_cast<uint16_t>(sign | 0x7f80u) : static_cast<uint16_t>(sign | b);
+    }
+    // below 2^-126 the spacing is 2^-133: round |x| * 2^133 to an integer (0..128)
+    const double q = __builtin_rint(__builtin_ldexp(__builtin_fabs(x), 133));
+    return static_cast<uint16_t>(sign | static_cast<uint16_t>(q));
+}
+
+}  // namespace csa

@@ -1,0 +1,68 @@
+// launch.hpp -- host-side launchers of the libcsa kernels (internal interface
+// between the C-ABI entry points and the kernel files).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa {
+
+// Validated shape with derived quantities.
+struct Dims {
+    int B, Hq, Hkv, G, d, n, L, nb;
+    int dtype;           // DT_F32 / DT_BF16
+    float scale;         // logit scale (natural units)
+    float ln_L, ln_last; // ln c_b of a full block and of the last block
+    int pairs() const { return B * Hkv; }
+};
+
+// ---- summaries -------------------------------------------------------------
+hipError_t launch_summary(const Dims& s, const void* K, const void* V, void* Kbar, void* Vbar,
+                          hipStream_t st);
+
+// ---- block scores ----------------------------------------------------------
+// Per-head block logits (natural log units).  When G == 1 they are the scores
+// and dst is scores [B, Hkv, nb]; otherwise dst is [B, Hq, nb] workspace.
+hipError_t launch_block_logits_summary(const Dims& s, const void* q, const void* Kbar, float* dst,
+                                       hipStream_t st);
+hipError_t launch_block_logits_exact(const Dims& s, const void* q, const void* K, float* dst,
+                                     hipStream_t st);
+hipError_t launch_group_score(const Dims& s, const float* logits, float* scores, hipStream_t st);
+
+// ---- top-k -----------------------------------------------------------------
+hipError_t launch_topk(int rows, int nb, int k, const float* scores, int32_t* sel, hipStream_t st);
+
+// ---- attention -------------------------------------------------------------
+struct AttnPlan {
+    int rows;            // virtual rows per KV head (exact + weighted + proxy)
+    int exact_rows;      // rows of the exact segment (k L, or n for dense)
+    int hg;              // query heads per workgroup
+    int hchunks;         // ceil(G / hg)
+    int splits;          // workgroups per (KV head, head chunk)
+    int rows_per_split;  // multiple of the wave tile
+    size_t ws_bytes;     // partial states when splits > 1
+};
+
+struct AttnInputs {
+    const void* q;
+    const void* K;
+    const void* V;
+    const void* Kbar;
+    const void* Vbar;
+    const int32_t* sel;
+    int k;
+    const int32_t* tok_idx;
+    const float* tok_logw;
+    int m;
+    int proxies;
+    int dense;
+    float* out;
+    float* lse;
+};
+
+AttnPlan plan_attention(const Dims& s, int k, int m, int proxies, int dense);
+hipError_t launch_attention(const Dims& s, const AttnPlan& plan, const AttnInputs& in, void* ws,
+                            hipStream_t st);
+
+}  // namespace csa

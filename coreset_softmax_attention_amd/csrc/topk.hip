@@ -1,0 +1,141 @@
+// topk.hip -- the k largest block scores of each row, ties to the lower index.
+//
+// One block set is chosen per KV head and shared by its query heads ("COBS:
+// Cumulant Order Block Sparse Attention", Eqs. (4)-(5)).  One workgroup per
+// row:
+//   1. scores are mapped to order-preserving unsigned keys (+0 and -0 map to
+//      the same key, so they tie);
+//   2. a most-significant-digit radix select (4 passes of 8 bits, histograms
+//      in LDS) finds the k-th largest key T and how many keys equal to T are
+//      needed after all keys greater than T;
+//   3. a scan in index order writes every index with key > T and the lowest
+//      indices with key == T, so the output is ascending by index.
+// Integer histograms and scans only: the result does not depend on timing.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace csa {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ uint32_t order_key(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u) u = 0;  // -0 ties with +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Exclusive prefix sum over the workgroup (256 threads); also returns the total.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* total, int* sm /* >= 4 ints */)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(incl, off);
+        if (lane >= off) incl += t;
+    }
+    if (lane == 63) sm[wave] = incl;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) {
+        if (w < wave) before += sm[w];
+        all += sm[w];
+    }
+    __syncthreads();
+    *total = all;
+    return before + incl - v;
+}
+
+__global__ void __launch_bounds__(kThreads) topk_kernel(const float* scores, int32_t* sel, int nb, int k)
+{
+    __shared__ int hist[256];
+    __shared__ int scan_sm[4];
+    __shared__ uint32_t sh_digit;
+    __shared__ int sh_rem;
+
+    const int row = blockIdx.x, tid = threadIdx.x;
+    const int kk = min(k, nb);
+    const float* s = scores + (size_t)row * nb;
+    int32_t* out = sel + (size_t)row * kk;
+    if (kk == 0) return;
+    if (kk == nb) {
+        for (int i = tid; i < nb; i += kThreads) out[i] = i;
+        return;
+    }
+
+    uint32_t prefix = 0, mask = 0;
+    int remaining = kk;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        hist[tid] = 0;
+        __syncthreads();
+        for (int i = tid; i < nb; i += kThreads) {
+            const uint32_t u = order_key(s[i]);
+            if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1);
+        }
+        __syncthreads();
+        // thread d: keys of the current prefix whose digit is above d (reverse scan)
+        const int d = 255 - tid;
+        const int cnt = hist[d];
+        int tot;
+        const int above = block_exclusive_scan(cnt, &tot, scan_sm);
+        if (above < remaining && above + cnt >= remaining) {
+            sh_digit = (uint32_t)d;
+            sh_rem = remaining - above;
+        }
+        __syncthreads();
+        prefix |= sh_digit << shift;
+        mask |= 0xffu << shift;
+        remaining = sh_rem;
+        __syncthreads();
+    }
+    const uint32_t T = prefix;
+    const int need_eq = remaining;  // keys equal to T still to take, lowest index first
+
+    const int per = (nb + kThreads - 1) / kThreads;
+    const int i0 = min(nb, tid * per), i1 = min(nb, i0 + per);
+    int eq = 0;
+    for (int i = i0; i < i1; ++i) eq += order_key(s[i]) == T;
+    int tot;
+    int eq_before = block_exclusive_scan(eq, &tot, scan_sm);
+    int take = 0;
+    {
+        int e = eq_before;
+        for (int i = i0; i < i1; ++i) {
+            const uint32_t u = order_key(s[i]);
+            if (u > T) {
+                ++take;
+            } else if (u == T) {
+                if (e < need_eq) ++take;
+                ++e;
+            }
+        }
+    }
+    int pos = block_exclusive_scan(take, &tot, scan_sm);
+    {
+        int e = eq_before;
+        for (int i = i0; i < i1; ++i) {
+            const uint32_t u = order_key(s[i]);
+            bool keep = false;
+            if (u > T) {
+                keep = true;
+            } else if (u == T) {
+                keep = e < need_eq;
+                ++e;
+            }
+            if (keep) out[pos++] = i;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_topk(int rows, int nb, int k, const float* scores, int32_t* sel, hipStream_t st)
+{
+    topk_kernel<<<dim3((unsigned)rows), dim3(kThreads), 0, st>>>(scores, sel, nb, k);
+    return hipGetLastError();
+}
+
+}  // namespace csa

@@ -1,0 +1,185 @@
+/*
+ * csa.h -- C-ABI of libcsa.so: selective decode attention for MI355X (gfx950).
+ *
+ * A decode query attends to a small read of its KV cache: the exact tokens of
+ * the top-k blocks of its KV head, optional weighted tokens, and one
+ * count-aware mean proxy per unread block.  Sources, cited by page title and
+ * section / equation:
+ *   [OA]   "OpenAttention reads 1% of the KV cache -- Count-aware tail proxy",
+ *          section "Skipping reviews without losing the verdict" (the proxy is
+ *          one virtual token: mean value of the tokens it replaces, logit =
+ *          their mean logit + ln count) and section "Three helpers that make
+ *          the proxy accurate" (exact tokens and proxies in one online-softmax
+ *          pass).
+ *   [COBS] "COBS: Cumulant Order Block Sparse Attention": Eq. (1) block mass
+ *          m_b, Eqs. (2)-(3) keep a block set and renormalise, Eq. (5) the
+ *          additive GQA block score, Eq. (18) the first-order mean-pool score,
+ *          and the OSA paragraph (exact masses from a dense key read).
+ *   [WC]   "WildCat: Near-Linear Attention in Theory and Practice", Abstract:
+ *          attention over a weighted subset, sum w e^s v / sum w e^s.
+ *
+ * Layout (all row-major, all device memory owned by the caller):
+ *   q            [B, Hq, d]        dtype          (unscaled)
+ *   K, V         [B, Hkv, n, d]    dtype
+ *   Kbar, Vbar   [B, Hkv, nb, d]   dtype          nb = ceil(n / L)
+ *   scores       [B, Hkv, nb]      float
+ *   sel          [B, Hkv, k]       int32, strictly ascending block indices
+ *   tok_idx      [B, Hkv, m]       int32 in [0, n)
+ *   tok_logw     [B, Hkv, m]       float (natural-log weights, finite)
+ *   out          [B, Hq, d]        float
+ *   lse          [B, Hq]           float (natural log of the softmax denominator)
+ * Query head h belongs to KV head h / G with G = Hq / Hkv.  Block b holds
+ * tokens [b L, min(n, (b + 1) L)); c_b is its token count.  The logit of a
+ * token is s_i = scale * q_h . K_i with scale = 1/sqrt(d) unless given.
+ *
+ * Conventions:
+ *   - Every entry point validates its arguments on the host before launching
+ *     anything; on a non-OK return nothing was launched and no output was
+ *     touched.  csa_last_error() then describes the problem.
+ *   - Launches are asynchronous on the given stream (NULL = the default
+ *     stream); nothing synchronises.  A launch failure returns CSA_ERR_HIP.
+ *   - Nothing is allocated.  Entry points that need scratch memory take a
+ *     workspace (ws, ws_bytes) of at least csa_workspace_size() bytes, 256-byte
+ *     aligned.  A workspace serves one call at a time; its contents between
+ *     calls are meaningless.
+ *   - No floating-point atomics: results are bitwise reproducible for the same
+ *     inputs, shapes and device.
+ *   - Supported in this version: dtype CSA_F32 or CSA_BF16, d in {64, 128},
+ *     G <= 64, n <= 2^30.  All pointers 16-byte aligned.
+ *   - Inputs must be finite.  Indices outside their range are rejected only
+ *     where the host can see them (sizes); device-resident index values are
+ *     trusted.
+ */
+#ifndef CSA_H
+#define CSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum csa_status {
+    CSA_OK = 0,
+    CSA_ERR_INVALID_ARG = -1, /* null pointer, bad shape or size, misalignment */
+    CSA_ERR_UNSUPPORTED = -2, /* valid but outside this version (d, dtype, G)  */
+    CSA_ERR_WORKSPACE = -3,   /* workspace missing, too small or misaligned    */
+    CSA_ERR_HIP = -4          /* a HIP launch or query failed                  */
+} csa_status;
+
+typedef enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
+
+typedef enum csa_score_mode {
+    CSA_SCORE_SUMMARY = 0,   /* first-order score from the mean key  [COBS] Eq. (18) */
+    CSA_SCORE_EXACT_MASS = 1 /* exact block mass from every key ("OSA")             */
+} csa_score_mode;
+
+typedef enum csa_proxy_mode {
+    CSA_PROXY_NONE = 0,      /* unread blocks are discarded, the rest renormalised   */
+    CSA_PROXY_COMPLEMENT = 1 /* one count-aware proxy per unread block       [OA]    */
+} csa_proxy_mode;
+
+typedef enum csa_entry {
+    CSA_WS_BLOCK_SCORE_SUMMARY = 0,
+    CSA_WS_BLOCK_SCORE_EXACT_MASS = 1,
+    CSA_WS_SPARSE_DECODE_ATTN = 2,
+    CSA_WS_DENSE_DECODE_ATTN = 3
+} csa_entry;
+
+typedef struct csa_shape {
+    int32_t batch;      /* B   >= 1                          */
+    int32_t n_q_heads;  /* Hq  >= 1, a multiple of Hkv       */
+    int32_t n_kv_heads; /* Hkv >= 1                          */
+    int32_t head_dim;   /* d: 64 or 128                      */
+    int32_t n_tokens;   /* n   >= 1                          */
+    int32_t block_size; /* L   >= 1                          */
+    csa_dtype dtype;    /* of q, K, V, Kbar, Vbar            */
+    float scale;        /* logit scale; 0 means 1/sqrt(d)    */
+} csa_shape;
+
+/*
+ * kv_summary_build -- per block, the mean key and the mean value
+ * ([OA] "Skipping reviews...": the proxy value is the mean of the values it
+ * replaces; [COBS] Eq. (18): the mean-pool summary is the mean key).
+ * Kbar_b = round(sum_{i in b} K_i / c_b), summed in fp64 token by token, then
+ * rounded once (to nearest, ties to even) to the storage dtype; Vbar alike.
+ * Reads K, V [B, Hkv, n, d]; writes Kbar, Vbar [B, Hkv, nb, d].
+ * Run once per cache (after prefill); no workspace.
+ */
+int kv_summary_build(const csa_shape* shape, const void* K, const void* V, void* Kbar, void* Vbar,
+                     hipStream_t stream);
+
+/*
+ * block_score -- the score by which blocks are ranked, per KV head.
+ * Per query head h and block b the block logit is
+ *   SUMMARY:    l_hb = scale q_h . Kbar_b + ln c_b         (keys = Kbar)  [COBS] Eq. (18)
+ *   EXACT_MASS: l_hb = ln m_hb = ln sum_{i in b} e^{s_i}   (keys = K)     [COBS] Eq. (1)
+ * and the score of block b of KV head j is
+ *   G = 1: l_hb (ranking by log-mass, [COBS] Eq. (5) with G = 1);
+ *   G > 1: ln sum_{h in group j} exp(l_hb - ln sum_b' e^{l_hb'}),
+ *          the logarithm of the additive GQA score of [COBS] Eq. (5).
+ * Writes scores [B, Hkv, nb].  Workspace: csa_workspace_size(shape,
+ * CSA_WS_BLOCK_SCORE_SUMMARY or _EXACT_MASS, 0, 0) bytes (0 when G = 1).
+ */
+int block_score(const csa_shape* shape, csa_score_mode mode, const void* q, const void* keys,
+                float* scores, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * topk_select -- per row, the k blocks of largest score; equal scores (+0 and
+ * -0 are equal) go to the lower index.  Selection is shared by the query heads
+ * of a KV head ([COBS] Eq. (4)-(5): one block set per KV head).
+ * scores [rows, nb] -> sel [rows, min(k, nb)] written in ascending index order.
+ * k >= nb selects every block; k = 0 writes nothing.  Scores must not be NaN.
+ */
+int topk_select(int32_t rows, int32_t nb, int32_t k, const float* scores, int32_t* sel,
+                hipStream_t stream);
+
+/*
+ * sparse_decode_attn -- one online-softmax pass over the virtual tokens of each
+ * KV head ([OA] "Three helpers...": exact tokens and proxies in one pass):
+ *   - every token of the k selected blocks sel (log-weight 0);
+ *   - m weighted tokens tok_idx with log-weights tok_logw ([WC] Abstract);
+ *   - with CSA_PROXY_COMPLEMENT, one proxy per block not in sel: key Kbar_b,
+ *     value Vbar_b, log-weight ln c_b ([OA] "Skipping reviews...").
+ * For each query head: l_e = scale q_h . key_e + logw_e, out_h = sum e^{l_e}
+ * val_e / sum e^{l_e}, lse_h = ln sum e^{l_e}.  With CSA_PROXY_NONE and m = 0
+ * this is keep-and-renormalise ([COBS] Eqs. (2)-(3)).
+ * sel may be NULL when k = 0; tok_idx/tok_logw may be NULL when m = 0;
+ * Kbar/Vbar may be NULL with CSA_PROXY_NONE; lse may be NULL.
+ * 0 <= k <= nb; an empty virtual-token set (k = 0, m = 0, no proxies) is
+ * CSA_ERR_INVALID_ARG.  Workspace: csa_workspace_size(shape,
+ * CSA_WS_SPARSE_DECODE_ATTN, k, m) bytes.
+ */
+int sparse_decode_attn(const csa_shape* shape, const void* q, const void* K, const void* V,
+                       const void* Kbar, const void* Vbar, const int32_t* sel, int32_t k,
+                       const int32_t* tok_idx, const float* tok_logw, int32_t m,
+                       csa_proxy_mode proxy_mode, float* out, float* lse, void* ws,
+                       size_t ws_bytes, hipStream_t stream);
+
+/*
+ * dense_decode_attn -- softmax attention over all n tokens (the reference the
+ * sparse path approximates; [COBS] Eq. (1) with every block kept).
+ * out [B, Hq, d], lse [B, Hq] (lse may be NULL).  Workspace:
+ * csa_workspace_size(shape, CSA_WS_DENSE_DECODE_ATTN, 0, 0) bytes.
+ */
+int dense_decode_attn(const csa_shape* shape, const void* q, const void* K, const void* V,
+                      float* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes needed by an entry point for this shape (k, m as the call
+ * will pass them).  Returns 0 for an invalid shape (see csa_last_error()). */
+size_t csa_workspace_size(const csa_shape* shape, csa_entry entry, int32_t k, int32_t m);
+
+/* Static description of a status code. */
+const char* csa_status_str(int status);
+
+/* Detail of the last non-OK return on this host thread ("" if none). */
+const char* csa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA_H */

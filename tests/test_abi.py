@@ -1,0 +1,149 @@
+"""The C-ABI library without a GPU: it loads, exports every function include/csa.h
+declares, and rejects invalid arguments on the host before launching anything.
+No call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from coreset_softmax_attention_amd import csa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa.h")
+FAKE = 0x10000  # a 16-byte aligned address that is never dereferenced (validation fails first)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(csa.library_path()):
+        from coreset_softmax_attention_amd import build_lib
+
+        build_lib.build()
+    return csa.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:int|size_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)
+
+
+def test_header_declares_the_entry_points():
+    names = set(declared_functions())
+    assert {"kv_summary_build", "block_score", "topk_select", "sparse_decode_attn", "dense_decode_attn",
+            "csa_workspace_size", "csa_status_str", "csa_last_error"} <= names
+
+
+def test_library_exports_every_declared_function(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", csa.library_path()], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(L, name) is not None
+
+
+def test_header_is_valid_c():
+    subprocess.run(["gcc", "-x", "c", "-std=c11", "-fsyntax-only", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                    "-I/opt/rocm/include", HEADER], check=True)
+
+
+def shape(B=2, Hq=8, Hkv=2, d=128, n=1024, L=64, dtype=csa.CSA_BF16, scale=0.0):
+    return csa.Shape(B, Hq, Hkv, d, n, L, dtype, scale)
+
+
+def sparse(L, s, k=2, m=0, proxy=1, sel=FAKE, ptrs=FAKE, ws=None, wsb=0, kbar=FAKE):
+    p = ptrs
+    return L.sparse_decode_attn(ctypes.byref(s) if s is not None else None, p, p, p, kbar, kbar, sel, k,
+                                FAKE if m else None, FAKE if m else None, m, proxy, p, p, ws, wsb, None)
+
+
+def test_status_strings(L):
+    assert L.csa_status_str(0) == b"ok"
+    assert L.csa_status_str(-1) == b"invalid argument"
+    assert L.csa_status_str(-2) == b"unsupported"
+    assert L.csa_status_str(-3) == b"workspace missing or too small"
+    assert L.csa_status_str(-4) == b"HIP error"
+
+
+@pytest.mark.parametrize("bad,code,msg", [
+    (dict(B=0), csa.CSA_ERR_INVALID_ARG, b"non-positive"),
+    (dict(Hq=6, Hkv=4), csa.CSA_ERR_INVALID_ARG, b"multiple"),
+    (dict(d=96), csa.CSA_ERR_UNSUPPORTED, b"head_dim 96"),
+    (dict(dtype=7), csa.CSA_ERR_INVALID_ARG, b"dtype"),
+    (dict(scale=float("inf")), csa.CSA_ERR_INVALID_ARG, b"scale"),
+    (dict(Hq=130, Hkv=2), csa.CSA_ERR_UNSUPPORTED, b"group size"),
+])
+def test_shape_validation(L, bad, code, msg):
+    s = shape(**bad)
+    assert sparse(L, s) == code
+    assert msg in L.csa_last_error()
+    assert L.dense_decode_attn(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == code
+    assert L.kv_summary_build(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None) == code
+    assert L.block_score(ctypes.byref(s), 0, FAKE, FAKE, FAKE, None, 0, None) == code
+    assert L.csa_workspace_size(ctypes.byref(s), 2, 1, 0) == 0
+
+
+def test_null_shape(L):
+    assert sparse(L, None) == csa.CSA_ERR_INVALID_ARG
+    assert b"shape is NULL" in L.csa_last_error()
+
+
+def test_sparse_argument_checks(L):
+    s = shape()  # nb = 16
+    assert sparse(L, s, k=0, m=0, proxy=0) == csa.CSA_ERR_INVALID_ARG
+    assert b"empty virtual-token set" in L.csa_last_error()
+    assert sparse(L, s, k=17) == csa.CSA_ERR_INVALID_ARG
+    assert sparse(L, s, k=-1) == csa.CSA_ERR_INVALID_ARG
+    assert sparse(L, s, k=2, sel=None) == csa.CSA_ERR_INVALID_ARG
+    assert sparse(L, s, proxy=5) == csa.CSA_ERR_INVALID_ARG
+    assert sparse(L, s, proxy=1, kbar=None) == csa.CSA_ERR_INVALID_ARG
+    assert sparse(L, s, ptrs=FAKE + 2) == csa.CSA_ERR_INVALID_ARG
+    assert b"misaligned" in L.csa_last_error()
+    m_bad = L.sparse_decode_attn(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, None, None, 3, 1, FAKE,
+                                 FAKE, None, 0, None)
+    assert m_bad == csa.CSA_ERR_INVALID_ARG and b"weighted tokens missing" in L.csa_last_error()
+
+
+def test_workspace_is_checked_before_launch(L):
+    s = shape(B=32, Hq=32, Hkv=8, n=32768)  # the 1 %-read decode shape needs split-K partials
+    need = L.csa_workspace_size(ctypes.byref(s), csa.CSA_WS_SPARSE_DECODE_ATTN, 5, 0)
+    assert need > 0
+    assert sparse(L, s, k=5, ws=None) == csa.CSA_ERR_WORKSPACE
+    assert sparse(L, s, k=5, ws=FAKE, wsb=need - 1) == csa.CSA_ERR_WORKSPACE
+    assert sparse(L, s, k=5, ws=FAKE + 8, wsb=need) == csa.CSA_ERR_WORKSPACE
+    dneed = L.csa_workspace_size(ctypes.byref(s), csa.CSA_WS_DENSE_DECODE_ATTN, 0, 0)
+    assert dneed > 0
+    assert L.dense_decode_attn(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == csa.CSA_ERR_WORKSPACE
+    bneed = L.csa_workspace_size(ctypes.byref(s), csa.CSA_WS_BLOCK_SCORE_SUMMARY, 0, 0)
+    assert bneed == 32 * 32 * 512 * 4
+    assert L.block_score(ctypes.byref(s), 0, FAKE, FAKE, FAKE, None, 0, None) == csa.CSA_ERR_WORKSPACE
+    assert L.block_score(ctypes.byref(s), 9, FAKE, FAKE, FAKE, None, 0, None) == csa.CSA_ERR_INVALID_ARG
+
+
+def test_workspace_sizes(L):
+    mha = shape(B=8, Hq=32, Hkv=32, n=32768)
+    assert L.csa_workspace_size(ctypes.byref(mha), csa.CSA_WS_BLOCK_SCORE_EXACT_MASS, 0, 0) == 0  # G = 1
+    assert L.csa_workspace_size(ctypes.byref(mha), 17, 0, 0) == 0
+    assert b"unknown entry" in L.csa_last_error()
+    assert L.csa_workspace_size(ctypes.byref(mha), csa.CSA_WS_SPARSE_DECODE_ATTN, 513, 0) == 0
+
+
+def test_topk_argument_checks(L):
+    assert L.topk_select(-1, 4, 2, FAKE, FAKE, None) == csa.CSA_ERR_INVALID_ARG
+    assert L.topk_select(3, 0, 2, FAKE, FAKE, None) == csa.CSA_ERR_INVALID_ARG
+    assert L.topk_select(3, 4, -2, FAKE, FAKE, None) == csa.CSA_ERR_INVALID_ARG
+    assert L.topk_select(3, 4, 2, None, FAKE, None) == csa.CSA_ERR_INVALID_ARG
+    assert L.topk_select(3, 4, 2, FAKE + 1, FAKE, None) == csa.CSA_ERR_INVALID_ARG
+    # nothing to do: no launch, OK
+    assert L.topk_select(0, 4, 2, None, None, None) == csa.CSA_OK
+    assert L.topk_select(3, 4, 0, None, None, None) == csa.CSA_OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(csa, "_LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(csa, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        csa.lib()
