@@ -198,7 +198,7 @@ size_t csa_workspace_size(const csa_shape* shape, csa_entry entry, int32_t k, in
         if (attn_rows_ok(d, k, m, 1, 0) != CSA_OK) return 0;
         // proxies change the row count; size for the larger of the two plans
         const size_t a = csa::plan_attention(d, k, m, 1, 0).ws_bytes;
-        const size_t b = csa::plan_attention(d, k, m, 0, 0).ws_bytes;
+        const size_t b = (k > 0 || m > 0) ? csa::plan_attention(d, k, m, 0, 0).ws_bytes : 0;
         return a > b ? a : b;
     }
     case CSA_WS_DENSE_DECODE_ATTN:

@@ -320,6 +320,12 @@ AttnPlan plan_attention(const Dims& s, int k, int m, int proxies, int dense)
     pl.rows = pl.exact_rows + m + (proxies ? s.nb : 0);
     pl.hg = s.G <= 8 ? s.G : 8;
     pl.hchunks = (s.G + pl.hg - 1) / pl.hg;
+    if (pl.rows <= 0) {  // empty virtual-token set: nothing to plan (callers reject it)
+        pl.splits = 1;
+        pl.rows_per_split = 0;
+        pl.ws_bytes = 0;
+        return pl;
+    }
     const int elem = s.dtype == DT_F32 ? 4 : 2;
     const int rpw = 64 / (s.d * elem / 16);
     const int tile = rpw * unroll_for(pl.hg);

@@ -123,6 +123,11 @@ def test_workspace_is_checked_before_launch(L):
     assert L.block_score(ctypes.byref(s), 9, FAKE, FAKE, FAKE, None, 0, None) == csa.CSA_ERR_INVALID_ARG
 
 
+def test_workspace_size_with_no_exact_or_weighted_tokens(L):
+    s = shape()
+    assert L.csa_workspace_size(ctypes.byref(s), csa.CSA_WS_SPARSE_DECODE_ATTN, 0, 0) >= 0
+
+
 def test_workspace_sizes(L):
     mha = shape(B=8, Hq=32, Hkv=32, n=32768)
     assert L.csa_workspace_size(ctypes.byref(mha), csa.CSA_WS_BLOCK_SCORE_EXACT_MASS, 0, 0) == 0  # G = 1
