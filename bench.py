@@ -4,22 +4,33 @@
 A step is one decode step of one attention layer for a batch of sequences:
     block_score (summary mode) -> topk_select -> sparse_decode_attn
 over a KV cache whose block summaries were built beforehand (kv_summary_build
-runs once per cache, after prefill, and is timed separately).  Inputs are the
-seeded synthetic workload (default: batch 32, 32K context, Llama-3.1-8B-shaped
-layer, 1 % of the tokens read exactly plus one proxy per unread block), resident
-in HBM before the timed region.  Before every step a 1 GiB buffer is written so
-that no input is served from the 256 MB last-level cache (cold cache, like a
-different layer's cache between two uses); each step is bracketed by HIP events
-on the stream the kernels run on, and the flush is outside the events.
+runs once per cache after prefill; it is timed separately for information).
+The step runs through selective_decode_step, which does the three in one
+kernel per KV head for this shape; the same step through the three separate
+entry points is timed too ("modular").
 
-Prints one JSON line (see the keys below).  --gpus above 1 is refused: this
-build runs on one GPU.
+Cold cache without flushing: the inputs are replicated into NL independent
+caches resident in HBM (like NL layers of a model) and consecutive steps use
+consecutive layers, so between two uses of one layer's data the step touches
+NL - 1 other layers' data (about 1 GB for the default shape, four times the
+256 MB last-level cache).  The default run:
+  * eager: K steps, one Python call per entry point, HIP events around the
+    whole loop;
+  * graph: the NL-layer decode captured once in a HIP graph and replayed
+    (the way a serving loop runs decode), HIP events around the replays;
+  * attention only: a graph of NL sparse_decode_attn launches (one per layer),
+    for the roofline figure of that kernel on its own.
+`value` is queries/s of the graph-replayed step (one query = one sequence's
+decode token through the layer, all query heads); the roofline object is for
+the step's kernel (bytes: every mean key, the mean values of unread blocks,
+the exact key/value rows, the queries and the outputs).
+
+Prints one JSON line.  --gpus above 1 is refused: this build runs on one GPU.
 """
 from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
 import sys
 import time
@@ -30,25 +41,54 @@ import numpy as np
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default=None, help="workload name (default: the headline decode shape)")
-    ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps (warm cache)")
+    ap.add_argument("--layers", type=int, default=8, help="independent cache copies cycled through")
+    ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU time budget of the oracle baseline")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--traffic", default=None, help="JSON file with measured HBM bytes per attention launch")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes 8 times (calibrates memory counters)")
     return ap.parse_args()
 
 
+def copy_probe(nbytes):
+    """A plain device-to-device copy of known size, for scaling hardware byte counters."""
+    import torch
+
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(8):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "launches": 8}), flush=True)
+
+
 def algorithmic_bytes(w, m=0):
-    """Bytes the sparse step must move per launch (reads, writes), following the read
-    accounting of the OpenAttention explainer ('A worked example...' / limits paragraph):
-    exact K/V rows of the kept blocks, proxy rows (mean key + mean value) of the other
-    blocks, weighted-token rows, the queries, the selection, and the outputs."""
+    """Bytes the sparse attention must move per launch (reads, writes), following the read
+    accounting of the OpenAttention explainer (exact rows, proxy rows and query-side data):
+    exact K/V rows of the kept blocks, mean key + mean value rows of the other blocks,
+    weighted-token rows (+ index and log-weight), the queries, the selection, the outputs."""
     e = w.elem_bytes
     d, L, k, nb, G = w.head_dim, w.block_size, w.k, w.n_blocks, w.group
     per_read = k * L * 2 * d * e + (nb - k if w.proxies else 0) * 2 * d * e + m * (2 * d * e + 8) + G * d * e + 4 * k
+    per_write = G * (d + 1) * 4
+    pairs = w.batch * w.n_kv_heads
+    return pairs * per_read, pairs * per_write
+
+
+def step_bytes(w, m=0):
+    """Bytes one selective decode step must move (reads, writes): every mean key once (it
+    ranks the blocks and gives the proxy logits), the mean values of the unread blocks,
+    the exact key/value rows of the kept blocks, weighted-token rows, the queries, and the
+    outputs with their log-normalisers."""
+    e = w.elem_bytes
+    d, L, k, nb, G = w.head_dim, w.block_size, w.k, w.n_blocks, w.group
+    per_read = nb * d * e + (nb - k if w.proxies else 0) * d * e + k * L * 2 * d * e + m * (2 * d * e + 8) + G * d * e
     per_write = G * (d + 1) * 4
     pairs = w.batch * w.n_kv_heads
     return pairs * per_read, pairs * per_write
@@ -60,6 +100,10 @@ def main():
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the selective decode path has no "
               "multi-GPU mode in this build.", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
 
     import torch
 
@@ -73,27 +117,33 @@ def main():
     w = W.WORKLOADS[args.workload or W.HEADLINE]
     t0 = time.time()
     data = W.generate(w)
-    gen_s = time.time() - t0
-    print(f"[bench] generated {w.name} in {gen_s:.1f} s", file=sys.stderr, flush=True)
+    print(f"[bench] generated {w.name} in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    q, K, V = (csa.to_device(data[x], dev) for x in ("q", "K", "V"))
+    NL = max(1, args.layers)
+    q = csa.to_device(data["q"], dev)
+    K0, V0 = csa.to_device(data["K"], dev), csa.to_device(data["V"], dev)
     tok_idx = csa.to_device(data["tok_idx"], dev) if w.coreset else None
     tok_logw = csa.to_device(data["tok_logw"], dev) if w.coreset else None
     m = w.coreset
+    del data
 
-    # prefill-time summaries (timed for information)
-    Kbar, Vbar = csa.kv_summary_build(K, V, w.block_size)
+    # prefill-time summaries of layer 0 (timed for information), then the other layers
+    Kbar0, Vbar0 = csa.kv_summary_build(K0, V0, w.block_size)
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    ev[0].record()
-    csa.kv_summary_build(K, V, w.block_size, Kbar, Vbar)
-    ev[1].record()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    csa.kv_summary_build(K0, V0, w.block_size, Kbar0, Vbar0)
+    e1.record()
     torch.cuda.synchronize()
-    summary_ms = ev[0].elapsed_time(ev[1])
+    summary_ms = e0.elapsed_time(e1)
+    layers = [(K0, V0, Kbar0, Vbar0)]
+    for _ in range(NL - 1):
+        layers.append(tuple(x.clone() for x in layers[0]))
+    torch.cuda.synchronize()
 
-    shape = csa.make_shape(q, K, w.block_size)
+    shape = csa.make_shape(q, K0, w.block_size)
     B, Hq, Hkv, nb = w.batch, w.n_q_heads, w.n_kv_heads, w.n_blocks
     scores = torch.empty((B, Hkv, nb), dtype=torch.float32, device=dev)
     sel = torch.empty((B, Hkv, min(w.k, nb)), dtype=torch.int32, device=dev)
@@ -103,45 +153,80 @@ def main():
     ws_score = torch.empty(max(1, csa.workspace_size(shape, mode_entry)), dtype=torch.uint8, device=dev)
     ws_attn = torch.empty(max(1, csa.workspace_size(shape, csa.CSA_WS_SPARSE_DECODE_ATTN, w.k, m)),
                           dtype=torch.uint8, device=dev)
-    keys = Kbar if w.score_mode == "summary" else K
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    ws_step = torch.empty(max(1, csa.workspace_size(shape, csa.CSA_WS_SELECTIVE_DECODE_STEP, w.k, m)),
+                          dtype=torch.uint8, device=dev)
 
-    def step():
+    def score_select(layer):
+        K, V, Kbar, Vbar = layer
+        keys = Kbar if w.score_mode == "summary" else K
         csa.block_score(q, keys, w.score_mode, w.block_size, n_tokens=w.n_tokens, scores=scores, ws=ws_score)
         csa.topk_select(scores, w.k, sel=sel)
-        e_mid.record()
+
+    def attend(layer):
+        K, V, Kbar, Vbar = layer
         csa.sparse_decode_attn(q, K, V, Kbar, Vbar, sel, w.block_size, proxies=w.proxies, tok_idx=tok_idx,
                                tok_logw=tok_logw, out=out, lse=lse, ws=ws_attn)
 
-    e_mid = torch.cuda.Event(enable_timing=True)
-    for i in range(args.warmup):
-        if not args.no_flush:
-            flush.fill_(i & 0xFF)
-        step()
-    torch.cuda.synchronize()
+    def modular(i):
+        score_select(layers[i % NL])
+        attend(layers[i % NL])
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    mids = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    def step(i):
+        K, V, Kbar, Vbar = layers[i % NL]
+        csa.selective_decode_step(q, K, V, Kbar, Vbar, w.k, w.block_size, mode=w.score_mode, proxies=w.proxies,
+                                  tok_idx=tok_idx, tok_logw=tok_logw, out=out, lse=lse, ws=ws_step)
+
+    def timed(fn, reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for r in range(reps):
+            fn(r)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    # eager
+    for i in range(args.warmup):
+        step(i)
+        modular(i)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    for i in range(args.steps):
-        if not args.no_flush:
-            flush.fill_((i + 1) & 0xFF)
-        starts[i].record()
-        e_mid = mids[i]
-        step()
-        ends[i].record()
-    torch.cuda.synchronize()
+    eager_ms = timed(step, args.steps) / args.steps
     wall = time.perf_counter() - wall0
-    step_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
-    attn_ms = np.array([mm.elapsed_time(e) for mm, e in zip(mids, ends)])
-    pre_ms = np.array([s.elapsed_time(mm) for s, mm in zip(starts, mids)])
-    t_step = float(step_ms.mean())
-    t_attn = float(attn_ms.mean())
+    eager_modular_ms = timed(modular, args.steps) / args.steps
 
+    graph_ms = attn_ms = score_ms = modular_ms = None
+    if not args.no_graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):  # warm the capture stream
+            for i in range(NL):
+                step(i)
+                modular(i)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        graphs = {}
+        for name, fn in (("step", step), ("modular", modular), ("score", lambda i: score_select(layers[i])),
+                         ("attn", lambda i: attend(layers[i]))):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(NL):
+                    fn(i)
+            graphs[name] = g
+        reps = max(1, args.steps // NL)
+        for g in graphs.values():
+            g.replay()
+        per = {name: timed(lambda r, g=g: g.replay(), reps) / (reps * NL) for name, g in graphs.items()}
+        graph_ms, modular_ms, score_ms, attn_ms = per["step"], per["modular"], per["score"], per["attn"]
+    else:
+        attn_ms = timed(lambda r: attend(layers[r % NL]), args.steps) / args.steps
+
+    t_step = graph_ms if graph_ms is not None else eager_ms
+    srd, swr = step_bytes(w, m)
+    step_achieved = (srd + swr) / (t_step * 1e-3) / 1e9
     rd, wr = algorithmic_bytes(w, m)
-    achieved = (rd + wr) / (t_attn * 1e-3) / 1e9
+    achieved = (rd + wr) / (attn_ms * 1e-3) / 1e9
     traffic = None
     if args.traffic and os.path.exists(args.traffic):
         traffic = json.load(open(args.traffic)).get("bytes_per_launch")
@@ -150,23 +235,16 @@ def main():
     if not args.no_dense:
         ws_dense = torch.empty(max(1, csa.workspace_size(shape, csa.CSA_WS_DENSE_DECODE_ATTN)), dtype=torch.uint8,
                                device=dev)
-        dout = torch.empty_like(out)
-        dlse = torch.empty_like(lse)
-        ts = []
-        for i in range(6):
-            flush.fill_(i & 0xFF)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            csa.dense_decode_attn(q, K, V, out=dout, lse=dlse, ws=ws_dense)
-            b.record()
-            torch.cuda.synchronize()
-            if i >= 1:
-                ts.append(a.elapsed_time(b))
-        dense_ms = float(np.mean(ts))
+        dout, dlse = torch.empty_like(out), torch.empty_like(lse)
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, data, args.cpu_seconds)
+        def dense(r):
+            K, V, _, _ = layers[r % NL]
+            csa.dense_decode_attn(q, K, V, out=dout, lse=dlse, ws=ws_dense)
+
+        dense(0)
+        dense_ms = timed(dense, 2 * NL) / (2 * NL)
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds)
 
     result = {
         "metric": "selective decode attn: queries/s + achieved HBM GB/s, B=32, 32K ctx, 1% read",
@@ -185,24 +263,38 @@ def main():
             "workload": w.name, "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": w.head_dim,
             "context": w.n_tokens, "block_size": w.block_size, "k_blocks": w.k,
             "exact_read_fraction": w.k * w.block_size / w.n_tokens, "score": w.score_mode, "proxies": w.proxies,
-            "weighted_tokens": m, "cache": "warm" if args.no_flush else "cold (1 GiB written before each step)",
+            "weighted_tokens": m, "layers_cycled": NL,
+            "timing": "HIP graph of the decode step replayed" if graph_ms is not None else "eager",
+            "entry_point": "selective_decode_step",
         },
-        "achieved_hbm_gb_s": achieved,
+        "achieved_hbm_gb_s": step_achieved,
         "head_queries_per_s": B * Hq / (t_step * 1e-3),
-        "step_breakdown_us": {"block_score+topk": float(pre_ms.mean()) * 1e3, "sparse_decode_attn": t_attn * 1e3},
-        "step_p10_p90_us": [float(np.percentile(step_ms, 10)) * 1e3, float(np.percentile(step_ms, 90)) * 1e3],
-        "wall_s_timed_region_incl_flush": wall,
+        "eager_ms_per_step": eager_ms,
+        "eager_wall_s": wall,
+        "modular_ms_per_step": {"graph": modular_ms, "eager": eager_modular_ms},
+        "modular_breakdown_us": {"block_score+topk_select": score_ms * 1e3 if score_ms else None,
+                                 "sparse_decode_attn": attn_ms * 1e3},
         "kv_summary_build_ms": summary_ms,
         "dense_decode_attn_ms": dense_ms,
-        "sparse_vs_dense_speedup": (dense_ms / t_attn) if dense_ms else None,
+        "step_vs_dense_speedup": (dense_ms / t_step) if dense_ms else None,
         "roofline": {
-            "kernel": "sparse_decode_attn",
+            "kernel": "selective_decode_step (decode_step_kernel)",
+            "bound": "hbm",
+            "achieved": step_achieved,
+            "peak": 8000.0,
+            "unit": "GB/s",
+            "frac": step_achieved / 8000.0,
+            "traffic": traffic.get("decode_step") if isinstance(traffic, dict) else None,
+            "algorithmic_bytes": srd + swr,
+        },
+        "roofline_sparse_decode_attn": {
+            "kernel": "sparse_decode_attn (attn_mfma_kernel)",
             "bound": "hbm",
             "achieved": achieved,
             "peak": 8000.0,
             "unit": "GB/s",
             "frac": achieved / 8000.0,
-            "traffic": traffic,
+            "traffic": traffic.get("sparse_decode_attn") if isinstance(traffic, dict) else None,
             "algorithmic_bytes": rd + wr,
         },
         "cpu_baseline": cpu,
@@ -210,14 +302,15 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(w, data, budget_s):
+def cpu_baseline(w, budget_s):
     """The fp64 oracle's decode step (block score, top-k, attention) on the host cores, on a
     bounded sample of the same workload: the first few sequences of the batch."""
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from coreset_softmax_attention_amd import workloads as W
     from oracle import oracle as O
 
     nseq = min(4, w.batch)
-    sub = {k: v[:nseq] for k, v in data.items()}
+    sub = W.generate(w, batches=range(nseq))
     shp = O.Shape(nseq, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_tokens, w.block_size, w.dtype)
     Kbar, Vbar = O.kv_summary_build(shp, sub["K"], sub["V"])  # cache state, not timed
     md = O.SUMMARY if w.score_mode == "summary" else O.EXACT_MASS
@@ -230,7 +323,7 @@ def cpu_baseline(w, data, budget_s):
                              sub.get("tok_idx"), sub.get("tok_logw"))
         reps += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or reps >= 10000:
+        if el >= budget_s or reps >= 100000:
             break
     cores = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
     model = ""

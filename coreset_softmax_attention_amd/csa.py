@@ -19,7 +19,7 @@ CSA_F32, CSA_BF16 = 0, 1
 CSA_SCORE_SUMMARY, CSA_SCORE_EXACT_MASS = 0, 1
 CSA_PROXY_NONE, CSA_PROXY_COMPLEMENT = 0, 1
 CSA_WS_BLOCK_SCORE_SUMMARY, CSA_WS_BLOCK_SCORE_EXACT_MASS = 0, 1
-CSA_WS_SPARSE_DECODE_ATTN, CSA_WS_DENSE_DECODE_ATTN = 2, 3
+CSA_WS_SPARSE_DECODE_ATTN, CSA_WS_DENSE_DECODE_ATTN, CSA_WS_SELECTIVE_DECODE_STEP = 2, 3, 4
 
 MODES = {"summary": CSA_SCORE_SUMMARY, "exact_mass": CSA_SCORE_EXACT_MASS}
 
@@ -57,6 +57,8 @@ _SIGS = {
     "sparse_decode_attn": [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _I32, _P, _P, _I32, ctypes.c_int,
                            _P, _P, _P, _SZ, _P],
     "dense_decode_attn": [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _SZ, _P],
+    "selective_decode_step": [ctypes.POINTER(Shape), ctypes.c_int, _P, _P, _P, _P, _P, _I32, _P, _P, _I32,
+                              ctypes.c_int, _P, _P, _P, _P, _P, _SZ, _P],
 }
 
 
@@ -220,6 +222,31 @@ def dense_decode_attn(q, K, V, scale: float = 0.0, out=None, lse=None, ws=None):
     _check(lib().dense_decode_attn(ctypes.byref(shape), _ptr(q), _ptr(K), _ptr(V), _ptr(out), _ptr(lse), _ptr(ws),
                                    wsb, _stream(dev)), "dense_decode_attn")
     return out, lse
+
+
+def selective_decode_step(q, K, V, Kbar, Vbar, k: int, block_size: int, mode: str = "summary",
+                          proxies: bool = True, tok_idx=None, tok_logw=None, scale: float = 0.0, scores=None,
+                          sel=None, out=None, lse=None, ws=None, want_scores: bool = False, want_sel: bool = False):
+    """block_score -> topk_select -> sparse_decode_attn in one call (one kernel where the shape
+    allows).  Returns (out, lse, scores or None, sel or None)."""
+    dev = _dev(q, K, V, Kbar, Vbar, tok_idx, tok_logw)
+    shape = make_shape(q, K, block_size, scale)
+    m = tok_idx.shape[-1] if tok_idx is not None else 0
+    B, Hq, d = q.shape
+    Hkv, nb = K.shape[1], shape.n_blocks
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev) if out is None else out
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if lse is None else lse
+    if want_scores and scores is None:
+        scores = torch.empty((B, Hkv, nb), dtype=torch.float32, device=dev)
+    if want_sel and sel is None:
+        sel = torch.empty((B, Hkv, min(k, nb)), dtype=torch.int32, device=dev)
+    ws, wsb = _workspace(shape, CSA_WS_SELECTIVE_DECODE_STEP, k, m, ws, dev)
+    _check(lib().selective_decode_step(ctypes.byref(shape), MODES[mode], _ptr(q), _ptr(K), _ptr(V), _ptr(Kbar),
+                                       _ptr(Vbar), k, _ptr(tok_idx), _ptr(tok_logw), m,
+                                       CSA_PROXY_COMPLEMENT if proxies else CSA_PROXY_NONE, _ptr(scores),
+                                       _ptr(sel), _ptr(out), _ptr(lse), _ptr(ws), wsb, _stream(dev)),
+           "selective_decode_step")
+    return out, lse, scores, sel
 
 
 def to_device(a, device="cuda"):

@@ -83,9 +83,33 @@ size_t block_score_ws(const csa::Dims& d)
 
 int attn_rows_ok(const csa::Dims& d, long long k, long long m, int proxies, int dense)
 {
+    const long long head_bytes = (long long)d.n * d.d * (d.dtype == csa::DT_F32 ? 4 : 2);
+    if (head_bytes >= (1ll << 32))
+        return fail(CSA_ERR_UNSUPPORTED, "one KV head's cache is %lld bytes (must be below 4 GiB)", head_bytes);
     const long long rows = (dense ? (long long)d.n : k * d.L) + m + (proxies ? d.nb : 0);
     if (rows >= kMaxRows) return fail(CSA_ERR_UNSUPPORTED, "virtual-token list of %lld rows above 2^31", rows);
     return CSA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace layout of the unfused decode step: scores | sel | block_score ws | attention ws.
+struct StepWs {
+    size_t scores, sel, score_ws, attn_ws, total;
+};
+
+StepWs step_ws(const csa::Dims& d, int k, int m)
+{
+    StepWs w{};
+    const int kk = k < d.nb ? k : d.nb;
+    w.scores = align256((size_t)d.pairs() * d.nb * sizeof(float));
+    w.sel = align256((size_t)d.pairs() * (kk > 0 ? kk : 1) * sizeof(int32_t));
+    w.score_ws = align256(block_score_ws(d));
+    const size_t a = csa::plan_attention(d, kk, m, 1, 0).ws_bytes;
+    const size_t b = (kk > 0 || m > 0) ? csa::plan_attention(d, kk, m, 0, 0).ws_bytes : 0;
+    w.attn_ws = align256(a > b ? a : b);
+    w.total = w.scores + w.sel + w.score_ws + w.attn_ws;
+    return w;
 }
 
 }  // namespace
@@ -114,6 +138,10 @@ int block_score(const csa_shape* shape, csa_score_mode mode, const void* q, cons
     if (!aligned16(q) || !aligned16(keys) || !aligned4(scores))
         return fail(CSA_ERR_INVALID_ARG, "block_score: misaligned tensor");
     if (int rc = check_ws(block_score_ws(d), ws, ws_bytes)) return rc;
+    if (mode == CSA_SCORE_SUMMARY && csa::fused_summary_score_ok(d)) {
+        const hipError_t e = csa::launch_score_summary_fused(d, q, keys, scores, stream);
+        return e == hipSuccess ? CSA_OK : hip_fail(e, "block_score");
+    }
     float* dst = d.G == 1 ? scores : static_cast<float*>(ws);
     hipError_t e = mode == CSA_SCORE_SUMMARY ? csa::launch_block_logits_summary(d, q, keys, dst, stream)
                                              : csa::launch_block_logits_exact(d, q, keys, dst, stream);
@@ -183,6 +211,55 @@ int dense_decode_attn(const csa_shape* shape, const void* q, const void* K, cons
     return e == hipSuccess ? CSA_OK : hip_fail(e, "dense_decode_attn");
 }
 
+int selective_decode_step(const csa_shape* shape, csa_score_mode mode, const void* q, const void* K, const void* V,
+                          const void* Kbar, const void* Vbar, int32_t k, const int32_t* tok_idx,
+                          const float* tok_logw, int32_t m, csa_proxy_mode proxy_mode, float* scores, int32_t* sel,
+                          float* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    csa::Dims d;
+    if (int rc = make_dims(shape, &d)) return rc;
+    if (mode != CSA_SCORE_SUMMARY && mode != CSA_SCORE_EXACT_MASS)
+        return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: unknown mode %d", (int)mode);
+    if (proxy_mode != CSA_PROXY_NONE && proxy_mode != CSA_PROXY_COMPLEMENT)
+        return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: unknown proxy mode %d", (int)proxy_mode);
+    const int proxies = proxy_mode == CSA_PROXY_COMPLEMENT;
+    if (k < 0 || m < 0) return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: k=%d m=%d", k, m);
+    const int kk = k < d.nb ? k : d.nb;
+    if (kk == 0 && m == 0 && !proxies)
+        return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: empty virtual-token set (k = 0, m = 0, no proxies)");
+    if (!q || !K || !V || !out) return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: NULL tensor pointer");
+    if ((mode == CSA_SCORE_SUMMARY || proxies) && !Kbar)
+        return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: Kbar is NULL");
+    if (proxies && !Vbar) return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: proxies need Vbar");
+    if (m > 0 && (!tok_idx || !tok_logw))
+        return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: weighted tokens missing with m=%d", m);
+    if (!aligned16(q) || !aligned16(K) || !aligned16(V) || (Kbar && !aligned16(Kbar)) || (Vbar && !aligned16(Vbar)) ||
+        !aligned4(out) || (lse && !aligned4(lse)) || (scores && !aligned4(scores)) || (sel && !aligned4(sel)) ||
+        (tok_idx && !aligned4(tok_idx)) || (tok_logw && !aligned4(tok_logw)))
+        return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: misaligned pointer");
+    if (int rc = attn_rows_ok(d, kk, m, proxies, 0)) return rc;
+
+    if (mode == CSA_SCORE_SUMMARY && csa::fused_step_ok(d, kk, m, proxies)) {
+        csa::StepInputs in{q, K, V, Kbar, Vbar, kk, tok_idx, tok_logw, m, proxies, scores, sel, out, lse};
+        const hipError_t e = csa::launch_decode_step(d, in, stream);
+        return e == hipSuccess ? CSA_OK : hip_fail(e, "selective_decode_step");
+    }
+    // the three kernels in turn; scores and selection go to the caller's arrays
+    // when given, else to the workspace
+    const StepWs w = step_ws(d, kk, m);
+    if (int rc = check_ws(w.total, ws, ws_bytes)) return rc;
+    char* base = static_cast<char*>(ws);
+    float* sc = scores ? scores : reinterpret_cast<float*>(base);
+    int32_t* sl = sel ? sel : reinterpret_cast<int32_t*>(base + w.scores);
+    void* sws = base + w.scores + w.sel;
+    void* aws = base + w.scores + w.sel + w.score_ws;
+    if (int rc = block_score(shape, mode, q, mode == CSA_SCORE_SUMMARY ? Kbar : K, sc, sws, w.score_ws, stream))
+        return rc;
+    if (int rc = topk_select(d.pairs(), d.nb, kk, sc, sl, stream)) return rc;
+    return sparse_decode_attn(shape, q, K, V, Kbar, Vbar, kk > 0 ? sl : nullptr, kk, tok_idx, tok_logw, m,
+                              proxy_mode, out, lse, aws, w.attn_ws, stream);
+}
+
 size_t csa_workspace_size(const csa_shape* shape, csa_entry entry, int32_t k, int32_t m)
 {
     csa::Dims d;
@@ -204,6 +281,15 @@ size_t csa_workspace_size(const csa_shape* shape, csa_entry entry, int32_t k, in
     case CSA_WS_DENSE_DECODE_ATTN:
         if (attn_rows_ok(d, 0, 0, 0, 1) != CSA_OK) return 0;
         return csa::plan_attention(d, 0, 0, 0, 1).ws_bytes;
+    case CSA_WS_SELECTIVE_DECODE_STEP: {
+        if (k < 0 || m < 0) {
+            fail(CSA_ERR_INVALID_ARG, "csa_workspace_size: k=%d or m=%d out of range", k, m);
+            return 0;
+        }
+        const int kk = k < d.nb ? k : d.nb;
+        if (attn_rows_ok(d, kk, m, 1, 0) != CSA_OK) return 0;
+        return step_ws(d, kk, m).total;
+    }
     }
     fail(CSA_ERR_INVALID_ARG, "csa_workspace_size: unknown entry %d", (int)entry);
     return 0;

@@ -1,27 +1,38 @@
 // attn.hip -- one online-softmax pass over the virtual tokens of a KV head.
 //
 // The virtual-token list of KV head (b, j) is the concatenation of
-//   [exact]    every token of the selected blocks, log-weight 0
-//              (dense mode: all n tokens in order);
-//   [weighted] m gathered tokens with their log-weights (weighted-coreset
-//              attention, "WildCat: Near-Linear Attention in Theory and
-//              Practice", Abstract);
 //   [proxy]    one row per block of the summary arrays, key Kbar_b, value
 //              Vbar_b, log-weight ln c_b; the rows of selected blocks are
 //              masked.  This is the count-aware proxy of "OpenAttention reads
 //              1% of the KV cache -- Count-aware tail proxy", section
-//              "Skipping reviews without losing the verdict".
+//              "Skipping reviews without losing the verdict";
+//   [weighted] m gathered tokens with their log-weights (weighted-coreset
+//              attention, "WildCat: Near-Linear Attention in Theory and
+//              Practice", Abstract);
+//   [exact]    every token of the selected blocks, log-weight 0
+//              (dense mode: all n tokens in order).
+// Proxy rows come first because their addresses do not depend on the
+// selection: their loads start while the selection is still being read.
 // Reading all summary rows contiguously and masking the few selected ones
 // costs k extra rows but keeps the proxy reads fully coalesced.
 //
 // Work split: a workgroup owns a contiguous range of virtual rows of one KV
-// head for up to 8 query heads of its group (split-K).  Each wave walks tiles
-// of U row-loads; a row's 16-byte chunks sit in LPR consecutive lanes, so one
-// wave-wide load moves 64/LPR whole rows.  Logits use the base-2 exponent:
-// x = log2(e) (scale q.k + logw).  Each lane group keeps an online-softmax
-// state (running max, sum, accumulator of its chunk of d); states are merged
-// across lane groups (shuffles), waves (LDS) and splits (merge kernel), always
-// in a fixed order, so results are bitwise reproducible.
+// head for up to 8 query heads of its group (split-K).  Logits use the base-2
+// exponent: x = log2(e) (scale q.k + logw).  Partial softmax states (running
+// max, sum, unnormalised output) are merged across lanes (shuffles), waves
+// (LDS) and splits (merge kernel), always in a fixed order, so results are
+// bitwise reproducible.
+//
+// bfloat16 path (attn_mfma_kernel): each wave takes tiles of 32 virtual rows.
+// The rows of a tile are resolved once (index, source array, log-weight) into
+// a per-wave LDS table.  q K^T for the tile is two 16x16x32 bf16 MFMA chains
+// (rows x heads, the group's heads padded to 16 columns); the online softmax
+// runs once per (row, head) on the MFMA output lanes; the probabilities go
+// through LDS to the lanes that hold the tile's value rows (16-byte chunks,
+// whole rows per lane group, coalesced), which accumulate P V in fp32.
+// binary32 path (attn_valu_kernel): rows as 16-byte chunks over LPR lanes,
+// dot products reduced with DPP, one online-softmax state per lane group.
+#include "attn_engine.hpp"
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -30,7 +41,21 @@ namespace {
 
 constexpr int kNW = 4;                // waves per workgroup
 constexpr int kMaxSplitRows = 8192;   // rows per workgroup (bitmap capacity)
+constexpr int kMaxSelLds = 512;       // selections kept in LDS by the bfloat16 kernel
+constexpr int kMaxTokLds = 1024;      // weighted tokens of a workgroup kept in LDS
 constexpr int kTargetWorkgroups = 2048;
+#ifndef CSA_MFMA_WAVES
+#define CSA_MFMA_WAVES 8
+#endif
+#ifndef CSA_MFMA_MIN_WGS
+#define CSA_MFMA_MIN_WGS 256
+#endif
+#ifndef CSA_MFMA_TILES_PER_WAVE
+#define CSA_MFMA_TILES_PER_WAVE 16
+#endif
+constexpr int kMfmaWaves = CSA_MFMA_WAVES;          // waves per workgroup, bfloat16 path
+constexpr int kMfmaMinWgs = CSA_MFMA_MIN_WGS;       // workgroups to cover every CU once
+constexpr int kMfmaTilesPerWave = CSA_MFMA_TILES_PER_WAVE;  // tiles a wave streams before splitting
 
 constexpr int unroll_for(int hg) { return hg <= 4 ? 8 : 4; }
 
@@ -49,12 +74,13 @@ struct AttnParams {
     int k, m, proxies, dense;
     int Hq, Hkv, G, n, L, nb;
     int rows, exact_rows, splits, rows_per_split;
+    int pend, wbeg, ebeg;      // end of the proxy rows, first weighted row, first exact row
     float scale_log2;          // scale * log2(e)
     float log2_L, log2_last;   // log2 c_b of a full and of the last block
 };
 
 template <int DT, int D, int HG, int U>
-__global__ void __launch_bounds__(kNW * 64) attn_kernel(const AttnParams p)
+__global__ void __launch_bounds__(kNW * 64) attn_valu_kernel(const AttnParams p)
 {
     using Gm = RowGeom<DT, D>;
     constexpr int LPR = Gm::lpr, RPW = Gm::rpw, EPL = Gm::epl, RB = Gm::row_bytes;
@@ -74,11 +100,10 @@ __global__ void __launch_bounds__(kNW * 64) attn_kernel(const AttnParams p)
 
     const int r0 = split * p.rows_per_split;
     const int r1 = min(p.rows, r0 + p.rows_per_split);
-    const int pbeg = p.exact_rows + p.m;   // first proxy row
 
     // Bitmap of selected blocks among the proxy rows [pb_lo, pb_hi) of this range.
-    const int pb_lo = max(r0 - pbeg, 0);
-    const int pb_hi = p.proxies ? min(r1 - pbeg, p.nb) : 0;
+    const int pb_lo = r0;
+    const int pb_hi = min(r1, p.pend);
     if (pb_hi > pb_lo) {
         const int words = (pb_hi - pb_lo + 31) >> 5;
         for (int w = threadIdx.x; w < words; w += kNW * 64) sel_bits[w] = 0;
@@ -128,29 +153,30 @@ __global__ void __launch_bounds__(kNW * 64) attn_kernel(const AttnParams p)
             const char* vb = p.V;
             size_t row = kv_pair;
             float w = 0.0f;
-            if (r < p.exact_rows) {
-                int tok;
-                if (p.dense) {
-                    tok = r;
-                } else {
-                    const int slot = r / p.L;
-                    tok = p.sel[(size_t)pair * p.k + slot] * p.L + (r - slot * p.L);
-                }
-                valid = valid && tok >= 0 && tok < p.n;
-                row = kv_pair + (valid ? tok : 0);
-            } else if (r < pbeg) {
-                const int t = r - p.exact_rows;
-                const int tok = p.tok_idx[(size_t)pair * p.m + t];
-                valid = valid && tok >= 0 && tok < p.n;
-                row = kv_pair + (valid ? tok : 0);
-                w = p.tok_logw[(size_t)pair * p.m + t] * kLog2e;
-            } else if (r < p.rows) {
-                const int blk = r - pbeg;
+            if (r < p.pend) {
+                const int blk = r;
                 kb = p.Kbar;
                 vb = p.Vbar;
                 row = sm_pair + blk;
                 w = blk == p.nb - 1 ? p.log2_last : p.log2_L;
                 if (valid) valid = !((sel_bits[(blk - pb_lo) >> 5] >> ((blk - pb_lo) & 31)) & 1u);
+            } else if (r >= p.wbeg && r < p.wbeg + p.m) {
+                const int t = r - p.wbeg;
+                const int tok = p.tok_idx[(size_t)pair * p.m + t];
+                valid = valid && tok >= 0 && tok < p.n;
+                row = kv_pair + (valid ? tok : 0);
+                w = p.tok_logw[(size_t)pair * p.m + t] * kLog2e;
+            } else if (r >= p.ebeg && r < p.rows) {
+                const int e = r - p.ebeg;
+                int tok;
+                if (p.dense) {
+                    tok = e;
+                } else {
+                    const int slot = e / p.L;
+                    tok = p.sel[(size_t)pair * p.k + slot] * p.L + (e - slot * p.L);
+                }
+                valid = valid && tok >= 0 && tok < p.n;
+                row = kv_pair + (valid ? tok : 0);
             } else {
                 valid = false;
             }
@@ -263,6 +289,192 @@ __global__ void __launch_bounds__(kNW * 64) attn_kernel(const AttnParams p)
     }
 }
 
+// ---------------------------------------------------------------------------
+// bfloat16 path: q K^T on the matrix cores
+// ---------------------------------------------------------------------------
+
+
+
+
+// Where resolve_row finds the selection and the weighted tokens: the
+// workgroup's copies in LDS once they are filled, the global arrays before.
+struct RowSources {
+    const int32_t* sel;      // selection of this KV head (k entries)
+    const int32_t* tok_idx;  // weighted tokens, indexed from tok_base
+    const float* tok_logw;
+    int tok_base;            // index of tok_idx[0] in the KV head's list
+};
+
+// Virtual row r of KV head `pair` -> (row index in its source array, log2-
+// weight); -inf marks a row outside [.., r1), a padding row, a token outside
+// the cache, or (when `mask`) a proxy of a selected block.  Invalid rows keep
+// row 0, a valid address.
+__device__ __forceinline__ void resolve_row(const AttnParams& p, const RowSources& src, int r, int r1, int pb_lo,
+                                            const uint32_t* sel_bits, bool mask, uint32_t& row, float& lw)
+{
+    row = 0;
+    lw = kNegInf;
+    if (r >= r1) return;
+    if (r < p.pend) {
+        row = (uint32_t)r;
+        if (!mask || !((sel_bits[(r - pb_lo) >> 5] >> ((r - pb_lo) & 31)) & 1u))
+            lw = r == p.nb - 1 ? p.log2_last : p.log2_L;
+    } else if (r >= p.wbeg && r < p.wbeg + p.m) {
+        const int t = r - p.wbeg - src.tok_base;
+        const int tok = src.tok_idx[t];
+        if (tok >= 0 && tok < p.n) {
+            row = (uint32_t)tok;
+            lw = src.tok_logw[t] * kLog2e;
+        }
+    } else if (r >= p.ebeg) {
+        const int e = r - p.ebeg;
+        int tok;
+        if (p.dense) {
+            tok = e;
+        } else {
+            const int slot = e / p.L;
+            tok = src.sel[slot] * p.L + (e - slot * p.L);
+        }
+        if (tok >= 0 && tok < p.n) {
+            row = (uint32_t)tok;
+            lw = 0.0f;
+        }
+    }
+}
+
+template <int D, int HG, int NW>
+__global__ void __launch_bounds__(NW * 64) attn_mfma_kernel(const AttnParams p)
+{
+    using E = MfmaEngine<D, HG, NW>;
+    constexpr int TR = kTileRows, RB = E::RB;
+    __shared__ uint32_t sel_bits[kMaxSplitRows / 32];
+    __shared__ int32_t sel_sm[kMaxSelLds];
+    __shared__ int32_t tok_sm[kMaxTokLds];
+    __shared__ float logw_sm[kMaxTokLds];
+    __shared__ typename E::Smem sm;
+
+    const int pair = blockIdx.x / p.splits, split = blockIdx.x - pair * p.splits;
+    const int b = pair / p.Hkv, j = pair - b * p.Hkv;
+    const int g0 = blockIdx.y * HG;
+    const int nh = min(HG, p.G - g0);
+    const int h0 = j * p.G + g0;
+    const int r0 = split * p.rows_per_split;
+    const int r1 = min(p.rows, r0 + p.rows_per_split);
+    // selected-block bitmap over the proxy rows [pb_lo, pb_hi) of this range; it is
+    // filled after the first tile's loads are in flight
+    const int pb_lo = r0;
+    const int pb_hi = min(r1, p.pend);
+    const int bitmap_words = pb_hi > pb_lo ? (pb_hi - pb_lo + 31) >> 5 : 0;
+    for (int w = threadIdx.x; w < bitmap_words; w += NW * 64) sel_bits[w] = 0;
+
+    E eng(sm, p.q + (size_t)(b * p.Hq + h0) * RB, nh);
+    const int lane = eng.lane, wave = eng.wave;
+
+    // Segments are padded to whole tiles, so every tile reads either the cache
+    // (weighted and exact rows) or the summaries (proxy rows).
+    const __amdgpu_buffer_rsrc_t Kc = buffer_rsrc(p.K + (size_t)pair * p.n * RB, (uint32_t)p.n * RB);
+    const __amdgpu_buffer_rsrc_t Vc = buffer_rsrc(p.V + (size_t)pair * p.n * RB, (uint32_t)p.n * RB);
+    const __amdgpu_buffer_rsrc_t Ks =
+        buffer_rsrc(p.proxies ? p.Kbar + (size_t)pair * p.nb * RB : p.K, p.proxies ? (uint32_t)p.nb * RB : 0u);
+    const __amdgpu_buffer_rsrc_t Vs =
+        buffer_rsrc(p.proxies ? p.Vbar + (size_t)pair * p.nb * RB : p.V, p.proxies ? (uint32_t)p.nb * RB : 0u);
+
+    // The selection and this workgroup's weighted tokens are copied to LDS
+    // (when they fit) after the first tile is issued; until then, and when
+    // they do not fit, rows are resolved from the global arrays.
+    const int w_lo = max(r0, p.wbeg), w_hi = min(r1, p.wbeg + p.m);  // weighted rows of this range
+    const bool sel_in_lds = !p.dense && p.k > 0 && p.k <= kMaxSelLds;
+    const bool tok_in_lds = w_hi > w_lo && w_hi - w_lo <= kMaxTokLds;
+    RowSources src{p.sel + (size_t)pair * p.k, p.tok_idx + (size_t)pair * p.m, p.tok_logw + (size_t)pair * p.m, 0};
+
+    auto issue = [&](int base, typename E::Tile& t, int tb, bool masked) {
+        if (lane < TR) {
+            uint32_t row;
+            float lw;
+            resolve_row(p, src, base + lane, r1, pb_lo, sel_bits, masked, row, lw);
+            eng.set_row(tb, lane, row, lw);
+        }
+        const bool summ = base < p.wbeg;  // uniform over the wave
+        eng.issue(t, tb, summ ? Ks : Kc, summ ? Vs : Vc, true);
+    };
+    auto compute = [&](const typename E::Tile& t, int tb) {
+        float x[8];
+        eng.logits_mfma(t, tb, p.scale_log2, x);
+        eng.softmax(x);
+    };
+
+    // Two tiles form the software pipeline: tile t's q K^T and softmax run before
+    // tile t+1's loads are issued (so t's key registers are free again), and t's
+    // P V runs while t+1 is in flight.
+    // Tile order: this range's proxy tiles, then its cache tiles, each list
+    // rotated by a per-workgroup offset, so that workgroups running side by
+    // side do not walk the same address offsets at the same time (their heads'
+    // arrays start at similarly aligned addresses and would all hit the same
+    // HBM channels).
+    const int pe = min(r1, p.wbeg), c0 = max(r0, p.wbeg);
+    const int nP = pe > r0 ? (pe - r0 + TR - 1) / TR : 0;
+    const int nC = r1 > c0 ? (r1 - c0 + TR - 1) / TR : 0;
+    const int nT = nP + nC;
+    const uint32_t hsh = (uint32_t)blockIdx.x * 0x9E3779B1u;
+    const int rotP = nP ? (int)((hsh >> 8) % (uint32_t)nP) : 0;
+    const int rotC = nC ? (int)((hsh >> 16) % (uint32_t)nC) : 0;
+    auto row0 = [&](int t) { return t < nP ? r0 + (t + rotP) % nP * TR : c0 + (t - nP + rotC) % nC * TR; };
+
+    // Two tiles form the software pipeline: tile t's q K^T and softmax run before
+    // tile t+1's loads are issued (so t's key registers are free again), and t's
+    // P V runs while t+1 is in flight.
+    typename E::Tile A, B;
+    int t = wave;
+    const int first = t < nT ? row0(t) : r1;
+    if (t < nT) issue(first, A, 0, false);
+    if (bitmap_words > 0 || sel_in_lds || tok_in_lds) {
+        __syncthreads();  // bitmap cleared
+        if (bitmap_words > 0 || sel_in_lds) {
+            const int32_t* S = p.sel + (size_t)pair * p.k;
+            for (int i = threadIdx.x; i < p.k; i += NW * 64) {
+                const int blk = S[i];
+                if (sel_in_lds) sel_sm[i] = blk;
+                if (blk >= pb_lo && blk < pb_hi) atomicOr(&sel_bits[(blk - pb_lo) >> 5], 1u << ((blk - pb_lo) & 31));
+            }
+        }
+        if (tok_in_lds) {
+            for (int i = threadIdx.x; i < w_hi - w_lo; i += NW * 64) {
+                tok_sm[i] = src.tok_idx[w_lo - p.wbeg + i];
+                logw_sm[i] = src.tok_logw[w_lo - p.wbeg + i];
+            }
+        }
+        __syncthreads();  // bitmap and copies complete
+        if (sel_in_lds) src.sel = sel_sm;
+        if (tok_in_lds) {
+            src.tok_idx = tok_sm;
+            src.tok_logw = logw_sm;
+            src.tok_base = w_lo - p.wbeg;
+        }
+        // mask the selected blocks among the first tile's proxy rows
+        const int r = first + lane;
+        if (bitmap_words > 0 && lane < TR && r < pb_hi && ((sel_bits[(r - pb_lo) >> 5] >> ((r - pb_lo) & 31)) & 1u))
+            sm.tab_lw[0][wave][lane] = kNegInf;
+        wave_lds_fence();
+    }
+    if (t < nT) {
+        for (;;) {
+            const int t1 = t + NW;
+            compute(A, 0);
+            if (t1 < nT) issue(row0(t1), B, 1, true);
+            eng.accumulate(A);
+            if (t1 >= nT) break;
+            const int t2 = t1 + NW;
+            compute(B, 1);
+            if (t2 < nT) issue(row0(t2), A, 0, true);
+            eng.accumulate(B);
+            if (t2 >= nT) break;
+            t = t2;
+        }
+    }
+    float* part = p.splits == 1 ? nullptr : p.part + (((size_t)pair * p.splits + split) * p.G + g0) * (D + 2);
+    eng.finish(nh, p.out + ((size_t)b * p.Hq + h0) * D, p.lse ? p.lse + (size_t)b * p.Hq + h0 : nullptr, part);
+}
+
 // Merge the per-split states of a KV head in split order.
 template <int D>
 __global__ void __launch_bounds__(256) attn_merge_kernel(const float* part, int splits, int G, int Hq, int Hkv,
@@ -288,27 +500,57 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(const float* part, int 
     }
 }
 
-template <int DT, int D>
-hipError_t launch_dtd(const AttnParams& p, int hg, int pairs, int hchunks, hipStream_t st)
+hipError_t launch_merge(const AttnParams& p, int D, int pairs, hipStream_t st)
+{
+    if (D == 128)
+        attn_merge_kernel<128><<<dim3((unsigned)pairs), dim3(256), 0, st>>>(p.part, p.splits, p.G, p.Hq, p.Hkv,
+                                                                            p.out, p.lse);
+    else
+        attn_merge_kernel<64><<<dim3((unsigned)pairs), dim3(256), 0, st>>>(p.part, p.splits, p.G, p.Hq, p.Hkv,
+                                                                           p.out, p.lse);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_f32(const AttnParams& p, int hg, int pairs, int hchunks, hipStream_t st)
 {
     const dim3 grid((unsigned)(pairs * p.splits), (unsigned)hchunks, 1);
     const dim3 block(kNW * 64);
     switch (hg) {
-    case 1: attn_kernel<DT, D, 1, unroll_for(1)><<<grid, block, 0, st>>>(p); break;
-    case 2: attn_kernel<DT, D, 2, unroll_for(2)><<<grid, block, 0, st>>>(p); break;
-    case 3: attn_kernel<DT, D, 3, unroll_for(3)><<<grid, block, 0, st>>>(p); break;
-    case 4: attn_kernel<DT, D, 4, unroll_for(4)><<<grid, block, 0, st>>>(p); break;
-    case 5: attn_kernel<DT, D, 5, unroll_for(5)><<<grid, block, 0, st>>>(p); break;
-    case 6: attn_kernel<DT, D, 6, unroll_for(6)><<<grid, block, 0, st>>>(p); break;
-    case 7: attn_kernel<DT, D, 7, unroll_for(7)><<<grid, block, 0, st>>>(p); break;
-    case 8: attn_kernel<DT, D, 8, unroll_for(8)><<<grid, block, 0, st>>>(p); break;
+    case 1: attn_valu_kernel<DT_F32, D, 1, unroll_for(1)><<<grid, block, 0, st>>>(p); break;
+    case 2: attn_valu_kernel<DT_F32, D, 2, unroll_for(2)><<<grid, block, 0, st>>>(p); break;
+    case 3: attn_valu_kernel<DT_F32, D, 3, unroll_for(3)><<<grid, block, 0, st>>>(p); break;
+    case 4: attn_valu_kernel<DT_F32, D, 4, unroll_for(4)><<<grid, block, 0, st>>>(p); break;
+    case 5: attn_valu_kernel<DT_F32, D, 5, unroll_for(5)><<<grid, block, 0, st>>>(p); break;
+    case 6: attn_valu_kernel<DT_F32, D, 6, unroll_for(6)><<<grid, block, 0, st>>>(p); break;
+    case 7: attn_valu_kernel<DT_F32, D, 7, unroll_for(7)><<<grid, block, 0, st>>>(p); break;
+    case 8: attn_valu_kernel<DT_F32, D, 8, unroll_for(8)><<<grid, block, 0, st>>>(p); break;
     default: return hipErrorInvalidValue;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
-    attn_merge_kernel<D><<<dim3((unsigned)pairs), dim3(256), 0, st>>>(p.part, p.splits, p.G, p.Hq, p.Hkv,
-                                                                      p.out, p.lse);
-    return hipGetLastError();
+    return launch_merge(p, D, pairs, st);
+}
+
+template <int D>
+hipError_t launch_bf16(const AttnParams& p, int hg, int pairs, int hchunks, hipStream_t st)
+{
+    const dim3 grid((unsigned)(pairs * p.splits), (unsigned)hchunks, 1);
+    const dim3 block(kMfmaWaves * 64);
+    switch (hg) {
+    case 1: attn_mfma_kernel<D, 1, kMfmaWaves><<<grid, block, 0, st>>>(p); break;
+    case 2: attn_mfma_kernel<D, 2, kMfmaWaves><<<grid, block, 0, st>>>(p); break;
+    case 3: attn_mfma_kernel<D, 3, kMfmaWaves><<<grid, block, 0, st>>>(p); break;
+    case 4: attn_mfma_kernel<D, 4, kMfmaWaves><<<grid, block, 0, st>>>(p); break;
+    case 5: attn_mfma_kernel<D, 5, kMfmaWaves><<<grid, block, 0, st>>>(p); break;
+    case 6: attn_mfma_kernel<D, 6, kMfmaWaves><<<grid, block, 0, st>>>(p); break;
+    case 7: attn_mfma_kernel<D, 7, kMfmaWaves><<<grid, block, 0, st>>>(p); break;
+    case 8: attn_mfma_kernel<D, 8, kMfmaWaves><<<grid, block, 0, st>>>(p); break;
+    default: return hipErrorInvalidValue;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.splits == 1) return e;
+    return launch_merge(p, D, pairs, st);
 }
 
 }  // namespace
@@ -317,7 +559,17 @@ AttnPlan plan_attention(const Dims& s, int k, int m, int proxies, int dense)
 {
     AttnPlan pl{};
     pl.exact_rows = dense ? s.n : k * s.L;
-    pl.rows = pl.exact_rows + m + (proxies ? s.nb : 0);
+    pl.pend = proxies ? s.nb : 0;
+    if (s.dtype == DT_BF16) {  // tiles never straddle two segments
+        const int pad = kTileRows;
+        pl.wbeg = (pl.pend + pad - 1) / pad * pad;
+        pl.ebeg = pl.wbeg + (m + pad - 1) / pad * pad;
+    } else {
+        pl.wbeg = pl.pend;
+        pl.ebeg = pl.pend + m;
+    }
+    pl.rows = pl.ebeg + pl.exact_rows;
+    if (pl.exact_rows == 0) pl.rows = m > 0 ? pl.wbeg + m : pl.pend;
     pl.hg = s.G <= 8 ? s.G : 8;
     pl.hchunks = (s.G + pl.hg - 1) / pl.hg;
     if (pl.rows <= 0) {  // empty virtual-token set: nothing to plan (callers reject it)
@@ -326,12 +578,23 @@ AttnPlan plan_attention(const Dims& s, int k, int m, int proxies, int dense)
         pl.ws_bytes = 0;
         return pl;
     }
-    const int elem = s.dtype == DT_F32 ? 4 : 2;
-    const int rpw = 64 / (s.d * elem / 16);
-    const int tile = rpw * unroll_for(pl.hg);
     const int items = s.pairs() * pl.hchunks;
-    const int max_splits = (pl.rows + tile - 1) / tile;
-    int splits = (kTargetWorkgroups + items - 1) / items;
+    int tile, splits, max_splits;
+    if (s.dtype == DT_F32) {
+        tile = 64 / (s.d * 4 / 16) * unroll_for(pl.hg);  // rows per wave iteration
+        max_splits = (pl.rows + tile - 1) / tile;
+        splits = (kTargetWorkgroups + items - 1) / items;
+    } else {
+        // one workgroup per (KV head, head chunk) unless that leaves CUs idle or a
+        // wave would stream more than kMfmaTilesPerWave tiles; never less than a
+        // tile per wave
+        tile = kTileRows;
+        const int tiles = (pl.rows + tile - 1) / tile;
+        max_splits = (tiles + kMfmaWaves - 1) / kMfmaWaves;
+        const int for_cus = (kMfmaMinWgs + items - 1) / items;
+        const int for_len = (tiles + kMfmaWaves * kMfmaTilesPerWave - 1) / (kMfmaWaves * kMfmaTilesPerWave);
+        splits = for_cus > for_len ? for_cus : for_len;
+    }
     splits = splits < 1 ? 1 : (splits > max_splits ? max_splits : splits);
     int per = (pl.rows + splits - 1) / splits;
     per = (per + tile - 1) / tile * tile;
@@ -369,6 +632,9 @@ hipError_t launch_attention(const Dims& s, const AttnPlan& pl, const AttnInputs&
     p.nb = s.nb;
     p.rows = pl.rows;
     p.exact_rows = pl.exact_rows;
+    p.pend = pl.pend;
+    p.wbeg = pl.wbeg;
+    p.ebeg = pl.ebeg;
     p.splits = pl.splits;
     p.rows_per_split = pl.rows_per_split;
     p.scale_log2 = s.scale * kLog2e;
@@ -376,11 +642,11 @@ hipError_t launch_attention(const Dims& s, const AttnPlan& pl, const AttnInputs&
     p.log2_last = s.ln_last * kLog2e;
     const int pairs = s.pairs();
     if (s.dtype == DT_BF16) {
-        if (s.d == 128) return launch_dtd<DT_BF16, 128>(p, pl.hg, pairs, pl.hchunks, st);
-        if (s.d == 64) return launch_dtd<DT_BF16, 64>(p, pl.hg, pairs, pl.hchunks, st);
+        if (s.d == 128) return launch_bf16<128>(p, pl.hg, pairs, pl.hchunks, st);
+        if (s.d == 64) return launch_bf16<64>(p, pl.hg, pairs, pl.hchunks, st);
     } else {
-        if (s.d == 128) return launch_dtd<DT_F32, 128>(p, pl.hg, pairs, pl.hchunks, st);
-        if (s.d == 64) return launch_dtd<DT_F32, 64>(p, pl.hg, pairs, pl.hchunks, st);
+        if (s.d == 128) return launch_f32<128>(p, pl.hg, pairs, pl.hchunks, st);
+        if (s.d == 64) return launch_f32<64>(p, pl.hg, pairs, pl.hchunks, st);
     }
     return hipErrorInvalidValue;
 }

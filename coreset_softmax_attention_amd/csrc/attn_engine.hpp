@@ -1,0 +1,248 @@
+// attn_engine.hpp -- the per-wave online-softmax engine of the bfloat16
+// attention kernels (sparse_decode_attn, dense_decode_attn and the fused
+// decode step).
+//
+// A wave processes tiles of 32 virtual rows, two in flight at a time.  For each
+// tile:
+//   1. lanes 0..31 resolve the tile's rows into one of two per-wave LDS tables
+//      (row index in its source array, log2-weight; -inf for a row that does not
+//      count);
+//   2. the tile's rows are loaded with buffer loads: key rows in the layout of
+//      the A operand of v_mfma_f32_16x16x32_bf16 (lane (n16, g16): row n16 of a
+//      16-row block, 16-byte chunks 4 s + g16), value rows as whole rows per
+//      lane group (16-byte chunks, coalesced);
+//   3. logits for up to 8 query heads come from two 16x16x32 MFMA chains (rows
+//      x heads, heads padded to 16 columns), or from LDS when the caller has
+//      them already; the online-softmax update runs once per (row, head) on the
+//      MFMA output lanes and the probabilities go through LDS to the value lanes;
+//   4. the value lanes accumulate P V in fp32.
+// All lane groups of a wave share one running maximum per head, so their
+// partial sums add directly; waves are merged through LDS at the end.
+#pragma once
+
+#include "device.hpp"
+
+namespace csa {
+
+constexpr int kTileRows = 32;
+
+template <int D, int HG, int NW>
+struct MfmaEngine {
+    static constexpr int RB = D * 2;            // row bytes
+    static constexpr int KS = D / 32;           // MFMA k-steps per row
+    static constexpr int TR = kTileRows;
+    static constexpr int LPV = RB / 16;         // lanes per value row
+    static constexpr int RPV = 64 / LPV;        // value rows per wave-wide load
+    static constexpr int NVI = TR / RPV;        // value loads per lane per tile
+    static constexpr int HP = HG <= 4 ? 4 : 8;  // padded heads per probability row
+    static_assert(KS * 32 == D && HG <= 8, "unsupported geometry");
+
+    struct Smem {
+        uint32_t tab_row[2][NW][TR];  // two row tables: two tiles are in flight
+        float tab_lw[2][NW][TR] __attribute__((aligned(16)));
+        float p[NW][TR][HP] __attribute__((aligned(16)));
+        float alpha[NW][HP] __attribute__((aligned(16)));
+        float m[NW][HG];
+        float l[NW][HG];
+        float acc[NW][HG][D];
+    };
+
+    // One tile's operands in registers.
+    struct Tile {
+        uint4 ak[2][KS];
+        uint4 vr[NVI];
+    };
+
+    Smem& sm;
+    const int lane, wave, n16, g16, gv, cv;
+    bf16x8_t bq[KS];
+    float m_run, l_part;  // MFMA lanes: head n16
+    float acc[HG][8];     // value lanes: chunk cv of the rows of group gv
+
+    __device__ __forceinline__ MfmaEngine(Smem& s, const char* q_first_head, int nh)
+        : sm(s),
+          lane(threadIdx.x & 63),
+          wave(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)),
+          n16(threadIdx.x & 15),
+          g16((threadIdx.x & 63) >> 4),
+          gv((threadIdx.x & 63) / LPV),
+          cv((threadIdx.x & 63) % LPV),
+          m_run(kNegInf),
+          l_part(0.0f)
+    {
+        load_q_operand<D>(q_first_head, nh, lane, bq);
+#pragma unroll
+        for (int g = 0; g < HG; ++g)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[g][e] = 0.0f;
+    }
+
+    // Row table entry (lanes 0..31 of the wave) of table `tb` (0 or 1).
+    __device__ __forceinline__ void set_row(int tb, int i, uint32_t row, float lw)
+    {
+        sm.tab_row[tb][wave][i] = row;
+        sm.tab_lw[tb][wave][i] = lw;
+    }
+
+    // Issue the loads of a tile whose row table `tb` is written.  with_keys: also
+    // the key rows (otherwise the caller supplies the logits).
+    __device__ __forceinline__ void issue(Tile& t, int tb, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
+                                          bool with_keys)
+    {
+        wave_lds_fence();
+        if (with_keys) {
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                const uint32_t off = sm.tab_row[tb][wave][rb * 16 + n16] * RB + g16 * 16;
+#pragma unroll
+                for (int s = 0; s < KS; ++s) t.ak[rb][s] = buffer_ld16(kr, off + s * 64);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < NVI; ++u) t.vr[u] = buffer_ld16(vr, sm.tab_row[tb][wave][gv * NVI + u] * RB + cv * 16);
+    }
+
+    // Logits (log2 units) of the tile from its key rows: lane (n16, g16) gets
+    // head n16 of rows 16 rb + 4 g16 + i as x[4 rb + i].
+    __device__ __forceinline__ void logits_mfma(const Tile& t, int tb, float scale_log2, float (&x)[8])
+    {
+        f32x4_t c0 = {0.0f, 0.0f, 0.0f, 0.0f}, c1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, t.ak[0][s]), bq[s], c0, 0, 0, 0);
+            c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, t.ak[1][s]), bq[s], c1, 0, 0, 0);
+        }
+        const float4 lw0 = *reinterpret_cast<const float4*>(&sm.tab_lw[tb][wave][4 * g16]);
+        const float4 lw1 = *reinterpret_cast<const float4*>(&sm.tab_lw[tb][wave][16 + 4 * g16]);
+        const float lws[8] = {lw0.x, lw0.y, lw0.z, lw0.w, lw1.x, lw1.y, lw1.z, lw1.w};
+        const float cs[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = lws[i] == kNegInf ? kNegInf : fmaf(cs[i], scale_log2, lws[i]);
+    }
+
+    // Logits (log2 units) of the tile from natural-log logits in LDS: head n16's
+    // values for the tile's 32 rows start at `row_logits` (16-byte aligned); a
+    // table log-weight of -inf masks the row, any other value is ignored.
+    __device__ __forceinline__ void logits_lds(int tb, const float* row_logits, float (&x)[8])
+    {
+        const float4 lw0 = *reinterpret_cast<const float4*>(&sm.tab_lw[tb][wave][4 * g16]);
+        const float4 lw1 = *reinterpret_cast<const float4*>(&sm.tab_lw[tb][wave][16 + 4 * g16]);
+        const float4 v0 = *reinterpret_cast<const float4*>(row_logits + 4 * g16);
+        const float4 v1 = *reinterpret_cast<const float4*>(row_logits + 16 + 4 * g16);
+        const float lws[8] = {lw0.x, lw0.y, lw0.z, lw0.w, lw1.x, lw1.y, lw1.z, lw1.w};
+        const float vs[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = lws[i] == kNegInf ? kNegInf : vs[i] * kLog2e;
+    }
+
+    // Online-softmax update with the tile's logits; probabilities to LDS.
+    __device__ __forceinline__ void softmax(float (&x)[8])
+    {
+        float mx = x[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = rescale(m_run, m_new);
+        m_run = m_new;
+        l_part *= alpha;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            x[i] = x[i] == kNegInf ? 0.0f : exp2_(x[i] - m_new);
+            l_part += x[i];
+        }
+        if (n16 < HG) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sm.p[wave][4 * g16 + i][n16] = x[i];
+                sm.p[wave][16 + 4 * g16 + i][n16] = x[4 + i];
+            }
+            if (g16 == 0) sm.alpha[wave][n16] = alpha;
+        }
+        wave_lds_fence();
+    }
+
+    // P V of the tile on the value lanes.
+    __device__ __forceinline__ void accumulate(const Tile& t)
+    {
+        float al[HP];
+        *reinterpret_cast<float4*>(&al[0]) = *reinterpret_cast<const float4*>(&sm.alpha[wave][0]);
+        if constexpr (HP == 8) *reinterpret_cast<float4*>(&al[4]) = *reinterpret_cast<const float4*>(&sm.alpha[wave][4]);
+#pragma unroll
+        for (int g = 0; g < HG; ++g)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[g][e] *= al[g];
+#pragma unroll
+        for (int u = 0; u < NVI; ++u) {
+#ifdef CSA_SCHED_BARRIER
+            __builtin_amdgcn_sched_barrier(0);
+#endif
+            float pr[HP];
+            *reinterpret_cast<float4*>(&pr[0]) = *reinterpret_cast<const float4*>(&sm.p[wave][gv * NVI + u][0]);
+            if constexpr (HP == 8)
+                *reinterpret_cast<float4*>(&pr[4]) = *reinterpret_cast<const float4*>(&sm.p[wave][gv * NVI + u][4]);
+            float vf[8];
+            unpack<DT_BF16>(t.vr[u], vf);
+#pragma unroll
+            for (int g = 0; g < HG; ++g)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(pr[g], vf[e], acc[g][e]);
+        }
+        wave_lds_fence();  // p / alpha are rewritten by the next tile
+    }
+
+    // Merge the waves (the whole workgroup must call this).  Writes, for each
+    // active head g < nh and element e, either the normalised output and the
+    // lse (part == nullptr) or the partial state (max, sum, unnormalised output)
+    // at part + g * (D + 2).
+    __device__ __forceinline__ void finish(int nh, float* out, float* lse, float* part)
+    {
+#pragma unroll
+        for (int off = 16; off < 64; off <<= 1) l_part += __shfl_xor(l_part, off);
+#pragma unroll
+        for (int off = LPV; off < 64; off <<= 1)
+#pragma unroll
+            for (int g = 0; g < HG; ++g)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[g][e] += __shfl_xor(acc[g][e], off);
+        if (gv == 0) {
+#pragma unroll
+            for (int g = 0; g < HG; ++g)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sm.acc[wave][g][cv * 8 + e] = acc[g][e];
+        }
+        if (lane < HG) {
+            sm.m[wave][lane] = m_run;
+            sm.l[wave][lane] = l_part;
+        }
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < HG * D; idx += NW * 64) {
+            const int g = idx / D, e = idx - g * D;
+            if (g >= nh) continue;
+            float M = kNegInf;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.m[w][g]);
+            float Ls = 0.0f, A = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const float a = rescale(sm.m[w][g], M);
+                Ls += sm.l[w][g] * a;
+                A += sm.acc[w][g][e] * a;
+            }
+            if (part == nullptr) {
+                out[(size_t)g * D + e] = A / Ls;
+                if (e == 0 && lse) lse[g] = (M + log2f(Ls)) * kLn2;
+            } else {
+                float* st = part + (size_t)g * (D + 2);
+                if (e == 0) {
+                    st[0] = M;
+                    st[1] = Ls;
+                }
+                st[2 + e] = A;
+            }
+        }
+    }
+};
+
+}  // namespace csa

@@ -119,6 +119,50 @@ __device__ __forceinline__ float rescale(float m_old, float m_new)
     return m_old == kNegInf ? 0.0f : exp2_(m_old - m_new);
 }
 
+// ---- matrix-core and buffer-load helpers ----------------------------------
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+
+// Raw buffer resource over [base, base + bytes): loads outside return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buffer_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Ordering point for LDS data passed between lanes of one wave (a wave
+// executes its LDS instructions in order; this keeps the compiler from
+// moving loads and stores across it).
+__device__ __forceinline__ void wave_lds_fence()
+{
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+// q of up to 16 heads as the B operand of v_mfma_f32_16x16x32_bf16 for a
+// 32-element k-step s: lane (n16, g16) holds head n16 (zero past nh), 16-byte
+// chunk 4 s + g16 of the row.  Rows are loaded as the A operand with the same
+// chunk assignment (row n16 of the 16-row block, chunk 4 s + g16), so the MFMA
+// sums q . k over the chunks of the k-step; over all D/32 steps it is q . k.
+template <int D>
+__device__ __forceinline__ void load_q_operand(const char* q_first_head, int nh, int lane, bf16x8_t (&bq)[D / 32])
+{
+    const int n16 = lane & 15, g16 = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (n16 < nh) v = ld16(q_first_head + (size_t)n16 * D * 2 + (4 * s + g16) * 16);
+        bq[s] = __builtin_bit_cast(bf16x8_t, v);
+    }
+}
+
 // fp64 -> bfloat16 bit pattern, round to nearest with ties to even, in one step.
 __device__ __forceinline__ uint16_t bf16_from_f64(double x)
 {

@@ -29,14 +29,19 @@ hipError_t launch_block_logits_summary(const Dims& s, const void* q, const void*
 hipError_t launch_block_logits_exact(const Dims& s, const void* q, const void* K, float* dst,
                                      hipStream_t st);
 hipError_t launch_group_score(const Dims& s, const float* logits, float* scores, hipStream_t st);
+// Summary mode with the logits, log-normalisers and group score in one kernel
+// (one workgroup per KV head); available when fused_summary_score_ok().
+bool fused_summary_score_ok(const Dims& s);
+hipError_t launch_score_summary_fused(const Dims& s, const void* q, const void* Kbar, float* scores, hipStream_t st);
 
 // ---- top-k -----------------------------------------------------------------
 hipError_t launch_topk(int rows, int nb, int k, const float* scores, int32_t* sel, hipStream_t st);
 
 // ---- attention -------------------------------------------------------------
 struct AttnPlan {
-    int rows;            // virtual rows per KV head (exact + weighted + proxy)
+    int rows;            // virtual rows per KV head (exact + weighted + proxy, with padding)
     int exact_rows;      // rows of the exact segment (k L, or n for dense)
+    int pend, wbeg, ebeg;  // end of the proxy rows, first weighted row, first exact row
     int hg;              // query heads per workgroup
     int hchunks;         // ceil(G / hg)
     int splits;          // workgroups per (KV head, head chunk)
@@ -62,6 +67,29 @@ struct AttnInputs {
 };
 
 AttnPlan plan_attention(const Dims& s, int k, int m, int proxies, int dense);
+
+// ---- fused decode step (summary score -> top-k -> attention, one launch) ----
+constexpr int kFusedStepMinPairs = 32;  // below this, the split kernels use the GPU better
+
+struct StepInputs {
+    const void* q;
+    const void* K;
+    const void* V;
+    const void* Kbar;
+    const void* Vbar;
+    int k;
+    const int32_t* tok_idx;
+    const float* tok_logw;
+    int m;
+    int proxies;
+    float* scores;  // may be null
+    int32_t* sel;   // may be null
+    float* out;
+    float* lse;     // may be null
+};
+
+bool fused_step_ok(const Dims& s, int k, int m, int proxies);
+hipError_t launch_decode_step(const Dims& s, const StepInputs& in, hipStream_t st);
 hipError_t launch_attention(const Dims& s, const AttnPlan& plan, const AttnInputs& in, void* ws,
                             hipStream_t st);
 

@@ -215,6 +215,129 @@ __global__ void __launch_bounds__(256) group_score_kernel(const float* logits, f
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Summary mode, whole group in one workgroup per KV head: the block logits of
+// all G heads go to LDS (MFMA over the mean keys), then each head's
+// log-normaliser, then the group score.  Used when G <= 8 and the logits fit
+// in 64 KiB of LDS.
+// ---------------------------------------------------------------------------
+
+constexpr int kFusedWaves = 8;
+constexpr int kFusedMaxLogits = 16384;  // G * nb floats in LDS
+
+struct FusedScoreParams {
+    const char* q;
+    const char* Kbar;
+    float* scores;
+    int Hq, Hkv, G, nb;
+    float scale, ln_L, ln_last;
+};
+
+template <int D>
+__global__ void __launch_bounds__(kFusedWaves * 64) score_summary_fused_kernel(const FusedScoreParams p)
+{
+    constexpr int RB = D * 2, KS = D / 32, NW = kFusedWaves;
+    extern __shared__ float lsm[];  // [G][nb] block logits
+    __shared__ float lse_h[8];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n16 = lane & 15, g16 = lane >> 4;
+    const int pair = blockIdx.x, b = pair / p.Hkv, j = pair - b * p.Hkv;
+    const int G = p.G, nb = p.nb;
+
+    bf16x8_t bq[KS];
+    load_q_operand<D>(p.q + ((size_t)b * p.Hq + (size_t)j * G) * RB, G, lane, bq);
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(p.Kbar + (size_t)pair * nb * RB, (uint32_t)nb * RB);
+
+    for (int base = wave * 32; base < nb; base += NW * 32) {
+        uint4 ak[2][KS];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            const uint32_t off = (uint32_t)(base + rb * 16 + n16) * RB + g16 * 16;  // past nb: zeros
+#pragma unroll
+            for (int s = 0; s < KS; ++s) ak[rb][s] = buffer_ld16(kr, off + s * 64);
+        }
+        f32x4_t c[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+                c[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ak[rb][s]), bq[s], c[rb],
+                                                                0, 0, 0);
+        if (n16 < G) {
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = base + rb * 16 + 4 * g16 + i;
+                    if (row < nb) lsm[n16 * nb + row] = fmaf(c[rb][i], p.scale, row == nb - 1 ? p.ln_last : p.ln_L);
+                }
+        }
+    }
+    __syncthreads();
+
+    if (G > 1) {
+        for (int h = wave; h < G; h += NW) {
+            const float* row = lsm + h * nb;
+            float mx = kNegInf;
+            for (int i = lane; i < nb; i += 64) mx = fmaxf(mx, row[i]);
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+            float sum = 0.0f;
+            for (int i = lane; i < nb; i += 64) sum += exp2_((row[i] - mx) * kLog2e);
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+            if (lane == 0) lse_h[h] = mx + logf(sum);
+        }
+        __syncthreads();
+    }
+    for (int i = threadIdx.x; i < nb; i += NW * 64) {
+        float v;
+        if (G == 1) {
+            v = lsm[i];
+        } else {
+            float mx = kNegInf;
+            for (int h = 0; h < G; ++h) mx = fmaxf(mx, lsm[h * nb + i] - lse_h[h]);
+            float sum = 0.0f;
+            for (int h = 0; h < G; ++h) sum += exp2_((lsm[h * nb + i] - lse_h[h] - mx) * kLog2e);
+            v = mx + logf(sum);
+        }
+        p.scores[(size_t)pair * nb + i] = v;
+    }
+}
+
+}  // namespace
+
+bool fused_summary_score_ok(const Dims& s)
+{
+    return s.dtype == DT_BF16 && s.G <= 8 && s.G * s.nb <= kFusedMaxLogits;
+}
+
+hipError_t launch_score_summary_fused(const Dims& s, const void* q, const void* Kbar, float* scores, hipStream_t st)
+{
+    FusedScoreParams p{};
+    p.q = static_cast<const char*>(q);
+    p.Kbar = static_cast<const char*>(Kbar);
+    p.scores = scores;
+    p.Hq = s.Hq;
+    p.Hkv = s.Hkv;
+    p.G = s.G;
+    p.nb = s.nb;
+    p.scale = s.scale;
+    p.ln_L = s.ln_L;
+    p.ln_last = s.ln_last;
+    const size_t shm = (size_t)s.G * s.nb * sizeof(float);
+    const dim3 grid((unsigned)s.pairs()), block(kFusedWaves * 64);
+    if (s.d == 128)
+        score_summary_fused_kernel<128><<<grid, block, shm, st>>>(p);
+    else
+        score_summary_fused_kernel<64><<<grid, block, shm, st>>>(p);
+    return hipGetLastError();
+}
+
+namespace {
+
 template <int DT, int D, bool EXACT>
 hipError_t launch_logits_dtd(const LogitParams& p, int hg, int pairs, int hchunks, hipStream_t st)
 {

@@ -1,0 +1,380 @@
+// step.hip -- the whole selective decode step of one KV head in one workgroup:
+// block score (summary mode) -> top-k -> attention over exact tokens, weighted
+// tokens and count-aware proxies.
+//
+// The first-order block logit of "COBS: Cumulant Order Block Sparse Attention",
+// Eq. (18) (scale q . mean key + ln c_b) is also exactly the logit of the
+// count-aware proxy of "OpenAttention reads 1% of the KV cache -- Count-aware
+// tail proxy" (section "Skipping reviews without losing the verdict"): the mean
+// logit of the block plus ln(count).  So the mean keys are read once: the
+// logits of all blocks and heads stay in LDS, rank the blocks (Eq. (5), log
+// domain) and then serve as the proxy logits; the proxy rows of the attention
+// load only their mean values.
+//
+// Phases of a workgroup (KV head (b, j), all G <= 8 query heads of the group):
+//   1. waves stream the mean keys in tiles of 32 rows; MFMA logits -> LDS;
+//   2. per-head log-normaliser, group score (written out if asked), top-k by
+//      one wave (packed score/index keys), selection (written out if asked),
+//      bitmap of selected blocks;
+//   3. attention tiles: proxy rows (values only, logits from LDS, selected
+//      blocks masked), weighted rows, exact rows of the selected blocks (keys
+//      and values, MFMA logits), in the engine of attn_engine.hpp.
+#include "attn_engine.hpp"
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace csa {
+namespace {
+
+constexpr int kStepWaves = 8;
+constexpr int kStepMaxK = 32;
+constexpr int kStepMaxBlocks = 2048;     // top-k by one wave: 32 keys per lane
+constexpr int kStepMaxLdsBytes = 65536;  // dynamic LDS: logits, scores, bitmap
+
+struct StepParams {
+    const char* q;
+    const char* K;
+    const char* V;
+    const char* Kbar;
+    const char* Vbar;
+    const int32_t* tok_idx;
+    const float* tok_logw;
+    float* scores;  // optional
+    int32_t* sel;   // optional
+    float* out;
+    float* lse;     // optional
+    int Hq, Hkv, G, n, L, nb, k, m, proxies;
+    int pend, wbeg, ebeg, rows;  // attention row layout: [proxies][weighted][exact]
+    int lstride;                 // LDS row stride of the logits (nb rounded up to 32)
+    float scale, ln_L, ln_last, scale_log2;
+};
+
+__device__ __forceinline__ uint32_t order_key(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u) u = 0;  // -0 ties with +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)v, off);
+        const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off);
+        const uint64_t o = ((uint64_t)hi << 32) | lo;
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+template <int D, int HG>
+__global__ void __launch_bounds__(kStepWaves * 64) decode_step_kernel(const StepParams p)
+{
+    constexpr int NW = kStepWaves, TR = kTileRows;
+    using E = MfmaEngine<D, HG, NW>;
+    constexpr int RB = E::RB, KS = E::KS;
+    extern __shared__ float dyn[];
+    __shared__ typename E::Smem sm;
+    __shared__ float lse_h[8];
+    __shared__ int32_t sel_sm[kStepMaxK];
+
+    const int LS = p.lstride, G = p.G, nb = p.nb;
+    float* lsm = dyn;                                              // [G][LS] block logits (natural log)
+    float* ssm = dyn + G * LS;                                     // [LS] group scores
+    uint32_t* bits = reinterpret_cast<uint32_t*>(ssm + LS);        // [LS / 32] selected blocks
+    const int pair = blockIdx.x, b = pair / p.Hkv, j = pair - b * p.Hkv;
+    const int h0 = j * G;
+
+    E eng(sm, p.q + (size_t)(b * p.Hq + h0) * RB, G);
+    const int lane = eng.lane, wave = eng.wave, n16 = eng.n16, g16 = eng.g16;
+    for (int w = threadIdx.x; w < LS / 32; w += NW * 64) bits[w] = 0;
+
+    const __amdgpu_buffer_rsrc_t Kc = buffer_rsrc(p.K + (size_t)pair * p.n * RB, (uint32_t)p.n * RB);
+    const __amdgpu_buffer_rsrc_t Vc = buffer_rsrc(p.V + (size_t)pair * p.n * RB, (uint32_t)p.n * RB);
+    const __amdgpu_buffer_rsrc_t Ks = buffer_rsrc(p.Kbar + (size_t)pair * nb * RB, (uint32_t)nb * RB);
+    const __amdgpu_buffer_rsrc_t Vs =
+        buffer_rsrc(p.proxies ? p.Vbar + (size_t)pair * nb * RB : p.V, p.proxies ? (uint32_t)nb * RB : 0u);
+
+    // The first attention tile of the wave is a proxy tile when the wave's index is
+    // below the proxy tile count: its mean values do not depend on the selection,
+    // so their loads go out now and overlap the scoring phases (its selected
+    // blocks are masked once the selection is known).
+    typename E::Tile A, B;
+    // Tile orders are rotated by a per-workgroup offset, so that workgroups
+    // running side by side do not walk the same address offsets at the same
+    // time (their heads' arrays start at similarly aligned addresses).
+    const uint32_t hsh = (uint32_t)blockIdx.x * 0x9E3779B1u;
+    const int nK = (nb + TR - 1) / TR;                                  // mean-key tiles
+    const int rotK = (int)((hsh >> 4) % (uint32_t)nK);
+    const int nP = p.wbeg / TR;                                          // proxy tiles
+    const int nC = p.rows > p.wbeg ? (p.rows - p.wbeg + TR - 1) / TR : 0;  // cache tiles
+    const int nT = nP + nC;
+    const int rotP = nP ? (int)((hsh >> 8) % (uint32_t)nP) : 0;
+    const int rotC = nC ? (int)((hsh >> 16) % (uint32_t)nC) : 0;
+    auto row0 = [&](int t) { return t < nP ? (t + rotP) % nP * TR : p.wbeg + (t - nP + rotC) % nC * TR; };
+    const int first = wave < nT ? row0(wave) : p.rows;
+    const bool prefetched = wave < nP;
+    if (prefetched) {
+        if (lane < TR) {
+            const int r = first + lane;
+            eng.set_row(0, lane, (uint32_t)r, r < p.pend ? 0.0f : kNegInf);
+        }
+        eng.issue(A, 0, Ks, Vs, false);
+    }
+
+    // ---- phase 1: block logits of every head -> LDS ---------------------------
+    auto logits_to_lds = [&](int base, const uint4 (&ak)[2][KS]) {
+        f32x4_t c[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+                c[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ak[rb][s]), eng.bq[s],
+                                                                c[rb], 0, 0, 0);
+        if (n16 < G) {
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = base + rb * 16 + 4 * g16 + i;
+                    if (row < nb) lsm[n16 * LS + row] = fmaf(c[rb][i], p.scale, row == nb - 1 ? p.ln_last : p.ln_L);
+                }
+        }
+    };
+    auto load_keys = [&](int base, uint4 (&ak)[2][KS]) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            const uint32_t off = (uint32_t)(base + rb * 16 + n16) * RB + g16 * 16;  // past nb: zeros
+#pragma unroll
+            for (int s = 0; s < KS; ++s) ak[rb][s] = buffer_ld16(Ks, off + s * 64);
+        }
+    };
+    for (int t = wave; t < nK; t += 2 * NW) {  // two tiles in flight
+        uint4 k0[2][KS], k1[2][KS];
+        const int b0 = (t + rotK) % nK * TR, b1 = (t + NW + rotK) % nK * TR;
+        load_keys(b0, k0);
+        const bool two = t + NW < nK;
+        if (two) load_keys(b1, k1);
+        logits_to_lds(b0, k0);
+        if (two) logits_to_lds(b1, k1);
+    }
+    __syncthreads();
+
+    // ---- phase 2: group score and top-k ----------------------------------------
+    if (G > 1) {
+        if (wave < G) {
+            const float* row = lsm + wave * LS;
+            float mx = kNegInf;
+            for (int i = lane; i < nb; i += 64) mx = fmaxf(mx, row[i]);
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+            float sum = 0.0f;
+            for (int i = lane; i < nb; i += 64) sum += exp2_((row[i] - mx) * kLog2e);
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+            if (lane == 0) lse_h[wave] = mx + logf(sum);
+        }
+        __syncthreads();
+    }
+    for (int i = threadIdx.x; i < nb; i += NW * 64) {
+        float v;
+        if (G == 1) {
+            v = lsm[i];
+        } else {
+            float mx = kNegInf;
+            for (int h = 0; h < G; ++h) mx = fmaxf(mx, lsm[h * LS + i] - lse_h[h]);
+            float sum = 0.0f;
+            for (int h = 0; h < G; ++h) sum += exp2_((lsm[h * LS + i] - lse_h[h] - mx) * kLog2e);
+            v = mx + logf(sum);
+        }
+        ssm[i] = v;
+        if (p.scores) p.scores[(size_t)pair * nb + i] = v;
+    }
+    __syncthreads();
+    const int kk = p.k;  // <= min(32, nb)
+    if (wave == 0 && kk > 0) {
+        // lane owns blocks [lane * per, lane * per + per); larger key = higher score, then lower index
+        const int per = (nb + 63) >> 6;
+        uint64_t key[kStepMaxK];
+#pragma unroll
+        for (int i = 0; i < kStepMaxK; ++i) {
+            const int idx = lane * per + i;
+            key[i] = (i < per && idx < nb) ? ((uint64_t)order_key(ssm[idx]) << 32) | (uint32_t)~(uint32_t)idx : 0;
+        }
+        uint32_t taken = 0;
+        for (int it = 0; it < kk; ++it) {
+            uint64_t best = 0;
+#pragma unroll
+            for (int i = 0; i < kStepMaxK; ++i)
+                if (!((taken >> i) & 1u) && key[i] > best) best = key[i];
+            best = wave_max_u64(best);
+            const uint32_t widx = ~(uint32_t)best;
+            if ((int)(widx / per) == lane) taken |= 1u << (widx % per);
+        }
+        const int cnt = __popc(taken);
+        int incl = cnt;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int t = __shfl_up(incl, off);
+            if (lane >= off) incl += t;
+        }
+        int pos = incl - cnt;
+#pragma unroll
+        for (int i = 0; i < kStepMaxK; ++i) {
+            if ((taken >> i) & 1u) {
+                const int idx = lane * per + i;
+                sel_sm[pos] = idx;
+                if (p.sel) p.sel[(size_t)pair * kk + pos] = idx;
+                atomicOr(&bits[idx >> 5], 1u << (idx & 31));
+                ++pos;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 3: attention ------------------------------------------------------
+    auto resolve = [&](int r, uint32_t& row, float& lw) {
+        row = 0;
+        lw = kNegInf;
+        if (r >= p.rows) return;
+        if (r < p.pend) {
+            row = (uint32_t)r;
+            if (!((bits[r >> 5] >> (r & 31)) & 1u)) lw = 0.0f;  // the logit itself comes from LDS
+        } else if (r >= p.wbeg && r < p.wbeg + p.m) {
+            const int t = r - p.wbeg;
+            const int tok = p.tok_idx[(size_t)pair * p.m + t];
+            if (tok >= 0 && tok < p.n) {
+                row = (uint32_t)tok;
+                lw = p.tok_logw[(size_t)pair * p.m + t] * kLog2e;
+            }
+        } else if (r >= p.ebeg) {
+            const int e = r - p.ebeg;
+            const int slot = e / p.L;
+            const int tok = sel_sm[slot] * p.L + (e - slot * p.L);
+            if (tok < p.n) {
+                row = (uint32_t)tok;
+                lw = 0.0f;
+            }
+        }
+    };
+    auto issue_any = [&](int base, typename E::Tile& t, int tb) {
+        if (lane < TR) {
+            uint32_t row;
+            float lw;
+            resolve(base + lane, row, lw);
+            eng.set_row(tb, lane, row, lw);
+        }
+        if (base < p.wbeg)
+            eng.issue(t, tb, Ks, Vs, false);  // proxy tile: values only
+        else
+            eng.issue(t, tb, Kc, Vc, true);
+    };
+    auto compute = [&](int base, const typename E::Tile& t, int tb) {
+        float x[8];
+        if (base < p.wbeg)
+            eng.logits_lds(tb, lsm + (n16 < G ? n16 : G - 1) * LS + base, x);
+        else
+            eng.logits_mfma(t, tb, p.scale_log2, x);
+        eng.softmax(x);
+    };
+
+    if (prefetched && lane < TR) {  // mask the selected blocks of the prefetched tile
+        const int r = first + lane;
+        if (r < p.pend && ((bits[r >> 5] >> (r & 31)) & 1u)) sm.tab_lw[0][wave][lane] = kNegInf;
+    }
+    int t = wave;
+    if (t < nT) {
+        if (!prefetched) issue_any(first, A, 0);
+        for (;;) {
+            const int t1 = t + NW;
+            compute(row0(t), A, 0);
+            if (t1 < nT) issue_any(row0(t1), B, 1);
+            eng.accumulate(A);
+            if (t1 >= nT) break;
+            const int t2 = t1 + NW;
+            compute(row0(t1), B, 1);
+            if (t2 < nT) issue_any(row0(t2), A, 0);
+            eng.accumulate(B);
+            if (t2 >= nT) break;
+            t = t2;
+        }
+    }
+    eng.finish(G, p.out + ((size_t)b * p.Hq + h0) * D, p.lse ? p.lse + (size_t)b * p.Hq + h0 : nullptr, nullptr);
+}
+
+size_t step_lds_bytes(const Dims& s)
+{
+    const int ls = (s.nb + kTileRows - 1) / kTileRows * kTileRows;
+    return (size_t)(s.G + 1) * ls * sizeof(float) + (size_t)(ls / 32) * sizeof(uint32_t);
+}
+
+template <int D>
+hipError_t launch_step_d(const StepParams& p, int pairs, size_t shm, hipStream_t st)
+{
+    const dim3 grid((unsigned)pairs), block(kStepWaves * 64);
+    switch (p.G) {
+    case 1: decode_step_kernel<D, 1><<<grid, block, shm, st>>>(p); break;
+    case 2: decode_step_kernel<D, 2><<<grid, block, shm, st>>>(p); break;
+    case 3: decode_step_kernel<D, 3><<<grid, block, shm, st>>>(p); break;
+    case 4: decode_step_kernel<D, 4><<<grid, block, shm, st>>>(p); break;
+    case 5: decode_step_kernel<D, 5><<<grid, block, shm, st>>>(p); break;
+    case 6: decode_step_kernel<D, 6><<<grid, block, shm, st>>>(p); break;
+    case 7: decode_step_kernel<D, 7><<<grid, block, shm, st>>>(p); break;
+    case 8: decode_step_kernel<D, 8><<<grid, block, shm, st>>>(p); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool fused_step_ok(const Dims& s, int k, int m, int proxies)
+{
+    (void)m;
+    (void)proxies;
+    return s.dtype == DT_BF16 && s.G <= 8 && k <= kStepMaxK && s.nb <= kStepMaxBlocks &&
+           s.pairs() >= kFusedStepMinPairs && step_lds_bytes(s) <= (size_t)kStepMaxLdsBytes;
+}
+
+hipError_t launch_decode_step(const Dims& s, const StepInputs& in, hipStream_t st)
+{
+    const int pad = kTileRows;
+    StepParams p{};
+    p.q = static_cast<const char*>(in.q);
+    p.K = static_cast<const char*>(in.K);
+    p.V = static_cast<const char*>(in.V);
+    p.Kbar = static_cast<const char*>(in.Kbar);
+    p.Vbar = static_cast<const char*>(in.Vbar);
+    p.tok_idx = in.tok_idx;
+    p.tok_logw = in.tok_logw;
+    p.scores = in.scores;
+    p.sel = in.sel;
+    p.out = in.out;
+    p.lse = in.lse;
+    p.Hq = s.Hq;
+    p.Hkv = s.Hkv;
+    p.G = s.G;
+    p.n = s.n;
+    p.L = s.L;
+    p.nb = s.nb;
+    p.k = in.k < s.nb ? in.k : s.nb;
+    p.m = in.m;
+    p.proxies = in.proxies;
+    p.pend = in.proxies ? s.nb : 0;
+    p.wbeg = (p.pend + pad - 1) / pad * pad;
+    p.ebeg = p.wbeg + (in.m + pad - 1) / pad * pad;
+    const int exact_rows = p.k * s.L;
+    p.rows = exact_rows > 0 ? p.ebeg + exact_rows : (in.m > 0 ? p.wbeg + in.m : p.pend);
+    p.lstride = (s.nb + pad - 1) / pad * pad;
+    p.scale = s.scale;
+    p.ln_L = s.ln_L;
+    p.ln_last = s.ln_last;
+    p.scale_log2 = s.scale * kLog2e;
+    const size_t shm = step_lds_bytes(s);
+    if (s.d == 128) return launch_step_d<128>(p, s.pairs(), shm, st);
+    if (s.d == 64) return launch_step_d<64>(p, s.pairs(), shm, st);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace csa

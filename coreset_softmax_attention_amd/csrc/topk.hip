@@ -11,6 +11,12 @@
 //   3. a scan in index order writes every index with key > T and the lowest
 //      indices with key == T, so the output is ascending by index.
 // Integer histograms and scans only: the result does not depend on timing.
+//
+// Small k (k <= 32, nb <= 2048) uses one wavefront per row instead: every lane
+// holds up to 32 packed keys (order-preserving score bits, then the inverted
+// index, so a larger key is a higher score or, on a tie, a lower index); k
+// rounds of a wave-wide maximum pick the winners, and a prefix count over the
+// lanes writes them in index order.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -130,10 +136,75 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(const float* scores, int
     }
 }
 
+
+constexpr int kWaveTopkMaxK = 32;
+constexpr int kWaveTopkMaxPer = 32;  // keys per lane
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)v, off);
+        const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off);
+        const uint64_t o = ((uint64_t)hi << 32) | lo;
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+template <int PER>
+__global__ void __launch_bounds__(256) topk_wave_kernel(const float* scores, int32_t* sel, int rows, int nb, int k)
+{
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;  // whole wave; no workgroup barrier below
+    const float* s = scores + (size_t)row * nb;
+    uint64_t key[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int idx = lane * PER + i;
+        key[i] = idx < nb ? ((uint64_t)order_key(s[idx]) << 32) | (uint32_t)~(uint32_t)idx : 0;
+    }
+    uint32_t taken = 0;
+    for (int it = 0; it < k; ++it) {
+        uint64_t best = 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+            if (!((taken >> i) & 1u) && key[i] > best) best = key[i];
+        best = wave_max_u64(best);
+        const uint32_t widx = ~(uint32_t)best;
+        if ((int)(widx / PER) == lane) taken |= 1u << (widx % PER);
+    }
+    // write the taken indices in ascending order
+    const int cnt = __popc(taken);
+    int incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(incl, off);
+        if (lane >= off) incl += t;
+    }
+    int pos = incl - cnt;
+    int32_t* out = sel + (size_t)row * k;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+        if ((taken >> i) & 1u) out[pos++] = lane * PER + i;
+}
+
 }  // namespace
 
 hipError_t launch_topk(int rows, int nb, int k, const float* scores, int32_t* sel, hipStream_t st)
 {
+    const int per = (nb + 63) / 64;
+    if (k < nb && k <= kWaveTopkMaxK && per <= kWaveTopkMaxPer) {
+        const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+        if (per <= 1) topk_wave_kernel<1><<<grid, block, 0, st>>>(scores, sel, rows, nb, k);
+        else if (per <= 2) topk_wave_kernel<2><<<grid, block, 0, st>>>(scores, sel, rows, nb, k);
+        else if (per <= 4) topk_wave_kernel<4><<<grid, block, 0, st>>>(scores, sel, rows, nb, k);
+        else if (per <= 8) topk_wave_kernel<8><<<grid, block, 0, st>>>(scores, sel, rows, nb, k);
+        else if (per <= 16) topk_wave_kernel<16><<<grid, block, 0, st>>>(scores, sel, rows, nb, k);
+        else topk_wave_kernel<32><<<grid, block, 0, st>>>(scores, sel, rows, nb, k);
+        return hipGetLastError();
+    }
     topk_kernel<<<dim3((unsigned)rows), dim3(kThreads), 0, st>>>(scores, sel, nb, k);
     return hipGetLastError();
 }

@@ -45,7 +45,8 @@
  *   - No floating-point atomics: results are bitwise reproducible for the same
  *     inputs, shapes and device.
  *   - Supported in this version: dtype CSA_F32 or CSA_BF16, d in {64, 128},
- *     G <= 64, n <= 2^30.  All pointers 16-byte aligned.
+ *     G <= 64, n <= 2^30, and one KV head's K (or V) below 4 GiB
+ *     (n * d * element bytes < 2^32).  All pointers 16-byte aligned.
  *   - Inputs must be finite.  Indices outside their range are rejected only
  *     where the host can see them (sizes); device-resident index values are
  *     trusted.
@@ -86,7 +87,8 @@ typedef enum csa_entry {
     CSA_WS_BLOCK_SCORE_SUMMARY = 0,
     CSA_WS_BLOCK_SCORE_EXACT_MASS = 1,
     CSA_WS_SPARSE_DECODE_ATTN = 2,
-    CSA_WS_DENSE_DECODE_ATTN = 3
+    CSA_WS_DENSE_DECODE_ATTN = 3,
+    CSA_WS_SELECTIVE_DECODE_STEP = 4
 } csa_entry;
 
 typedef struct csa_shape {
@@ -167,6 +169,28 @@ int sparse_decode_attn(const csa_shape* shape, const void* q, const void* K, con
  */
 int dense_decode_attn(const csa_shape* shape, const void* q, const void* K, const void* V,
                       float* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * selective_decode_step -- block_score, topk_select and sparse_decode_attn of
+ * one decode step in a single call, same results as calling the three in turn
+ * (scores and selection bit for bit, outputs to rounding).
+ * In summary mode the first-order block logit scale q_h . Kbar_b + ln c_b
+ * ([COBS] Eq. (18)) is also the logit of the block's count-aware proxy ([OA]
+ * "Skipping reviews...": mean logit + ln count), so where the shape allows
+ * (bfloat16, G <= 8, k <= 32, nb <= 2048, B * Hkv >= 32) one kernel per KV head
+ * reads Kbar once, keeps the logits on chip for both uses, selects the blocks
+ * and attends; otherwise the three entry points run in turn.
+ * keys = Kbar (SUMMARY) or K (EXACT_MASS) as for block_score; Kbar may be NULL
+ * in EXACT_MASS mode without proxies.  scores [B, Hkv, nb] and
+ * sel [B, Hkv, min(k, nb)] are written when not NULL.  0 <= k; k = 0 with no
+ * proxies and m = 0 is CSA_ERR_INVALID_ARG.  Workspace: csa_workspace_size(
+ * shape, CSA_WS_SELECTIVE_DECODE_STEP, k, m) bytes.
+ */
+int selective_decode_step(const csa_shape* shape, csa_score_mode mode, const void* q, const void* K,
+                          const void* V, const void* Kbar, const void* Vbar, int32_t k,
+                          const int32_t* tok_idx, const float* tok_logw, int32_t m,
+                          csa_proxy_mode proxy_mode, float* scores, int32_t* sel, float* out,
+                          float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Workspace bytes needed by an entry point for this shape (k, m as the call
  * will pass them).  Returns 0 for an invalid shape (see csa_last_error()). */

@@ -33,7 +33,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = set(declared_functions())
     assert {"kv_summary_build", "block_score", "topk_select", "sparse_decode_attn", "dense_decode_attn",
-            "csa_workspace_size", "csa_status_str", "csa_last_error"} <= names
+            "selective_decode_step", "csa_workspace_size", "csa_status_str", "csa_last_error"} <= names
 
 
 def test_library_exports_every_declared_function(L):
@@ -108,7 +108,7 @@ def test_sparse_argument_checks(L):
 
 
 def test_workspace_is_checked_before_launch(L):
-    s = shape(B=32, Hq=32, Hkv=8, n=32768)  # the 1 %-read decode shape needs split-K partials
+    s = shape(B=1, Hq=32, Hkv=8, n=32768)  # one sequence: split-K partials need a workspace
     need = L.csa_workspace_size(ctypes.byref(s), csa.CSA_WS_SPARSE_DECODE_ATTN, 5, 0)
     assert need > 0
     assert sparse(L, s, k=5, ws=None) == csa.CSA_ERR_WORKSPACE
@@ -118,7 +118,7 @@ def test_workspace_is_checked_before_launch(L):
     assert dneed > 0
     assert L.dense_decode_attn(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == csa.CSA_ERR_WORKSPACE
     bneed = L.csa_workspace_size(ctypes.byref(s), csa.CSA_WS_BLOCK_SCORE_SUMMARY, 0, 0)
-    assert bneed == 32 * 32 * 512 * 4
+    assert bneed == 1 * 32 * 512 * 4
     assert L.block_score(ctypes.byref(s), 0, FAKE, FAKE, FAKE, None, 0, None) == csa.CSA_ERR_WORKSPACE
     assert L.block_score(ctypes.byref(s), 9, FAKE, FAKE, FAKE, None, 0, None) == csa.CSA_ERR_INVALID_ARG
 
@@ -152,3 +152,28 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(csa, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         csa.lib()
+
+
+def step(L, s, mode=0, k=2, m=0, proxy=1, ptrs=FAKE, kbar=FAKE, ws=None, wsb=0):
+    p = ptrs
+    return L.selective_decode_step(ctypes.byref(s) if s is not None else None, mode, p, p, p, kbar, kbar, k,
+                                   FAKE if m else None, FAKE if m else None, m, proxy, None, None, p, p, ws, wsb,
+                                   None)
+
+
+def test_decode_step_argument_checks(L):
+    s = shape()
+    assert step(L, None) == csa.CSA_ERR_INVALID_ARG
+    assert step(L, s, mode=4) == csa.CSA_ERR_INVALID_ARG
+    assert step(L, s, proxy=3) == csa.CSA_ERR_INVALID_ARG
+    assert step(L, s, k=0, proxy=0) == csa.CSA_ERR_INVALID_ARG
+    assert b"empty virtual-token set" in L.csa_last_error()
+    assert step(L, s, k=-1) == csa.CSA_ERR_INVALID_ARG
+    assert step(L, s, kbar=None) == csa.CSA_ERR_INVALID_ARG
+    assert step(L, s, ptrs=FAKE + 4) == csa.CSA_ERR_INVALID_ARG
+    assert step(L, shape(d=80)) == csa.CSA_ERR_UNSUPPORTED
+    # a shape the one-kernel path does not take (B * Hkv < 32) needs the workspace
+    need = L.csa_workspace_size(ctypes.byref(s), csa.CSA_WS_SELECTIVE_DECODE_STEP, 2, 0)
+    assert need >= 2 * 2 * 16 * 4
+    assert step(L, s, ws=None) == csa.CSA_ERR_WORKSPACE
+    assert step(L, s, ws=FAKE, wsb=need - 1) == csa.CSA_ERR_WORKSPACE

@@ -331,3 +331,125 @@ def test_full_size_sampled(name):
               "score": g["score"][b:b + 1, j:j + 1], "sel": g["sel"][b:b + 1, j:j + 1],
               "out": g["out"][b:b + 1, j * G:(j + 1) * G], "lse": g["lse"][b:b + 1, j * G:(j + 1) * G]}
         compare_pipelines(w, gs, o, f"{name} pair ({b},{j})")
+
+
+def test_graph_replay_matches_eager():
+    """The decode step captured in a HIP graph and replayed several times, with eager work on
+    the same buffers between replays, reproduces the eager result bit for bit each time."""
+    w = small("llama3_8b_layer_b1", batch=4, n_tokens=8192, n_kv_heads=2)
+    data = W.generate(w)
+    q, K, V = dev(data["q"]), dev(data["K"]), dev(data["V"])
+    Kbar, Vbar = csa.kv_summary_build(K, V, w.block_size)
+    shape = csa.make_shape(q, K, w.block_size)
+    scores = torch.empty((w.batch, w.n_kv_heads, w.n_blocks), dtype=torch.float32, device="cuda")
+    sel = torch.empty((w.batch, w.n_kv_heads, w.k), dtype=torch.int32, device="cuda")
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.batch, w.n_q_heads), dtype=torch.float32, device="cuda")
+    ws_s = torch.empty(max(1, csa.workspace_size(shape, csa.CSA_WS_BLOCK_SCORE_SUMMARY)), dtype=torch.uint8,
+                       device="cuda")
+    ws_a = torch.empty(max(1, csa.workspace_size(shape, csa.CSA_WS_SPARSE_DECODE_ATTN, w.k, 0)),
+                       dtype=torch.uint8, device="cuda")
+
+    def step():
+        csa.block_score(q, Kbar, "summary", w.block_size, n_tokens=w.n_tokens, scores=scores, ws=ws_s)
+        csa.topk_select(scores, w.k, sel=sel)
+        csa.sparse_decode_attn(q, K, V, Kbar, Vbar, sel, w.block_size, out=out, lse=lse, ws=ws_a)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [host(t).copy() for t in (scores, sel, out, lse)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(4):
+        for t in (scores, out, lse):
+            t.fill_(float(i))
+        sel.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, (scores, sel, out, lse)):
+            assert np.array_equal(bits(a), bits(host(b))), f"replay {i}"
+
+
+# ---------------------------------------------------------------------------
+# the one-call decode step (one kernel per KV head where the shape allows)
+# ---------------------------------------------------------------------------
+
+def gpu_step(w, data, k=None, mode=None, proxies=None):
+    k = w.k if k is None else k
+    mode = w.score_mode if mode is None else mode
+    proxies = w.proxies if proxies is None else proxies
+    q, K, V = dev(data["q"]), dev(data["K"]), dev(data["V"])
+    Kbar, Vbar = csa.kv_summary_build(K, V, w.block_size)
+    ti = dev(data["tok_idx"]) if "tok_idx" in data else None
+    tw = dev(data["tok_logw"]) if "tok_logw" in data else None
+    out, lse, scores, sel = csa.selective_decode_step(q, K, V, Kbar, Vbar, k, w.block_size, mode=mode,
+                                                      proxies=proxies, tok_idx=ti, tok_logw=tw, want_scores=True,
+                                                      want_sel=True)
+    torch.cuda.synchronize()
+    return {"Kbar": host(Kbar), "Vbar": host(Vbar), "score": host(scores), "sel": host(sel), "out": host(out),
+            "lse": host(lse)}
+
+
+STEP_CASES = [  # B * Hkv >= 32 takes the one-kernel path
+    ("llama_b8_4k", small("llama3_8b_layer_b32", batch=8, n_tokens=4096, n_kv_heads=4), {}),
+    ("llama_b8_4k_k32", small("llama3_8b_layer_b32", batch=8, n_tokens=4096, n_kv_heads=4), {"k": 32}),
+    ("llama_b8_4k_k0", small("llama3_8b_layer_b32", batch=8, n_tokens=4096, n_kv_heads=4), {"k": 0}),
+    ("llama_b8_discard", small("llama3_8b_layer_b32", batch=8, n_tokens=4096, n_kv_heads=4), {"proxies": False}),
+    ("mha_b8_summary", small("exact_mass_mha_b8", batch=2, n_tokens=4096, n_kv_heads=16),
+     {"mode": "summary", "proxies": True}),
+    ("coreset_g7_b8", small("weighted_coreset_128k", batch=8, n_tokens=8192, n_kv_heads=4).with_(coreset=300), {}),
+    ("few_pairs_unfused", small("llama3_8b_layer_b1", batch=2, n_tokens=4096, n_kv_heads=2), {}),
+    ("exact_mass_unfused", small("exact_mass_gqa_b8", batch=8, n_tokens=4096, n_kv_heads=4), {}),
+]
+
+
+@pytest.mark.parametrize("name,w,kw", STEP_CASES, ids=[c[0] for c in STEP_CASES])
+def test_decode_step_matches_oracle(name, w, kw):
+    data = W.generate(w)
+    compare_pipelines(w.with_(**{k: v for k, v in kw.items() if k == "k"}), gpu_step(w, data, **kw),
+                      oracle_pipeline(w, data, **kw), name)
+
+
+@pytest.mark.parametrize("dtype,G,d,n,L", [("bf16", 3, 128, 1000, 64), ("bf16", 8, 64, 2000, 32),
+                                           ("bf16", 1, 128, 700, 16)])
+def test_decode_step_shapes(dtype, G, d, n, L):
+    """Ragged last blocks, d = 64, G = 8 and G = 1 through the one-kernel path."""
+    B, Hkv = 8, 4
+    w = W.Workload("step_shape", 0, B, G * Hkv, Hkv, d, n, L, dtype, 4, "summary", True, "clusters")
+    data = rand_inputs(300 + G + n, B, G * Hkv, Hkv, d, n, dtype)
+    compare_pipelines(w, gpu_step(w, data), oracle_pipeline(w, data), f"step G={G} d={d} n={n} L={L}")
+
+
+def test_decode_step_scores_and_selection_equal_modular_path():
+    """The one-kernel step ranks with exactly the scores block_score computes and selects what
+    topk_select selects (bit for bit); outputs agree with sparse_decode_attn to rounding."""
+    w = small("llama3_8b_layer_b32", batch=8, n_tokens=8192, n_kv_heads=4)
+    data = W.generate(w)
+    a, b = gpu_step(w, data), gpu_pipeline(w, data)
+    assert np.array_equal(bits(a["score"]), bits(b["score"]))
+    assert np.array_equal(a["sel"], b["sel"])
+    assert row_err(a["out"], b["out"]) < 1e-5
+    assert np.abs(a["lse"] - b["lse"]).max() < 1e-5
+
+
+def test_decode_step_full_size_sampled():
+    w = W.WORKLOADS["llama3_8b_layer_b32"]
+    data = W.generate(w)
+    g = gpu_step(w, data)
+    rng = np.random.default_rng(77)
+    G = w.group
+    for b, j in sorted({(int(rng.integers(w.batch)), int(rng.integers(w.n_kv_heads))) for _ in range(4)}):
+        sub = {"q": data["q"][b:b + 1, j * G:(j + 1) * G], "K": data["K"][b:b + 1, j:j + 1],
+               "V": data["V"][b:b + 1, j:j + 1]}
+        o = oracle_pipeline(w, sub)
+        gs = {"Kbar": g["Kbar"][b:b + 1, j:j + 1], "Vbar": g["Vbar"][b:b + 1, j:j + 1],
+              "score": g["score"][b:b + 1, j:j + 1], "sel": g["sel"][b:b + 1, j:j + 1],
+              "out": g["out"][b:b + 1, j * G:(j + 1) * G], "lse": g["lse"][b:b + 1, j * G:(j + 1) * G]}
+        compare_pipelines(w, gs, o, f"step pair ({b},{j})")
