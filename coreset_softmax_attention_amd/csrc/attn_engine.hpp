@@ -35,11 +35,13 @@ struct MfmaEngine {
     static constexpr int RPV = 64 / LPV;        // value rows per wave-wide load
     static constexpr int NVI = TR / RPV;        // value loads per lane per tile
     static constexpr int HP = HG <= 4 ? 4 : 8;  // padded heads per probability row
-    static_assert(KS * 32 == D && HG <= 8, "unsupported geometry");
+    static_assert(KS * 32 == D && HG <= 8 && (LPV == 8 || LPV == 16), "unsupported geometry");
+
+    static constexpr int NTAB = 4;  // row tables per wave (tiles in flight or pending)
 
     struct Smem {
-        uint32_t tab_row[2][NW][TR];  // two row tables: two tiles are in flight
-        float tab_lw[2][NW][TR] __attribute__((aligned(16)));
+        uint32_t tab_row[NTAB][NW][TR];
+        float tab_lw[NTAB][NW][TR] __attribute__((aligned(16)));
         float p[NW][TR][HP] __attribute__((aligned(16)));
         float alpha[NW][HP] __attribute__((aligned(16)));
         float m[NW][HG];
@@ -102,6 +104,14 @@ struct MfmaEngine {
         for (int u = 0; u < NVI; ++u) t.vr[u] = buffer_ld16(vr, sm.tab_row[tb][wave][gv * NVI + u] * RB + cv * 16);
     }
 
+    // Issue only the value rows of a tile (its logits come from the caller).
+    __device__ __forceinline__ void issue_values(uint4 (&vr)[NVI], int tb, __amdgpu_buffer_rsrc_t rsrc)
+    {
+        wave_lds_fence();
+#pragma unroll
+        for (int u = 0; u < NVI; ++u) vr[u] = buffer_ld16(rsrc, sm.tab_row[tb][wave][gv * NVI + u] * RB + cv * 16);
+    }
+
     // Logits (log2 units) of the tile from its key rows: lane (n16, g16) gets
     // head n16 of rows 16 rb + 4 g16 + i as x[4 rb + i].
     __device__ __forceinline__ void logits_mfma(const Tile& t, int tb, float scale_log2, float (&x)[8])
@@ -141,8 +151,7 @@ struct MfmaEngine {
         float mx = x[0];
 #pragma unroll
         for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = max_xor32(max_xor16(mx));
         const float m_new = fmaxf(m_run, mx);
         const float alpha = rescale(m_run, m_new);
         m_run = m_new;
@@ -164,7 +173,9 @@ struct MfmaEngine {
     }
 
     // P V of the tile on the value lanes.
-    __device__ __forceinline__ void accumulate(const Tile& t)
+    __device__ __forceinline__ void accumulate(const Tile& t) { accumulate_values(t.vr); }
+
+    __device__ __forceinline__ void accumulate_values(const uint4 (&vr)[NVI])
     {
         float al[HP];
         *reinterpret_cast<float4*>(&al[0]) = *reinterpret_cast<const float4*>(&sm.alpha[wave][0]);
@@ -183,7 +194,7 @@ struct MfmaEngine {
             if constexpr (HP == 8)
                 *reinterpret_cast<float4*>(&pr[4]) = *reinterpret_cast<const float4*>(&sm.p[wave][gv * NVI + u][4]);
             float vf[8];
-            unpack<DT_BF16>(t.vr[u], vf);
+            unpack<DT_BF16>(vr[u], vf);
 #pragma unroll
             for (int g = 0; g < HG; ++g)
 #pragma unroll
@@ -198,14 +209,17 @@ struct MfmaEngine {
     // at part + g * (D + 2).
     __device__ __forceinline__ void finish(int nh, float* out, float* lse, float* part)
     {
+        l_part = add_xor32(add_xor16(l_part));
+        // sum the lane groups holding the same value columns (lanes l ^ LPV, ...)
 #pragma unroll
-        for (int off = 16; off < 64; off <<= 1) l_part += __shfl_xor(l_part, off);
+        for (int g = 0; g < HG; ++g)
 #pragma unroll
-        for (int off = LPV; off < 64; off <<= 1)
-#pragma unroll
-            for (int g = 0; g < HG; ++g)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[g][e] += __shfl_xor(acc[g][e], off);
+            for (int e = 0; e < 8; ++e) {
+                float a = acc[g][e];
+                if constexpr (LPV == 8) a += dpp<DPP_ROW_ROR8>(a);
+                a = add_xor32(add_xor16(a));
+                acc[g][e] = a;
+            }
         if (gv == 0) {
 #pragma unroll
             for (int g = 0; g < HG; ++g)

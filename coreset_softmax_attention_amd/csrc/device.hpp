@@ -78,6 +78,7 @@ enum : int {
     DPP_QUAD_2301 = 0x4E,     // quad_perm [2,3,0,1]
     DPP_ROW_MIRROR = 0x140,   // lane i <-> 15 - i within 16 lanes
     DPP_ROW_HMIRROR = 0x141,  // lane i <-> 7 - i within 8 lanes
+    DPP_ROW_ROR8 = 0x128,     // lane i <- lane (i + 8) mod 16 within 16 lanes, i.e. i ^ 8
 };
 
 template <int CTRL>
@@ -86,8 +87,56 @@ __device__ __forceinline__ float dpp(float v)
     return __builtin_amdgcn_update_dpp(0.0f, v, CTRL, 0xf, 0xf, false);
 }
 
-// Sum over aligned groups of W lanes (W = 8, 16 or 32); every lane of the group
-// receives the group's sum.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+
+// Values of lanes l and l ^ 16 (Swap16) or l and l ^ 32 (Swap32), from the
+// gfx950 lane-swap instructions: v_permlane16_swap exchanges the odd 16-lane
+// rows of its first operand with the even rows of its second, v_permlane32_swap
+// the upper half of the first with the lower half of the second.  Given the
+// same register twice, every lane ends up holding its own value and its
+// partner's (in .a and .b, in an order that depends on the lane's row, which
+// does not matter for the commutative combines below).  These are ALU
+// instructions, unlike ds_bpermute, which goes through the LDS pipeline.
+struct LanePair {
+    uint32_t a, b;
+};
+__device__ __forceinline__ LanePair swap16(uint32_t v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return {r[0], r[1]};
+}
+__device__ __forceinline__ LanePair swap32(uint32_t v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return {r[0], r[1]};
+}
+__device__ __forceinline__ float add_xor16(float v)
+{
+    const LanePair r = swap16(__float_as_uint(v));
+    return __uint_as_float(r.a) + __uint_as_float(r.b);
+}
+__device__ __forceinline__ float add_xor32(float v)
+{
+    const LanePair r = swap32(__float_as_uint(v));
+    return __uint_as_float(r.a) + __uint_as_float(r.b);
+}
+__device__ __forceinline__ float max_xor16(float v)
+{
+    const LanePair r = swap16(__float_as_uint(v));
+    return fmaxf(__uint_as_float(r.a), __uint_as_float(r.b));
+}
+__device__ __forceinline__ float max_xor32(float v)
+{
+    const LanePair r = swap32(__float_as_uint(v));
+    return fmaxf(__uint_as_float(r.a), __uint_as_float(r.b));
+}
+
+// Sum over aligned groups of W lanes (W = 8, 16, 32 or 64); every lane of the
+// group receives the group's sum.
 template <int W>
 __device__ __forceinline__ float group_sum(float v)
 {
@@ -95,7 +144,8 @@ __device__ __forceinline__ float group_sum(float v)
     v += dpp<DPP_QUAD_2301>(v);
     v += dpp<DPP_ROW_HMIRROR>(v);
     if constexpr (W >= 16) v += dpp<DPP_ROW_MIRROR>(v);
-    if constexpr (W >= 32) v += __shfl_xor(v, 16);
+    if constexpr (W >= 32) v = add_xor16(v);
+    if constexpr (W >= 64) v = add_xor32(v);
     return v;
 }
 
@@ -106,7 +156,8 @@ __device__ __forceinline__ float group_max(float v)
     v = fmaxf(v, dpp<DPP_QUAD_2301>(v));
     v = fmaxf(v, dpp<DPP_ROW_HMIRROR>(v));
     if constexpr (W >= 16) v = fmaxf(v, dpp<DPP_ROW_MIRROR>(v));
-    if constexpr (W >= 32) v = fmaxf(v, __shfl_xor(v, 16));
+    if constexpr (W >= 32) v = max_xor16(v);
+    if constexpr (W >= 64) v = max_xor32(v);
     return v;
 }
 

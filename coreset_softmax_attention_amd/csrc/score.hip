@@ -12,6 +12,7 @@
 // the ranking of Eq. (5) and cannot underflow.
 #include "device.hpp"
 #include "launch.hpp"
+#include "select.hpp"
 
 namespace csa {
 namespace {
@@ -279,30 +280,13 @@ __global__ void __launch_bounds__(kFusedWaves * 64) score_summary_fused_kernel(c
 
     if (G > 1) {
         for (int h = wave; h < G; h += NW) {
-            const float* row = lsm + h * nb;
-            float mx = kNegInf;
-            for (int i = lane; i < nb; i += 64) mx = fmaxf(mx, row[i]);
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-            float sum = 0.0f;
-            for (int i = lane; i < nb; i += 64) sum += exp2_((row[i] - mx) * kLog2e);
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
-            if (lane == 0) lse_h[h] = mx + logf(sum);
+            const float lse = head_lse(lsm + h * nb, nb, lane);
+            if (lane == 0) lse_h[h] = lse;
         }
         __syncthreads();
     }
     for (int i = threadIdx.x; i < nb; i += NW * 64) {
-        float v;
-        if (G == 1) {
-            v = lsm[i];
-        } else {
-            float mx = kNegInf;
-            for (int h = 0; h < G; ++h) mx = fmaxf(mx, lsm[h * nb + i] - lse_h[h]);
-            float sum = 0.0f;
-            for (int h = 0; h < G; ++h) sum += exp2_((lsm[h * nb + i] - lse_h[h] - mx) * kLog2e);
-            v = mx + logf(sum);
-        }
+        const float v = G == 1 ? lsm[i] : group_score<8>(lsm + i, nb, lse_h, G);
         p.scores[(size_t)pair * nb + i] = v;
     }
 }

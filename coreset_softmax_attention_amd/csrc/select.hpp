@@ -1,0 +1,238 @@
+// select.hpp -- wave-level pieces of block scoring and top-k selection shared
+// by the modular kernels and the fused decode step, so that both produce the
+// same bits.
+//
+// Group score (additive GQA score of "COBS: Cumulant Order Block Sparse
+// Attention", Eq. (5)): the mass that head h puts on block b is
+// exp(l_hb - LSE_h) with LSE_h the log-normaliser of head h over the blocks;
+// the group score of b is the log of its summed mass over the G heads of the
+// KV head, ln sum_h exp(l_hb - LSE_h), which orders the blocks like the summed
+// mass itself.  With one head per KV head the score is the block logit.
+//
+// Selection: the kk blocks with the largest scores, ties to the lower index,
+// reported in ascending index order.
+#pragma once
+
+#include "device.hpp"
+
+namespace csa {
+
+// Monotone map float -> uint32 (larger float -> larger key); -0 ties with +0.
+__device__ __forceinline__ uint32_t order_key(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u) u = 0;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Log-normaliser of one head's block logits row[0..nb) in LDS, by one wave;
+// every lane returns it.  Lane l takes the logits l, l + 64, ... in that order;
+// the loads of a chunk of CH per lane go out together (one LDS round trip per
+// chunk instead of one per logit).
+template <int CH = 8>
+__device__ __forceinline__ float head_lse(const float* row, int nb, int lane)
+{
+    auto load_chunk = [&](int base, float (&v)[CH]) {
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const int i = base + lane + 64 * j;
+            v[j] = row[i < nb ? i : 0];
+        }
+    };
+    float v[CH];
+    float mx = kNegInf, sum = 0.0f;
+    if (nb <= 64 * CH) {  // one chunk: both passes from registers
+        load_chunk(0, v);
+#pragma unroll
+        for (int j = 0; j < CH; ++j)
+            if (lane + 64 * j < nb) mx = fmaxf(mx, v[j]);
+        mx = group_max<64>(mx);
+#pragma unroll
+        for (int j = 0; j < CH; ++j)
+            if (lane + 64 * j < nb) sum += exp2_((v[j] - mx) * kLog2e);
+    } else {
+        for (int base = 0; base < nb; base += 64 * CH) {
+            load_chunk(base, v);
+#pragma unroll
+            for (int j = 0; j < CH; ++j)
+                if (base + lane + 64 * j < nb) mx = fmaxf(mx, v[j]);
+        }
+        mx = group_max<64>(mx);
+        for (int base = 0; base < nb; base += 64 * CH) {
+            load_chunk(base, v);
+#pragma unroll
+            for (int j = 0; j < CH; ++j)
+                if (base + lane + 64 * j < nb) sum += exp2_((v[j] - mx) * kLog2e);
+        }
+    }
+    sum = group_sum<64>(sum);
+    return mx + logf(sum);
+}
+
+// Group score of one block from its G <= MAXG head logits l[h * stride].
+template <int MAXG>
+__device__ __forceinline__ float group_score(const float* l, int stride, const float* lse_h, int G)
+{
+    float x[MAXG];
+#pragma unroll
+    for (int h = 0; h < MAXG; ++h) x[h] = l[(h < G ? h : 0) * stride] - lse_h[h < G ? h : 0];
+    float mx = kNegInf;
+#pragma unroll
+    for (int h = 0; h < MAXG; ++h)
+        if (h < G) mx = fmaxf(mx, x[h]);
+    float sum = 0.0f;
+#pragma unroll
+    for (int h = 0; h < MAXG; ++h)
+        if (h < G) sum += exp2_((x[h] - mx) * kLog2e);
+    return mx + logf(sum);
+}
+
+// Key (hi, lo) = (order_key(score), ~index): larger key = larger score, then
+// lower index.  Replaces (h, l) by the larger of itself and (oh, ol).
+__device__ __forceinline__ void key_max(uint32_t& h, uint32_t& l, uint32_t oh, uint32_t ol)
+{
+    const bool gt = oh > h || (oh == h && ol > l);
+    h = gt ? oh : h;
+    l = gt ? ol : l;
+}
+
+// Largest key of the wave, in every lane (DPP within 16-lane rows, then the
+// lane-swap instructions across rows).
+__device__ __forceinline__ void wave_key_max(uint32_t& h, uint32_t& l)
+{
+    key_max(h, l, dpp_u32<DPP_QUAD_1032>(h), dpp_u32<DPP_QUAD_1032>(l));
+    key_max(h, l, dpp_u32<DPP_QUAD_2301>(h), dpp_u32<DPP_QUAD_2301>(l));
+    key_max(h, l, dpp_u32<DPP_ROW_HMIRROR>(h), dpp_u32<DPP_ROW_HMIRROR>(l));
+    key_max(h, l, dpp_u32<DPP_ROW_MIRROR>(h), dpp_u32<DPP_ROW_MIRROR>(l));
+    LanePair ph = swap16(h), pl = swap16(l);
+    h = ph.a;
+    l = pl.a;
+    key_max(h, l, ph.b, pl.b);
+    ph = swap32(h);
+    pl = swap32(l);
+    h = ph.a;
+    l = pl.a;
+    key_max(h, l, ph.b, pl.b);
+}
+
+// Largest uint32 of the wave, in every lane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    v = max(v, dpp_u32<DPP_QUAD_1032>(v));
+    v = max(v, dpp_u32<DPP_QUAD_2301>(v));
+    v = max(v, dpp_u32<DPP_ROW_HMIRROR>(v));
+    v = max(v, dpp_u32<DPP_ROW_MIRROR>(v));
+    LanePair r = swap16(v);
+    v = max(r.a, r.b);
+    r = swap32(v);
+    return max(r.a, r.b);
+}
+
+// Number of lanes below this one whose bit is set in a wave-wide mask.
+__device__ __forceinline__ int lanes_below(uint64_t mask)
+{
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Top-kk (1 <= kk <= nb, kk <= 64, nb <= 64 * MAXPER) of the scores load(0..nb)
+// by one wave.  Block i belongs to lane i % 64 (slot i / 64), which keeps the
+// order keys of its blocks in registers.  At the end emit(r, i) is called, in
+// lane r < kk, with the r-th smallest selected index i (ascending order).
+// cand: 128 words of LDS owned by the wave.
+//
+// Candidates first: the kk-th largest of the 64 per-lane maximum keys is a
+// lower bound tau for the kk-th largest key overall (the kk largest lane maxima
+// are kk distinct blocks), so every selected block has key >= tau.  When at
+// most 64 blocks reach tau, they are gathered one per lane, in ascending index
+// order, and each is ranked against the others by (key, lower index); else
+// (many equal scores) the blocks are taken one round at a time.
+template <int MAXPER, typename Load, typename Emit>
+__device__ __forceinline__ void wave_topk(Load load, int nb, int kk, int lane, uint32_t* cand, Emit emit)
+{
+    uint32_t key[MAXPER];
+    uint32_t lmax = 0;
+#pragma unroll
+    for (int j = 0; j < MAXPER; ++j) {
+        const int i = lane + 64 * j;
+        const float f = load(i < nb ? i : 0);  // unconditional: the loads go out together
+        key[j] = i < nb ? order_key(f) : 0u;
+        lmax = max(lmax, key[j]);
+    }
+    // tau: the kk-th largest lane maximum, counting equal maxima separately
+    // (lanes without a block drop out at once; at least kk lanes hold one, so
+    // the loop ends within kk rounds)
+    bool live = lane < nb;
+    uint32_t tau = 0;  // stays 0 (every block a candidate) if the bound is not reached
+    for (int got = 0, round = 0; round < 64; ++round) {
+        const uint32_t mx = wave_max_u32(live ? lmax : 0u);
+        const uint64_t hit = __ballot(live && lmax == mx);
+        got += __popcll(hit);
+        if (got >= kk) {
+            tau = mx;
+            break;
+        }
+        if (live && lmax == mx) live = false;
+    }
+    uint64_t cmask[MAXPER];
+    int ncand = 0;
+#pragma unroll
+    for (int j = 0; j < MAXPER; ++j) {
+        cmask[j] = __ballot(lane + 64 * j < nb && key[j] >= tau);
+        ncand += __popcll(cmask[j]);
+    }
+    if (ncand <= 64) {
+        int base = 0;
+#pragma unroll
+        for (int j = 0; j < MAXPER; ++j) {
+            if ((cmask[j] >> lane) & 1u) {
+                const int pos = base + lanes_below(cmask[j]);
+                cand[pos] = key[j];
+                cand[64 + pos] = (uint32_t)(lane + 64 * j);
+            }
+            base += __popcll(cmask[j]);
+        }
+        wave_lds_fence();
+        const bool mine = lane < ncand;
+        const uint32_t ck = mine ? cand[lane] : 0u, ci = mine ? cand[64 + lane] : 0u;
+        int rank = 0;  // candidates ahead of this one: larger key, or equal key and lower index
+        for (int q = 0; q < ncand; ++q) {
+            const uint32_t qk = (uint32_t)__builtin_amdgcn_readlane((int)ck, q);
+            const uint32_t qi = (uint32_t)__builtin_amdgcn_readlane((int)ci, q);
+            rank += (qk > ck || (qk == ck && qi < ci)) ? 1 : 0;
+        }
+        const bool take = mine && rank < kk;
+        const uint64_t tm = __ballot(take);
+        if (take) emit(lanes_below(tm), (int)ci);
+        wave_lds_fence();  // cand is reused by the next call
+        return;
+    }
+    // fallback: kk rounds, each taking the wave's largest (key, lower index)
+    uint32_t taken = 0;
+    auto lane_best = [&](uint32_t& bh, uint32_t& bl) {
+        bh = 0;
+        bl = 0;  // below every real key: real keys have a nonzero low word
+#pragma unroll
+        for (int j = 0; j < MAXPER; ++j) {
+            const int i = lane + 64 * j;
+            if (i < nb && !((taken >> j) & 1u)) key_max(bh, bl, key[j], ~(uint32_t)i);
+        }
+    };
+    uint32_t bh, bl;
+    lane_best(bh, bl);
+    int got = 0;  // lane r keeps the r-th block taken
+    for (int it = 0; it < kk; ++it) {
+        uint32_t h = bh, l = bl;
+        wave_key_max(h, l);
+        const int widx = (int)~l;
+        if (lane == it) got = widx;
+        if ((widx & 63) == lane) {
+            taken |= 1u << (widx >> 6);
+            lane_best(bh, bl);
+        }
+    }
+    int rank = 0;  // place among the taken blocks in ascending order
+    for (int j = 0; j < kk; ++j) rank += __builtin_amdgcn_readlane(got, j) < got ? 1 : 0;
+    if (lane < kk) emit(rank, got);
+}
+
+}  // namespace csa

@@ -22,13 +22,14 @@
 #include "attn_engine.hpp"
 #include "device.hpp"
 #include "launch.hpp"
+#include "select.hpp"
 
 namespace csa {
 namespace {
 
 constexpr int kStepWaves = 8;
 constexpr int kStepMaxK = 32;
-constexpr int kStepMaxBlocks = 2048;     // top-k by one wave: 32 keys per lane
+constexpr int kStepMaxBlocks = 2048;     // top-k by one wave: up to 32 scores per lane
 constexpr int kStepMaxLdsBytes = 65536;  // dynamic LDS: logits, scores, bitmap
 
 struct StepParams {
@@ -49,25 +50,6 @@ struct StepParams {
     float scale, ln_L, ln_last, scale_log2;
 };
 
-__device__ __forceinline__ uint32_t order_key(float f)
-{
-    uint32_t u = __float_as_uint(f);
-    if (u == 0x80000000u) u = 0;  // -0 ties with +0
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
-{
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        const uint32_t lo = __shfl_xor((uint32_t)v, off);
-        const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off);
-        const uint64_t o = ((uint64_t)hi << 32) | lo;
-        v = o > v ? o : v;
-    }
-    return v;
-}
-
 template <int D, int HG>
 __global__ void __launch_bounds__(kStepWaves * 64) decode_step_kernel(const StepParams p)
 {
@@ -78,6 +60,7 @@ __global__ void __launch_bounds__(kStepWaves * 64) decode_step_kernel(const Step
     __shared__ typename E::Smem sm;
     __shared__ float lse_h[8];
     __shared__ int32_t sel_sm[kStepMaxK];
+    __shared__ uint32_t cand_sm[128];  // top-k candidates
 
     const int LS = p.lstride, G = p.G, nb = p.nb;
     float* lsm = dyn;                                              // [G][LS] block logits (natural log)
@@ -96,11 +79,6 @@ __global__ void __launch_bounds__(kStepWaves * 64) decode_step_kernel(const Step
     const __amdgpu_buffer_rsrc_t Vs =
         buffer_rsrc(p.proxies ? p.Vbar + (size_t)pair * nb * RB : p.V, p.proxies ? (uint32_t)nb * RB : 0u);
 
-    // The first attention tile of the wave is a proxy tile when the wave's index is
-    // below the proxy tile count: its mean values do not depend on the selection,
-    // so their loads go out now and overlap the scoring phases (its selected
-    // blocks are masked once the selection is known).
-    typename E::Tile A, B;
     // Tile orders are rotated by a per-workgroup offset, so that workgroups
     // running side by side do not walk the same address offsets at the same
     // time (their heads' arrays start at similarly aligned addresses).
@@ -113,15 +91,34 @@ __global__ void __launch_bounds__(kStepWaves * 64) decode_step_kernel(const Step
     const int rotP = nP ? (int)((hsh >> 8) % (uint32_t)nP) : 0;
     const int rotC = nC ? (int)((hsh >> 16) % (uint32_t)nC) : 0;
     auto row0 = [&](int t) { return t < nP ? (t + rotP) % nP * TR : p.wbeg + (t - nP + rotC) % nC * TR; };
-    const int first = wave < nT ? row0(wave) : p.rows;
-    const bool prefetched = wave < nP;
-    if (prefetched) {
+    // this wave's tiles are t = wave + j NW: first Pw proxy tiles, then cache tiles
+    const int Pw = wave < nP ? (nP - wave + NW - 1) / NW : 0;
+    const int Tw = wave < nT ? (nT - wave + NW - 1) / NW : 0;
+    auto tile_of = [&](int jj) { return wave + jj * NW; };
+
+    // Proxy tiles hold only mean values (their logits are the block logits of
+    // phase 1) and do not depend on the selection: the wave's first two are
+    // loaded now and overlap the scoring phases; their selected blocks are
+    // masked once the selection is known.
+    uint4 VA[E::NVI], VB[E::NVI];
+    auto set_proxy_rows = [&](int tb, int jj, bool masked) {
         if (lane < TR) {
-            const int r = first + lane;
-            eng.set_row(0, lane, (uint32_t)r, r < p.pend ? 0.0f : kNegInf);
+            const int r = row0(tile_of(jj)) + lane;
+            float lw = r < p.pend ? 0.0f : kNegInf;  // the logit itself comes from LDS
+            if (masked && r < p.pend && ((bits[r >> 5] >> (r & 31)) & 1u)) lw = kNegInf;
+            eng.set_row(tb, lane, (uint32_t)(r < p.pend ? r : 0), lw);
         }
-        eng.issue(A, 0, Ks, Vs, false);
-    }
+    };
+    auto issue_first_proxies = [&]() {
+        if (Pw > 0) {
+            set_proxy_rows(0, 0, false);
+            eng.issue_values(VA, 0, Vs);
+        }
+        if (Pw > 1) {
+            set_proxy_rows(1, 1, false);
+            eng.issue_values(VB, 1, Vs);
+        }
+    };
 
     // ---- phase 1: block logits of every head -> LDS ---------------------------
     auto logits_to_lds = [&](int base, const uint4 (&ak)[2][KS]) {
@@ -150,6 +147,9 @@ __global__ void __launch_bounds__(kStepWaves * 64) decode_step_kernel(const Step
             for (int s = 0; s < KS; ++s) ak[rb][s] = buffer_ld16(Ks, off + s * 64);
         }
     };
+    // The mean keys decide the selection: they have the memory system to
+    // themselves.  The wave's first two proxy value tiles go out once its keys
+    // have arrived, and stream in while the selection is made.
     for (int t = wave; t < nK; t += 2 * NW) {  // two tiles in flight
         uint4 k0[2][KS], k1[2][KS];
         const int b0 = (t + rotK) % nK * TR, b1 = (t + NW + rotK) % nK * TR;
@@ -159,89 +159,44 @@ __global__ void __launch_bounds__(kStepWaves * 64) decode_step_kernel(const Step
         logits_to_lds(b0, k0);
         if (two) logits_to_lds(b1, k1);
     }
+    issue_first_proxies();
     __syncthreads();
 
     // ---- phase 2: group score and top-k ----------------------------------------
     if (G > 1) {
         if (wave < G) {
-            const float* row = lsm + wave * LS;
-            float mx = kNegInf;
-            for (int i = lane; i < nb; i += 64) mx = fmaxf(mx, row[i]);
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-            float sum = 0.0f;
-            for (int i = lane; i < nb; i += 64) sum += exp2_((row[i] - mx) * kLog2e);
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
-            if (lane == 0) lse_h[wave] = mx + logf(sum);
+            const float lse = head_lse(lsm + wave * LS, nb, lane);
+            if (lane == 0) lse_h[wave] = lse;
         }
         __syncthreads();
     }
     for (int i = threadIdx.x; i < nb; i += NW * 64) {
-        float v;
-        if (G == 1) {
-            v = lsm[i];
-        } else {
-            float mx = kNegInf;
-            for (int h = 0; h < G; ++h) mx = fmaxf(mx, lsm[h * LS + i] - lse_h[h]);
-            float sum = 0.0f;
-            for (int h = 0; h < G; ++h) sum += exp2_((lsm[h * LS + i] - lse_h[h] - mx) * kLog2e);
-            v = mx + logf(sum);
-        }
+        const float v = G == 1 ? lsm[i] : group_score<HG>(lsm + i, LS, lse_h, G);
         ssm[i] = v;
         if (p.scores) p.scores[(size_t)pair * nb + i] = v;
     }
     __syncthreads();
     const int kk = p.k;  // <= min(32, nb)
     if (wave == 0 && kk > 0) {
-        // lane owns blocks [lane * per, lane * per + per); larger key = higher score, then lower index
-        const int per = (nb + 63) >> 6;
-        uint64_t key[kStepMaxK];
-#pragma unroll
-        for (int i = 0; i < kStepMaxK; ++i) {
-            const int idx = lane * per + i;
-            key[i] = (i < per && idx < nb) ? ((uint64_t)order_key(ssm[idx]) << 32) | (uint32_t)~(uint32_t)idx : 0;
-        }
-        uint32_t taken = 0;
-        for (int it = 0; it < kk; ++it) {
-            uint64_t best = 0;
-#pragma unroll
-            for (int i = 0; i < kStepMaxK; ++i)
-                if (!((taken >> i) & 1u) && key[i] > best) best = key[i];
-            best = wave_max_u64(best);
-            const uint32_t widx = ~(uint32_t)best;
-            if ((int)(widx / per) == lane) taken |= 1u << (widx % per);
-        }
-        const int cnt = __popc(taken);
-        int incl = cnt;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int t = __shfl_up(incl, off);
-            if (lane >= off) incl += t;
-        }
-        int pos = incl - cnt;
-#pragma unroll
-        for (int i = 0; i < kStepMaxK; ++i) {
-            if ((taken >> i) & 1u) {
-                const int idx = lane * per + i;
-                sel_sm[pos] = idx;
-                if (p.sel) p.sel[(size_t)pair * kk + pos] = idx;
-                atomicOr(&bits[idx >> 5], 1u << (idx & 31));
-                ++pos;
-            }
-        }
+        auto load = [&](int i) { return ssm[i]; };
+        auto emit = [&](int r, int idx) {
+            sel_sm[r] = idx;
+            if (p.sel) p.sel[(size_t)pair * kk + r] = idx;
+            atomicOr(&bits[idx >> 5], 1u << (idx & 31));
+        };
+        if (nb <= 8 * 64)
+            wave_topk<8>(load, nb, kk, lane, cand_sm, emit);
+        else
+            wave_topk<kStepMaxBlocks / 64>(load, nb, kk, lane, cand_sm, emit);
     }
     __syncthreads();
 
     // ---- phase 3: attention ------------------------------------------------------
-    auto resolve = [&](int r, uint32_t& row, float& lw) {
+    auto resolve_cache = [&](int r, uint32_t& row, float& lw) {
         row = 0;
         lw = kNegInf;
         if (r >= p.rows) return;
-        if (r < p.pend) {
-            row = (uint32_t)r;
-            if (!((bits[r >> 5] >> (r & 31)) & 1u)) lw = 0.0f;  // the logit itself comes from LDS
-        } else if (r >= p.wbeg && r < p.wbeg + p.m) {
+        if (r >= p.wbeg && r < p.wbeg + p.m) {
             const int t = r - p.wbeg;
             const int tok = p.tok_idx[(size_t)pair * p.m + t];
             if (tok >= 0 && tok < p.n) {
@@ -258,47 +213,62 @@ __global__ void __launch_bounds__(kStepWaves * 64) decode_step_kernel(const Step
             }
         }
     };
-    auto issue_any = [&](int base, typename E::Tile& t, int tb) {
+    auto issue_cache = [&](int jj, typename E::Tile& t, int tb) {
         if (lane < TR) {
             uint32_t row;
             float lw;
-            resolve(base + lane, row, lw);
+            resolve_cache(row0(tile_of(jj)) + lane, row, lw);
             eng.set_row(tb, lane, row, lw);
         }
-        if (base < p.wbeg)
-            eng.issue(t, tb, Ks, Vs, false);  // proxy tile: values only
-        else
-            eng.issue(t, tb, Kc, Vc, true);
+        eng.issue(t, tb, Kc, Vc, true);
     };
-    auto compute = [&](int base, const typename E::Tile& t, int tb) {
+    auto proxy_tile = [&](int jj, const uint4 (&vr)[E::NVI], int tb) {
         float x[8];
-        if (base < p.wbeg)
-            eng.logits_lds(tb, lsm + (n16 < G ? n16 : G - 1) * LS + base, x);
-        else
-            eng.logits_mfma(t, tb, p.scale_log2, x);
+        eng.logits_lds(tb, lsm + (n16 < G ? n16 : G - 1) * LS + row0(tile_of(jj)), x);
+        eng.softmax(x);
+        eng.accumulate_values(vr);
+    };
+    auto cache_logits = [&](const typename E::Tile& t, int tb) {
+        float x[8];
+        eng.logits_mfma(t, tb, p.scale_log2, x);
         eng.softmax(x);
     };
 
-    if (prefetched && lane < TR) {  // mask the selected blocks of the prefetched tile
-        const int r = first + lane;
-        if (r < p.pend && ((bits[r >> 5] >> (r & 31)) & 1u)) sm.tab_lw[0][wave][lane] = kNegInf;
-    }
-    int t = wave;
-    if (t < nT) {
-        if (!prefetched) issue_any(first, A, 0);
-        for (;;) {
-            const int t1 = t + NW;
-            compute(row0(t), A, 0);
-            if (t1 < nT) issue_any(row0(t1), B, 1);
-            eng.accumulate(A);
-            if (t1 >= nT) break;
-            const int t2 = t1 + NW;
-            compute(row0(t1), B, 1);
-            if (t2 < nT) issue_any(row0(t2), A, 0);
-            eng.accumulate(B);
-            if (t2 >= nT) break;
-            t = t2;
+    // The selection is known: mask the selected blocks in the prefetched proxy
+    // tiles and finish the proxy tiles (two value tiles in flight), then stream
+    // the cache tiles (key and value tiles, one and a half in flight).  Issuing
+    // the first cache tile before the proxy tiles would hold three tiles of
+    // registers at once and spill.
+    if (Pw > 0) set_proxy_rows(0, 0, true);
+    if (Pw > 1) set_proxy_rows(1, 1, true);
+    typename E::Tile CA, CB;
+    const bool any_cache = Tw > Pw;
+    for (int jj = 0; jj < Pw; jj += 2) {
+        proxy_tile(jj, VA, 0);
+        if (jj + 2 < Pw) {
+            set_proxy_rows(0, jj + 2, true);
+            eng.issue_values(VA, 0, Vs);
         }
+        if (jj + 1 < Pw) {
+            proxy_tile(jj + 1, VB, 1);
+            if (jj + 3 < Pw) {
+                set_proxy_rows(1, jj + 3, true);
+                eng.issue_values(VB, 1, Vs);
+            }
+        }
+    }
+    if (any_cache) issue_cache(Pw, CA, 2);
+    // cache tiles (weighted and exact rows): keys and values; the next tile's
+    // loads go out once this tile's keys are consumed (one and a half tiles of
+    // registers in flight)
+    for (int jj = Pw; jj < Tw; jj += 2) {
+        cache_logits(CA, 2);
+        if (jj + 1 < Tw) issue_cache(jj + 1, CB, 3);
+        eng.accumulate(CA);
+        if (jj + 1 >= Tw) break;
+        cache_logits(CB, 3);
+        if (jj + 2 < Tw) issue_cache(jj + 2, CA, 2);
+        eng.accumulate(CB);
     }
     eng.finish(G, p.out + ((size_t)b * p.Hq + h0) * D, p.lse ? p.lse + (size_t)b * p.Hq + h0 : nullptr, nullptr);
 }

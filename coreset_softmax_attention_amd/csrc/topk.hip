@@ -19,18 +19,12 @@
 // lanes writes them in index order.
 #include "device.hpp"
 #include "launch.hpp"
+#include "select.hpp"
 
 namespace csa {
 namespace {
 
 constexpr int kThreads = 256;
-
-__device__ __forceinline__ uint32_t order_key(float f)
-{
-    uint32_t u = __float_as_uint(f);
-    if (u == 0x80000000u) u = 0;  // -0 ties with +0
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
 
 // Exclusive prefix sum over the workgroup (256 threads); also returns the total.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* total, int* sm /* >= 4 ints */)
@@ -140,54 +134,17 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(const float* scores, int
 constexpr int kWaveTopkMaxK = 32;
 constexpr int kWaveTopkMaxPer = 32;  // keys per lane
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
-{
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        const uint32_t lo = __shfl_xor((uint32_t)v, off);
-        const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off);
-        const uint64_t o = ((uint64_t)hi << 32) | lo;
-        v = o > v ? o : v;
-    }
-    return v;
-}
-
+// One wave per row (k <= 32, nb <= 64 * PER).
 template <int PER>
 __global__ void __launch_bounds__(256) topk_wave_kernel(const float* scores, int32_t* sel, int rows, int nb, int k)
 {
-    const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    __shared__ uint32_t cand[4][128];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int row = blockIdx.x * 4 + wave;
     if (row >= rows) return;  // whole wave; no workgroup barrier below
     const float* s = scores + (size_t)row * nb;
-    uint64_t key[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int idx = lane * PER + i;
-        key[i] = idx < nb ? ((uint64_t)order_key(s[idx]) << 32) | (uint32_t)~(uint32_t)idx : 0;
-    }
-    uint32_t taken = 0;
-    for (int it = 0; it < k; ++it) {
-        uint64_t best = 0;
-#pragma unroll
-        for (int i = 0; i < PER; ++i)
-            if (!((taken >> i) & 1u) && key[i] > best) best = key[i];
-        best = wave_max_u64(best);
-        const uint32_t widx = ~(uint32_t)best;
-        if ((int)(widx / PER) == lane) taken |= 1u << (widx % PER);
-    }
-    // write the taken indices in ascending order
-    const int cnt = __popc(taken);
-    int incl = cnt;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int t = __shfl_up(incl, off);
-        if (lane >= off) incl += t;
-    }
-    int pos = incl - cnt;
     int32_t* out = sel + (size_t)row * k;
-#pragma unroll
-    for (int i = 0; i < PER; ++i)
-        if ((taken >> i) & 1u) out[pos++] = lane * PER + i;
+    wave_topk<PER>([&](int i) { return s[i]; }, nb, k, lane, cand[wave], [&](int r, int idx) { out[r] = idx; });
 }
 
 }  // namespace
