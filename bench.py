@@ -49,10 +49,85 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU time budget of the oracle baseline")
     ap.add_argument("--no-dense", action="store_true")
-    ap.add_argument("--traffic", default=None, help="JSON file with measured HBM bytes per attention launch")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON file with measured HBM bytes per launch (default: profiles/traffic_<workload>.json)")
+    ap.add_argument("--counters", nargs=4, default=None,
+                    metavar=("FETCH_DB", "WRITE_DB", "COPY_FETCH_DB", "COPY_WRITE_DB"),
+                    help="only turn four rocprofv3 --pmc result databases (FETCH_SIZE and WRITE_SIZE of a "
+                         "run of this script, then of --copy-probe) into the traffic file given by --traffic")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 8 times (calibrates memory counters)")
     return ap.parse_args()
+
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+COPY_PROBE_BYTES = 1 << 30
+# kernels whose HBM traffic is reported, by the name rocprofv3 records
+TRAFFIC_KERNELS = {"decode_step": "decode_step_kernel", "sparse_decode_attn": "attn_mfma_kernel"}
+
+
+def source_hash():
+    """Hash of the HIP sources: a traffic file measured on other sources is stale."""
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(HERE, "coreset_softmax_attention_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.hpp"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def default_traffic_path(workload):
+    return os.path.join(HERE, "profiles", f"traffic_{workload}.json")
+
+
+def counters_to_traffic(fetch_db, write_db, copy_fetch_db, copy_write_db, out_path, workload):
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of each reported kernel, scaled by
+    what the same counters read for a plain copy of COPY_PROBE_BYTES bytes."""
+    import sqlite3
+
+    def per_dispatch(db, counter, name_part):
+        con = sqlite3.connect(db)
+        rows = con.execute("select name, counter_value from pmc_events where counter_name = ?", (counter,)).fetchall()
+        con.close()
+        vals = [v for n, v in rows if name_part in n]
+        if not vals:
+            raise SystemExit(f"{db}: no {counter} rows for a kernel named like {name_part!r}")
+        return sum(vals) / len(vals), len(vals)
+
+    copy_fetch, _ = per_dispatch(copy_fetch_db, "FETCH_SIZE", "copyBuffer")
+    copy_write, _ = per_dispatch(copy_write_db, "WRITE_SIZE", "copyBuffer")
+    fetch_scale = COPY_PROBE_BYTES / (copy_fetch * 1024.0)
+    write_scale = COPY_PROBE_BYTES / (copy_write * 1024.0)
+    kernels = {}
+    for key, name in TRAFFIC_KERNELS.items():
+        f, nf = per_dispatch(fetch_db, "FETCH_SIZE", name)
+        w, nw = per_dispatch(write_db, "WRITE_SIZE", name)
+        kernels[key] = {"kernel": name, "fetch_kib": f, "write_kib": w, "dispatches": [nf, nw],
+                        "bytes": f * 1024.0 * fetch_scale + w * 1024.0 * write_scale}
+    rec = {"workload": workload, "source_hash": source_hash(),
+           "copy_probe": {"bytes": COPY_PROBE_BYTES, "fetch_kib": copy_fetch, "write_kib": copy_write,
+                          "fetch_scale": fetch_scale, "write_scale": write_scale},
+           "kernels": kernels,
+           "bytes_per_launch": {k: v["bytes"] for k, v in kernels.items()}}
+    with open(out_path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(rec["bytes_per_launch"]))
+
+
+def load_traffic(path):
+    """Measured bytes per launch, or None when absent or measured on other kernel sources."""
+    if not path or not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_hash") != source_hash():
+        print(f"[bench] {path} was measured on other kernel sources: traffic not reported", file=sys.stderr)
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def copy_probe(nbytes):
@@ -103,6 +178,12 @@ def main():
 
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.counters:
+        from coreset_softmax_attention_amd import workloads as W
+
+        name = args.workload or W.HEADLINE
+        counters_to_traffic(*args.counters, args.traffic or default_traffic_path(name), name)
         return
 
     import torch
@@ -227,9 +308,7 @@ def main():
     step_achieved = (srd + swr) / (t_step * 1e-3) / 1e9
     rd, wr = algorithmic_bytes(w, m)
     achieved = (rd + wr) / (attn_ms * 1e-3) / 1e9
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        traffic = json.load(open(args.traffic)).get("bytes_per_launch")
+    traffic = load_traffic(args.traffic or default_traffic_path(w.name))
 
     dense_ms = None
     if not args.no_dense:
