@@ -139,7 +139,12 @@ int block_score(const csa_shape* shape, csa_score_mode mode, const void* q, cons
         return fail(CSA_ERR_INVALID_ARG, "block_score: misaligned tensor");
     if (int rc = check_ws(block_score_ws(d), ws, ws_bytes)) return rc;
     if (mode == CSA_SCORE_SUMMARY && csa::fused_summary_score_ok(d)) {
-        const hipError_t e = csa::launch_score_summary_fused(d, q, keys, scores, stream);
+        // one workgroup per KV head when there are enough of them, else the split kernels
+        const hipError_t e =
+            d.pairs() >= csa::kFusedStepMinPairs
+                ? csa::launch_score_summary_fused(d, q, keys, scores, stream)
+                : csa::launch_score_summary_split(d, q, keys, d.G == 1 ? scores : static_cast<float*>(ws), scores,
+                                                  nullptr, 0, stream);
         return e == hipSuccess ? CSA_OK : hip_fail(e, "block_score");
     }
     float* dst = d.G == 1 ? scores : static_cast<float*>(ws);
@@ -147,7 +152,8 @@ int block_score(const csa_shape* shape, csa_score_mode mode, const void* q, cons
                                              : csa::launch_block_logits_exact(d, q, keys, dst, stream);
     if (e != hipSuccess) return hip_fail(e, "block_score");
     if (d.G > 1) {
-        e = csa::launch_group_score(d, dst, scores, stream);
+        e = csa::score_finish_ok(d) ? csa::launch_score_finish(d, dst, scores, nullptr, 0, stream)
+                                    : csa::launch_group_score(d, dst, scores, stream);
         if (e != hipSuccess) return hip_fail(e, "block_score (group score)");
     }
     return CSA_OK;
@@ -253,9 +259,23 @@ int selective_decode_step(const csa_shape* shape, csa_score_mode mode, const voi
     int32_t* sl = sel ? sel : reinterpret_cast<int32_t*>(base + w.scores);
     void* sws = base + w.scores + w.sel;
     void* aws = base + w.scores + w.sel + w.score_ws;
-    if (int rc = block_score(shape, mode, q, mode == CSA_SCORE_SUMMARY ? Kbar : K, sc, sws, w.score_ws, stream))
-        return rc;
-    if (int rc = topk_select(d.pairs(), d.nb, kk, sc, sl, stream)) return rc;
+    if (mode == CSA_SCORE_SUMMARY && csa::fused_summary_score_ok(d) && d.pairs() < csa::kFusedStepMinPairs &&
+        csa::split_select_ok(d, kk)) {
+        // scores and selection from the split kernels (the top-k rides on the group-score kernel)
+        const hipError_t e = csa::launch_score_summary_split(d, q, Kbar, d.G == 1 ? sc : static_cast<float*>(sws),
+                                                             sc, sl, kk, stream);
+        if (e != hipSuccess) return hip_fail(e, "selective_decode_step (score)");
+    } else if (mode == CSA_SCORE_EXACT_MASS && d.G > 1 && csa::score_finish_ok(d) && csa::split_select_ok(d, kk)) {
+        // exact masses, then group scores and selection in one kernel
+        float* lg = static_cast<float*>(sws);
+        hipError_t e = csa::launch_block_logits_exact(d, q, K, lg, stream);
+        if (e == hipSuccess) e = csa::launch_score_finish(d, lg, sc, sl, kk, stream);
+        if (e != hipSuccess) return hip_fail(e, "selective_decode_step (score)");
+    } else {
+        if (int rc = block_score(shape, mode, q, mode == CSA_SCORE_SUMMARY ? Kbar : K, sc, sws, w.score_ws, stream))
+            return rc;
+        if (int rc = topk_select(d.pairs(), d.nb, kk, sc, sl, stream)) return rc;
+    }
     return sparse_decode_attn(shape, q, K, V, Kbar, Vbar, kk > 0 ? sl : nullptr, kk, tok_idx, tok_logw, m,
                               proxy_mode, out, lse, aws, w.attn_ws, stream);
 }

@@ -475,39 +475,60 @@ __global__ void __launch_bounds__(NW * 64) attn_mfma_kernel(const AttnParams p)
     eng.finish(nh, p.out + ((size_t)b * p.Hq + h0) * D, p.lse ? p.lse + (size_t)b * p.Hq + h0 : nullptr, part);
 }
 
-// Merge the per-split states of a KV head in split order.
+// Merge the per-split states of one query head, in split order: one workgroup
+// per (KV head, head), one thread per output element.  The states of a chunk of
+// splits are loaded together, so the merge costs a few memory round trips
+// rather than one per split.
 template <int D>
-__global__ void __launch_bounds__(256) attn_merge_kernel(const float* part, int splits, int G, int Hq, int Hkv,
-                                                         float* out, float* lse)
+__global__ void __launch_bounds__(D) attn_merge_kernel(const float* part, int splits, int G, int Hq, int Hkv,
+                                                       float* out, float* lse)
 {
-    const int pair = blockIdx.x;
+    constexpr int CH = 8;
+    const int pair = blockIdx.x / G, g = blockIdx.x - pair * G;
     const int b = pair / Hkv, j = pair - b * Hkv;
-    for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
-        const int g = idx / D, e = idx - g * D;
-        const float* st = part + ((size_t)pair * splits * G + g) * (D + 2);
-        const size_t stride = (size_t)G * (D + 2);
-        float M = kNegInf;
-        for (int s = 0; s < splits; ++s) M = fmaxf(M, st[s * stride]);
-        float Ls = 0.0f, A = 0.0f;
-        for (int s = 0; s < splits; ++s) {
-            const float a = rescale(st[s * stride], M);
-            Ls += st[s * stride + 1] * a;
-            A += st[s * stride + 2 + e] * a;
-        }
-        const int h = j * G + g;
-        out[((size_t)b * Hq + h) * D + e] = A / Ls;
-        if (e == 0 && lse) lse[(size_t)b * Hq + h] = (M + log2f(Ls)) * kLn2;
+    const int e = threadIdx.x;
+    const size_t stride = (size_t)G * (D + 2);
+    const float* st = part + ((size_t)pair * splits * G + g) * (D + 2);
+    float M = kNegInf;
+    for (int s0 = 0; s0 < splits; s0 += CH) {
+        float m[CH];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) m[c] = s0 + c < splits ? st[(s0 + c) * stride] : kNegInf;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) M = fmaxf(M, m[c]);
     }
+    float Ls = 0.0f, A = 0.0f;
+    for (int s0 = 0; s0 < splits; s0 += CH) {
+        float m[CH], l[CH], a[CH];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const bool in = s0 + c < splits;
+            const float* sc = st + (in ? s0 + c : 0) * stride;
+            m[c] = in ? sc[0] : kNegInf;
+            l[c] = sc[1];
+            a[c] = sc[2 + e];
+        }
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            if (s0 + c < splits) {
+                const float w = rescale(m[c], M);
+                Ls += l[c] * w;
+                A += a[c] * w;
+            }
+        }
+    }
+    const int h = j * G + g;
+    out[((size_t)b * Hq + h) * D + e] = A / Ls;
+    if (e == 0 && lse) lse[(size_t)b * Hq + h] = (M + log2f(Ls)) * kLn2;
 }
 
 hipError_t launch_merge(const AttnParams& p, int D, int pairs, hipStream_t st)
 {
+    const dim3 grid((unsigned)(pairs * p.G));
     if (D == 128)
-        attn_merge_kernel<128><<<dim3((unsigned)pairs), dim3(256), 0, st>>>(p.part, p.splits, p.G, p.Hq, p.Hkv,
-                                                                            p.out, p.lse);
+        attn_merge_kernel<128><<<grid, dim3(128), 0, st>>>(p.part, p.splits, p.G, p.Hq, p.Hkv, p.out, p.lse);
     else
-        attn_merge_kernel<64><<<dim3((unsigned)pairs), dim3(256), 0, st>>>(p.part, p.splits, p.G, p.Hq, p.Hkv,
-                                                                           p.out, p.lse);
+        attn_merge_kernel<64><<<grid, dim3(64), 0, st>>>(p.part, p.splits, p.G, p.Hq, p.Hkv, p.out, p.lse);
     return hipGetLastError();
 }
 

@@ -33,6 +33,17 @@ hipError_t launch_group_score(const Dims& s, const float* logits, float* scores,
 // (one workgroup per KV head); available when fused_summary_score_ok().
 bool fused_summary_score_ok(const Dims& s);
 hipError_t launch_score_summary_fused(const Dims& s, const void* q, const void* Kbar, float* scores, hipStream_t st);
+// The same in two kernels for few KV heads: logits over (KV head, tile chunk)
+// workgroups into `logits` ([B, Hq, nb]; may be `scores` when G == 1), then one
+// workgroup per KV head for the group scores (to `scores`, may be null) and,
+// when k > 0 (split_select_ok), the top-k to `sel`.
+bool split_select_ok(const Dims& s, int k);
+// Group scores (and the top-k when k > 0) from per-head logits [B, Hq, nb], one
+// workgroup per KV head with the logits in LDS; when score_finish_ok().
+bool score_finish_ok(const Dims& s);
+hipError_t launch_score_finish(const Dims& s, const float* logits, float* scores, int32_t* sel, int k, hipStream_t st);
+hipError_t launch_score_summary_split(const Dims& s, const void* q, const void* Kbar, float* logits, float* scores,
+                                      int32_t* sel, int k, hipStream_t st);
 
 // ---- top-k -----------------------------------------------------------------
 hipError_t launch_topk(int rows, int nb, int k, const float* scores, int32_t* sel, hipStream_t st);

@@ -180,6 +180,98 @@ __global__ void __launch_bounds__(kNW * 64) logits_exact_kernel(const LogitParam
     }
 }
 
+// Exact-mass logits on the matrix cores (bfloat16, G <= 16, L a multiple of
+// 32): ln m_{h,b} = log-sum-exp over the block's tokens of scale * q_h . K_i.
+// A wave streams the 32-token key tiles of its blocks (two tiles in flight),
+// q K^T of a tile is two 16x16x32 MFMA chains (tokens x heads), and each
+// output lane keeps an online (max, sum) for its head over its rows; at the
+// end of a block the four row groups of a head are merged with lane swaps.
+constexpr int kExactWaves = 4;
+
+template <int D>
+__global__ void __launch_bounds__(kExactWaves * 64) logits_exact_mfma_kernel(const LogitParams p)
+{
+    constexpr int RB = D * 2, KS = D / 32;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n16 = lane & 15, g16 = lane >> 4;
+    const int pair = blockIdx.x / p.chunks, chunk = blockIdx.x - pair * p.chunks;
+    const int b = pair / p.Hkv, j = pair - b * p.Hkv;
+    // this wave's blocks: a contiguous share of the chunk's
+    const int blk0 = chunk * p.items_per_wg, blk1 = min(p.nb, blk0 + p.items_per_wg);
+    const int per_wave = (blk1 - blk0 + kExactWaves - 1) / kExactWaves;
+    const int wb0 = blk0 + wave * per_wave, wb1 = min(blk1, wb0 + per_wave);
+    if (wb0 >= wb1) return;  // whole wave; no barrier in this kernel
+    const int tpb = p.L / 32;  // tiles per block
+    const int t0 = wb0 * tpb, t1 = wb1 * tpb;
+
+    bf16x8_t bq[KS];
+    load_q_operand<D>(p.q + ((size_t)b * p.Hq + (size_t)j * p.G) * RB, p.G, lane, bq);
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(p.keys + (size_t)pair * p.n * RB, (uint32_t)p.n * RB);
+
+    auto load = [&](int t, uint4 (&ak)[2][KS]) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            const uint32_t off = (uint32_t)(t * 32 + rb * 16 + n16) * RB + g16 * 16;  // past n: zeros
+#pragma unroll
+            for (int s = 0; s < KS; ++s) ak[rb][s] = buffer_ld16(kr, off + s * 64);
+        }
+    };
+    float m_run = kNegInf, l_run = 0.0f;  // this lane's head n16, its rows of the current block
+    auto consume = [&](int t, const uint4 (&ak)[2][KS]) {
+        f32x4_t c[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+                c[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ak[rb][s]), bq[s], c[rb], 0,
+                                                                0, 0);
+        float x[8];
+        float mx = m_run;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = t * 32 + rb * 16 + 4 * g16 + i;
+                x[rb * 4 + i] = row < p.n ? c[rb][i] * p.scale_log2 : kNegInf;
+                mx = fmaxf(mx, x[rb * 4 + i]);
+            }
+        float acc = l_run * rescale(m_run, mx);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc += x[e] == kNegInf ? 0.0f : exp2_(x[e] - mx);
+        m_run = mx;
+        l_run = acc;
+        if ((t + 1) % tpb == 0) {  // block complete: merge the four row groups of each head
+#pragma unroll
+            for (int level = 0; level < 2; ++level) {
+                const LanePair pm = level == 0 ? swap16(__float_as_uint(m_run)) : swap32(__float_as_uint(m_run));
+                const LanePair pl = level == 0 ? swap16(__float_as_uint(l_run)) : swap32(__float_as_uint(l_run));
+                const float ma = __uint_as_float(pm.a), mb = __uint_as_float(pm.b);
+                const float mn = fmaxf(ma, mb);
+                l_run = __uint_as_float(pl.a) * rescale(ma, mn) + __uint_as_float(pl.b) * rescale(mb, mn);
+                m_run = mn;
+            }
+            const int blk = t / tpb;
+            if (g16 == 0 && n16 < p.G) {
+                const size_t at = p.G == 1 ? (size_t)pair * p.nb + blk : ((size_t)b * p.Hq + j * p.G + n16) * p.nb + blk;
+                p.dst[at] = (m_run + log2f(l_run)) * kLn2;
+            }
+            m_run = kNegInf;
+            l_run = 0.0f;
+        }
+    };
+    uint4 A[2][KS], B[2][KS];
+    load(t0, A);
+    if (t0 + 1 < t1) load(t0 + 1, B);
+    for (int t = t0; t < t1; t += 2) {
+        consume(t, A);
+        if (t + 2 < t1) load(t + 2, A);
+        if (t + 1 >= t1) break;
+        consume(t + 1, B);
+        if (t + 3 < t1) load(t + 3, B);
+    }
+}
+
 // Group score per KV head from the per-head logits [B, Hq, nb] (G > 1).
 __global__ void __launch_bounds__(256) group_score_kernel(const float* logits, float* scores, int Hq, int Hkv,
                                                          int G, int nb)
@@ -218,66 +310,87 @@ __global__ void __launch_bounds__(256) group_score_kernel(const float* logits, f
 
 
 // ---------------------------------------------------------------------------
-// Summary mode, whole group in one workgroup per KV head: the block logits of
-// all G heads go to LDS (MFMA over the mean keys), then each head's
-// log-normaliser, then the group score.  Used when G <= 8 and the logits fit
-// in 64 KiB of LDS.
+// Summary mode on the matrix cores.  A tile of 32 blocks of one KV head: the
+// mean keys are the A operand of v_mfma_f32_16x16x32_bf16 (two 16-row chains),
+// the G query heads the B operand (padded to 16 columns); the logit of head h
+// and block b is scale * (q_h . Kbar_b) + ln c_b.
+//   * fused: one workgroup per KV head keeps all its logits in LDS, then the
+//     per-head log-normalisers and the group scores (many KV heads);
+//   * split: the tiles of a KV head spread over several workgroups that write
+//     the logits to a workspace, then one workgroup per KV head finishes the
+//     group scores and, for the decode step, the top-k (few KV heads).
+// Both produce the same bits.
 // ---------------------------------------------------------------------------
 
 constexpr int kFusedWaves = 8;
 constexpr int kFusedMaxLogits = 16384;  // G * nb floats in LDS
+constexpr int kSplitWaves = 4;          // waves (one tile each) per workgroup of the split logits kernel
+constexpr int kFinishMaxK = 32;
+constexpr int kFinishMaxBlocks = 2048;  // top-k by one wave: up to 32 scores per lane
 
 struct FusedScoreParams {
     const char* q;
     const char* Kbar;
     float* scores;
-    int Hq, Hkv, G, nb;
+    float* logits;  // split: [B, Hq, nb] (the scores when G == 1)
+    int32_t* sel;   // finish: selection [B, Hkv, k] when k > 0
+    int Hq, Hkv, G, nb, k, chunks;
     float scale, ln_L, ln_last;
 };
 
+// The mean keys of the tile of blocks [base, base + 32) in the A-operand layout
+// (lane (n16, g16): row n16 of each 16-row half, 16-byte chunks 4 s + g16).
 template <int D>
-__global__ void __launch_bounds__(kFusedWaves * 64) score_summary_fused_kernel(const FusedScoreParams p)
+struct KeyTile {
+    uint4 ak[2][D / 32];
+};
+
+template <int D>
+__device__ __forceinline__ void load_key_tile(__amdgpu_buffer_rsrc_t kr, int base, int lane, KeyTile<D>& t)
 {
-    constexpr int RB = D * 2, KS = D / 32, NW = kFusedWaves;
-    extern __shared__ float lsm[];  // [G][nb] block logits
-    __shared__ float lse_h[8];
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    constexpr int RB = D * 2, KS = D / 32;
     const int n16 = lane & 15, g16 = lane >> 4;
-    const int pair = blockIdx.x, b = pair / p.Hkv, j = pair - b * p.Hkv;
-    const int G = p.G, nb = p.nb;
-
-    bf16x8_t bq[KS];
-    load_q_operand<D>(p.q + ((size_t)b * p.Hq + (size_t)j * G) * RB, G, lane, bq);
-    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(p.Kbar + (size_t)pair * nb * RB, (uint32_t)nb * RB);
-
-    for (int base = wave * 32; base < nb; base += NW * 32) {
-        uint4 ak[2][KS];
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-            const uint32_t off = (uint32_t)(base + rb * 16 + n16) * RB + g16 * 16;  // past nb: zeros
+    for (int rb = 0; rb < 2; ++rb) {
+        const uint32_t off = (uint32_t)(base + rb * 16 + n16) * RB + g16 * 16;  // past nb: zeros
 #pragma unroll
-            for (int s = 0; s < KS; ++s) ak[rb][s] = buffer_ld16(kr, off + s * 64);
-        }
-        f32x4_t c[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-                c[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ak[rb][s]), bq[s], c[rb],
-                                                                0, 0, 0);
-        if (n16 < G) {
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = base + rb * 16 + 4 * g16 + i;
-                    if (row < nb) lsm[n16 * nb + row] = fmaf(c[rb][i], p.scale, row == nb - 1 ? p.ln_last : p.ln_L);
-                }
-        }
+        for (int s = 0; s < KS; ++s) t.ak[rb][s] = buffer_ld16(kr, off + s * 64);
     }
-    __syncthreads();
+}
 
+// Logits of a loaded tile for every head of the group: dst[h * stride + b].
+template <int D>
+__device__ __forceinline__ void key_tile_logits(const FusedScoreParams& p, const KeyTile<D>& t,
+                                                const bf16x8_t (&bq)[D / 32], int base, float* dst, int stride,
+                                                int lane)
+{
+    constexpr int KS = D / 32;
+    const int n16 = lane & 15, g16 = lane >> 4;
+    f32x4_t c[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+            c[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, t.ak[rb][s]), bq[s], c[rb], 0, 0,
+                                                            0);
+    if (n16 < p.G) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = base + rb * 16 + 4 * g16 + i;
+                if (row < p.nb) dst[n16 * stride + row] = fmaf(c[rb][i], p.scale, row == p.nb - 1 ? p.ln_last : p.ln_L);
+            }
+    }
+}
+
+// Group scores of one KV head from its logits lsm[h * nb + b] in LDS, by the
+// whole workgroup (NW waves): written to lsm[b] (row 0, in place: block b's
+// column is read only by the thread that writes it) and to scores when given.
+template <int NW>
+__device__ __forceinline__ void group_scores_in_lds(float* lsm, float* lse_h, int G, int nb, float* scores)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if (G > 1) {
         for (int h = wave; h < G; h += NW) {
             const float lse = head_lse(lsm + h * nb, nb, lane);
@@ -287,7 +400,93 @@ __global__ void __launch_bounds__(kFusedWaves * 64) score_summary_fused_kernel(c
     }
     for (int i = threadIdx.x; i < nb; i += NW * 64) {
         const float v = G == 1 ? lsm[i] : group_score<8>(lsm + i, nb, lse_h, G);
-        p.scores[(size_t)pair * nb + i] = v;
+        lsm[i] = v;
+        if (scores) scores[i] = v;
+    }
+}
+
+template <int D>
+__global__ void __launch_bounds__(kFusedWaves * 64) score_summary_fused_kernel(const FusedScoreParams p)
+{
+    constexpr int RB = D * 2, KS = D / 32, NW = kFusedWaves;
+    extern __shared__ float lsm[];  // [G][nb] block logits
+    __shared__ float lse_h[8];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int pair = blockIdx.x, b = pair / p.Hkv, j = pair - b * p.Hkv;
+
+    bf16x8_t bq[KS];
+    load_q_operand<D>(p.q + ((size_t)b * p.Hq + (size_t)j * p.G) * RB, p.G, lane, bq);
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(p.Kbar + (size_t)pair * p.nb * RB, (uint32_t)p.nb * RB);
+    for (int base = wave * 32; base < p.nb; base += 2 * NW * 32) {  // two tiles in flight
+        KeyTile<D> t0, t1;
+        const int base1 = base + NW * 32;
+        load_key_tile<D>(kr, base, lane, t0);
+        if (base1 < p.nb) load_key_tile<D>(kr, base1, lane, t1);
+        key_tile_logits<D>(p, t0, bq, base, lsm, p.nb, lane);
+        if (base1 < p.nb) key_tile_logits<D>(p, t1, bq, base1, lsm, p.nb, lane);
+    }
+    __syncthreads();
+    group_scores_in_lds<NW>(lsm, lse_h, p.G, p.nb, p.scores + (size_t)pair * p.nb);
+}
+
+// Split logits: workgroup (pair, chunk) computes tiles chunk * kSplitWaves + wave.
+template <int D>
+__global__ void __launch_bounds__(kSplitWaves * 64) score_logits_split_kernel(const FusedScoreParams p)
+{
+    constexpr int RB = D * 2, KS = D / 32;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int pair = blockIdx.x / p.chunks, chunk = blockIdx.x - pair * p.chunks;
+    const int b = pair / p.Hkv, j = pair - b * p.Hkv;
+    const int base = (chunk * kSplitWaves + wave) * 32;
+    if (base >= p.nb) return;  // whole wave; no barrier in this kernel
+    bf16x8_t bq[KS];
+    load_q_operand<D>(p.q + ((size_t)b * p.Hq + (size_t)j * p.G) * RB, p.G, lane, bq);
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(p.Kbar + (size_t)pair * p.nb * RB, (uint32_t)p.nb * RB);
+    KeyTile<D> t;
+    load_key_tile<D>(kr, base, lane, t);
+    key_tile_logits<D>(p, t, bq, base, p.logits + (size_t)pair * p.G * p.nb, p.nb, lane);
+}
+
+// Group scores (and the top-k when p.k > 0) of one KV head from split logits.
+__global__ void __launch_bounds__(kFusedWaves * 64) score_finish_kernel(const FusedScoreParams p)
+{
+    constexpr int NW = kFusedWaves;
+    extern __shared__ float lsm[];  // [G][nb] block logits, then the scores in row 0
+    __shared__ float lse_h[8];
+    __shared__ uint32_t cand[128];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int pair = blockIdx.x, G = p.G, nb = p.nb;
+    // copy the logits in (chunks of loads issued together: one memory round trip each)
+    const float* src = p.logits + (size_t)pair * G * nb;
+    constexpr int CH = 8;
+    for (int i0 = 0; i0 < G * nb; i0 += CH * NW * 64) {
+        float v[CH];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int i = i0 + c * NW * 64 + threadIdx.x;
+            v[c] = i < G * nb ? src[i] : 0.0f;
+        }
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int i = i0 + c * NW * 64 + threadIdx.x;
+            if (i < G * nb) lsm[i] = v[c];
+        }
+    }
+    __syncthreads();
+    group_scores_in_lds<NW>(lsm, lse_h, G, nb, p.scores ? p.scores + (size_t)pair * nb : nullptr);
+    if (p.k > 0) {
+        __syncthreads();
+        if (wave == 0) {
+            int32_t* out = p.sel + (size_t)pair * p.k;
+            auto load = [&](int i) { return lsm[i]; };
+            auto emit = [&](int r, int idx) { out[r] = idx; };
+            if (nb <= 8 * 64)
+                wave_topk<8>(load, nb, p.k, lane, cand, emit);
+            else
+                wave_topk<kFinishMaxBlocks / 64>(load, nb, p.k, lane, cand, emit);
+        }
     }
 }
 
@@ -298,12 +497,11 @@ bool fused_summary_score_ok(const Dims& s)
     return s.dtype == DT_BF16 && s.G <= 8 && s.G * s.nb <= kFusedMaxLogits;
 }
 
-hipError_t launch_score_summary_fused(const Dims& s, const void* q, const void* Kbar, float* scores, hipStream_t st)
+FusedScoreParams summary_params(const Dims& s, const void* q, const void* Kbar)
 {
     FusedScoreParams p{};
     p.q = static_cast<const char*>(q);
     p.Kbar = static_cast<const char*>(Kbar);
-    p.scores = scores;
     p.Hq = s.Hq;
     p.Hkv = s.Hkv;
     p.G = s.G;
@@ -311,12 +509,63 @@ hipError_t launch_score_summary_fused(const Dims& s, const void* q, const void* 
     p.scale = s.scale;
     p.ln_L = s.ln_L;
     p.ln_last = s.ln_last;
+    return p;
+}
+
+hipError_t launch_score_summary_fused(const Dims& s, const void* q, const void* Kbar, float* scores, hipStream_t st)
+{
+    FusedScoreParams p = summary_params(s, q, Kbar);
+    p.scores = scores;
     const size_t shm = (size_t)s.G * s.nb * sizeof(float);
     const dim3 grid((unsigned)s.pairs()), block(kFusedWaves * 64);
     if (s.d == 128)
         score_summary_fused_kernel<128><<<grid, block, shm, st>>>(p);
     else
         score_summary_fused_kernel<64><<<grid, block, shm, st>>>(p);
+    return hipGetLastError();
+}
+
+bool split_select_ok(const Dims& s, int k)
+{
+    return k <= kFinishMaxK && s.nb <= kFinishMaxBlocks;
+}
+
+hipError_t launch_score_summary_split(const Dims& s, const void* q, const void* Kbar, float* logits, float* scores,
+                                      int32_t* sel, int k, hipStream_t st)
+{
+    FusedScoreParams p = summary_params(s, q, Kbar);
+    p.logits = logits;
+    p.scores = scores;
+    p.sel = sel;
+    p.k = k;
+    const int tiles = (s.nb + 31) / 32;
+    p.chunks = (tiles + kSplitWaves - 1) / kSplitWaves;
+    const dim3 grid((unsigned)(s.pairs() * p.chunks)), block(kSplitWaves * 64);
+    if (s.d == 128)
+        score_logits_split_kernel<128><<<grid, block, 0, st>>>(p);
+    else
+        score_logits_split_kernel<64><<<grid, block, 0, st>>>(p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || (s.G == 1 && k == 0)) return e;  // G == 1: the logits are the scores
+    return launch_score_finish(s, logits, scores, sel, k, st);
+}
+
+bool score_finish_ok(const Dims& s)
+{
+    return s.G <= 8 && s.G * s.nb <= kFusedMaxLogits;
+}
+
+hipError_t launch_score_finish(const Dims& s, const float* logits, float* scores, int32_t* sel, int k, hipStream_t st)
+{
+    FusedScoreParams p{};
+    p.logits = const_cast<float*>(logits);
+    p.scores = scores;
+    p.sel = sel;
+    p.k = k;
+    p.G = s.G;
+    p.nb = s.nb;
+    const size_t shm = (size_t)s.G * s.nb * sizeof(float);
+    score_finish_kernel<<<dim3((unsigned)s.pairs()), dim3(kFusedWaves * 64), shm, st>>>(p);
     return hipGetLastError();
 }
 
@@ -346,6 +595,14 @@ hipError_t launch_logits_dtd(const LogitParams& p, int hg, int pairs, int hchunk
     }
 #undef CSA_LOGITS_CASE
     return hipGetLastError();
+}
+
+// The matrix-core exact-mass kernel: bfloat16, a group of 2 to 16 heads (one
+// head per KV head is already at the memory roofline on the vector units),
+// whole 32-token tiles per block.
+bool exact_mfma_ok(const Dims& s)
+{
+    return s.dtype == DT_BF16 && s.G >= 2 && s.G <= 16 && s.L % 32 == 0;
 }
 
 template <bool EXACT>
@@ -380,6 +637,19 @@ hipError_t launch_logits(const Dims& s, const void* q, const void* keys, float* 
         per = per < tile ? tile : (per + tile - 1) / tile * tile;
         p.items_per_wg = per;
         p.chunks = (s.nb + per - 1) / per;
+    }
+    if (EXACT && exact_mfma_ok(s)) {
+        // blocks per workgroup: about 1024 workgroups, a few blocks per wave
+        int per = (int)(((long long)s.nb * s.pairs() + 1023) / 1024);
+        per = per < kExactWaves ? kExactWaves : (per + kExactWaves - 1) / kExactWaves * kExactWaves;
+        p.items_per_wg = per;
+        p.chunks = (s.nb + per - 1) / per;
+        const dim3 grid((unsigned)(s.pairs() * p.chunks)), block(kExactWaves * 64);
+        if (s.d == 128)
+            logits_exact_mfma_kernel<128><<<grid, block, 0, st>>>(p);
+        else
+            logits_exact_mfma_kernel<64><<<grid, block, 0, st>>>(p);
+        return hipGetLastError();
     }
     if (s.dtype == DT_BF16) {
         if (s.d == 128) return launch_logits_dtd<DT_BF16, 128, EXACT>(p, hg, s.pairs(), hchunks, st);
