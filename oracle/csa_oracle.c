@@ -157,14 +157,53 @@ int oracle_kv_summary_build(const oracle_shape* s, const void* K, const void* V,
     return 0;
 }
 
+int oracle_kv_box_build(const oracle_shape* s, const void* K, void* Kbox)
+{
+    if (!shape_ok(s) || !K || !Kbox) return -1;
+    const int nb = n_blocks(s), d = s->head_dim;
+    const int pairs = s->batch * s->n_kv_heads;
+#pragma omp parallel for schedule(dynamic)
+    for (int p = 0; p < pairs; ++p) {
+        const int b = p / s->n_kv_heads, j = p % s->n_kv_heads;
+        for (int blk = 0; blk < nb; ++blk) {
+            const int c = block_count(s, blk);
+            for (int t = 0; t < d; ++t) {
+                double lo = elem(K, s->dtype, kv_off(s, b, j, s->n_tokens, blk * s->block_size) + t), hi = lo;
+                for (int i = 1; i < c; ++i) {
+                    const double x = elem(K, s->dtype, kv_off(s, b, j, s->n_tokens, blk * s->block_size + i) + t);
+                    if (x < lo) lo = x;
+                    if (x > hi) hi = x;
+                }
+                store(Kbox, s->dtype, kv_off(s, b, j, 2 * nb, 2 * blk) + t, lo);
+                store(Kbox, s->dtype, kv_off(s, b, j, 2 * nb, 2 * blk + 1) + t, hi);
+            }
+        }
+    }
+    return 0;
+}
+
 /* ----------------------------------------------------------------------------
  * Block logits and the group score
  * ------------------------------------------------------------------------- */
 
+/* The largest q . k over the box [lo, hi] of a block: each coordinate of the
+ * maximiser sits at whichever end of its range gives the larger product. */
+static double box_dot_scaled(const oracle_shape* s, const void* q, size_t qo, const void* box, size_t lo_off,
+                             size_t hi_off)
+{
+    double acc = 0.0;
+    for (int t = 0; t < s->head_dim; ++t) {
+        const double qt = elem(q, s->dtype, qo + t);
+        const double a = qt * elem(box, s->dtype, lo_off + t), c = qt * elem(box, s->dtype, hi_off + t);
+        acc += a > c ? a : c;
+    }
+    return acc * logit_scale(s);
+}
+
 int oracle_block_logits(const oracle_shape* s, int mode, const void* q, const void* keys,
                         double* logits)
 {
-    if (!shape_ok(s) || !q || !keys || !logits || (mode != 0 && mode != 1)) return -1;
+    if (!shape_ok(s) || !q || !keys || !logits || mode < 0 || mode > 2) return -1;
     const int nb = n_blocks(s), G = s->n_q_heads / s->n_kv_heads;
 #pragma omp parallel for schedule(dynamic)
     for (int bh = 0; bh < s->batch * s->n_q_heads; ++bh) {
@@ -176,6 +215,10 @@ int oracle_block_logits(const oracle_shape* s, int mode, const void* q, const vo
             if (mode == 0) {
                 /* first-order (mean-pool) estimate of ln m_b: ln c_b + scale q . kbar_b */
                 row[blk] = dot_scaled(s, q, q_off(s, b, h), keys, kv_off(s, b, j, nb, blk)) + log((double)c);
+            } else if (mode == 2) {
+                /* the largest logit any point of the block's key box could give */
+                row[blk] = box_dot_scaled(s, q, q_off(s, b, h), keys, kv_off(s, b, j, 2 * nb, 2 * blk),
+                                          kv_off(s, b, j, 2 * nb, 2 * blk + 1));
             } else {
                 /* exact ln m_b = ln sum_{i in b} exp(s_i) */
                 for (int i = 0; i < c; ++i)

@@ -52,10 +52,19 @@ typedef struct oracle_shape {
 int oracle_kv_summary_build(const oracle_shape* s, const void* K, const void* V,
                             void* Kbar, void* Vbar);
 
+/* Box summaries (Quest, as analysed in "COBS: Cumulant Order Block Sparse
+ * Attention", section on escaping the first-order ceiling): per block the
+ * element-wise minimum and maximum of its keys, an axis-aligned bounding box.
+ * Kbox is [B, Hkv, nb, 2, d]: row 2b the minimum, row 2b + 1 the maximum, in
+ * the key dtype (a minimum or maximum of stored values is a stored value). */
+int oracle_kv_box_build(const oracle_shape* s, const void* K, void* Kbox);
+
 /* Per-query-head block logits [B, Hq, nb].
  * mode 0 (summary):    scale * q_h . Kbar_b + ln c_b          (COBS Eq. (18))
  * mode 1 (exact mass): ln m_hb = LSE_{i in b} scale * q_h . K_i (COBS Eq. (1))
- * keys is Kbar for mode 0 and K for mode 1. */
+ * mode 2 (box):        scale * max over the block's box of q_h . k
+ *                      = scale * sum_t max(q_t min_bt, q_t max_bt)
+ * keys is Kbar for mode 0, K for mode 1 and Kbox for mode 2. */
 int oracle_block_logits(const oracle_shape* s, int mode, const void* q, const void* keys,
                         double* logits);
 

@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "csa_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "libcsa_oracle.so")
 
-SUMMARY, EXACT_MASS = 0, 1
+SUMMARY, EXACT_MASS, BOX = 0, 1, 2
 
 
 def build(force: bool = False) -> str:
@@ -140,10 +140,24 @@ def kv_summary_build(shape: Shape, K, V):
     return Kbar, Vbar
 
 
+def kv_box_build(shape: Shape, K):
+    """Element-wise minimum and maximum key of every block, [B, Hkv, nb, 2, d]."""
+    kv = (shape.batch, shape.n_kv_heads, shape.n_tokens, shape.head_dim)
+    K = _stored(shape, K, kv)
+    Kbox = np.empty((shape.batch, shape.n_kv_heads, shape.n_blocks, 2, shape.head_dim), shape.np_dtype)
+    _check(_load().oracle_kv_box_build(ctypes.byref(shape.c()), _ptr(K), _ptr(Kbox)), "kv_box_build")
+    return Kbox
+
+
 def block_logits(shape: Shape, mode: int, q, keys):
-    """Per-query-head block logits [B, Hq, nb]: first-order summary score or exact ln m_b."""
-    rows = shape.n_blocks if mode == SUMMARY else shape.n_tokens
+    """Per-query-head block logits [B, Hq, nb]: first-order summary score, exact ln m_b, or the
+    largest logit over the block's key box."""
+    rows = {SUMMARY: shape.n_blocks, EXACT_MASS: shape.n_tokens, BOX: 2 * shape.n_blocks}[mode]
     q = _stored(shape, q, (shape.batch, shape.n_q_heads, shape.head_dim))
+    if mode == BOX:  # [B, Hkv, nb, 2, d] is [B, Hkv, 2 nb, d] in memory
+        keys = np.asarray(keys)
+        if keys.ndim == 5:
+            keys = keys.reshape(shape.batch, shape.n_kv_heads, rows, shape.head_dim)
     keys = _stored(shape, keys, (shape.batch, shape.n_kv_heads, rows, shape.head_dim))
     out = np.empty((shape.batch, shape.n_q_heads, shape.n_blocks), np.float64)
     _check(_load().oracle_block_logits(ctypes.byref(shape.c()), mode, _ptr(q), _ptr(keys), _ptr(out)),

@@ -28,6 +28,8 @@ MUTANTS = {
     "query head on the wrong KV head": ("j = h / G;", "j = h % s->n_kv_heads;"),
     "lse without the maximum": ("*lse = mx + log(denom);", "*lse = log(denom);"),
     "exact mass as the maximum logit": ("    return mx + log(sum);", "    return mx + 0.0 * log(sum);"),
+    "box scored at its worst corner": ("acc += a > c ? a : c;", "acc += a < c ? a : c;"),
+    "box maximum taken as the minimum": ("if (x > hi) hi = x;", "if (x < hi) hi = x;"),
 }
 
 BATTERY = [
@@ -46,6 +48,9 @@ BATTERY = [
     (P.test_mixture_and_renormalised_error_identities, ()),
     (P.test_worked_example_from_the_page, ()),
     (P.test_integer_weights_equal_multiplicities, ()),
+    (P.test_box_build_is_elementwise_min_and_max, ("f32", 200, 16)),
+    (P.test_box_score_bounds_every_token_logit, ("f32",)),
+    (P.test_box_score_is_the_best_corner, ()),
 ]
 
 

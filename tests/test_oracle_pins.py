@@ -483,3 +483,73 @@ def test_heavy_hitters_are_planted():
     assert (cos > 0.9).sum() == 8
     hh = np.nonzero(cos > 0.9)[0]
     assert np.allclose(np.linalg.norm(K[hh], axis=1), 3.0, atol=0.5)
+
+
+# ---------------------------------------------------------------------------
+# box score (Quest, as analysed in [COBS], section on escaping the first-order
+# ceiling: per block the element-wise minimum and maximum of its keys, scored by
+# the largest inner product any point of that box could attain with the query)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,n,L", [("f32", 200, 16), ("bf16", 250, 32)])
+def test_box_build_is_elementwise_min_and_max(dtype, n, L):
+    shp = O.Shape(2, 2, 2, 64, n, L, dtype)
+    _, K, _ = rand_case(30, 2, 2, 2, 64, n, dtype)
+    box = O.kv_box_build(shp, K)
+    Kf = O.widen(dtype, K)
+    for b in range(2):
+        for j in range(2):
+            for blk in range(shp.n_blocks):
+                rows = Kf[b, j, blk * L:min(n, (blk + 1) * L)]
+                assert np.array_equal(O.widen(dtype, box[b, j, blk, 0]), rows.min(axis=0))
+                assert np.array_equal(O.widen(dtype, box[b, j, blk, 1]), rows.max(axis=0))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_box_score_bounds_every_token_logit(dtype):
+    """The box contains every key of its block, so its best inner product bounds each
+    token's logit from above."""
+    n, L, d = 512, 32, 128
+    shp = O.Shape(1, 4, 2, d, n, L, dtype)
+    q, K, _ = rand_case(31, 1, 4, 2, d, n, dtype, qscale=2.0)
+    box = O.kv_box_build(shp, K)
+    lg = O.block_logits(shp, O.BOX, q, box)
+    s = np.einsum("bhd,bhnd->bhn", O.widen(dtype, q), np.repeat(O.widen(dtype, K), 2, axis=1)) / math.sqrt(d)
+    tok_max = s.reshape(1, 4, shp.n_blocks, L).max(axis=-1)
+    assert (lg - tok_max).min() > -1e-12
+    assert (lg - tok_max).max() > 0.1  # a real box is strictly looser for random keys
+
+
+def test_box_score_is_exact_for_a_point_box():
+    """A box that is a single point (all keys of the block equal, or blocks of one
+    token) gives exactly that key's logit."""
+    n, L, d = 64, 8, 32
+    shp = O.Shape(1, 1, 1, d, n, L, "f32")
+    q, K, _ = rand_case(32, 1, 1, 1, d, n, "f32", qscale=2.0)
+    K[0, 0, 0:L] = K[0, 0, 3]
+    lg = O.block_logits(shp, O.BOX, q, O.kv_box_build(shp, K))
+    want = float(np.dot(q[0, 0].astype(np.float64), K[0, 0, 3].astype(np.float64))) / math.sqrt(d)
+    assert abs(lg[0, 0, 0] - want) < 1e-12
+    shp1 = O.Shape(1, 1, 1, d, n, 1, "f32")
+    lg1 = O.block_logits(shp1, O.BOX, q, O.kv_box_build(shp1, K))[0, 0]
+    tok = K[0, 0].astype(np.float64) @ q[0, 0].astype(np.float64) / math.sqrt(d)
+    assert np.abs(lg1 - tok).max() < 1e-12
+
+
+def test_box_score_is_the_best_corner():
+    """Brute force: the largest inner product over a box is attained at one of its 2^d
+    corners; enumerate them all for d = 8."""
+    import itertools
+
+    n, L, d = 48, 12, 8
+    shp = O.Shape(1, 2, 1, d, n, L, "f32")
+    q, K, _ = rand_case(33, 1, 2, 1, d, n, "f32", qscale=2.0)
+    box = O.kv_box_build(shp, K)
+    lg = O.block_logits(shp, O.BOX, q, box)
+    for h in range(2):
+        qh = q[0, h].astype(np.float64)
+        for blk in range(shp.n_blocks):
+            lo, hi = box[0, 0, blk, 0].astype(np.float64), box[0, 0, blk, 1].astype(np.float64)
+            best = max(float(np.dot(qh, np.where(np.array(c), hi, lo)))
+                       for c in itertools.product((0, 1), repeat=d))
+            assert abs(lg[0, h, blk] - best / math.sqrt(d)) < 1e-12
