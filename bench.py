@@ -157,13 +157,22 @@ def algorithmic_bytes(w, m=0):
 
 
 def step_bytes(w, m=0):
-    """Bytes one selective decode step must move (reads, writes): every mean key once (it
-    ranks the blocks and gives the proxy logits), the mean values of the unread blocks,
-    the exact key/value rows of the kept blocks, weighted-token rows, the queries, and the
-    outputs with their log-normalisers."""
+    """Bytes one selective decode step must move (reads, writes).  Summary scores: every mean
+    key once (it ranks the blocks and gives the proxy logits), the mean values of the unread
+    blocks and the exact key/value rows of the kept blocks.  Exact-mass scores: every key
+    once, the values of the kept blocks, both mean rows of the unread blocks.  Box scores:
+    both box rows of every block, both mean rows of the unread blocks, the exact rows.  Plus
+    weighted-token rows, the queries, and the outputs with their log-normalisers."""
     e = w.elem_bytes
     d, L, k, nb, G = w.head_dim, w.block_size, w.k, w.n_blocks, w.group
-    per_read = nb * d * e + (nb - k if w.proxies else 0) * d * e + k * L * 2 * d * e + m * (2 * d * e + 8) + G * d * e
+    unread = (nb - k) if w.proxies else 0
+    if w.score_mode == "summary":
+        per_read = nb * d * e + unread * d * e + k * L * 2 * d * e
+    elif w.score_mode == "exact_mass":
+        per_read = w.n_tokens * d * e + k * L * d * e + unread * 2 * d * e
+    else:
+        per_read = 2 * nb * d * e + unread * 2 * d * e + k * L * 2 * d * e
+    per_read += m * (2 * d * e + 8) + G * d * e
     per_write = G * (d + 1) * 4
     pairs = w.batch * w.n_kv_heads
     return pairs * per_read, pairs * per_write
@@ -219,9 +228,11 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     summary_ms = e0.elapsed_time(e1)
-    layers = [(K0, V0, Kbar0, Vbar0)]
+    box = w.score_mode == "box"
+    Kbox0 = csa.kv_box_build(K0, w.block_size) if box else None
+    layers = [(K0, V0, Kbar0, Vbar0, Kbox0)]
     for _ in range(NL - 1):
-        layers.append(tuple(x.clone() for x in layers[0]))
+        layers.append(tuple(None if x is None else x.clone() for x in layers[0]))
     torch.cuda.synchronize()
 
     shape = csa.make_shape(q, K0, w.block_size)
@@ -230,7 +241,8 @@ def main():
     sel = torch.empty((B, Hkv, min(w.k, nb)), dtype=torch.int32, device=dev)
     out = torch.empty((B, Hq, w.head_dim), dtype=torch.float32, device=dev)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
-    mode_entry = csa.CSA_WS_BLOCK_SCORE_SUMMARY if w.score_mode == "summary" else csa.CSA_WS_BLOCK_SCORE_EXACT_MASS
+    mode_entry = {"summary": csa.CSA_WS_BLOCK_SCORE_SUMMARY, "exact_mass": csa.CSA_WS_BLOCK_SCORE_EXACT_MASS,
+                  "box": csa.CSA_WS_BLOCK_SCORE_BOX}[w.score_mode]
     ws_score = torch.empty(max(1, csa.workspace_size(shape, mode_entry)), dtype=torch.uint8, device=dev)
     ws_attn = torch.empty(max(1, csa.workspace_size(shape, csa.CSA_WS_SPARSE_DECODE_ATTN, w.k, m)),
                           dtype=torch.uint8, device=dev)
@@ -238,13 +250,13 @@ def main():
                           dtype=torch.uint8, device=dev)
 
     def score_select(layer):
-        K, V, Kbar, Vbar = layer
-        keys = Kbar if w.score_mode == "summary" else K
+        K, V, Kbar, Vbar, Kbox = layer
+        keys = {"summary": Kbar, "exact_mass": K, "box": Kbox}[w.score_mode]
         csa.block_score(q, keys, w.score_mode, w.block_size, n_tokens=w.n_tokens, scores=scores, ws=ws_score)
         csa.topk_select(scores, w.k, sel=sel)
 
     def attend(layer):
-        K, V, Kbar, Vbar = layer
+        K, V, Kbar, Vbar, _ = layer
         csa.sparse_decode_attn(q, K, V, Kbar, Vbar, sel, w.block_size, proxies=w.proxies, tok_idx=tok_idx,
                                tok_logw=tok_logw, out=out, lse=lse, ws=ws_attn)
 
@@ -253,7 +265,10 @@ def main():
         attend(layers[i % NL])
 
     def step(i):
-        K, V, Kbar, Vbar = layers[i % NL]
+        if box:  # box scores need Kbox: the three entry points in turn
+            modular(i)
+            return
+        K, V, Kbar, Vbar, _ = layers[i % NL]
         csa.selective_decode_step(q, K, V, Kbar, Vbar, w.k, w.block_size, mode=w.score_mode, proxies=w.proxies,
                                   tok_idx=tok_idx, tok_logw=tok_logw, out=out, lse=lse, ws=ws_step)
 
@@ -317,7 +332,7 @@ def main():
         dout, dlse = torch.empty_like(out), torch.empty_like(lse)
 
         def dense(r):
-            K, V, _, _ = layers[r % NL]
+            K, V = layers[r % NL][:2]
             csa.dense_decode_attn(q, K, V, out=dout, lse=dlse, ws=ws_dense)
 
         dense(0)
@@ -344,7 +359,7 @@ def main():
             "exact_read_fraction": w.k * w.block_size / w.n_tokens, "score": w.score_mode, "proxies": w.proxies,
             "weighted_tokens": m, "layers_cycled": NL,
             "timing": "HIP graph of the decode step replayed" if graph_ms is not None else "eager",
-            "entry_point": "selective_decode_step",
+            "entry_point": "block_score + topk_select + sparse_decode_attn" if box else "selective_decode_step",
         },
         "achieved_hbm_gb_s": step_achieved,
         "head_queries_per_s": B * Hq / (t_step * 1e-3),
@@ -357,7 +372,8 @@ def main():
         "dense_decode_attn_ms": dense_ms,
         "step_vs_dense_speedup": (dense_ms / t_step) if dense_ms else None,
         "roofline": {
-            "kernel": "selective_decode_step (decode_step_kernel)",
+            "kernel": "block_score + topk_select + sparse_decode_attn (three kernels)" if box
+                      else "selective_decode_step (decode_step_kernel)",
             "bound": "hbm",
             "achieved": step_achieved,
             "peak": 8000.0,

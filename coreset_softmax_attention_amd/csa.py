@@ -16,12 +16,15 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so"
 
 CSA_OK, CSA_ERR_INVALID_ARG, CSA_ERR_UNSUPPORTED, CSA_ERR_WORKSPACE, CSA_ERR_HIP = 0, -1, -2, -3, -4
 CSA_F32, CSA_BF16 = 0, 1
-CSA_SCORE_SUMMARY, CSA_SCORE_EXACT_MASS = 0, 1
+CSA_SCORE_SUMMARY, CSA_SCORE_EXACT_MASS, CSA_SCORE_BOX = 0, 1, 2
 CSA_PROXY_NONE, CSA_PROXY_COMPLEMENT = 0, 1
 CSA_WS_BLOCK_SCORE_SUMMARY, CSA_WS_BLOCK_SCORE_EXACT_MASS = 0, 1
 CSA_WS_SPARSE_DECODE_ATTN, CSA_WS_DENSE_DECODE_ATTN, CSA_WS_SELECTIVE_DECODE_STEP = 2, 3, 4
+CSA_WS_BLOCK_SCORE_BOX = 5
 
-MODES = {"summary": CSA_SCORE_SUMMARY, "exact_mass": CSA_SCORE_EXACT_MASS}
+MODES = {"summary": CSA_SCORE_SUMMARY, "exact_mass": CSA_SCORE_EXACT_MASS, "box": CSA_SCORE_BOX}
+_SCORE_WS = {"summary": CSA_WS_BLOCK_SCORE_SUMMARY, "exact_mass": CSA_WS_BLOCK_SCORE_EXACT_MASS,
+             "box": CSA_WS_BLOCK_SCORE_BOX}
 
 
 class CsaError(RuntimeError):
@@ -52,6 +55,7 @@ _lib = None
 _P, _I32, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
 _SIGS = {
     "kv_summary_build": [ctypes.POINTER(Shape), _P, _P, _P, _P, _P],
+    "kv_box_build": [ctypes.POINTER(Shape), _P, _P, _P],
     "block_score": [ctypes.POINTER(Shape), ctypes.c_int, _P, _P, _P, _P, _SZ, _P],
     "topk_select": [_I32, _I32, _I32, _P, _P, _P],
     "sparse_decode_attn": [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _I32, _P, _P, _I32, ctypes.c_int,
@@ -156,26 +160,38 @@ def kv_summary_build(K: torch.Tensor, V: torch.Tensor, block_size: int, Kbar=Non
     return Kbar, Vbar
 
 
+def kv_box_build(K: torch.Tensor, block_size: int, Kbox=None):
+    """Element-wise minimum and maximum key of every block: Kbox [B, Hkv, nb, 2, d]."""
+    dev = _dev(K, Kbox)
+    B, Hkv, n, d = K.shape
+    shape = Shape(B, Hkv, Hkv, d, n, block_size, _dtype_code(K), 0.0)
+    Kbox = torch.empty((B, Hkv, shape.n_blocks, 2, d), dtype=K.dtype, device=dev) if Kbox is None else Kbox
+    _check(lib().kv_box_build(ctypes.byref(shape), _ptr(K), _ptr(Kbox), _stream(dev)), "kv_box_build")
+    return Kbox
+
+
 def block_score(q: torch.Tensor, keys: torch.Tensor, mode: str, block_size: int, n_tokens: int | None = None,
                 scale: float = 0.0, scores=None, ws=None):
-    """Block scores [B, Hkv, nb].  keys = Kbar (mode 'summary') or K (mode 'exact_mass');
-    n_tokens is needed in summary mode (the cache length the summaries describe)."""
+    """Block scores [B, Hkv, nb].  keys = Kbar (mode 'summary'), K (mode 'exact_mass') or Kbox
+    (mode 'box'); n_tokens is needed in summary and box modes (the cache length the summaries
+    describe)."""
     dev = _dev(q, keys, scores)
     B, Hq, d = q.shape
     Hkv = keys.shape[1]
-    if mode == "summary":
+    if mode in ("summary", "box"):
         if n_tokens is None:
-            raise ValueError("summary mode needs n_tokens")
+            raise ValueError(f"{mode} mode needs n_tokens")
         n = n_tokens
     else:
         n = keys.shape[2]
     shape = Shape(B, Hq, Hkv, d, n, block_size, _dtype_code(q), float(scale))
     nb = shape.n_blocks
-    if mode == "summary" and keys.shape[2] != nb:
-        raise ValueError(f"Kbar has {keys.shape[2]} rows, expected {nb}")
+    if mode in ("summary", "box") and keys.shape[2] != nb:
+        raise ValueError(f"the summaries have {keys.shape[2]} blocks, expected {nb}")
+    if mode == "box" and (keys.dim() != 5 or keys.shape[3] != 2):
+        raise ValueError("box mode needs Kbox [B, Hkv, nb, 2, d]")
     scores = torch.empty((B, Hkv, nb), dtype=torch.float32, device=dev) if scores is None else scores
-    entry = CSA_WS_BLOCK_SCORE_SUMMARY if mode == "summary" else CSA_WS_BLOCK_SCORE_EXACT_MASS
-    ws, wsb = _workspace(shape, entry, 0, 0, ws, dev)
+    ws, wsb = _workspace(shape, _SCORE_WS[mode], 0, 0, ws, dev)
     _check(lib().block_score(ctypes.byref(shape), MODES[mode], _ptr(q), _ptr(keys), _ptr(scores), _ptr(ws), wsb,
                              _stream(dev)), "block_score")
     return scores

@@ -127,12 +127,22 @@ int kv_summary_build(const csa_shape* shape, const void* K, const void* V, void*
     return e == hipSuccess ? CSA_OK : hip_fail(e, "kv_summary_build");
 }
 
+int kv_box_build(const csa_shape* shape, const void* K, void* Kbox, hipStream_t stream)
+{
+    csa::Dims d;
+    if (int rc = make_dims(shape, &d)) return rc;
+    if (!K || !Kbox) return fail(CSA_ERR_INVALID_ARG, "kv_box_build: NULL tensor pointer");
+    if (!aligned16(K) || !aligned16(Kbox)) return fail(CSA_ERR_INVALID_ARG, "kv_box_build: tensors must be 16-byte aligned");
+    const hipError_t e = csa::launch_box(d, K, Kbox, stream);
+    return e == hipSuccess ? CSA_OK : hip_fail(e, "kv_box_build");
+}
+
 int block_score(const csa_shape* shape, csa_score_mode mode, const void* q, const void* keys, float* scores, void* ws,
                 size_t ws_bytes, hipStream_t stream)
 {
     csa::Dims d;
     if (int rc = make_dims(shape, &d)) return rc;
-    if (mode != CSA_SCORE_SUMMARY && mode != CSA_SCORE_EXACT_MASS)
+    if (mode != CSA_SCORE_SUMMARY && mode != CSA_SCORE_EXACT_MASS && mode != CSA_SCORE_BOX)
         return fail(CSA_ERR_INVALID_ARG, "block_score: unknown mode %d", (int)mode);
     if (!q || !keys || !scores) return fail(CSA_ERR_INVALID_ARG, "block_score: NULL tensor pointer");
     if (!aligned16(q) || !aligned16(keys) || !aligned4(scores))
@@ -149,6 +159,7 @@ int block_score(const csa_shape* shape, csa_score_mode mode, const void* q, cons
     }
     float* dst = d.G == 1 ? scores : static_cast<float*>(ws);
     hipError_t e = mode == CSA_SCORE_SUMMARY ? csa::launch_block_logits_summary(d, q, keys, dst, stream)
+                   : mode == CSA_SCORE_BOX   ? csa::launch_block_logits_box(d, q, keys, dst, stream)
                                              : csa::launch_block_logits_exact(d, q, keys, dst, stream);
     if (e != hipSuccess) return hip_fail(e, "block_score");
     if (d.G > 1) {
@@ -224,6 +235,9 @@ int selective_decode_step(const csa_shape* shape, csa_score_mode mode, const voi
 {
     csa::Dims d;
     if (int rc = make_dims(shape, &d)) return rc;
+    if (mode == CSA_SCORE_BOX)
+        return fail(CSA_ERR_UNSUPPORTED, "selective_decode_step: box scores need Kbox; call block_score, "
+                                         "topk_select and sparse_decode_attn");
     if (mode != CSA_SCORE_SUMMARY && mode != CSA_SCORE_EXACT_MASS)
         return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: unknown mode %d", (int)mode);
     if (proxy_mode != CSA_PROXY_NONE && proxy_mode != CSA_PROXY_COMPLEMENT)
@@ -286,7 +300,8 @@ size_t csa_workspace_size(const csa_shape* shape, csa_entry entry, int32_t k, in
     if (make_dims(shape, &d) != CSA_OK) return 0;
     switch (entry) {
     case CSA_WS_BLOCK_SCORE_SUMMARY:
-    case CSA_WS_BLOCK_SCORE_EXACT_MASS: return block_score_ws(d);
+    case CSA_WS_BLOCK_SCORE_EXACT_MASS:
+    case CSA_WS_BLOCK_SCORE_BOX: return block_score_ws(d);
     case CSA_WS_SPARSE_DECODE_ATTN: {
         if (k < 0 || k > d.nb || m < 0) {
             fail(CSA_ERR_INVALID_ARG, "csa_workspace_size: k=%d or m=%d out of range", k, m);

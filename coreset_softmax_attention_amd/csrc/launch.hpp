@@ -29,6 +29,9 @@ hipError_t launch_block_logits_summary(const Dims& s, const void* q, const void*
 hipError_t launch_block_logits_exact(const Dims& s, const void* q, const void* K, float* dst,
                                      hipStream_t st);
 hipError_t launch_group_score(const Dims& s, const float* logits, float* scores, hipStream_t st);
+// Box logits (Kbox [B, Hkv, nb, 2, d]); same destinations as the other logits.
+hipError_t launch_block_logits_box(const Dims& s, const void* q, const void* Kbox, float* dst, hipStream_t st);
+hipError_t launch_box(const Dims& s, const void* K, void* Kbox, hipStream_t st);
 // Summary mode with the logits, log-normalisers and group score in one kernel
 // (one workgroup per KV head); available when fused_summary_score_ok().
 bool fused_summary_score_ok(const Dims& s);

@@ -98,6 +98,55 @@ __global__ void __launch_bounds__(kNW * 64) logits_summary_kernel(const LogitPar
     }
 }
 
+// Box logits: scale * sum_t max(q_t lo_bt, q_t hi_bt), the largest logit any
+// point of block b's key box [lo_b, hi_b] could give (Kbox rows 2b and 2b + 1).
+template <int DT, int D, int HG, int U>
+__global__ void __launch_bounds__(kNW * 64) logits_box_kernel(const LogitParams p)
+{
+    using Gm = RowGeom<DT, D>;
+    constexpr int LPR = Gm::lpr, RPW = Gm::rpw, EPL = Gm::epl, RB = Gm::row_bytes;
+    constexpr int T = RPW * U;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int gi = lane / LPR, li = lane % LPR;
+    const int pair = blockIdx.x / p.chunks, chunk = blockIdx.x - pair * p.chunks;
+    const int b = pair / p.Hkv, j = pair - b * p.Hkv;
+    const int g0 = blockIdx.y * HG, nh = min(HG, p.G - g0), h0 = j * p.G + g0;
+    float qf[HG][EPL];
+    load_q<DT, EPL, HG>(p, b, h0, nh, li, qf, D);
+
+    const int r0 = chunk * p.items_per_wg, r1 = min(p.nb, r0 + p.items_per_wg);
+    const char* base_ptr = p.keys + (size_t)pair * 2 * p.nb * RB + li * 16;
+    for (int base = r0 + wave * T; base < r1; base += kNW * T) {
+        uint4 lr[U], hr[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int r = min(base + u * RPW + gi, r1 - 1);
+            lr[u] = ld16(base_ptr + (size_t)(2 * r) * RB);
+            hr[u] = ld16(base_ptr + (size_t)(2 * r + 1) * RB);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int r = base + u * RPW + gi;
+            float lf[EPL], hf[EPL];
+            unpack<DT>(lr[u], lf);
+            unpack<DT>(hr[u], hf);
+            float mine = 0.0f;
+#pragma unroll
+            for (int g = 0; g < HG; ++g) {
+                float s = 0.0f;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) s += fmaxf(qf[g][e] * lf[e], qf[g][e] * hf[e]);
+                s = group_sum<LPR>(s);
+                if (li == g) mine = s;
+            }
+            if (r < r1 && li < nh) {
+                const size_t at = p.G == 1 ? (size_t)pair * p.nb + r : ((size_t)b * p.Hq + h0 + li) * p.nb + r;
+                p.dst[at] = mine * p.scale;
+            }
+        }
+    }
+}
+
 // Exact-mass logits: each wave reduces whole blocks (log-sum-exp of the
 // block's token logits).
 template <int DT, int D, int HG, int U>
@@ -662,6 +711,59 @@ hipError_t launch_logits(const Dims& s, const void* q, const void* keys, float* 
 }
 
 }  // namespace
+
+namespace {
+
+template <int DT, int D>
+hipError_t launch_box_dtd(const LogitParams& p, int hg, int pairs, int hchunks, hipStream_t st)
+{
+    const dim3 grid((unsigned)(pairs * p.chunks), (unsigned)hchunks, 1), block(kNW * 64);
+    switch (hg) {
+    case 1: logits_box_kernel<DT, D, 1, score_unroll(1)><<<grid, block, 0, st>>>(p); break;
+    case 2: logits_box_kernel<DT, D, 2, score_unroll(2)><<<grid, block, 0, st>>>(p); break;
+    case 3: logits_box_kernel<DT, D, 3, score_unroll(3)><<<grid, block, 0, st>>>(p); break;
+    case 4: logits_box_kernel<DT, D, 4, score_unroll(4)><<<grid, block, 0, st>>>(p); break;
+    case 5: logits_box_kernel<DT, D, 5, score_unroll(5)><<<grid, block, 0, st>>>(p); break;
+    case 6: logits_box_kernel<DT, D, 6, score_unroll(6)><<<grid, block, 0, st>>>(p); break;
+    case 7: logits_box_kernel<DT, D, 7, score_unroll(7)><<<grid, block, 0, st>>>(p); break;
+    case 8: logits_box_kernel<DT, D, 8, score_unroll(8)><<<grid, block, 0, st>>>(p); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_block_logits_box(const Dims& s, const void* q, const void* Kbox, float* dst, hipStream_t st)
+{
+    LogitParams p{};
+    p.q = static_cast<const char*>(q);
+    p.keys = static_cast<const char*>(Kbox);
+    p.dst = dst;
+    p.Hq = s.Hq;
+    p.Hkv = s.Hkv;
+    p.G = s.G;
+    p.n = s.n;
+    p.L = s.L;
+    p.nb = s.nb;
+    p.scale = s.scale;
+    const int hg = s.G <= 8 ? s.G : 8, hchunks = (s.G + hg - 1) / hg;
+    const int items = s.pairs() * hchunks;
+    const int elem = s.dtype == DT_F32 ? 4 : 2;
+    const int tile = 64 / (s.d * elem / 16) * score_unroll(hg) * kNW;
+    int per = (int)(((long long)s.nb * items + 1023) / 1024);
+    per = per < tile ? tile : (per + tile - 1) / tile * tile;
+    p.items_per_wg = per;
+    p.chunks = (s.nb + per - 1) / per;
+    if (s.dtype == DT_BF16) {
+        if (s.d == 128) return launch_box_dtd<DT_BF16, 128>(p, hg, s.pairs(), hchunks, st);
+        if (s.d == 64) return launch_box_dtd<DT_BF16, 64>(p, hg, s.pairs(), hchunks, st);
+    } else {
+        if (s.d == 128) return launch_box_dtd<DT_F32, 128>(p, hg, s.pairs(), hchunks, st);
+        if (s.d == 64) return launch_box_dtd<DT_F32, 64>(p, hg, s.pairs(), hchunks, st);
+    }
+    return hipErrorInvalidValue;
+}
 
 hipError_t launch_block_logits_summary(const Dims& s, const void* q, const void* Kbar, float* dst, hipStream_t st)
 {

@@ -96,7 +96,94 @@ hipError_t launch_dtd(const Dims& s, const void* K, const void* V, void* Kbar, v
     return hipGetLastError();
 }
 
+// Box summaries (Quest, as analysed in "COBS: Cumulant Order Block Sparse
+// Attention", section on escaping the first-order ceiling): the element-wise
+// minimum and maximum of each block's keys, Kbox [pairs, nb, 2, d].  Strict
+// comparisons in token order keep the first of equal values (so -0 and +0
+// resolve the same way everywhere); a minimum or maximum of stored values is a
+// stored value, so nothing is rounded.
+template <int DT, int D>
+__global__ void __launch_bounds__(kNW * 64) box_kernel(const char* K, char* Kbox, int n, int L, int nb, long long total)
+{
+    using Gm = RowGeom<DT, D>;
+    constexpr int LPR = Gm::lpr, RPW = Gm::rpw, EPL = Gm::epl, RB = Gm::row_bytes;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int gi = lane / LPR, li = lane % LPR;
+    const long long gblk = ((long long)blockIdx.x * kNW + wave) * RPW + gi;
+    if (gblk >= total) return;  // no cross-lane operations below
+    const long long pair = gblk / nb;
+    const int blk = (int)(gblk - pair * nb);
+    const int t0 = blk * L, c = min(L, n - t0);
+    const char* kp = K + ((size_t)pair * n + t0) * RB + li * 16;
+
+    float lo[EPL], hi[EPL];
+    {
+        float kf[EPL];
+        unpack<DT>(ld16_nt(kp), kf);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) lo[e] = hi[e] = kf[e];
+    }
+    for (int i = 1; i < c; i += kU) {
+        uint4 kr[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) kr[u] = ld16_nt(kp + (size_t)min(i + u, c - 1) * RB);
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            if (i + u < c) {  // tokens in order
+                float kf[EPL];
+                unpack<DT>(kr[u], kf);
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) {
+                    if (kf[e] < lo[e]) lo[e] = kf[e];
+                    if (kf[e] > hi[e]) hi[e] = kf[e];
+                }
+            }
+        }
+    }
+    uint32_t wl[4], wh[4];
+    if constexpr (DT == DT_F32) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            wl[e] = __float_as_uint(lo[e]);
+            wh[e] = __float_as_uint(hi[e]);
+        }
+    } else {  // the values are bfloat16 widened exactly: keep their upper halves
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            wl[e] = (__float_as_uint(lo[2 * e]) >> 16) | (__float_as_uint(lo[2 * e + 1]) & 0xffff0000u);
+            wh[e] = (__float_as_uint(hi[2 * e]) >> 16) | (__float_as_uint(hi[2 * e + 1]) & 0xffff0000u);
+        }
+    }
+    char* out = Kbox + ((size_t)pair * nb + blk) * 2 * RB + li * 16;
+    *reinterpret_cast<uint4*>(out) = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+    *reinterpret_cast<uint4*>(out + RB) = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+}
+
+template <int DT, int D>
+hipError_t launch_box_dtd(const Dims& s, const void* K, void* Kbox, hipStream_t st)
+{
+    using Gm = RowGeom<DT, D>;
+    const long long total = (long long)s.pairs() * s.nb;
+    const long long per_wg = (long long)kNW * Gm::rpw;
+    const long long wgs = (total + per_wg - 1) / per_wg;
+    box_kernel<DT, D><<<dim3((unsigned)wgs), dim3(kNW * 64), 0, st>>>(static_cast<const char*>(K),
+                                                                        static_cast<char*>(Kbox), s.n, s.L, s.nb, total);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_box(const Dims& s, const void* K, void* Kbox, hipStream_t st)
+{
+    if (s.dtype == DT_BF16) {
+        if (s.d == 128) return launch_box_dtd<DT_BF16, 128>(s, K, Kbox, st);
+        if (s.d == 64) return launch_box_dtd<DT_BF16, 64>(s, K, Kbox, st);
+    } else {
+        if (s.d == 128) return launch_box_dtd<DT_F32, 128>(s, K, Kbox, st);
+        if (s.d == 64) return launch_box_dtd<DT_F32, 64>(s, K, Kbox, st);
+    }
+    return hipErrorInvalidValue;
+}
 
 hipError_t launch_summary(const Dims& s, const void* K, const void* V, void* Kbar, void* Vbar, hipStream_t st)
 {

@@ -50,7 +50,7 @@ class Workload:
     block_size: int
     dtype: str  # "f32" or "bf16"
     k: int  # blocks read exactly per KV head
-    score_mode: str  # "summary" or "exact_mass"
+    score_mode: str  # "summary", "exact_mass" or "box"
     proxies: bool  # one count-aware proxy per unread block
     keys: str  # "heavy_hitters" or "clusters"
     n_clusters: int = 64
@@ -89,6 +89,8 @@ WORKLOADS = {
         Workload("weighted_coreset_128k", 1004, 4, 28, 4, 128, 131072, 64, "bf16", 8, "summary", True, "clusters",
                  coreset=2048,
                  description="128K context, G=7: top-8 blocks + 2048 weighted coreset tokens + proxies"),
+        Workload("llama3_8b_layer_b32_box", 1002, 32, 32, 8, 128, 32768, 64, "bf16", 5, "box", True, "clusters",
+                 description="the headline layer with blocks ranked by their min/max key box (Quest)"),
     ]
 }
 

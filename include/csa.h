@@ -74,8 +74,9 @@ typedef enum csa_status {
 typedef enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
 
 typedef enum csa_score_mode {
-    CSA_SCORE_SUMMARY = 0,   /* first-order score from the mean key  [COBS] Eq. (18) */
-    CSA_SCORE_EXACT_MASS = 1 /* exact block mass from every key ("OSA")             */
+    CSA_SCORE_SUMMARY = 0,    /* first-order score from the mean key  [COBS] Eq. (18) */
+    CSA_SCORE_EXACT_MASS = 1, /* exact block mass from every key ("OSA")             */
+    CSA_SCORE_BOX = 2         /* best logit over the block's min/max key box (Quest) */
 } csa_score_mode;
 
 typedef enum csa_proxy_mode {
@@ -88,7 +89,8 @@ typedef enum csa_entry {
     CSA_WS_BLOCK_SCORE_EXACT_MASS = 1,
     CSA_WS_SPARSE_DECODE_ATTN = 2,
     CSA_WS_DENSE_DECODE_ATTN = 3,
-    CSA_WS_SELECTIVE_DECODE_STEP = 4
+    CSA_WS_SELECTIVE_DECODE_STEP = 4,
+    CSA_WS_BLOCK_SCORE_BOX = 5
 } csa_entry;
 
 typedef struct csa_shape {
@@ -115,16 +117,28 @@ int kv_summary_build(const csa_shape* shape, const void* K, const void* V, void*
                      hipStream_t stream);
 
 /*
+ * kv_box_build -- per block, the element-wise minimum and maximum of its keys:
+ * the axis-aligned bounding box that Quest caches, as analysed in [COBS]
+ * (section on escaping the first-order ceiling).  Reads K [B, Hkv, n, d];
+ * writes Kbox [B, Hkv, nb, 2, d] (row 0 the minimum, row 1 the maximum), in
+ * the storage dtype: a minimum or maximum of stored values is stored exactly.
+ * Run once per cache (after prefill); no workspace.
+ */
+int kv_box_build(const csa_shape* shape, const void* K, void* Kbox, hipStream_t stream);
+
+/*
  * block_score -- the score by which blocks are ranked, per KV head.
  * Per query head h and block b the block logit is
  *   SUMMARY:    l_hb = scale q_h . Kbar_b + ln c_b         (keys = Kbar)  [COBS] Eq. (18)
  *   EXACT_MASS: l_hb = ln m_hb = ln sum_{i in b} e^{s_i}   (keys = K)     [COBS] Eq. (1)
+ *   BOX:        l_hb = scale sum_t max(q_t lo_bt, q_t hi_bt) (keys = Kbox), the
+ *               largest logit any point of the block's key box could give
  * and the score of block b of KV head j is
  *   G = 1: l_hb (ranking by log-mass, [COBS] Eq. (5) with G = 1);
  *   G > 1: ln sum_{h in group j} exp(l_hb - ln sum_b' e^{l_hb'}),
  *          the logarithm of the additive GQA score of [COBS] Eq. (5).
  * Writes scores [B, Hkv, nb].  Workspace: csa_workspace_size(shape,
- * CSA_WS_BLOCK_SCORE_SUMMARY or _EXACT_MASS, 0, 0) bytes (0 when G = 1).
+ * CSA_WS_BLOCK_SCORE_SUMMARY, _EXACT_MASS or _BOX, 0, 0) bytes (0 when G = 1).
  */
 int block_score(const csa_shape* shape, csa_score_mode mode, const void* q, const void* keys,
                 float* scores, void* ws, size_t ws_bytes, hipStream_t stream);
@@ -180,8 +194,9 @@ int dense_decode_attn(const csa_shape* shape, const void* q, const void* K, cons
  * (bfloat16, G <= 8, k <= 32, nb <= 2048, B * Hkv >= 32) one kernel per KV head
  * reads Kbar once, keeps the logits on chip for both uses, selects the blocks
  * and attends; otherwise the three entry points run in turn.
- * keys = Kbar (SUMMARY) or K (EXACT_MASS) as for block_score; Kbar may be NULL
- * in EXACT_MASS mode without proxies.  scores [B, Hkv, nb] and
+ * keys = Kbar (SUMMARY) or K (EXACT_MASS) as for block_score (BOX scores are
+ * CSA_ERR_UNSUPPORTED here: they need Kbox besides Kbar; use the three entry
+ * points); Kbar may be NULL in EXACT_MASS mode without proxies.  scores [B, Hkv, nb] and
  * sel [B, Hkv, min(k, nb)] are written when not NULL.  0 <= k; k = 0 with no
  * proxies and m = 0 is CSA_ERR_INVALID_ARG.  Workspace: csa_workspace_size(
  * shape, CSA_WS_SELECTIVE_DECODE_STEP, k, m) bytes.

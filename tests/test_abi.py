@@ -32,8 +32,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = set(declared_functions())
-    assert {"kv_summary_build", "block_score", "topk_select", "sparse_decode_attn", "dense_decode_attn",
-            "selective_decode_step", "csa_workspace_size", "csa_status_str", "csa_last_error"} <= names
+    assert {"kv_summary_build", "kv_box_build", "block_score", "topk_select", "sparse_decode_attn",
+            "dense_decode_attn", "selective_decode_step", "csa_workspace_size", "csa_status_str",
+            "csa_last_error"} <= names
 
 
 def test_library_exports_every_declared_function(L):
@@ -82,7 +83,9 @@ def test_shape_validation(L, bad, code, msg):
     assert msg in L.csa_last_error()
     assert L.dense_decode_attn(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == code
     assert L.kv_summary_build(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None) == code
+    assert L.kv_box_build(ctypes.byref(s), FAKE, FAKE, None) == code
     assert L.block_score(ctypes.byref(s), 0, FAKE, FAKE, FAKE, None, 0, None) == code
+    assert L.block_score(ctypes.byref(s), 2, FAKE, FAKE, FAKE, None, 0, None) == code
     assert L.csa_workspace_size(ctypes.byref(s), 2, 1, 0) == 0
 
 
@@ -121,6 +124,16 @@ def test_workspace_is_checked_before_launch(L):
     assert bneed == 1 * 32 * 512 * 4
     assert L.block_score(ctypes.byref(s), 0, FAKE, FAKE, FAKE, None, 0, None) == csa.CSA_ERR_WORKSPACE
     assert L.block_score(ctypes.byref(s), 9, FAKE, FAKE, FAKE, None, 0, None) == csa.CSA_ERR_INVALID_ARG
+    assert L.csa_workspace_size(ctypes.byref(s), csa.CSA_WS_BLOCK_SCORE_BOX, 0, 0) == bneed
+    assert L.block_score(ctypes.byref(s), csa.CSA_SCORE_BOX, FAKE, FAKE, FAKE, None, 0, None) == csa.CSA_ERR_WORKSPACE
+
+
+def test_box_build_argument_checks(L):
+    s = shape()
+    assert L.kv_box_build(ctypes.byref(s), None, FAKE, None) == csa.CSA_ERR_INVALID_ARG
+    assert L.kv_box_build(ctypes.byref(s), FAKE, FAKE + 8, None) == csa.CSA_ERR_INVALID_ARG
+    assert b"aligned" in L.csa_last_error()
+    assert L.kv_box_build(None, FAKE, FAKE, None) == csa.CSA_ERR_INVALID_ARG
 
 
 def test_workspace_size_with_no_exact_or_weighted_tokens(L):
@@ -165,6 +178,8 @@ def test_decode_step_argument_checks(L):
     s = shape()
     assert step(L, None) == csa.CSA_ERR_INVALID_ARG
     assert step(L, s, mode=4) == csa.CSA_ERR_INVALID_ARG
+    assert step(L, s, mode=csa.CSA_SCORE_BOX) == csa.CSA_ERR_UNSUPPORTED
+    assert b"Kbox" in L.csa_last_error()
     assert step(L, s, proxy=3) == csa.CSA_ERR_INVALID_ARG
     assert step(L, s, k=0, proxy=0) == csa.CSA_ERR_INVALID_ARG
     assert b"empty virtual-token set" in L.csa_last_error()

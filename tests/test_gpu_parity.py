@@ -93,7 +93,8 @@ def gpu_pipeline(w, data, k=None, mode=None, proxies=None):
     proxies = w.proxies if proxies is None else proxies
     q, K, V = dev(data["q"]), dev(data["K"]), dev(data["V"])
     Kbar, Vbar = csa.kv_summary_build(K, V, w.block_size)
-    keys = Kbar if mode == "summary" else K
+    Kbox = csa.kv_box_build(K, w.block_size) if mode == "box" else None
+    keys = {"summary": Kbar, "exact_mass": K, "box": Kbox}[mode]
     scores = csa.block_score(q, keys, mode, w.block_size, n_tokens=w.n_tokens)
     sel = csa.topk_select(scores, k)
     ti = dev(data["tok_idx"]) if "tok_idx" in data else None
@@ -101,8 +102,11 @@ def gpu_pipeline(w, data, k=None, mode=None, proxies=None):
     out, lse = csa.sparse_decode_attn(q, K, V, Kbar, Vbar, sel, w.block_size, proxies=proxies, tok_idx=ti,
                                       tok_logw=tw)
     torch.cuda.synchronize()
-    return {"Kbar": host(Kbar), "Vbar": host(Vbar), "score": host(scores), "sel": host(sel), "out": host(out),
-            "lse": host(lse)}
+    r = {"Kbar": host(Kbar), "Vbar": host(Vbar), "score": host(scores), "sel": host(sel), "out": host(out),
+         "lse": host(lse)}
+    if Kbox is not None:
+        r["Kbox"] = host(Kbox)
+    return r
 
 
 def oracle_pipeline(w, data, k=None, mode=None, proxies=None):
@@ -112,12 +116,17 @@ def oracle_pipeline(w, data, k=None, mode=None, proxies=None):
     B = data["q"].shape[0]
     shp = oshape(w, B=B, Hkv=data["K"].shape[1])
     Kbar, Vbar = O.kv_summary_build(shp, data["K"], data["V"])
-    md = O.SUMMARY if mode == "summary" else O.EXACT_MASS
-    score = O.block_score(shp, md, data["q"], Kbar if mode == "summary" else data["K"])
+    Kbox = O.kv_box_build(shp, data["K"]) if mode == "box" else None
+    md = {"summary": O.SUMMARY, "exact_mass": O.EXACT_MASS, "box": O.BOX}[mode]
+    keys = {"summary": Kbar, "exact_mass": data["K"], "box": Kbox}[mode]
+    score = O.block_score(shp, md, data["q"], keys)
     sel, margin = O.topk_select(score, k)
     out, lse = O.sparse_decode_attn(shp, data["q"], data["K"], data["V"], Kbar, Vbar, sel, proxies,
                                     data.get("tok_idx"), data.get("tok_logw"))
-    return {"Kbar": Kbar, "Vbar": Vbar, "score": score, "sel": sel, "margin": margin, "out": out, "lse": lse}
+    r = {"Kbar": Kbar, "Vbar": Vbar, "score": score, "sel": sel, "margin": margin, "out": out, "lse": lse}
+    if Kbox is not None:
+        r["Kbox"] = Kbox
+    return r
 
 
 def bits(a):
@@ -128,6 +137,8 @@ def bits(a):
 def compare_pipelines(w, g, o, what):
     assert np.array_equal(bits(g["Kbar"]), bits(o["Kbar"])), f"{what}: Kbar not bit-exact"
     assert np.array_equal(bits(g["Vbar"]), bits(o["Vbar"])), f"{what}: Vbar not bit-exact"
+    if "Kbox" in o:
+        assert np.array_equal(bits(g["Kbox"]), bits(o["Kbox"])), f"{what}: Kbox not bit-exact"
     assert_scores(g["score"], o["score"], what)
     assert_selection(g["sel"], o["sel"], o["score"], o["margin"], w.k, what)
     assert_out(g["out"], g["lse"], o["out"], o["lse"], w.dtype, what)
@@ -157,6 +168,7 @@ SMALL = [
     ("mha_exact_4k", small("exact_mass_mha_b8", batch=2, n_tokens=4096, n_kv_heads=3)),
     ("gqa_exact_4k", small("exact_mass_gqa_b8", batch=2, n_tokens=4096, n_kv_heads=2)),
     ("coreset_g7_8k", small("weighted_coreset_128k", batch=2, n_tokens=8192, n_kv_heads=2).with_(coreset=300)),
+    ("box_b2_4k", small("llama3_8b_layer_b32_box", batch=2, n_tokens=4096, n_kv_heads=2)),
 ]
 
 
@@ -166,7 +178,7 @@ def test_pipeline_small(name, w):
     compare_pipelines(w, gpu_pipeline(w, data), oracle_pipeline(w, data), name)
 
 
-@pytest.mark.parametrize("mode", ["summary", "exact_mass"])
+@pytest.mark.parametrize("mode", ["summary", "exact_mass", "box"])
 @pytest.mark.parametrize("proxies", [True, False])
 def test_tiny_mode_matrix(mode, proxies):
     """Single-head fp32 decode: {summary, exact mass} x {proxies, discard} at k = 8, and keeping
@@ -192,7 +204,7 @@ def test_pipeline_shapes(dtype, G, d, n, L):
     Hkv = 2
     w = W.Workload("shape_case", 0, 2, G * Hkv, Hkv, d, n, L, dtype, 3, "summary", True, "clusters")
     data = rand_inputs(100 + G + d + n, 2, G * Hkv, Hkv, d, n, dtype)
-    for mode in ("summary", "exact_mass"):
+    for mode in ("summary", "exact_mass", "box"):
         for proxies in (True, False):
             k = min(3, w.n_blocks)
             compare_pipelines(w.with_(k=k), gpu_pipeline(w, data, k=k, mode=mode, proxies=proxies),
@@ -307,7 +319,7 @@ def test_invalid_arguments_raise():
 # ---------------------------------------------------------------------------
 
 FULL = ["llama3_8b_layer_b1", "llama3_8b_layer_b32", "exact_mass_mha_b8", "exact_mass_gqa_b8",
-        "weighted_coreset_128k"]
+        "weighted_coreset_128k", "llama3_8b_layer_b32_box"]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -330,6 +342,8 @@ def test_full_size_sampled(name):
         gs = {"Kbar": g["Kbar"][b:b + 1, j:j + 1], "Vbar": g["Vbar"][b:b + 1, j:j + 1],
               "score": g["score"][b:b + 1, j:j + 1], "sel": g["sel"][b:b + 1, j:j + 1],
               "out": g["out"][b:b + 1, j * G:(j + 1) * G], "lse": g["lse"][b:b + 1, j * G:(j + 1) * G]}
+        if "Kbox" in g:
+            gs["Kbox"] = g["Kbox"][b:b + 1, j:j + 1]
         compare_pipelines(w, gs, o, f"{name} pair ({b},{j})")
 
 
@@ -452,4 +466,6 @@ def test_decode_step_full_size_sampled():
         gs = {"Kbar": g["Kbar"][b:b + 1, j:j + 1], "Vbar": g["Vbar"][b:b + 1, j:j + 1],
               "score": g["score"][b:b + 1, j:j + 1], "sel": g["sel"][b:b + 1, j:j + 1],
               "out": g["out"][b:b + 1, j * G:(j + 1) * G], "lse": g["lse"][b:b + 1, j * G:(j + 1) * G]}
+        if "Kbox" in g:
+            gs["Kbox"] = g["Kbox"][b:b + 1, j:j + 1]
         compare_pipelines(w, gs, o, f"step pair ({b},{j})")
