@@ -148,13 +148,14 @@ int block_score(const csa_shape* shape, csa_score_mode mode, const void* q, cons
     if (!aligned16(q) || !aligned16(keys) || !aligned4(scores))
         return fail(CSA_ERR_INVALID_ARG, "block_score: misaligned tensor");
     if (int rc = check_ws(block_score_ws(d), ws, ws_bytes)) return rc;
-    if (mode == CSA_SCORE_SUMMARY && csa::fused_summary_score_ok(d)) {
-        // one workgroup per KV head when there are enough of them, else the split kernels
+    if ((mode == CSA_SCORE_SUMMARY || mode == CSA_SCORE_BOX) && csa::fused_summary_score_ok(d)) {
+        // matrix cores; one workgroup per KV head when there are enough of them, else the split kernels
+        const bool box = mode == CSA_SCORE_BOX;
         const hipError_t e =
             d.pairs() >= csa::kFusedStepMinPairs
-                ? csa::launch_score_summary_fused(d, q, keys, scores, stream)
+                ? csa::launch_score_summary_fused(d, q, keys, scores, stream, box)
                 : csa::launch_score_summary_split(d, q, keys, d.G == 1 ? scores : static_cast<float*>(ws), scores,
-                                                  nullptr, 0, stream);
+                                                  nullptr, 0, stream, box);
         return e == hipSuccess ? CSA_OK : hip_fail(e, "block_score");
     }
     float* dst = d.G == 1 ? scores : static_cast<float*>(ws);

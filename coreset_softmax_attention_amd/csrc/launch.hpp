@@ -35,7 +35,9 @@ hipError_t launch_box(const Dims& s, const void* K, void* Kbox, hipStream_t st);
 // Summary mode with the logits, log-normalisers and group score in one kernel
 // (one workgroup per KV head); available when fused_summary_score_ok().
 bool fused_summary_score_ok(const Dims& s);
-hipError_t launch_score_summary_fused(const Dims& s, const void* q, const void* Kbar, float* scores, hipStream_t st);
+// box = true: box scores from Kbox rows ([min | max], 2d wide) instead of Kbar.
+hipError_t launch_score_summary_fused(const Dims& s, const void* q, const void* Kbar, float* scores, hipStream_t st,
+                                      bool box = false);
 // The same in two kernels for few KV heads: logits over (KV head, tile chunk)
 // workgroups into `logits` ([B, Hq, nb]; may be `scores` when G == 1), then one
 // workgroup per KV head for the group scores (to `scores`, may be null) and,
@@ -46,7 +48,7 @@ bool split_select_ok(const Dims& s, int k);
 bool score_finish_ok(const Dims& s);
 hipError_t launch_score_finish(const Dims& s, const float* logits, float* scores, int32_t* sel, int k, hipStream_t st);
 hipError_t launch_score_summary_split(const Dims& s, const void* q, const void* Kbar, float* logits, float* scores,
-                                      int32_t* sel, int k, hipStream_t st);
+                                      int32_t* sel, int k, hipStream_t st, bool box = false);
 
 // ---- top-k -----------------------------------------------------------------
 hipError_t launch_topk(int rows, int nb, int k, const float* scores, int32_t* sel, hipStream_t st);

@@ -454,10 +454,39 @@ __device__ __forceinline__ void group_scores_in_lds(float* lsm, float* lse_h, in
     }
 }
 
-template <int D>
+// The query operand of the block-logit product.  Summary rows (D = d): q
+// itself.  Box rows (D = 2d, the block's [minimum | maximum] keys): the vector
+// [min(q, 0) | max(q, 0)], since per coordinate max(q lo, q hi) is q hi when
+// q >= 0 and q lo otherwise, so the best logit over the box is one dot product.
+template <int D, bool BOX>
+__device__ __forceinline__ void load_score_q(const char* q_first_head, int nh, int lane, bf16x8_t (&bq)[D / 32])
+{
+    if constexpr (!BOX) {
+        load_q_operand<D>(q_first_head, nh, lane, bq);
+    } else {
+        constexpr int DQ = D / 2;  // head_dim
+        const int n16 = lane & 15, g16 = lane >> 4;
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) {
+            const int c = 4 * s + g16;  // 16-byte chunk of the 2d-vector
+            const bool low_half = c < DQ / 8;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (n16 < nh) v = ld16(q_first_head + (size_t)n16 * DQ * 2 + (low_half ? c : c - DQ / 8) * 16);
+            uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t neg = ((w[i] & 0x80008000u) >> 15) * 0xffffu;  // bfloat16 lanes with the sign set
+                w[i] &= low_half ? neg : ~neg;
+            }
+            bq[s] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+        }
+    }
+}
+
+template <int D, bool BOX>
 __global__ void __launch_bounds__(kFusedWaves * 64) score_summary_fused_kernel(const FusedScoreParams p)
 {
-    constexpr int RB = D * 2, KS = D / 32, NW = kFusedWaves;
+    constexpr int RB = D * 2, KS = D / 32, NW = kFusedWaves, QB = BOX ? D : RB;  // QB: bytes per query row
     extern __shared__ float lsm[];  // [G][nb] block logits
     __shared__ float lse_h[8];
     const int lane = threadIdx.x & 63;
@@ -465,7 +494,7 @@ __global__ void __launch_bounds__(kFusedWaves * 64) score_summary_fused_kernel(c
     const int pair = blockIdx.x, b = pair / p.Hkv, j = pair - b * p.Hkv;
 
     bf16x8_t bq[KS];
-    load_q_operand<D>(p.q + ((size_t)b * p.Hq + (size_t)j * p.G) * RB, p.G, lane, bq);
+    load_score_q<D, BOX>(p.q + ((size_t)b * p.Hq + (size_t)j * p.G) * QB, p.G, lane, bq);
     const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(p.Kbar + (size_t)pair * p.nb * RB, (uint32_t)p.nb * RB);
     for (int base = wave * 32; base < p.nb; base += 2 * NW * 32) {  // two tiles in flight
         KeyTile<D> t0, t1;
@@ -480,10 +509,10 @@ __global__ void __launch_bounds__(kFusedWaves * 64) score_summary_fused_kernel(c
 }
 
 // Split logits: workgroup (pair, chunk) computes tiles chunk * kSplitWaves + wave.
-template <int D>
+template <int D, bool BOX>
 __global__ void __launch_bounds__(kSplitWaves * 64) score_logits_split_kernel(const FusedScoreParams p)
 {
-    constexpr int RB = D * 2, KS = D / 32;
+    constexpr int RB = D * 2, KS = D / 32, QB = BOX ? D : RB;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int pair = blockIdx.x / p.chunks, chunk = blockIdx.x - pair * p.chunks;
@@ -491,7 +520,7 @@ __global__ void __launch_bounds__(kSplitWaves * 64) score_logits_split_kernel(co
     const int base = (chunk * kSplitWaves + wave) * 32;
     if (base >= p.nb) return;  // whole wave; no barrier in this kernel
     bf16x8_t bq[KS];
-    load_q_operand<D>(p.q + ((size_t)b * p.Hq + (size_t)j * p.G) * RB, p.G, lane, bq);
+    load_score_q<D, BOX>(p.q + ((size_t)b * p.Hq + (size_t)j * p.G) * QB, p.G, lane, bq);
     const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(p.Kbar + (size_t)pair * p.nb * RB, (uint32_t)p.nb * RB);
     KeyTile<D> t;
     load_key_tile<D>(kr, base, lane, t);
@@ -546,7 +575,7 @@ bool fused_summary_score_ok(const Dims& s)
     return s.dtype == DT_BF16 && s.G <= 8 && s.G * s.nb <= kFusedMaxLogits;
 }
 
-FusedScoreParams summary_params(const Dims& s, const void* q, const void* Kbar)
+FusedScoreParams summary_params(const Dims& s, const void* q, const void* Kbar, bool box)
 {
     FusedScoreParams p{};
     p.q = static_cast<const char*>(q);
@@ -556,21 +585,29 @@ FusedScoreParams summary_params(const Dims& s, const void* q, const void* Kbar)
     p.G = s.G;
     p.nb = s.nb;
     p.scale = s.scale;
-    p.ln_L = s.ln_L;
-    p.ln_last = s.ln_last;
+    p.ln_L = box ? 0.0f : s.ln_L;  // the box score has no count term
+    p.ln_last = box ? 0.0f : s.ln_last;
     return p;
 }
 
-hipError_t launch_score_summary_fused(const Dims& s, const void* q, const void* Kbar, float* scores, hipStream_t st)
+hipError_t launch_score_summary_fused(const Dims& s, const void* q, const void* Kbar, float* scores, hipStream_t st,
+                                      bool box)
 {
-    FusedScoreParams p = summary_params(s, q, Kbar);
+    FusedScoreParams p = summary_params(s, q, Kbar, box);
     p.scores = scores;
     const size_t shm = (size_t)s.G * s.nb * sizeof(float);
     const dim3 grid((unsigned)s.pairs()), block(kFusedWaves * 64);
-    if (s.d == 128)
-        score_summary_fused_kernel<128><<<grid, block, shm, st>>>(p);
-    else
-        score_summary_fused_kernel<64><<<grid, block, shm, st>>>(p);
+    if (box) {
+        if (s.d == 128)
+            score_summary_fused_kernel<256, true><<<grid, block, shm, st>>>(p);
+        else
+            score_summary_fused_kernel<128, true><<<grid, block, shm, st>>>(p);
+    } else {
+        if (s.d == 128)
+            score_summary_fused_kernel<128, false><<<grid, block, shm, st>>>(p);
+        else
+            score_summary_fused_kernel<64, false><<<grid, block, shm, st>>>(p);
+    }
     return hipGetLastError();
 }
 
@@ -580,9 +617,9 @@ bool split_select_ok(const Dims& s, int k)
 }
 
 hipError_t launch_score_summary_split(const Dims& s, const void* q, const void* Kbar, float* logits, float* scores,
-                                      int32_t* sel, int k, hipStream_t st)
+                                      int32_t* sel, int k, hipStream_t st, bool box)
 {
-    FusedScoreParams p = summary_params(s, q, Kbar);
+    FusedScoreParams p = summary_params(s, q, Kbar, box);
     p.logits = logits;
     p.scores = scores;
     p.sel = sel;
@@ -590,10 +627,17 @@ hipError_t launch_score_summary_split(const Dims& s, const void* q, const void* 
     const int tiles = (s.nb + 31) / 32;
     p.chunks = (tiles + kSplitWaves - 1) / kSplitWaves;
     const dim3 grid((unsigned)(s.pairs() * p.chunks)), block(kSplitWaves * 64);
-    if (s.d == 128)
-        score_logits_split_kernel<128><<<grid, block, 0, st>>>(p);
-    else
-        score_logits_split_kernel<64><<<grid, block, 0, st>>>(p);
+    if (box) {
+        if (s.d == 128)
+            score_logits_split_kernel<256, true><<<grid, block, 0, st>>>(p);
+        else
+            score_logits_split_kernel<128, true><<<grid, block, 0, st>>>(p);
+    } else {
+        if (s.d == 128)
+            score_logits_split_kernel<128, false><<<grid, block, 0, st>>>(p);
+        else
+            score_logits_split_kernel<64, false><<<grid, block, 0, st>>>(p);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || (s.G == 1 && k == 0)) return e;  // G == 1: the logits are the scores
     return launch_score_finish(s, logits, scores, sel, k, st);
