@@ -67,6 +67,13 @@ static void store(void* base, int dtype, size_t i, double x)
         ((uint16_t*)base)[i] = oracle_round_bf16(x);
 }
 
+int oracle_store_array(int dtype, size_t n, const double* x, void* out)
+{
+    if ((dtype != OR_F32 && dtype != OR_BF16) || (n && (!x || !out))) return -1;
+    for (size_t i = 0; i < n; ++i) store(out, dtype, i, x[i]);
+    return 0;
+}
+
 /* ----------------------------------------------------------------------------
  * Shape helpers
  * ------------------------------------------------------------------------- */

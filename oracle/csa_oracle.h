@@ -59,6 +59,10 @@ int oracle_kv_summary_build(const oracle_shape* s, const void* K, const void* V,
  * the key dtype (a minimum or maximum of stored values is a stored value). */
 int oracle_kv_box_build(const oracle_shape* s, const void* K, void* Kbox);
 
+/* Round n fp64 values to the storage dtype (0 = f32, 1 = bf16 bit patterns),
+ * to nearest with ties to even, in one step. */
+int oracle_store_array(int dtype, size_t n, const double* x, void* out);
+
 /* Per-query-head block logits [B, Hq, nb].
  * mode 0 (summary):    scale * q_h . Kbar_b + ln c_b          (COBS Eq. (18))
  * mode 1 (exact mass): ln m_hb = LSE_{i in b} scale * q_h . K_i (COBS Eq. (1))

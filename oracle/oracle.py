@@ -10,6 +10,7 @@ dtype float32 (binary32) or uint16 (bfloat16 bit patterns); every result is fp64
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 from dataclasses import dataclass
@@ -20,7 +21,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "csa_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "libcsa_oracle.so")
 
-SUMMARY, EXACT_MASS, BOX = 0, 1, 2
+SUMMARY, EXACT_MASS, BOX, COBS2 = 0, 1, 2, 3
+COBS_RANK = 4  # scaled eigenvectors per block in the second-order descriptor
 
 
 def build(force: bool = False) -> str:
@@ -103,6 +105,10 @@ def _load():
         lib.oracle_block_mass.argtypes = [SP, P, P, P, P, P]
         lib.oracle_round_bf16.argtypes = [ctypes.c_double]
         lib.oracle_round_bf16.restype = ctypes.c_uint16
+        lib.oracle_kv_box_build.argtypes = [SP, P, P]
+        lib.oracle_kv_box_build.restype = I
+        lib.oracle_store_array.argtypes = [I, ctypes.c_size_t, P, P]
+        lib.oracle_store_array.restype = I
         for f in ("oracle_kv_summary_build", "oracle_block_logits", "oracle_group_score",
                   "oracle_topk", "oracle_attend", "oracle_dense", "oracle_block_mass"):
             getattr(lib, f).restype = I
@@ -149,9 +155,67 @@ def kv_box_build(shape: Shape, K):
     return Kbox
 
 
+def store_array(shape_or_dtype, x):
+    """fp64 array -> stored array (binary32, or bfloat16 bit patterns), rounded once."""
+    dt = shape_or_dtype.dtype if isinstance(shape_or_dtype, Shape) else shape_or_dtype
+    x = np.ascontiguousarray(x, np.float64)
+    out = np.empty(x.shape, np.float32 if dt == "f32" else np.uint16)
+    _check(_load().oracle_store_array(0 if dt == "f32" else 1, x.size, _ptr(x), _ptr(out)), "store_array")
+    return out
+
+
+def cov_build(shape: Shape, K, Kbar=None, rank: int = COBS_RANK):
+    """Second-order block descriptors of "COBS: Cumulant Order Block Sparse Attention": per
+    block the mean key and the top-`rank` scaled eigenvectors xi_i = sqrt(lambda_i) u_i of the
+    within-block key covariance Sigma_b = (1/c) sum_i (k_i - kbar)(k_i - kbar)^T (the second
+    cumulant of the block's keys; the low-rank spectral form of the section on compressing the
+    covariance).  Returns [B, Hkv, nb, 1 + rank, d] in the storage dtype: row 0 the mean key
+    (the same bits as kv_summary_build), rows 1.. the eigenvectors by decreasing eigenvalue,
+    each signed so that its largest-magnitude coordinate is positive."""
+    B, Hkv, n, d, L, nb = shape.batch, shape.n_kv_heads, shape.n_tokens, shape.head_dim, shape.block_size, \
+        shape.n_blocks
+    Kf = widen(shape, _stored(shape, K, (B, Hkv, n, d)))
+    if Kbar is None:
+        Kbar, _ = kv_summary_build(shape, K, K)
+    xi = np.zeros((B, Hkv, nb, rank, d), np.float64)
+    for b in range(B):
+        for j in range(Hkv):
+            for blk in range(nb):
+                X = Kf[b, j, blk * L:min(n, (blk + 1) * L)]
+                Xc = X - X.mean(axis=0)
+                lam, U = np.linalg.eigh(Xc.T @ Xc / X.shape[0])  # ascending
+                for i in range(min(rank, d)):
+                    u = U[:, d - 1 - i]
+                    u = u if u[np.argmax(np.abs(u))] > 0 else -u
+                    xi[b, j, blk, i] = math.sqrt(max(lam[d - 1 - i], 0.0)) * u
+    out = np.empty((B, Hkv, nb, 1 + rank, d), shape.np_dtype)
+    out[:, :, :, 0] = np.asarray(Kbar).reshape(B, Hkv, nb, d)
+    out[:, :, :, 1:] = store_array(shape, xi)
+    return out
+
+
+def cobs2_logits(shape: Shape, q, Kcov):
+    """Second-order block logits [B, Hq, nb] ([COBS] cumulant expansion truncated at second
+    order, with the rank-r covariance): scale q.kbar_b + ln c_b + (1/2) scale^2 sum_i (q.xi_i)^2,
+    from the stored descriptors."""
+    B, Hq, Hkv, d, nb = shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.n_blocks
+    G = Hq // Hkv
+    qf = widen(shape, _stored(shape, q, (B, Hq, d)))
+    C = widen(shape, np.asarray(Kcov)).reshape(B, Hkv, nb, -1, d)
+    scale = shape.scale if shape.scale else 1.0 / math.sqrt(d)
+    counts = np.array([min(shape.block_size, shape.n_tokens - i * shape.block_size) for i in range(nb)], np.float64)
+    out = np.empty((B, Hq, nb), np.float64)
+    for h in range(Hq):
+        dots = np.einsum("bd,bkrd->bkr", qf[:, h], C[:, h // G])  # [B, nb, 1 + r]
+        out[:, h] = scale * dots[:, :, 0] + np.log(counts) + 0.5 * scale * scale * (dots[:, :, 1:] ** 2).sum(-1)
+    return out
+
+
 def block_logits(shape: Shape, mode: int, q, keys):
     """Per-query-head block logits [B, Hq, nb]: first-order summary score, exact ln m_b, or the
     largest logit over the block's key box."""
+    if mode == COBS2:
+        return cobs2_logits(shape, q, keys)
     rows = {SUMMARY: shape.n_blocks, EXACT_MASS: shape.n_tokens, BOX: 2 * shape.n_blocks}[mode]
     q = _stored(shape, q, (shape.batch, shape.n_q_heads, shape.head_dim))
     if mode == BOX:  # [B, Hkv, nb, 2, d] is [B, Hkv, 2 nb, d] in memory

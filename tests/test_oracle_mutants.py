@@ -1,7 +1,8 @@
 """The pins are strong enough: each plausible mistake planted in a copy of the oracle's C
-source (a dropped term, a wrong sign, a wrong operand or index, a wrong tie rule) makes at
-least one pin of test_oracle_pins fail.  The mutants are built on the CPU into a temporary
-directory; the real oracle is untouched and restored afterwards."""
+source or of its Python front end (a dropped term, a wrong sign, a wrong operand or index, a
+wrong tie rule, a wrong normalisation) makes at least one pin of test_oracle_pins fail.  The
+mutants are built on the CPU (C ones into a temporary directory); the real oracle is
+untouched and restored afterwards."""
 import os
 import subprocess
 
@@ -87,3 +88,59 @@ def test_pins_catch_planted_mistake(name, tmp_path):
     finally:
         O.use_library(None)
     assert failed, f"no pin caught the mutant {name!r}"
+
+
+# The second-order descriptors and logits live in the oracle's Python front end;
+# their mutants are planted in a copy of that module.
+PY_SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "oracle.py")
+PY_MUTANTS = {
+    "second-order term without the one half": ("+ 0.5 * scale * scale *", "+ 1.0 * scale * scale *"),
+    "covariance with the sample divisor": ("Xc.T @ Xc / X.shape[0]", "Xc.T @ Xc / (X.shape[0] - 1)"),
+    "eigenvectors not scaled by the root eigenvalue": ("math.sqrt(max(lam[d - 1 - i], 0.0)) * u",
+                                                       "max(lam[d - 1 - i], 0.0) * u"),
+    "smallest eigendirections kept": ("u = U[:, d - 1 - i]", "u = U[:, i]"),
+}
+PY_BATTERY = [
+    P.test_cov_descriptor_is_the_top_eigen_truncation,
+    P.test_second_order_term_is_half_the_logit_variance_at_full_rank,
+    P.test_equal_logit_block_has_no_second_order_term,
+    P.test_second_order_estimate_tracks_the_exact_mass,
+]
+
+
+def _py_failures(module):
+    failed = []
+    saved = P.O
+    P.O = module
+    try:
+        for fn in PY_BATTERY:
+            try:
+                fn()
+            except (AssertionError, ValueError):
+                failed.append(fn.__name__)
+    finally:
+        P.O = saved
+    return failed
+
+
+def test_unmutated_python_oracle_passes_its_battery():
+    assert _py_failures(O) == []
+
+
+@pytest.mark.parametrize("name", sorted(PY_MUTANTS))
+def test_pins_catch_planted_python_mistake(name):
+    import types
+
+    old, new = PY_MUTANTS[name]
+    src = open(PY_SRC).read()
+    assert src.count(old) >= 1, f"mutation site for {name!r} not found"
+    import sys
+
+    mod = types.ModuleType("oracle_mutant")
+    mod.__file__ = PY_SRC  # the compiled C library is shared with the original
+    sys.modules["oracle_mutant"] = mod  # dataclasses look their module up
+    try:
+        exec(compile(src.replace(old, new), PY_SRC, "exec"), mod.__dict__)
+        assert _py_failures(mod), f"no pin caught the mutant {name!r}"
+    finally:
+        del sys.modules["oracle_mutant"]

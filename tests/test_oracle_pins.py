@@ -553,3 +553,88 @@ def test_box_score_is_the_best_corner():
             best = max(float(np.dot(qh, np.where(np.array(c), hi, lo)))
                        for c in itertools.product((0, 1), repeat=d))
             assert abs(lg[0, h, blk] - best / math.sqrt(d)) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# second-order block score ([COBS]: the cumulant expansion of ln m_b truncated
+# at second order, ln c_b + q.kbar_b + (1/2) q^T Sigma_b q, with Sigma_b kept as
+# its top-r scaled eigenvectors xi_i = sqrt(lambda_i) u_i)
+# ---------------------------------------------------------------------------
+
+def explicit_covariance(X):
+    """(1/c) sum_i (x_i - mean)(x_i - mean)^T by an explicit loop over the tokens."""
+    X = np.asarray(X, np.float64)
+    mean = X.sum(axis=0) / X.shape[0]
+    S = np.zeros((X.shape[1], X.shape[1]))
+    for x in X:
+        S += np.outer(x - mean, x - mean)
+    return S / X.shape[0]
+
+
+def test_cov_descriptor_is_the_top_eigen_truncation():
+    """sum_i xi_i xi_i^T equals the best rank-r approximation of the block covariance
+    (computed here by an explicit loop and an SVD, not the oracle's eigh)."""
+    n, L, d = 96, 32, 16
+    shp = O.Shape(1, 1, 1, d, n, L, "f32")
+    _, K, _ = rand_case(40, 1, 1, 1, d, n, "f32")
+    C = O.cov_build(shp, K)
+    Kbar, _ = O.kv_summary_build(shp, K, K)
+    assert np.array_equal(C[0, 0, :, 0], Kbar[0, 0])  # row 0 is the stored mean key
+    for blk in range(shp.n_blocks):
+        S = explicit_covariance(K[0, 0, blk * L:(blk + 1) * L])
+        U, sv, _ = np.linalg.svd(S)
+        best = (U[:, :O.COBS_RANK] * sv[:O.COBS_RANK]) @ U[:, :O.COBS_RANK].T
+        xi = C[0, 0, blk, 1:].astype(np.float64)
+        got = xi.T @ xi
+        assert np.linalg.norm(got - best) <= 1e-6 * np.linalg.norm(best)
+        # ordered by decreasing eigenvalue, largest-magnitude coordinate positive
+        norms = np.linalg.norm(xi, axis=1)
+        assert np.all(np.diff(norms) <= 1e-6 * norms[0])
+        assert all(x[np.argmax(np.abs(x))] > 0 for x in xi)
+
+
+def test_second_order_term_is_half_the_logit_variance_at_full_rank():
+    """When r reaches the covariance's rank (blocks of at most r + 1 tokens), the quadratic term
+    (1/2) q^T Sigma_b q is exactly half the (population) variance of the block's logits."""
+    n, L, d = 40, 4, 32  # c = 4: rank <= 3 <= r
+    shp = O.Shape(1, 2, 1, d, n, L, "f32")
+    q, K, _ = rand_case(41, 1, 2, 1, d, n, "f32", qscale=2.0)
+    C = O.cov_build(shp, K)
+    second = O.block_logits(shp, O.COBS2, q, C) - O.block_logits(shp, O.SUMMARY, q, C[:, :, :, 0])
+    s = np.einsum("hd,nd->hn", q[0].astype(np.float64), K[0, 0].astype(np.float64)) / math.sqrt(d)
+    half_var = 0.5 * s.reshape(2, -1, L).var(axis=-1)
+    assert np.abs(second[0] - half_var).max() <= 1e-6 * np.abs(half_var).max()
+
+
+def test_equal_logit_block_has_no_second_order_term():
+    """Keys that differ only where the query is zero give equal logits: no curvature."""
+    n, L, d = 128, 32, 16
+    shp = O.Shape(1, 1, 1, d, n, L, "f32")
+    rng = np.random.default_rng(42)
+    q = np.zeros((1, 1, d), np.float32)
+    q[0, 0, :d // 2] = rng.standard_normal(d // 2)
+    K = np.repeat(rng.standard_normal((1, 1, 1, d)), n, axis=2).astype(np.float32)
+    K[0, 0, :, d // 2:] += rng.standard_normal((n, d // 2)).astype(np.float32)
+    C = O.cov_build(shp, K)
+    second = O.block_logits(shp, O.COBS2, q, C) - O.block_logits(shp, O.SUMMARY, q, C[:, :, :, 0])
+    assert np.abs(second).max() < 1e-12
+
+
+def test_second_order_estimate_tracks_the_exact_mass():
+    """For blocks whose logits spread little, the second-order estimate of ln m_b is closer to
+    the exact block mass than the first-order one, and its error shrinks like the third power
+    of the spread (the next cumulant)."""
+    n, L, d = 1024, 16, 8
+    shp = O.Shape(1, 1, 1, d, n, L, "f32")
+    errs = []
+    for spread in (0.2, 0.1):
+        rng = np.random.default_rng(43)
+        q = (rng.standard_normal((1, 1, d)) * spread * math.sqrt(d)).astype(np.float32)
+        K = rng.standard_normal((1, 1, n, d)).astype(np.float32)
+        C = O.cov_build(shp, K, rank=d)  # full rank: no truncation error
+        exact = O.block_logits(shp, O.EXACT_MASS, q, K)[0, 0]
+        first = O.block_logits(shp, O.SUMMARY, q, C[:, :, :, 0])[0, 0]
+        second = O.block_logits(shp, O.COBS2, q, C)[0, 0]
+        assert np.mean(np.abs(second - exact) < np.abs(first - exact)) > 0.9
+        errs.append(np.abs(second - exact).mean())
+    assert errs[1] < errs[0] / 4  # halving the spread cuts the error by about 8
