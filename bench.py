@@ -170,8 +170,10 @@ def step_bytes(w, m=0):
         per_read = nb * d * e + unread * d * e + k * L * 2 * d * e
     elif w.score_mode == "exact_mass":
         per_read = w.n_tokens * d * e + k * L * d * e + unread * 2 * d * e
-    else:
+    elif w.score_mode == "box":
         per_read = 2 * nb * d * e + unread * 2 * d * e + k * L * 2 * d * e
+    else:  # second-order: the mean key and four eigenvector rows of every block
+        per_read = 5 * nb * d * e + unread * d * e + k * L * 2 * d * e
     per_read += m * (2 * d * e + 8) + G * d * e
     per_write = G * (d + 1) * 4
     pairs = w.batch * w.n_kv_heads
@@ -228,8 +230,18 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     summary_ms = e0.elapsed_time(e1)
-    box = w.score_mode == "box"
-    Kbox0 = csa.kv_box_build(K0, w.block_size) if box else None
+    box = w.score_mode in ("box", "cobs2")  # scored from extra per-block summaries
+    Kbox0 = None
+    extra_ms = None
+    if box:
+        build = csa.kv_box_build if w.score_mode == "box" else csa.kv_cov_build
+        Kbox0 = build(K0, w.block_size)
+        torch.cuda.synchronize()
+        e0.record()
+        build(K0, w.block_size, Kbox0)
+        e1.record()
+        torch.cuda.synchronize()
+        extra_ms = e0.elapsed_time(e1)
     layers = [(K0, V0, Kbar0, Vbar0, Kbox0)]
     for _ in range(NL - 1):
         layers.append(tuple(None if x is None else x.clone() for x in layers[0]))
@@ -242,7 +254,7 @@ def main():
     out = torch.empty((B, Hq, w.head_dim), dtype=torch.float32, device=dev)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
     mode_entry = {"summary": csa.CSA_WS_BLOCK_SCORE_SUMMARY, "exact_mass": csa.CSA_WS_BLOCK_SCORE_EXACT_MASS,
-                  "box": csa.CSA_WS_BLOCK_SCORE_BOX}[w.score_mode]
+                  "box": csa.CSA_WS_BLOCK_SCORE_BOX, "cobs2": csa.CSA_WS_BLOCK_SCORE_COBS2}[w.score_mode]
     ws_score = torch.empty(max(1, csa.workspace_size(shape, mode_entry)), dtype=torch.uint8, device=dev)
     ws_attn = torch.empty(max(1, csa.workspace_size(shape, csa.CSA_WS_SPARSE_DECODE_ATTN, w.k, m)),
                           dtype=torch.uint8, device=dev)
@@ -251,7 +263,7 @@ def main():
 
     def score_select(layer):
         K, V, Kbar, Vbar, Kbox = layer
-        keys = {"summary": Kbar, "exact_mass": K, "box": Kbox}[w.score_mode]
+        keys = {"summary": Kbar, "exact_mass": K, "box": Kbox, "cobs2": Kbox}[w.score_mode]
         csa.block_score(q, keys, w.score_mode, w.block_size, n_tokens=w.n_tokens, scores=scores, ws=ws_score)
         csa.topk_select(scores, w.k, sel=sel)
 
@@ -265,7 +277,7 @@ def main():
         attend(layers[i % NL])
 
     def step(i):
-        if box:  # box scores need Kbox: the three entry points in turn
+        if box:  # box and second-order scores need their summaries: the three entry points in turn
             modular(i)
             return
         K, V, Kbar, Vbar, _ = layers[i % NL]
@@ -369,6 +381,7 @@ def main():
         "modular_breakdown_us": {"block_score+topk_select": score_ms * 1e3 if score_ms else None,
                                  "sparse_decode_attn": attn_ms * 1e3},
         "kv_summary_build_ms": summary_ms,
+        **({f"kv_{'box' if w.score_mode == 'box' else 'cov'}_build_ms": extra_ms} if extra_ms is not None else {}),
         "dense_decode_attn_ms": dense_ms,
         "step_vs_dense_speedup": (dense_ms / t_step) if dense_ms else None,
         "roofline": {

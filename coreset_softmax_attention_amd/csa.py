@@ -16,15 +16,18 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so"
 
 CSA_OK, CSA_ERR_INVALID_ARG, CSA_ERR_UNSUPPORTED, CSA_ERR_WORKSPACE, CSA_ERR_HIP = 0, -1, -2, -3, -4
 CSA_F32, CSA_BF16 = 0, 1
-CSA_SCORE_SUMMARY, CSA_SCORE_EXACT_MASS, CSA_SCORE_BOX = 0, 1, 2
+CSA_SCORE_SUMMARY, CSA_SCORE_EXACT_MASS, CSA_SCORE_BOX, CSA_SCORE_COBS2 = 0, 1, 2, 3
+CSA_COBS_RANK = 4
 CSA_PROXY_NONE, CSA_PROXY_COMPLEMENT = 0, 1
 CSA_WS_BLOCK_SCORE_SUMMARY, CSA_WS_BLOCK_SCORE_EXACT_MASS = 0, 1
 CSA_WS_SPARSE_DECODE_ATTN, CSA_WS_DENSE_DECODE_ATTN, CSA_WS_SELECTIVE_DECODE_STEP = 2, 3, 4
-CSA_WS_BLOCK_SCORE_BOX = 5
+CSA_WS_BLOCK_SCORE_BOX, CSA_WS_BLOCK_SCORE_COBS2 = 5, 6
 
-MODES = {"summary": CSA_SCORE_SUMMARY, "exact_mass": CSA_SCORE_EXACT_MASS, "box": CSA_SCORE_BOX}
+MODES = {"summary": CSA_SCORE_SUMMARY, "exact_mass": CSA_SCORE_EXACT_MASS, "box": CSA_SCORE_BOX,
+         "cobs2": CSA_SCORE_COBS2}
 _SCORE_WS = {"summary": CSA_WS_BLOCK_SCORE_SUMMARY, "exact_mass": CSA_WS_BLOCK_SCORE_EXACT_MASS,
-             "box": CSA_WS_BLOCK_SCORE_BOX}
+             "box": CSA_WS_BLOCK_SCORE_BOX, "cobs2": CSA_WS_BLOCK_SCORE_COBS2}
+_SUMMARY_ROWS = {"summary": None, "box": 2, "cobs2": 1 + CSA_COBS_RANK}  # rows per block of the keys
 
 
 class CsaError(RuntimeError):
@@ -56,6 +59,7 @@ _P, _I32, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
 _SIGS = {
     "kv_summary_build": [ctypes.POINTER(Shape), _P, _P, _P, _P, _P],
     "kv_box_build": [ctypes.POINTER(Shape), _P, _P, _P],
+    "kv_cov_build": [ctypes.POINTER(Shape), _P, _P, _P],
     "block_score": [ctypes.POINTER(Shape), ctypes.c_int, _P, _P, _P, _P, _SZ, _P],
     "topk_select": [_I32, _I32, _I32, _P, _P, _P],
     "sparse_decode_attn": [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _I32, _P, _P, _I32, ctypes.c_int,
@@ -170,15 +174,27 @@ def kv_box_build(K: torch.Tensor, block_size: int, Kbox=None):
     return Kbox
 
 
+def kv_cov_build(K: torch.Tensor, block_size: int, Kcov=None):
+    """Second-order descriptors: Kcov [B, Hkv, nb, 1 + CSA_COBS_RANK, d] (mean key, then the
+    top scaled eigenvectors of each block's key covariance)."""
+    dev = _dev(K, Kcov)
+    B, Hkv, n, d = K.shape
+    shape = Shape(B, Hkv, Hkv, d, n, block_size, _dtype_code(K), 0.0)
+    if Kcov is None:
+        Kcov = torch.empty((B, Hkv, shape.n_blocks, 1 + CSA_COBS_RANK, d), dtype=K.dtype, device=dev)
+    _check(lib().kv_cov_build(ctypes.byref(shape), _ptr(K), _ptr(Kcov), _stream(dev)), "kv_cov_build")
+    return Kcov
+
+
 def block_score(q: torch.Tensor, keys: torch.Tensor, mode: str, block_size: int, n_tokens: int | None = None,
                 scale: float = 0.0, scores=None, ws=None):
-    """Block scores [B, Hkv, nb].  keys = Kbar (mode 'summary'), K (mode 'exact_mass') or Kbox
-    (mode 'box'); n_tokens is needed in summary and box modes (the cache length the summaries
-    describe)."""
+    """Block scores [B, Hkv, nb].  keys = Kbar (mode 'summary'), K (mode 'exact_mass'), Kbox
+    (mode 'box') or Kcov (mode 'cobs2'); n_tokens is needed in every mode but 'exact_mass' (the
+    cache length the summaries describe)."""
     dev = _dev(q, keys, scores)
     B, Hq, d = q.shape
     Hkv = keys.shape[1]
-    if mode in ("summary", "box"):
+    if mode in _SUMMARY_ROWS:
         if n_tokens is None:
             raise ValueError(f"{mode} mode needs n_tokens")
         n = n_tokens
@@ -186,10 +202,11 @@ def block_score(q: torch.Tensor, keys: torch.Tensor, mode: str, block_size: int,
         n = keys.shape[2]
     shape = Shape(B, Hq, Hkv, d, n, block_size, _dtype_code(q), float(scale))
     nb = shape.n_blocks
-    if mode in ("summary", "box") and keys.shape[2] != nb:
+    if mode in _SUMMARY_ROWS and keys.shape[2] != nb:
         raise ValueError(f"the summaries have {keys.shape[2]} blocks, expected {nb}")
-    if mode == "box" and (keys.dim() != 5 or keys.shape[3] != 2):
-        raise ValueError("box mode needs Kbox [B, Hkv, nb, 2, d]")
+    rows = _SUMMARY_ROWS.get(mode)
+    if rows is not None and (keys.dim() != 5 or keys.shape[3] != rows):
+        raise ValueError(f"{mode} mode needs keys [B, Hkv, nb, {rows}, d]")
     scores = torch.empty((B, Hkv, nb), dtype=torch.float32, device=dev) if scores is None else scores
     ws, wsb = _workspace(shape, _SCORE_WS[mode], 0, 0, ws, dev)
     _check(lib().block_score(ctypes.byref(shape), MODES[mode], _ptr(q), _ptr(keys), _ptr(scores), _ptr(ws), wsb,

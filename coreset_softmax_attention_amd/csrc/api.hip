@@ -137,17 +137,36 @@ int kv_box_build(const csa_shape* shape, const void* K, void* Kbox, hipStream_t 
     return e == hipSuccess ? CSA_OK : hip_fail(e, "kv_box_build");
 }
 
+int kv_cov_build(const csa_shape* shape, const void* K, void* Kcov, hipStream_t stream)
+{
+    csa::Dims d;
+    if (int rc = make_dims(shape, &d)) return rc;
+    if (!K || !Kcov) return fail(CSA_ERR_INVALID_ARG, "kv_cov_build: NULL tensor pointer");
+    if (!aligned16(K) || !aligned16(Kcov)) return fail(CSA_ERR_INVALID_ARG, "kv_cov_build: tensors must be 16-byte aligned");
+    if (!csa::cov_build_ok(d))
+        return fail(CSA_ERR_UNSUPPORTED, "kv_cov_build: blocks of %d tokens (at most 64 supported)", d.L);
+    const hipError_t e = csa::launch_cov(d, K, Kcov, stream);
+    return e == hipSuccess ? CSA_OK : hip_fail(e, "kv_cov_build");
+}
+
 int block_score(const csa_shape* shape, csa_score_mode mode, const void* q, const void* keys, float* scores, void* ws,
                 size_t ws_bytes, hipStream_t stream)
 {
     csa::Dims d;
     if (int rc = make_dims(shape, &d)) return rc;
-    if (mode != CSA_SCORE_SUMMARY && mode != CSA_SCORE_EXACT_MASS && mode != CSA_SCORE_BOX)
+    if (mode != CSA_SCORE_SUMMARY && mode != CSA_SCORE_EXACT_MASS && mode != CSA_SCORE_BOX && mode != CSA_SCORE_COBS2)
         return fail(CSA_ERR_INVALID_ARG, "block_score: unknown mode %d", (int)mode);
+    if (mode == CSA_SCORE_COBS2 && !csa::fused_summary_score_ok(d))
+        return fail(CSA_ERR_UNSUPPORTED, "block_score: second-order scores need bfloat16, G <= 8 and G nb <= 16384");
     if (!q || !keys || !scores) return fail(CSA_ERR_INVALID_ARG, "block_score: NULL tensor pointer");
     if (!aligned16(q) || !aligned16(keys) || !aligned4(scores))
         return fail(CSA_ERR_INVALID_ARG, "block_score: misaligned tensor");
     if (int rc = check_ws(block_score_ws(d), ws, ws_bytes)) return rc;
+    if (mode == CSA_SCORE_COBS2) {
+        const hipError_t e =
+            csa::launch_score_cobs2(d, q, keys, d.G == 1 ? scores : static_cast<float*>(ws), scores, stream);
+        return e == hipSuccess ? CSA_OK : hip_fail(e, "block_score");
+    }
     if ((mode == CSA_SCORE_SUMMARY || mode == CSA_SCORE_BOX) && csa::fused_summary_score_ok(d)) {
         // matrix cores; one workgroup per KV head when there are enough of them, else the split kernels
         const bool box = mode == CSA_SCORE_BOX;
@@ -236,9 +255,9 @@ int selective_decode_step(const csa_shape* shape, csa_score_mode mode, const voi
 {
     csa::Dims d;
     if (int rc = make_dims(shape, &d)) return rc;
-    if (mode == CSA_SCORE_BOX)
-        return fail(CSA_ERR_UNSUPPORTED, "selective_decode_step: box scores need Kbox; call block_score, "
-                                         "topk_select and sparse_decode_attn");
+    if (mode == CSA_SCORE_BOX || mode == CSA_SCORE_COBS2)
+        return fail(CSA_ERR_UNSUPPORTED, "selective_decode_step: box and second-order scores need Kbox or Kcov; "
+                                         "call block_score, topk_select and sparse_decode_attn");
     if (mode != CSA_SCORE_SUMMARY && mode != CSA_SCORE_EXACT_MASS)
         return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: unknown mode %d", (int)mode);
     if (proxy_mode != CSA_PROXY_NONE && proxy_mode != CSA_PROXY_COMPLEMENT)
@@ -302,7 +321,8 @@ size_t csa_workspace_size(const csa_shape* shape, csa_entry entry, int32_t k, in
     switch (entry) {
     case CSA_WS_BLOCK_SCORE_SUMMARY:
     case CSA_WS_BLOCK_SCORE_EXACT_MASS:
-    case CSA_WS_BLOCK_SCORE_BOX: return block_score_ws(d);
+    case CSA_WS_BLOCK_SCORE_BOX:
+    case CSA_WS_BLOCK_SCORE_COBS2: return block_score_ws(d);
     case CSA_WS_SPARSE_DECODE_ATTN: {
         if (k < 0 || k > d.nb || m < 0) {
             fail(CSA_ERR_INVALID_ARG, "csa_workspace_size: k=%d or m=%d out of range", k, m);

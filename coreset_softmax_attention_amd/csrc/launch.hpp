@@ -32,6 +32,16 @@ hipError_t launch_group_score(const Dims& s, const float* logits, float* scores,
 // Box logits (Kbox [B, Hkv, nb, 2, d]); same destinations as the other logits.
 hipError_t launch_block_logits_box(const Dims& s, const void* q, const void* Kbox, float* dst, hipStream_t st);
 hipError_t launch_box(const Dims& s, const void* K, void* Kbox, hipStream_t st);
+// Second-order descriptors Kcov [B, Hkv, nb, 1 + kCobsRank, d]: the mean key,
+// then the top kCobsRank scaled eigenvectors of the block's key covariance.
+constexpr int kCobsRank = 4;
+bool cov_build_ok(const Dims& s);  // blocks of at most 64 tokens
+hipError_t launch_cov(const Dims& s, const void* K, void* Kcov, hipStream_t st);
+// Second-order block scores from Kcov (bfloat16, fused_summary_score_ok()); with
+// fewer than kFusedStepMinPairs KV heads the logits go through `logits`
+// ([B, Hq, nb], or the scores themselves when G == 1).
+hipError_t launch_score_cobs2(const Dims& s, const void* q, const void* Kcov, float* logits, float* scores,
+                              hipStream_t st);
 // Summary mode with the logits, log-normalisers and group score in one kernel
 // (one workgroup per KV head); available when fused_summary_score_ok().
 bool fused_summary_score_ok(const Dims& s);

@@ -527,6 +527,118 @@ __global__ void __launch_bounds__(kSplitWaves * 64) score_logits_split_kernel(co
     key_tile_logits<D>(p, t, bq, base, p.logits + (size_t)pair * p.G * p.nb, p.nb, lane);
 }
 
+// Second-order logits (COBS, cumulant expansion of ln m_b truncated at second
+// order): scale q.kbar_b + ln c_b + (1/2) scale^2 sum_i (q.xi_bi)^2 from the
+// descriptor rows Kcov [.., nb, 1 + kCobsRank, d].  For a tile of 32 blocks
+// [base, base + 32): the mean rows (tile row r -> block base + r) and four
+// sub-tiles of 8 blocks x 4 eigenvector rows (tile row r -> block
+// base + 8 u + r / 4, eigenvector r % 4), all through the same MFMA; an output
+// lane of a sub-tile holds the four eigenvector products of one block, so the
+// sum of squares needs no lane exchange.  The two parts meet in a per-wave LDS
+// tile tmp[8 heads][32 blocks] and go to dst[h * stride + b].
+template <int D>
+__device__ __forceinline__ void cobs2_tile_logits(const FusedScoreParams& p, __amdgpu_buffer_rsrc_t kr,
+                                                  const bf16x8_t (&bq)[D / 32], int base, float* dst, int stride,
+                                                  int lane, float (*tmp)[32])
+{
+    constexpr int RB = D * 2, KS = D / 32, NR = 1 + kCobsRank;
+    static_assert(kCobsRank == 4, "one output lane holds one block's four eigenvector products");
+    const int n16 = lane & 15, g16 = lane >> 4;
+    uint4 am[2][KS], ax[4][2][KS];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int tr = rb * 16 + n16;
+        const uint32_t om = (uint32_t)(base + tr) * NR * RB + g16 * 16;  // past nb: zeros
+#pragma unroll
+        for (int s = 0; s < KS; ++s) am[rb][s] = buffer_ld16(kr, om + s * 64);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t ox = ((uint32_t)(base + 8 * u + tr / 4) * NR + 1 + tr % 4) * RB + g16 * 16;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) ax[u][rb][s] = buffer_ld16(kr, ox + s * 64);
+        }
+    }
+    f32x4_t cm[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+            cm[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, am[rb][s]), bq[s], cm[rb], 0, 0,
+                                                             0);
+    float sq[4][2];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        f32x4_t cx[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+                cx[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ax[u][rb][s]), bq[s],
+                                                                 cx[rb], 0, 0, 0);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+            sq[u][rb] = (cx[rb][0] * cx[rb][0] + cx[rb][1] * cx[rb][1]) + (cx[rb][2] * cx[rb][2] + cx[rb][3] * cx[rb][3]);
+    }
+    if (n16 < p.G) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int tr = rb * 16 + 4 * g16 + i;
+                tmp[n16][tr] = fmaf(cm[rb][i], p.scale, base + tr == p.nb - 1 ? p.ln_last : p.ln_L);
+            }
+    }
+    wave_lds_fence();
+    const float half_s2 = 0.5f * p.scale * p.scale;
+    if (n16 < p.G) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) tmp[n16][8 * u + 4 * rb + g16] += half_s2 * sq[u][rb];
+    }
+    wave_lds_fence();
+    for (int e = lane; e < p.G * 32; e += 64) {
+        const int h = e >> 5, b = e & 31;
+        if (base + b < p.nb) dst[h * stride + base + b] = tmp[h][b];
+    }
+    wave_lds_fence();  // tmp is reused by the next tile
+}
+
+template <int D>
+__global__ void __launch_bounds__(kFusedWaves * 64) score_cobs2_fused_kernel(const FusedScoreParams p)
+{
+    constexpr int RB = D * 2, KS = D / 32, NW = kFusedWaves, NR = 1 + kCobsRank;
+    extern __shared__ float lsm[];  // [G][nb] block logits
+    __shared__ float lse_h[8];
+    __shared__ float tmp[NW][8][32];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int pair = blockIdx.x, b = pair / p.Hkv, j = pair - b * p.Hkv;
+    bf16x8_t bq[KS];
+    load_q_operand<D>(p.q + ((size_t)b * p.Hq + (size_t)j * p.G) * RB, p.G, lane, bq);
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(p.Kbar + (size_t)pair * p.nb * NR * RB, (uint32_t)p.nb * NR * RB);
+    for (int base = wave * 32; base < p.nb; base += NW * 32) cobs2_tile_logits<D>(p, kr, bq, base, lsm, p.nb, lane, tmp[wave]);
+    __syncthreads();
+    group_scores_in_lds<NW>(lsm, lse_h, p.G, p.nb, p.scores + (size_t)pair * p.nb);
+}
+
+template <int D>
+__global__ void __launch_bounds__(kSplitWaves * 64) score_cobs2_split_kernel(const FusedScoreParams p)
+{
+    constexpr int RB = D * 2, KS = D / 32, NR = 1 + kCobsRank;
+    __shared__ float tmp[kSplitWaves][8][32];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int pair = blockIdx.x / p.chunks, chunk = blockIdx.x - pair * p.chunks;
+    const int b = pair / p.Hkv, j = pair - b * p.Hkv;
+    const int base = (chunk * kSplitWaves + wave) * 32;
+    if (base >= p.nb) return;  // whole wave; no workgroup barrier in this kernel
+    bf16x8_t bq[KS];
+    load_q_operand<D>(p.q + ((size_t)b * p.Hq + (size_t)j * p.G) * RB, p.G, lane, bq);
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(p.Kbar + (size_t)pair * p.nb * NR * RB, (uint32_t)p.nb * NR * RB);
+    cobs2_tile_logits<D>(p, kr, bq, base, p.logits + (size_t)pair * p.G * p.nb, p.nb, lane, tmp[wave]);
+}
+
 // Group scores (and the top-k when p.k > 0) of one KV head from split logits.
 __global__ void __launch_bounds__(kFusedWaves * 64) score_finish_kernel(const FusedScoreParams p)
 {
@@ -641,6 +753,33 @@ hipError_t launch_score_summary_split(const Dims& s, const void* q, const void* 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || (s.G == 1 && k == 0)) return e;  // G == 1: the logits are the scores
     return launch_score_finish(s, logits, scores, sel, k, st);
+}
+
+hipError_t launch_score_cobs2(const Dims& s, const void* q, const void* Kcov, float* logits, float* scores,
+                              hipStream_t st)
+{
+    FusedScoreParams p = summary_params(s, q, Kcov, false);
+    p.scores = scores;
+    p.logits = logits;
+    if (s.pairs() >= kFusedStepMinPairs) {
+        const size_t shm = (size_t)s.G * s.nb * sizeof(float);
+        const dim3 grid((unsigned)s.pairs()), block(kFusedWaves * 64);
+        if (s.d == 128)
+            score_cobs2_fused_kernel<128><<<grid, block, shm, st>>>(p);
+        else
+            score_cobs2_fused_kernel<64><<<grid, block, shm, st>>>(p);
+        return hipGetLastError();
+    }
+    const int tiles = (s.nb + 31) / 32;
+    p.chunks = (tiles + kSplitWaves - 1) / kSplitWaves;
+    const dim3 grid((unsigned)(s.pairs() * p.chunks)), block(kSplitWaves * 64);
+    if (s.d == 128)
+        score_cobs2_split_kernel<128><<<grid, block, 0, st>>>(p);
+    else
+        score_cobs2_split_kernel<64><<<grid, block, 0, st>>>(p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || s.G == 1) return e;  // G == 1: the logits are the scores
+    return launch_score_finish(s, logits, scores, nullptr, 0, st);
 }
 
 bool score_finish_ok(const Dims& s)

@@ -50,7 +50,7 @@ class Workload:
     block_size: int
     dtype: str  # "f32" or "bf16"
     k: int  # blocks read exactly per KV head
-    score_mode: str  # "summary", "exact_mass" or "box"
+    score_mode: str  # "summary", "exact_mass", "box" or "cobs2"
     proxies: bool  # one count-aware proxy per unread block
     keys: str  # "heavy_hitters" or "clusters"
     n_clusters: int = 64
@@ -91,6 +91,8 @@ WORKLOADS = {
                  description="128K context, G=7: top-8 blocks + 2048 weighted coreset tokens + proxies"),
         Workload("llama3_8b_layer_b32_box", 1002, 32, 32, 8, 128, 32768, 64, "bf16", 5, "box", True, "clusters",
                  description="the headline layer with blocks ranked by their min/max key box (Quest)"),
+        Workload("llama3_8b_layer_b32_cobs2", 1002, 32, 32, 8, 128, 32768, 64, "bf16", 5, "cobs2", True,
+                 "clusters", description="the headline layer with second-order (mean + rank-4 covariance) scores"),
     ]
 }
 

@@ -76,8 +76,12 @@ typedef enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
 typedef enum csa_score_mode {
     CSA_SCORE_SUMMARY = 0,    /* first-order score from the mean key  [COBS] Eq. (18) */
     CSA_SCORE_EXACT_MASS = 1, /* exact block mass from every key ("OSA")             */
-    CSA_SCORE_BOX = 2         /* best logit over the block's min/max key box (Quest) */
+    CSA_SCORE_BOX = 2,        /* best logit over the block's min/max key box (Quest) */
+    CSA_SCORE_COBS2 = 3       /* second-order (mean + covariance) estimate of ln m_b */
 } csa_score_mode;
+
+/* Scaled eigenvectors per block in the second-order descriptor (kv_cov_build). */
+#define CSA_COBS_RANK 4
 
 typedef enum csa_proxy_mode {
     CSA_PROXY_NONE = 0,      /* unread blocks are discarded, the rest renormalised   */
@@ -90,7 +94,8 @@ typedef enum csa_entry {
     CSA_WS_SPARSE_DECODE_ATTN = 2,
     CSA_WS_DENSE_DECODE_ATTN = 3,
     CSA_WS_SELECTIVE_DECODE_STEP = 4,
-    CSA_WS_BLOCK_SCORE_BOX = 5
+    CSA_WS_BLOCK_SCORE_BOX = 5,
+    CSA_WS_BLOCK_SCORE_COBS2 = 6
 } csa_entry;
 
 typedef struct csa_shape {
@@ -127,18 +132,36 @@ int kv_summary_build(const csa_shape* shape, const void* K, const void* V, void*
 int kv_box_build(const csa_shape* shape, const void* K, void* Kbox, hipStream_t stream);
 
 /*
+ * kv_cov_build -- per block, the second-order descriptor of [COBS] (the
+ * cumulant expansion of ln m_b truncated at second order, with the block's key
+ * covariance kept as its top CSA_COBS_RANK scaled eigenvectors): row 0 the
+ * mean key (the same bits as kv_summary_build's Kbar), rows 1..CSA_COBS_RANK
+ * xi_i = sqrt(lambda_i) u_i for the largest eigenvalues lambda_i of
+ * Sigma_b = (1/c_b) sum_{i in b} (K_i - mean)(K_i - mean)^T, largest first,
+ * each signed so that its largest-magnitude coordinate is positive; fp32
+ * eigen-solve, rounded once to the storage dtype.  Reads K [B, Hkv, n, d];
+ * writes Kcov [B, Hkv, nb, 1 + CSA_COBS_RANK, d].  Blocks of at most 64 tokens
+ * (else CSA_ERR_UNSUPPORTED).  Run once per cache (after prefill); no workspace.
+ */
+int kv_cov_build(const csa_shape* shape, const void* K, void* Kcov, hipStream_t stream);
+
+/*
  * block_score -- the score by which blocks are ranked, per KV head.
  * Per query head h and block b the block logit is
  *   SUMMARY:    l_hb = scale q_h . Kbar_b + ln c_b         (keys = Kbar)  [COBS] Eq. (18)
  *   EXACT_MASS: l_hb = ln m_hb = ln sum_{i in b} e^{s_i}   (keys = K)     [COBS] Eq. (1)
  *   BOX:        l_hb = scale sum_t max(q_t lo_bt, q_t hi_bt) (keys = Kbox), the
  *               largest logit any point of the block's key box could give
+ *   COBS2:      l_hb = scale q_h . Kbar_b + ln c_b + (1/2) scale^2 sum_i (q_h . xi_bi)^2
+ *               (keys = Kcov from kv_cov_build; bfloat16, G <= 8 and G nb <= 16384,
+ *               else CSA_ERR_UNSUPPORTED)
  * and the score of block b of KV head j is
  *   G = 1: l_hb (ranking by log-mass, [COBS] Eq. (5) with G = 1);
  *   G > 1: ln sum_{h in group j} exp(l_hb - ln sum_b' e^{l_hb'}),
  *          the logarithm of the additive GQA score of [COBS] Eq. (5).
  * Writes scores [B, Hkv, nb].  Workspace: csa_workspace_size(shape,
- * CSA_WS_BLOCK_SCORE_SUMMARY, _EXACT_MASS or _BOX, 0, 0) bytes (0 when G = 1).
+ * CSA_WS_BLOCK_SCORE_SUMMARY, _EXACT_MASS, _BOX or _COBS2, 0, 0) bytes (0 when
+ * G = 1).
  */
 int block_score(const csa_shape* shape, csa_score_mode mode, const void* q, const void* keys,
                 float* scores, void* ws, size_t ws_bytes, hipStream_t stream);
@@ -194,9 +217,9 @@ int dense_decode_attn(const csa_shape* shape, const void* q, const void* K, cons
  * (bfloat16, G <= 8, k <= 32, nb <= 2048, B * Hkv >= 32) one kernel per KV head
  * reads Kbar once, keeps the logits on chip for both uses, selects the blocks
  * and attends; otherwise the three entry points run in turn.
- * keys = Kbar (SUMMARY) or K (EXACT_MASS) as for block_score (BOX scores are
- * CSA_ERR_UNSUPPORTED here: they need Kbox besides Kbar; use the three entry
- * points); Kbar may be NULL in EXACT_MASS mode without proxies.  scores [B, Hkv, nb] and
+ * keys = Kbar (SUMMARY) or K (EXACT_MASS) as for block_score (BOX and COBS2
+ * scores are CSA_ERR_UNSUPPORTED here: they need Kbox or Kcov besides Kbar; use
+ * the three entry points); Kbar may be NULL in EXACT_MASS mode without proxies.  scores [B, Hkv, nb] and
  * sel [B, Hkv, min(k, nb)] are written when not NULL.  0 <= k; k = 0 with no
  * proxies and m = 0 is CSA_ERR_INVALID_ARG.  Workspace: csa_workspace_size(
  * shape, CSA_WS_SELECTIVE_DECODE_STEP, k, m) bytes.

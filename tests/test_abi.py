@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = set(declared_functions())
-    assert {"kv_summary_build", "kv_box_build", "block_score", "topk_select", "sparse_decode_attn",
+    assert {"kv_summary_build", "kv_box_build", "kv_cov_build", "block_score", "topk_select", "sparse_decode_attn",
             "dense_decode_attn", "selective_decode_step", "csa_workspace_size", "csa_status_str",
             "csa_last_error"} <= names
 
@@ -126,6 +126,19 @@ def test_workspace_is_checked_before_launch(L):
     assert L.block_score(ctypes.byref(s), 9, FAKE, FAKE, FAKE, None, 0, None) == csa.CSA_ERR_INVALID_ARG
     assert L.csa_workspace_size(ctypes.byref(s), csa.CSA_WS_BLOCK_SCORE_BOX, 0, 0) == bneed
     assert L.block_score(ctypes.byref(s), csa.CSA_SCORE_BOX, FAKE, FAKE, FAKE, None, 0, None) == csa.CSA_ERR_WORKSPACE
+
+
+def test_cov_build_argument_checks(L):
+    s = shape()
+    assert L.kv_cov_build(ctypes.byref(s), None, FAKE, None) == csa.CSA_ERR_INVALID_ARG
+    assert L.kv_cov_build(ctypes.byref(s), FAKE, FAKE + 4, None) == csa.CSA_ERR_INVALID_ARG
+    big = shape(L=128)
+    assert L.kv_cov_build(ctypes.byref(big), FAKE, FAKE, None) == csa.CSA_ERR_UNSUPPORTED
+    assert b"at most 64" in L.csa_last_error()
+    f32 = shape(dtype=csa.CSA_F32)
+    assert L.block_score(ctypes.byref(f32), csa.CSA_SCORE_COBS2, FAKE, FAKE, FAKE, FAKE, 1 << 20,
+                         None) == csa.CSA_ERR_UNSUPPORTED
+    assert step(L, s, mode=csa.CSA_SCORE_COBS2) == csa.CSA_ERR_UNSUPPORTED
 
 
 def test_box_build_argument_checks(L):
