@@ -592,3 +592,14 @@ def test_cobs2_full_size_sampled():
         o = {"Kbar": Kbar_o, "Vbar": Vbar_o, "score": score, "sel": sel_o, "margin": margin, "out": out_o,
              "lse": lse_o}
         compare_pipelines(w, g, o, f"cobs2 full pair ({b},{j})")
+
+
+@pytest.mark.parametrize("mode", ["summary", "exact_mass"])
+def test_largest_group_and_long_context(mode):
+    """Edge of the supported sizes: one sequence with a 64-head group over a 1M-token cache
+    (256 MiB per tensor: 32-bit buffer offsets near their top), 16384 blocks (the radix top-k),
+    k = 32, proxies for the rest, fully checked against the oracle."""
+    n, G, d, L, k = 1 << 20, 64, 128, 64, 32
+    w = W.Workload("max_case", 0, 1, G, 1, d, n, L, "bf16", k, mode, True, "clusters")
+    data = rand_inputs(400, 1, G, 1, d, n, "bf16", qscale=3.0)
+    compare_pipelines(w, gpu_pipeline(w, data), oracle_pipeline(w, data), f"max case {mode}")
