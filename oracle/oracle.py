@@ -21,7 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "csa_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "libcsa_oracle.so")
 
-SUMMARY, EXACT_MASS, BOX, COBS2 = 0, 1, 2, 3
+SUMMARY, EXACT_MASS, BOX, COBS2, PROXY_ERROR = 0, 1, 2, 3, 4
 COBS_RANK = 4  # scaled eigenvectors per block in the second-order descriptor
 
 
@@ -211,6 +211,87 @@ def cobs2_logits(shape: Shape, q, Kcov):
     return out
 
 
+def var_build(shape: Shape, K, Kbar=None):
+    """Mean and variance tokens of every block, the cached pair that the proxy-error ranking of
+    "OpenAttention reads 1% of the KV cache -- Count-aware tail proxy" reads (section "Three
+    helpers that make the proxy accurate").  Returns [B, Hkv, nb, 2, d] in the storage dtype:
+    row 0 the mean key (the bits of kv_summary_build), row 1 the per-coordinate population
+    variance of the block's keys about their exact mean, (1/c) sum_i (k_i - mean)^2.  Both
+    sums run token by token in fp64; the variance is rounded once."""
+    B, Hkv, n, d, L, nb = shape.batch, shape.n_kv_heads, shape.n_tokens, shape.head_dim, shape.block_size, \
+        shape.n_blocks
+    Kf = widen(shape, _stored(shape, K, (B, Hkv, n, d)))
+    if Kbar is None:
+        Kbar, _ = kv_summary_build(shape, K, K)
+    var = np.empty((B, Hkv, nb, d), np.float64)
+    for blk in range(nb):
+        X = Kf[:, :, blk * L:min(n, (blk + 1) * L)]  # [B, Hkv, c, d]
+        c = X.shape[2]
+        s1 = np.zeros((B, Hkv, d))
+        for i in range(c):
+            s1 = s1 + X[:, :, i]
+        mean = s1 / c
+        s2 = np.zeros((B, Hkv, d))
+        for i in range(c):
+            dv = X[:, :, i] - mean
+            s2 = s2 + dv * dv
+        var[:, :, blk] = s2 / c
+    out = np.empty((B, Hkv, nb, 2, d), shape.np_dtype)
+    out[:, :, :, 0] = np.asarray(Kbar).reshape(B, Hkv, nb, d)
+    out[:, :, :, 1] = store_array(shape, var)
+    return out
+
+
+def proxy_error_logits(shape: Shape, q, Kvar):
+    """Per query head h and block b, from the stored mean and variance tokens:
+    shat_hb = scale q_h.kbar_b + ln c_b, the log-mass of the block's count-aware proxy
+    ("OpenAttention ... Count-aware tail proxy", section "Skipping reviews without losing the
+    verdict": mean logit plus ln count), and the log of the proxy's estimated weight error,
+    its mass times the spread of the logits it hides (same section), shat_hb + ln sigma_hb with
+    sigma_hb = scale sqrt(sum_t q_ht^2 var_bt), the standard deviation of the block's logits
+    when its key coordinates are uncorrelated (-inf when sigma = 0).  Returns (shat, lerr),
+    each [B, Hq, nb]."""
+    B, Hq, Hkv, d, nb = shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.n_blocks
+    G = Hq // Hkv
+    qf = widen(shape, _stored(shape, q, (B, Hq, d)))
+    C = widen(shape, np.asarray(Kvar)).reshape(B, Hkv, nb, 2, d)
+    scale = shape.scale if shape.scale else 1.0 / math.sqrt(d)
+    counts = np.array([min(shape.block_size, shape.n_tokens - i * shape.block_size) for i in range(nb)], np.float64)
+    shat = np.empty((B, Hq, nb))
+    lerr = np.empty((B, Hq, nb))
+    for h in range(Hq):
+        mean_dot = np.einsum("bd,bkd->bk", qf[:, h], C[:, h // G, :, 0])
+        spread2 = scale * scale * np.einsum("bd,bkd->bk", qf[:, h] ** 2, C[:, h // G, :, 1])
+        shat[:, h] = scale * mean_dot + np.log(counts)
+        with np.errstate(divide="ignore"):
+            lerr[:, h] = np.where(spread2 > 0, shat[:, h] + 0.5 * np.log(np.where(spread2 > 0, spread2, 1.0)),
+                                  -np.inf)
+    return shat, lerr
+
+
+def _lse(x, axis):
+    m = np.max(x, axis=axis, keepdims=True)
+    mf = np.where(np.isfinite(m), m, 0.0)
+    with np.errstate(divide="ignore"):
+        return np.squeeze(mf + np.log(np.sum(np.exp(x - mf), axis=axis, keepdims=True)), axis)
+
+
+def proxy_error_score(shape: Shape, q, Kvar):
+    """Block scores [B, Hkv, nb] of the proxy-error ranking: exact reads go to the blocks whose
+    proxies would leave the largest weight error ("OpenAttention ... Count-aware tail proxy",
+    section "Three helpers that make the proxy accurate").  G = 1: the log-error itself.  G > 1:
+    ln sum_h exp(lerr_hb - ln sum_b' exp(shat_hb')), each head's error as a share of its
+    proxy-estimated softmax denominator, added over the group as in the additive GQA score of
+    "COBS: Cumulant Order Block Sparse Attention", Eq. (5)."""
+    B, Hq, Hkv, nb = shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.n_blocks
+    G = Hq // Hkv
+    shat, lerr = proxy_error_logits(shape, q, Kvar)
+    if G == 1:
+        return lerr.reshape(B, Hkv, nb)
+    rel = lerr - _lse(shat, axis=2)[:, :, None]  # [B, Hq, nb]
+    return _lse(rel.reshape(B, Hkv, G, nb), axis=2)
+
+
 def block_logits(shape: Shape, mode: int, q, keys):
     """Per-query-head block logits [B, Hq, nb]: first-order summary score, exact ln m_b, or the
     largest logit over the block's key box."""
@@ -239,6 +320,8 @@ def group_score(shape: Shape, logits):
 
 
 def block_score(shape: Shape, mode: int, q, keys):
+    if mode == PROXY_ERROR:
+        return proxy_error_score(shape, q, keys)
     return group_score(shape, block_logits(shape, mode, q, keys))
 
 

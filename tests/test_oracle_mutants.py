@@ -99,12 +99,22 @@ PY_MUTANTS = {
     "eigenvectors not scaled by the root eigenvalue": ("math.sqrt(max(lam[d - 1 - i], 0.0)) * u",
                                                        "max(lam[d - 1 - i], 0.0) * u"),
     "smallest eigendirections kept": ("u = U[:, d - 1 - i]", "u = U[:, i]"),
+    "error ranked by the logit variance, not its spread": ("shat[:, h] + 0.5 * np.log(", "shat[:, h] + 1.0 * np.log("),
+    "proxy mass without the count": ("shat[:, h] = scale * mean_dot + np.log(counts)", "shat[:, h] = scale * mean_dot"),
+    "group normalised by the errors instead of the masses": ("rel = lerr - _lse(shat, axis=2)", "rel = lerr - _lse(lerr, axis=2)"),
+    "variance about zero instead of the block mean": ("dv = X[:, :, i] - mean", "dv = X[:, :, i]"),
+    "variance with the sample divisor": ("var[:, :, blk] = s2 / c", "var[:, :, blk] = s2 / max(c - 1, 1)"),
+    "spread without the logit scale": ("spread2 = scale * scale * np.einsum", "spread2 = np.einsum"),
 }
 PY_BATTERY = [
     P.test_cov_descriptor_is_the_top_eigen_truncation,
     P.test_second_order_term_is_half_the_logit_variance_at_full_rank,
     P.test_equal_logit_block_has_no_second_order_term,
     P.test_second_order_estimate_tracks_the_exact_mass,
+    P.test_variance_token_closed_forms,
+    P.test_spread_is_the_std_of_the_block_logits_and_error_is_mass_times_spread,
+    P.test_scaling_every_spread_shifts_every_score_by_its_log,
+    P.test_exact_proxies_carry_no_error,
 ]
 
 

@@ -638,3 +638,120 @@ def test_second_order_estimate_tracks_the_exact_mass():
         assert np.mean(np.abs(second - exact) < np.abs(first - exact)) > 0.9
         errs.append(np.abs(second - exact).mean())
     assert errs[1] < errs[0] / 4  # halving the spread cuts the error by about 8
+
+
+# ---------------------------------------------------------------------------
+# proxy-error ranking: mean and variance tokens, estimated error = mass x spread
+# ("OpenAttention reads 1% of the KV cache -- Count-aware tail proxy")
+# ---------------------------------------------------------------------------
+
+def test_variance_token_closed_forms():
+    """Two-token blocks: the population variance per coordinate is ((a - b) / 2)^2; a block
+    of equal keys and a one-token block have variance 0; a constant shift of every key
+    leaves it unchanged; against E[x^2] - E[x]^2 in exact rational arithmetic."""
+    d, n = 16, 64
+    rng = np.random.default_rng(40)
+    K = rng.standard_normal((1, 1, n, d)).astype(np.float32)
+    K[0, 0, 8:16] = K[0, 0, 9]  # block 2 of L = 4 ... block 3: equal keys
+    shp2 = O.Shape(1, 1, 1, d, n, 2, "f32")
+    var2 = O.widen("f32", O.var_build(shp2, K)[0, 0, :, 1])
+    Kd = K[0, 0].astype(np.float64)
+    want = ((Kd[0::2] - Kd[1::2]) / 2) ** 2
+    assert np.abs(var2 - want).max() <= 2.0 ** -23 * want.max()
+    shp4 = O.Shape(1, 1, 1, d, n, 4, "f32")
+    var4 = O.widen("f32", O.var_build(shp4, K)[0, 0, :, 1])
+    assert np.all(var4[2:4] == 0.0)
+    shp1 = O.Shape(1, 1, 1, d, n, 1, "f32")
+    assert np.all(O.widen("f32", O.var_build(shp1, K)[0, 0, :, 1]) == 0.0)
+    Ks = (K + np.float32(3.0)).astype(np.float32)  # exact in binary32 for |k| < 2^20 ulps apart
+    var4s = O.widen("f32", O.var_build(shp4, Ks)[0, 0, :, 1])
+    assert np.abs(var4s - var4).max() <= 1e-5 * max(var4.max(), 1.0)
+    for blk in (0, 5, 11):
+        rows = [[Fraction(float(v)) for v in Ks[0, 0, blk * 4 + i]] for i in range(4)]
+        for t in (0, 7, 15):
+            m1 = sum(r[t] for r in rows) / 4
+            m2 = sum(r[t] * r[t] for r in rows) / 4
+            exact = float(m2 - m1 * m1)
+            assert abs(var4s[blk, t] - exact) <= 2.0 ** -23 * exact + 1e-30
+
+
+def _axis_blocks(seed, B, Hkv, d, nb, L, spread):
+    """Keys whose blocks vary along one coordinate each (so each block's covariance is
+    diagonal), symmetric about the block mean (so the mean is exact)."""
+    rng = np.random.default_rng(seed)
+    K = np.empty((B, Hkv, nb * L, d), np.float32)
+    for b in range(B):
+        for j in range(Hkv):
+            for blk in range(nb):
+                base = np.round(rng.standard_normal(d) * 8) / 8
+                t = int(rng.integers(d))
+                off = np.round(rng.standard_normal(L // 2) * 16) / 16 * spread
+                rows = np.repeat(base[None], L, axis=0)
+                rows[: L // 2, t] += off
+                rows[L // 2:, t] -= off
+                K[b, j, blk * L:(blk + 1) * L] = rows
+    return K
+
+
+def _quarter_q(seed, B, Hq, d):
+    """Queries on a grid of quarters with no zero coordinate (every block's spread > 0)."""
+    q = np.round(np.random.default_rng(seed).standard_normal((B, Hq, d)) * 4) / 4
+    return np.where(q == 0, 0.25, q).astype(np.float32)
+
+
+def test_spread_is_the_std_of_the_block_logits_and_error_is_mass_times_spread():
+    """Brute force from token logits: for blocks whose keys vary along one coordinate the
+    covariance is diagonal, so the spread from the variance token is exactly the standard
+    deviation of the block's logits; the proxy mass is c exp(mean logit); G = 1 ranks by
+    ln(mass x spread) and G = 2 by ln sum_h mass_hb spread_hb / sum_b' mass_hb'."""
+    B, Hkv, d, nb, L = 1, 2, 32, 6, 8
+    for G in (1, 2):
+        Hq = G * Hkv
+        K = _axis_blocks(41, B, Hkv, d, nb, L, spread=1.0)
+        q = _quarter_q(42, B, Hq, d)
+        shp = O.Shape(B, Hq, Hkv, d, nb * L, L, "f32")
+        Kvar = O.var_build(shp, K)
+        score = O.block_score(shp, O.PROXY_ERROR, q, Kvar)
+        scale = 1.0 / math.sqrt(d)
+        for j in range(Hkv):
+            num = np.zeros(nb)
+            for g in range(G):
+                h = j * G + g
+                s = (K[0, j].astype(np.float64) @ q[0, h].astype(np.float64)) * scale  # token logits
+                s = s.reshape(nb, L)
+                mass = L * np.exp(s.mean(axis=1))
+                spread = s.std(axis=1)
+                num += mass * spread / (mass.sum() if G > 1 else 1.0)
+            assert np.abs(score[0, j] - np.log(num)).max() < 1e-9
+
+
+def test_scaling_every_spread_shifts_every_score_by_its_log():
+    """Multiplying every block's deviations from its mean by 2 doubles every spread and
+    leaves every proxy mass (and so each head's normaliser) unchanged: every score moves
+    by exactly ln 2, whatever G."""
+    B, Hkv, d, nb, L = 1, 2, 32, 8, 8
+    for G in (1, 3):
+        Hq = G * Hkv
+        q = _quarter_q(43, B, Hq, d)
+        shp = O.Shape(B, Hq, Hkv, d, nb * L, L, "f32")
+        s1 = O.block_score(shp, O.PROXY_ERROR, q, O.var_build(shp, _axis_blocks(44, B, Hkv, d, nb, L, 1.0)))
+        s2 = O.block_score(shp, O.PROXY_ERROR, q, O.var_build(shp, _axis_blocks(44, B, Hkv, d, nb, L, 2.0)))
+        assert np.abs(s2 - s1 - math.log(2.0)).max() < 1e-12
+
+
+def test_exact_proxies_carry_no_error():
+    """A block of equal keys (or of one token) is represented exactly by its proxy: its
+    estimated error is 0 (score -inf), so it is read only once every other block is; the
+    others keep finite scores."""
+    d, n, L = 16, 64, 8
+    rng = np.random.default_rng(45)
+    K = rng.standard_normal((1, 1, n, d)).astype(np.float32)
+    K[0, 0, 16:24] = K[0, 0, 16]
+    q = rng.standard_normal((1, 2, d)).astype(np.float32)
+    shp = O.Shape(1, 2, 1, d, n, L, "f32")
+    sc = O.block_score(shp, O.PROXY_ERROR, q, O.var_build(shp, K))[0, 0]
+    assert sc[2] == -np.inf and np.all(np.isfinite(np.delete(sc, 2)))
+    sel, _ = O.topk_select(sc[None], 7)
+    assert 2 not in sel[0]
+    shp1 = O.Shape(1, 2, 1, d, n, 1, "f32")
+    assert np.all(O.block_score(shp1, O.PROXY_ERROR, q, O.var_build(shp1, K)) == -np.inf)
