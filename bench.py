@@ -161,7 +161,10 @@ def step_bytes(w, m=0):
     key once (it ranks the blocks and gives the proxy logits), the mean values of the unread
     blocks and the exact key/value rows of the kept blocks.  Exact-mass scores: every key
     once, the values of the kept blocks, both mean rows of the unread blocks.  Box scores:
-    both box rows of every block, both mean rows of the unread blocks, the exact rows.  Plus
+    both box rows of every block, both mean rows of the unread blocks, the exact rows.
+    Proxy-error scores: the mean and variance rows of every block, then both mean rows of
+    the unread blocks (the mean keys are read a second time by the attention), the exact
+    rows.  Second-order scores: the mean and four eigenvector rows of every block.  Plus
     weighted-token rows, the queries, and the outputs with their log-normalisers."""
     e = w.elem_bytes
     d, L, k, nb, G = w.head_dim, w.block_size, w.k, w.n_blocks, w.group
@@ -171,6 +174,8 @@ def step_bytes(w, m=0):
     elif w.score_mode == "exact_mass":
         per_read = w.n_tokens * d * e + k * L * d * e + unread * 2 * d * e
     elif w.score_mode == "box":
+        per_read = 2 * nb * d * e + unread * 2 * d * e + k * L * 2 * d * e
+    elif w.score_mode == "proxy_error":  # mean and variance tokens of every block, then as box
         per_read = 2 * nb * d * e + unread * 2 * d * e + k * L * 2 * d * e
     else:  # second-order: the mean key and four eigenvector rows of every block
         per_read = 5 * nb * d * e + unread * d * e + k * L * 2 * d * e
@@ -230,11 +235,11 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     summary_ms = e0.elapsed_time(e1)
-    box = w.score_mode in ("box", "cobs2")  # scored from extra per-block summaries
+    box = w.score_mode in ("box", "cobs2", "proxy_error")  # scored from extra per-block summaries
     Kbox0 = None
     extra_ms = None
     if box:
-        build = csa.kv_box_build if w.score_mode == "box" else csa.kv_cov_build
+        build = {"box": csa.kv_box_build, "cobs2": csa.kv_cov_build, "proxy_error": csa.kv_var_build}[w.score_mode]
         Kbox0 = build(K0, w.block_size)
         torch.cuda.synchronize()
         e0.record()
@@ -254,7 +259,8 @@ def main():
     out = torch.empty((B, Hq, w.head_dim), dtype=torch.float32, device=dev)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
     mode_entry = {"summary": csa.CSA_WS_BLOCK_SCORE_SUMMARY, "exact_mass": csa.CSA_WS_BLOCK_SCORE_EXACT_MASS,
-                  "box": csa.CSA_WS_BLOCK_SCORE_BOX, "cobs2": csa.CSA_WS_BLOCK_SCORE_COBS2}[w.score_mode]
+                  "box": csa.CSA_WS_BLOCK_SCORE_BOX, "cobs2": csa.CSA_WS_BLOCK_SCORE_COBS2,
+                  "proxy_error": csa.CSA_WS_BLOCK_SCORE_PROXY_ERROR}[w.score_mode]
     ws_score = torch.empty(max(1, csa.workspace_size(shape, mode_entry)), dtype=torch.uint8, device=dev)
     ws_attn = torch.empty(max(1, csa.workspace_size(shape, csa.CSA_WS_SPARSE_DECODE_ATTN, w.k, m)),
                           dtype=torch.uint8, device=dev)
@@ -263,7 +269,7 @@ def main():
 
     def score_select(layer):
         K, V, Kbar, Vbar, Kbox = layer
-        keys = {"summary": Kbar, "exact_mass": K, "box": Kbox, "cobs2": Kbox}[w.score_mode]
+        keys = {"summary": Kbar, "exact_mass": K, "box": Kbox, "cobs2": Kbox, "proxy_error": Kbox}[w.score_mode]
         csa.block_score(q, keys, w.score_mode, w.block_size, n_tokens=w.n_tokens, scores=scores, ws=ws_score)
         csa.topk_select(scores, w.k, sel=sel)
 
@@ -381,7 +387,8 @@ def main():
         "modular_breakdown_us": {"block_score+topk_select": score_ms * 1e3 if score_ms else None,
                                  "sparse_decode_attn": attn_ms * 1e3},
         "kv_summary_build_ms": summary_ms,
-        **({f"kv_{'box' if w.score_mode == 'box' else 'cov'}_build_ms": extra_ms} if extra_ms is not None else {}),
+        **({f"kv_{ {'box': 'box', 'cobs2': 'cov', 'proxy_error': 'var'}[w.score_mode]}_build_ms": extra_ms}
+           if extra_ms is not None else {}),
         "dense_decode_attn_ms": dense_ms,
         "step_vs_dense_speedup": (dense_ms / t_step) if dense_ms else None,
         "roofline": {

@@ -16,18 +16,19 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so"
 
 CSA_OK, CSA_ERR_INVALID_ARG, CSA_ERR_UNSUPPORTED, CSA_ERR_WORKSPACE, CSA_ERR_HIP = 0, -1, -2, -3, -4
 CSA_F32, CSA_BF16 = 0, 1
-CSA_SCORE_SUMMARY, CSA_SCORE_EXACT_MASS, CSA_SCORE_BOX, CSA_SCORE_COBS2 = 0, 1, 2, 3
+CSA_SCORE_SUMMARY, CSA_SCORE_EXACT_MASS, CSA_SCORE_BOX, CSA_SCORE_COBS2, CSA_SCORE_PROXY_ERROR = 0, 1, 2, 3, 4
 CSA_COBS_RANK = 4
 CSA_PROXY_NONE, CSA_PROXY_COMPLEMENT = 0, 1
 CSA_WS_BLOCK_SCORE_SUMMARY, CSA_WS_BLOCK_SCORE_EXACT_MASS = 0, 1
 CSA_WS_SPARSE_DECODE_ATTN, CSA_WS_DENSE_DECODE_ATTN, CSA_WS_SELECTIVE_DECODE_STEP = 2, 3, 4
-CSA_WS_BLOCK_SCORE_BOX, CSA_WS_BLOCK_SCORE_COBS2 = 5, 6
+CSA_WS_BLOCK_SCORE_BOX, CSA_WS_BLOCK_SCORE_COBS2, CSA_WS_BLOCK_SCORE_PROXY_ERROR = 5, 6, 7
 
 MODES = {"summary": CSA_SCORE_SUMMARY, "exact_mass": CSA_SCORE_EXACT_MASS, "box": CSA_SCORE_BOX,
-         "cobs2": CSA_SCORE_COBS2}
+         "cobs2": CSA_SCORE_COBS2, "proxy_error": CSA_SCORE_PROXY_ERROR}
 _SCORE_WS = {"summary": CSA_WS_BLOCK_SCORE_SUMMARY, "exact_mass": CSA_WS_BLOCK_SCORE_EXACT_MASS,
-             "box": CSA_WS_BLOCK_SCORE_BOX, "cobs2": CSA_WS_BLOCK_SCORE_COBS2}
-_SUMMARY_ROWS = {"summary": None, "box": 2, "cobs2": 1 + CSA_COBS_RANK}  # rows per block of the keys
+             "box": CSA_WS_BLOCK_SCORE_BOX, "cobs2": CSA_WS_BLOCK_SCORE_COBS2,
+             "proxy_error": CSA_WS_BLOCK_SCORE_PROXY_ERROR}
+_SUMMARY_ROWS = {"summary": None, "box": 2, "cobs2": 1 + CSA_COBS_RANK, "proxy_error": 2}  # rows per block
 
 
 class CsaError(RuntimeError):
@@ -60,6 +61,7 @@ _SIGS = {
     "kv_summary_build": [ctypes.POINTER(Shape), _P, _P, _P, _P, _P],
     "kv_box_build": [ctypes.POINTER(Shape), _P, _P, _P],
     "kv_cov_build": [ctypes.POINTER(Shape), _P, _P, _P],
+    "kv_var_build": [ctypes.POINTER(Shape), _P, _P, _P],
     "block_score": [ctypes.POINTER(Shape), ctypes.c_int, _P, _P, _P, _P, _SZ, _P],
     "topk_select": [_I32, _I32, _I32, _P, _P, _P],
     "sparse_decode_attn": [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _I32, _P, _P, _I32, ctypes.c_int,
@@ -186,10 +188,21 @@ def kv_cov_build(K: torch.Tensor, block_size: int, Kcov=None):
     return Kcov
 
 
+def kv_var_build(K: torch.Tensor, block_size: int, Kvar=None):
+    """Mean and variance tokens of every block: Kvar [B, Hkv, nb, 2, d] (row 0 the mean key,
+    row 1 the per-coordinate key variance), for the proxy-error scores."""
+    dev = _dev(K, Kvar)
+    B, Hkv, n, d = K.shape
+    shape = Shape(B, Hkv, Hkv, d, n, block_size, _dtype_code(K), 0.0)
+    Kvar = torch.empty((B, Hkv, shape.n_blocks, 2, d), dtype=K.dtype, device=dev) if Kvar is None else Kvar
+    _check(lib().kv_var_build(ctypes.byref(shape), _ptr(K), _ptr(Kvar), _stream(dev)), "kv_var_build")
+    return Kvar
+
+
 def block_score(q: torch.Tensor, keys: torch.Tensor, mode: str, block_size: int, n_tokens: int | None = None,
                 scale: float = 0.0, scores=None, ws=None):
     """Block scores [B, Hkv, nb].  keys = Kbar (mode 'summary'), K (mode 'exact_mass'), Kbox
-    (mode 'box') or Kcov (mode 'cobs2'); n_tokens is needed in every mode but 'exact_mass' (the
+    (mode 'box'), Kcov (mode 'cobs2') or Kvar (mode 'proxy_error'); n_tokens is needed in every mode but 'exact_mass' (the
     cache length the summaries describe)."""
     dev = _dev(q, keys, scores)
     B, Hq, d = q.shape

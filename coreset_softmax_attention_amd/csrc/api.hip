@@ -93,6 +93,12 @@ int attn_rows_ok(const csa::Dims& d, long long k, long long m, int proxies, int 
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Proxy-error scores: the log-errors, then the per-tile normaliser states.
+size_t error_score_ws(const csa::Dims& d)
+{
+    return d.G > 1 ? align256(block_score_ws(d)) + csa::score_err_parts_bytes(d) : 0;
+}
+
 // Workspace layout of the unfused decode step: scores | sel | block_score ws | attention ws.
 struct StepWs {
     size_t scores, sel, score_ws, attn_ws, total;
@@ -149,18 +155,39 @@ int kv_cov_build(const csa_shape* shape, const void* K, void* Kcov, hipStream_t 
     return e == hipSuccess ? CSA_OK : hip_fail(e, "kv_cov_build");
 }
 
+int kv_var_build(const csa_shape* shape, const void* K, void* Kvar, hipStream_t stream)
+{
+    csa::Dims d;
+    if (int rc = make_dims(shape, &d)) return rc;
+    if (!K || !Kvar) return fail(CSA_ERR_INVALID_ARG, "kv_var_build: NULL tensor pointer");
+    if (!aligned16(K) || !aligned16(Kvar)) return fail(CSA_ERR_INVALID_ARG, "kv_var_build: tensors must be 16-byte aligned");
+    const hipError_t e = csa::launch_var(d, K, Kvar, stream);
+    return e == hipSuccess ? CSA_OK : hip_fail(e, "kv_var_build");
+}
+
 int block_score(const csa_shape* shape, csa_score_mode mode, const void* q, const void* keys, float* scores, void* ws,
                 size_t ws_bytes, hipStream_t stream)
 {
     csa::Dims d;
     if (int rc = make_dims(shape, &d)) return rc;
-    if (mode != CSA_SCORE_SUMMARY && mode != CSA_SCORE_EXACT_MASS && mode != CSA_SCORE_BOX && mode != CSA_SCORE_COBS2)
+    if (mode != CSA_SCORE_SUMMARY && mode != CSA_SCORE_EXACT_MASS && mode != CSA_SCORE_BOX && mode != CSA_SCORE_COBS2 &&
+        mode != CSA_SCORE_PROXY_ERROR)
         return fail(CSA_ERR_INVALID_ARG, "block_score: unknown mode %d", (int)mode);
     if (mode == CSA_SCORE_COBS2 && !csa::fused_summary_score_ok(d))
         return fail(CSA_ERR_UNSUPPORTED, "block_score: second-order scores need bfloat16, G <= 8 and G nb <= 16384");
+    if (mode == CSA_SCORE_PROXY_ERROR && !csa::fused_summary_score_ok(d))
+        return fail(CSA_ERR_UNSUPPORTED, "block_score: proxy-error scores need bfloat16, G <= 8 and G nb <= 16384");
     if (!q || !keys || !scores) return fail(CSA_ERR_INVALID_ARG, "block_score: NULL tensor pointer");
     if (!aligned16(q) || !aligned16(keys) || !aligned4(scores))
         return fail(CSA_ERR_INVALID_ARG, "block_score: misaligned tensor");
+    if (mode == CSA_SCORE_PROXY_ERROR) {
+        if (int rc = check_ws(error_score_ws(d), ws, ws_bytes)) return rc;
+        float* lg = d.G == 1 ? scores : static_cast<float*>(ws);
+        float* parts = d.G == 1 ? nullptr
+                                : reinterpret_cast<float*>(static_cast<char*>(ws) + align256(block_score_ws(d)));
+        const hipError_t e = csa::launch_score_err(d, q, keys, lg, parts, scores, stream);
+        return e == hipSuccess ? CSA_OK : hip_fail(e, "block_score");
+    }
     if (int rc = check_ws(block_score_ws(d), ws, ws_bytes)) return rc;
     if (mode == CSA_SCORE_COBS2) {
         const hipError_t e =
@@ -255,9 +282,9 @@ int selective_decode_step(const csa_shape* shape, csa_score_mode mode, const voi
 {
     csa::Dims d;
     if (int rc = make_dims(shape, &d)) return rc;
-    if (mode == CSA_SCORE_BOX || mode == CSA_SCORE_COBS2)
-        return fail(CSA_ERR_UNSUPPORTED, "selective_decode_step: box and second-order scores need Kbox or Kcov; "
-                                         "call block_score, topk_select and sparse_decode_attn");
+    if (mode == CSA_SCORE_BOX || mode == CSA_SCORE_COBS2 || mode == CSA_SCORE_PROXY_ERROR)
+        return fail(CSA_ERR_UNSUPPORTED, "selective_decode_step: box, second-order and proxy-error scores need "
+                                         "Kbox, Kcov or Kvar; call block_score, topk_select and sparse_decode_attn");
     if (mode != CSA_SCORE_SUMMARY && mode != CSA_SCORE_EXACT_MASS)
         return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: unknown mode %d", (int)mode);
     if (proxy_mode != CSA_PROXY_NONE && proxy_mode != CSA_PROXY_COMPLEMENT)
@@ -323,6 +350,7 @@ size_t csa_workspace_size(const csa_shape* shape, csa_entry entry, int32_t k, in
     case CSA_WS_BLOCK_SCORE_EXACT_MASS:
     case CSA_WS_BLOCK_SCORE_BOX:
     case CSA_WS_BLOCK_SCORE_COBS2: return block_score_ws(d);
+    case CSA_WS_BLOCK_SCORE_PROXY_ERROR: return error_score_ws(d);
     case CSA_WS_SPARSE_DECODE_ATTN: {
         if (k < 0 || k > d.nb || m < 0) {
             fail(CSA_ERR_INVALID_ARG, "csa_workspace_size: k=%d or m=%d out of range", k, m);

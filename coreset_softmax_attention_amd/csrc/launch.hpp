@@ -42,6 +42,15 @@ hipError_t launch_cov(const Dims& s, const void* K, void* Kcov, hipStream_t st);
 // ([B, Hq, nb], or the scores themselves when G == 1).
 hipError_t launch_score_cobs2(const Dims& s, const void* q, const void* Kcov, float* logits, float* scores,
                               hipStream_t st);
+// Mean and variance tokens Kvar [B, Hkv, nb, 2, d] of the proxy-error scores.
+hipError_t launch_var(const Dims& s, const void* K, void* Kvar, hipStream_t st);
+// Proxy-error block scores from Kvar (bfloat16, fused_summary_score_ok()); with
+// fewer than kFusedStepMinPairs KV heads the log-errors go through `logits`
+// ([B, Hq, nb], or the scores themselves when G == 1) and the normaliser
+// states through `parts` (score_err_parts_bytes()).
+size_t score_err_parts_bytes(const Dims& s);
+hipError_t launch_score_err(const Dims& s, const void* q, const void* Kvar, float* logits, float* parts,
+                            float* scores, hipStream_t st);
 // Summary mode with the logits, log-normalisers and group score in one kernel
 // (one workgroup per KV head); available when fused_summary_score_ok().
 bool fused_summary_score_ok(const Dims& s);

@@ -383,6 +383,7 @@ struct FusedScoreParams {
     float* scores;
     float* logits;  // split: [B, Hq, nb] (the scores when G == 1)
     int32_t* sel;   // finish: selection [B, Hkv, k] when k > 0
+    float* parts;   // proxy-error split: per (KV head, tile, head) log2 (max, sum) of the summary logits
     int Hq, Hkv, G, nb, k, chunks;
     float scale, ln_L, ln_last;
 };
@@ -437,10 +438,11 @@ __device__ __forceinline__ void key_tile_logits(const FusedScoreParams& p, const
 // whole workgroup (NW waves): written to lsm[b] (row 0, in place: block b's
 // column is read only by the thread that writes it) and to scores when given.
 template <int NW>
-__device__ __forceinline__ void group_scores_in_lds(float* lsm, float* lse_h, int G, int nb, float* scores)
+__device__ __forceinline__ void group_scores_in_lds(float* lsm, float* lse_h, int G, int nb, float* scores,
+                                                    bool lse_given = false)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (G > 1) {
+    if (G > 1 && !lse_given) {
         for (int h = wave; h < G; h += NW) {
             const float lse = head_lse(lsm + h * nb, nb, lane);
             if (lane == 0) lse_h[h] = lse;
@@ -639,6 +641,176 @@ __global__ void __launch_bounds__(kSplitWaves * 64) score_cobs2_split_kernel(con
     cobs2_tile_logits<D>(p, kr, bq, base, p.logits + (size_t)pair * p.G * p.nb, p.nb, lane, tmp[wave]);
 }
 
+// Proxy-error logits ("OpenAttention reads 1% of the KV cache -- Count-aware
+// tail proxy": the weight error a proxy leaves is its mass times the spread of
+// the weights it hides, estimated from cached mean and variance tokens).  Rows
+// Kvar [.., nb, 2, d]: the mean key and the per-coordinate key variance of each
+// block.  For the tile of blocks [base, base + 32), lane (n16, g16) gets head
+// n16 of blocks base + 16 rb + 4 g16 + i from three MFMA chains: the summary
+// logit shat = scale q.kbar + ln c from the mean rows, and sum_t q_t^2 var_t
+// from the variance rows against q^2 split into two bfloat16 halves (q is
+// bfloat16, so q^2 has at most 16 significant bits and hi + lo holds it
+// exactly; the products are exact in fp32).  The log-error shat + ln sigma,
+// sigma = scale sqrt(sum), goes to dst[h * stride + b] (-inf for sigma = 0);
+// the lane's online log-sum-exp of shat (log2 units) is kept in (m2, s2).
+template <int D>
+__device__ __forceinline__ void err_tile_logits(const FusedScoreParams& p, __amdgpu_buffer_rsrc_t kr,
+                                                const bf16x8_t (&bq)[D / 32], const bf16x8_t (&bqh)[D / 32],
+                                                const bf16x8_t (&bql)[D / 32], int base, float* dst, int stride,
+                                                int lane, float& m2, float& s2)
+{
+    constexpr int RB = D * 2, KS = D / 32;
+    const int n16 = lane & 15, g16 = lane >> 4;
+    uint4 am[2][KS], av[2][KS];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const uint32_t om = (uint32_t)(base + rb * 16 + n16) * 2 * RB + g16 * 16;  // past nb: zeros
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            am[rb][s] = buffer_ld16(kr, om + s * 64);
+            av[rb][s] = buffer_ld16(kr, om + RB + s * 64);
+        }
+    }
+    f32x4_t cm[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+    f32x4_t cv[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            cm[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, am[rb][s]), bq[s], cm[rb], 0, 0,
+                                                             0);
+            cv[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[rb][s]), bqh[s], cv[rb], 0,
+                                                             0, 0);
+            cv[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[rb][s]), bql[s], cv[rb], 0,
+                                                             0, 0);
+        }
+    if (n16 < p.G) {
+        const float s2c = p.scale * p.scale;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int b = base + rb * 16 + 4 * g16 + i;
+                if (b < p.nb) {
+                    const float sh = fmaf(cm[rb][i], p.scale, b == p.nb - 1 ? p.ln_last : p.ln_L);
+                    const float var = cv[rb][i] * s2c;
+                    dst[n16 * stride + b] = var > 0.0f ? sh + 0.5f * logf(var) : kNegInf;
+                    const float t = sh * kLog2e;
+                    const float mn = fmaxf(m2, t);
+                    s2 = s2 * rescale(m2, mn) + exp2_(t - mn);
+                    m2 = mn;
+                }
+            }
+    }
+}
+
+// q^2 as two bfloat16 operands (hi + lo == q^2 exactly) in the layout of bq.
+template <int D>
+__device__ __forceinline__ void square_q_operand(const bf16x8_t (&bq)[D / 32], bf16x8_t (&hi)[D / 32],
+                                                 bf16x8_t (&lo)[D / 32])
+{
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+        const uint4 v = __builtin_bit_cast(uint4, bq[s]);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        uint32_t wh[4], wl[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            uint32_t h2 = 0, l2 = 0;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const float f = __uint_as_float(half ? (w[e] & 0xffff0000u) : (w[e] << 16));
+                const float sq = f * f;  // exact: 8 significant bits squared
+                const uint32_t hb = bf16_from_f64((double)sq);
+                const uint32_t lb = bf16_from_f64((double)(sq - __uint_as_float(hb << 16)));
+                h2 |= hb << (16 * half);
+                l2 |= lb << (16 * half);
+            }
+            wh[e] = h2;
+            wl[e] = l2;
+        }
+        hi[s] = __builtin_bit_cast(bf16x8_t, make_uint4(wh[0], wh[1], wh[2], wh[3]));
+        lo[s] = __builtin_bit_cast(bf16x8_t, make_uint4(wl[0], wl[1], wl[2], wl[3]));
+    }
+}
+
+// Merge the online log-sum-exp states of the four lane groups holding one head:
+// lanes n16, n16 + 16, n16 + 32, n16 + 48.
+__device__ __forceinline__ void merge_lse_groups(float& m2, float& s2)
+{
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const LanePair pm = r == 0 ? swap16(__float_as_uint(m2)) : swap32(__float_as_uint(m2));
+        const LanePair ps = r == 0 ? swap16(__float_as_uint(s2)) : swap32(__float_as_uint(s2));
+        const float ma = __uint_as_float(pm.a), mb = __uint_as_float(pm.b);
+        const float mn = fmaxf(ma, mb);
+        s2 = __uint_as_float(ps.a) * rescale(ma, mn) + __uint_as_float(ps.b) * rescale(mb, mn);
+        m2 = mn;
+    }
+}
+
+template <int D>
+__global__ void __launch_bounds__(kFusedWaves * 64) score_err_fused_kernel(const FusedScoreParams p)
+{
+    constexpr int RB = D * 2, KS = D / 32, NW = kFusedWaves;
+    extern __shared__ float lsm[];  // [G][nb] log-errors
+    __shared__ float lse_h[8];
+    __shared__ float pm[NW][8], ps[NW][8];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int pair = blockIdx.x, b = pair / p.Hkv, j = pair - b * p.Hkv;
+    bf16x8_t bq[KS], bqh[KS], bql[KS];
+    load_q_operand<D>(p.q + ((size_t)b * p.Hq + (size_t)j * p.G) * RB, p.G, lane, bq);
+    square_q_operand<D>(bq, bqh, bql);
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(p.Kbar + (size_t)pair * p.nb * 2 * RB, (uint32_t)p.nb * 2 * RB);
+    float m2 = kNegInf, s2 = 0.0f;
+    for (int base = wave * 32; base < p.nb; base += NW * 32)
+        err_tile_logits<D>(p, kr, bq, bqh, bql, base, lsm, p.nb, lane, m2, s2);
+    merge_lse_groups(m2, s2);
+    if (lane < 8) {
+        pm[wave][lane] = m2;
+        ps[wave][lane] = s2;
+    }
+    __syncthreads();
+    if (threadIdx.x < (unsigned)p.G) {
+        float M = kNegInf;
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, pm[w][threadIdx.x]);
+        float S = 0.0f;
+        for (int w = 0; w < NW; ++w) S += ps[w][threadIdx.x] * rescale(pm[w][threadIdx.x], M);
+        lse_h[threadIdx.x] = (M + log2f(S)) * kLn2;
+    }
+    __syncthreads();
+    group_scores_in_lds<NW>(lsm, lse_h, p.G, p.nb, p.scores + (size_t)pair * p.nb, true);
+}
+
+// Split form: workgroup (pair, chunk), one tile per wave; the log-errors go to
+// p.logits and each wave's log-sum-exp state of the summary logits, per head,
+// to p.parts [pair][tile][8][2].
+template <int D>
+__global__ void __launch_bounds__(kSplitWaves * 64) score_err_split_kernel(const FusedScoreParams p)
+{
+    constexpr int RB = D * 2, KS = D / 32;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int pair = blockIdx.x / p.chunks, chunk = blockIdx.x - pair * p.chunks;
+    const int b = pair / p.Hkv, j = pair - b * p.Hkv;
+    const int tile = chunk * kSplitWaves + wave, base = tile * 32;
+    if (base >= p.nb) return;  // whole wave; no barrier in this kernel
+    bf16x8_t bq[KS], bqh[KS], bql[KS];
+    load_q_operand<D>(p.q + ((size_t)b * p.Hq + (size_t)j * p.G) * RB, p.G, lane, bq);
+    square_q_operand<D>(bq, bqh, bql);
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(p.Kbar + (size_t)pair * p.nb * 2 * RB, (uint32_t)p.nb * 2 * RB);
+    float m2 = kNegInf, s2 = 0.0f;
+    err_tile_logits<D>(p, kr, bq, bqh, bql, base, p.logits + (size_t)pair * p.G * p.nb, p.nb, lane, m2, s2);
+    merge_lse_groups(m2, s2);
+    if (p.parts && lane < 8) {
+        const int tiles = (p.nb + 31) / 32;
+        float* dst = p.parts + (((size_t)pair * tiles + tile) * 8 + lane) * 2;
+        dst[0] = m2;
+        dst[1] = s2;
+    }
+}
+
 // Group scores (and the top-k when p.k > 0) of one KV head from split logits.
 __global__ void __launch_bounds__(kFusedWaves * 64) score_finish_kernel(const FusedScoreParams p)
 {
@@ -664,8 +836,17 @@ __global__ void __launch_bounds__(kFusedWaves * 64) score_finish_kernel(const Fu
             if (i < G * nb) lsm[i] = v[c];
         }
     }
+    if (p.parts && threadIdx.x < (unsigned)G) {  // proxy-error scores: normalisers from the tile states
+        const int tiles = (nb + 31) / 32;
+        const float* st = p.parts + (size_t)pair * tiles * 16 + threadIdx.x * 2;
+        float M = kNegInf;
+        for (int t = 0; t < tiles; ++t) M = fmaxf(M, st[t * 16]);
+        float S = 0.0f;
+        for (int t = 0; t < tiles; ++t) S += st[t * 16 + 1] * rescale(st[t * 16], M);
+        lse_h[threadIdx.x] = (M + log2f(S)) * kLn2;
+    }
     __syncthreads();
-    group_scores_in_lds<NW>(lsm, lse_h, G, nb, p.scores ? p.scores + (size_t)pair * nb : nullptr);
+    group_scores_in_lds<NW>(lsm, lse_h, G, nb, p.scores ? p.scores + (size_t)pair * nb : nullptr, p.parts != nullptr);
     if (p.k > 0) {
         __syncthreads();
         if (wave == 0) {
@@ -780,6 +961,47 @@ hipError_t launch_score_cobs2(const Dims& s, const void* q, const void* Kcov, fl
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || s.G == 1) return e;  // G == 1: the logits are the scores
     return launch_score_finish(s, logits, scores, nullptr, 0, st);
+}
+
+size_t score_err_parts_bytes(const Dims& s)
+{
+    return (size_t)s.pairs() * ((s.nb + 31) / 32) * 16 * sizeof(float);
+}
+
+hipError_t launch_score_err(const Dims& s, const void* q, const void* Kvar, float* logits, float* parts,
+                            float* scores, hipStream_t st)
+{
+    FusedScoreParams p = summary_params(s, q, Kvar, false);
+    p.scores = scores;
+    p.logits = logits;
+    if (s.pairs() >= kFusedStepMinPairs) {
+        const size_t shm = (size_t)s.G * s.nb * sizeof(float);
+        const dim3 grid((unsigned)s.pairs()), block(kFusedWaves * 64);
+        if (s.d == 128)
+            score_err_fused_kernel<128><<<grid, block, shm, st>>>(p);
+        else
+            score_err_fused_kernel<64><<<grid, block, shm, st>>>(p);
+        return hipGetLastError();
+    }
+    p.parts = s.G == 1 ? nullptr : parts;
+    const int tiles = (s.nb + 31) / 32;
+    p.chunks = (tiles + kSplitWaves - 1) / kSplitWaves;
+    const dim3 grid((unsigned)(s.pairs() * p.chunks)), block(kSplitWaves * 64);
+    if (s.d == 128)
+        score_err_split_kernel<128><<<grid, block, 0, st>>>(p);
+    else
+        score_err_split_kernel<64><<<grid, block, 0, st>>>(p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || s.G == 1) return e;  // G == 1: the log-errors are the scores
+    FusedScoreParams f{};
+    f.logits = logits;
+    f.scores = scores;
+    f.parts = parts;
+    f.G = s.G;
+    f.nb = s.nb;
+    const size_t shm = (size_t)s.G * s.nb * sizeof(float);
+    score_finish_kernel<<<dim3((unsigned)s.pairs()), dim3(kFusedWaves * 64), shm, st>>>(f);
+    return hipGetLastError();
 }
 
 bool score_finish_ok(const Dims& s)

@@ -80,6 +80,7 @@ __device__ __forceinline__ float group_score(const float* l, int stride, const f
 #pragma unroll
     for (int h = 0; h < MAXG; ++h)
         if (h < G) mx = fmaxf(mx, x[h]);
+    if (mx == kNegInf) return kNegInf;  // no head gives the block any weight
     float sum = 0.0f;
 #pragma unroll
     for (int h = 0; h < MAXG; ++h)

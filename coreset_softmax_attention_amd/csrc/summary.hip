@@ -1,4 +1,5 @@
-// summary.hip -- per-block mean key and mean value.
+// summary.hip -- per-block mean key and mean value; the key box and the
+// variance token of the alternative block scores.
 //
 // The count-aware proxy of an unread block is one virtual token whose value is
 // the mean value of the block's tokens ("OpenAttention reads 1% of the KV cache
@@ -171,7 +172,110 @@ hipError_t launch_box_dtd(const Dims& s, const void* K, void* Kbox, hipStream_t 
     return hipGetLastError();
 }
 
+// Mean and variance tokens (the proxy-error ranking of "OpenAttention reads 1%
+// of the KV cache -- Count-aware tail proxy", section "Three helpers that make
+// the proxy accurate"): Kvar [pairs, nb, 2, d], row 0 the mean key (the bits of
+// the summary kernel: token-order fp64 sum over the count, rounded once), row 1
+// the per-coordinate variance about the exact fp64 mean, (1/c) sum_i (k_i -
+// mean)^2, also summed token by token in fp64 (no fused multiply-add, so the
+// sum is the same sequence of roundings everywhere) and rounded once.  The
+// keys are read twice; the second pass finds them in cache.
+template <int DT, int D>
+__global__ void __launch_bounds__(kNW * 64) var_kernel(const char* K, char* Kvar, int n, int L, int nb, long long total)
+{
+#pragma clang fp contract(off)
+    using Gm = RowGeom<DT, D>;
+    constexpr int LPR = Gm::lpr, RPW = Gm::rpw, EPL = Gm::epl, RB = Gm::row_bytes;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int gi = lane / LPR, li = lane % LPR;
+    const long long gblk = ((long long)blockIdx.x * kNW + wave) * RPW + gi;
+    if (gblk >= total) return;  // no cross-lane operations below
+    const long long pair = gblk / nb;
+    const int blk = (int)(gblk - pair * nb);
+    const int t0 = blk * L, c = min(L, n - t0);
+    const char* kp = K + ((size_t)pair * n + t0) * RB + li * 16;
+
+    double s1[EPL], s2[EPL], mean[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) s1[e] = s2[e] = 0.0;
+    for (int i = 0; i < c; i += kU) {
+        uint4 kr[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) kr[u] = ld16(kp + (size_t)min(i + u, c - 1) * RB);
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            if (i + u < c) {  // tokens in order
+                float kf[EPL];
+                unpack<DT>(kr[u], kf);
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) s1[e] += (double)kf[e];
+            }
+        }
+    }
+    const double cd = (double)c;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) mean[e] = s1[e] / cd;
+    for (int i = 0; i < c; i += kU) {
+        uint4 kr[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) kr[u] = ld16_nt(kp + (size_t)min(i + u, c - 1) * RB);
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            if (i + u < c) {
+                float kf[EPL];
+                unpack<DT>(kr[u], kf);
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) {
+                    const double dv = (double)kf[e] - mean[e];
+                    s2[e] += dv * dv;
+                }
+            }
+        }
+    }
+    uint32_t wm[4], wv[4];
+    if constexpr (DT == DT_F32) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            wm[e] = __float_as_uint((float)mean[e]);
+            wv[e] = __float_as_uint((float)(s2[e] / cd));
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            wm[e] = (uint32_t)bf16_from_f64(mean[2 * e]) | ((uint32_t)bf16_from_f64(mean[2 * e + 1]) << 16);
+            wv[e] = (uint32_t)bf16_from_f64(s2[2 * e] / cd) | ((uint32_t)bf16_from_f64(s2[2 * e + 1] / cd) << 16);
+        }
+    }
+    char* out = Kvar + ((size_t)pair * nb + blk) * 2 * RB + li * 16;
+    *reinterpret_cast<uint4*>(out) = make_uint4(wm[0], wm[1], wm[2], wm[3]);
+    *reinterpret_cast<uint4*>(out + RB) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+}
+
+template <int DT, int D>
+hipError_t launch_var_dtd(const Dims& s, const void* K, void* Kvar, hipStream_t st)
+{
+    using Gm = RowGeom<DT, D>;
+    const long long total = (long long)s.pairs() * s.nb;
+    const long long per_wg = (long long)kNW * Gm::rpw;
+    const long long wgs = (total + per_wg - 1) / per_wg;
+    var_kernel<DT, D><<<dim3((unsigned)wgs), dim3(kNW * 64), 0, st>>>(static_cast<const char*>(K),
+                                                                        static_cast<char*>(Kvar), s.n, s.L, s.nb, total);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_var(const Dims& s, const void* K, void* Kvar, hipStream_t st)
+{
+    if (s.dtype == DT_BF16) {
+        if (s.d == 128) return launch_var_dtd<DT_BF16, 128>(s, K, Kvar, st);
+        if (s.d == 64) return launch_var_dtd<DT_BF16, 64>(s, K, Kvar, st);
+    } else {
+        if (s.d == 128) return launch_var_dtd<DT_F32, 128>(s, K, Kvar, st);
+        if (s.d == 64) return launch_var_dtd<DT_F32, 64>(s, K, Kvar, st);
+    }
+    return hipErrorInvalidValue;
+}
 
 hipError_t launch_box(const Dims& s, const void* K, void* Kbox, hipStream_t st)
 {

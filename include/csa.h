@@ -77,7 +77,8 @@ typedef enum csa_score_mode {
     CSA_SCORE_SUMMARY = 0,    /* first-order score from the mean key  [COBS] Eq. (18) */
     CSA_SCORE_EXACT_MASS = 1, /* exact block mass from every key ("OSA")             */
     CSA_SCORE_BOX = 2,        /* best logit over the block's min/max key box (Quest) */
-    CSA_SCORE_COBS2 = 3       /* second-order (mean + covariance) estimate of ln m_b */
+    CSA_SCORE_COBS2 = 3,      /* second-order (mean + covariance) estimate of ln m_b */
+    CSA_SCORE_PROXY_ERROR = 4 /* estimated weight error of the block's proxy [OA]   */
 } csa_score_mode;
 
 /* Scaled eigenvectors per block in the second-order descriptor (kv_cov_build). */
@@ -95,7 +96,8 @@ typedef enum csa_entry {
     CSA_WS_DENSE_DECODE_ATTN = 3,
     CSA_WS_SELECTIVE_DECODE_STEP = 4,
     CSA_WS_BLOCK_SCORE_BOX = 5,
-    CSA_WS_BLOCK_SCORE_COBS2 = 6
+    CSA_WS_BLOCK_SCORE_COBS2 = 6,
+    CSA_WS_BLOCK_SCORE_PROXY_ERROR = 7
 } csa_entry;
 
 typedef struct csa_shape {
@@ -146,6 +148,21 @@ int kv_box_build(const csa_shape* shape, const void* K, void* Kbox, hipStream_t 
 int kv_cov_build(const csa_shape* shape, const void* K, void* Kcov, hipStream_t stream);
 
 /*
+ * kv_var_build -- per block, the mean and the variance tokens that the
+ * proxy-error ranking of [OA] reads (section "Three helpers that make the
+ * proxy accurate": mean and variance tokens cached per group of tokens, the
+ * variance being the half row of the 1.5 rows per group; the error it
+ * estimates is the one described in section "Skipping reviews without losing
+ * the verdict"): row 0 the mean key (the same bits as kv_summary_build's
+ * Kbar), row 1 the per-coordinate variance of the block's keys about their
+ * exact mean, var_bt = (1/c_b) sum_{i in b} (K_it - mean_bt)^2, summed in fp64
+ * token by token and rounded once to the storage dtype.  Reads K [B, Hkv, n, d];
+ * writes Kvar [B, Hkv, nb, 2, d].  Run once per cache (after prefill); no
+ * workspace.
+ */
+int kv_var_build(const csa_shape* shape, const void* K, void* Kvar, hipStream_t stream);
+
+/*
  * block_score -- the score by which blocks are ranked, per KV head.
  * Per query head h and block b the block logit is
  *   SUMMARY:    l_hb = scale q_h . Kbar_b + ln c_b         (keys = Kbar)  [COBS] Eq. (18)
@@ -155,13 +172,24 @@ int kv_cov_build(const csa_shape* shape, const void* K, void* Kcov, hipStream_t 
  *   COBS2:      l_hb = scale q_h . Kbar_b + ln c_b + (1/2) scale^2 sum_i (q_h . xi_bi)^2
  *               (keys = Kcov from kv_cov_build; bfloat16, G <= 8 and G nb <= 16384,
  *               else CSA_ERR_UNSUPPORTED)
+ *   PROXY_ERROR: l_hb = shat_hb + ln sigma_hb, the log of the estimated weight
+ *               error of the block's proxy, its mass e^{shat_hb} times the spread
+ *               of the logits it hides ([OA]), with shat_hb the SUMMARY logit and
+ *               sigma_hb = scale sqrt(sum_t q_ht^2 var_bt) the standard deviation
+ *               of the block's logits over its tokens when its key coordinates
+ *               are uncorrelated (-inf when the block's keys are all equal: its
+ *               proxy is exact).  keys = Kvar from kv_var_build; bfloat16,
+ *               G <= 8 and G nb <= 16384, else CSA_ERR_UNSUPPORTED.
  * and the score of block b of KV head j is
  *   G = 1: l_hb (ranking by log-mass, [COBS] Eq. (5) with G = 1);
  *   G > 1: ln sum_{h in group j} exp(l_hb - ln sum_b' e^{l_hb'}),
- *          the logarithm of the additive GQA score of [COBS] Eq. (5).
+ *          the logarithm of the additive GQA score of [COBS] Eq. (5);
+ *          PROXY_ERROR normalises by the proxy masses instead,
+ *          ln sum_h exp(l_hb - ln sum_b' e^{shat_hb'}): each head's error as a
+ *          share of its estimated softmax denominator.
  * Writes scores [B, Hkv, nb].  Workspace: csa_workspace_size(shape,
- * CSA_WS_BLOCK_SCORE_SUMMARY, _EXACT_MASS, _BOX or _COBS2, 0, 0) bytes (0 when
- * G = 1).
+ * CSA_WS_BLOCK_SCORE_SUMMARY, _EXACT_MASS, _BOX, _COBS2 or _PROXY_ERROR, 0, 0)
+ * bytes (0 when G = 1).
  */
 int block_score(const csa_shape* shape, csa_score_mode mode, const void* q, const void* keys,
                 float* scores, void* ws, size_t ws_bytes, hipStream_t stream);
@@ -217,9 +245,10 @@ int dense_decode_attn(const csa_shape* shape, const void* q, const void* K, cons
  * (bfloat16, G <= 8, k <= 32, nb <= 2048, B * Hkv >= 32) one kernel per KV head
  * reads Kbar once, keeps the logits on chip for both uses, selects the blocks
  * and attends; otherwise the three entry points run in turn.
- * keys = Kbar (SUMMARY) or K (EXACT_MASS) as for block_score (BOX and COBS2
- * scores are CSA_ERR_UNSUPPORTED here: they need Kbox or Kcov besides Kbar; use
- * the three entry points); Kbar may be NULL in EXACT_MASS mode without proxies.  scores [B, Hkv, nb] and
+ * keys = Kbar (SUMMARY) or K (EXACT_MASS) as for block_score (BOX, COBS2 and
+ * PROXY_ERROR scores are CSA_ERR_UNSUPPORTED here: they need Kbox, Kcov or Kvar
+ * besides Kbar; use the three entry points); Kbar may be NULL in EXACT_MASS
+ * mode without proxies.  scores [B, Hkv, nb] and
  * sel [B, Hkv, min(k, nb)] are written when not NULL.  0 <= k; k = 0 with no
  * proxies and m = 0 is CSA_ERR_INVALID_ARG.  Workspace: csa_workspace_size(
  * shape, CSA_WS_SELECTIVE_DECODE_STEP, k, m) bytes.

@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = set(declared_functions())
-    assert {"kv_summary_build", "kv_box_build", "kv_cov_build", "block_score", "topk_select", "sparse_decode_attn",
+    assert {"kv_summary_build", "kv_box_build", "kv_cov_build", "kv_var_build", "block_score", "topk_select", "sparse_decode_attn",
             "dense_decode_attn", "selective_decode_step", "csa_workspace_size", "csa_status_str",
             "csa_last_error"} <= names
 
@@ -141,6 +141,26 @@ def test_cov_build_argument_checks(L):
     assert step(L, s, mode=csa.CSA_SCORE_COBS2) == csa.CSA_ERR_UNSUPPORTED
 
 
+def test_var_build_and_proxy_error_argument_checks(L):
+    s = shape()  # B=2, Hq=8, Hkv=2, n=1024, L=64: nb = 16, one tile of 32 blocks per KV head
+    assert L.kv_var_build(ctypes.byref(s), None, FAKE, None) == csa.CSA_ERR_INVALID_ARG
+    assert L.kv_var_build(ctypes.byref(s), FAKE, FAKE + 8, None) == csa.CSA_ERR_INVALID_ARG
+    assert b"aligned" in L.csa_last_error()
+    assert L.kv_var_build(None, FAKE, FAKE, None) == csa.CSA_ERR_INVALID_ARG
+    # log-errors [B, Hq, nb], 256-byte aligned, then (max, sum) per (KV head, tile, 8 heads)
+    need = L.csa_workspace_size(ctypes.byref(s), csa.CSA_WS_BLOCK_SCORE_PROXY_ERROR, 0, 0)
+    assert need == 2 * 8 * 16 * 4 + 2 * 2 * 1 * 16 * 4
+    assert L.block_score(ctypes.byref(s), csa.CSA_SCORE_PROXY_ERROR, FAKE, FAKE, FAKE, None, 0,
+                         None) == csa.CSA_ERR_WORKSPACE
+    g1 = shape(Hq=2)
+    assert L.csa_workspace_size(ctypes.byref(g1), csa.CSA_WS_BLOCK_SCORE_PROXY_ERROR, 0, 0) == 0
+    f32 = shape(dtype=csa.CSA_F32)
+    assert L.block_score(ctypes.byref(f32), csa.CSA_SCORE_PROXY_ERROR, FAKE, FAKE, FAKE, FAKE, 1 << 20,
+                         None) == csa.CSA_ERR_UNSUPPORTED
+    assert b"proxy-error" in L.csa_last_error()
+    assert step(L, s, mode=csa.CSA_SCORE_PROXY_ERROR) == csa.CSA_ERR_UNSUPPORTED
+
+
 def test_box_build_argument_checks(L):
     s = shape()
     assert L.kv_box_build(ctypes.byref(s), None, FAKE, None) == csa.CSA_ERR_INVALID_ARG
@@ -190,7 +210,7 @@ def step(L, s, mode=0, k=2, m=0, proxy=1, ptrs=FAKE, kbar=FAKE, ws=None, wsb=0):
 def test_decode_step_argument_checks(L):
     s = shape()
     assert step(L, None) == csa.CSA_ERR_INVALID_ARG
-    assert step(L, s, mode=4) == csa.CSA_ERR_INVALID_ARG
+    assert step(L, s, mode=9) == csa.CSA_ERR_INVALID_ARG
     assert step(L, s, mode=csa.CSA_SCORE_BOX) == csa.CSA_ERR_UNSUPPORTED
     assert b"Kbox" in L.csa_last_error()
     assert step(L, s, proxy=3) == csa.CSA_ERR_INVALID_ARG
