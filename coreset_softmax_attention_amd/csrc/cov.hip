@@ -8,138 +8,207 @@
 // decreasing eigenvalue, each signed so that its largest-magnitude coordinate
 // is positive (the first such coordinate on ties).
 //
-// One wave per block (c <= 64 tokens).  With X the centred c x d key matrix,
-// the nonzero spectrum of Sigma is that of the c x c Gram matrix G = X X^T
-// over c: if G v = mu v with |v| = 1 then xi = X^T v / sqrt(c) (its squared
-// norm is mu / c = lambda).  Lane l owns row l of X (in LDS) and of G (in
-// registers).  The top eigenvectors of G come from a Lanczos run with full
-// reorthogonalisation run to the whole Krylov space (so the Ritz pairs are the
-// eigenpairs); the Ritz values are found by bisection on Sturm counts
-// of the tridiagonal matrix, all 64 lanes testing shifts at once, and their
-// vectors by inverse iteration.  Everything is fp32 except the mean.
+// One workgroup of one wave per block (c <= 64 tokens; ~38 KiB of LDS, so four
+// blocks share a compute unit).  With X the centred c x d key matrix, the
+// nonzero spectrum of Sigma is that of the c x c Gram matrix G = X X^T over c:
+// if G v = mu v with |v| = 1 then xi = X^T v / sqrt(c) (its squared norm is
+// mu / c = lambda).  Lane l owns row l of X (in LDS) and of G (in registers).
+// The top eigenvectors of G come from a Lanczos run with full
+// reorthogonalisation (two batched classical Gram-Schmidt passes per step, no
+// cross-lane sums) run to the whole Krylov space, so the Ritz pairs are the
+// eigenpairs; the Ritz values are found by multisection on Sturm counts of the
+// tridiagonal matrix (a group of 16 lanes per eigenvalue) and their vectors by
+// inverse iteration; xi reads the keys again.  Everything is fp32 except the
+// mean.
 #include "device.hpp"
 #include "launch.hpp"
+#include "select.hpp"
 
 namespace csa {
 namespace {
 
-constexpr int kCovWaves = 2;    // waves (blocks) per workgroup
 constexpr int kCovMaxRows = 64; // tokens per block
 constexpr int kLanczos = 64;    // Lanczos steps: the whole Krylov space of a 64-token block
 
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 
-// LDS of one wave.
+// LDS of one wave (one block per workgroup).  The centred keys are needed only
+// to form the Gram matrix; their space then holds the Lanczos vectors.  Rows
+// are padded to a multiple of 4 floats plus 4, so that 16-byte row reads by 16
+// lanes at once fall on distinct banks.
 template <int D>
 struct CovSmem {
-    float x[kCovMaxRows][D + 1];  // centred keys (+1: no bank conflicts on column walks)
-    float v[kLanczos + 1][kCovMaxRows];  // Lanczos vectors
+    union {
+        float x[kCovMaxRows][D + 4];  // centred keys
+        struct {
+            float v[kLanczos + 1][kCovMaxRows + 4];  // Lanczos vectors, row k = v_k
+            float w[kCovMaxRows];                    // the vector being orthogonalised
+            float h[kLanczos];                       // its coefficients on v_0 .. v_k
+        } lz;
+    };
     float alpha[kLanczos], beta[kLanczos];
-    float theta[4];               // Ritz values, largest first
-    float y[4][kLanczos];         // their eigenvectors of the tridiagonal matrix
+    float theta[4];                          // Ritz values, largest first
+    float y[4][kLanczos];                    // their eigenvectors of the tridiagonal matrix
     float cp[4][kLanczos], dp[4][kLanczos];  // tridiagonal elimination
+    float z[4][kCovMaxRows];                 // Ritz vectors over the block's rows
 };
 
 template <int DT, int D, int R>
-__global__ void __launch_bounds__(kCovWaves * 64) cov_kernel(const char* K, char* Kcov, int n, int L, int nb,
-                                                             long long total)
+__global__ void __launch_bounds__(64) cov_kernel(const char* K, char* Kcov, int n, int L, int nb)
 {
-    constexpr int RB = D * Elem<DT>::bytes;  // bytes per key row
-    constexpr int CPL = D / 64;              // columns per lane
-    __shared__ CovSmem<D> smem[kCovWaves];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    CovSmem<D>& sm = smem[wave];
-    const long long gblk = (long long)blockIdx.x * kCovWaves + wave;
-    if (gblk >= total) return;  // whole wave; no workgroup barrier in this kernel
+    constexpr int EB = Elem<DT>::bytes;
+    constexpr int RB = D * EB;      // bytes per key row
+    constexpr int CPL = D / 64;     // columns per lane: lane owns CPL lane .. CPL lane + CPL - 1
+    static_assert(R <= 4, "at most four descriptors");
+    __shared__ CovSmem<D> sm;
+    const int lane = threadIdx.x;
+    const long long gblk = blockIdx.x;
     const long long pair = gblk / nb;
     const int blk = (int)(gblk - pair * nb);
     const int t0 = blk * L, c = min(L, n - t0);
     const char* kp = K + ((size_t)pair * n + t0) * RB;
     char* out = Kcov + ((size_t)pair * nb + blk) * (1 + R) * RB;
 
-    // ---- keys -> LDS (row per lane), mean row (fp64, token order, one rounding)
+    // ---- keys -> LDS (row per lane), mean of this lane's columns (fp64, token
+    // order, one rounding: the bits of the summary)
     if (lane < c) {
 #pragma unroll
         for (int ch = 0; ch < RB / 16; ++ch) {
             float f[Elem<DT>::per16];
             unpack<DT>(ld16(kp + (size_t)lane * RB + ch * 16), f);
 #pragma unroll
-            for (int e = 0; e < Elem<DT>::per16; ++e) sm.x[lane][ch * Elem<DT>::per16 + e] = f[e];
+            for (int e = 0; e < Elem<DT>::per16; e += 4)
+                *reinterpret_cast<float4*>(&sm.x[lane][ch * Elem<DT>::per16 + e]) = make_float4(f[e], f[e + 1], f[e + 2], f[e + 3]);
         }
     } else {
-        for (int t = 0; t < D; ++t) sm.x[lane][t] = 0.0f;
+        for (int t = 0; t < D; t += 4) *reinterpret_cast<float4*>(&sm.x[lane][t]) = make_float4(0.f, 0.f, 0.f, 0.f);
     }
     wave_lds_fence();
     double mean[CPL];
 #pragma unroll
-    for (int u = 0; u < CPL; ++u) {
-        const int t = lane + 64 * u;
+    for (int e = 0; e < CPL; ++e) {
+        const int t = CPL * lane + e;
         double s = 0.0;
         for (int i = 0; i < c; ++i) s += (double)sm.x[i][t];
-        mean[u] = s / (double)c;
+        mean[e] = s / (double)c;
     }
+    if constexpr (DT == DT_F32) {
 #pragma unroll
-    for (int u = 0; u < CPL; ++u) {
-        const int t = lane + 64 * u;
-        if constexpr (DT == DT_F32) {
-            reinterpret_cast<float*>(out)[t] = (float)mean[u];
-        } else {
-            reinterpret_cast<uint16_t*>(out)[t] = bf16_from_f64(mean[u]);
-        }
+        for (int e = 0; e < CPL; ++e) reinterpret_cast<float*>(out)[CPL * lane + e] = (float)mean[e];
+    } else {
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) reinterpret_cast<uint16_t*>(out)[CPL * lane + e] = bf16_from_f64(mean[e]);
     }
-    // centre
+    float meanf[CPL];
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) meanf[e] = (float)mean[e];
+    // centre (rows past the block stay zero)
     for (int i = 0; i < c; ++i) {
 #pragma unroll
-        for (int u = 0; u < CPL; ++u) sm.x[i][lane + 64 * u] -= (float)mean[u];
+        for (int e = 0; e < CPL; ++e) sm.x[i][CPL * lane + e] -= meanf[e];
     }
     wave_lds_fence();
 
-    // ---- Gram matrix row of this lane: g[j] = x_lane . x_j
+    // ---- Gram matrix row of this lane: g[j] = x_lane . x_j (16-byte LDS reads)
     float g[kCovMaxRows];
 #pragma unroll
     for (int j = 0; j < kCovMaxRows; ++j) g[j] = 0.0f;
-    for (int t = 0; t < D; ++t) {
-        const float xl = sm.x[lane][t];
+    for (int t = 0; t < D; t += 4) {
+        const float4 xl = *reinterpret_cast<const float4*>(&sm.x[lane][t]);
 #pragma unroll
-        for (int j = 0; j < kCovMaxRows; ++j) g[j] = fmaf(xl, sm.x[j][t], g[j]);
+        for (int j = 0; j < kCovMaxRows; ++j) {
+            const float4 xj = *reinterpret_cast<const float4*>(&sm.x[j][t]);
+            g[j] = fmaf(xl.x, xj.x, g[j]);
+            g[j] = fmaf(xl.y, xj.y, g[j]);
+            g[j] = fmaf(xl.z, xj.z, g[j]);
+            g[j] = fmaf(xl.w, xj.w, g[j]);
+        }
     }
     if (lane >= c) {
 #pragma unroll
         for (int j = 0; j < kCovMaxRows; ++j) g[j] = 0.0f;
     }
+    wave_lds_fence();  // the keys' space is reused for the Lanczos vectors
+    // start from zeros there: the batched projections read rows past the last
+    // vector (with zero weights), which must not hold stale non-finite bits
+    {
+        float* vz = &sm.lz.v[0][0];
+        constexpr int NV = (kLanczos + 1) * (kCovMaxRows + 4);
+        for (int i = 4 * lane; i < NV; i += 256) *reinterpret_cast<float4*>(vz + i) = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    wave_lds_fence();
 
-    // ---- Lanczos with full reorthogonalisation
+    // ---- Lanczos with full reorthogonalisation (classical Gram-Schmidt, two
+    // passes, batched: lane i forms the coefficient on v_i from its row of V, then
+    // lane l subtracts sum_i h_i v_i[l] reading its column; no cross-lane sums)
     const int steps = min(kLanczos, c);
     // start: a fixed pseudo-random vector over the block's rows (the all-ones
     // vector is in G's null space: the rows are centred)
     float v = 0.0f;
     if (lane < c) {
-        uint32_t h = (uint32_t)lane * 0x9E3779B1u + 0x7F4A7C15u;
-        h ^= h >> 15;
-        h *= 0x2C1B3C6Du;
-        h ^= h >> 12;
-        v = (float)(h & 0xFFFF) / 65536.0f + 0.5f;
+        uint32_t hsh = (uint32_t)lane * 0x9E3779B1u + 0x7F4A7C15u;
+        hsh ^= hsh >> 15;
+        hsh *= 0x2C1B3C6Du;
+        hsh ^= hsh >> 12;
+        v = (float)(hsh & 0xFFFF) / 65536.0f + 0.5f;
     }
     v /= sqrtf(wave_sum(v * v));
     int m = 0;  // Lanczos vectors kept
     float gnorm = 0.0f;
     for (int k = 0; k < steps; ++k) {
-        sm.v[k][lane] = v;
+        sm.lz.v[k][lane] = v;
         wave_lds_fence();
         float w = 0.0f;
 #pragma unroll
-        for (int j = 0; j < kCovMaxRows; ++j) w = fmaf(g[j], sm.v[k][j], w);
+        for (int j = 0; j < kCovMaxRows; j += 4) {
+            const float4 vj = *reinterpret_cast<const float4*>(&sm.lz.v[k][j]);
+            w = fmaf(g[j], vj.x, w);
+            w = fmaf(g[j + 1], vj.y, w);
+            w = fmaf(g[j + 2], vj.z, w);
+            w = fmaf(g[j + 3], vj.w, w);
+        }
         const float a = wave_sum(w * v);
         sm.alpha[k] = a;
         m = k + 1;
-        // w -= a v + beta v_{k-1}, then against every kept vector, twice
         w -= a * v;
-        if (k > 0) w -= sm.beta[k - 1] * sm.v[k - 1][lane];
-        for (int pass = 0; pass < 2; ++pass)
-            for (int i = 0; i <= k; ++i) {
-                const float vi = sm.v[i][lane];
-                w -= wave_sum(w * vi) * vi;
+        if (k > 0) w -= sm.beta[k - 1] * sm.lz.v[k - 1][lane];
+        for (int pass = 0; pass < 2; ++pass) {
+            sm.lz.w[lane] = w;
+            wave_lds_fence();
+            // lane i <= k: v_i . w (every load of the row issued before the products)
+            float4 vi[kCovMaxRows / 4], wl[kCovMaxRows / 4];
+#pragma unroll
+            for (int u = 0; u < kCovMaxRows / 4; ++u) {
+                vi[u] = *reinterpret_cast<const float4*>(&sm.lz.v[lane][4 * u]);
+                wl[u] = *reinterpret_cast<const float4*>(&sm.lz.w[4 * u]);
             }
+            float h0 = 0.0f, h1 = 0.0f;
+#pragma unroll
+            for (int u = 0; u < kCovMaxRows / 4; u += 2) {
+                h0 = fmaf(vi[u].x, wl[u].x, h0);
+                h0 = fmaf(vi[u].y, wl[u].y, h0);
+                h0 = fmaf(vi[u].z, wl[u].z, h0);
+                h0 = fmaf(vi[u].w, wl[u].w, h0);
+                h1 = fmaf(vi[u + 1].x, wl[u + 1].x, h1);
+                h1 = fmaf(vi[u + 1].y, wl[u + 1].y, h1);
+                h1 = fmaf(vi[u + 1].z, wl[u + 1].z, h1);
+                h1 = fmaf(vi[u + 1].w, wl[u + 1].w, h1);
+            }
+            sm.lz.h[lane] = lane <= k ? h0 + h1 : 0.0f;  // rows past v_k hold stale data
+            wave_lds_fence();
+            // w -= sum_{i <= k} h_i v_i, eight terms per round (h_i = 0 past k)
+            for (int i0 = 0; i0 <= k; i0 += 8) {
+                const float4 ha = *reinterpret_cast<const float4*>(&sm.lz.h[i0]);
+                const float4 hb = *reinterpret_cast<const float4*>(&sm.lz.h[i0 + 4]);
+                float vv[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) vv[u] = sm.lz.v[i0 + u][lane];
+                const float pa = (ha.x * vv[0] + ha.y * vv[1]) + (ha.z * vv[2] + ha.w * vv[3]);
+                const float pb = (hb.x * vv[4] + hb.y * vv[5]) + (hb.z * vv[6] + hb.w * vv[7]);
+                w -= pa + pb;
+            }
+            wave_lds_fence();  // w and h are rewritten by the next pass
+        }
         const float b = sqrtf(wave_sum(w * w));
         gnorm = fmaxf(gnorm, fabsf(a) + b);
         if (k + 1 == steps || b <= 1e-6f * gnorm) break;  // Krylov space exhausted
@@ -148,10 +217,10 @@ __global__ void __launch_bounds__(kCovWaves * 64) cov_kernel(const char* K, char
     }
     wave_lds_fence();
 
-    // ---- Ritz values: the R largest eigenvalues of the m x m tridiagonal T,
-    // by multisection on Sturm counts (all lanes test one shift each)
-    // number of eigenvalues of T below x
-    auto below = [&](float x) {
+    // ---- Ritz values: the R largest eigenvalues of the m x m tridiagonal T, by
+    // multisection on Sturm counts, all R at once: lane group r = lane / 16 brackets
+    // eigenvalue r with 16 shifts per round (4 bits per round)
+    auto below = [&](float x) {  // number of eigenvalues of T below x
         int cnt = 0;
         float dk = sm.alpha[0] - x;
         if (dk < 0.0f) ++cnt;
@@ -169,27 +238,27 @@ __global__ void __launch_bounds__(kCovWaves * 64) cov_kernel(const char* K, char
         ghi = fmaxf(ghi, sm.alpha[k] + r);
     }
     ghi *= 1.0001f;
-    for (int i = 0; i < R; ++i) {
-        const int idx = m - 1 - i;  // eigenvalue index in ascending order
+    {
+        const int r = lane >> 4, sub = lane & 15;
+        const int idx = m - 1 - r;  // eigenvalue index in ascending order
         float lo = glo, hi = ghi;
-        if (idx >= 0) {
-            for (int round = 0; round < 5; ++round) {
-                // lane l tests lo + (l + 1) (hi - lo) / 65
-                const float x = lo + (float)(lane + 1) * ((hi - lo) / 65.0f);
-                const bool above = below(x) <= idx;  // the eigenvalue lies at or above x
-                const uint64_t mk = __ballot(above);
-                const int nab = __popcll(mk);  // lanes 0..nab-1 have x below the eigenvalue
-                const float nlo = lo + (float)nab * ((hi - lo) / 65.0f);
-                const float nhi = lo + (float)(nab + 1) * ((hi - lo) / 65.0f);
-                lo = nlo;
-                hi = nhi;
-            }
+        for (int round = 0; round < 8; ++round) {
+            // lane (r, sub) tests lo + (sub + 1) (hi - lo) / 17
+            const float step = (hi - lo) / 17.0f;
+            const float x = lo + (float)(sub + 1) * step;
+            const bool above = idx >= 0 && below(x) <= idx;  // the eigenvalue lies at or above x
+            const uint64_t mk = __ballot(above);
+            const int nab = __popcll((mk >> (16 * r)) & 0xffffull);  // shifts of group r below it
+            const float nlo = lo + (float)nab * step;
+            hi = lo + (float)(nab + 1) * step;
+            lo = nlo;
         }
-        if (lane == 0) sm.theta[i] = idx >= 0 ? fmaxf(0.5f * (lo + hi), 0.0f) : 0.0f;
+        if (sub == 0 && r < R) sm.theta[r] = idx >= 0 ? fmaxf(0.5f * (lo + hi), 0.0f) : 0.0f;
     }
     wave_lds_fence();
 
-    // ---- eigenvectors of T by inverse iteration (lane i < R solves for theta_i)
+    // ---- eigenvectors of T by inverse iteration (lane i < R solves for theta_i);
+    // the elimination carries its last pivot and right-hand side in registers
     if (lane < R) {
         float* y = sm.y[lane];
         float* cp = sm.cp[lane];
@@ -201,18 +270,28 @@ __global__ void __launch_bounds__(kCovWaves * 64) cov_kernel(const char* K, char
             // solve (T - th I) z = y by elimination on the tridiagonal
             float den = sm.alpha[0] - th;
             den = fabsf(den) < tiny ? (den < 0.0f ? -tiny : tiny) : den;
-            cp[0] = m > 1 ? sm.beta[0] / den : 0.0f;
-            dp[0] = y[0] / den;
+            float cprev = m > 1 ? sm.beta[0] / den : 0.0f;
+            float dprev = y[0] / den;
+            cp[0] = cprev;
+            dp[0] = dprev;
             for (int k = 1; k < m; ++k) {
-                den = sm.alpha[k] - th - sm.beta[k - 1] * cp[k - 1];
+                const float bk1 = sm.beta[k - 1];
+                den = sm.alpha[k] - th - bk1 * cprev;
                 den = fabsf(den) < tiny ? (den < 0.0f ? -tiny : tiny) : den;
-                cp[k] = k + 1 < m ? sm.beta[k] / den : 0.0f;
-                dp[k] = (y[k] - sm.beta[k - 1] * dp[k - 1]) / den;
+                const float inv = 1.0f / den;
+                cprev = k + 1 < m ? sm.beta[k] * inv : 0.0f;
+                dprev = (y[k] - bk1 * dprev) * inv;
+                cp[k] = cprev;
+                dp[k] = dprev;
             }
-            y[m - 1] = dp[m - 1];
-            for (int k = m - 2; k >= 0; --k) y[k] = dp[k] - cp[k] * y[k + 1];
-            float nn = 0.0f;
-            for (int k = 0; k < m; ++k) nn += y[k] * y[k];
+            float yk = dprev;
+            y[m - 1] = yk;
+            float nn = yk * yk;
+            for (int k = m - 2; k >= 0; --k) {
+                yk = dp[k] - cp[k] * yk;
+                y[k] = yk;
+                nn += yk * yk;
+            }
             if (!(nn > 0.0f && nn < 3.0e38f)) {  // degenerate: fall back to a unit vector
                 for (int k = 0; k < m; ++k) y[k] = k == 0 ? 1.0f : 0.0f;
                 break;
@@ -223,56 +302,79 @@ __global__ void __launch_bounds__(kCovWaves * 64) cov_kernel(const char* K, char
     }
     wave_lds_fence();
 
-    // ---- xi_i = X^T (V y_i) / sqrt(c); sign: largest-magnitude coordinate positive
+    // ---- Ritz vectors over the rows: z_i[l] = sum_k v_k[l] y_i[k]
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        float zz = 0.0f;
+        if (i < m)
+            for (int k = 0; k < m; ++k) zz = fmaf(sm.lz.v[k][lane], sm.y[i][k], zz);
+        sm.z[i][lane] = lane < c ? zz : 0.0f;
+    }
+    wave_lds_fence();
+
+    // ---- xi_i = X^T z_i / sqrt(c), the centred keys read again from memory (the
+    // same fp32 values as in LDS before); sign: largest-magnitude coordinate positive
+    float xi[R][CPL];
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) xi[i][e] = 0.0f;
+    for (int l = 0; l < c; ++l) {
+        float f[CPL];
+        const char* row = kp + (size_t)l * RB + CPL * lane * EB;
+        if constexpr (DT == DT_F32) {
+            if constexpr (CPL == 2) {
+                const float2 v2 = *reinterpret_cast<const float2*>(row);
+                f[0] = v2.x;
+                f[1] = v2.y;
+            } else {
+                f[0] = *reinterpret_cast<const float*>(row);
+            }
+        } else {
+            if constexpr (CPL == 2) {
+                const uint32_t u = *reinterpret_cast<const uint32_t*>(row);
+                f[0] = __uint_as_float(u << 16);
+                f[1] = __uint_as_float(u & 0xffff0000u);
+            } else {
+                f[0] = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(row) << 16);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) f[e] -= meanf[e];
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const float zi = sm.z[i][l];
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) xi[i][e] = fmaf(f[e], zi, xi[i][e]);
+        }
+    }
     const float inv_sqrt_c = 1.0f / sqrtf((float)c);
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-        // Ritz vector component of this lane's row, through LDS for the X^T product
-        float z = 0.0f;
-        for (int k = 0; k < m; ++k) z = fmaf(sm.v[k][lane], sm.y[i][k], z);
-        if (i >= m) z = 0.0f;  // fewer Lanczos vectors than descriptors: nothing left
-        wave_lds_fence();
-        sm.v[kLanczos][lane] = z;
-        wave_lds_fence();
-        float xi[CPL];
-#pragma unroll
-        for (int u = 0; u < CPL; ++u) {
-            const int t = lane + 64 * u;
-            float s = 0.0f;
-            for (int l = 0; l < c; ++l) s = fmaf(sm.x[l][t], sm.v[kLanczos][l], s);
-            xi[u] = s * inv_sqrt_c;
-        }
-        // the first coordinate of largest magnitude decides the sign
         float best = -1.0f;
         int bt = 0;
 #pragma unroll
-        for (int u = 0; u < CPL; ++u) {
-            const float a = fabsf(xi[u]);
+        for (int e = 0; e < CPL; ++e) {
+            xi[i][e] *= inv_sqrt_c;
+            const float a = fabsf(xi[i][e]);
             if (a > best) {
                 best = a;
-                bt = lane + 64 * u;
+                bt = CPL * lane + e;
             }
         }
-        // wave-wide (magnitude, -index) maximum
+        // wave-wide (magnitude, -index) maximum: the first coordinate of largest magnitude
         uint32_t hkey = __float_as_uint(best), lkey = ~(uint32_t)bt;
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const uint32_t oh = __shfl_xor(hkey, off), ol = __shfl_xor(lkey, off);
-            if (oh > hkey || (oh == hkey && ol > lkey)) {
-                hkey = oh;
-                lkey = ol;
-            }
-        }
+        wave_key_max(hkey, lkey);
         const int at = (int)~lkey;
         float sgn_src = 0.0f;
 #pragma unroll
-        for (int u = 0; u < CPL; ++u)
-            if (lane + 64 * u == at) sgn_src = xi[u];
-        const float sgn = __shfl(sgn_src, at & 63) < 0.0f ? -1.0f : 1.0f;
+        for (int e = 0; e < CPL; ++e)
+            if (CPL * lane + e == at) sgn_src = xi[i][e];
+        const float sgn = __shfl(sgn_src, at / CPL) < 0.0f ? -1.0f : 1.0f;
 #pragma unroll
-        for (int u = 0; u < CPL; ++u) {
-            const int t = lane + 64 * u;
-            const float val = xi[u] * sgn;
+        for (int e = 0; e < CPL; ++e) {
+            const int t = CPL * lane + e;
+            const float val = xi[i][e] * sgn;
             if constexpr (DT == DT_F32) {
                 reinterpret_cast<float*>(out + (size_t)(1 + i) * RB)[t] = val;
             } else {
@@ -285,10 +387,9 @@ __global__ void __launch_bounds__(kCovWaves * 64) cov_kernel(const char* K, char
 template <int DT, int D>
 hipError_t launch_cov_dtd(const Dims& s, const void* K, void* Kcov, hipStream_t st)
 {
-    const long long total = (long long)s.pairs() * s.nb;
-    const long long wgs = (total + kCovWaves - 1) / kCovWaves;
-    cov_kernel<DT, D, kCobsRank><<<dim3((unsigned)wgs), dim3(kCovWaves * 64), 0, st>>>(
-        static_cast<const char*>(K), static_cast<char*>(Kcov), s.n, s.L, s.nb, total);
+    const long long total = (long long)s.pairs() * s.nb;  // one workgroup (one wave) per block
+    cov_kernel<DT, D, kCobsRank><<<dim3((unsigned)total), dim3(64), 0, st>>>(
+        static_cast<const char*>(K), static_cast<char*>(Kcov), s.n, s.L, s.nb);
     return hipGetLastError();
 }
 
