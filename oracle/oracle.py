@@ -21,7 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "csa_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "libcsa_oracle.so")
 
-SUMMARY, EXACT_MASS, BOX, COBS2, PROXY_ERROR = 0, 1, 2, 3, 4
+SUMMARY, EXACT_MASS, BOX, COBS2, PROXY_ERROR, COBS2_FP4 = 0, 1, 2, 3, 4, 5
 COBS_RANK = 4  # scaled eigenvectors per block in the second-order descriptor
 
 
@@ -292,11 +292,94 @@ def proxy_error_score(shape: Shape, q, Kvar):
     return _lse(rel.reshape(B, Hkv, G, nb), axis=2)
 
 
+# E2M1 (FP4) magnitudes by 3-bit code: exponent bits 2-1, mantissa bit 0.
+E2M1 = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def fp4_block_bytes(d: int, rank: int = COBS_RANK) -> int:
+    """Bytes per block of the FP4 second-order descriptor: the bfloat16 mean key, one fp32
+    scale per eigenvector, then the eigenvectors' 4-bit codes (two per byte)."""
+    return 2 * d + 4 * rank + rank * d // 2
+
+
+def e2m1_code(r: np.float32) -> int:
+    """4-bit E2M1 code of r (binary32) rounded to the nearest grid value, ties to the even
+    mantissa (code bit 0 clear); zero magnitudes are +0."""
+    a = abs(float(r))
+    best = 0
+    for c in range(1, 8):
+        d_new, d_old = abs(a - E2M1[c]), abs(a - E2M1[best])
+        if d_new < d_old or (d_new == d_old and c % 2 == 0 and best % 2 == 1):
+            best = c
+    return best | (8 if (float(r) < 0 and best) else 0)
+
+
+def cov4_pack(shape: Shape, Kcov):
+    """FP4 storage of the second-order descriptors ("COBS: Cumulant Order Block Sparse
+    Attention", section on quantising the stored factors: E2M1 codes, one fp32 scale per
+    eigenvector, the block mean in bfloat16), from the stored bfloat16 descriptors Kcov
+    [B, Hkv, nb, 1 + r, d].  Per block: the mean row (its bits), the scales
+    s_i = max_t |xi_it| / 6 (binary32), then for each eigenvector the codes of xi_it / s_i
+    (binary32 quotient) with coordinate 2t in the low and 2t + 1 in the high nibble of byte t.
+    Returns uint8 [B, Hkv, nb, fp4_block_bytes(d)]."""
+    assert shape.dtype == "bf16"
+    B, Hkv, nb, d, r = shape.batch, shape.n_kv_heads, shape.n_blocks, shape.head_dim, COBS_RANK
+    C = np.asarray(Kcov, np.uint16).reshape(B, Hkv, nb, 1 + r, d)
+    out = np.zeros((B, Hkv, nb, fp4_block_bytes(d)), np.uint8)
+    out[..., :2 * d] = C[:, :, :, 0].copy().view(np.uint8).reshape(B, Hkv, nb, 2 * d)
+    xi = widen("bf16", C[:, :, :, 1:]).astype(np.float32)  # exact
+    for b in range(B):
+        for j in range(Hkv):
+            for blk in range(nb):
+                for i in range(r):
+                    x = xi[b, j, blk, i]
+                    sc = np.float32(np.abs(x).max()) / np.float32(6.0)
+                    out[b, j, blk, 2 * d + 4 * i:2 * d + 4 * i + 4] = np.frombuffer(np.float32(sc).tobytes(), np.uint8)
+                    codes = [e2m1_code(np.float32(v) / sc) if sc > 0 else 0 for v in x]
+                    base = 2 * d + 4 * r + i * d // 2
+                    for t in range(d // 2):
+                        out[b, j, blk, base + t] = codes[2 * t] | (codes[2 * t + 1] << 4)
+    return out
+
+
+def cov4_unpack(shape: Shape, packed):
+    """Mean keys (fp64) [B, Hkv, nb, d] and decoded eigenvectors s_i x E2M1(code) (fp64)
+    [B, Hkv, nb, r, d] of FP4 descriptors."""
+    B, Hkv, nb, d, r = shape.batch, shape.n_kv_heads, shape.n_blocks, shape.head_dim, COBS_RANK
+    P = np.asarray(packed, np.uint8).reshape(B, Hkv, nb, fp4_block_bytes(d))
+    mean = widen("bf16", P[..., :2 * d].copy().view(np.uint16))
+    scales = P[..., 2 * d:2 * d + 4 * r].copy().view(np.float32).astype(np.float64)  # [B, Hkv, nb, r]
+    codes = P[..., 2 * d + 4 * r:].reshape(B, Hkv, nb, r, d // 2)
+    nib = np.stack([codes & 15, codes >> 4], axis=-1).reshape(B, Hkv, nb, r, d)
+    mag = np.asarray(E2M1)[nib & 7]
+    val = np.where(nib & 8, -mag, mag)
+    return mean, scales[..., None] * val
+
+
+def cobs2_fp4_logits(shape: Shape, q, packed):
+    """Second-order block logits [B, Hq, nb] from FP4 descriptors: the formula of
+    cobs2_logits with the decoded eigenvectors."""
+    B, Hq, Hkv, d, nb = shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.n_blocks
+    G = Hq // Hkv
+    qf = widen(shape, _stored(shape, q, (B, Hq, d)))
+    mean, xi = cov4_unpack(shape, packed)
+    scale = shape.scale if shape.scale else 1.0 / math.sqrt(d)
+    counts = np.array([min(shape.block_size, shape.n_tokens - i * shape.block_size) for i in range(nb)], np.float64)
+    out = np.empty((B, Hq, nb), np.float64)
+    for h in range(Hq):
+        m1 = np.einsum("bd,bkd->bk", qf[:, h], mean[:, h // G])
+        m2 = np.einsum("bd,bkrd->bkr", qf[:, h], xi[:, h // G])
+        out[:, h] = scale * m1 + np.log(counts) + 0.5 * scale * scale * (m2 ** 2).sum(-1)
+    return out
+
+
 def block_logits(shape: Shape, mode: int, q, keys):
     """Per-query-head block logits [B, Hq, nb]: first-order summary score, exact ln m_b, or the
     largest logit over the block's key box."""
     if mode == COBS2:
         return cobs2_logits(shape, q, keys)
+    if mode == COBS2_FP4:
+        return cobs2_fp4_logits(shape, q, keys)
     rows = {SUMMARY: shape.n_blocks, EXACT_MASS: shape.n_tokens, BOX: 2 * shape.n_blocks}[mode]
     q = _stored(shape, q, (shape.batch, shape.n_q_heads, shape.head_dim))
     if mode == BOX:  # [B, Hkv, nb, 2, d] is [B, Hkv, 2 nb, d] in memory

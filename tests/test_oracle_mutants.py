@@ -105,6 +105,11 @@ PY_MUTANTS = {
     "variance about zero instead of the block mean": ("dv = X[:, :, i] - mean", "dv = X[:, :, i]"),
     "variance with the sample divisor": ("var[:, :, blk] = s2 / c", "var[:, :, blk] = s2 / max(c - 1, 1)"),
     "spread without the logit scale": ("spread2 = scale * scale * np.einsum", "spread2 = np.einsum"),
+    "FP4 ties to the odd mantissa": ("c % 2 == 0 and best % 2 == 1", "c % 2 == 1 and best % 2 == 0"),
+    "FP4 scale for a largest code of 4": ("/ np.float32(6.0)", "/ np.float32(4.0)"),
+    "FP4 nibbles swapped": ("codes[2 * t] | (codes[2 * t + 1] << 4)", "codes[2 * t + 1] | (codes[2 * t] << 4)"),
+    "FP4 sign dropped": ("return best | (8 if (float(r) < 0 and best) else 0)", "return best"),
+    "FP4 decoded without the scale": ("return mean, scales[..., None] * val", "return mean, val"),
 }
 PY_BATTERY = [
     P.test_cov_descriptor_is_the_top_eigen_truncation,
@@ -115,6 +120,10 @@ PY_BATTERY = [
     P.test_spread_is_the_std_of_the_block_logits_and_error_is_mass_times_spread,
     P.test_scaling_every_spread_shifts_every_score_by_its_log,
     P.test_exact_proxies_carry_no_error,
+    P.test_e2m1_rounding_matches_its_binade_definition,
+    P.test_fp4_pack_layout_by_hand,
+    P.test_fp4_decode_error_is_within_half_a_grid_step,
+    P.test_fp4_score_equals_bf16_score_on_grid_exact_descriptors,
 ]
 
 

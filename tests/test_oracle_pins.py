@@ -755,3 +755,102 @@ def test_exact_proxies_carry_no_error():
     assert 2 not in sel[0]
     shp1 = O.Shape(1, 2, 1, d, n, 1, "f32")
     assert np.all(O.block_score(shp1, O.PROXY_ERROR, q, O.var_build(shp1, K)) == -np.inf)
+
+
+# ---------------------------------------------------------------------------
+# FP4 (E2M1) storage of the second-order descriptors ("COBS: Cumulant Order Block
+# Sparse Attention", section on quantising the stored eigenvectors)
+# ---------------------------------------------------------------------------
+
+def _e2m1_by_binade(r):
+    """E2M1 rounding by its binades: below 1 the spacing is 0.5 (0, 0.5, 1), in [1, 2) 0.5,
+    in [2, 4) 1, from 4 on 2 (4, 6); half-way cases to the even mantissa; largest value 6."""
+    a = abs(r)
+    if a >= 4.0:
+        m = 4.0 if a <= 5.0 else 6.0  # 5 ties to 4 (even), beyond 5 to 6
+    else:
+        step = 0.5 if a < 2.0 else 1.0
+        m = round(a / step) * step  # Python rounds half to even: the even multiple is the even mantissa
+    return -m if (r < 0 and m > 0) else m
+
+
+def test_e2m1_rounding_matches_its_binade_definition():
+    grid = O.E2M1
+    vals = [0.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 5.9, 6.0, 0.2, 0.3, 0.74, 0.76, 1.1, 2.4, 2.6, 3.6, 4.9]
+    rng = np.random.default_rng(50)
+    vals += list(rng.uniform(-6, 6, 400)) + [-v for v in vals]
+    for v in vals:
+        c = O.e2m1_code(np.float32(v))
+        got = (-1 if c & 8 else 1) * grid[c & 7]
+        assert got == _e2m1_by_binade(float(np.float32(v))), (v, c)
+    # ties go to the even mantissa: 0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4
+    assert [grid[O.e2m1_code(np.float32(v))] for v in (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)] == \
+        [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0]
+
+
+def test_fp4_descriptor_size_is_the_pages_figure():
+    """Rank 4 at d = 128: the covariance factor shrinks from 1024 bytes (bfloat16) to 272 bytes
+    per block (FP4 codes and four fp32 scales), the bfloat16 mean not counted."""
+    assert 4 * 128 * 2 == 1024
+    assert O.fp4_block_bytes(128) - 2 * 128 == 272
+
+
+def test_fp4_pack_layout_by_hand():
+    """One block, d = 64: xi_1 = 2^-3 x [6, -0.5, 1.5, 0, 0, ...], the others zero.  Scale
+    2^-3 (binary32 0x3E000000), codes 7, 9 (sign + 0.5), 3, 0 -> bytes 0x97, 0x03; zero
+    eigenvectors get scale 0 and zero codes; the mean row is copied bit for bit."""
+    d = 64
+    shp = O.Shape(1, 1, 1, d, 4, 4, "bf16")
+    xi = np.zeros((1 + O.COBS_RANK, d))
+    xi[1, :3] = np.array([6.0, -0.5, 1.5]) / 8
+    xi[0, :4] = [1.0, -2.0, 0.5, 3.0]
+    Kcov = O.store_array("bf16", xi).reshape(1, 1, 1, 1 + O.COBS_RANK, d)
+    P = O.cov4_pack(shp, Kcov)[0, 0, 0]
+    assert P.shape == (O.fp4_block_bytes(d),)
+    assert np.array_equal(P[:2 * d].view(np.uint16), Kcov[0, 0, 0, 0])
+    assert list(P[2 * d:2 * d + 4]) == [0x00, 0x00, 0x00, 0x3E]
+    assert not P[2 * d + 4:2 * d + 16].any()
+    codes = P[2 * d + 16:]
+    assert codes[0] == 0x97 and codes[1] == 0x03 and not codes[2:].any()
+
+
+def test_fp4_decode_error_is_within_half_a_grid_step():
+    """Every decoded coordinate lies within half the grid spacing at its magnitude (0.25 s
+    below 2 s, 0.5 s below 4 s, s above), and each eigenvector's largest coordinate is exact."""
+    n, L, d = 512, 64, 64
+    shp = O.Shape(1, 2, 1, d, n, L, "bf16")
+    _, K, _ = rand_case(51, 1, 2, 1, d, n, "bf16")
+    Kcov = O.cov_build(shp, K)
+    P = O.cov4_pack(shp, Kcov)
+    _, xi_hat = O.cov4_unpack(shp, P)
+    xi = O.widen("bf16", Kcov[:, :, :, 1:])
+    s = np.abs(xi).max(axis=-1, keepdims=True) / 6
+    err = np.abs(xi - xi_hat)
+    a = np.abs(xi) / np.where(s > 0, s, 1)
+    half = np.where(a < 2, 0.25, np.where(a < 4, 0.5, 1.0)) * s
+    assert np.all(err <= half * (1 + 1e-6) + 1e-30)
+    top = np.argmax(np.abs(xi), axis=-1)
+    assert np.allclose(np.take_along_axis(np.abs(xi_hat), top[..., None], -1), 6 * s, rtol=1e-6)
+
+
+def test_fp4_score_equals_bf16_score_on_grid_exact_descriptors():
+    """Descriptors whose eigenvectors are already scale x E2M1 values (scale 2^-3, each row's
+    first coordinate 6 x scale) survive FP4 storage unchanged, so the FP4 and bfloat16
+    second-order scores agree exactly."""
+    d, n, L = 64, 256, 32
+    shp = O.Shape(1, 4, 2, d, n, L, "bf16")
+    rng = np.random.default_rng(52)
+    nb = shp.n_blocks
+    xi = np.zeros((1, 2, nb, 1 + O.COBS_RANK, d))
+    xi[..., 0, :] = rng.standard_normal((1, 2, nb, d))
+    codes = rng.integers(0, 8, (1, 2, nb, O.COBS_RANK, d))
+    signs = np.where(rng.random(codes.shape) < 0.5, -1.0, 1.0)
+    xi[..., 1:, :] = signs * np.asarray(O.E2M1)[codes] / 8
+    xi[..., 1:, 0] = 6.0 / 8
+    Kcov = O.store_array("bf16", xi)
+    assert np.array_equal(O.widen("bf16", Kcov[..., 1:, :]), xi[..., 1:, :])  # bfloat16-exact
+    q, _, _ = rand_case(53, 1, 4, 2, d, n, "bf16")
+    P = O.cov4_pack(shp, Kcov)
+    _, xi_hat = O.cov4_unpack(shp, P)
+    assert np.array_equal(xi_hat, xi[..., 1:, :])
+    assert np.abs(O.cobs2_fp4_logits(shp, q, P) - O.cobs2_logits(shp, q, Kcov)).max() < 1e-12
