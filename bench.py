@@ -162,9 +162,10 @@ def step_bytes(w, m=0):
     blocks and the exact key/value rows of the kept blocks.  Exact-mass scores: every key
     once, the values of the kept blocks, both mean rows of the unread blocks.  Box scores:
     both box rows of every block, both mean rows of the unread blocks, the exact rows.
-    Proxy-error scores: the mean and variance rows of every block, then both mean rows of
-    the unread blocks (the mean keys are read a second time by the attention), the exact
-    rows.  Second-order scores: the mean and four eigenvector rows of every block.  Plus
+    Proxy-error and second-order scores: the descriptor of every block (mean and variance
+    rows; mean and four eigenvector rows, bfloat16 or FP4 with scales), whose mean row
+    also gives the proxy logits, then the mean values of the unread blocks and the exact
+    rows (the three-call route reads the mean keys a second time: not counted).  Plus
     weighted-token rows, the queries, and the outputs with their log-normalisers."""
     e = w.elem_bytes
     d, L, k, nb, G = w.head_dim, w.block_size, w.k, w.n_blocks, w.group
@@ -175,8 +176,10 @@ def step_bytes(w, m=0):
         per_read = w.n_tokens * d * e + k * L * d * e + unread * 2 * d * e
     elif w.score_mode == "box":
         per_read = 2 * nb * d * e + unread * 2 * d * e + k * L * 2 * d * e
-    elif w.score_mode == "proxy_error":  # mean and variance tokens of every block, then as box
-        per_read = 2 * nb * d * e + unread * 2 * d * e + k * L * 2 * d * e
+    elif w.score_mode == "proxy_error":  # mean and variance tokens of every block
+        per_read = 2 * nb * d * e + unread * d * e + k * L * 2 * d * e
+    elif w.score_mode == "cobs2_fp4":  # mean key, four fp32 scales and FP4 codes of every block
+        per_read = nb * (2 * d + 16 + 4 * d // 2) + unread * d * e + k * L * 2 * d * e
     else:  # second-order: the mean key and four eigenvector rows of every block
         per_read = 5 * nb * d * e + unread * d * e + k * L * 2 * d * e
     per_read += m * (2 * d * e + 8) + G * d * e
@@ -235,11 +238,12 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     summary_ms = e0.elapsed_time(e1)
-    box = w.score_mode in ("box", "cobs2", "proxy_error")  # scored from extra per-block summaries
+    box = w.score_mode in ("box", "cobs2", "proxy_error", "cobs2_fp4")  # scored from extra per-block summaries
     Kbox0 = None
     extra_ms = None
     if box:
-        build = {"box": csa.kv_box_build, "cobs2": csa.kv_cov_build, "proxy_error": csa.kv_var_build}[w.score_mode]
+        build = {"box": csa.kv_box_build, "cobs2": csa.kv_cov_build, "proxy_error": csa.kv_var_build,
+                 "cobs2_fp4": csa.kv_cov4_build}[w.score_mode]
         Kbox0 = build(K0, w.block_size)
         torch.cuda.synchronize()
         e0.record()
@@ -260,7 +264,8 @@ def main():
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
     mode_entry = {"summary": csa.CSA_WS_BLOCK_SCORE_SUMMARY, "exact_mass": csa.CSA_WS_BLOCK_SCORE_EXACT_MASS,
                   "box": csa.CSA_WS_BLOCK_SCORE_BOX, "cobs2": csa.CSA_WS_BLOCK_SCORE_COBS2,
-                  "proxy_error": csa.CSA_WS_BLOCK_SCORE_PROXY_ERROR}[w.score_mode]
+                  "proxy_error": csa.CSA_WS_BLOCK_SCORE_PROXY_ERROR,
+                  "cobs2_fp4": csa.CSA_WS_BLOCK_SCORE_COBS2_FP4}[w.score_mode]
     ws_score = torch.empty(max(1, csa.workspace_size(shape, mode_entry)), dtype=torch.uint8, device=dev)
     ws_attn = torch.empty(max(1, csa.workspace_size(shape, csa.CSA_WS_SPARSE_DECODE_ATTN, w.k, m)),
                           dtype=torch.uint8, device=dev)
@@ -269,7 +274,7 @@ def main():
 
     def score_select(layer):
         K, V, Kbar, Vbar, Kbox = layer
-        keys = {"summary": Kbar, "exact_mass": K, "box": Kbox, "cobs2": Kbox, "proxy_error": Kbox}[w.score_mode]
+        keys = Kbar if w.score_mode == "summary" else K if w.score_mode == "exact_mass" else Kbox
         csa.block_score(q, keys, w.score_mode, w.block_size, n_tokens=w.n_tokens, scores=scores, ws=ws_score)
         csa.topk_select(scores, w.k, sel=sel)
 
@@ -387,7 +392,7 @@ def main():
         "modular_breakdown_us": {"block_score+topk_select": score_ms * 1e3 if score_ms else None,
                                  "sparse_decode_attn": attn_ms * 1e3},
         "kv_summary_build_ms": summary_ms,
-        **({f"kv_{ {'box': 'box', 'cobs2': 'cov', 'proxy_error': 'var'}[w.score_mode]}_build_ms": extra_ms}
+        **({f"kv_{ {'box': 'box', 'cobs2': 'cov', 'proxy_error': 'var', 'cobs2_fp4': 'cov4'}[w.score_mode]}_build_ms": extra_ms}
            if extra_ms is not None else {}),
         "dense_decode_attn_ms": dense_ms,
         "step_vs_dense_speedup": (dense_ms / t_step) if dense_ms else None,

@@ -17,18 +17,26 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so"
 CSA_OK, CSA_ERR_INVALID_ARG, CSA_ERR_UNSUPPORTED, CSA_ERR_WORKSPACE, CSA_ERR_HIP = 0, -1, -2, -3, -4
 CSA_F32, CSA_BF16 = 0, 1
 CSA_SCORE_SUMMARY, CSA_SCORE_EXACT_MASS, CSA_SCORE_BOX, CSA_SCORE_COBS2, CSA_SCORE_PROXY_ERROR = 0, 1, 2, 3, 4
+CSA_SCORE_COBS2_FP4 = 5
 CSA_COBS_RANK = 4
 CSA_PROXY_NONE, CSA_PROXY_COMPLEMENT = 0, 1
 CSA_WS_BLOCK_SCORE_SUMMARY, CSA_WS_BLOCK_SCORE_EXACT_MASS = 0, 1
 CSA_WS_SPARSE_DECODE_ATTN, CSA_WS_DENSE_DECODE_ATTN, CSA_WS_SELECTIVE_DECODE_STEP = 2, 3, 4
 CSA_WS_BLOCK_SCORE_BOX, CSA_WS_BLOCK_SCORE_COBS2, CSA_WS_BLOCK_SCORE_PROXY_ERROR = 5, 6, 7
+CSA_WS_BLOCK_SCORE_COBS2_FP4 = 8
 
 MODES = {"summary": CSA_SCORE_SUMMARY, "exact_mass": CSA_SCORE_EXACT_MASS, "box": CSA_SCORE_BOX,
-         "cobs2": CSA_SCORE_COBS2, "proxy_error": CSA_SCORE_PROXY_ERROR}
+         "cobs2": CSA_SCORE_COBS2, "proxy_error": CSA_SCORE_PROXY_ERROR, "cobs2_fp4": CSA_SCORE_COBS2_FP4}
 _SCORE_WS = {"summary": CSA_WS_BLOCK_SCORE_SUMMARY, "exact_mass": CSA_WS_BLOCK_SCORE_EXACT_MASS,
              "box": CSA_WS_BLOCK_SCORE_BOX, "cobs2": CSA_WS_BLOCK_SCORE_COBS2,
-             "proxy_error": CSA_WS_BLOCK_SCORE_PROXY_ERROR}
-_SUMMARY_ROWS = {"summary": None, "box": 2, "cobs2": 1 + CSA_COBS_RANK, "proxy_error": 2}  # rows per block
+             "proxy_error": CSA_WS_BLOCK_SCORE_PROXY_ERROR, "cobs2_fp4": CSA_WS_BLOCK_SCORE_COBS2_FP4}
+_SUMMARY_ROWS = {"summary": None, "box": 2, "cobs2": 1 + CSA_COBS_RANK, "proxy_error": 2,
+                 "cobs2_fp4": 0}  # rows per block (0: packed bytes)
+
+
+def cov4_block_bytes(d: int) -> int:
+    """Bytes per block of the FP4 second-order descriptor (CSA_COV4_BLOCK_BYTES)."""
+    return 2 * d + 4 * CSA_COBS_RANK + CSA_COBS_RANK * d // 2
 
 
 class CsaError(RuntimeError):
@@ -62,6 +70,7 @@ _SIGS = {
     "kv_box_build": [ctypes.POINTER(Shape), _P, _P, _P],
     "kv_cov_build": [ctypes.POINTER(Shape), _P, _P, _P],
     "kv_var_build": [ctypes.POINTER(Shape), _P, _P, _P],
+    "kv_cov4_build": [ctypes.POINTER(Shape), _P, _P, _P],
     "block_score": [ctypes.POINTER(Shape), ctypes.c_int, _P, _P, _P, _P, _SZ, _P],
     "topk_select": [_I32, _I32, _I32, _P, _P, _P],
     "sparse_decode_attn": [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _I32, _P, _P, _I32, ctypes.c_int,
@@ -188,6 +197,18 @@ def kv_cov_build(K: torch.Tensor, block_size: int, Kcov=None):
     return Kcov
 
 
+def kv_cov4_build(K: torch.Tensor, block_size: int, Kcov4=None):
+    """Second-order descriptors with FP4 (E2M1) eigenvectors: Kcov4 uint8
+    [B, Hkv, nb, cov4_block_bytes(d)] (bfloat16 mean key, fp32 scales, 4-bit codes)."""
+    dev = _dev(K, Kcov4)
+    B, Hkv, n, d = K.shape
+    shape = Shape(B, Hkv, Hkv, d, n, block_size, _dtype_code(K), 0.0)
+    if Kcov4 is None:
+        Kcov4 = torch.empty((B, Hkv, shape.n_blocks, cov4_block_bytes(d)), dtype=torch.uint8, device=dev)
+    _check(lib().kv_cov4_build(ctypes.byref(shape), _ptr(K), _ptr(Kcov4), _stream(dev)), "kv_cov4_build")
+    return Kcov4
+
+
 def kv_var_build(K: torch.Tensor, block_size: int, Kvar=None):
     """Mean and variance tokens of every block: Kvar [B, Hkv, nb, 2, d] (row 0 the mean key,
     row 1 the per-coordinate key variance), for the proxy-error scores."""
@@ -218,7 +239,10 @@ def block_score(q: torch.Tensor, keys: torch.Tensor, mode: str, block_size: int,
     if mode in _SUMMARY_ROWS and keys.shape[2] != nb:
         raise ValueError(f"the summaries have {keys.shape[2]} blocks, expected {nb}")
     rows = _SUMMARY_ROWS.get(mode)
-    if rows is not None and (keys.dim() != 5 or keys.shape[3] != rows):
+    if rows == 0:
+        if keys.dim() != 4 or keys.dtype != torch.uint8 or keys.shape[3] != cov4_block_bytes(d):
+            raise ValueError(f"{mode} mode needs keys uint8 [B, Hkv, nb, {cov4_block_bytes(d)}]")
+    elif rows is not None and (keys.dim() != 5 or keys.shape[3] != rows):
         raise ValueError(f"{mode} mode needs keys [B, Hkv, nb, {rows}, d]")
     scores = torch.empty((B, Hkv, nb), dtype=torch.float32, device=dev) if scores is None else scores
     ws, wsb = _workspace(shape, _SCORE_WS[mode], 0, 0, ws, dev)

@@ -155,6 +155,20 @@ int kv_cov_build(const csa_shape* shape, const void* K, void* Kcov, hipStream_t 
     return e == hipSuccess ? CSA_OK : hip_fail(e, "kv_cov_build");
 }
 
+int kv_cov4_build(const csa_shape* shape, const void* K, void* Kcov4, hipStream_t stream)
+{
+    csa::Dims d;
+    if (int rc = make_dims(shape, &d)) return rc;
+    if (!K || !Kcov4) return fail(CSA_ERR_INVALID_ARG, "kv_cov4_build: NULL tensor pointer");
+    if (!aligned16(K) || !aligned16(Kcov4))
+        return fail(CSA_ERR_INVALID_ARG, "kv_cov4_build: tensors must be 16-byte aligned");
+    if (d.dtype != csa::DT_BF16) return fail(CSA_ERR_UNSUPPORTED, "kv_cov4_build: FP4 descriptors need a bfloat16 cache");
+    if (!csa::cov_build_ok(d))
+        return fail(CSA_ERR_UNSUPPORTED, "kv_cov4_build: blocks of %d tokens (at most 64 supported)", d.L);
+    const hipError_t e = csa::launch_cov4(d, K, Kcov4, stream);
+    return e == hipSuccess ? CSA_OK : hip_fail(e, "kv_cov4_build");
+}
+
 int kv_var_build(const csa_shape* shape, const void* K, void* Kvar, hipStream_t stream)
 {
     csa::Dims d;
@@ -171,9 +185,9 @@ int block_score(const csa_shape* shape, csa_score_mode mode, const void* q, cons
     csa::Dims d;
     if (int rc = make_dims(shape, &d)) return rc;
     if (mode != CSA_SCORE_SUMMARY && mode != CSA_SCORE_EXACT_MASS && mode != CSA_SCORE_BOX && mode != CSA_SCORE_COBS2 &&
-        mode != CSA_SCORE_PROXY_ERROR)
+        mode != CSA_SCORE_PROXY_ERROR && mode != CSA_SCORE_COBS2_FP4)
         return fail(CSA_ERR_INVALID_ARG, "block_score: unknown mode %d", (int)mode);
-    if (mode == CSA_SCORE_COBS2 && !csa::fused_summary_score_ok(d))
+    if ((mode == CSA_SCORE_COBS2 || mode == CSA_SCORE_COBS2_FP4) && !csa::fused_summary_score_ok(d))
         return fail(CSA_ERR_UNSUPPORTED, "block_score: second-order scores need bfloat16, G <= 8 and G nb <= 16384");
     if (mode == CSA_SCORE_PROXY_ERROR && !csa::fused_summary_score_ok(d))
         return fail(CSA_ERR_UNSUPPORTED, "block_score: proxy-error scores need bfloat16, G <= 8 and G nb <= 16384");
@@ -189,9 +203,9 @@ int block_score(const csa_shape* shape, csa_score_mode mode, const void* q, cons
         return e == hipSuccess ? CSA_OK : hip_fail(e, "block_score");
     }
     if (int rc = check_ws(block_score_ws(d), ws, ws_bytes)) return rc;
-    if (mode == CSA_SCORE_COBS2) {
-        const hipError_t e =
-            csa::launch_score_cobs2(d, q, keys, d.G == 1 ? scores : static_cast<float*>(ws), scores, stream);
+    if (mode == CSA_SCORE_COBS2 || mode == CSA_SCORE_COBS2_FP4) {
+        const hipError_t e = csa::launch_score_cobs2(d, q, keys, d.G == 1 ? scores : static_cast<float*>(ws), scores,
+                                                     stream, mode == CSA_SCORE_COBS2_FP4);
         return e == hipSuccess ? CSA_OK : hip_fail(e, "block_score");
     }
     if ((mode == CSA_SCORE_SUMMARY || mode == CSA_SCORE_BOX) && csa::fused_summary_score_ok(d)) {
@@ -282,7 +296,8 @@ int selective_decode_step(const csa_shape* shape, csa_score_mode mode, const voi
 {
     csa::Dims d;
     if (int rc = make_dims(shape, &d)) return rc;
-    if (mode == CSA_SCORE_BOX || mode == CSA_SCORE_COBS2 || mode == CSA_SCORE_PROXY_ERROR)
+    if (mode == CSA_SCORE_BOX || mode == CSA_SCORE_COBS2 || mode == CSA_SCORE_PROXY_ERROR ||
+        mode == CSA_SCORE_COBS2_FP4)
         return fail(CSA_ERR_UNSUPPORTED, "selective_decode_step: box, second-order and proxy-error scores need "
                                          "Kbox, Kcov or Kvar; call block_score, topk_select and sparse_decode_attn");
     if (mode != CSA_SCORE_SUMMARY && mode != CSA_SCORE_EXACT_MASS)
@@ -349,7 +364,8 @@ size_t csa_workspace_size(const csa_shape* shape, csa_entry entry, int32_t k, in
     case CSA_WS_BLOCK_SCORE_SUMMARY:
     case CSA_WS_BLOCK_SCORE_EXACT_MASS:
     case CSA_WS_BLOCK_SCORE_BOX:
-    case CSA_WS_BLOCK_SCORE_COBS2: return block_score_ws(d);
+    case CSA_WS_BLOCK_SCORE_COBS2:
+    case CSA_WS_BLOCK_SCORE_COBS2_FP4: return block_score_ws(d);
     case CSA_WS_BLOCK_SCORE_PROXY_ERROR: return error_score_ws(d);
     case CSA_WS_SPARSE_DECODE_ATTN: {
         if (k < 0 || k > d.nb || m < 0) {

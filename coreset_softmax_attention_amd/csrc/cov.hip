@@ -53,7 +53,21 @@ struct CovSmem {
     float z[4][kCovMaxRows];                 // Ritz vectors over the block's rows
 };
 
-template <int DT, int D, int R>
+// E2M1 code of r: nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6 by magnitude, ties to the
+// even mantissa (code bit 0 clear); a zero magnitude is +0.
+__device__ __forceinline__ uint32_t e2m1_code(float r)
+{
+    const float a = fabsf(r);
+    const uint32_t c = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+                     : a <= 2.5f  ? 4u : a < 3.5f  ? 5u : a <= 5.0f  ? 6u : 7u;
+    return c | ((r < 0.0f && c != 0u) ? 8u : 0u);
+}
+
+// FP4: the descriptor is stored as [mean: d bfloat16][R fp32 scales][R x d/2 bytes of
+// E2M1 codes] per block (bfloat16 caches): each eigenvector, rounded to bfloat16 as
+// in the plain descriptor, is divided by its scale max_t |xi_t| / 6 and rounded to
+// E2M1; byte t of a row holds coordinates 2t (low nibble) and 2t + 1 (high nibble).
+template <int DT, int D, int R, bool FP4>
 __global__ void __launch_bounds__(64) cov_kernel(const char* K, char* Kcov, int n, int L, int nb)
 {
     constexpr int EB = Elem<DT>::bytes;
@@ -67,7 +81,9 @@ __global__ void __launch_bounds__(64) cov_kernel(const char* K, char* Kcov, int 
     const int blk = (int)(gblk - pair * nb);
     const int t0 = blk * L, c = min(L, n - t0);
     const char* kp = K + ((size_t)pair * n + t0) * RB;
-    char* out = Kcov + ((size_t)pair * nb + blk) * (1 + R) * RB;
+    static_assert(!FP4 || (DT == DT_BF16 && (D == 128 || D == 64)), "FP4 descriptors are for bfloat16 caches");
+    constexpr int BB = FP4 ? 2 * D + 4 * R + R * D / 2 : (1 + R) * RB;  // bytes per block
+    char* out = Kcov + ((size_t)pair * nb + blk) * BB;
 
     // ---- keys -> LDS (row per lane), mean of this lane's columns (fp64, token
     // order, one rounding: the bits of the summary)
@@ -371,24 +387,47 @@ __global__ void __launch_bounds__(64) cov_kernel(const char* K, char* Kcov, int 
         for (int e = 0; e < CPL; ++e)
             if (CPL * lane + e == at) sgn_src = xi[i][e];
         const float sgn = __shfl(sgn_src, at / CPL) < 0.0f ? -1.0f : 1.0f;
+        if constexpr (FP4) {
+            float vb[CPL];  // the bfloat16-rounded coordinates, widened exactly
+            float amax = 0.0f;
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) {
-            const int t = CPL * lane + e;
-            const float val = xi[i][e] * sgn;
-            if constexpr (DT == DT_F32) {
-                reinterpret_cast<float*>(out + (size_t)(1 + i) * RB)[t] = val;
+            for (int e = 0; e < CPL; ++e) {
+                vb[e] = __uint_as_float((uint32_t)bf16_from_f64((double)(xi[i][e] * sgn)) << 16);
+                amax = fmaxf(amax, fabsf(vb[e]));
+            }
+            amax = __uint_as_float(wave_max_u32(__float_as_uint(amax)));  // non-negative: bits order as values
+            const float sc = amax / 6.0f;
+            if (lane == 0) *reinterpret_cast<float*>(out + 2 * D + 4 * i) = sc;
+            uint32_t code[CPL];
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) code[e] = sc > 0.0f ? e2m1_code(vb[e] / sc) : 0u;
+            uint8_t* row = reinterpret_cast<uint8_t*>(out + 2 * D + 4 * R + i * (D / 2));
+            if constexpr (CPL == 2) {
+                row[lane] = (uint8_t)(code[0] | (code[1] << 4));
             } else {
-                reinterpret_cast<uint16_t*>(out + (size_t)(1 + i) * RB)[t] = bf16_from_f64((double)val);
+                const uint32_t hi = (uint32_t)__shfl_xor((int)code[0], 1);
+                if ((lane & 1) == 0) row[lane >> 1] = (uint8_t)(code[0] | (hi << 4));
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) {
+                const int t = CPL * lane + e;
+                const float val = xi[i][e] * sgn;
+                if constexpr (DT == DT_F32) {
+                    reinterpret_cast<float*>(out + (size_t)(1 + i) * RB)[t] = val;
+                } else {
+                    reinterpret_cast<uint16_t*>(out + (size_t)(1 + i) * RB)[t] = bf16_from_f64((double)val);
+                }
             }
         }
     }
 }
 
-template <int DT, int D>
+template <int DT, int D, bool FP4>
 hipError_t launch_cov_dtd(const Dims& s, const void* K, void* Kcov, hipStream_t st)
 {
     const long long total = (long long)s.pairs() * s.nb;  // one workgroup (one wave) per block
-    cov_kernel<DT, D, kCobsRank><<<dim3((unsigned)total), dim3(64), 0, st>>>(
+    cov_kernel<DT, D, kCobsRank, FP4><<<dim3((unsigned)total), dim3(64), 0, st>>>(
         static_cast<const char*>(K), static_cast<char*>(Kcov), s.n, s.L, s.nb);
     return hipGetLastError();
 }
@@ -403,12 +442,20 @@ bool cov_build_ok(const Dims& s)
 hipError_t launch_cov(const Dims& s, const void* K, void* Kcov, hipStream_t st)
 {
     if (s.dtype == DT_BF16) {
-        if (s.d == 128) return launch_cov_dtd<DT_BF16, 128>(s, K, Kcov, st);
-        if (s.d == 64) return launch_cov_dtd<DT_BF16, 64>(s, K, Kcov, st);
+        if (s.d == 128) return launch_cov_dtd<DT_BF16, 128, false>(s, K, Kcov, st);
+        if (s.d == 64) return launch_cov_dtd<DT_BF16, 64, false>(s, K, Kcov, st);
     } else {
-        if (s.d == 128) return launch_cov_dtd<DT_F32, 128>(s, K, Kcov, st);
-        if (s.d == 64) return launch_cov_dtd<DT_F32, 64>(s, K, Kcov, st);
+        if (s.d == 128) return launch_cov_dtd<DT_F32, 128, false>(s, K, Kcov, st);
+        if (s.d == 64) return launch_cov_dtd<DT_F32, 64, false>(s, K, Kcov, st);
     }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_cov4(const Dims& s, const void* K, void* Kcov4, hipStream_t st)
+{
+    if (s.dtype != DT_BF16) return hipErrorInvalidValue;
+    if (s.d == 128) return launch_cov_dtd<DT_BF16, 128, true>(s, K, Kcov4, st);
+    if (s.d == 64) return launch_cov_dtd<DT_BF16, 64, true>(s, K, Kcov4, st);
     return hipErrorInvalidValue;
 }
 

@@ -188,6 +188,11 @@ __device__ __forceinline__ uint4 buffer_ld16(__amdgpu_buffer_rsrc_t r, uint32_t 
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+__device__ __forceinline__ uint32_t buffer_ld4(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+
 // Ordering point for LDS data passed between lanes of one wave (a wave
 // executes its LDS instructions in order; this keeps the compiler from
 // moving loads and stores across it).

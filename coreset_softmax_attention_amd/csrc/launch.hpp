@@ -37,11 +37,14 @@ hipError_t launch_box(const Dims& s, const void* K, void* Kbox, hipStream_t st);
 constexpr int kCobsRank = 4;
 bool cov_build_ok(const Dims& s);  // blocks of at most 64 tokens
 hipError_t launch_cov(const Dims& s, const void* K, void* Kcov, hipStream_t st);
-// Second-order block scores from Kcov (bfloat16, fused_summary_score_ok()); with
-// fewer than kFusedStepMinPairs KV heads the logits go through `logits`
-// ([B, Hq, nb], or the scores themselves when G == 1).
+// The same with FP4 eigenvectors (bfloat16 caches): per block the mean key,
+// kCobsRank fp32 scales and kCobsRank x d/2 bytes of E2M1 codes.
+hipError_t launch_cov4(const Dims& s, const void* K, void* Kcov4, hipStream_t st);
+// Second-order block scores from Kcov, or from Kcov4 when fp4 (bfloat16,
+// fused_summary_score_ok()); with fewer than kFusedStepMinPairs KV heads the
+// logits go through `logits` ([B, Hq, nb], or the scores themselves when G == 1).
 hipError_t launch_score_cobs2(const Dims& s, const void* q, const void* Kcov, float* logits, float* scores,
-                              hipStream_t st);
+                              hipStream_t st, bool fp4 = false);
 // Mean and variance tokens Kvar [B, Hkv, nb, 2, d] of the proxy-error scores.
 hipError_t launch_var(const Dims& s, const void* K, void* Kvar, hipStream_t st);
 // Proxy-error block scores from Kvar (bfloat16, fused_summary_score_ok()); with

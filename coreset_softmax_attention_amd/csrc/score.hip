@@ -606,28 +606,153 @@ __device__ __forceinline__ void cobs2_tile_logits(const FusedScoreParams& p, __a
     wave_lds_fence();  // tmp is reused by the next tile
 }
 
+// FP4 descriptors, per block [mean: d bfloat16][4 fp32 scales][4 x d/2 bytes of E2M1
+// codes] (kv_cov4_build).  The same tile as cobs2_tile_logits: the mean rows
+// against q, and the eigenvector rows, their codes widened to bfloat16 by the
+// hardware conversion (exact), against a copy of q whose k-chunks follow the
+// code bytes each lane loads (lane g16 of a row loads its d/8 consecutive code
+// bytes, i.e. coordinates [4 g16 KS, 4 (g16 + 1) KS) ... so the q operand takes
+// 16-byte chunk KS g16 + s at k-step s); each product is then multiplied by
+// the eigenvector's fp32 scale before it is squared.
+constexpr int fp4_block_bytes(int d) { return 2 * d + 4 * kCobsRank + kCobsRank * d / 2; }
+
 template <int D>
+__device__ __forceinline__ void cobs2_fp4_tile_logits(const FusedScoreParams& p, __amdgpu_buffer_rsrc_t kr,
+                                                      const bf16x8_t (&bq)[D / 32], const bf16x8_t (&bqp)[D / 32],
+                                                      int base, float* dst, int stride, int lane, float (*tmp)[32])
+{
+    constexpr int KS = D / 32, BB = fp4_block_bytes(D), CB = D / 8;  // code bytes per lane and row
+    static_assert(kCobsRank == 4, "one output lane holds one block's four eigenvector products");
+    const int n16 = lane & 15, g16 = lane >> 4;
+    uint4 am[2][KS];
+    uint32_t ac[4][2][KS];  // four code bytes per k-step
+    float4 scl[4][2];       // the four scales of the block an output lane holds
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int tr = rb * 16 + n16;
+        const uint32_t om = (uint32_t)(base + tr) * BB + g16 * 16;  // past nb: zeros
+#pragma unroll
+        for (int s = 0; s < KS; ++s) am[rb][s] = buffer_ld16(kr, om + s * 64);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t oc = (uint32_t)(base + 8 * u + tr / 4) * BB + 2 * D + 16 + (tr % 4) * (D / 2) + g16 * CB;
+            if constexpr (KS == 4) {
+                const uint4 c4 = buffer_ld16(kr, oc);
+                ac[u][rb][0] = c4.x;
+                ac[u][rb][1] = c4.y;
+                ac[u][rb][2] = c4.z;
+                ac[u][rb][3] = c4.w;
+            } else {
+                ac[u][rb][0] = buffer_ld4(kr, oc);
+                ac[u][rb][1] = buffer_ld4(kr, oc + 4);
+            }
+            const uint32_t os = (uint32_t)(base + 8 * u + 4 * rb + g16) * BB + 2 * D;
+            scl[u][rb] = __builtin_bit_cast(float4, buffer_ld16(kr, os));
+        }
+    }
+    f32x4_t cm[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+            cm[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, am[rb][s]), bq[s], cm[rb], 0, 0,
+                                                             0);
+    float sq[4][2];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        f32x4_t cx[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                const uint32_t w = ac[u][rb][s];
+                typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+                const bf16x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0);
+                const bf16x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1);
+                const bf16x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2);
+                const bf16x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3);
+                const uint4 a = make_uint4(__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1),
+                                           __builtin_bit_cast(uint32_t, v2), __builtin_bit_cast(uint32_t, v3));
+                cx[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), bqp[s], cx[rb], 0, 0,
+                                                                 0);
+            }
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            const float e0 = cx[rb][0] * scl[u][rb].x, e1 = cx[rb][1] * scl[u][rb].y;
+            const float e2 = cx[rb][2] * scl[u][rb].z, e3 = cx[rb][3] * scl[u][rb].w;
+            sq[u][rb] = (e0 * e0 + e1 * e1) + (e2 * e2 + e3 * e3);
+        }
+    }
+    if (n16 < p.G) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int tr = rb * 16 + 4 * g16 + i;
+                tmp[n16][tr] = fmaf(cm[rb][i], p.scale, base + tr == p.nb - 1 ? p.ln_last : p.ln_L);
+            }
+    }
+    wave_lds_fence();
+    const float half_s2 = 0.5f * p.scale * p.scale;
+    if (n16 < p.G) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) tmp[n16][8 * u + 4 * rb + g16] += half_s2 * sq[u][rb];
+    }
+    wave_lds_fence();
+    for (int e = lane; e < p.G * 32; e += 64) {
+        const int h = e >> 5, b = e & 31;
+        if (base + b < p.nb) dst[h * stride + base + b] = tmp[h][b];
+    }
+    wave_lds_fence();  // tmp is reused by the next tile
+}
+
+// The query operand with 16-byte chunk KS g16 + s at k-step s (see above).
+template <int D>
+__device__ __forceinline__ void load_q_operand_by_lane_chunks(const char* q_first_head, int nh, int lane,
+                                                              bf16x8_t (&bq)[D / 32])
+{
+    constexpr int KS = D / 32;
+    const int n16 = lane & 15, g16 = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (n16 < nh) v = ld16(q_first_head + (size_t)n16 * D * 2 + (KS * g16 + s) * 16);
+        bq[s] = __builtin_bit_cast(bf16x8_t, v);
+    }
+}
+
+template <int D, bool FP4>
 __global__ void __launch_bounds__(kFusedWaves * 64) score_cobs2_fused_kernel(const FusedScoreParams p)
 {
     constexpr int RB = D * 2, KS = D / 32, NW = kFusedWaves, NR = 1 + kCobsRank;
+    constexpr int BB = FP4 ? fp4_block_bytes(D) : NR * RB;
     extern __shared__ float lsm[];  // [G][nb] block logits
     __shared__ float lse_h[8];
     __shared__ float tmp[NW][8][32];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int pair = blockIdx.x, b = pair / p.Hkv, j = pair - b * p.Hkv;
-    bf16x8_t bq[KS];
+    bf16x8_t bq[KS], bqp[KS];
     load_q_operand<D>(p.q + ((size_t)b * p.Hq + (size_t)j * p.G) * RB, p.G, lane, bq);
-    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(p.Kbar + (size_t)pair * p.nb * NR * RB, (uint32_t)p.nb * NR * RB);
-    for (int base = wave * 32; base < p.nb; base += NW * 32) cobs2_tile_logits<D>(p, kr, bq, base, lsm, p.nb, lane, tmp[wave]);
+    if constexpr (FP4) load_q_operand_by_lane_chunks<D>(p.q + ((size_t)b * p.Hq + (size_t)j * p.G) * RB, p.G, lane, bqp);
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(p.Kbar + (size_t)pair * p.nb * BB, (uint32_t)p.nb * BB);
+    for (int base = wave * 32; base < p.nb; base += NW * 32) {
+        if constexpr (FP4)
+            cobs2_fp4_tile_logits<D>(p, kr, bq, bqp, base, lsm, p.nb, lane, tmp[wave]);
+        else
+            cobs2_tile_logits<D>(p, kr, bq, base, lsm, p.nb, lane, tmp[wave]);
+    }
     __syncthreads();
     group_scores_in_lds<NW>(lsm, lse_h, p.G, p.nb, p.scores + (size_t)pair * p.nb);
 }
 
-template <int D>
+template <int D, bool FP4>
 __global__ void __launch_bounds__(kSplitWaves * 64) score_cobs2_split_kernel(const FusedScoreParams p)
 {
     constexpr int RB = D * 2, KS = D / 32, NR = 1 + kCobsRank;
+    constexpr int BB = FP4 ? fp4_block_bytes(D) : NR * RB;
     __shared__ float tmp[kSplitWaves][8][32];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -635,10 +760,15 @@ __global__ void __launch_bounds__(kSplitWaves * 64) score_cobs2_split_kernel(con
     const int b = pair / p.Hkv, j = pair - b * p.Hkv;
     const int base = (chunk * kSplitWaves + wave) * 32;
     if (base >= p.nb) return;  // whole wave; no workgroup barrier in this kernel
-    bf16x8_t bq[KS];
+    bf16x8_t bq[KS], bqp[KS];
     load_q_operand<D>(p.q + ((size_t)b * p.Hq + (size_t)j * p.G) * RB, p.G, lane, bq);
-    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(p.Kbar + (size_t)pair * p.nb * NR * RB, (uint32_t)p.nb * NR * RB);
-    cobs2_tile_logits<D>(p, kr, bq, base, p.logits + (size_t)pair * p.G * p.nb, p.nb, lane, tmp[wave]);
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(p.Kbar + (size_t)pair * p.nb * BB, (uint32_t)p.nb * BB);
+    if constexpr (FP4) {
+        load_q_operand_by_lane_chunks<D>(p.q + ((size_t)b * p.Hq + (size_t)j * p.G) * RB, p.G, lane, bqp);
+        cobs2_fp4_tile_logits<D>(p, kr, bq, bqp, base, p.logits + (size_t)pair * p.G * p.nb, p.nb, lane, tmp[wave]);
+    } else {
+        cobs2_tile_logits<D>(p, kr, bq, base, p.logits + (size_t)pair * p.G * p.nb, p.nb, lane, tmp[wave]);
+    }
 }
 
 // Proxy-error logits ("OpenAttention reads 1% of the KV cache -- Count-aware
@@ -936,8 +1066,9 @@ hipError_t launch_score_summary_split(const Dims& s, const void* q, const void* 
     return launch_score_finish(s, logits, scores, sel, k, st);
 }
 
-hipError_t launch_score_cobs2(const Dims& s, const void* q, const void* Kcov, float* logits, float* scores,
-                              hipStream_t st)
+template <bool FP4>
+hipError_t launch_score_cobs2_t(const Dims& s, const void* q, const void* Kcov, float* logits, float* scores,
+                                hipStream_t st)
 {
     FusedScoreParams p = summary_params(s, q, Kcov, false);
     p.scores = scores;
@@ -946,21 +1077,28 @@ hipError_t launch_score_cobs2(const Dims& s, const void* q, const void* Kcov, fl
         const size_t shm = (size_t)s.G * s.nb * sizeof(float);
         const dim3 grid((unsigned)s.pairs()), block(kFusedWaves * 64);
         if (s.d == 128)
-            score_cobs2_fused_kernel<128><<<grid, block, shm, st>>>(p);
+            score_cobs2_fused_kernel<128, FP4><<<grid, block, shm, st>>>(p);
         else
-            score_cobs2_fused_kernel<64><<<grid, block, shm, st>>>(p);
+            score_cobs2_fused_kernel<64, FP4><<<grid, block, shm, st>>>(p);
         return hipGetLastError();
     }
     const int tiles = (s.nb + 31) / 32;
     p.chunks = (tiles + kSplitWaves - 1) / kSplitWaves;
     const dim3 grid((unsigned)(s.pairs() * p.chunks)), block(kSplitWaves * 64);
     if (s.d == 128)
-        score_cobs2_split_kernel<128><<<grid, block, 0, st>>>(p);
+        score_cobs2_split_kernel<128, FP4><<<grid, block, 0, st>>>(p);
     else
-        score_cobs2_split_kernel<64><<<grid, block, 0, st>>>(p);
+        score_cobs2_split_kernel<64, FP4><<<grid, block, 0, st>>>(p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || s.G == 1) return e;  // G == 1: the logits are the scores
     return launch_score_finish(s, logits, scores, nullptr, 0, st);
+}
+
+hipError_t launch_score_cobs2(const Dims& s, const void* q, const void* Kcov, float* logits, float* scores,
+                              hipStream_t st, bool fp4)
+{
+    return fp4 ? launch_score_cobs2_t<true>(s, q, Kcov, logits, scores, st)
+               : launch_score_cobs2_t<false>(s, q, Kcov, logits, scores, st);
 }
 
 size_t score_err_parts_bytes(const Dims& s)

@@ -50,7 +50,7 @@ class Workload:
     block_size: int
     dtype: str  # "f32" or "bf16"
     k: int  # blocks read exactly per KV head
-    score_mode: str  # "summary", "exact_mass", "box", "cobs2" or "proxy_error"
+    score_mode: str  # "summary", "exact_mass", "box", "cobs2", "cobs2_fp4" or "proxy_error"
     proxies: bool  # one count-aware proxy per unread block
     keys: str  # "heavy_hitters" or "clusters"
     n_clusters: int = 64
@@ -93,6 +93,8 @@ WORKLOADS = {
                  description="the headline layer with blocks ranked by their min/max key box (Quest)"),
         Workload("llama3_8b_layer_b32_cobs2", 1002, 32, 32, 8, 128, 32768, 64, "bf16", 5, "cobs2", True,
                  "clusters", description="the headline layer with second-order (mean + rank-4 covariance) scores"),
+        Workload("llama3_8b_layer_b32_cobs2_fp4", 1002, 32, 32, 8, 128, 32768, 64, "bf16", 5, "cobs2_fp4", True,
+                 "clusters", description="the headline layer with second-order scores from FP4 (E2M1) eigenvectors"),
         Workload("llama3_8b_layer_b32_err", 1002, 32, 32, 8, 128, 32768, 64, "bf16", 5, "proxy_error", True,
                  "clusters", description="the headline layer with exact reads spent on the largest estimated "
                                          "proxy errors (mean and variance tokens)"),

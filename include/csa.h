@@ -78,7 +78,8 @@ typedef enum csa_score_mode {
     CSA_SCORE_EXACT_MASS = 1, /* exact block mass from every key ("OSA")             */
     CSA_SCORE_BOX = 2,        /* best logit over the block's min/max key box (Quest) */
     CSA_SCORE_COBS2 = 3,      /* second-order (mean + covariance) estimate of ln m_b */
-    CSA_SCORE_PROXY_ERROR = 4 /* estimated weight error of the block's proxy [OA]   */
+    CSA_SCORE_PROXY_ERROR = 4, /* estimated weight error of the block's proxy [OA]  */
+    CSA_SCORE_COBS2_FP4 = 5    /* COBS2 from FP4 (E2M1) eigenvectors                */
 } csa_score_mode;
 
 /* Scaled eigenvectors per block in the second-order descriptor (kv_cov_build). */
@@ -97,7 +98,8 @@ typedef enum csa_entry {
     CSA_WS_SELECTIVE_DECODE_STEP = 4,
     CSA_WS_BLOCK_SCORE_BOX = 5,
     CSA_WS_BLOCK_SCORE_COBS2 = 6,
-    CSA_WS_BLOCK_SCORE_PROXY_ERROR = 7
+    CSA_WS_BLOCK_SCORE_PROXY_ERROR = 7,
+    CSA_WS_BLOCK_SCORE_COBS2_FP4 = 8
 } csa_entry;
 
 typedef struct csa_shape {
@@ -148,6 +150,23 @@ int kv_box_build(const csa_shape* shape, const void* K, void* Kbox, hipStream_t 
 int kv_cov_build(const csa_shape* shape, const void* K, void* Kcov, hipStream_t stream);
 
 /*
+ * kv_cov4_build -- the descriptor of kv_cov_build with its eigenvectors stored in
+ * the E2M1 FP4 format, one fp32 scale per eigenvector, the mean key kept in
+ * bfloat16 ([COBS] section on quantising the stored eigenvectors: at rank 4 and
+ * d = 128 the covariance factor takes 272 bytes per block instead of 1024).
+ * Per block, CSA_COV4_BLOCK_BYTES(d) bytes: the mean key (d bfloat16, the bits
+ * of Kbar), the CSA_COBS_RANK scales s_i = max_t |xi_it| / 6 (binary32), then
+ * for each eigenvector d/2 bytes of codes, coordinate 2t in the low and 2t + 1
+ * in the high nibble of byte t.  xi_it is the bfloat16 value kv_cov_build
+ * stores; its code is xi_it / s_i (binary32 quotient) rounded to the nearest of
+ * +-{0, 0.5, 1, 1.5, 2, 3, 4, 6}, ties to the even mantissa, zero as +0.  Reads
+ * K [B, Hkv, n, d] (bfloat16 only, else CSA_ERR_UNSUPPORTED); writes Kcov4
+ * [B, Hkv, nb, CSA_COV4_BLOCK_BYTES(d)] bytes.  Blocks of at most 64 tokens.
+ */
+#define CSA_COV4_BLOCK_BYTES(d) (2 * (d) + 4 * CSA_COBS_RANK + CSA_COBS_RANK * (d) / 2)
+int kv_cov4_build(const csa_shape* shape, const void* K, void* Kcov4, hipStream_t stream);
+
+/*
  * kv_var_build -- per block, the mean and the variance tokens that the
  * proxy-error ranking of [OA] reads (section "Three helpers that make the
  * proxy accurate": mean and variance tokens cached per group of tokens, the
@@ -172,6 +191,8 @@ int kv_var_build(const csa_shape* shape, const void* K, void* Kvar, hipStream_t 
  *   COBS2:      l_hb = scale q_h . Kbar_b + ln c_b + (1/2) scale^2 sum_i (q_h . xi_bi)^2
  *               (keys = Kcov from kv_cov_build; bfloat16, G <= 8 and G nb <= 16384,
  *               else CSA_ERR_UNSUPPORTED)
+ *   COBS2_FP4:  the COBS2 logit with xi_bi = s_i x E2M1(code) decoded from keys =
+ *               Kcov4 (kv_cov4_build); the same conditions as COBS2
  *   PROXY_ERROR: l_hb = shat_hb + ln sigma_hb, the log of the estimated weight
  *               error of the block's proxy, its mass e^{shat_hb} times the spread
  *               of the logits it hides ([OA]), with shat_hb the SUMMARY logit and
@@ -188,7 +209,7 @@ int kv_var_build(const csa_shape* shape, const void* K, void* Kvar, hipStream_t 
  *          ln sum_h exp(l_hb - ln sum_b' e^{shat_hb'}): each head's error as a
  *          share of its estimated softmax denominator.
  * Writes scores [B, Hkv, nb].  Workspace: csa_workspace_size(shape,
- * CSA_WS_BLOCK_SCORE_SUMMARY, _EXACT_MASS, _BOX, _COBS2 or _PROXY_ERROR, 0, 0)
+ * CSA_WS_BLOCK_SCORE_SUMMARY, _EXACT_MASS, _BOX, _COBS2, _COBS2_FP4 or _PROXY_ERROR, 0, 0)
  * bytes (0 when G = 1).
  */
 int block_score(const csa_shape* shape, csa_score_mode mode, const void* q, const void* keys,
@@ -245,8 +266,8 @@ int dense_decode_attn(const csa_shape* shape, const void* q, const void* K, cons
  * (bfloat16, G <= 8, k <= 32, nb <= 2048, B * Hkv >= 32) one kernel per KV head
  * reads Kbar once, keeps the logits on chip for both uses, selects the blocks
  * and attends; otherwise the three entry points run in turn.
- * keys = Kbar (SUMMARY) or K (EXACT_MASS) as for block_score (BOX, COBS2 and
- * PROXY_ERROR scores are CSA_ERR_UNSUPPORTED here: they need Kbox, Kcov or Kvar
+ * keys = Kbar (SUMMARY) or K (EXACT_MASS) as for block_score (BOX, COBS2,
+ * COBS2_FP4 and PROXY_ERROR scores are CSA_ERR_UNSUPPORTED here: they need Kbox, Kcov, Kcov4 or Kvar
  * besides Kbar; use the three entry points); Kbar may be NULL in EXACT_MASS
  * mode without proxies.  scores [B, Hkv, nb] and
  * sel [B, Hkv, min(k, nb)] are written when not NULL.  0 <= k; k = 0 with no

@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = set(declared_functions())
-    assert {"kv_summary_build", "kv_box_build", "kv_cov_build", "kv_var_build", "block_score", "topk_select", "sparse_decode_attn",
+    assert {"kv_summary_build", "kv_box_build", "kv_cov_build", "kv_cov4_build", "kv_var_build", "block_score", "topk_select", "sparse_decode_attn",
             "dense_decode_attn", "selective_decode_step", "csa_workspace_size", "csa_status_str",
             "csa_last_error"} <= names
 
@@ -159,6 +159,21 @@ def test_var_build_and_proxy_error_argument_checks(L):
                          None) == csa.CSA_ERR_UNSUPPORTED
     assert b"proxy-error" in L.csa_last_error()
     assert step(L, s, mode=csa.CSA_SCORE_PROXY_ERROR) == csa.CSA_ERR_UNSUPPORTED
+
+
+def test_cov4_build_argument_checks(L):
+    s = shape()
+    assert L.kv_cov4_build(ctypes.byref(s), None, FAKE, None) == csa.CSA_ERR_INVALID_ARG
+    assert L.kv_cov4_build(ctypes.byref(s), FAKE, FAKE + 4, None) == csa.CSA_ERR_INVALID_ARG
+    assert L.kv_cov4_build(ctypes.byref(shape(L=128)), FAKE, FAKE, None) == csa.CSA_ERR_UNSUPPORTED
+    assert L.kv_cov4_build(ctypes.byref(shape(dtype=csa.CSA_F32)), FAKE, FAKE, None) == csa.CSA_ERR_UNSUPPORTED
+    assert b"bfloat16" in L.csa_last_error()
+    assert csa.cov4_block_bytes(128) == 256 + 16 + 256  # mean, scales, codes: the factor is 272 bytes
+    assert L.csa_workspace_size(ctypes.byref(s), csa.CSA_WS_BLOCK_SCORE_COBS2_FP4, 0, 0) == \
+        L.csa_workspace_size(ctypes.byref(s), csa.CSA_WS_BLOCK_SCORE_COBS2, 0, 0)
+    assert L.block_score(ctypes.byref(shape(dtype=csa.CSA_F32)), csa.CSA_SCORE_COBS2_FP4, FAKE, FAKE, FAKE, FAKE,
+                         1 << 20, None) == csa.CSA_ERR_UNSUPPORTED
+    assert step(L, s, mode=csa.CSA_SCORE_COBS2_FP4) == csa.CSA_ERR_UNSUPPORTED
 
 
 def test_box_build_argument_checks(L):

@@ -567,6 +567,89 @@ def test_cobs2_pipeline_matches_oracle(B, Hkv, G, n, L, k):
     compare_pipelines(w, g, o, f"cobs2 B={B} Hkv={Hkv} G={G} n={n} L={L}")
 
 
+def test_cov4_descriptors_are_the_fp4_storage_of_the_bf16_ones():
+    """kv_cov4_build stores exactly what the oracle's FP4 packing makes of kv_cov_build's
+    bfloat16 descriptors (same eigen-solve on the GPU): bit for bit, d = 128 and 64, ragged."""
+    for B, Hkv, d, n, L in [(2, 2, 128, 1000, 64), (1, 3, 64, 700, 16), (2, 1, 128, 4096, 64)]:
+        data = rand_inputs(800 + n + d, B, Hkv, Hkv, d, n, "bf16")
+        K = dev(data["K"])
+        kc, k4 = host(csa.kv_cov_build(K, L)), host(csa.kv_cov4_build(K, L))
+        torch.cuda.synchronize()
+        shp = O.Shape(B, Hkv, Hkv, d, n, L, "bf16")
+        assert np.array_equal(k4, O.cov4_pack(shp, kc)), f"Kcov4 differs (B={B} Hkv={Hkv} d={d} n={n} L={L})"
+
+
+def cobs2_fp4_case(w, data, k=None, proxies=True):
+    """GPU pipeline with FP4 second-order scores; the oracle decodes and scores the GPU's
+    stored FP4 descriptors."""
+    k = w.k if k is None else k
+    q, K, V = dev(data["q"]), dev(data["K"]), dev(data["V"])
+    Kbar, Vbar = csa.kv_summary_build(K, V, w.block_size)
+    Kcov4 = csa.kv_cov4_build(K, w.block_size)
+    scores = csa.block_score(q, Kcov4, "cobs2_fp4", w.block_size, n_tokens=w.n_tokens)
+    sel = csa.topk_select(scores, k)
+    out, lse = csa.sparse_decode_attn(q, K, V, Kbar, Vbar, sel, w.block_size, proxies=proxies)
+    torch.cuda.synchronize()
+    g = {"Kbar": host(Kbar), "Vbar": host(Vbar), "score": host(scores), "sel": host(sel), "out": host(out),
+         "lse": host(lse)}
+    shp = oshape(w, B=data["q"].shape[0], Hkv=data["K"].shape[1])
+    Kbar_o, Vbar_o = O.kv_summary_build(shp, data["K"], data["V"])
+    k4 = host(Kcov4)
+    assert np.array_equal(k4[..., :2 * w.head_dim].copy().view(np.uint16), Kbar_o), "FP4 mean rows not bit-exact"
+    score = O.group_score(shp, O.cobs2_fp4_logits(shp, data["q"], k4))
+    sel_o, margin = O.topk_select(score, k)
+    out_o, lse_o = O.sparse_decode_attn(shp, data["q"], data["K"], data["V"], Kbar_o, Vbar_o, sel_o, proxies)
+    o = {"Kbar": Kbar_o, "Vbar": Vbar_o, "score": score, "sel": sel_o, "margin": margin, "out": out_o, "lse": lse_o}
+    return g, o
+
+
+@pytest.mark.parametrize("B,Hkv,G,n,L,k,d", [
+    (2, 2, 4, 4096, 64, 5, 128),    # split scoring path (few KV heads)
+    (8, 4, 4, 4096, 64, 5, 128),    # one workgroup per KV head
+    (2, 2, 7, 3000, 64, 8, 128),    # G = 7, ragged last block
+    (8, 4, 2, 2000, 32, 4, 64),     # d = 64, one workgroup per KV head, ragged
+    (2, 2, 1, 1000, 16, 3, 64),     # d = 64, G = 1, split path
+])
+def test_cobs2_fp4_pipeline_matches_oracle(B, Hkv, G, n, L, k, d):
+    w = W.Workload("cobs2_fp4_case", 0, B, G * Hkv, Hkv, d, n, L, "bf16", k, "cobs2_fp4", True, "clusters")
+    data = rand_inputs(900 + B + G + n + d, B, G * Hkv, Hkv, d, n, "bf16")
+    g, o = cobs2_fp4_case(w, data)
+    compare_pipelines(w, g, o, f"cobs2 fp4 B={B} Hkv={Hkv} G={G} n={n} L={L} d={d}")
+
+
+def test_cobs2_fp4_full_size_sampled():
+    """The headline shape with FP4 second-order scores, as the benchmark runs it; the
+    oracle scores a seeded sample of KV heads from the stored FP4 descriptors."""
+    w = W.WORKLOADS["llama3_8b_layer_b32_cobs2_fp4"]
+    data = W.generate(w)
+    q, K, V = dev(data["q"]), dev(data["K"]), dev(data["V"])
+    Kbar, Vbar = csa.kv_summary_build(K, V, w.block_size)
+    Kcov4 = csa.kv_cov4_build(K, w.block_size)
+    scores = csa.block_score(q, Kcov4, "cobs2_fp4", w.block_size, n_tokens=w.n_tokens)
+    sel = csa.topk_select(scores, w.k)
+    out, lse = csa.sparse_decode_attn(q, K, V, Kbar, Vbar, sel, w.block_size, proxies=True)
+    torch.cuda.synchronize()
+    k4, sc, sl, o_, l_ = host(Kcov4), host(scores), host(sel), host(out), host(lse)
+    assert np.isfinite(o_).all() and np.isfinite(l_).all()
+    rng = np.random.default_rng(zlib.crc32(w.name.encode()))
+    pairs = {(int(rng.integers(w.batch)), int(rng.integers(w.n_kv_heads))) for _ in range(3)}
+    G = w.group
+    for b, j in sorted(pairs):
+        sub = {"q": data["q"][b:b + 1, j * G:(j + 1) * G], "K": data["K"][b:b + 1, j:j + 1],
+               "V": data["V"][b:b + 1, j:j + 1]}
+        shp = oshape(w, B=1, Hkv=1)
+        Kbar_o, Vbar_o = O.kv_summary_build(shp, sub["K"], sub["V"])
+        score = O.group_score(shp, O.cobs2_fp4_logits(shp, sub["q"], k4[b:b + 1, j:j + 1]))
+        sel_o, margin = O.topk_select(score, w.k)
+        out_o, lse_o = O.sparse_decode_attn(shp, sub["q"], sub["K"], sub["V"], Kbar_o, Vbar_o, sel_o, True)
+        g = {"Kbar": host(Kbar)[b:b + 1, j:j + 1], "Vbar": host(Vbar)[b:b + 1, j:j + 1],
+             "score": sc[b:b + 1, j:j + 1], "sel": sl[b:b + 1, j:j + 1], "out": o_[b:b + 1, j * G:(j + 1) * G],
+             "lse": l_[b:b + 1, j * G:(j + 1) * G]}
+        o = {"Kbar": Kbar_o, "Vbar": Vbar_o, "score": score, "sel": sel_o, "margin": margin, "out": out_o,
+             "lse": lse_o}
+        compare_pipelines(w, g, o, f"cobs2 fp4 full pair ({b},{j})")
+
+
 def test_cobs2_needs_bfloat16():
     w = W.WORKLOADS["tiny_f32_d64"]
     data = W.generate(w)
