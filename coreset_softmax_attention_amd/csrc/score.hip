@@ -950,9 +950,10 @@ __global__ void __launch_bounds__(kFusedWaves * 64) score_finish_kernel(const Fu
     __shared__ uint32_t cand[128];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int pair = blockIdx.x, G = p.G, nb = p.nb;
-    // copy the logits in (chunks of loads issued together: one memory round trip each)
+    // copy the logits in (chunks of loads issued together: one memory round trip each;
+    // a chunk covers kFusedMaxLogits, so one round trip)
     const float* src = p.logits + (size_t)pair * G * nb;
-    constexpr int CH = 8;
+    constexpr int CH = kFusedMaxLogits / (NW * 64);
     for (int i0 = 0; i0 < G * nb; i0 += CH * NW * 64) {
         float v[CH];
 #pragma unroll
