@@ -25,7 +25,7 @@ decode token through the layer, all query heads); the roofline object is for
 the step's kernel (bytes: every mean key, the mean values of unread blocks,
 the exact key/value rows, the queries and the outputs).
 
-Prints one JSON line.  --gpus above 1 is refused: this build runs on one GPU.
+Prints one JSON line.  --gpus above 1 is refused: the selective decode path runs on one GPU.
 """
 from __future__ import annotations
 
@@ -192,7 +192,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the selective decode path has no "
-              "multi-GPU mode in this build.", file=sys.stderr)
+              "multi-GPU mode.", file=sys.stderr)
         sys.exit(2)
 
     if args.copy_probe:

@@ -9,7 +9,7 @@ Every stream is a NumPy PCG64 generator seeded by a SeedSequence of
 query head, 1) for queries, so a stream does not depend on which other streams
 are drawn, and a subset of the batch can be generated on its own.
 
-Recipes (the readings of the configuration texts are listed in the design doc):
+Recipes (where a configuration text is open, the plainest reading is taken):
 
 * tiny_f32_d64 -- B=1, one query and one KV head, d=64, n=1024, binary32.
   K, V ~ N(0, 1); q = 2 N(0, 1); 8 distinct heavy-hitter positions drawn

@@ -1,6 +1,6 @@
 """Parity of the HIP path (through the C-ABI) with the fp64 oracle on the same seeded inputs.
 
-Bars (written here, derived in the design doc):
+Bars (written here; each follows from fp32 accumulation against the fp64 oracle):
   * summaries and selections: bit-exact;
   * outputs: per row ||o - o_ref||_inf / ||o_ref||_inf <= 2e-3 for bfloat16 inputs, 1e-5 for
     binary32 inputs (fp32 accumulation against fp64);
