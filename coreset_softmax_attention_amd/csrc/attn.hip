@@ -44,18 +44,11 @@ constexpr int kMaxSplitRows = 8192;   // rows per workgroup (bitmap capacity)
 constexpr int kMaxSelLds = 512;       // selections kept in LDS by the bfloat16 kernel
 constexpr int kMaxTokLds = 1024;      // weighted tokens of a workgroup kept in LDS
 constexpr int kTargetWorkgroups = 2048;
-#ifndef CSA_MFMA_WAVES
-#define CSA_MFMA_WAVES 8
-#endif
-#ifndef CSA_MFMA_MIN_WGS
-#define CSA_MFMA_MIN_WGS 256
-#endif
-#ifndef CSA_MFMA_TILES_PER_WAVE
-#define CSA_MFMA_TILES_PER_WAVE 16
-#endif
-constexpr int kMfmaWaves = CSA_MFMA_WAVES;          // waves per workgroup, bfloat16 path
-constexpr int kMfmaMinWgs = CSA_MFMA_MIN_WGS;       // workgroups to cover every CU once
-constexpr int kMfmaTilesPerWave = CSA_MFMA_TILES_PER_WAVE;  // tiles a wave streams before splitting
+// bfloat16 path, chosen by measurement over (waves, workgroups) on the headline
+// shape: eight waves (two per SIMD), one workgroup per CU at least
+constexpr int kMfmaWaves = 8;          // waves per workgroup
+constexpr int kMfmaMinWgs = 256;       // workgroups to cover every CU once
+constexpr int kMfmaTilesPerWave = 16;  // tiles a wave streams before the rows are split
 
 constexpr int unroll_for(int hg) { return hg <= 4 ? 8 : 4; }
 

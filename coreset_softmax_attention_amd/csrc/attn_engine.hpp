@@ -186,9 +186,6 @@ struct MfmaEngine {
             for (int e = 0; e < 8; ++e) acc[g][e] *= al[g];
 #pragma unroll
         for (int u = 0; u < NVI; ++u) {
-#ifdef CSA_SCHED_BARRIER
-            __builtin_amdgcn_sched_barrier(0);
-#endif
             float pr[HP];
             *reinterpret_cast<float4*>(&pr[0]) = *reinterpret_cast<const float4*>(&sm.p[wave][gv * NVI + u][0]);
             if constexpr (HP == 8)
