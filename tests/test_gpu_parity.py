@@ -650,6 +650,50 @@ def test_cobs2_fp4_full_size_sampled():
         compare_pipelines(w, g, o, f"cobs2 fp4 full pair ({b},{j})")
 
 
+@pytest.mark.parametrize("mode", ["proxy_error", "cobs2_fp4", "box"])
+@pytest.mark.parametrize("batch,n_kv_heads", [(2, 2), (8, 4)])  # split route, one workgroup per KV head
+def test_descriptor_scores_replay_in_a_graph(mode, batch, n_kv_heads):
+    """block_score over each descriptor captured in a HIP graph with topk_select and replayed
+    several times, with eager work on the same buffers between replays: bit for bit the eager
+    result each time."""
+    w = small("llama3_8b_layer_b1", batch=batch, n_tokens=4096, n_kv_heads=n_kv_heads)
+    data = W.generate(w)
+    q, K = dev(data["q"]), dev(data["K"])
+    build = {"proxy_error": csa.kv_var_build, "cobs2_fp4": csa.kv_cov4_build, "box": csa.kv_box_build}[mode]
+    keys = build(K, w.block_size)
+    shape = csa.make_shape(q, K, w.block_size)
+    entry = {"proxy_error": csa.CSA_WS_BLOCK_SCORE_PROXY_ERROR, "cobs2_fp4": csa.CSA_WS_BLOCK_SCORE_COBS2_FP4,
+             "box": csa.CSA_WS_BLOCK_SCORE_BOX}[mode]
+    ws = torch.empty(max(1, csa.workspace_size(shape, entry)), dtype=torch.uint8, device="cuda")
+    scores = torch.empty((w.batch, w.n_kv_heads, w.n_blocks), dtype=torch.float32, device="cuda")
+    sel = torch.empty((w.batch, w.n_kv_heads, w.k), dtype=torch.int32, device="cuda")
+
+    def run():
+        csa.block_score(q, keys, mode, w.block_size, n_tokens=w.n_tokens, scores=scores, ws=ws)
+        csa.topk_select(scores, w.k, sel=sel)
+
+    run()
+    torch.cuda.synchronize()
+    ref = [host(scores).copy(), host(sel).copy()]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for i in range(3):
+        scores.fill_(float(i))
+        sel.fill_(-1)
+        ws.fill_(i)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(ref[0]), bits(host(scores))), f"{mode}: replay {i} scores"
+        assert np.array_equal(ref[1], host(sel)), f"{mode}: replay {i} selection"
+
+
 def test_cobs2_needs_bfloat16():
     w = W.WORKLOADS["tiny_f32_d64"]
     data = W.generate(w)
