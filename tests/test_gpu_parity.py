@@ -570,7 +570,8 @@ def test_cobs2_pipeline_matches_oracle(B, Hkv, G, n, L, k):
 def test_cov4_descriptors_are_the_fp4_storage_of_the_bf16_ones():
     """kv_cov4_build stores exactly what the oracle's FP4 packing makes of kv_cov_build's
     bfloat16 descriptors (same eigen-solve on the GPU): bit for bit, d = 128 and 64, ragged."""
-    for B, Hkv, d, n, L in [(2, 2, 128, 1000, 64), (1, 3, 64, 700, 16), (2, 1, 128, 4096, 64)]:
+    # L = 3: at most two nonzero eigenvectors, the others have scale 0 and zero codes
+    for B, Hkv, d, n, L in [(2, 2, 128, 1000, 64), (1, 3, 64, 700, 16), (2, 1, 128, 4096, 64), (1, 2, 128, 300, 3)]:
         data = rand_inputs(800 + n + d, B, Hkv, Hkv, d, n, "bf16")
         K = dev(data["K"])
         kc, k4 = host(csa.kv_cov_build(K, L)), host(csa.kv_cov4_build(K, L))
