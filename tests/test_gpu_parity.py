@@ -429,10 +429,10 @@ STEP_CASES = [  # B * Hkv >= 32 takes the one-kernel path
     ("mha_b8_summary", small("exact_mass_mha_b8", batch=2, n_tokens=4096, n_kv_heads=16),
      {"mode": "summary", "proxies": True}),
     ("coreset_g7_b8", small("weighted_coreset_128k", batch=8, n_tokens=8192, n_kv_heads=4).with_(coreset=300), {}),
-    # more than 16 mean-key tiles: the proxy values stay in registers
+    # 1024 blocks: more than 16 mean-key tiles, so waves take more than two proxy tiles each
     ("llama_b8_8k_L8", small("llama3_8b_layer_b32", batch=8, n_tokens=8192, n_kv_heads=4).with_(block_size=8),
      {"k": 24}),
-    # G = 8 over 512 blocks: logits of 8 heads leave no LDS for the proxy values
+    # G = 8 heads over 512 blocks: the largest logit table in LDS
     ("g8_d64_nb512", W.Workload("g8_d64_nb512", 1003, 4, 64, 8, 64, 8192, 16, "bf16", 12, "summary", True,
                                 "clusters"), {}),
     ("few_pairs_unfused", small("llama3_8b_layer_b1", batch=2, n_tokens=4096, n_kv_heads=2), {}),
