@@ -104,6 +104,19 @@ struct MfmaEngine {
         for (int u = 0; u < NVI; ++u) t.vr[u] = buffer_ld16(vr, sm.tab_row[tb][wave][gv * NVI + u] * RB + cv * 16);
     }
 
+    // Issue only the key rows of a tile whose row table `tb` is written (its
+    // value rows follow with issue_values).
+    __device__ __forceinline__ void issue_keys(Tile& t, int tb, __amdgpu_buffer_rsrc_t kr)
+    {
+        wave_lds_fence();
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            const uint32_t off = sm.tab_row[tb][wave][rb * 16 + n16] * RB + g16 * 16;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) t.ak[rb][s] = buffer_ld16(kr, off + s * 64);
+        }
+    }
+
     // Issue only the value rows of a tile (its logits come from the caller).
     __device__ __forceinline__ void issue_values(uint4 (&vr)[NVI], int tb, __amdgpu_buffer_rsrc_t rsrc)
     {

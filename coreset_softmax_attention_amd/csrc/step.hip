@@ -213,13 +213,16 @@ __global__ void __launch_bounds__(kStepWaves * 64) decode_step_kernel(const Step
             }
         }
     };
-    auto issue_cache = [&](int jj, typename E::Tile& t, int tb) {
+    auto set_cache_rows = [&](int jj, int tb) {
         if (lane < TR) {
             uint32_t row;
             float lw;
             resolve_cache(row0(tile_of(jj)) + lane, row, lw);
             eng.set_row(tb, lane, row, lw);
         }
+    };
+    auto issue_cache = [&](int jj, typename E::Tile& t, int tb) {
+        set_cache_rows(jj, tb);
         eng.issue(t, tb, Kc, Vc, true);
     };
     auto proxy_tile = [&](int jj, const uint4 (&vr)[E::NVI], int tb) {
@@ -236,13 +239,21 @@ __global__ void __launch_bounds__(kStepWaves * 64) decode_step_kernel(const Step
 
     // The selection is known: mask the selected blocks in the prefetched proxy
     // tiles and finish the proxy tiles (two value tiles in flight), then stream
-    // the cache tiles (key and value tiles, one and a half in flight).  Issuing
-    // the first cache tile before the proxy tiles would hold three tiles of
-    // registers at once and spill.
+    // the cache tiles (key and value tiles, one and a half in flight).  When the
+    // wave's proxy values are all in flight already (at most two tiles), the
+    // keys of its first cache tile go out now, so that they stream behind the
+    // proxy values instead of after them; its values follow once the proxy
+    // tiles are done (the whole first tile now would not fit in registers
+    // beside them).  With more than four heads the keys wait too.
     if (Pw > 0) set_proxy_rows(0, 0, true);
     if (Pw > 1) set_proxy_rows(1, 1, true);
     typename E::Tile CA, CB;
     const bool any_cache = Tw > Pw;
+    const bool early_keys = HG <= 4 && any_cache && Pw <= 2;
+    if (early_keys) {
+        set_cache_rows(Pw, 2);
+        eng.issue_keys(CA, 2, Kc);
+    }
     for (int jj = 0; jj < Pw; jj += 2) {
         proxy_tile(jj, VA, 0);
         if (jj + 2 < Pw) {
@@ -257,7 +268,10 @@ __global__ void __launch_bounds__(kStepWaves * 64) decode_step_kernel(const Step
             }
         }
     }
-    if (any_cache) issue_cache(Pw, CA, 2);
+    if (early_keys)
+        eng.issue_values(CA.vr, 2, Vc);
+    else if (any_cache)
+        issue_cache(Pw, CA, 2);
     // cache tiles (weighted and exact rows): keys and values; the next tile's
     // loads go out once this tile's keys are consumed (one and a half tiles of
     // registers in flight)
