@@ -380,15 +380,25 @@ __global__ void __launch_bounds__(NW * 64) attn_mfma_kernel(const AttnParams p)
     const bool tok_in_lds = w_hi > w_lo && w_hi - w_lo <= kMaxTokLds;
     RowSources src{p.sel + (size_t)pair * p.k, p.tok_idx + (size_t)pair * p.m, p.tok_logw + (size_t)pair * p.m, 0};
 
-    auto issue = [&](int base, typename E::Tile& t, int tb, bool masked) {
+    auto set_rows = [&](int base, int tb, bool masked) {
         if (lane < TR) {
             uint32_t row;
             float lw;
             resolve_row(p, src, base + lane, r1, pb_lo, sel_bits, masked, row, lw);
             eng.set_row(tb, lane, row, lw);
         }
+    };
+    auto issue = [&](int base, typename E::Tile& t, int tb, bool masked) {
+        set_rows(base, tb, masked);
         const bool summ = base < p.wbeg;  // uniform over the wave
         eng.issue(t, tb, summ ? Ks : Kc, summ ? Vs : Vc, true);
+    };
+    auto issue_keys = [&](int base, typename E::Tile& t, int tb) {
+        set_rows(base, tb, true);
+        eng.issue_keys(t, tb, base < p.wbeg ? Ks : Kc);
+    };
+    auto issue_values = [&](int base, typename E::Tile& t, int tb) {
+        eng.issue_values(t.vr, tb, base < p.wbeg ? Vs : Vc);
     };
     auto compute = [&](const typename E::Tile& t, int tb) {
         float x[8];
@@ -450,18 +460,39 @@ __global__ void __launch_bounds__(NW * 64) attn_mfma_kernel(const AttnParams p)
         wave_lds_fence();
     }
     if (t < nT) {
-        for (;;) {
-            const int t1 = t + NW;
-            compute(A, 0);
-            if (t1 < nT) issue(row0(t1), B, 1, true);
-            eng.accumulate(A);
-            if (t1 >= nT) break;
-            const int t2 = t1 + NW;
-            compute(B, 1);
-            if (t2 < nT) issue(row0(t2), A, 0, true);
-            eng.accumulate(B);
-            if (t2 >= nT) break;
-            t = t2;
+        if constexpr (HG <= 4) {
+            // a tile's keys go out before the logits of the tile ahead of it,
+            // its values right after them
+            int t1 = t + NW;
+            if (t1 < nT) issue_keys(row0(t1), B, 1);
+            for (;;) {
+                compute(A, 0);
+                if (t1 < nT) issue_values(row0(t1), B, 1);
+                eng.accumulate(A);
+                if (t1 >= nT) break;
+                const int t2 = t1 + NW;
+                if (t2 < nT) issue_keys(row0(t2), A, 0);
+                compute(B, 1);
+                if (t2 < nT) issue_values(row0(t2), A, 0);
+                eng.accumulate(B);
+                if (t2 >= nT) break;
+                t1 = t2 + NW;
+                if (t1 < nT) issue_keys(row0(t1), B, 1);
+            }
+        } else {
+            for (;;) {
+                const int t1 = t + NW;
+                compute(A, 0);
+                if (t1 < nT) issue(row0(t1), B, 1, true);
+                eng.accumulate(A);
+                if (t1 >= nT) break;
+                const int t2 = t1 + NW;
+                compute(B, 1);
+                if (t2 < nT) issue(row0(t2), A, 0, true);
+                eng.accumulate(B);
+                if (t2 >= nT) break;
+                t = t2;
+            }
         }
     }
     float* part = p.splits == 1 ? nullptr : p.part + (((size_t)pair * p.splits + split) * p.G + g0) * (D + 2);
