@@ -258,12 +258,18 @@ __global__ void __launch_bounds__(kExactWaves * 64) logits_exact_mfma_kernel(con
     load_q_operand<D>(p.q + ((size_t)b * p.Hq + (size_t)j * p.G) * RB, p.G, lane, bq);
     const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(p.keys + (size_t)pair * p.n * RB, (uint32_t)p.n * RB);
 
+    // Every tile load is issued unconditionally (a tile past the wave's share
+    // reads through an empty buffer: zeros, no memory traffic) and the loop
+    // has no exit between its two halves, so that the compiler's wait before a
+    // tile's MFMAs covers that tile's loads only, not the next tile's too.
+    const __amdgpu_buffer_rsrc_t none = buffer_rsrc(p.keys, 0u);
     auto load = [&](int t, uint4 (&ak)[2][KS]) {
+        const __amdgpu_buffer_rsrc_t r = t < t1 ? kr : none;
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
             const uint32_t off = (uint32_t)(t * 32 + rb * 16 + n16) * RB + g16 * 16;  // past n: zeros
 #pragma unroll
-            for (int s = 0; s < KS; ++s) ak[rb][s] = buffer_ld16(kr, off + s * 64);
+            for (int s = 0; s < KS; ++s) ak[rb][s] = buffer_ld16(r, off + s * 64);
         }
     };
     float m_run = kNegInf, l_run = 0.0f;  // this lane's head n16, its rows of the current block
@@ -311,14 +317,15 @@ __global__ void __launch_bounds__(kExactWaves * 64) logits_exact_mfma_kernel(con
     };
     uint4 A[2][KS], B[2][KS];
     load(t0, A);
-    if (t0 + 1 < t1) load(t0 + 1, B);
-    for (int t = t0; t < t1; t += 2) {
+    load(t0 + 1, B);
+    int t = t0;
+    for (; t + 1 < t1; t += 2) {
         consume(t, A);
-        if (t + 2 < t1) load(t + 2, A);
-        if (t + 1 >= t1) break;
+        load(t + 2, A);
         consume(t + 1, B);
-        if (t + 3 < t1) load(t + 3, B);
+        load(t + 3, B);
     }
+    if (t < t1) consume(t, A);
 }
 
 // Group score per KV head from the per-head logits [B, Hq, nb] (G > 1).
