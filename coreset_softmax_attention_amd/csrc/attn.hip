@@ -363,15 +363,6 @@ __global__ void __launch_bounds__(NW * 64) attn_mfma_kernel(const AttnParams p)
     E eng(sm, p.q + (size_t)(b * p.Hq + h0) * RB, nh);
     const int lane = eng.lane, wave = eng.wave;
 
-    // Segments are padded to whole tiles, so every tile reads either the cache
-    // (weighted and exact rows) or the summaries (proxy rows).
-    const __amdgpu_buffer_rsrc_t Kc = buffer_rsrc(p.K + (size_t)pair * p.n * RB, (uint32_t)p.n * RB);
-    const __amdgpu_buffer_rsrc_t Vc = buffer_rsrc(p.V + (size_t)pair * p.n * RB, (uint32_t)p.n * RB);
-    const __amdgpu_buffer_rsrc_t Ks =
-        buffer_rsrc(p.proxies ? p.Kbar + (size_t)pair * p.nb * RB : p.K, p.proxies ? (uint32_t)p.nb * RB : 0u);
-    const __amdgpu_buffer_rsrc_t Vs =
-        buffer_rsrc(p.proxies ? p.Vbar + (size_t)pair * p.nb * RB : p.V, p.proxies ? (uint32_t)p.nb * RB : 0u);
-
     // The selection and this workgroup's weighted tokens are copied to LDS
     // (when they fit) after the first tile is issued; until then, and when
     // they do not fit, rows are resolved from the global arrays.
@@ -388,17 +379,33 @@ __global__ void __launch_bounds__(NW * 64) attn_mfma_kernel(const AttnParams p)
             eng.set_row(tb, lane, row, lw);
         }
     };
-    auto issue = [&](int base, typename E::Tile& t, int tb, bool masked) {
-        set_rows(base, tb, masked);
+    // Tile loads are issued unconditionally: a tile past the wave's list reads
+    // through empty buffers (zeros, no memory traffic).  Together with loops
+    // that have no exit between their halves, this lets the compiler's wait
+    // before a tile's use cover that tile's loads only.
+    // Segments are padded to whole tiles, so every tile reads either the cache
+    // (weighted and exact rows) or the summaries (proxy rows).  The buffers are
+    // built from wave-uniform base addresses and sizes.
+    const char* const kc = p.K + (size_t)pair * p.n * RB;
+    const char* const vc = p.V + (size_t)pair * p.n * RB;
+    const char* const ks = p.proxies ? p.Kbar + (size_t)pair * p.nb * RB : p.K;
+    const char* const vs = p.proxies ? p.Vbar + (size_t)pair * p.nb * RB : p.V;
+    const uint32_t cbytes = (uint32_t)p.n * RB, sbytes = p.proxies ? (uint32_t)p.nb * RB : 0u;
+    auto rsrc = [&](int base, bool live, bool keys) {
         const bool summ = base < p.wbeg;  // uniform over the wave
-        eng.issue(t, tb, summ ? Ks : Kc, summ ? Vs : Vc, true);
+        const uint32_t bytes = (uint32_t)__builtin_amdgcn_readfirstlane((int)(live ? (summ ? sbytes : cbytes) : 0u));
+        return buffer_rsrc(summ ? (keys ? ks : vs) : (keys ? kc : vc), bytes);
     };
-    auto issue_keys = [&](int base, typename E::Tile& t, int tb) {
-        set_rows(base, tb, true);
-        eng.issue_keys(t, tb, base < p.wbeg ? Ks : Kc);
+    auto issue = [&](int base, typename E::Tile& t, int tb, bool masked, bool live) {
+        if (live) set_rows(base, tb, masked);
+        eng.issue(t, tb, rsrc(base, live, true), rsrc(base, live, false), true);
     };
-    auto issue_values = [&](int base, typename E::Tile& t, int tb) {
-        eng.issue_values(t.vr, tb, base < p.wbeg ? Vs : Vc);
+    auto issue_keys = [&](int base, typename E::Tile& t, int tb, bool live) {
+        if (live) set_rows(base, tb, true);
+        eng.issue_keys(t, tb, rsrc(base, live, true));
+    };
+    auto issue_values = [&](int base, typename E::Tile& t, int tb, bool live) {
+        eng.issue_values(t.vr, tb, rsrc(base, live, false));
     };
     auto compute = [&](const typename E::Tile& t, int tb) {
         float x[8];
@@ -423,13 +430,12 @@ __global__ void __launch_bounds__(NW * 64) attn_mfma_kernel(const AttnParams p)
     const int rotC = nC ? (int)((hsh >> 16) % (uint32_t)nC) : 0;
     auto row0 = [&](int t) { return t < nP ? r0 + (t + rotP) % nP * TR : c0 + (t - nP + rotC) % nC * TR; };
 
-    // Two tiles form the software pipeline: tile t's q K^T and softmax run before
-    // tile t+1's loads are issued (so t's key registers are free again), and t's
-    // P V runs while t+1 is in flight.
     typename E::Tile A, B;
-    int t = wave;
-    const int first = t < nT ? row0(t) : r1;
-    if (t < nT) issue(first, A, 0, false);
+    // this wave's tiles: jt = 0 .. Tw - 1 at t = wave + jt NW
+    const int Tw = wave < nT ? (nT - wave + NW - 1) / NW : 0;
+    auto base_of = [&](int jt) { return jt < Tw ? row0(wave + jt * NW) : 0; };
+    const int first = Tw > 0 ? row0(wave) : r1;
+    issue(first, A, 0, false, Tw > 0);
     if (bitmap_words > 0 || sel_in_lds || tok_in_lds) {
         __syncthreads();  // bitmap cleared
         if (bitmap_words > 0 || sel_in_lds) {
@@ -459,41 +465,35 @@ __global__ void __launch_bounds__(NW * 64) attn_mfma_kernel(const AttnParams p)
             sm.tab_lw[0][wave][lane] = kNegInf;
         wave_lds_fence();
     }
-    if (t < nT) {
-        if constexpr (HG <= 4) {
-            // a tile's keys go out before the logits of the tile ahead of it,
-            // its values right after them
-            int t1 = t + NW;
-            if (t1 < nT) issue_keys(row0(t1), B, 1);
-            for (;;) {
-                compute(A, 0);
-                if (t1 < nT) issue_values(row0(t1), B, 1);
-                eng.accumulate(A);
-                if (t1 >= nT) break;
-                const int t2 = t1 + NW;
-                if (t2 < nT) issue_keys(row0(t2), A, 0);
-                compute(B, 1);
-                if (t2 < nT) issue_values(row0(t2), A, 0);
-                eng.accumulate(B);
-                if (t2 >= nT) break;
-                t1 = t2 + NW;
-                if (t1 < nT) issue_keys(row0(t1), B, 1);
-            }
-        } else {
-            for (;;) {
-                const int t1 = t + NW;
-                compute(A, 0);
-                if (t1 < nT) issue(row0(t1), B, 1, true);
-                eng.accumulate(A);
-                if (t1 >= nT) break;
-                const int t2 = t1 + NW;
-                compute(B, 1);
-                if (t2 < nT) issue(row0(t2), A, 0, true);
-                eng.accumulate(B);
-                if (t2 >= nT) break;
-                t = t2;
-            }
+    int jt = 0;
+    if constexpr (HG <= 4) {
+        // a tile's keys go out before the logits of the tile ahead of it, its
+        // values right after them
+        issue_keys(base_of(1), B, 1, 1 < Tw);
+        for (; jt + 1 < Tw; jt += 2) {
+            compute(A, 0);
+            issue_values(base_of(jt + 1), B, 1, true);
+            eng.accumulate(A);
+            issue_keys(base_of(jt + 2), A, 0, jt + 2 < Tw);
+            compute(B, 1);
+            issue_values(base_of(jt + 2), A, 0, jt + 2 < Tw);
+            eng.accumulate(B);
+            issue_keys(base_of(jt + 3), B, 1, jt + 3 < Tw);
         }
+    } else {
+        // tile jt+1's loads go out once tile jt's keys are consumed
+        for (; jt + 1 < Tw; jt += 2) {
+            compute(A, 0);
+            issue(base_of(jt + 1), B, 1, true, true);
+            eng.accumulate(A);
+            compute(B, 1);
+            issue(base_of(jt + 2), A, 0, true, jt + 2 < Tw);
+            eng.accumulate(B);
+        }
+    }
+    if (jt < Tw) {  // odd tile count: the last tile is in A
+        compute(A, 0);
+        eng.accumulate(A);
     }
     float* part = p.splits == 1 ? nullptr : p.part + (((size_t)pair * p.splits + split) * p.G + g0) * (D + 2);
     eng.finish(nh, p.out + ((size_t)b * p.Hq + h0) * D, p.lse ? p.lse + (size_t)b * p.Hq + h0 : nullptr, part);

@@ -73,11 +73,23 @@ __global__ void __launch_bounds__(kStepWaves * 64) decode_step_kernel(const Step
     const int lane = eng.lane, wave = eng.wave, n16 = eng.n16, g16 = eng.g16;
     for (int w = threadIdx.x; w < LS / 32; w += NW * 64) bits[w] = 0;
 
-    const __amdgpu_buffer_rsrc_t Kc = buffer_rsrc(p.K + (size_t)pair * p.n * RB, (uint32_t)p.n * RB);
-    const __amdgpu_buffer_rsrc_t Vc = buffer_rsrc(p.V + (size_t)pair * p.n * RB, (uint32_t)p.n * RB);
-    const __amdgpu_buffer_rsrc_t Ks = buffer_rsrc(p.Kbar + (size_t)pair * nb * RB, (uint32_t)nb * RB);
-    const __amdgpu_buffer_rsrc_t Vs =
-        buffer_rsrc(p.proxies ? p.Vbar + (size_t)pair * nb * RB : p.V, p.proxies ? (uint32_t)nb * RB : 0u);
+    // Loads are issued unconditionally: a tile that does not exist reads
+    // through an empty buffer (zeros, no memory traffic).  With loops that
+    // have no exit between their halves, this lets the compiler's wait before
+    // a tile's use cover that tile's loads only.  The buffers are built from
+    // wave-uniform base addresses and sizes.
+    const char* const kc = p.K + (size_t)pair * p.n * RB;
+    const char* const vc = p.V + (size_t)pair * p.n * RB;
+    const char* const ks = p.Kbar + (size_t)pair * nb * RB;
+    const char* const vs = p.proxies ? p.Vbar + (size_t)pair * nb * RB : p.V;
+    const uint32_t cbytes = (uint32_t)p.n * RB, sbytes = (uint32_t)nb * RB;
+    auto size = [](bool live, uint32_t bytes) {  // uniform: keeps the buffer in scalar registers
+        return (uint32_t)__builtin_amdgcn_readfirstlane((int)(live ? bytes : 0u));
+    };
+    auto Kc = [&](bool live) { return buffer_rsrc(kc, size(live, cbytes)); };
+    auto Vc = [&](bool live) { return buffer_rsrc(vc, size(live, cbytes)); };
+    auto Ks = [&](bool live) { return buffer_rsrc(ks, size(live, sbytes)); };
+    auto Vs = [&](bool live) { return buffer_rsrc(vs, size(live && p.proxies, sbytes)); };
 
     // Tile orders are rotated by a per-workgroup offset, so that workgroups
     // running side by side do not walk the same address offsets at the same
@@ -110,14 +122,10 @@ __global__ void __launch_bounds__(kStepWaves * 64) decode_step_kernel(const Step
         }
     };
     auto issue_first_proxies = [&]() {
-        if (Pw > 0) {
-            set_proxy_rows(0, 0, false);
-            eng.issue_values(VA, 0, Vs);
-        }
-        if (Pw > 1) {
-            set_proxy_rows(1, 1, false);
-            eng.issue_values(VB, 1, Vs);
-        }
+        if (Pw > 0) set_proxy_rows(0, 0, false);
+        eng.issue_values(VA, 0, Vs(Pw > 0));
+        if (Pw > 1) set_proxy_rows(1, 1, false);
+        eng.issue_values(VB, 1, Vs(Pw > 1));
     };
 
     // ---- phase 1: block logits of every head -> LDS ---------------------------
@@ -139,12 +147,13 @@ __global__ void __launch_bounds__(kStepWaves * 64) decode_step_kernel(const Step
                 }
         }
     };
-    auto load_keys = [&](int base, uint4 (&ak)[2][KS]) {
+    auto load_keys = [&](int base, uint4 (&ak)[2][KS], bool live) {
+        const __amdgpu_buffer_rsrc_t r = Ks(live);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
             const uint32_t off = (uint32_t)(base + rb * 16 + n16) * RB + g16 * 16;  // past nb: zeros
 #pragma unroll
-            for (int s = 0; s < KS; ++s) ak[rb][s] = buffer_ld16(Ks, off + s * 64);
+            for (int s = 0; s < KS; ++s) ak[rb][s] = buffer_ld16(r, off + s * 64);
         }
     };
     // The mean keys decide the selection: they have the memory system to
@@ -153,9 +162,9 @@ __global__ void __launch_bounds__(kStepWaves * 64) decode_step_kernel(const Step
     for (int t = wave; t < nK; t += 2 * NW) {  // two tiles in flight
         uint4 k0[2][KS], k1[2][KS];
         const int b0 = (t + rotK) % nK * TR, b1 = (t + NW + rotK) % nK * TR;
-        load_keys(b0, k0);
         const bool two = t + NW < nK;
-        if (two) load_keys(b1, k1);
+        load_keys(b0, k0, true);
+        load_keys(b1, k1, two);
         logits_to_lds(b0, k0);
         if (two) logits_to_lds(b1, k1);
     }
@@ -221,9 +230,9 @@ __global__ void __launch_bounds__(kStepWaves * 64) decode_step_kernel(const Step
             eng.set_row(tb, lane, row, lw);
         }
     };
-    auto issue_cache = [&](int jj, typename E::Tile& t, int tb) {
-        set_cache_rows(jj, tb);
-        eng.issue(t, tb, Kc, Vc, true);
+    auto issue_cache = [&](int jj, typename E::Tile& t, int tb, bool live) {
+        if (live) set_cache_rows(jj, tb);
+        eng.issue(t, tb, Kc(live), Vc(live), true);
     };
     auto proxy_tile = [&](int jj, const uint4 (&vr)[E::NVI], int tb) {
         float x[8];
@@ -239,50 +248,49 @@ __global__ void __launch_bounds__(kStepWaves * 64) decode_step_kernel(const Step
 
     // The selection is known: mask the selected blocks in the prefetched proxy
     // tiles and finish the proxy tiles (two value tiles in flight), then stream
-    // the cache tiles (key and value tiles, one and a half in flight).  When the
-    // wave's proxy values are all in flight already (at most two tiles), the
-    // keys of its first cache tile go out now, so that they stream behind the
-    // proxy values instead of after them; its values follow once the proxy
-    // tiles are done (the whole first tile now would not fit in registers
-    // beside them).  With more than four heads the keys wait too.
+    // the cache tiles (key and value tiles, one and a half in flight).  Up to
+    // four heads, the keys of the wave's first cache tile go out now, so that
+    // they stream behind the proxy values instead of after them; its values
+    // follow once the proxy tiles are done (the whole first tile now would not
+    // fit in registers beside them).  With more heads the keys wait too.
     if (Pw > 0) set_proxy_rows(0, 0, true);
     if (Pw > 1) set_proxy_rows(1, 1, true);
     typename E::Tile CA, CB;
     const bool any_cache = Tw > Pw;
-    const bool early_keys = HG <= 4 && any_cache && Pw <= 2;
-    if (early_keys) {
-        set_cache_rows(Pw, 2);
-        eng.issue_keys(CA, 2, Kc);
+    if constexpr (HG <= 4) {
+        if (any_cache) set_cache_rows(Pw, 2);
+        eng.issue_keys(CA, 2, Kc(any_cache));
     }
-    for (int jj = 0; jj < Pw; jj += 2) {
+    int jj = 0;
+    for (; jj + 1 < Pw; jj += 2) {
         proxy_tile(jj, VA, 0);
-        if (jj + 2 < Pw) {
-            set_proxy_rows(0, jj + 2, true);
-            eng.issue_values(VA, 0, Vs);
-        }
-        if (jj + 1 < Pw) {
-            proxy_tile(jj + 1, VB, 1);
-            if (jj + 3 < Pw) {
-                set_proxy_rows(1, jj + 3, true);
-                eng.issue_values(VB, 1, Vs);
-            }
-        }
+        if (jj + 2 < Pw) set_proxy_rows(0, jj + 2, true);
+        eng.issue_values(VA, 0, Vs(jj + 2 < Pw));
+        proxy_tile(jj + 1, VB, 1);
+        if (jj + 3 < Pw) set_proxy_rows(1, jj + 3, true);
+        eng.issue_values(VB, 1, Vs(jj + 3 < Pw));
     }
-    if (early_keys)
-        eng.issue_values(CA.vr, 2, Vc);
-    else if (any_cache)
-        issue_cache(Pw, CA, 2);
+    if (jj < Pw) proxy_tile(jj, VA, 0);  // odd count: the last proxy tile is in VA
+    if constexpr (HG <= 4) {
+        eng.issue_values(CA.vr, 2, Vc(any_cache));
+    } else {
+        issue_cache(Pw, CA, 2, any_cache);
+    }
     // cache tiles (weighted and exact rows): keys and values; the next tile's
     // loads go out once this tile's keys are consumed (one and a half tiles of
     // registers in flight)
-    for (int jj = Pw; jj < Tw; jj += 2) {
+    int jc = Pw;
+    for (; jc + 1 < Tw; jc += 2) {
         cache_logits(CA, 2);
-        if (jj + 1 < Tw) issue_cache(jj + 1, CB, 3);
+        issue_cache(jc + 1, CB, 3, true);
         eng.accumulate(CA);
-        if (jj + 1 >= Tw) break;
         cache_logits(CB, 3);
-        if (jj + 2 < Tw) issue_cache(jj + 2, CA, 2);
+        issue_cache(jc + 2, CA, 2, jc + 2 < Tw);
         eng.accumulate(CB);
+    }
+    if (jc < Tw) {  // odd count: the last cache tile is in CA
+        cache_logits(CA, 2);
+        eng.accumulate(CA);
     }
     eng.finish(G, p.out + ((size_t)b * p.Hq + h0) * D, p.lse ? p.lse + (size_t)b * p.Hq + h0 : nullptr, nullptr);
 }
