@@ -429,6 +429,10 @@ STEP_CASES = [  # B * Hkv >= 32 takes the one-kernel path
     ("mha_b8_summary", small("exact_mass_mha_b8", batch=2, n_tokens=4096, n_kv_heads=16),
      {"mode": "summary", "proxies": True}),
     ("coreset_g7_b8", small("weighted_coreset_128k", batch=8, n_tokens=8192, n_kv_heads=4).with_(coreset=300), {}),
+    # 640 blocks of 16: 20 proxy tiles (three for waves 0-3, two for the others) and 6 exact
+    # tiles, so odd and even tile counts, and waves without exact tiles, meet in one launch
+    ("llama_b8_L16_nb640", small("llama3_8b_layer_b32", batch=8, n_tokens=10240, n_kv_heads=4).with_(block_size=16),
+     {"k": 12}),
     # 1024 blocks: more than 16 mean-key tiles, so waves take more than two proxy tiles each
     ("llama_b8_8k_L8", small("llama3_8b_layer_b32", batch=8, n_tokens=8192, n_kv_heads=4).with_(block_size=8),
      {"k": 24}),
