@@ -236,4 +236,103 @@ __device__ __forceinline__ void wave_topk(Load load, int nb, int kk, int lane, u
     if (lane < kk) emit(rank, got);
 }
 
+// Top-kk of the blocks i < nb by a workgroup of NW waves, for kk <= NW: thread t
+// holds the order keys of blocks t + 64 NW j (j < SPT) in key[j].  Every wave
+// finds its largest key; the kk-th largest of the NW wave maxima (counting equal
+// maxima separately) is a lower bound tau for the kk-th largest key overall, as
+// the kk largest wave maxima belong to kk distinct blocks.  Each wave puts its
+// blocks whose keys reach tau into its 64 / NW slots of LDS (ordered by j, then
+// lane) and, when every wave's fit, wave 0 ranks each candidate against the
+// others by (key, lower index) and calls emit(r, i) in lane r < kk with the
+// r-th smallest selected index i.  When some wave has more candidates (many
+// equal scores), or kk > NW, fallback() runs in wave 0 instead.  The whole
+// workgroup must call it: it holds two workgroup barriers.  sm: 2 NW + 128
+// words of LDS; 64 / NW slots per wave.
+template <int NW, int SPT, typename Fallback, typename Emit>
+__device__ __forceinline__ void block_topk(const uint32_t (&key)[SPT], int nb, int kk, uint32_t* sm, Fallback fallback,
+                                           Emit emit)
+{
+    constexpr int T = NW * 64, CPW = 64 / NW;
+    static_assert(CPW * NW == 64, "64 candidate slots over the waves");
+    uint32_t* wmax = sm;                // [NW] largest key of each wave
+    uint32_t* over = sm + NW;           // [NW] wave has more candidates than slots
+    uint32_t* ck = sm + 2 * NW;         // [64] candidate keys, 0 for an empty slot
+    uint32_t* ci = sm + 2 * NW + 64;    // [64] candidate indices
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    uint32_t lmax = 0;  // below every real key (the key of -inf is 0x007fffff)
+#pragma unroll
+    for (int j = 0; j < SPT; ++j)
+        if ((int)threadIdx.x + T * j < nb) lmax = max(lmax, key[j]);
+    const uint32_t wm = wave_max_u32(lmax);
+    if (lane == 0) wmax[wave] = wm;
+    __syncthreads();
+    // tau: the kk-th largest wave maximum; 0 (every block a candidate) if kk > NW.
+    // Lane w < NW ranks wave w's maximum against the others.
+    uint32_t tau = 0;
+    if (kk <= NW) {
+        const uint32_t m = lane < NW ? wmax[lane] : 0u;
+        int above = 0;  // wave maxima ranked before this lane's
+#pragma unroll
+        for (int v = 0; v < NW; ++v) {
+            const uint32_t o = wmax[v];
+            above += (o > m || (o == m && v < lane)) ? 1 : 0;
+        }
+        const uint64_t at = __ballot(lane < NW && above == kk - 1);
+        tau = (uint32_t)__builtin_amdgcn_readlane((int)m, (int)__builtin_ctzll(at));
+    }
+    uint64_t cmask[SPT];
+    int mine = 0;
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+        cmask[j] = __ballot((int)threadIdx.x + T * j < nb && key[j] >= tau);
+        mine += __popcll(cmask[j]);
+    }
+    if (lane == 0) over[wave] = mine > CPW ? 1u : 0u;
+    if (mine <= CPW) {
+        if (lane >= mine && lane < CPW) {  // empty slots
+            ck[CPW * wave + lane] = 0u;
+            ci[CPW * wave + lane] = 0u;
+        }
+        int pos = CPW * wave;
+#pragma unroll
+        for (int j = 0; j < SPT; ++j) {
+            if ((cmask[j] >> lane) & 1u) {
+                ck[pos + lanes_below(cmask[j])] = key[j];
+                ci[pos + lanes_below(cmask[j])] = (uint32_t)((int)threadIdx.x + T * j);
+            }
+            pos += __popcll(cmask[j]);
+        }
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    uint32_t overflow = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) overflow |= over[w];
+    if (overflow) {
+        fallback();
+        return;
+    }
+    const uint32_t k0 = ck[lane], i0 = ci[lane];
+    const bool live = k0 != 0u;
+    int rank = 0;  // candidates ahead of this one: larger key, or equal key and lower index
+    for (uint64_t m = __ballot(live); m; m &= m - 1) {
+        const int c = (int)__builtin_ctzll(m);
+        const uint32_t kc = (uint32_t)__builtin_amdgcn_readlane((int)k0, c);
+        const uint32_t ic = (uint32_t)__builtin_amdgcn_readlane((int)i0, c);
+        rank += (kc > k0 || (kc == k0 && ic < i0)) ? 1 : 0;
+    }
+    const bool take = live && rank < kk;
+    const uint64_t tm = __ballot(take);
+    int before;  // taken candidates with a lower index
+    if constexpr (SPT == 1) {
+        before = lanes_below(tm);  // one block per thread: the slots are in index order
+    } else {
+        before = 0;
+        for (uint64_t m = tm; m; m &= m - 1)
+            before += (uint32_t)__builtin_amdgcn_readlane((int)i0, (int)__builtin_ctzll(m)) < i0 ? 1 : 0;
+    }
+    if (take) emit(before, (int)i0);
+}
+
 }  // namespace csa

@@ -13,12 +13,16 @@
 //
 // Phases of a workgroup (KV head (b, j), all G <= 8 query heads of the group):
 //   1. waves stream the mean keys in tiles of 32 rows; MFMA logits -> LDS;
-//   2. per-head log-normaliser, group score (written out if asked), top-k by
-//      one wave (packed score/index keys), selection (written out if asked),
+//   2. per-head log-normaliser; group scores (written out if asked), one or
+//      four blocks per thread; top-k from a bound on the k-th largest score
+//      (the k-th largest of the waves' maxima) and the few blocks that reach
+//      it, else by one wave over all scores; selection (written out if asked),
 //      bitmap of selected blocks;
 //   3. attention tiles: proxy rows (values only, logits from LDS, selected
 //      blocks masked), weighted rows, exact rows of the selected blocks (keys
 //      and values, MFMA logits), in the engine of attn_engine.hpp.
+#include <type_traits>
+
 #include "attn_engine.hpp"
 #include "device.hpp"
 #include "launch.hpp"
@@ -60,7 +64,8 @@ __global__ void __launch_bounds__(kStepWaves * 64) decode_step_kernel(const Step
     __shared__ typename E::Smem sm;
     __shared__ float lse_h[8];
     __shared__ int32_t sel_sm[kStepMaxK];
-    __shared__ uint32_t cand_sm[128];  // top-k candidates
+    __shared__ uint32_t cand_sm[128];          // top-k candidates of the one-wave ranking
+    __shared__ __attribute__((aligned(16))) uint32_t topk_sm[2 * NW + 128];  // wave maxima, counts, candidates
 
     const int LS = p.lstride, G = p.G, nb = p.nb;
     float* lsm = dyn;                                              // [G][LS] block logits (natural log)
@@ -179,25 +184,44 @@ __global__ void __launch_bounds__(kStepWaves * 64) decode_step_kernel(const Step
         }
         __syncthreads();
     }
-    for (int i = threadIdx.x; i < nb; i += NW * 64) {
-        const float v = G == 1 ? lsm[i] : group_score<HG>(lsm + i, LS, lse_h, G);
-        ssm[i] = v;
-        if (p.scores) p.scores[(size_t)pair * nb + i] = v;
-    }
-    __syncthreads();
+    // group scores of blocks threadIdx.x + 64 NW j, ranked by the whole
+    // workgroup (one wave-wide maximum per wave, then the few candidates that
+    // reach the kk-th largest of them); one wave ranks all scores from LDS when
+    // that bound does not apply
     const int kk = p.k;  // <= min(32, nb)
-    if (wave == 0 && kk > 0) {
+    auto emit = [&](int r, int idx) {
+        sel_sm[r] = idx;
+        if (p.sel) p.sel[(size_t)pair * kk + r] = idx;
+        atomicOr(&bits[idx >> 5], 1u << (idx & 31));
+    };
+    auto one_wave_topk = [&]() {
         auto load = [&](int i) { return ssm[i]; };
-        auto emit = [&](int r, int idx) {
-            sel_sm[r] = idx;
-            if (p.sel) p.sel[(size_t)pair * kk + r] = idx;
-            atomicOr(&bits[idx >> 5], 1u << (idx & 31));
-        };
         if (nb <= 8 * 64)
             wave_topk<8>(load, nb, kk, lane, cand_sm, emit);
         else
             wave_topk<kStepMaxBlocks / 64>(load, nb, kk, lane, cand_sm, emit);
-    }
+    };
+    auto score_and_select = [&](auto spt) {
+        constexpr int SPT = decltype(spt)::value;
+        uint32_t key[SPT];
+#pragma unroll
+        for (int j = 0; j < SPT; ++j) {
+            const int i = (int)threadIdx.x + NW * 64 * j;
+            key[j] = 0;
+            if (i < nb) {
+                const float v = G == 1 ? lsm[i] : group_score<HG>(lsm + i, LS, lse_h, G);
+                ssm[i] = v;
+                key[j] = order_key(v);
+                if (p.scores) p.scores[(size_t)pair * nb + i] = v;
+            }
+        }
+        if (kk > 0) block_topk<NW, SPT>(key, nb, kk, topk_sm, one_wave_topk, emit);
+    };
+    static_assert(kStepMaxBlocks == NW * 64 * 4, "scores of up to four blocks per thread");
+    if (nb <= NW * 64)
+        score_and_select(std::integral_constant<int, 1>{});
+    else
+        score_and_select(std::integral_constant<int, 4>{});
     __syncthreads();
 
     // ---- phase 3: attention ------------------------------------------------------
