@@ -10,6 +10,8 @@
 //       ln sum_{h in group} exp(l_hb - ln sum_b' exp(l_hb'))
 // i.e. the logarithm of the sum of per-head normalised masses, which keeps
 // the ranking of Eq. (5) and cannot underflow.
+#include <type_traits>
+
 #include "device.hpp"
 #include "launch.hpp"
 #include "select.hpp"
@@ -954,8 +956,9 @@ __global__ void __launch_bounds__(kFusedWaves * 64) score_finish_kernel(const Fu
     constexpr int NW = kFusedWaves;
     extern __shared__ float lsm[];  // [G][nb] block logits, then the scores in row 0
     __shared__ float lse_h[8];
-    __shared__ uint32_t cand[128];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __shared__ uint32_t cand[128];               // candidates of the one-wave ranking
+    __shared__ uint32_t topk_sm[2 * NW + 128];  // wave maxima, overflow flags, candidate slots
+    const int lane = threadIdx.x & 63;
     const int pair = blockIdx.x, G = p.G, nb = p.nb;
     // copy the logits in (chunks of loads issued together: one memory round trip each;
     // a chunk covers kFusedMaxLogits, so one round trip)
@@ -987,14 +990,20 @@ __global__ void __launch_bounds__(kFusedWaves * 64) score_finish_kernel(const Fu
     group_scores_in_lds<NW>(lsm, lse_h, G, nb, p.scores ? p.scores + (size_t)pair * nb : nullptr, p.parts != nullptr);
     if (p.k > 0) {
         __syncthreads();
-        if (wave == 0) {
-            int32_t* out = p.sel + (size_t)pair * p.k;
+        int32_t* out = p.sel + (size_t)pair * p.k;
+        auto emit = [&](int r, int idx) { out[r] = idx; };
+        auto one_wave_topk = [&]() {
             auto load = [&](int i) { return lsm[i]; };
-            auto emit = [&](int r, int idx) { out[r] = idx; };
             if (nb <= 8 * 64)
                 wave_topk<8>(load, nb, p.k, lane, cand, emit);
             else
                 wave_topk<kFinishMaxBlocks / 64>(load, nb, p.k, lane, cand, emit);
+        };
+        if (nb <= NW * 64) {  // the bound from the waves' maxima; one wave over more blocks
+            uint32_t key[1] = {(int)threadIdx.x < nb ? order_key(lsm[threadIdx.x]) : 0u};
+            block_topk<NW, 1>(key, nb, p.k, topk_sm, one_wave_topk, emit);
+        } else if (threadIdx.x < 64) {
+            one_wave_topk();
         }
     }
 }

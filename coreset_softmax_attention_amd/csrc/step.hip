@@ -14,10 +14,10 @@
 // Phases of a workgroup (KV head (b, j), all G <= 8 query heads of the group):
 //   1. waves stream the mean keys in tiles of 32 rows; MFMA logits -> LDS;
 //   2. per-head log-normaliser; group scores (written out if asked), one or
-//      four blocks per thread; top-k from a bound on the k-th largest score
-//      (the k-th largest of the waves' maxima) and the few blocks that reach
-//      it, else by one wave over all scores; selection (written out if asked),
-//      bitmap of selected blocks;
+//      four blocks per thread; top-k (up to 512 blocks) from a bound on the
+//      k-th largest score (the k-th largest of the waves' maxima) and the few
+//      blocks that reach it, else by one wave over all scores; selection
+//      (written out if asked), bitmap of selected blocks;
 //   3. attention tiles: proxy rows (values only, logits from LDS, selected
 //      blocks masked), weighted rows, exact rows of the selected blocks (keys
 //      and values, MFMA logits), in the engine of attn_engine.hpp.
@@ -215,7 +215,13 @@ __global__ void __launch_bounds__(kStepWaves * 64) decode_step_kernel(const Step
                 if (p.scores) p.scores[(size_t)pair * nb + i] = v;
             }
         }
-        if (kk > 0) block_topk<NW, SPT>(key, nb, kk, topk_sm, one_wave_topk, emit);
+        if (kk == 0) return;
+        if constexpr (SPT == 1) {
+            block_topk<NW, 1>(key, nb, kk, topk_sm, one_wave_topk, emit);
+        } else {  // more blocks than threads: one wave over all scores
+            __syncthreads();
+            if (wave == 0) one_wave_topk();
+        }
     };
     static_assert(kStepMaxBlocks == NW * 64 * 4, "scores of up to four blocks per thread");
     if (nb <= NW * 64)

@@ -12,7 +12,10 @@
 //      indices with key == T, so the output is ascending by index.
 // Integer histograms and scans only: the result does not depend on timing.
 //
-// Small k (k <= 32, nb <= 2048) uses one wavefront per row instead: every lane
+// Small k (k <= 8, nb <= 512) uses a workgroup of eight waves per row: each
+// wave's largest score, the k-th largest of those as a lower bound, and a rank
+// among the few scores that reach it.  Other small k (k <= 32, nb <= 2048) use
+// one wavefront per row: every lane
 // holds up to 32 packed keys (order-preserving score bits, then the inverted
 // index, so a larger key is a higher score or, on a tie, a lower index); k
 // rounds of a wave-wide maximum pick the winners, and a prefix count over the
@@ -147,10 +150,35 @@ __global__ void __launch_bounds__(256) topk_wave_kernel(const float* scores, int
     wave_topk<PER>([&](int i) { return s[i]; }, nb, k, lane, cand[wave], [&](int r, int idx) { out[r] = idx; });
 }
 
+constexpr int kBlockTopkWaves = 8;
+constexpr int kBlockTopkMaxK = kBlockTopkWaves;  // the bound from the waves' maxima needs k <= waves
+constexpr int kBlockTopkMaxBlocks = kBlockTopkWaves * 64;
+
+// One workgroup of eight waves per row (k <= 8, nb <= 512): the bound from the
+// waves' maxima, one wave over all scores when it does not apply.
+__global__ void __launch_bounds__(kBlockTopkWaves * 64) topk_block_kernel(const float* scores, int32_t* sel, int nb,
+                                                                            int k)
+{
+    constexpr int NW = kBlockTopkWaves;
+    __shared__ uint32_t cand[128];
+    __shared__ uint32_t topk_sm[2 * NW + 128];
+    const int row = blockIdx.x, lane = threadIdx.x & 63;
+    const float* s = scores + (size_t)row * nb;
+    int32_t* out = sel + (size_t)row * k;
+    uint32_t key[1] = {(int)threadIdx.x < nb ? order_key(s[threadIdx.x]) : 0u};
+    auto emit = [&](int r, int idx) { out[r] = idx; };
+    auto one_wave_topk = [&]() { wave_topk<kBlockTopkMaxBlocks / 64>([&](int i) { return s[i]; }, nb, k, lane, cand, emit); };
+    block_topk<NW, 1>(key, nb, k, topk_sm, one_wave_topk, emit);
+}
+
 }  // namespace
 
 hipError_t launch_topk(int rows, int nb, int k, const float* scores, int32_t* sel, hipStream_t st)
 {
+    if (k < nb && k <= kBlockTopkMaxK && nb <= kBlockTopkMaxBlocks) {
+        topk_block_kernel<<<dim3((unsigned)rows), dim3(kBlockTopkWaves * 64), 0, st>>>(scores, sel, nb, k);
+        return hipGetLastError();
+    }
     const int per = (nb + 63) / 64;
     if (k < nb && k <= kWaveTopkMaxK && per <= kWaveTopkMaxPer) {
         const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
