@@ -292,15 +292,16 @@ def test_topk_ties_and_sizes():
     """Generated fp32 score rows with planted ties (including +0 / -0) against the oracle's
     top-k on the same values: bit-exact."""
     rng = np.random.default_rng(50)
-    for nb in (1, 5, 64, 100, 512, 1000, 2048, 4099):
+    for nb in (1, 5, 9, 64, 100, 512, 513, 1000, 2048, 4099):
         s = rng.standard_normal((6, nb)).astype(np.float32)
         s[1] = np.round(s[1] * 2) / 2  # many exact ties
         s[2] = 0.0
         s[2, ::3] = -0.0
         s[3] = np.float32(1.5)
         s[4, : nb // 2] = np.float32(-3.0)
+        s[5] = np.arange(nb, dtype=np.float32)  # the largest scores all in the last blocks
         t = torch.from_numpy(s).cuda()
-        for k in sorted({0, 1, 2, 5, 16, nb // 2, nb - 1, nb, nb + 3}):
+        for k in sorted({0, 1, 2, 3, 5, 8, 9, 16, nb // 2, nb - 1, nb, nb + 3}):
             if k < 0:
                 continue
             got = host(csa.topk_select(t, k))
