@@ -1248,8 +1248,9 @@ hipError_t launch_logits(const Dims& s, const void* q, const void* keys, float* 
         p.chunks = (s.nb + per - 1) / per;
     }
     if (EXACT && exact_mfma_ok(s)) {
-        // blocks per workgroup: about 1024 workgroups, a few blocks per wave
-        int per = (int)(((long long)s.nb * s.pairs() + 1023) / 1024);
+        // blocks per workgroup: about 4096 workgroups (sixteen per CU; two blocks per
+        // wave at the GQA exact-mass shape: 97 us against 101 us with 1024)
+        int per = (int)(((long long)s.nb * s.pairs() + 4095) / 4096);
         per = per < kExactWaves ? kExactWaves : (per + kExactWaves - 1) / kExactWaves * kExactWaves;
         p.items_per_wg = per;
         p.chunks = (s.nb + per - 1) / per;
