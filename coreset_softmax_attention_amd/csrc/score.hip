@@ -1234,8 +1234,8 @@ hipError_t launch_logits(const Dims& s, const void* q, const void* keys, float* 
     const int hg = s.G <= 8 ? s.G : 8, hchunks = (s.G + hg - 1) / hg;
     const int items = s.pairs() * hchunks;
     if (EXACT) {
-        // blocks per workgroup: aim for >= 1024 workgroups, at least one block per wave
-        int per = (int)(((long long)s.nb * items + 1023) / 1024);
+        // blocks per workgroup: aim for >= 4096 workgroups, at least one block per wave
+        int per = (int)(((long long)s.nb * items + 4095) / 4096);
         per = per < kNW ? kNW : (per + kNW - 1) / kNW * kNW;
         p.items_per_wg = per;
         p.chunks = (s.nb + per - 1) / per;
