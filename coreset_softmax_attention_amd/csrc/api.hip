@@ -187,6 +187,18 @@ int block_score(const csa_shape* shape, csa_score_mode mode, const void* q, cons
     if (mode != CSA_SCORE_SUMMARY && mode != CSA_SCORE_EXACT_MASS && mode != CSA_SCORE_BOX && mode != CSA_SCORE_COBS2 &&
         mode != CSA_SCORE_PROXY_ERROR && mode != CSA_SCORE_COBS2_FP4)
         return fail(CSA_ERR_INVALID_ARG, "block_score: unknown mode %d", (int)mode);
+    {  // the kernels address one KV head's key rows with 32-bit offsets
+        const long long row = (long long)d.d * (d.dtype == csa::DT_F32 ? 4 : 2);
+        const long long rows_per_block = mode == CSA_SCORE_BOX || mode == CSA_SCORE_PROXY_ERROR ? 2
+                                         : mode == CSA_SCORE_COBS2                              ? 5
+                                                                                                : 1;
+        const long long key_bytes = mode == CSA_SCORE_EXACT_MASS  ? (long long)d.n * row
+                                    : mode == CSA_SCORE_COBS2_FP4 ? (long long)d.nb * CSA_COV4_BLOCK_BYTES(d.d)
+                                                                  : (long long)d.nb * rows_per_block * row;
+        if (key_bytes >= (1ll << 32))
+            return fail(CSA_ERR_UNSUPPORTED, "block_score: one KV head's keys are %lld bytes (must be below 4 GiB)",
+                        key_bytes);
+    }
     if ((mode == CSA_SCORE_COBS2 || mode == CSA_SCORE_COBS2_FP4) && !csa::fused_summary_score_ok(d))
         return fail(CSA_ERR_UNSUPPORTED, "block_score: second-order scores need bfloat16, G <= 8 and G nb <= 16384");
     if (mode == CSA_SCORE_PROXY_ERROR && !csa::fused_summary_score_ok(d))

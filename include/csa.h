@@ -210,7 +210,8 @@ int kv_var_build(const csa_shape* shape, const void* K, void* Kvar, hipStream_t 
  *          share of its estimated softmax denominator.
  * Writes scores [B, Hkv, nb].  Workspace: csa_workspace_size(shape,
  * CSA_WS_BLOCK_SCORE_SUMMARY, _EXACT_MASS, _BOX, _COBS2, _COBS2_FP4 or _PROXY_ERROR, 0, 0)
- * bytes (0 when G = 1).
+ * bytes (0 when G = 1).  One KV head's keys (K, or its summary or descriptor
+ * rows) must be below 4 GiB, else CSA_ERR_UNSUPPORTED.
  */
 int block_score(const csa_shape* shape, csa_score_mode mode, const void* q, const void* keys,
                 float* scores, void* ws, size_t ws_bytes, hipStream_t stream);

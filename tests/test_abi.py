@@ -240,3 +240,14 @@ def test_decode_step_argument_checks(L):
     assert need >= 2 * 2 * 16 * 4
     assert step(L, s, ws=None) == csa.CSA_ERR_WORKSPACE
     assert step(L, s, ws=FAKE, wsb=need - 1) == csa.CSA_ERR_WORKSPACE
+
+
+def test_block_score_rejects_keys_of_4_gib_per_kv_head(L):
+    """The scoring kernels address one KV head's key rows with 32-bit offsets."""
+    big_exact = shape(B=1, Hq=2, Hkv=1, n=1 << 24)  # 2^24 tokens x 256 B
+    assert L.block_score(ctypes.byref(big_exact), csa.CSA_SCORE_EXACT_MASS, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                         None) == csa.CSA_ERR_UNSUPPORTED
+    assert b"4 GiB" in L.csa_last_error()
+    big_box = shape(B=1, Hq=2, Hkv=1, n=1 << 23, L=1)  # 2^23 blocks x 2 rows x 256 B
+    assert L.block_score(ctypes.byref(big_box), csa.CSA_SCORE_BOX, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                         None) == csa.CSA_ERR_UNSUPPORTED
