@@ -143,6 +143,19 @@ def copy_probe(nbytes):
     print(json.dumps({"copy_probe_bytes": nbytes, "launches": 8}), flush=True)
 
 
+def step_kernels(w):
+    """Which kernels selective_decode_step runs for workload w: the library takes one kernel per
+    KV head for summary scores in bfloat16 with G <= 8, k <= 32 and nb <= 2048 when there are at
+    least 32 KV heads or each one's share is small ((proxies + k L + m) G <= 4096), else the
+    split kernels.  Used for the label of the roofline entry only."""
+    nb, k = w.n_blocks, min(w.k, w.n_blocks)
+    rows = (nb - k if w.proxies else 0) + k * w.block_size + w.coreset
+    one = (w.score_mode == "summary" and w.dtype == "bf16" and w.group <= 8 and k <= 32 and nb <= 2048
+           and (w.batch * w.n_kv_heads >= 32 or rows * w.group <= 4096))
+    return ("selective_decode_step (decode_step_kernel)" if one else
+            "selective_decode_step (the block_score, topk_select and sparse_decode_attn kernels in turn)")
+
+
 def algorithmic_bytes(w, m=0):
     """Bytes the sparse attention must move per launch (reads, writes), following the read
     accounting of the OpenAttention explainer (exact rows, proxy rows and query-side data):
@@ -398,7 +411,7 @@ def main():
         "step_vs_dense_speedup": (dense_ms / t_step) if dense_ms else None,
         "roofline": {
             "kernel": "block_score + topk_select + sparse_decode_attn (three kernels)" if box
-                      else "selective_decode_step (decode_step_kernel)",
+                      else step_kernels(w),
             "bound": "hbm",
             "achieved": step_achieved,
             "peak": 8000.0,

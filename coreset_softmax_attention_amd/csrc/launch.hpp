@@ -108,6 +108,13 @@ AttnPlan plan_attention(const Dims& s, int k, int m, int proxies, int dense);
 
 // ---- fused decode step (summary score -> top-k -> attention, one launch) ----
 constexpr int kFusedStepMinPairs = 32;  // below this, the split kernels use the GPU better
+// With fewer KV heads the one-kernel step still wins while each KV head's
+// share is small (its virtual rows times its query heads at most this much):
+// one workgroup streams it faster than four split kernels launch one after
+// another.  Measured on the 32-head / 8-KV-head layer at one and two sequences:
+// 14.2 against 19.3 us at 8K tokens, 16.6 against 19.2 us at 32K; from 64K
+// tokens (5376) and at G = 7 over 32K tokens (7168) the split kernels win.
+constexpr long kFusedStepSmallWork = 4096;
 
 struct StepInputs {
     const void* q;

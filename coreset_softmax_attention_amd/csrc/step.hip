@@ -353,10 +353,10 @@ hipError_t launch_step_d(const StepParams& p, int pairs, size_t shm, hipStream_t
 
 bool fused_step_ok(const Dims& s, int k, int m, int proxies)
 {
-    (void)m;
-    (void)proxies;
-    return s.dtype == DT_BF16 && s.G <= 8 && k <= kStepMaxK && s.nb <= kStepMaxBlocks &&
-           s.pairs() >= kFusedStepMinPairs && step_lds_bytes(s) <= (size_t)kStepMaxLdsBytes;
+    const long rows = (proxies ? (long)(s.nb - k) : 0L) + (long)k * s.L + m;  // virtual rows per KV head
+    const bool enough = s.pairs() >= kFusedStepMinPairs || rows * s.G <= kFusedStepSmallWork;
+    return s.dtype == DT_BF16 && s.G <= 8 && k <= kStepMaxK && s.nb <= kStepMaxBlocks && enough &&
+           step_lds_bytes(s) <= (size_t)kStepMaxLdsBytes;
 }
 
 hipError_t launch_decode_step(const Dims& s, const StepInputs& in, hipStream_t st)

@@ -264,9 +264,11 @@ int dense_decode_attn(const csa_shape* shape, const void* q, const void* K, cons
  * In summary mode the first-order block logit scale q_h . Kbar_b + ln c_b
  * ([COBS] Eq. (18)) is also the logit of the block's count-aware proxy ([OA]
  * "Skipping reviews...": mean logit + ln count), so where the shape allows
- * (bfloat16, G <= 8, k <= 32, nb <= 2048, B * Hkv >= 32) one kernel per KV head
- * reads Kbar once, keeps the logits on chip for both uses, selects the blocks
- * and attends; otherwise the three entry points run in turn.
+ * (bfloat16, G <= 8, k <= 32, nb <= 2048, and either B * Hkv >= 32 or a small
+ * share per KV head: (proxies + k L + m) G <= 4096 virtual rows times query
+ * heads) one kernel per KV head reads Kbar once, keeps the logits on chip for
+ * both uses, selects the blocks and attends; otherwise the three entry points
+ * run in turn.
  * keys = Kbar (SUMMARY) or K (EXACT_MASS) as for block_score (BOX, COBS2,
  * COBS2_FP4 and PROXY_ERROR scores are CSA_ERR_UNSUPPORTED here: they need Kbox, Kcov, Kcov4 or Kvar
  * besides Kbar; use the three entry points); Kbar may be NULL in EXACT_MASS

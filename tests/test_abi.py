@@ -235,11 +235,13 @@ def test_decode_step_argument_checks(L):
     assert step(L, s, kbar=None) == csa.CSA_ERR_INVALID_ARG
     assert step(L, s, ptrs=FAKE + 4) == csa.CSA_ERR_INVALID_ARG
     assert step(L, shape(d=80)) == csa.CSA_ERR_UNSUPPORTED
-    # a shape the one-kernel path does not take (B * Hkv < 32) needs the workspace
-    need = L.csa_workspace_size(ctypes.byref(s), csa.CSA_WS_SELECTIVE_DECODE_STEP, 2, 0)
-    assert need >= 2 * 2 * 16 * 4
-    assert step(L, s, ws=None) == csa.CSA_ERR_WORKSPACE
-    assert step(L, s, ws=FAKE, wsb=need - 1) == csa.CSA_ERR_WORKSPACE
+    # a shape the one-kernel path does not take (B * Hkv < 32 and a large share per KV head:
+    # (1022 proxies + 2 x 64 exact rows) x 4 heads > 4096) needs the workspace
+    big = shape(n=65536)
+    need = L.csa_workspace_size(ctypes.byref(big), csa.CSA_WS_SELECTIVE_DECODE_STEP, 2, 0)
+    assert need >= 2 * 2 * 1024 * 4
+    assert step(L, big, ws=None) == csa.CSA_ERR_WORKSPACE
+    assert step(L, big, ws=FAKE, wsb=need - 1) == csa.CSA_ERR_WORKSPACE
 
 
 def test_block_score_rejects_keys_of_4_gib_per_kv_head(L):

@@ -422,7 +422,9 @@ def gpu_step(w, data, k=None, mode=None, proxies=None):
             "lse": host(lse)}
 
 
-STEP_CASES = [  # B * Hkv >= 32 takes the one-kernel path
+# B * Hkv >= 32 takes the one-kernel path, and so does a small share per KV head
+# ((proxies + k L + m) G <= 4096); the rest runs the split kernels
+STEP_CASES = [
     ("llama_b8_4k", small("llama3_8b_layer_b32", batch=8, n_tokens=4096, n_kv_heads=4), {}),
     ("llama_b8_4k_k32", small("llama3_8b_layer_b32", batch=8, n_tokens=4096, n_kv_heads=4), {"k": 32}),
     ("llama_b8_4k_k0", small("llama3_8b_layer_b32", batch=8, n_tokens=4096, n_kv_heads=4), {"k": 0}),
@@ -440,7 +442,9 @@ STEP_CASES = [  # B * Hkv >= 32 takes the one-kernel path
     # G = 8 heads over 512 blocks: the largest logit table in LDS
     ("g8_d64_nb512", W.Workload("g8_d64_nb512", 1003, 4, 64, 8, 64, 8192, 16, "bf16", 12, "summary", True,
                                 "clusters"), {}),
-    ("few_pairs_unfused", small("llama3_8b_layer_b1", batch=2, n_tokens=4096, n_kv_heads=2), {}),
+    # four KV heads: (59 + 320) x 4 rows x heads, one kernel; with k = 16, (48 + 1024) x 4 > 4096, split
+    ("few_pairs_small_share", small("llama3_8b_layer_b1", batch=2, n_tokens=4096, n_kv_heads=2), {}),
+    ("few_pairs_unfused", small("llama3_8b_layer_b1", batch=2, n_tokens=4096, n_kv_heads=2), {"k": 16}),
     ("exact_mass_unfused", small("exact_mass_gqa_b8", batch=8, n_tokens=4096, n_kv_heads=4), {}),
 ]
 
@@ -474,22 +478,29 @@ def test_decode_step_scores_and_selection_equal_modular_path():
     assert np.abs(a["lse"] - b["lse"]).max() < 1e-5
 
 
-def test_decode_step_full_size_sampled():
-    w = W.WORKLOADS["llama3_8b_layer_b32"]
+@pytest.mark.parametrize("name", ["llama3_8b_layer_b32", "llama3_8b_layer_b1", "weighted_coreset_128k"])
+def test_decode_step_full_size_sampled(name):
+    """selective_decode_step as the benchmark calls it: one kernel per KV head at 32 sequences and
+    at one (a small share per KV head), the split kernels over 128K tokens with weighted tokens."""
+    w = W.WORKLOADS[name]
     data = W.generate(w)
     g = gpu_step(w, data)
     rng = np.random.default_rng(77)
     G = w.group
-    for b, j in sorted({(int(rng.integers(w.batch)), int(rng.integers(w.n_kv_heads))) for _ in range(4)}):
+    pairs = {(int(rng.integers(w.batch)), int(rng.integers(w.n_kv_heads))) for _ in range(4)}
+    for b, j in sorted(pairs | {(w.batch - 1, w.n_kv_heads - 1)}):
         sub = {"q": data["q"][b:b + 1, j * G:(j + 1) * G], "K": data["K"][b:b + 1, j:j + 1],
                "V": data["V"][b:b + 1, j:j + 1]}
+        if w.coreset:
+            sub["tok_idx"] = data["tok_idx"][b:b + 1, j:j + 1]
+            sub["tok_logw"] = data["tok_logw"][b:b + 1, j:j + 1]
         o = oracle_pipeline(w, sub)
         gs = {"Kbar": g["Kbar"][b:b + 1, j:j + 1], "Vbar": g["Vbar"][b:b + 1, j:j + 1],
               "score": g["score"][b:b + 1, j:j + 1], "sel": g["sel"][b:b + 1, j:j + 1],
               "out": g["out"][b:b + 1, j * G:(j + 1) * G], "lse": g["lse"][b:b + 1, j * G:(j + 1) * G]}
         if "Kbox" in g:
             gs["Kbox"] = g["Kbox"][b:b + 1, j:j + 1]
-        compare_pipelines(w, gs, o, f"step pair ({b},{j})")
+        compare_pipelines(w, gs, o, f"{name} step pair ({b},{j})")
 
 
 # ---------------------------------------------------------------------------
