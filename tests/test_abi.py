@@ -253,3 +253,26 @@ def test_block_score_rejects_keys_of_4_gib_per_kv_head(L):
     big_box = shape(B=1, Hq=2, Hkv=1, n=1 << 23, L=1)  # 2^23 blocks x 2 rows x 256 B
     assert L.block_score(ctypes.byref(big_box), csa.CSA_SCORE_BOX, FAKE, FAKE, FAKE, FAKE, 1 << 30,
                          None) == csa.CSA_ERR_UNSUPPORTED
+
+
+def test_kernels_fit_their_registers(L):
+    """No kernel spills to scratch memory (a spill in a streaming kernel costs more than its
+    loads), except the instantiations for eight query heads per KV head at d = 128 of the
+    attention and decode-step kernels, whose value accumulators alone take 64 registers per lane;
+    the decode-step and attention kernels of four heads run two waves per SIMD.  Figures from
+    the compiler's resource report, written when the library is built."""
+    import json
+    from coreset_softmax_attention_amd import build_lib
+
+    if not os.path.exists(build_lib.RESOURCES) or (os.path.getmtime(build_lib.RESOURCES) <
+                                                    os.path.getmtime(csa.library_path()) - 60):
+        build_lib.build()
+    res = json.load(open(build_lib.RESOURCES))
+    assert len(res) > 100, "resource report incomplete"
+    allowed = {"attn_mfma_kernelILi128ELi8ELi8E": 64, "decode_step_kernelILi128ELi8E": 160}
+    for name, r in res.items():
+        limit = next((v for k, v in allowed.items() if k in name), 0)
+        assert r.get("scratch_bytes_per_lane", 0) <= limit, f"{name} spills: {r}"
+    for part in ("decode_step_kernelILi128ELi4E", "attn_mfma_kernelILi128ELi4ELi8E"):
+        (name,) = [n for n in res if part in n]
+        assert res[name]["waves_per_simd"] == 2 and res[name]["scratch_bytes_per_lane"] == 0, res[name]

@@ -456,6 +456,48 @@ def test_decode_step_matches_oracle(name, w, kw):
                       oracle_pipeline(w, data, **kw), name)
 
 
+def large_nb_inputs(seed, nb, keys):
+    """One sequence, 2 KV heads of 8 query heads, d = 64, blocks of 64.  keys: "random";
+    "ties" (blocks 300, 700 and 1000 mod nb hold the same keys, pointed along their group's
+    mean query: they tie for the top score); "equal" (all keys zero: every block ties)."""
+    B, Hq, Hkv, d, L = 1, 16, 2, 64, 64
+    n = nb * L
+    data = rand_inputs(seed, B, Hq, Hkv, d, n, "bf16")
+    if keys == "random":
+        return data
+    rng = np.random.default_rng(seed + 1)
+    if keys == "equal":
+        K = np.zeros((B, Hkv, n, d), np.float32)
+    else:
+        q = (data["q"].astype(np.uint32) << 16).view(np.float32).reshape(B, Hkv, Hq // Hkv, d)
+        K = 0.1 * rng.standard_normal((B, Hkv, n, d)).astype(np.float32)
+        top = 3.0 * q.mean(axis=2)[:, :, None, :] + 0.1 * rng.standard_normal((B, Hkv, L, d))
+        for blk in sorted({700 % nb, 300 % nb, 1000 % nb}):
+            K[:, :, blk * L:(blk + 1) * L] = top
+    data["K"] = W.to_bf16_bits(K)
+    return data
+
+
+@pytest.mark.parametrize("keys", ["random", "ties", "equal"])
+@pytest.mark.parametrize("nb,k", [(600, 1), (600, 8), (1024, 3), (2048, 5), (2048, 8), (2048, 9)])
+def test_split_step_selection_beyond_512_blocks(nb, k, keys):
+    """selective_decode_step on the split kernels (2 KV heads of 8 query heads) with more than
+    512 blocks, where the group-score kernel ranks with one wave over up to 32 scores per lane:
+    candidates from the bound of the lane maxima, or rounds of wave-wide maxima when that bound
+    admits more than 64 (every block tied).  Against the oracle, and scores and selection bit for
+    bit against block_score + topk_select."""
+    w = W.Workload("large_nb", 0, 1, 16, 2, 64, nb * 64, 64, "bf16", k, "summary", True, "clusters")
+    data = large_nb_inputs(500 + nb + k, nb, keys)
+    g, m = gpu_step(w, data), gpu_pipeline(w, data)
+    assert np.array_equal(bits(g["score"]), bits(m["score"])), "scores differ from block_score"
+    assert np.array_equal(g["sel"], m["sel"]), "selection differs from topk_select"
+    if keys == "equal":
+        assert (g["sel"] == np.arange(k)).all()
+    if keys == "ties" and k == 1:
+        assert (g["sel"] == min(700 % nb, 300 % nb, 1000 % nb)).all()
+    compare_pipelines(w, g, oracle_pipeline(w, data), f"split step nb={nb} k={k} {keys}")
+
+
 @pytest.mark.parametrize("dtype,G,d,n,L", [("bf16", 3, 128, 1000, 64), ("bf16", 8, 64, 2000, 32),
                                            ("bf16", 1, 128, 700, 16)])
 def test_decode_step_shapes(dtype, G, d, n, L):
