@@ -66,17 +66,21 @@ COPY_PROBE_BYTES = 1 << 30
 TRAFFIC_KERNELS = {"decode_step": "decode_step_kernel", "sparse_decode_attn": "attn_mfma_kernel"}
 
 
-def source_hash():
-    """Hash of the HIP sources: a traffic file measured on other sources is stale."""
+def source_hash(csrc=None):
+    """Hash of the HIP sources' code (comments and whitespace dropped): a traffic file
+    measured on other code is stale."""
     import glob
     import hashlib
+    import re
 
     h = hashlib.sha256()
-    csrc = os.path.join(HERE, "coreset_softmax_attention_amd", "csrc")
+    csrc = csrc or os.path.join(HERE, "coreset_softmax_attention_amd", "csrc")
     for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.hpp"))):
         h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            code = re.sub(r"/\*.*?\*/", " ", fh.read(), flags=re.S)
+        code = re.sub(r"//[^\n]*", " ", code)
+        h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 

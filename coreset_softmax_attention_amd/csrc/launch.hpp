@@ -41,8 +41,9 @@ hipError_t launch_cov(const Dims& s, const void* K, void* Kcov, hipStream_t st);
 // kCobsRank fp32 scales and kCobsRank x d/2 bytes of E2M1 codes.
 hipError_t launch_cov4(const Dims& s, const void* K, void* Kcov4, hipStream_t st);
 // Second-order block scores from Kcov, or from Kcov4 when fp4 (bfloat16,
-// fused_summary_score_ok()); with fewer than kFusedStepMinPairs KV heads the
-// logits go through `logits` ([B, Hq, nb], or the scores themselves when G == 1).
+// fused_summary_score_ok()).  Kcov, and Kcov4 with fewer than
+// kFusedStepMinPairs KV heads, go through the tile-split kernel, whose logits
+// land in `logits` ([B, Hq, nb], or the scores themselves when G == 1).
 hipError_t launch_score_cobs2(const Dims& s, const void* q, const void* Kcov, float* logits, float* scores,
                               hipStream_t st, bool fp4 = false);
 // Mean and variance tokens Kvar [B, Hkv, nb, 2, d] of the proxy-error scores.
