@@ -16,10 +16,12 @@ NL - 1 other layers' data (about 1 GB for the default shape, four times the
 256 MB last-level cache).  The default run:
   * eager: K steps, one Python call per entry point, HIP events around the
     whole loop;
-  * graph: the NL-layer decode captured once in a HIP graph and replayed
-    (the way a serving loop runs decode), HIP events around the replays;
-  * attention only: a graph of NL sparse_decode_attn launches (one per layer),
-    for the roofline figure of that kernel on its own.
+  * graph: K decode steps (layers cycled) captured once in a HIP graph and
+    replayed (the way a serving loop runs decode); each timed window is one
+    replay, i.e. exactly K steps, started behind a GPU sleep so that the host's
+    submission is not timed; the median of --windows windows is reported;
+  * attention only: the same with K sparse_decode_attn launches, for the
+    roofline figure of that kernel on its own.
 `value` is queries/s of the graph-replayed step (one query = one sequence's
 decode token through the layer, all query heads); the roofline object is for
 the step's kernel (bytes: every mean key, the mean values of unread blocks,
@@ -45,6 +47,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default=None, help="workload name (default: the headline decode shape)")
     ap.add_argument("--layers", type=int, default=8, help="independent cache copies cycled through")
+    ap.add_argument("--windows", type=int, default=15,
+                    help="timed windows of exactly --steps graph-replayed steps each (the median is reported)")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU time budget of the oracle baseline")
@@ -312,6 +316,22 @@ def main():
         csa.selective_decode_step(q, K, V, Kbar, Vbar, w.k, w.block_size, mode=w.score_mode, proxies=w.proxies,
                                   tok_idx=tok_idx, tok_logw=tok_logw, out=out, lse=lse, ws=ws_step)
 
+    def graph_windows(g, steps, nwin):
+        """ms per step of `nwin` windows, each one replay of a graph of `steps` launches.  A GPU
+        sleep is queued before each window's start event, so the host has submitted the replay
+        before the GPU reaches it: the window holds the launches' GPU time only."""
+        out = []
+        for _ in range(nwin):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            torch.cuda._sleep(200_000)  # about 0.1 ms at the GPU clock
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            out.append(a.elapsed_time(b) / steps)
+        return out
+
     def timed(fn, reps):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -333,6 +353,7 @@ def main():
     eager_modular_ms = timed(modular, args.steps) / args.steps
 
     graph_ms = attn_ms = score_ms = modular_ms = None
+    windows = None
     if not args.no_graph:
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
@@ -342,18 +363,21 @@ def main():
                 modular(i)
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
+        # one graph per route holding exactly K launches (layers cycled); each timed window
+        # replays it once, so a window times exactly K steps
         graphs = {}
-        for name, fn in (("step", step), ("modular", modular), ("score", lambda i: score_select(layers[i])),
-                         ("attn", lambda i: attend(layers[i]))):
+        for name, fn in (("step", step), ("modular", modular), ("score", lambda i: score_select(layers[i % NL])),
+                         ("attn", lambda i: attend(layers[i % NL]))):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                for i in range(NL):
+                for i in range(args.steps):
                     fn(i)
             graphs[name] = g
-        reps = max(1, args.steps // NL)
         for g in graphs.values():
             g.replay()
-        per = {name: timed(lambda r, g=g: g.replay(), reps) / (reps * NL) for name, g in graphs.items()}
+        torch.cuda.synchronize()
+        windows = {name: graph_windows(g, args.steps, args.windows) for name, g in graphs.items()}
+        per = {name: float(np.median(v)) for name, v in windows.items()}
         graph_ms, modular_ms, score_ms, attn_ms = per["step"], per["modular"], per["score"], per["attn"]
     else:
         attn_ms = timed(lambda r: attend(layers[r % NL]), args.steps) / args.steps
@@ -387,6 +411,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "timing_detail": timing_detail(args, windows),
         "ms_per_step": t_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -439,6 +464,34 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def timing_detail(args, windows):
+    """What was timed: windows of exactly `steps` launches, median reported."""
+    if windows is None:
+        return {"mode": "eager", "timed_launches": args.steps, "windows": 1}
+    v = sorted(windows["step"])
+    pick = lambda f: v[min(len(v) - 1, int(round(f * (len(v) - 1))))]
+    return {"mode": "HIP graph of exactly `steps` launches, one replay per window, median window reported",
+            "timed_launches_per_window": args.steps, "windows": len(v), "timed_launches": args.steps * len(v),
+            "step_us": {"median": 1e3 * pick(0.5), "p10": 1e3 * pick(0.1), "p90": 1e3 * pick(0.9),
+                        "min": 1e3 * v[0], "max": 1e3 * v[-1]}}
+
+
+def cpu_model():
+    """CPU model string with family / model / stepping, and the logical CPUs in this process's affinity."""
+    info = {}
+    try:
+        for line in open("/proc/cpuinfo"):
+            if ":" in line:
+                k, v = (x.strip() for x in line.split(":", 1))
+                if k in ("model name", "cpu family", "model", "stepping", "vendor_id") and k not in info:
+                    info[k] = v
+    except OSError:
+        pass
+    return (f"{info.get('model name', '?')} ({info.get('vendor_id', '?')} family {info.get('cpu family', '?')} "
+            f"model {info.get('model', '?')} stepping {info.get('stepping', '?')}), "
+            f"{len(os.sched_getaffinity(0))} logical CPUs in the process affinity")
+
+
 def cpu_baseline(w, budget_s):
     """The fp64 oracle's decode step (block score, top-k, attention) on the host cores, on a
     bounded sample of the same workload: the first few sequences of the batch."""
@@ -463,17 +516,9 @@ def cpu_baseline(w, budget_s):
         if el >= budget_s or reps >= 100000:
             break
     cores = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
-    model = ""
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                model = line.split(":", 1)[1].strip()
-                break
-    except OSError:
-        pass
     return {"value": nseq * reps / el, "unit": "queries/s", "cores": cores, "kind": "oracle",
             "sample": f"{reps} repetitions of the decode step for the first {nseq} of {w.batch} sequences "
-                      f"({el:.1f} s, fp64, OpenMP over KV heads)", "cpu": model}
+                      f"({el:.1f} s, fp64, OpenMP over KV heads)", "cpu": cpu_model()}
 
 
 if __name__ == "__main__":

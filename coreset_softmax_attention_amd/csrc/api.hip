@@ -30,6 +30,7 @@ int hip_fail(hipError_t e, const char* where)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
 
 constexpr long long kMaxRows = 1ll << 31;
 
@@ -72,7 +73,7 @@ int check_ws(size_t need, const void* ws, size_t ws_bytes)
     if (need == 0) return CSA_OK;
     if (!ws) return fail(CSA_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
     if (ws_bytes < need) return fail(CSA_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", need, ws_bytes);
-    if (!aligned16(ws)) return fail(CSA_ERR_WORKSPACE, "workspace is not 16-byte aligned");
+    if (!aligned256(ws)) return fail(CSA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
     return CSA_OK;
 }
 

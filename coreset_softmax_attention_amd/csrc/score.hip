@@ -781,8 +781,9 @@ __global__ void __launch_bounds__(kSplitWaves * 64) score_cobs2_split_kernel(con
 }
 
 // Proxy-error logits ("OpenAttention reads 1% of the KV cache -- Count-aware
-// tail proxy": the weight error a proxy leaves is its mass times the spread of
-// the weights it hides, estimated from cached mean and variance tokens).  Rows
+// tail proxy", section "Skipping reviews without losing the verdict": a proxy's
+// weight error grows with its mass and with the spread of its block's logits,
+// here estimated from cached mean and variance tokens).  Rows
 // Kvar [.., nb, 2, d]: the mean key and the per-coordinate key variance of each
 // block.  For the tile of blocks [base, base + 32), lane (n16, g16) gets head
 // n16 of blocks base + 16 rb + 4 g16 + i from three MFMA chains: the summary

@@ -247,7 +247,8 @@ def proxy_error_logits(shape: Shape, q, Kvar):
     shat_hb = scale q_h.kbar_b + ln c_b, the log-mass of the block's count-aware proxy
     ("OpenAttention ... Count-aware tail proxy", section "Skipping reviews without losing the
     verdict": mean logit plus ln count), and the log of the proxy's estimated weight error,
-    its mass times the spread of the logits it hides (same section), shat_hb + ln sigma_hb with
+    read as the proxy mass times the standard deviation of its block's logits (same section),
+    shat_hb + ln sigma_hb with
     sigma_hb = scale sqrt(sum_t q_ht^2 var_bt), the standard deviation of the block's logits
     when its key coordinates are uncorrelated (-inf when sigma = 0).  Returns (shat, lerr),
     each [B, Hq, nb]."""

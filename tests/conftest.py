@@ -13,3 +13,10 @@ if TESTS not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    import parity_report
+
+    for line in parity_report.lines():
+        terminalreporter.write_line(line)

@@ -117,6 +117,8 @@ def test_workspace_is_checked_before_launch(L):
     assert sparse(L, s, k=5, ws=None) == csa.CSA_ERR_WORKSPACE
     assert sparse(L, s, k=5, ws=FAKE, wsb=need - 1) == csa.CSA_ERR_WORKSPACE
     assert sparse(L, s, k=5, ws=FAKE + 8, wsb=need) == csa.CSA_ERR_WORKSPACE
+    assert sparse(L, s, k=5, ws=FAKE + 128, wsb=need) == csa.CSA_ERR_WORKSPACE  # 16- but not 256-aligned
+    assert b"256-byte" in L.csa_last_error()
     dneed = L.csa_workspace_size(ctypes.byref(s), csa.CSA_WS_DENSE_DECODE_ATTN, 0, 0)
     assert dneed > 0
     assert L.dense_decode_attn(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == csa.CSA_ERR_WORKSPACE

@@ -58,3 +58,18 @@ def test_several_gpus_are_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_timing_detail_counts_what_was_timed():
+    class A:
+        steps, windows = 20, 15
+
+    d = bench.timing_detail(A, {"step": [0.025 + 0.001 * i for i in range(15)]})
+    assert d["timed_launches_per_window"] == 20 and d["windows"] == 15 and d["timed_launches"] == 300
+    assert abs(d["step_us"]["median"] - 32.0) < 1e-9 and d["step_us"]["min"] == 25.0
+    assert bench.timing_detail(A, None) == {"mode": "eager", "timed_launches": 20, "windows": 1}
+
+
+def test_cpu_model_names_family_and_affinity():
+    s = bench.cpu_model()
+    assert "family" in s and "logical CPUs" in s

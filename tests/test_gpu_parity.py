@@ -6,15 +6,17 @@ Bars (written here; each follows from fp32 accumulation against the fp64 oracle)
     binary32 inputs (fp32 accumulation against fp64);
   * lse: |lse - lse_ref| <= 1e-3 (bfloat16) / 1e-5 (binary32);
   * scores: |s - s_ref| <= 1e-4 + 1e-5 |s_ref| (fp32 dot products and log-sum-exp).
-A selection row whose oracle margin (k-th minus (k+1)-th score) is below the score bound may
-legitimately differ between fp32 and fp64; there only the near-tied blocks may differ.
+A selection row is near-tied when its oracle margin s_(k) - s_(k+1) is below that same score
+bound at s_(k): there the fp32 scores may order the two sides of the boundary either way.  Only
+near-tied rows may select differently, and only among blocks whose oracle scores lie within the
+bound of s_(k).  Every near-tied row is recorded (parity_report) and printed at the end of the
+run, with whether its selection differs.
 """
-import zlib
-
 import numpy as np
 import pytest
 import torch
 
+import parity_report
 from coreset_softmax_attention_amd import csa
 from coreset_softmax_attention_amd import workloads as W
 from oracle import oracle as O
@@ -24,7 +26,11 @@ pytestmark = pytest.mark.gpu
 OUT_TOL = {"bf16": 2e-3, "f32": 1e-5}
 LSE_TOL = {"bf16": 1e-3, "f32": 1e-5}
 SCORE_ATOL, SCORE_RTOL = 1e-4, 1e-5
-MARGIN = 1e-3  # selection rows with a smaller oracle margin count as near-ties
+
+
+def score_bound(s):
+    """The asserted score error at oracle score s."""
+    return SCORE_ATOL + SCORE_RTOL * np.abs(s)
 
 
 def dev(a):
@@ -60,29 +66,42 @@ def assert_out(out, lse, ref_out, ref_lse, dtype, what=""):
 
 
 def assert_scores(s, ref, what=""):
+    """Scores within the bound; returns the largest error as a fraction of its bound."""
     s, ref = np.asarray(s, np.float64), np.asarray(ref, np.float64)
     same_inf = np.isinf(s) & (s == ref)  # -inf: a block whose proxy leaves no error
     with np.errstate(invalid="ignore"):
-        bad = ~same_inf & ~(np.abs(s - ref) <= SCORE_ATOL + SCORE_RTOL * np.abs(ref))
-    assert not bad.any(), f"{what}: {bad.sum()} scores off, max err {np.abs(s - ref).max():.3e}"
+        err = np.where(same_inf, 0.0, np.abs(s - ref))
+        bad = ~(err <= score_bound(np.where(same_inf, 0.0, ref)))
+    assert not bad.any(), f"{what}: {bad.sum()} scores off, max err {np.nanmax(err):.3e}"
+    return float((err / score_bound(np.where(same_inf, 0.0, ref))).max()) if err.size else 0.0
 
 
-def assert_selection(sel, ref_sel, ref_score, margin, k, what=""):
+def assert_selection(sel, ref_sel, ref_score, margin, what="", score_err=None):
+    """Bit-exact selection except in near-tied rows; records every near-tied row."""
     if ref_sel.shape[-1] == 0:
         assert np.asarray(sel).size == 0, f"{what}: k = 0 selected blocks"
         return
-    sel = np.asarray(sel).reshape(-1, ref_sel.shape[-1])
+    kk = ref_sel.shape[-1]
+    sel = np.asarray(sel).reshape(-1, kk)
     ref_sel = ref_sel.reshape(sel.shape)
-    ref_score = ref_score.reshape(sel.shape[0], -1)
+    ref_score = np.asarray(ref_score, np.float64).reshape(sel.shape[0], -1)
     margin = np.asarray(margin).reshape(-1)
+    kth = -np.sort(-ref_score, axis=1)[:, kk - 1]  # the oracle's k-th largest score per row
+    bound = score_bound(kth)
+    near = []
     for r in range(sel.shape[0]):
         assert np.all(np.diff(sel[r]) > 0), f"{what}: row {r} not strictly ascending"
-        if np.array_equal(sel[r], ref_sel[r]):
+        same = np.array_equal(sel[r], ref_sel[r])
+        tied = bool(margin[r] < bound[r])
+        if tied:
+            near.append((r, float(margin[r]), float(bound[r]), not same))
+        if same:
             continue
-        assert margin[r] < MARGIN, f"{what}: row {r} differs with margin {margin[r]:.3e}: {sel[r]} vs {ref_sel[r]}"
-        kth = np.sort(ref_score[r])[::-1][len(ref_sel[r]) - 1]
+        assert tied, f"{what}: row {r} differs with margin {margin[r]:.3e} >= {bound[r]:.3e}: " \
+                     f"{sel[r]} vs {ref_sel[r]}"
         for blk in set(sel[r].tolist()) ^ set(ref_sel[r].tolist()):
-            assert abs(ref_score[r, blk] - kth) < MARGIN, f"{what}: row {r} block {blk} is not near-tied"
+            assert abs(ref_score[r, blk] - kth[r]) < bound[r], f"{what}: row {r} block {blk} is not near-tied"
+    parity_report.add(what, sel.shape[0], near, score_err)
 
 
 # ---------------------------------------------------------------------------
@@ -149,8 +168,8 @@ def compare_pipelines(w, g, o, what):
         assert np.array_equal(bits(g["Kbox"]), bits(o["Kbox"])), f"{what}: Kbox not bit-exact"
     if "Kvar" in o:
         assert np.array_equal(bits(g["Kvar"]), bits(o["Kvar"])), f"{what}: Kvar not bit-exact"
-    assert_scores(g["score"], o["score"], what)
-    assert_selection(g["sel"], o["sel"], o["score"], o["margin"], w.k, what)
+    err = assert_scores(g["score"], o["score"], what)
+    assert_selection(g["sel"], o["sel"], o["score"], o["margin"], what, err)
     assert_out(g["out"], g["lse"], o["out"], o["lse"], w.dtype, what)
 
 
@@ -326,36 +345,29 @@ def test_invalid_arguments_raise():
 
 # ---------------------------------------------------------------------------
 # the full-size workloads, in the launch configuration the benchmark times;
-# the oracle recomputes a seeded sample of KV heads
+# the oracle recomputes every (b, KV head) pair
 # ---------------------------------------------------------------------------
 
 FULL = ["llama3_8b_layer_b1", "llama3_8b_layer_b32", "exact_mass_mha_b8", "exact_mass_gqa_b8",
-        "weighted_coreset_128k", "llama3_8b_layer_b32_box"]
+        "weighted_coreset_128k", "llama3_8b_layer_b32_box", "llama3_8b_layer_b32_err"]
 
 
 @pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled(name):
+def test_full_size_all_pairs(name):
+    """Every (b, KV head) pair of the full-size workload: summaries (and box or variance
+    tokens) bit for bit, scores within the bound, selections bit for bit outside near-tied
+    rows, outputs per row; through the three entry points and, for the summary and
+    exact-mass scores, through selective_decode_step as the benchmark calls it."""
     w = W.WORKLOADS[name]
     data = W.generate(w)
+    o = oracle_pipeline(w, data)
     g = gpu_pipeline(w, data)
     assert np.isfinite(g["out"]).all() and np.isfinite(g["lse"]).all()
-    rng = np.random.default_rng(zlib.crc32(name.encode()))
-    pairs = {(int(rng.integers(w.batch)), int(rng.integers(w.n_kv_heads))) for _ in range(4)}
-    pairs |= {(w.batch - 1, w.n_kv_heads - 1)}
-    G = w.group
-    for b, j in sorted(pairs):
-        sub = {"q": data["q"][b:b + 1, j * G:(j + 1) * G], "K": data["K"][b:b + 1, j:j + 1],
-               "V": data["V"][b:b + 1, j:j + 1]}
-        if w.coreset:
-            sub["tok_idx"] = data["tok_idx"][b:b + 1, j:j + 1]
-            sub["tok_logw"] = data["tok_logw"][b:b + 1, j:j + 1]
-        o = oracle_pipeline(w, sub)
-        gs = {"Kbar": g["Kbar"][b:b + 1, j:j + 1], "Vbar": g["Vbar"][b:b + 1, j:j + 1],
-              "score": g["score"][b:b + 1, j:j + 1], "sel": g["sel"][b:b + 1, j:j + 1],
-              "out": g["out"][b:b + 1, j * G:(j + 1) * G], "lse": g["lse"][b:b + 1, j * G:(j + 1) * G]}
-        if "Kbox" in g:
-            gs["Kbox"] = g["Kbox"][b:b + 1, j:j + 1]
-        compare_pipelines(w, gs, o, f"{name} pair ({b},{j})")
+    compare_pipelines(w, g, o, f"{name} (three entry points)")
+    if w.score_mode in ("summary", "exact_mass"):
+        st = gpu_step(w, data)
+        compare_pipelines(w, st, o, f"{name} (selective_decode_step)")
+        assert np.array_equal(st["sel"], g["sel"]), f"{name}: the step and the three calls select differently"
 
 
 def test_graph_replay_matches_eager():
@@ -520,31 +532,6 @@ def test_decode_step_scores_and_selection_equal_modular_path():
     assert np.abs(a["lse"] - b["lse"]).max() < 1e-5
 
 
-@pytest.mark.parametrize("name", ["llama3_8b_layer_b32", "llama3_8b_layer_b1", "weighted_coreset_128k"])
-def test_decode_step_full_size_sampled(name):
-    """selective_decode_step as the benchmark calls it: one kernel per KV head at 32 sequences and
-    at one (a small share per KV head), the split kernels over 128K tokens with weighted tokens."""
-    w = W.WORKLOADS[name]
-    data = W.generate(w)
-    g = gpu_step(w, data)
-    rng = np.random.default_rng(77)
-    G = w.group
-    pairs = {(int(rng.integers(w.batch)), int(rng.integers(w.n_kv_heads))) for _ in range(4)}
-    for b, j in sorted(pairs | {(w.batch - 1, w.n_kv_heads - 1)}):
-        sub = {"q": data["q"][b:b + 1, j * G:(j + 1) * G], "K": data["K"][b:b + 1, j:j + 1],
-               "V": data["V"][b:b + 1, j:j + 1]}
-        if w.coreset:
-            sub["tok_idx"] = data["tok_idx"][b:b + 1, j:j + 1]
-            sub["tok_logw"] = data["tok_logw"][b:b + 1, j:j + 1]
-        o = oracle_pipeline(w, sub)
-        gs = {"Kbar": g["Kbar"][b:b + 1, j:j + 1], "Vbar": g["Vbar"][b:b + 1, j:j + 1],
-              "score": g["score"][b:b + 1, j:j + 1], "sel": g["sel"][b:b + 1, j:j + 1],
-              "out": g["out"][b:b + 1, j * G:(j + 1) * G], "lse": g["lse"][b:b + 1, j * G:(j + 1) * G]}
-        if "Kbox" in g:
-            gs["Kbox"] = g["Kbox"][b:b + 1, j:j + 1]
-        compare_pipelines(w, gs, o, f"{name} step pair ({b},{j})")
-
-
 # ---------------------------------------------------------------------------
 # second-order (COBS) descriptors and scores
 # ---------------------------------------------------------------------------
@@ -602,10 +589,10 @@ def cobs2_case(w, data, k=None, proxies=True):
     out, lse = csa.sparse_decode_attn(q, K, V, Kbar, Vbar, sel, w.block_size, proxies=proxies)
     torch.cuda.synchronize()
     g = {"Kbar": host(Kbar), "Vbar": host(Vbar), "score": host(scores), "sel": host(sel), "out": host(out),
-         "lse": host(lse)}
+         "lse": host(lse), "Kcov": host(Kcov)}
     shp = oshape(w, B=data["q"].shape[0], Hkv=data["K"].shape[1])
     Kbar_o, Vbar_o = O.kv_summary_build(shp, data["K"], data["V"])
-    score = O.group_score(shp, O.cobs2_logits(shp, data["q"], host(Kcov)))
+    score = O.group_score(shp, O.cobs2_logits(shp, data["q"], g["Kcov"]))
     sel_o, margin = O.topk_select(score, k)
     out_o, lse_o = O.sparse_decode_attn(shp, data["q"], data["K"], data["V"], Kbar_o, Vbar_o, sel_o, proxies)
     o = {"Kbar": Kbar_o, "Vbar": Vbar_o, "score": score, "sel": sel_o, "margin": margin, "out": out_o, "lse": lse_o}
@@ -676,37 +663,14 @@ def test_cobs2_fp4_pipeline_matches_oracle(B, Hkv, G, n, L, k, d):
     compare_pipelines(w, g, o, f"cobs2 fp4 B={B} Hkv={Hkv} G={G} n={n} L={L} d={d}")
 
 
-def test_cobs2_fp4_full_size_sampled():
-    """The headline shape with FP4 second-order scores, as the benchmark runs it; the
-    oracle scores a seeded sample of KV heads from the stored FP4 descriptors."""
+def test_cobs2_fp4_full_size_all_pairs():
+    """The headline shape with FP4 second-order scores, as the benchmark runs it; the oracle
+    scores every (b, KV head) pair from the stored FP4 descriptors."""
     w = W.WORKLOADS["llama3_8b_layer_b32_cobs2_fp4"]
     data = W.generate(w)
-    q, K, V = dev(data["q"]), dev(data["K"]), dev(data["V"])
-    Kbar, Vbar = csa.kv_summary_build(K, V, w.block_size)
-    Kcov4 = csa.kv_cov4_build(K, w.block_size)
-    scores = csa.block_score(q, Kcov4, "cobs2_fp4", w.block_size, n_tokens=w.n_tokens)
-    sel = csa.topk_select(scores, w.k)
-    out, lse = csa.sparse_decode_attn(q, K, V, Kbar, Vbar, sel, w.block_size, proxies=True)
-    torch.cuda.synchronize()
-    k4, sc, sl, o_, l_ = host(Kcov4), host(scores), host(sel), host(out), host(lse)
-    assert np.isfinite(o_).all() and np.isfinite(l_).all()
-    rng = np.random.default_rng(zlib.crc32(w.name.encode()))
-    pairs = {(int(rng.integers(w.batch)), int(rng.integers(w.n_kv_heads))) for _ in range(3)}
-    G = w.group
-    for b, j in sorted(pairs):
-        sub = {"q": data["q"][b:b + 1, j * G:(j + 1) * G], "K": data["K"][b:b + 1, j:j + 1],
-               "V": data["V"][b:b + 1, j:j + 1]}
-        shp = oshape(w, B=1, Hkv=1)
-        Kbar_o, Vbar_o = O.kv_summary_build(shp, sub["K"], sub["V"])
-        score = O.group_score(shp, O.cobs2_fp4_logits(shp, sub["q"], k4[b:b + 1, j:j + 1]))
-        sel_o, margin = O.topk_select(score, w.k)
-        out_o, lse_o = O.sparse_decode_attn(shp, sub["q"], sub["K"], sub["V"], Kbar_o, Vbar_o, sel_o, True)
-        g = {"Kbar": host(Kbar)[b:b + 1, j:j + 1], "Vbar": host(Vbar)[b:b + 1, j:j + 1],
-             "score": sc[b:b + 1, j:j + 1], "sel": sl[b:b + 1, j:j + 1], "out": o_[b:b + 1, j * G:(j + 1) * G],
-             "lse": l_[b:b + 1, j * G:(j + 1) * G]}
-        o = {"Kbar": Kbar_o, "Vbar": Vbar_o, "score": score, "sel": sel_o, "margin": margin, "out": out_o,
-             "lse": lse_o}
-        compare_pipelines(w, g, o, f"cobs2 fp4 full pair ({b},{j})")
+    g, o = cobs2_fp4_case(w, data)
+    assert np.isfinite(g["out"]).all() and np.isfinite(g["lse"]).all()
+    compare_pipelines(w, g, o, "cobs2 fp4 full size")
 
 
 @pytest.mark.parametrize("mode", ["proxy_error", "cobs2_fp4", "box"])
@@ -761,39 +725,59 @@ def test_cobs2_needs_bfloat16():
         csa.block_score(dev(data["q"]), Kcov, "cobs2", w.block_size, n_tokens=w.n_tokens)
 
 
-def test_cobs2_full_size_sampled():
-    """The headline shape with second-order scores, as the benchmark runs it; the oracle
-    recomputes a seeded sample of KV heads (descriptors for one of them)."""
+def test_cobs2_full_size_all_pairs():
+    """The headline shape with second-order scores, as the benchmark runs it; the oracle scores
+    every (b, KV head) pair from the stored descriptors and checks one pair's descriptors
+    against its own eigen-solve."""
     w = W.WORKLOADS["llama3_8b_layer_b32_cobs2"]
     data = W.generate(w)
-    q, K, V = dev(data["q"]), dev(data["K"]), dev(data["V"])
-    Kbar, Vbar = csa.kv_summary_build(K, V, w.block_size)
-    Kcov = csa.kv_cov_build(K, w.block_size)
-    scores = csa.block_score(q, Kcov, "cobs2", w.block_size, n_tokens=w.n_tokens)
-    sel = csa.topk_select(scores, w.k)
-    out, lse = csa.sparse_decode_attn(q, K, V, Kbar, Vbar, sel, w.block_size, proxies=True)
+    g, o = cobs2_case(w, data)
+    assert np.isfinite(g["out"]).all() and np.isfinite(g["lse"]).all()
+    compare_pipelines(w, g, o, "cobs2 full size")
+    b, j = w.batch - 1, w.n_kv_heads - 1
+    check_cov_descriptors(g["Kcov"][b:b + 1, j:j + 1], data["K"][b:b + 1, j:j + 1], oshape(w, B=1, Hkv=1),
+                          f"pair ({b},{j})", 2e-2)
+
+
+@pytest.mark.parametrize("fp4", [False, True], ids=["bf16", "fp4"])
+def test_cobs2_end_to_end_selection_agreement(fp4):
+    """Second-order ranking from the raw keys on both sides: the GPU builds its descriptors
+    (fp32 eigen-solve, bfloat16 or FP4 storage) and ranks with them; the oracle builds its own
+    (fp64 eigen-solve, the same storage) and ranks with those.  Eigenvectors differ in their
+    last bits, so the selections are compared as a whole: the fraction of (b, KV head) rows that
+    agree is reported, and a row may disagree only where the score change that the descriptor
+    difference itself causes (the oracle's scores from the GPU's descriptors against those from
+    its own) reaches the row's margin."""
+    w = small("llama3_8b_layer_b32_cobs2", batch=4, n_tokens=4096)  # 32 rows of 64 blocks
+    data = W.generate(w)
+    shp = oshape(w)
+    q, K = dev(data["q"]), dev(data["K"])
+    mode = "cobs2_fp4" if fp4 else "cobs2"
+    desc = (csa.kv_cov4_build if fp4 else csa.kv_cov_build)(K, w.block_size)
+    sel_g = host(csa.topk_select(csa.block_score(q, desc, mode, w.block_size, n_tokens=w.n_tokens), w.k))
     torch.cuda.synchronize()
-    kc, sc, sl, o_, l_ = host(Kcov), host(scores), host(sel), host(out), host(lse)
-    assert np.isfinite(o_).all() and np.isfinite(l_).all()
-    rng = np.random.default_rng(zlib.crc32(w.name.encode()))
-    pairs = {(int(rng.integers(w.batch)), int(rng.integers(w.n_kv_heads))) for _ in range(3)}
-    G = w.group
-    for i, (b, j) in enumerate(sorted(pairs)):
-        sub = {"q": data["q"][b:b + 1, j * G:(j + 1) * G], "K": data["K"][b:b + 1, j:j + 1],
-               "V": data["V"][b:b + 1, j:j + 1]}
-        shp = oshape(w, B=1, Hkv=1)
-        if i == 0:
-            check_cov_descriptors(kc[b:b + 1, j:j + 1], sub["K"], shp, f"pair ({b},{j})", 2e-2)
-        Kbar_o, Vbar_o = O.kv_summary_build(shp, sub["K"], sub["V"])
-        score = O.group_score(shp, O.cobs2_logits(shp, sub["q"], kc[b:b + 1, j:j + 1]))
-        sel_o, margin = O.topk_select(score, w.k)
-        out_o, lse_o = O.sparse_decode_attn(shp, sub["q"], sub["K"], sub["V"], Kbar_o, Vbar_o, sel_o, True)
-        g = {"Kbar": host(Kbar)[b:b + 1, j:j + 1], "Vbar": host(Vbar)[b:b + 1, j:j + 1],
-             "score": sc[b:b + 1, j:j + 1], "sel": sl[b:b + 1, j:j + 1], "out": o_[b:b + 1, j * G:(j + 1) * G],
-             "lse": l_[b:b + 1, j * G:(j + 1) * G]}
-        o = {"Kbar": Kbar_o, "Vbar": Vbar_o, "score": score, "sel": sel_o, "margin": margin, "out": out_o,
-             "lse": lse_o}
-        compare_pipelines(w, g, o, f"cobs2 full pair ({b},{j})")
+    desc_g = host(desc)
+    desc_o = O.cov_build(shp, data["K"])
+    if fp4:
+        desc_o = O.cov4_pack(shp, desc_o)
+    logits = O.cobs2_fp4_logits if fp4 else O.cobs2_logits
+    score_o = O.group_score(shp, logits(shp, data["q"], desc_o))
+    score_x = O.group_score(shp, logits(shp, data["q"], desc_g))
+    sel_o, margin = O.topk_select(score_o, w.k)
+    rows = sel_o.shape[0] * sel_o.shape[1]
+    sel_o, sel_g = sel_o.reshape(rows, -1), sel_g.reshape(rows, -1)
+    pert = np.abs(score_x - score_o).reshape(rows, -1).max(axis=1)
+    kth = -np.sort(-score_o.reshape(rows, -1), axis=1)[:, w.k - 1]
+    margin = margin.reshape(-1)
+    differ = [r for r in range(rows) if not np.array_equal(sel_o[r], sel_g[r])]
+    parity_report.note(f"second-order ranking end to end ({mode}, descriptors built on each side): "
+                       f"{rows - len(differ)} of {rows} rows select the same blocks")
+    for r in differ:
+        parity_report.note(f"  row {r}: margin {margin[r]:.3e}, score change from the descriptor difference "
+                           f"{pert[r]:.3e}")
+        assert margin[r] <= 2 * pert[r] + 2 * score_bound(kth[r]), \
+            f"{mode}: row {r} disagrees with margin {margin[r]:.3e} beyond the descriptor change {pert[r]:.3e}"
+    assert len(differ) <= rows // 4, f"{mode}: {len(differ)} of {rows} rows disagree"
 
 
 @pytest.mark.parametrize("mode", ["summary", "exact_mass"])
@@ -862,30 +846,3 @@ def test_proxy_error_needs_bfloat16():
     Kvar = csa.kv_var_build(dev(data["K"]), w.block_size)
     with pytest.raises(csa.CsaError, match="bfloat16"):
         csa.block_score(dev(data["q"]), Kvar, "proxy_error", w.block_size, n_tokens=w.n_tokens)
-
-
-def test_proxy_error_full_size_sampled():
-    """The headline shape ranked by estimated proxy error, as the benchmark runs it; the
-    oracle recomputes a seeded sample of KV heads end to end."""
-    w = W.WORKLOADS["llama3_8b_layer_b32_err"]
-    data = W.generate(w)
-    q, K, V = dev(data["q"]), dev(data["K"]), dev(data["V"])
-    Kbar, Vbar = csa.kv_summary_build(K, V, w.block_size)
-    Kvar = csa.kv_var_build(K, w.block_size)
-    scores = csa.block_score(q, Kvar, "proxy_error", w.block_size, n_tokens=w.n_tokens)
-    sel = csa.topk_select(scores, w.k)
-    out, lse = csa.sparse_decode_attn(q, K, V, Kbar, Vbar, sel, w.block_size, proxies=True)
-    torch.cuda.synchronize()
-    kv, sc, sl, o_, l_ = host(Kvar), host(scores), host(sel), host(out), host(lse)
-    assert np.isfinite(o_).all() and np.isfinite(l_).all()
-    rng = np.random.default_rng(zlib.crc32(w.name.encode()))
-    pairs = {(int(rng.integers(w.batch)), int(rng.integers(w.n_kv_heads))) for _ in range(3)}
-    G = w.group
-    for b, j in sorted(pairs):
-        sub = {"q": data["q"][b:b + 1, j * G:(j + 1) * G], "K": data["K"][b:b + 1, j:j + 1],
-               "V": data["V"][b:b + 1, j:j + 1]}
-        o = oracle_pipeline(w, sub)
-        g = {"Kbar": host(Kbar)[b:b + 1, j:j + 1], "Vbar": host(Vbar)[b:b + 1, j:j + 1],
-             "Kvar": kv[b:b + 1, j:j + 1], "score": sc[b:b + 1, j:j + 1], "sel": sl[b:b + 1, j:j + 1],
-             "out": o_[b:b + 1, j * G:(j + 1) * G], "lse": l_[b:b + 1, j * G:(j + 1) * G]}
-        compare_pipelines(w, g, o, f"proxy error full pair ({b},{j})")
