@@ -78,7 +78,10 @@ _SIGS = {
     "dense_decode_attn": [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _SZ, _P],
     "selective_decode_step": [ctypes.POINTER(Shape), ctypes.c_int, _P, _P, _P, _P, _P, _I32, _P, _P, _I32,
                               ctypes.c_int, _P, _P, _P, _P, _P, _SZ, _P],
+    "selective_decode_step_noalloc": [ctypes.POINTER(Shape), ctypes.c_int, _P, _P, _P, _P, _P, _I32, _P, _P, _I32,
+                                      ctypes.c_int, _P, _P, _P, _P, _P],
 }
+CSA_STEP_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def library_path() -> str:
@@ -316,6 +319,26 @@ def selective_decode_step(q, K, V, Kbar, Vbar, k: int, block_size: int, mode: st
                                        CSA_PROXY_COMPLEMENT if proxies else CSA_PROXY_NONE, _ptr(scores),
                                        _ptr(sel), _ptr(out), _ptr(lse), _ptr(ws), wsb, _stream(dev)),
            "selective_decode_step")
+    return out, lse, scores, sel
+
+
+def selective_decode_step_noalloc(q, K, V, Kbar, Vbar, k: int, block_size: int, mode: str = "summary",
+                                  proxies: bool = True, tok_idx=None, tok_logw=None, scale: float = 0.0,
+                                  scores=None, sel=None, out=None, lse=None):
+    """selective_decode_step without a workspace: the library's static per-GPU scratch serves
+    instead (calls overlapping on one GPU race).  All outputs must be given (nothing is
+    allocated here either, so the call can sit inside a capture that forbids allocation);
+    scores and sel may be None.  Returns (out, lse, scores, sel)."""
+    dev = _dev(q, K, V, Kbar, Vbar, tok_idx, tok_logw)
+    if out is None or lse is None:
+        raise ValueError("selective_decode_step_noalloc: out and lse must be given")
+    shape = make_shape(q, K, block_size, scale)
+    m = tok_idx.shape[-1] if tok_idx is not None else 0
+    _check(lib().selective_decode_step_noalloc(ctypes.byref(shape), MODES[mode], _ptr(q), _ptr(K), _ptr(V),
+                                               _ptr(Kbar), _ptr(Vbar), k, _ptr(tok_idx), _ptr(tok_logw), m,
+                                               CSA_PROXY_COMPLEMENT if proxies else CSA_PROXY_NONE, _ptr(scores),
+                                               _ptr(sel), _ptr(out), _ptr(lse), _stream(dev)),
+           "selective_decode_step_noalloc")
     return out, lse, scores, sel
 
 

@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "../../include/csa.h"
 #include "device.hpp"
 #include "launch.hpp"
@@ -117,6 +119,123 @@ StepWs step_ws(const csa::Dims& d, int k, int m)
     w.attn_ws = align256(a > b ? a : b);
     w.total = w.scores + w.sel + w.score_ws + w.attn_ws;
     return w;
+}
+
+// ---- the static scratch of selective_decode_step_noalloc ---------------------
+
+constexpr size_t kScratchBytes = (size_t)CSA_STEP_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each GPU, set on first use
+
+}  // namespace
+
+// Scratch of the allocation-free decode step: one copy per GPU, held by the
+// loaded code object until the process ends.  In host code `scratch` names a
+// host-side stand-in, never the device memory: its device address comes from
+// hipGetSymbolAddress (scratch_of_current_device) and only that address is
+// passed to kernels.
+static __device__ __align__(256) unsigned char scratch[CSA_STEP_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// Device address of the current GPU's scratch, looked up once per GPU with that
+// GPU current.
+int scratch_of_current_device(void** out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "selective_decode_step_noalloc: hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(CSA_ERR_UNSUPPORTED, "selective_decode_step_noalloc: device %d (at most %d devices)", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "selective_decode_step_noalloc: hipGetSymbolAddress");
+        if (!p || !aligned256(p))
+            return fail(CSA_ERR_HIP, "selective_decode_step_noalloc: scratch address %p is not 256-byte aligned", p);
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return CSA_OK;
+}
+
+// The decode step.  get_ws(need, &ws, &ws_bytes) supplies the workspace of the
+// three-kernel route once the arguments are valid (need > 0 only there).
+template <typename GetWs>
+int step_impl(const csa_shape* shape, csa_score_mode mode, const void* q, const void* K, const void* V,
+              const void* Kbar, const void* Vbar, int32_t k, const int32_t* tok_idx, const float* tok_logw, int32_t m,
+              csa_proxy_mode proxy_mode, float* scores, int32_t* sel, float* out, float* lse, GetWs get_ws,
+              hipStream_t stream)
+{
+    csa::Dims d;
+    if (int rc = make_dims(shape, &d)) return rc;
+    if (mode == CSA_SCORE_BOX || mode == CSA_SCORE_COBS2 || mode == CSA_SCORE_PROXY_ERROR ||
+        mode == CSA_SCORE_COBS2_FP4)
+        return fail(CSA_ERR_UNSUPPORTED, "selective_decode_step: box, second-order and proxy-error scores need "
+                                         "Kbox, Kcov or Kvar; call block_score, topk_select and sparse_decode_attn");
+    if (mode != CSA_SCORE_SUMMARY && mode != CSA_SCORE_EXACT_MASS)
+        return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: unknown mode %d", (int)mode);
+    if (proxy_mode != CSA_PROXY_NONE && proxy_mode != CSA_PROXY_COMPLEMENT)
+        return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: unknown proxy mode %d", (int)proxy_mode);
+    const int proxies = proxy_mode == CSA_PROXY_COMPLEMENT;
+    if (k < 0 || m < 0) return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: k=%d m=%d", k, m);
+    const int kk = k < d.nb ? k : d.nb;
+    if (kk == 0 && m == 0 && !proxies)
+        return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: empty virtual-token set (k = 0, m = 0, no proxies)");
+    if (!q || !K || !V || !out) return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: NULL tensor pointer");
+    if ((mode == CSA_SCORE_SUMMARY || proxies) && !Kbar)
+        return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: Kbar is NULL");
+    if (proxies && !Vbar) return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: proxies need Vbar");
+    if (m > 0 && (!tok_idx || !tok_logw))
+        return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: weighted tokens missing with m=%d", m);
+    if (!aligned16(q) || !aligned16(K) || !aligned16(V) || (Kbar && !aligned16(Kbar)) || (Vbar && !aligned16(Vbar)) ||
+        !aligned4(out) || (lse && !aligned4(lse)) || (scores && !aligned4(scores)) || (sel && !aligned4(sel)) ||
+        (tok_idx && !aligned4(tok_idx)) || (tok_logw && !aligned4(tok_logw)))
+        return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: misaligned pointer");
+    if (int rc = attn_rows_ok(d, kk, m, proxies, 0)) return rc;
+
+    if (mode == CSA_SCORE_SUMMARY && csa::fused_step_ok(d, kk, m, proxies)) {
+        void* none = nullptr;
+        size_t none_bytes = 0;
+        if (int rc = get_ws(0, &none, &none_bytes)) return rc;
+        csa::StepInputs in{q, K, V, Kbar, Vbar, kk, tok_idx, tok_logw, m, proxies, scores, sel, out, lse};
+        const hipError_t e = csa::launch_decode_step(d, in, stream);
+        return e == hipSuccess ? CSA_OK : hip_fail(e, "selective_decode_step");
+    }
+    // the three kernels in turn; scores and selection go to the caller's arrays
+    // when given, else to the workspace
+    const StepWs w = step_ws(d, kk, m);
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    if (int rc = get_ws(w.total, &ws, &ws_bytes)) return rc;
+    if (int rc = check_ws(w.total, ws, ws_bytes)) return rc;
+    char* base = static_cast<char*>(ws);
+    float* sc = scores ? scores : reinterpret_cast<float*>(base);
+    int32_t* sl = sel ? sel : reinterpret_cast<int32_t*>(base + w.scores);
+    void* sws = base + w.scores + w.sel;
+    void* aws = base + w.scores + w.sel + w.score_ws;
+    if (mode == CSA_SCORE_SUMMARY && csa::fused_summary_score_ok(d) && d.pairs() < csa::kFusedStepMinPairs &&
+        csa::split_select_ok(d, kk)) {
+        // scores and selection from the split kernels (the top-k rides on the group-score kernel)
+        const hipError_t e = csa::launch_score_summary_split(d, q, Kbar, d.G == 1 ? sc : static_cast<float*>(sws),
+                                                             sc, sl, kk, stream);
+        if (e != hipSuccess) return hip_fail(e, "selective_decode_step (score)");
+    } else if (mode == CSA_SCORE_EXACT_MASS && d.G > 1 && csa::score_finish_ok(d) && csa::split_select_ok(d, kk)) {
+        // exact masses, then group scores and selection in one kernel
+        float* lg = static_cast<float*>(sws);
+        hipError_t e = csa::launch_block_logits_exact(d, q, K, lg, stream);
+        if (e == hipSuccess) e = csa::launch_score_finish(d, lg, sc, sl, kk, stream);
+        if (e != hipSuccess) return hip_fail(e, "selective_decode_step (score)");
+    } else {
+        if (int rc = block_score(shape, mode, q, mode == CSA_SCORE_SUMMARY ? Kbar : K, sc, sws, w.score_ws, stream))
+            return rc;
+        if (int rc = topk_select(d.pairs(), d.nb, kk, sc, sl, stream)) return rc;
+    }
+    return sparse_decode_attn(shape, q, K, V, Kbar, Vbar, kk > 0 ? sl : nullptr, kk, tok_idx, tok_logw, m,
+                              proxy_mode, out, lse, aws, w.attn_ws, stream);
 }
 
 }  // namespace
@@ -307,66 +426,33 @@ int selective_decode_step(const csa_shape* shape, csa_score_mode mode, const voi
                           const float* tok_logw, int32_t m, csa_proxy_mode proxy_mode, float* scores, int32_t* sel,
                           float* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream)
 {
-    csa::Dims d;
-    if (int rc = make_dims(shape, &d)) return rc;
-    if (mode == CSA_SCORE_BOX || mode == CSA_SCORE_COBS2 || mode == CSA_SCORE_PROXY_ERROR ||
-        mode == CSA_SCORE_COBS2_FP4)
-        return fail(CSA_ERR_UNSUPPORTED, "selective_decode_step: box, second-order and proxy-error scores need "
-                                         "Kbox, Kcov or Kvar; call block_score, topk_select and sparse_decode_attn");
-    if (mode != CSA_SCORE_SUMMARY && mode != CSA_SCORE_EXACT_MASS)
-        return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: unknown mode %d", (int)mode);
-    if (proxy_mode != CSA_PROXY_NONE && proxy_mode != CSA_PROXY_COMPLEMENT)
-        return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: unknown proxy mode %d", (int)proxy_mode);
-    const int proxies = proxy_mode == CSA_PROXY_COMPLEMENT;
-    if (k < 0 || m < 0) return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: k=%d m=%d", k, m);
-    const int kk = k < d.nb ? k : d.nb;
-    if (kk == 0 && m == 0 && !proxies)
-        return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: empty virtual-token set (k = 0, m = 0, no proxies)");
-    if (!q || !K || !V || !out) return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: NULL tensor pointer");
-    if ((mode == CSA_SCORE_SUMMARY || proxies) && !Kbar)
-        return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: Kbar is NULL");
-    if (proxies && !Vbar) return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: proxies need Vbar");
-    if (m > 0 && (!tok_idx || !tok_logw))
-        return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: weighted tokens missing with m=%d", m);
-    if (!aligned16(q) || !aligned16(K) || !aligned16(V) || (Kbar && !aligned16(Kbar)) || (Vbar && !aligned16(Vbar)) ||
-        !aligned4(out) || (lse && !aligned4(lse)) || (scores && !aligned4(scores)) || (sel && !aligned4(sel)) ||
-        (tok_idx && !aligned4(tok_idx)) || (tok_logw && !aligned4(tok_logw)))
-        return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: misaligned pointer");
-    if (int rc = attn_rows_ok(d, kk, m, proxies, 0)) return rc;
+    auto caller_ws = [&](size_t, void** p, size_t* n) {
+        *p = ws;
+        *n = ws_bytes;
+        return (int)CSA_OK;
+    };
+    return step_impl(shape, mode, q, K, V, Kbar, Vbar, k, tok_idx, tok_logw, m, proxy_mode, scores, sel, out, lse,
+                     caller_ws, stream);
+}
 
-    if (mode == CSA_SCORE_SUMMARY && csa::fused_step_ok(d, kk, m, proxies)) {
-        csa::StepInputs in{q, K, V, Kbar, Vbar, kk, tok_idx, tok_logw, m, proxies, scores, sel, out, lse};
-        const hipError_t e = csa::launch_decode_step(d, in, stream);
-        return e == hipSuccess ? CSA_OK : hip_fail(e, "selective_decode_step");
-    }
-    // the three kernels in turn; scores and selection go to the caller's arrays
-    // when given, else to the workspace
-    const StepWs w = step_ws(d, kk, m);
-    if (int rc = check_ws(w.total, ws, ws_bytes)) return rc;
-    char* base = static_cast<char*>(ws);
-    float* sc = scores ? scores : reinterpret_cast<float*>(base);
-    int32_t* sl = sel ? sel : reinterpret_cast<int32_t*>(base + w.scores);
-    void* sws = base + w.scores + w.sel;
-    void* aws = base + w.scores + w.sel + w.score_ws;
-    if (mode == CSA_SCORE_SUMMARY && csa::fused_summary_score_ok(d) && d.pairs() < csa::kFusedStepMinPairs &&
-        csa::split_select_ok(d, kk)) {
-        // scores and selection from the split kernels (the top-k rides on the group-score kernel)
-        const hipError_t e = csa::launch_score_summary_split(d, q, Kbar, d.G == 1 ? sc : static_cast<float*>(sws),
-                                                             sc, sl, kk, stream);
-        if (e != hipSuccess) return hip_fail(e, "selective_decode_step (score)");
-    } else if (mode == CSA_SCORE_EXACT_MASS && d.G > 1 && csa::score_finish_ok(d) && csa::split_select_ok(d, kk)) {
-        // exact masses, then group scores and selection in one kernel
-        float* lg = static_cast<float*>(sws);
-        hipError_t e = csa::launch_block_logits_exact(d, q, K, lg, stream);
-        if (e == hipSuccess) e = csa::launch_score_finish(d, lg, sc, sl, kk, stream);
-        if (e != hipSuccess) return hip_fail(e, "selective_decode_step (score)");
-    } else {
-        if (int rc = block_score(shape, mode, q, mode == CSA_SCORE_SUMMARY ? Kbar : K, sc, sws, w.score_ws, stream))
-            return rc;
-        if (int rc = topk_select(d.pairs(), d.nb, kk, sc, sl, stream)) return rc;
-    }
-    return sparse_decode_attn(shape, q, K, V, Kbar, Vbar, kk > 0 ? sl : nullptr, kk, tok_idx, tok_logw, m,
-                              proxy_mode, out, lse, aws, w.attn_ws, stream);
+int selective_decode_step_noalloc(const csa_shape* shape, csa_score_mode mode, const void* q, const void* K,
+                                  const void* V, const void* Kbar, const void* Vbar, int32_t k,
+                                  const int32_t* tok_idx, const float* tok_logw, int32_t m,
+                                  csa_proxy_mode proxy_mode, float* scores, int32_t* sel, float* out, float* lse,
+                                  hipStream_t stream)
+{
+    auto static_ws = [&](size_t need, void** p, size_t* n) {
+        if (need > kScratchBytes)
+            return fail(CSA_ERR_WORKSPACE,
+                        "selective_decode_step_noalloc: this shape needs %zu bytes of scratch, above the %zu of the "
+                        "static buffer (use selective_decode_step with a workspace)",
+                        need, kScratchBytes);
+        if (int rc = scratch_of_current_device(p)) return rc;
+        *n = kScratchBytes;
+        return (int)CSA_OK;
+    };
+    return step_impl(shape, mode, q, K, V, Kbar, Vbar, k, tok_idx, tok_logw, m, proxy_mode, scores, sel, out, lse,
+                     static_ws, stream);
 }
 
 size_t csa_workspace_size(const csa_shape* shape, csa_entry entry, int32_t k, int32_t m)

@@ -283,6 +283,30 @@ int selective_decode_step(const csa_shape* shape, csa_score_mode mode, const voi
                           csa_proxy_mode proxy_mode, float* scores, int32_t* sel, float* out,
                           float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * selective_decode_step_noalloc -- selective_decode_step for callers that cannot
+ * allocate device memory: code running under HIP graph capture, tight serving
+ * loops and harnesses that forbid hipMalloc.  Same arguments, results and
+ * errors as selective_decode_step, without the workspace: where that route
+ * needs one, it uses a static device buffer of the library instead, of
+ * CSA_STEP_NOALLOC_SCRATCH_BYTES bytes on each GPU (part of the loaded code
+ * object, held until the process ends).  A shape whose workspace
+ * (csa_workspace_size(shape, CSA_WS_SELECTIVE_DECODE_STEP, k, m)) is larger is
+ * rejected with CSA_ERR_WORKSPACE before anything is launched.  The first call
+ * on a GPU looks up the buffer's device address there (hipGetSymbolAddress,
+ * which allocates nothing); no call allocates or frees memory.  Every call on
+ * one GPU shares that GPU's buffer, so calls that overlap in time on one GPU
+ * (different streams, or host threads without ordering) race and give wrong
+ * results; calls ordered on one stream are safe.  Nothing in the buffer needs
+ * to start at zero: every call writes what it reads.
+ */
+#define CSA_STEP_NOALLOC_SCRATCH_BYTES (64u << 20)
+int selective_decode_step_noalloc(const csa_shape* shape, csa_score_mode mode, const void* q, const void* K,
+                                  const void* V, const void* Kbar, const void* Vbar, int32_t k,
+                                  const int32_t* tok_idx, const float* tok_logw, int32_t m,
+                                  csa_proxy_mode proxy_mode, float* scores, int32_t* sel, float* out, float* lse,
+                                  hipStream_t stream);
+
 /* Workspace bytes needed by an entry point for this shape (k, m as the call
  * will pass them).  Returns 0 for an invalid shape (see csa_last_error()). */
 size_t csa_workspace_size(const csa_shape* shape, csa_entry entry, int32_t k, int32_t m);

@@ -278,3 +278,29 @@ def test_kernels_fit_their_registers(L):
     for part in ("decode_step_kernelILi128ELi4E", "attn_mfma_kernelILi128ELi4ELi8E"):
         (name,) = [n for n in res if part in n]
         assert res[name]["waves_per_simd"] == 2 and res[name]["scratch_bytes_per_lane"] == 0, res[name]
+
+
+def test_noalloc_step_rejects_shapes_beyond_its_static_scratch(L):
+    """selective_decode_step_noalloc validates like selective_decode_step and refuses, before any
+    HIP call, a shape whose workspace exceeds the static scratch (exact-mass logits of 256
+    sequences x 64 heads x 4096 blocks: 256 MiB)."""
+    big = shape(B=256, Hq=64, Hkv=1, n=65536, L=16)
+    need = L.csa_workspace_size(ctypes.byref(big), csa.CSA_WS_SELECTIVE_DECODE_STEP, 4, 0)
+    assert need > csa.CSA_STEP_NOALLOC_SCRATCH_BYTES
+    p = FAKE
+    rc = L.selective_decode_step_noalloc(ctypes.byref(big), csa.CSA_SCORE_EXACT_MASS, p, p, p, None, None, 4, None,
+                                         None, 0, csa.CSA_PROXY_NONE, None, None, p, p, None)
+    assert rc == csa.CSA_ERR_WORKSPACE and b"static buffer" in L.csa_last_error()
+    s = shape()
+    rc = L.selective_decode_step_noalloc(ctypes.byref(s), csa.CSA_SCORE_SUMMARY, p, p, p, p, p, 0, None, None, 0,
+                                         csa.CSA_PROXY_NONE, None, None, p, p, None)
+    assert rc == csa.CSA_ERR_INVALID_ARG and b"empty virtual-token set" in L.csa_last_error()
+    rc = L.selective_decode_step_noalloc(ctypes.byref(s), csa.CSA_SCORE_SUMMARY, p, p, p, None, p, 2, None, None, 0,
+                                         csa.CSA_PROXY_COMPLEMENT, None, None, p, p, None)
+    assert rc == csa.CSA_ERR_INVALID_ARG and b"Kbar" in L.csa_last_error()
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define CSA_STEP_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == csa.CSA_STEP_NOALLOC_SCRATCH_BYTES
