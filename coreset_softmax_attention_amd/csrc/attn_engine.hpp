@@ -7,10 +7,11 @@
 //   1. lanes 0..31 resolve the tile's rows into one of two per-wave LDS tables
 //      (row index in its source array, log2-weight; -inf for a row that does not
 //      count);
-//   2. the tile's rows are loaded with buffer loads: key rows in the layout of
-//      the A operand of v_mfma_f32_16x16x32_bf16 (lane (n16, g16): row n16 of a
-//      16-row block, 16-byte chunks 4 s + g16), value rows as whole rows per
-//      lane group (16-byte chunks, coalesced);
+//   2. the tile's rows are loaded with non-temporal buffer loads, whole rows per
+//      lane group (16-byte chunks, coalesced: RB / 16 lanes per row); the key
+//      rows then pass through a per-wave LDS slot into the layout of the A
+//      operand of v_mfma_f32_16x16x32_bf16 (lane (n16, g16): row n16 of a
+//      16-row block, 16-byte chunks 4 s + g16);
 //   3. logits for up to 8 query heads come from two 16x16x32 MFMA chains (rows
 //      x heads, heads padded to 16 columns), or from LDS when the caller has
 //      them already; the online-softmax update runs once per (row, head) on the
@@ -34,8 +35,15 @@ struct MfmaEngine {
     static constexpr int LPV = RB / 16;         // lanes per value row
     static constexpr int RPV = 64 / LPV;        // value rows per wave-wide load
     static constexpr int NVI = TR / RPV;        // value loads per lane per tile
+    static constexpr int NI = TR / RPV;         // key loads per lane per tile (rows RPV j + gv)
     static constexpr int HP = HG <= 4 ? 4 : 8;  // padded heads per probability row
     static_assert(KS * 32 == D && HG <= 8 && (LPV == 8 || LPV == 16), "unsupported geometry");
+    static_assert(NI == 2 * KS && RPV * NI / 2 == 16, "a half tile of key loads covers one 16-row MFMA block");
+    // Key rows go through LDS (coalesced non-temporal loads, then the layout
+    // change) up to six heads; with seven or eight the value accumulators leave
+    // no room for it, and the keys are loaded in the operand layout directly
+    // (kr[KS rb + s] = operand s of block rb).
+    static constexpr bool kLdsKeys = HG <= 6;
 
     static constexpr int NTAB = 4;  // row tables per wave (tiles in flight or pending)
 
@@ -47,11 +55,14 @@ struct MfmaEngine {
         float m[NW][HG];
         float l[NW][HG];
         float acc[NW][HG][D];
+        uint4 kt[kLdsKeys ? NW : 1][16 * (LPV + 1)];  // per-wave staging of 16 key rows (layout change)
     };
 
-    // One tile's operands in registers.
+    // One tile's rows in registers, as loaded: kr[j] and vr[j] hold 16-byte
+    // chunk cv of key and value row RPV j + gv (four or eight consecutive rows
+    // per instruction; one row offset serves both).
     struct Tile {
-        uint4 ak[2][KS];
+        uint4 kr[NI];
         uint4 vr[NVI];
     };
 
@@ -59,7 +70,7 @@ struct MfmaEngine {
     const int lane, wave, n16, g16, gv, cv;
     bf16x8_t bq[KS];
     float m_run, l_part;  // MFMA lanes: head n16
-    float acc[HG][8];     // value lanes: chunk cv of the rows of group gv
+    float acc[HG][8];     // value lanes: chunk cv of the rows RPV j + gv
 
     __device__ __forceinline__ MfmaEngine(Smem& s, const char* q_first_head, int nh)
         : sm(s),
@@ -92,16 +103,30 @@ struct MfmaEngine {
                                           bool with_keys)
     {
         wave_lds_fence();
-        if (with_keys) {
+        if constexpr (kLdsKeys) {
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-                const uint32_t off = sm.tab_row[tb][wave][rb * 16 + n16] * RB + g16 * 16;
-#pragma unroll
-                for (int s = 0; s < KS; ++s) t.ak[rb][s] = buffer_ld16(kr, off + s * 64);
+            for (int j = 0; j < NI; ++j) {
+                const uint32_t off = sm.tab_row[tb][wave][RPV * j + gv] * RB + cv * 16;
+                if (with_keys) t.kr[j] = buffer_ld16_nt(kr, off);
+                t.vr[j] = buffer_ld16_nt(vr, off);
             }
-        }
+        } else {
+            if (with_keys) operand_keys(t.kr, tb, kr);
 #pragma unroll
-        for (int u = 0; u < NVI; ++u) t.vr[u] = buffer_ld16(vr, sm.tab_row[tb][wave][gv * NVI + u] * RB + cv * 16);
+            for (int j = 0; j < NVI; ++j) t.vr[j] = buffer_ld16_nt(vr, sm.tab_row[tb][wave][RPV * j + gv] * RB + cv * 16);
+        }
+    }
+
+    // Key rows in the operand layout: lane (n16, g16) loads chunk 4 s + g16 of
+    // row 16 rb + n16 into kr[KS rb + s] (half a cache line per row per load).
+    __device__ __forceinline__ void operand_keys(uint4 (&kr)[NI], int tb, __amdgpu_buffer_rsrc_t r)
+    {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            const uint32_t off = sm.tab_row[tb][wave][rb * 16 + n16] * RB + g16 * 16;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) kr[KS * rb + s] = buffer_ld16(r, off + s * 64);
+        }
     }
 
     // Issue only the key rows of a tile whose row table `tb` is written (its
@@ -109,11 +134,47 @@ struct MfmaEngine {
     __device__ __forceinline__ void issue_keys(Tile& t, int tb, __amdgpu_buffer_rsrc_t kr)
     {
         wave_lds_fence();
+        if constexpr (kLdsKeys) {
+#pragma unroll
+            for (int j = 0; j < NI; ++j) t.kr[j] = buffer_ld16_nt(kr, sm.tab_row[tb][wave][RPV * j + gv] * RB + cv * 16);
+        } else {
+            operand_keys(t.kr, tb, kr);
+        }
+    }
+
+    // Key rows as loaded (kr[j]: chunk cv of row RPV j + gv) -> A operand of the
+    // 16-row MFMA block rb (a[s]: chunk 4 s + g16 of row 16 rb + n16), through
+    // the wave's LDS slot.  Slot rows are padded to LPV + 1 chunks, which puts the
+    // 16 rows' starts on 16 different groups of four banks: the lanes of a write
+    // (whole rows) and of a read (one chunk of 16 rows) hit different banks, and
+    // every access is one base address plus an immediate offset.
+    __device__ __forceinline__ void key_block(const uint4 (&kr)[NI], int rb, uint4 (&a)[KS])
+    {
+        if constexpr (!kLdsKeys) {
+#pragma unroll
+            for (int s = 0; s < KS; ++s) a[s] = kr[KS * rb + s];
+            return;
+        }
+        uint4* slot = sm.kt[wave];
+#pragma unroll
+        for (int j = 0; j < NI / 2; ++j) slot[(RPV * j + gv) * (LPV + 1) + cv] = kr[rb * (NI / 2) + j];
+        wave_lds_fence();
+#pragma unroll
+        for (int s = 0; s < KS; ++s) a[s] = slot[n16 * (LPV + 1) + 4 * s + g16];
+        wave_lds_fence();  // the slot is rewritten next
+    }
+
+    // q K^T of the tile's two 16-row blocks: c[rb][i] is head n16 of row 16 rb + 4 g16 + i.
+    __device__ __forceinline__ void qk_tile(const uint4 (&kr)[NI], f32x4_t (&c)[2])
+    {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
-            const uint32_t off = sm.tab_row[tb][wave][rb * 16 + n16] * RB + g16 * 16;
+            uint4 a[KS];
+            key_block(kr, rb, a);
+            c[rb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int s = 0; s < KS; ++s) t.ak[rb][s] = buffer_ld16(kr, off + s * 64);
+            for (int s = 0; s < KS; ++s)
+                c[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[s]), bq[s], c[rb], 0, 0, 0);
         }
     }
 
@@ -122,19 +183,16 @@ struct MfmaEngine {
     {
         wave_lds_fence();
 #pragma unroll
-        for (int u = 0; u < NVI; ++u) vr[u] = buffer_ld16(rsrc, sm.tab_row[tb][wave][gv * NVI + u] * RB + cv * 16);
+        for (int u = 0; u < NVI; ++u) vr[u] = buffer_ld16_nt(rsrc, sm.tab_row[tb][wave][RPV * u + gv] * RB + cv * 16);
     }
 
     // Logits (log2 units) of the tile from its key rows: lane (n16, g16) gets
     // head n16 of rows 16 rb + 4 g16 + i as x[4 rb + i].
     __device__ __forceinline__ void logits_mfma(const Tile& t, int tb, float scale_log2, float (&x)[8])
     {
-        f32x4_t c0 = {0.0f, 0.0f, 0.0f, 0.0f}, c1 = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, t.ak[0][s]), bq[s], c0, 0, 0, 0);
-            c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, t.ak[1][s]), bq[s], c1, 0, 0, 0);
-        }
+        f32x4_t c[2];
+        qk_tile(t.kr, c);
+        const f32x4_t c0 = c[0], c1 = c[1];
         const float4 lw0 = *reinterpret_cast<const float4*>(&sm.tab_lw[tb][wave][4 * g16]);
         const float4 lw1 = *reinterpret_cast<const float4*>(&sm.tab_lw[tb][wave][16 + 4 * g16]);
         const float lws[8] = {lw0.x, lw0.y, lw0.z, lw0.w, lw1.x, lw1.y, lw1.z, lw1.w};
@@ -200,9 +258,9 @@ struct MfmaEngine {
 #pragma unroll
         for (int u = 0; u < NVI; ++u) {
             float pr[HP];
-            *reinterpret_cast<float4*>(&pr[0]) = *reinterpret_cast<const float4*>(&sm.p[wave][gv * NVI + u][0]);
+            *reinterpret_cast<float4*>(&pr[0]) = *reinterpret_cast<const float4*>(&sm.p[wave][RPV * u + gv][0]);
             if constexpr (HP == 8)
-                *reinterpret_cast<float4*>(&pr[4]) = *reinterpret_cast<const float4*>(&sm.p[wave][gv * NVI + u][4]);
+                *reinterpret_cast<float4*>(&pr[4]) = *reinterpret_cast<const float4*>(&sm.p[wave][RPV * u + gv][4]);
             float vf[8];
             unpack<DT_BF16>(vr[u], vf);
 #pragma unroll
