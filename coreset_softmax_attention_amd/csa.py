@@ -12,7 +12,8 @@ import os
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so")
+# CSA_LIBRARY names another build of the same library (the host-sanitized build of the tests)
+_LIB_PATH = os.environ.get("CSA_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so")
 
 CSA_OK, CSA_ERR_INVALID_ARG, CSA_ERR_UNSUPPORTED, CSA_ERR_WORKSPACE, CSA_ERR_HIP = 0, -1, -2, -3, -4
 CSA_F32, CSA_BF16 = 0, 1
@@ -106,6 +107,8 @@ def lib():
         L.csa_status_str.restype = ctypes.c_char_p
         L.csa_last_error.argtypes = []
         L.csa_last_error.restype = ctypes.c_char_p
+        L.csa_set_index_checks.argtypes = [ctypes.c_int]
+        L.csa_set_index_checks.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -340,6 +343,12 @@ def selective_decode_step_noalloc(q, K, V, Kbar, Vbar, k: int, block_size: int, 
                                                _ptr(sel), _ptr(out), _ptr(lse), _stream(dev)),
            "selective_decode_step_noalloc")
     return out, lse, scores, sel
+
+
+def set_index_checks(enable: bool) -> bool:
+    """Turn the host-side check of device-resident index arrays on or off (csa_set_index_checks);
+    returns the previous setting."""
+    return bool(lib().csa_set_index_checks(1 if enable else 0))
 
 
 def to_device(a, device="cuda"):

@@ -5,8 +5,13 @@
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
 
+#include <algorithm>
+#include <atomic>
 #include <mutex>
+#include <vector>
 
 #include "../../include/csa.h"
 #include "device.hpp"
@@ -30,6 +35,18 @@ int hip_fail(hipError_t e, const char* where)
     return fail(CSA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
 }
 
+// The integer a caller passed for a C enum.  Copied byte for byte: a value
+// outside the enumerators (which validation then rejects) must not be read
+// as the enum type itself, whose range C++ limits to its enumerators' bits.
+template <typename E>
+int raw_enum(const E& e)
+{
+    static_assert(sizeof(E) == sizeof(int), "C enums are int-sized");
+    int v;
+    memcpy(&v, &e, sizeof v);
+    return v;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
@@ -47,8 +64,8 @@ int make_dims(const csa_shape* sh, csa::Dims* d)
     if (sh->n_q_heads % sh->n_kv_heads != 0)
         return fail(CSA_ERR_INVALID_ARG, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)", sh->n_q_heads,
                     sh->n_kv_heads);
-    if (sh->dtype != CSA_F32 && sh->dtype != CSA_BF16)
-        return fail(CSA_ERR_INVALID_ARG, "unknown dtype %d", (int)sh->dtype);
+    const int dtype = raw_enum(sh->dtype);
+    if (dtype != CSA_F32 && dtype != CSA_BF16) return fail(CSA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
     if (!isfinite(sh->scale)) return fail(CSA_ERR_INVALID_ARG, "scale is not finite");
     if (sh->head_dim != 64 && sh->head_dim != 128)
         return fail(CSA_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", sh->head_dim);
@@ -63,7 +80,7 @@ int make_dims(const csa_shape* sh, csa::Dims* d)
     d->n = sh->n_tokens;
     d->L = sh->block_size < sh->n_tokens ? sh->block_size : sh->n_tokens;  // one ragged block if L >= n
     d->nb = (sh->n_tokens + d->L - 1) / d->L;
-    d->dtype = sh->dtype == CSA_F32 ? csa::DT_F32 : csa::DT_BF16;
+    d->dtype = dtype == CSA_F32 ? csa::DT_F32 : csa::DT_BF16;
     d->scale = sh->scale != 0.0f ? sh->scale : (float)(1.0 / sqrt((double)sh->head_dim));
     d->ln_L = (float)log((double)d->L);
     d->ln_last = (float)log((double)(sh->n_tokens - (d->nb - 1) * d->L));
@@ -76,6 +93,64 @@ int check_ws(size_t need, const void* ws, size_t ws_bytes)
     if (!ws) return fail(CSA_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
     if (ws_bytes < need) return fail(CSA_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", need, ws_bytes);
     if (!aligned256(ws)) return fail(CSA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    return CSA_OK;
+}
+
+// ---- optional check of device-resident indices --------------------------------
+
+std::atomic<int> g_index_checks{-1};  // -1: not yet read from the environment
+
+bool index_checks_on()
+{
+    int v = g_index_checks.load();
+    if (v < 0) {
+        const char* e = getenv("CSA_CHECK_INDICES");
+        v = (e && *e && !(e[0] == '0' && e[1] == 0)) ? 1 : 0;
+        int expected = -1;
+        g_index_checks.compare_exchange_strong(expected, v);
+        v = g_index_checks.load();
+    }
+    return v == 1;
+}
+
+// Copies the caller's index arrays to the host (which waits for the stream's
+// earlier work) and rejects what the oracle rejects: a selection row that
+// names a block twice or outside [0, nb), a weighted token outside [0, n).
+int check_device_indices(const char* where, const csa::Dims& d, const int32_t* sel, int k, const int32_t* tok_idx,
+                         int m, hipStream_t st)
+{
+    const size_t rows = (size_t)d.pairs();
+    if (k > 0) {
+        std::vector<int32_t> h(rows * (size_t)k);
+        hipError_t e = hipMemcpyAsync(h.data(), sel, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost, st);
+        if (e == hipSuccess) e = hipStreamSynchronize(st);
+        if (e != hipSuccess) return hip_fail(e, "index check (sel)");
+        std::vector<int32_t> row((size_t)k);
+        for (size_t r = 0; r < rows; ++r) {
+            for (int i = 0; i < k; ++i) {
+                const int32_t b = h[r * k + i];
+                if (b < 0 || b >= d.nb)
+                    return fail(CSA_ERR_INVALID_ARG, "%s: sel[%zu][%d] = %d outside [0, %d)", where, r, i, b, d.nb);
+                row[i] = b;
+            }
+            std::sort(row.begin(), row.end());
+            for (int i = 1; i < k; ++i)
+                if (row[i] == row[i - 1])
+                    return fail(CSA_ERR_INVALID_ARG, "%s: sel row %zu names block %d twice", where, r, row[i]);
+        }
+    }
+    if (m > 0) {
+        std::vector<int32_t> h(rows * (size_t)m);
+        hipError_t e = hipMemcpyAsync(h.data(), tok_idx, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost, st);
+        if (e == hipSuccess) e = hipStreamSynchronize(st);
+        if (e != hipSuccess) return hip_fail(e, "index check (tok_idx)");
+        for (size_t r = 0; r < rows; ++r)
+            for (int i = 0; i < m; ++i) {
+                const int32_t t = h[r * m + i];
+                if (t < 0 || t >= d.n)
+                    return fail(CSA_ERR_INVALID_ARG, "%s: tok_idx[%zu][%d] = %d outside [0, %d)", where, r, i, t, d.n);
+            }
+    }
     return CSA_OK;
 }
 
@@ -165,10 +240,9 @@ int scratch_of_current_device(void** out)
 // The decode step.  get_ws(need, &ws, &ws_bytes) supplies the workspace of the
 // three-kernel route once the arguments are valid (need > 0 only there).
 template <typename GetWs>
-int step_impl(const csa_shape* shape, csa_score_mode mode, const void* q, const void* K, const void* V,
-              const void* Kbar, const void* Vbar, int32_t k, const int32_t* tok_idx, const float* tok_logw, int32_t m,
-              csa_proxy_mode proxy_mode, float* scores, int32_t* sel, float* out, float* lse, GetWs get_ws,
-              hipStream_t stream)
+int step_impl(const csa_shape* shape, int mode, const void* q, const void* K, const void* V, const void* Kbar,
+              const void* Vbar, int32_t k, const int32_t* tok_idx, const float* tok_logw, int32_t m, int proxy_mode,
+              float* scores, int32_t* sel, float* out, float* lse, GetWs get_ws, hipStream_t stream)
 {
     csa::Dims d;
     if (int rc = make_dims(shape, &d)) return rc;
@@ -177,9 +251,9 @@ int step_impl(const csa_shape* shape, csa_score_mode mode, const void* q, const 
         return fail(CSA_ERR_UNSUPPORTED, "selective_decode_step: box, second-order and proxy-error scores need "
                                          "Kbox, Kcov or Kvar; call block_score, topk_select and sparse_decode_attn");
     if (mode != CSA_SCORE_SUMMARY && mode != CSA_SCORE_EXACT_MASS)
-        return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: unknown mode %d", (int)mode);
+        return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: unknown mode %d", mode);
     if (proxy_mode != CSA_PROXY_NONE && proxy_mode != CSA_PROXY_COMPLEMENT)
-        return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: unknown proxy mode %d", (int)proxy_mode);
+        return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: unknown proxy mode %d", proxy_mode);
     const int proxies = proxy_mode == CSA_PROXY_COMPLEMENT;
     if (k < 0 || m < 0) return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: k=%d m=%d", k, m);
     const int kk = k < d.nb ? k : d.nb;
@@ -196,6 +270,8 @@ int step_impl(const csa_shape* shape, csa_score_mode mode, const void* q, const 
         (tok_idx && !aligned4(tok_idx)) || (tok_logw && !aligned4(tok_logw)))
         return fail(CSA_ERR_INVALID_ARG, "selective_decode_step: misaligned pointer");
     if (int rc = attn_rows_ok(d, kk, m, proxies, 0)) return rc;
+    if (index_checks_on())
+        if (int rc = check_device_indices("selective_decode_step", d, nullptr, 0, tok_idx, m, stream)) return rc;
 
     if (mode == CSA_SCORE_SUMMARY && csa::fused_step_ok(d, kk, m, proxies)) {
         void* none = nullptr;
@@ -230,12 +306,13 @@ int step_impl(const csa_shape* shape, csa_score_mode mode, const void* q, const 
         if (e == hipSuccess) e = csa::launch_score_finish(d, lg, sc, sl, kk, stream);
         if (e != hipSuccess) return hip_fail(e, "selective_decode_step (score)");
     } else {
-        if (int rc = block_score(shape, mode, q, mode == CSA_SCORE_SUMMARY ? Kbar : K, sc, sws, w.score_ws, stream))
+        if (int rc = block_score(shape, static_cast<csa_score_mode>(mode), q, mode == CSA_SCORE_SUMMARY ? Kbar : K, sc,
+                                 sws, w.score_ws, stream))
             return rc;
         if (int rc = topk_select(d.pairs(), d.nb, kk, sc, sl, stream)) return rc;
     }
     return sparse_decode_attn(shape, q, K, V, Kbar, Vbar, kk > 0 ? sl : nullptr, kk, tok_idx, tok_logw, m,
-                              proxy_mode, out, lse, aws, w.attn_ws, stream);
+                              static_cast<csa_proxy_mode>(proxy_mode), out, lse, aws, w.attn_ws, stream);
 }
 
 }  // namespace
@@ -299,14 +376,15 @@ int kv_var_build(const csa_shape* shape, const void* K, void* Kvar, hipStream_t 
     return e == hipSuccess ? CSA_OK : hip_fail(e, "kv_var_build");
 }
 
-int block_score(const csa_shape* shape, csa_score_mode mode, const void* q, const void* keys, float* scores, void* ws,
-                size_t ws_bytes, hipStream_t stream)
+int block_score(const csa_shape* shape, csa_score_mode mode_arg, const void* q, const void* keys, float* scores,
+                void* ws, size_t ws_bytes, hipStream_t stream)
 {
+    const int mode = raw_enum(mode_arg);
     csa::Dims d;
     if (int rc = make_dims(shape, &d)) return rc;
     if (mode != CSA_SCORE_SUMMARY && mode != CSA_SCORE_EXACT_MASS && mode != CSA_SCORE_BOX && mode != CSA_SCORE_COBS2 &&
         mode != CSA_SCORE_PROXY_ERROR && mode != CSA_SCORE_COBS2_FP4)
-        return fail(CSA_ERR_INVALID_ARG, "block_score: unknown mode %d", (int)mode);
+        return fail(CSA_ERR_INVALID_ARG, "block_score: unknown mode %d", mode);
     {  // the kernels address one KV head's key rows with 32-bit offsets
         const long long row = (long long)d.d * (d.dtype == csa::DT_F32 ? 4 : 2);
         const long long rows_per_block = mode == CSA_SCORE_BOX || mode == CSA_SCORE_PROXY_ERROR ? 2
@@ -376,13 +454,14 @@ int topk_select(int32_t rows, int32_t nb, int32_t k, const float* scores, int32_
 
 int sparse_decode_attn(const csa_shape* shape, const void* q, const void* K, const void* V, const void* Kbar,
                        const void* Vbar, const int32_t* sel, int32_t k, const int32_t* tok_idx,
-                       const float* tok_logw, int32_t m, csa_proxy_mode proxy_mode, float* out, float* lse,
+                       const float* tok_logw, int32_t m, csa_proxy_mode proxy_arg, float* out, float* lse,
                        void* ws, size_t ws_bytes, hipStream_t stream)
 {
+    const int proxy_mode = raw_enum(proxy_arg);
     csa::Dims d;
     if (int rc = make_dims(shape, &d)) return rc;
     if (proxy_mode != CSA_PROXY_NONE && proxy_mode != CSA_PROXY_COMPLEMENT)
-        return fail(CSA_ERR_INVALID_ARG, "sparse_decode_attn: unknown proxy mode %d", (int)proxy_mode);
+        return fail(CSA_ERR_INVALID_ARG, "sparse_decode_attn: unknown proxy mode %d", proxy_mode);
     const int proxies = proxy_mode == CSA_PROXY_COMPLEMENT;
     if (k < 0 || k > d.nb) return fail(CSA_ERR_INVALID_ARG, "sparse_decode_attn: k=%d outside [0, %d]", k, d.nb);
     if (m < 0) return fail(CSA_ERR_INVALID_ARG, "sparse_decode_attn: m=%d is negative", m);
@@ -400,6 +479,8 @@ int sparse_decode_attn(const csa_shape* shape, const void* q, const void* K, con
     if (int rc = attn_rows_ok(d, k, m, proxies, 0)) return rc;
     const csa::AttnPlan plan = csa::plan_attention(d, k, m, proxies, 0);
     if (int rc = check_ws(plan.ws_bytes, ws, ws_bytes)) return rc;
+    if (index_checks_on())
+        if (int rc = check_device_indices("sparse_decode_attn", d, sel, k, tok_idx, m, stream)) return rc;
     csa::AttnInputs in{q, K, V, Kbar, Vbar, sel, k, tok_idx, tok_logw, m, proxies, 0, out, lse};
     const hipError_t e = csa::launch_attention(d, plan, in, ws, stream);
     return e == hipSuccess ? CSA_OK : hip_fail(e, "sparse_decode_attn");
@@ -431,8 +512,8 @@ int selective_decode_step(const csa_shape* shape, csa_score_mode mode, const voi
         *n = ws_bytes;
         return (int)CSA_OK;
     };
-    return step_impl(shape, mode, q, K, V, Kbar, Vbar, k, tok_idx, tok_logw, m, proxy_mode, scores, sel, out, lse,
-                     caller_ws, stream);
+    return step_impl(shape, raw_enum(mode), q, K, V, Kbar, Vbar, k, tok_idx, tok_logw, m, raw_enum(proxy_mode), scores,
+                     sel, out, lse, caller_ws, stream);
 }
 
 int selective_decode_step_noalloc(const csa_shape* shape, csa_score_mode mode, const void* q, const void* K,
@@ -451,12 +532,13 @@ int selective_decode_step_noalloc(const csa_shape* shape, csa_score_mode mode, c
         *n = kScratchBytes;
         return (int)CSA_OK;
     };
-    return step_impl(shape, mode, q, K, V, Kbar, Vbar, k, tok_idx, tok_logw, m, proxy_mode, scores, sel, out, lse,
-                     static_ws, stream);
+    return step_impl(shape, raw_enum(mode), q, K, V, Kbar, Vbar, k, tok_idx, tok_logw, m, raw_enum(proxy_mode), scores,
+                     sel, out, lse, static_ws, stream);
 }
 
-size_t csa_workspace_size(const csa_shape* shape, csa_entry entry, int32_t k, int32_t m)
+size_t csa_workspace_size(const csa_shape* shape, csa_entry entry_arg, int32_t k, int32_t m)
 {
+    const int entry = raw_enum(entry_arg);
     csa::Dims d;
     if (make_dims(shape, &d) != CSA_OK) return 0;
     switch (entry) {
@@ -490,7 +572,7 @@ size_t csa_workspace_size(const csa_shape* shape, csa_entry entry, int32_t k, in
         return step_ws(d, kk, m).total;
     }
     }
-    fail(CSA_ERR_INVALID_ARG, "csa_workspace_size: unknown entry %d", (int)entry);
+    fail(CSA_ERR_INVALID_ARG, "csa_workspace_size: unknown entry %d", entry);
     return 0;
 }
 
@@ -507,5 +589,12 @@ const char* csa_status_str(int status)
 }
 
 const char* csa_last_error(void) { return g_last_error; }
+
+int csa_set_index_checks(int enable)
+{
+    const int prev = index_checks_on() ? 1 : 0;
+    g_index_checks.store(enable ? 1 : 0);
+    return prev;
+}
 
 }  // extern "C"

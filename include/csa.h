@@ -49,7 +49,7 @@
  *     (n * d * element bytes < 2^32).  All pointers 16-byte aligned.
  *   - Inputs must be finite.  Indices outside their range are rejected only
  *     where the host can see them (sizes); device-resident index values are
- *     trusted.
+ *     trusted unless csa_set_index_checks() turns their checks on.
  */
 #ifndef CSA_H
 #define CSA_H
@@ -316,6 +316,22 @@ const char* csa_status_str(int status);
 
 /* Detail of the last non-OK return on this host thread ("" if none). */
 const char* csa_last_error(void);
+
+/*
+ * csa_set_index_checks -- debugging aid for the index arrays that live in
+ * device memory and are otherwise trusted: with checks on, sparse_decode_attn
+ * (sel, tok_idx) and selective_decode_step (tok_idx) first copy them to the
+ * host, which waits for the earlier work on their stream (so such calls
+ * synchronise and cannot be captured in a graph), and return
+ * CSA_ERR_INVALID_ARG, launching nothing, for a selection row that names a
+ * block twice or outside [0, nb), or a weighted token outside [0, n) -- the
+ * inputs the fp64 reference rejects.  With checks off
+ * (the default) those entries are excluded on the device: such a row or token
+ * gets log-weight -inf.  The environment variable CSA_CHECK_INDICES=1 turns
+ * the checks on from the first call.  Process-wide; returns the previous
+ * setting (0 or 1).
+ */
+int csa_set_index_checks(int enable);
 
 #ifdef __cplusplus
 }

@@ -304,3 +304,32 @@ def test_noalloc_scratch_size_matches_the_header():
     text = open(HEADER).read()
     m = re.search(r"#define CSA_STEP_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == csa.CSA_STEP_NOALLOC_SCRATCH_BYTES
+
+
+def test_index_checks_toggle(L):
+    prev = L.csa_set_index_checks(1)
+    try:
+        assert L.csa_set_index_checks(0) == 1
+        assert L.csa_set_index_checks(0) == 0
+    finally:
+        L.csa_set_index_checks(prev)
+
+
+@pytest.mark.parametrize("value", [-1, 2, 7, 99, -(1 << 31), (1 << 31) - 1])
+def test_out_of_range_enum_values_are_rejected(L, value):
+    """Enum arguments arrive as plain C ints: values outside the enumerators are rejected (the
+    host-sanitized build of this file checks that reading them is well defined)."""
+    s = shape(dtype=value) if value not in (0, 1) else shape()
+    if value not in (0, 1):
+        assert sparse(L, s) == csa.CSA_ERR_INVALID_ARG and b"dtype" in L.csa_last_error()
+    s = shape()
+    if value not in range(0, 6):
+        rc = L.block_score(ctypes.byref(s), value, FAKE, FAKE, FAKE, FAKE, 1 << 20, None)
+        assert rc == csa.CSA_ERR_INVALID_ARG and b"mode" in L.csa_last_error()
+    if value not in (0, 1):
+        assert sparse(L, s, proxy=value) == csa.CSA_ERR_INVALID_ARG and b"proxy mode" in L.csa_last_error()
+        rc = L.selective_decode_step(ctypes.byref(s), value, FAKE, FAKE, FAKE, FAKE, FAKE, 2, None, None, 0, 1, None,
+                                     None, FAKE, FAKE, FAKE, 1 << 20, None)
+        assert rc in (csa.CSA_ERR_INVALID_ARG, csa.CSA_ERR_UNSUPPORTED)
+    if value not in range(0, 9):
+        assert L.csa_workspace_size(ctypes.byref(s), value, 0, 0) == 0 and b"entry" in L.csa_last_error()

@@ -336,6 +336,54 @@ def test_runs_are_bitwise_reproducible():
         assert np.array_equal(a[key], b[key]), key
 
 
+def test_index_checks_reject_what_the_oracle_rejects():
+    """With csa_set_index_checks on, selections that name a block twice or outside [0, nb), and
+    weighted tokens outside [0, n), are rejected on the host before any launch, as the oracle
+    rejects them; valid lists give the same bits as without the checks."""
+    B, Hkv, G, d, n, L = 2, 2, 4, 128, 1024, 64
+    nb = n // L
+    data = rand_inputs(901, B, G * Hkv, Hkv, d, n, "bf16")
+    shp = O.Shape(B, G * Hkv, Hkv, d, n, L, "bf16")
+    q, K, V = dev(data["q"]), dev(data["K"]), dev(data["V"])
+    Kbar, Vbar = csa.kv_summary_build(K, V, L)
+    Kb_o, Vb_o = O.kv_summary_build(shp, data["K"], data["V"])
+    good = np.tile(np.array([1, 4, 9], np.int32), (B, Hkv, 1))
+    tok = np.tile(np.array([3, 500, 1023], np.int32), (B, Hkv, 1))
+    logw = np.zeros((B, Hkv, 3), np.float32)
+    bad_sels = [good.copy(), good.copy(), good.copy()]
+    bad_sels[0][1, 0] = [4, 4, 9]       # a block twice
+    bad_sels[1][0, 1, 2] = nb          # past the last block
+    bad_sels[2][1, 1, 0] = -1          # negative
+    bad_tok = tok.copy()
+    bad_tok[1, 0, 1] = n
+    prev = csa.set_index_checks(True)
+    try:
+        for sel in bad_sels:
+            with pytest.raises(ValueError):
+                O.sparse_decode_attn(shp, data["q"], data["K"], data["V"], Kb_o, Vb_o, sel, True)
+            with pytest.raises(csa.CsaError, match="sel") as e:
+                csa.sparse_decode_attn(q, K, V, Kbar, Vbar, dev(sel), L, proxies=True)
+            assert e.value.status == csa.CSA_ERR_INVALID_ARG
+        with pytest.raises(ValueError):
+            O.sparse_decode_attn(shp, data["q"], data["K"], data["V"], Kb_o, Vb_o, good, True, bad_tok, logw)
+        with pytest.raises(csa.CsaError, match="tok_idx") as e:
+            csa.sparse_decode_attn(q, K, V, Kbar, Vbar, dev(good), L, proxies=True, tok_idx=dev(bad_tok),
+                                   tok_logw=dev(logw))
+        assert e.value.status == csa.CSA_ERR_INVALID_ARG
+        with pytest.raises(csa.CsaError, match="tok_idx"):
+            csa.selective_decode_step(q, K, V, Kbar, Vbar, 3, L, tok_idx=dev(bad_tok), tok_logw=dev(logw))
+        checked = csa.sparse_decode_attn(q, K, V, Kbar, Vbar, dev(good), L, proxies=True, tok_idx=dev(tok),
+                                         tok_logw=dev(logw))
+        torch.cuda.synchronize()
+    finally:
+        csa.set_index_checks(prev)
+    plain = csa.sparse_decode_attn(q, K, V, Kbar, Vbar, dev(good), L, proxies=True, tok_idx=dev(tok),
+                                   tok_logw=dev(logw))
+    torch.cuda.synchronize()
+    for a, b in zip(checked, plain):
+        assert np.array_equal(bits(host(a)), bits(host(b)))
+
+
 def test_invalid_arguments_raise():
     q = torch.zeros((1, 4, 96), dtype=torch.bfloat16, device="cuda")
     K = torch.zeros((1, 2, 64, 96), dtype=torch.bfloat16, device="cuda")
