@@ -50,12 +50,15 @@ class Workload:
     block_size: int
     dtype: str  # "f32" or "bf16"
     k: int  # blocks read exactly per KV head
-    score_mode: str  # "summary", "exact_mass", "box", "cobs2", "cobs2_fp4" or "proxy_error"
+    score_mode: str  # "summary", "exact_mass", "box", "cobs2", "cobs2_fp4", "proxy_error" or "cluster"
     proxies: bool  # one count-aware proxy per unread block
     keys: str  # "heavy_hitters" or "clusters"
     n_clusters: int = 64
     coreset: int = 0  # weighted tokens per KV head
     description: str = ""
+    qgc: int = 0  # query-guided clusters per KV head (score_mode "cluster"), 0 = blocks
+    qgc_iters: int = 8  # Lloyd rounds of the cluster build
+    qgc_rank: int = 16  # dimensions of the projection the clusters are found in
 
     @property
     def group(self) -> int:
@@ -98,6 +101,10 @@ WORKLOADS = {
         Workload("llama3_8b_layer_b32_err", 1002, 32, 32, 8, 128, 32768, 64, "bf16", 5, "proxy_error", True,
                  "clusters", description="the headline layer with exact reads spent on the largest estimated "
                                          "proxy errors (mean and variance tokens)"),
+        Workload("llama3_8b_layer_b32_qgc", 1002, 32, 32, 8, 128, 32768, 64, "bf16", 5, "cluster", True,
+                 "clusters", qgc=512, description="the headline layer with one proxy per query-guided cluster "
+                                                  "(512 k-means clusters in the 16-dimensional query subspace) "
+                                                  "and the tokens of the top-5 clusters read exactly"),
     ]
 }
 
@@ -205,6 +212,22 @@ def generate(w: Workload, batches=None, threads: int | None = None) -> dict:
     out = {"q": q, "K": K, "V": V}
     if w.coreset:
         out["tok_idx"], out["tok_logw"] = tok_idx, tok_logw
+    return out
+
+
+def prefill_queries(w: Workload, count: int, batches=None) -> np.ndarray:
+    """Queries seen during prefill, [B', Hkv, count, d] float64: for each KV head, `count` draws
+    of the decode-query recipe (a centre of the KV head's key clusters + 0.5 N(0, I)) from a
+    stream of their own (seed, b, KV head, 2).  Random data only: what a caller derives from
+    them (the query basis of the cluster build) is computed by the caller."""
+    batches = list(range(w.batch)) if batches is None else list(batches)
+    out = np.empty((len(batches), w.n_kv_heads, count, w.head_dim), np.float64)
+    for i, b in enumerate(batches):
+        for j in range(w.n_kv_heads):
+            centres = _centres(w, _kv_rng(w, b, j)).astype(np.float64)
+            rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, b, j, 2])))
+            pick = rng.integers(w.n_clusters, size=count)
+            out[i, j] = centres[pick] + 0.5 * rng.standard_normal((count, w.head_dim))
     return out
 
 

@@ -457,3 +457,193 @@ int oracle_block_mass(const oracle_shape* s, const void* q, const void* K, const
     }
     return 0;
 }
+
+/* ----------------------------------------------------------------------------
+ * Query-guided clusters ("OpenAttention reads 1% of the KV cache -- Count-aware
+ * tail proxy", section "Three helpers that make the proxy accurate": keys are
+ * projected onto the top eigenvectors of the queries and clustered by k-means
+ * in that space once after prefill; each cluster then has one proxy).
+ * ------------------------------------------------------------------------- */
+
+/* Squared distance of projected point x to centroid c in r dimensions, the
+ * coordinates taken in order. */
+static double sq_dist(const double* x, const double* c, int r)
+{
+    double acc = 0.0;
+    for (int j = 0; j < r; ++j) {
+        const double t = x[j] - c[j];
+        acc += t * t;
+    }
+    return acc;
+}
+
+/* Nearest centroid of x among C; equal distances go to the lower index. */
+static int nearest(const double* x, const double* cent, int C, int r)
+{
+    int best = 0;
+    double bd = sq_dist(x, cent, r);
+    for (int c = 1; c < C; ++c) {
+        const double dc = sq_dist(x, cent + (size_t)c * r, r);
+        if (dc < bd) {
+            bd = dc;
+            best = c;
+        }
+    }
+    return best;
+}
+
+int oracle_cluster_build(const oracle_shape* s, int C, int r, int iters, const void* K, const void* V,
+                         const float* U, const int32_t* init_idx, int32_t* assign, int32_t* order,
+                         int32_t* offsets, void* Kc, void* Vc, double* cent_out)
+{
+    if (!shape_ok(s) || C < 1 || r < 1 || iters < 0 || !K || !V || !U || !init_idx || !assign || !order ||
+        !offsets || !Kc || !Vc)
+        return -1;
+    const int n = s->n_tokens, d = s->head_dim, pairs = s->batch * s->n_kv_heads;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic) reduction(| : bad)
+    for (int p = 0; p < pairs; ++p) {
+        const int b = p / s->n_kv_heads, j = p % s->n_kv_heads;
+        const float* Up = U + (size_t)p * d * r; /* [d, r] */
+        double* P = (double*)malloc(sizeof(double) * (size_t)n * r);
+        double* cent = (double*)malloc(sizeof(double) * (size_t)C * r);
+        double* sum = (double*)malloc(sizeof(double) * (size_t)C * r);
+        int* cnt = (int*)malloc(sizeof(int) * (size_t)C);
+        int32_t* a = assign + (size_t)p * n;
+        /* projections P_i = K_i U */
+        for (int i = 0; i < n; ++i)
+            for (int jj = 0; jj < r; ++jj) {
+                double acc = 0.0;
+                for (int t = 0; t < d; ++t)
+                    acc += elem(K, s->dtype, kv_off(s, b, j, n, i) + t) * (double)Up[(size_t)t * r + jj];
+                P[(size_t)i * r + jj] = acc;
+            }
+        /* initial centroids: the projections of the seed tokens */
+        for (int c = 0; c < C; ++c) {
+            const int i = init_idx[(size_t)p * C + c];
+            if (i < 0 || i >= n) bad = 1;
+            for (int jj = 0; jj < r; ++jj) cent[(size_t)c * r + jj] = (i >= 0 && i < n) ? P[(size_t)i * r + jj] : 0.0;
+        }
+        /* Lloyd's iterations: assign to the nearest centroid, move each centroid
+         * to the mean of its points (an empty cluster keeps its centroid) */
+        for (int it = 0; it <= iters; ++it) {
+            for (int i = 0; i < n; ++i) a[i] = nearest(P + (size_t)i * r, cent, C, r);
+            if (it == iters) break; /* the last assignment is to the final centroids */
+            for (int c = 0; c < C; ++c) {
+                cnt[c] = 0;
+                for (int jj = 0; jj < r; ++jj) sum[(size_t)c * r + jj] = 0.0;
+            }
+            for (int i = 0; i < n; ++i) { /* tokens in order */
+                cnt[a[i]] += 1;
+                for (int jj = 0; jj < r; ++jj) sum[(size_t)a[i] * r + jj] += P[(size_t)i * r + jj];
+            }
+            for (int c = 0; c < C; ++c)
+                if (cnt[c] > 0)
+                    for (int jj = 0; jj < r; ++jj) cent[(size_t)c * r + jj] = sum[(size_t)c * r + jj] / cnt[c];
+        }
+        /* the gathered layout: tokens by cluster, in token order within one */
+        int32_t* off = offsets + (size_t)p * (C + 1);
+        for (int c = 0; c < C; ++c) cnt[c] = 0;
+        for (int i = 0; i < n; ++i) cnt[a[i]] += 1;
+        off[0] = 0;
+        for (int c = 0; c < C; ++c) off[c + 1] = off[c] + cnt[c];
+        int32_t* ord = order + (size_t)p * n;
+        for (int c = 0; c < C; ++c) cnt[c] = 0;
+        for (int i = 0; i < n; ++i) ord[off[a[i]] + cnt[a[i]]++] = i;
+        /* per cluster the mean key and mean value, summed in token order in fp64,
+         * rounded once (zero rows for an empty cluster) */
+        for (int c = 0; c < C; ++c) {
+            const int m = off[c + 1] - off[c];
+            for (int t = 0; t < d; ++t) {
+                double sk = 0.0, sv = 0.0;
+                for (int o = off[c]; o < off[c + 1]; ++o) {
+                    sk += elem(K, s->dtype, kv_off(s, b, j, n, ord[o]) + t);
+                    sv += elem(V, s->dtype, kv_off(s, b, j, n, ord[o]) + t);
+                }
+                store(Kc, s->dtype, kv_off(s, b, j, C, c) + t, m > 0 ? sk / m : 0.0);
+                store(Vc, s->dtype, kv_off(s, b, j, C, c) + t, m > 0 ? sv / m : 0.0);
+            }
+        }
+        if (cent_out) memcpy(cent_out + (size_t)p * C * r, cent, sizeof(double) * (size_t)C * r);
+        free(cnt);
+        free(sum);
+        free(cent);
+        free(P);
+    }
+    return bad ? -1 : 0;
+}
+
+/* Cluster logits [B, Hq, C]: scale q_h . Kc_c + ln count_c (-inf for an empty
+ * cluster), the count-aware proxy's logit of the section "Skipping reviews
+ * without losing the verdict", per cluster instead of per block. */
+int oracle_cluster_logits(const oracle_shape* s, int C, const void* q, const void* Kc, const int32_t* offsets,
+                          double* logits)
+{
+    if (!shape_ok(s) || C < 1 || !q || !Kc || !offsets || !logits) return -1;
+    const int G = s->n_q_heads / s->n_kv_heads;
+#pragma omp parallel for schedule(dynamic)
+    for (int bh = 0; bh < s->batch * s->n_q_heads; ++bh) {
+        const int b = bh / s->n_q_heads, h = bh % s->n_q_heads, j = h / G;
+        const int32_t* off = offsets + ((size_t)b * s->n_kv_heads + j) * (C + 1);
+        for (int c = 0; c < C; ++c) {
+            const int m = off[c + 1] - off[c];
+            logits[(size_t)bh * C + c] =
+                m > 0 ? dot_scaled(s, q, q_off(s, b, h), Kc, kv_off(s, b, j, C, c)) + log((double)m) : -INFINITY;
+        }
+    }
+    return 0;
+}
+
+/* Attention over the virtual tokens of the clustered cache: every token of the
+ * k selected clusters (log-weight 0) and, with proxies, one proxy per other
+ * non-empty cluster (key Kc, value Vc, log-weight ln count).  The tokens of a
+ * cluster are the order[] entries of its range. */
+int oracle_cluster_attend(const oracle_shape* s, int C, const void* q, const void* K, const void* V,
+                          const void* Kc, const void* Vc, const int32_t* order, const int32_t* offsets,
+                          const int32_t* sel, int k, int proxy_mode, double* out, double* lse)
+{
+    if (!shape_ok(s) || C < 1 || !q || !K || !V || !order || !offsets || !out || !lse) return -1;
+    if (k < 0 || k > C || (k > 0 && !sel) || (proxy_mode != 0 && proxy_mode != 1)) return -1;
+    if (proxy_mode == 1 && (!Kc || !Vc)) return -1;
+    const int G = s->n_q_heads / s->n_kv_heads, n = s->n_tokens;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic) reduction(| : bad)
+    for (int bh = 0; bh < s->batch * s->n_q_heads; ++bh) {
+        const int b = bh / s->n_q_heads, h = bh % s->n_q_heads, j = h / G;
+        const size_t pair = (size_t)b * s->n_kv_heads + j;
+        const int32_t* off = offsets + pair * (C + 1);
+        const int32_t* ord = order + pair * n;
+        vtoken* e = (vtoken*)malloc(sizeof(vtoken) * ((size_t)n + C));
+        char* kept = (char*)calloc((size_t)C, 1);
+        int ne = 0;
+        for (int i = 0; i < k; ++i) {
+            const int c = sel[pair * k + i];
+            if (c < 0 || c >= C || kept[c]) { bad = 1; continue; }
+            kept[c] = 1;
+            for (int o = off[c]; o < off[c + 1]; ++o) {
+                const size_t ko = kv_off(s, b, j, n, ord[o]);
+                e[ne].logit = dot_scaled(s, q, q_off(s, b, h), K, ko);
+                e[ne].vbase = V;
+                e[ne].voff = ko;
+                ++ne;
+            }
+        }
+        if (proxy_mode == 1)
+            for (int c = 0; c < C; ++c) {
+                const int m = off[c + 1] - off[c];
+                if (kept[c] || m == 0) continue;
+                const size_t co = kv_off(s, b, j, C, c);
+                e[ne].logit = dot_scaled(s, q, q_off(s, b, h), Kc, co) + log((double)m);
+                e[ne].vbase = Vc;
+                e[ne].voff = co;
+                ++ne;
+            }
+        if (ne == 0)
+            bad = 1;
+        else
+            softmax_average(s, e, ne, out + (size_t)bh * s->head_dim, lse + bh);
+        free(kept);
+        free(e);
+    }
+    return bad ? -1 : 0;
+}

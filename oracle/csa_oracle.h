@@ -107,6 +107,35 @@ int oracle_block_mass(const oracle_shape* s, const void* q, const void* K, const
                       double* ln_m, double* centroid);
 
 /* Storage rounding exposed for the pins: fp64 -> bf16 bits (ties to even). */
+/* Query-guided clusters ("OpenAttention reads 1% of the KV cache -- Count-aware
+ * tail proxy", section "Three helpers that make the proxy accurate").  Per KV
+ * head: projections P_i = K_i U (U [B, Hkv, d, r], fp32, the caller's basis:
+ * the top-r eigenvectors of the queries' second moment), fp64, dimensions
+ * summed in order; centroids start at the projections of the seed tokens
+ * init_idx [B, Hkv, C]; `iters` rounds of (assign each token to the nearest
+ * centroid by squared distance, ties to the lower index; move each centroid to
+ * the mean of its points, summed in token order, an empty cluster keeping its
+ * centroid), then a final assignment.  Outputs: assign [B, Hkv, n]; order
+ * [B, Hkv, n] the tokens by cluster and token index; offsets [B, Hkv, C + 1]
+ * the clusters' ranges in order; Kc, Vc [B, Hkv, C, d] the mean key and value
+ * of each cluster (fp64 sums in token order, one rounding to the storage
+ * dtype; zero rows for an empty cluster); cent_out [B, Hkv, C, r] (may be
+ * NULL) the final centroids.  -1 on a seed index outside [0, n). */
+int oracle_cluster_build(const oracle_shape* s, int C, int r, int iters, const void* K, const void* V,
+                         const float* U, const int32_t* init_idx, int32_t* assign, int32_t* order,
+                         int32_t* offsets, void* Kc, void* Vc, double* cent_out);
+
+/* Cluster logits [B, Hq, C]: scale q_h . Kc_c + ln count_c, -inf for an empty
+ * cluster. */
+int oracle_cluster_logits(const oracle_shape* s, int C, const void* q, const void* Kc, const int32_t* offsets,
+                          double* logits);
+
+/* Attention over every token of the k selected clusters (log-weight 0) and,
+ * with proxy_mode 1, one proxy per other non-empty cluster (Kc, Vc, ln count). */
+int oracle_cluster_attend(const oracle_shape* s, int C, const void* q, const void* K, const void* V,
+                          const void* Kc, const void* Vc, const int32_t* order, const int32_t* offsets,
+                          const int32_t* sel, int k, int proxy_mode, double* out, double* lse);
+
 uint16_t oracle_round_bf16(double x);
 
 #ifdef __cplusplus

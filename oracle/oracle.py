@@ -109,6 +109,12 @@ def _load():
         lib.oracle_kv_box_build.restype = I
         lib.oracle_store_array.argtypes = [I, ctypes.c_size_t, P, P]
         lib.oracle_store_array.restype = I
+        lib.oracle_cluster_build.argtypes = [SP, I, I, I, P, P, P, P, P, P, P, P, P, P]
+        lib.oracle_cluster_build.restype = I
+        lib.oracle_cluster_logits.argtypes = [SP, I, P, P, P, P]
+        lib.oracle_cluster_logits.restype = I
+        lib.oracle_cluster_attend.argtypes = [SP, I, P, P, P, P, P, P, P, P, I, I, P, P]
+        lib.oracle_cluster_attend.restype = I
         for f in ("oracle_kv_summary_build", "oracle_block_logits", "oracle_group_score",
                   "oracle_topk", "oracle_attend", "oracle_dense", "oracle_block_mass"):
             getattr(lib, f).restype = I
@@ -487,3 +493,69 @@ def widen(shape_or_dtype, a):
     if dt == "f32":
         return np.asarray(a, np.float32).astype(np.float64)
     return (np.asarray(a, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Query-guided clusters ("OpenAttention reads 1% of the KV cache -- Count-aware
+# tail proxy", section "Three helpers that make the proxy accurate")
+# ---------------------------------------------------------------------------
+
+def cluster_build(shape: Shape, K, V, U, init_idx, iters: int):
+    """k-means of the keys projected on U [B, Hkv, d, r] (fp32), seeded at the tokens init_idx
+    [B, Hkv, C], `iters` Lloyd rounds then a final assignment.  Returns a dict: assign [B, Hkv, n],
+    order [B, Hkv, n], offsets [B, Hkv, C + 1], Kc, Vc [B, Hkv, C, d] (storage dtype), cent
+    [B, Hkv, C, r] (fp64 final centroids)."""
+    B, Hkv, n, d = shape.batch, shape.n_kv_heads, shape.n_tokens, shape.head_dim
+    K, V = _stored(shape, K, (B, Hkv, n, d)), _stored(shape, V, (B, Hkv, n, d))
+    U = np.ascontiguousarray(U, np.float32)
+    init_idx = np.ascontiguousarray(init_idx, np.int32)
+    r, C = U.shape[-1], init_idx.shape[-1]
+    assert U.shape == (B, Hkv, d, r) and init_idx.shape == (B, Hkv, C)
+    out = {"assign": np.empty((B, Hkv, n), np.int32), "order": np.empty((B, Hkv, n), np.int32),
+           "offsets": np.empty((B, Hkv, C + 1), np.int32), "Kc": np.empty((B, Hkv, C, d), shape.np_dtype),
+           "Vc": np.empty((B, Hkv, C, d), shape.np_dtype), "cent": np.empty((B, Hkv, C, r), np.float64)}
+    _check(_load().oracle_cluster_build(ctypes.byref(shape.c()), C, r, iters, _ptr(K), _ptr(V), _ptr(U),
+                                        _ptr(init_idx), _ptr(out["assign"]), _ptr(out["order"]),
+                                        _ptr(out["offsets"]), _ptr(out["Kc"]), _ptr(out["Vc"]), _ptr(out["cent"])),
+           "cluster_build")
+    return out
+
+
+def cluster_logits(shape: Shape, q, Kc, offsets):
+    """[B, Hq, C]: scale q.Kc + ln count per cluster (-inf when empty)."""
+    B, Hkv, d = shape.batch, shape.n_kv_heads, shape.head_dim
+    offsets = np.ascontiguousarray(offsets, np.int32)
+    C = offsets.shape[-1] - 1
+    q = _stored(shape, q, (B, shape.n_q_heads, d))
+    Kc = _stored(shape, Kc, (B, Hkv, C, d))
+    out = np.empty((B, shape.n_q_heads, C), np.float64)
+    _check(_load().oracle_cluster_logits(ctypes.byref(shape.c()), C, _ptr(q), _ptr(Kc), _ptr(offsets), _ptr(out)),
+           "cluster_logits")
+    return out
+
+
+def cluster_score(shape: Shape, q, Kc, offsets):
+    """Cluster scores [B, Hkv, C]: the group rule of block_score over the cluster logits."""
+    lg = cluster_logits(shape, q, Kc, offsets)
+    C = lg.shape[-1]
+    gs = Shape(shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, C, 1, shape.dtype, shape.scale)
+    return group_score(gs, lg)
+
+
+def cluster_attend(shape: Shape, q, K, V, Kc, Vc, order, offsets, sel, proxies: bool):
+    """Attention over every token of the selected clusters and a proxy per other cluster."""
+    B, Hkv, n, d = shape.batch, shape.n_kv_heads, shape.n_tokens, shape.head_dim
+    offsets = np.ascontiguousarray(offsets, np.int32)
+    C = offsets.shape[-1] - 1
+    q = _stored(shape, q, (B, shape.n_q_heads, d))
+    K, V = _stored(shape, K, (B, Hkv, n, d)), _stored(shape, V, (B, Hkv, n, d))
+    Kc, Vc = _stored(shape, Kc, (B, Hkv, C, d)), _stored(shape, Vc, (B, Hkv, C, d))
+    order = np.ascontiguousarray(order, np.int32)
+    sel = np.ascontiguousarray(sel, np.int32)
+    k = sel.shape[-1]
+    out = np.empty((B, shape.n_q_heads, d), np.float64)
+    lse = np.empty((B, shape.n_q_heads), np.float64)
+    _check(_load().oracle_cluster_attend(ctypes.byref(shape.c()), C, _ptr(q), _ptr(K), _ptr(V), _ptr(Kc), _ptr(Vc),
+                                         _ptr(order), _ptr(offsets), _ptr(sel), k, 1 if proxies else 0, _ptr(out),
+                                         _ptr(lse)), "cluster_attend")
+    return out, lse

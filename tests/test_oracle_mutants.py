@@ -32,6 +32,14 @@ MUTANTS = {
     "exact mass as the maximum logit": ("    return mx + log(sum);", "    return mx + 0.0 * log(sum);"),
     "box scored at its worst corner": ("acc += a > c ? a : c;", "acc += a < c ? a : c;"),
     "box maximum taken as the minimum": ("if (x > hi) hi = x;", "if (x < hi) hi = x;"),
+    "equal distances to the higher cluster": ("if (dc < bd) {", "if (dc <= bd) {"),
+    "centroid divided by count + 1": ("sum[(size_t)c * r + jj] / cnt[c];", "sum[(size_t)c * r + jj] / (cnt[c] + 1);"),
+    "cluster logit without ln count": ("Kc, kv_off(s, b, j, C, c)) + log((double)m)", "Kc, kv_off(s, b, j, C, c))"),
+    "cluster proxy without ln count": ("Kc, co) + log((double)m);", "Kc, co);"),
+    "cluster mean divided by n": ("m > 0 ? sk / m : 0.0", "m > 0 ? sk / n : 0.0"),
+    "projection with the basis transposed": ("(double)Up[(size_t)t * r + jj]", "(double)Up[(size_t)jj * d + t]"),
+    "selected cluster also kept as a proxy": ("if (kept[c] || m == 0) continue;", "if (m == 0) continue;"),
+    "no assignment to the final centroids": ("if (it == iters) break;", "if (it == iters) { a[0] = a[0]; }"),
 }
 
 BATTERY = [
@@ -53,6 +61,14 @@ BATTERY = [
     (P.test_box_build_is_elementwise_min_and_max, ("f32", 200, 16)),
     (P.test_box_score_bounds_every_token_logit, ("f32",)),
     (P.test_box_score_is_the_best_corner, ()),
+    (P.test_cluster_assignments_are_the_nearest_centroids, ()),
+    (P.test_cluster_centroids_are_the_means_of_their_points_at_convergence, ()),
+    (P.test_lloyd_rounds_never_increase_the_objective, ()),
+    (P.test_cluster_layout_is_a_stable_partition, ()),
+    (P.test_cluster_means_are_exact_means_rounded_once, ("bf16",)),
+    (P.test_one_token_per_cluster_makes_the_proxies_exact, ()),
+    (P.test_contiguous_clusters_are_the_block_method, (3,)),
+    (P.test_equal_distances_go_to_the_lower_cluster, ()),
 ]
 
 

@@ -854,3 +854,173 @@ def test_fp4_score_equals_bf16_score_on_grid_exact_descriptors():
     _, xi_hat = O.cov4_unpack(shp, P)
     assert np.array_equal(xi_hat, xi[..., 1:, :])
     assert np.abs(O.cobs2_fp4_logits(shp, q, P) - O.cobs2_logits(shp, q, Kcov)).max() < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# query-guided clusters ([OA] "Three helpers that make the proxy accurate")
+# ---------------------------------------------------------------------------
+
+import qgc_inputs as QI  # noqa: E402
+
+
+def qgc_case(seed=5, B=1, Hkv=2, G=2, d=64, n=1024, C=16, r=8, dtype="bf16"):
+    w = W.Workload("qgc_pin", 2000 + seed, B, Hkv * G, Hkv, d, n, 64, dtype, 3, "cluster", True, "clusters",
+                   n_clusters=16, qgc=C, qgc_rank=r)
+    data = W.generate(w)
+    U = QI.query_basis(W.prefill_queries(w, 256), r)
+    seeds = QI.seed_tokens(B, Hkv, n, C)
+    shp = O.Shape(B, Hkv * G, Hkv, d, n, 64, dtype)
+    return w, data, U, seeds, shp
+
+
+def projections(shp, K, U):
+    return np.einsum("bjnd,bjdr->bjnr", O.widen(shp, K), U.astype(np.float64))
+
+
+def test_cluster_assignments_are_the_nearest_centroids():
+    """Every token is assigned to the centroid nearest to its projection (numpy distances to the
+    oracle's final centroids; equal distances to the lower index)."""
+    w, data, U, seeds, shp = qgc_case()
+    res = O.cluster_build(shp, data["K"], data["V"], U, seeds, iters=4)
+    P = projections(shp, data["K"], U)
+    dist = ((P[:, :, :, None, :] - res["cent"][:, :, None, :, :]) ** 2).sum(-1)  # [B, Hkv, n, C]
+    near = dist.argmin(-1)
+    srt = np.sort(dist, axis=-1)
+    clear = (srt[..., 1] - srt[..., 0]) > 1e-9 * (1 + srt[..., 0])
+    assert clear.mean() > 0.99
+    assert np.array_equal(res["assign"][clear], near[clear])
+
+
+def test_cluster_centroids_are_the_means_of_their_points_at_convergence():
+    """Once the assignment no longer changes, each centroid is the mean of its points'
+    projections (k-means fixed point), and an empty cluster keeps its seed."""
+    w, data, U, seeds, shp = qgc_case(seed=6, C=12)
+    a = O.cluster_build(shp, data["K"], data["V"], U, seeds, iters=40)
+    b = O.cluster_build(shp, data["K"], data["V"], U, seeds, iters=41)
+    assert np.array_equal(a["assign"], b["assign"])
+    P = projections(shp, data["K"], U)
+    for bb in range(shp.batch):
+        for j in range(shp.n_kv_heads):
+            for c in range(seeds.shape[-1]):
+                pts = P[bb, j][a["assign"][bb, j] == c]
+                if len(pts):
+                    assert np.allclose(a["cent"][bb, j, c], pts.mean(0), rtol=0, atol=1e-9)
+
+
+def test_lloyd_rounds_never_increase_the_objective():
+    """The sum of squared distances to the assigned centroids does not grow with more rounds."""
+    w, data, U, seeds, shp = qgc_case(seed=7, C=24)
+    P = projections(shp, data["K"], U)
+    prev = None
+    for it in range(6):
+        res = O.cluster_build(shp, data["K"], data["V"], U, seeds, iters=it)
+        sse = sum(((P[b, j] - res["cent"][b, j][res["assign"][b, j]]) ** 2).sum()
+                  for b in range(shp.batch) for j in range(shp.n_kv_heads))
+        if prev is not None:
+            assert sse <= prev * (1 + 1e-12)
+        prev = sse
+
+
+def test_cluster_layout_is_a_stable_partition():
+    """order lists every token once, by cluster, in token order within a cluster; offsets are the
+    clusters' ranges and the counts of the assignment."""
+    w, data, U, seeds, shp = qgc_case(seed=8)
+    res = O.cluster_build(shp, data["K"], data["V"], U, seeds, iters=3)
+    n, C = shp.n_tokens, seeds.shape[-1]
+    for b in range(shp.batch):
+        for j in range(shp.n_kv_heads):
+            a, order, off = res["assign"][b, j], res["order"][b, j], res["offsets"][b, j]
+            assert np.array_equal(np.sort(order), np.arange(n))
+            assert off[0] == 0 and off[-1] == n and np.all(np.diff(off) == np.bincount(a, minlength=C))
+            for c in range(C):
+                seg = order[off[c]:off[c + 1]]
+                assert np.all(a[seg] == c) and np.all(np.diff(seg) > 0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_cluster_means_are_exact_means_rounded_once(dtype):
+    """The proxy of a cluster: its mean key and mean value, an exact rational mean rounded once
+    by an independent routine."""
+    w, data, U, seeds, shp = qgc_case(seed=9, n=512, C=8, dtype=dtype)
+    res = O.cluster_build(shp, data["K"], data["V"], U, seeds, iters=2)
+    Kw, Vw = nested(data["K"], dtype), nested(data["V"], dtype)
+    for j in range(shp.n_kv_heads):
+        off, order = res["offsets"][0, j], res["order"][0, j]
+        for c in range(3):
+            rows = order[off[c]:off[c + 1]]
+            if len(rows) == 0:
+                continue
+            for src, mean in ((Kw[0][j], res["Kc"]), (Vw[0][j], res["Vc"])):
+                exact = brute.mean_rows([src[i] for i in rows], dtype)
+                assert O.widen(dtype, mean[0, j, c]).tolist() == exact
+
+
+def test_one_token_per_cluster_makes_the_proxies_exact():
+    """As many clusters as tokens, each seeded at its own token: every cluster holds one token,
+    its proxy is that token, and attention equals dense for any selection."""
+    w, data, U, seeds, shp = qgc_case(seed=10, n=128, C=128, r=16)
+    res = O.cluster_build(shp, data["K"], data["V"], U, QI.seed_tokens(1, 2, 128, 128), iters=3)
+    assert np.all(np.diff(res["offsets"], axis=-1) == 1)
+    ref, ref_lse = O.dense_decode_attn(shp, data["q"], data["K"], data["V"])
+    for k in (0, 5):
+        sel = np.tile(np.arange(k, dtype=np.int32) * 7, (1, 2, 1))
+        out, lse = O.cluster_attend(shp, data["q"], data["K"], data["V"], res["Kc"], res["Vc"], res["order"],
+                                    res["offsets"], sel, True)
+        assert np.abs(out - ref).max() < 1e-12 and np.abs(lse - ref_lse).max() < 1e-12
+
+
+def test_equal_logit_cluster_proxy_is_exact():
+    """One cluster whose tokens all have the same logit: its count-aware proxy carries the
+    cluster's mass exactly, so the proxy alone equals dense attention (128 tokens: the stored
+    mean value is exact)."""
+    d, n = 64, 128
+    rng = np.random.default_rng(11)
+    q = np.zeros((1, 1, d))
+    q[0, 0, : d // 2] = rng.integers(-8, 9, d // 2) / 4
+    K = rng.integers(-8, 9, (1, 1, n, d)) / 4
+    K[0, 0, :, : d // 2] = rng.integers(-8, 9, d // 2) / 4
+    V = rng.integers(-8, 9, (1, 1, n, d)) / 4
+    q, K, V = (x.astype(np.float32) for x in (q, K, V))
+    shp = O.Shape(1, 1, 1, d, n, 16, "f32")
+    U = np.zeros((1, 1, d, 2), np.float32)
+    U[0, 0, 0, 0] = U[0, 0, 1, 1] = 1.0
+    res = O.cluster_build(shp, K, V, U, np.zeros((1, 1, 1), np.int32), iters=1)
+    out, lse = O.cluster_attend(shp, q, K, V, res["Kc"], res["Vc"], res["order"], res["offsets"],
+                                np.zeros((1, 1, 0), np.int32), True)
+    ref, ref_lse = O.dense_decode_attn(shp, q, K, V)
+    assert np.abs(out - ref).max() < 1e-12 and abs(lse - ref_lse).max() < 1e-12
+
+
+@pytest.mark.parametrize("G", [1, 3])
+def test_contiguous_clusters_are_the_block_method(G):
+    """With the layout of contiguous blocks (order the identity, ranges of L tokens), cluster
+    logits, scores and attention are those of the block summaries."""
+    q, K, V = rand_case(12, 1, 2 * G, 2, 64, 1000, "bf16")
+    L = 64
+    shp = O.Shape(1, 2 * G, 2, 64, 1000, L, "bf16")
+    nb = shp.n_blocks
+    Kbar, Vbar = O.kv_summary_build(shp, K, V)
+    order = np.tile(np.arange(1000, dtype=np.int32), (1, 2, 1))
+    offsets = np.tile(np.minimum(np.arange(nb + 1) * L, 1000).astype(np.int32), (1, 2, 1))
+    lg = O.cluster_logits(shp, q, Kbar, offsets)
+    assert np.allclose(lg, O.block_logits(shp, O.SUMMARY, q, Kbar), rtol=0, atol=1e-12)
+    sc = O.cluster_score(shp, q, Kbar, offsets)
+    assert np.allclose(sc, O.block_score(shp, O.SUMMARY, q, Kbar), rtol=0, atol=1e-12)
+    sel, _ = O.topk_select(sc, 3)
+    out, lse = O.cluster_attend(shp, q, K, V, Kbar, Vbar, order, offsets, sel, True)
+    ref, ref_lse = O.sparse_decode_attn(shp, q, K, V, Kbar, Vbar, sel, True)
+    assert np.abs(out - ref).max() < 1e-13 and np.abs(lse - ref_lse).max() < 1e-13
+
+
+def test_equal_distances_go_to_the_lower_cluster():
+    """Two seeds at tokens with identical keys: every point is as near to one as to the other,
+    so all of them join the lower cluster and the other stays empty (logit -inf, zero rows)."""
+    w, data, U, seeds, shp = qgc_case(seed=13, n=256, C=2)
+    K = data["K"].copy()
+    K[:, :, 200] = K[:, :, 10]
+    seeds = np.tile(np.array([10, 200], np.int32), (1, 2, 1))
+    res = O.cluster_build(shp, K, data["V"], U, seeds, iters=0)
+    assert np.all(res["assign"] == 0) and np.all(res["offsets"][..., 1] == 256)
+    assert np.all(res["Kc"][:, :, 1] == 0) and np.all(res["Vc"][:, :, 1] == 0)
+    lg = O.cluster_logits(shp, data["q"], res["Kc"], res["offsets"])
+    assert np.all(lg[:, :, 1] == -np.inf)
