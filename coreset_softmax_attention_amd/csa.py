@@ -25,6 +25,7 @@ CSA_WS_BLOCK_SCORE_SUMMARY, CSA_WS_BLOCK_SCORE_EXACT_MASS = 0, 1
 CSA_WS_SPARSE_DECODE_ATTN, CSA_WS_DENSE_DECODE_ATTN, CSA_WS_SELECTIVE_DECODE_STEP = 2, 3, 4
 CSA_WS_BLOCK_SCORE_BOX, CSA_WS_BLOCK_SCORE_COBS2, CSA_WS_BLOCK_SCORE_PROXY_ERROR = 5, 6, 7
 CSA_WS_BLOCK_SCORE_COBS2_FP4 = 8
+CSA_WS_KV_CLUSTER_BUILD, CSA_WS_CLUSTER_SCORE = 9, 10
 
 MODES = {"summary": CSA_SCORE_SUMMARY, "exact_mass": CSA_SCORE_EXACT_MASS, "box": CSA_SCORE_BOX,
          "cobs2": CSA_SCORE_COBS2, "proxy_error": CSA_SCORE_PROXY_ERROR, "cobs2_fp4": CSA_SCORE_COBS2_FP4}
@@ -81,6 +82,11 @@ _SIGS = {
                               ctypes.c_int, _P, _P, _P, _P, _P, _SZ, _P],
     "selective_decode_step_noalloc": [ctypes.POINTER(Shape), ctypes.c_int, _P, _P, _P, _P, _P, _I32, _P, _P, _I32,
                                       ctypes.c_int, _P, _P, _P, _P, _P],
+    "kv_cluster_build": [ctypes.POINTER(Shape), _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                         _SZ, _P],
+    "cluster_score": [ctypes.POINTER(Shape), _I32, _P, _P, _P, _P, _P, _SZ, _P],
+    "cluster_decode_attn": [ctypes.POINTER(Shape), _I32, _P, _P, _P, _P, _P, _P, _P, _I32, ctypes.c_int, _P, _P,
+                            _P],
 }
 CSA_STEP_NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -343,6 +349,64 @@ def selective_decode_step_noalloc(q, K, V, Kbar, Vbar, k: int, block_size: int, 
                                                _ptr(sel), _ptr(out), _ptr(lse), _stream(dev)),
            "selective_decode_step_noalloc")
     return out, lse, scores, sel
+
+
+def kv_cluster_build(K: torch.Tensor, V: torch.Tensor, U: torch.Tensor, seeds: torch.Tensor, iters: int,
+                     out: dict | None = None, ws=None) -> dict:
+    """Query-guided clusters of each KV head's keys: k-means of K U (U [B, Hkv, d, r] float32)
+    from the seed tokens seeds [B, Hkv, C] (int32), `iters` rounds and a final assignment.
+    Returns a dict of assign, order [B, Hkv, n], offsets [B, Hkv, C + 1] (int32), Kg, Vg
+    [B, Hkv, n, d] (the cache in cluster order) and Kc, Vc [B, Hkv, C, d] (cluster means);
+    tensors given in `out` are written in place."""
+    dev = _dev(K, V, U, seeds)
+    B, Hkv, n, d = K.shape
+    C, r = seeds.shape[-1], U.shape[-1]
+    shape = Shape(B, Hkv, Hkv, d, n, n, _dtype_code(K), 0.0)
+    o = dict(out or {})
+    want = {"assign": ((B, Hkv, n), torch.int32), "order": ((B, Hkv, n), torch.int32),
+            "offsets": ((B, Hkv, C + 1), torch.int32), "Kg": ((B, Hkv, n, d), K.dtype),
+            "Vg": ((B, Hkv, n, d), K.dtype), "Kc": ((B, Hkv, C, d), K.dtype), "Vc": ((B, Hkv, C, d), K.dtype)}
+    for name, (shp, dt) in want.items():
+        if o.get(name) is None:
+            o[name] = torch.empty(shp, dtype=dt, device=dev)
+    ws, wsb = _workspace(shape, CSA_WS_KV_CLUSTER_BUILD, C, r, ws, dev)
+    _check(lib().kv_cluster_build(ctypes.byref(shape), C, r, iters, _ptr(K), _ptr(V), _ptr(U), _ptr(seeds),
+                                  _ptr(o["assign"]), _ptr(o["order"]), _ptr(o["offsets"]), _ptr(o["Kg"]),
+                                  _ptr(o["Vg"]), _ptr(o["Kc"]), _ptr(o["Vc"]), _ptr(ws), wsb, _stream(dev)),
+           "kv_cluster_build")
+    return o
+
+
+def cluster_score(q: torch.Tensor, Kc: torch.Tensor, offsets: torch.Tensor, n_tokens: int, scale: float = 0.0,
+                  scores=None, ws=None):
+    """Cluster scores [B, Hkv, C]: scale q.Kc + ln count per head, combined by the block-score group rule."""
+    dev = _dev(q, Kc, offsets)
+    B, Hq, d = q.shape
+    _, Hkv, C, _ = Kc.shape
+    shape = Shape(B, Hq, Hkv, d, n_tokens, n_tokens, _dtype_code(Kc), float(scale))
+    scores = torch.empty((B, Hkv, C), dtype=torch.float32, device=dev) if scores is None else scores
+    ws, wsb = _workspace(shape, CSA_WS_CLUSTER_SCORE, C, 0, ws, dev)
+    _check(lib().cluster_score(ctypes.byref(shape), C, _ptr(q), _ptr(Kc), _ptr(offsets), _ptr(scores), _ptr(ws), wsb,
+                               _stream(dev)), "cluster_score")
+    return scores
+
+
+def cluster_decode_attn(q, Kg, Vg, Kc, Vc, offsets, sel, proxies: bool = True, scale: float = 0.0, out=None,
+                        lse=None):
+    """Attention over every token of the selected clusters (rows of Kg, Vg) and one proxy per
+    other non-empty cluster.  Returns (out [B, Hq, d] float32, lse [B, Hq] float32)."""
+    dev = _dev(q, Kg, Vg, Kc, Vc, offsets, sel)
+    shape = make_shape(q, Kg, Kg.shape[2], scale)
+    C = offsets.shape[-1] - 1
+    k = sel.shape[-1] if sel is not None else 0
+    B, Hq, d = q.shape
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev) if out is None else out
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if lse is None else lse
+    _check(lib().cluster_decode_attn(ctypes.byref(shape), C, _ptr(q), _ptr(Kg), _ptr(Vg), _ptr(Kc), _ptr(Vc),
+                                     _ptr(offsets), _ptr(sel), k,
+                                     CSA_PROXY_COMPLEMENT if proxies else CSA_PROXY_NONE, _ptr(out), _ptr(lse),
+                                     _stream(dev)), "cluster_decode_attn")
+    return out, lse
 
 
 def set_index_checks(enable: bool) -> bool:

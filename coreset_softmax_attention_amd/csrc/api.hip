@@ -536,6 +536,113 @@ int selective_decode_step_noalloc(const csa_shape* shape, csa_score_mode mode, c
                      sel, out, lse, static_ws, stream);
 }
 
+int kv_cluster_build(const csa_shape* shape, int32_t n_clusters, int32_t rank, int32_t iters, const void* K,
+                     const void* V, const float* U, const int32_t* seeds, int32_t* assign, int32_t* order,
+                     int32_t* offsets, void* Kg, void* Vg, void* Kc, void* Vc, void* ws, size_t ws_bytes,
+                     hipStream_t stream)
+{
+    csa::Dims d;
+    if (int rc = make_dims(shape, &d)) return rc;
+    if (iters < 0) return fail(CSA_ERR_INVALID_ARG, "kv_cluster_build: iters=%d is negative", iters);
+    if (n_clusters < 1 || rank < 1)
+        return fail(CSA_ERR_INVALID_ARG, "kv_cluster_build: n_clusters=%d rank=%d", n_clusters, rank);
+    if (!csa::cluster_build_ok(n_clusters, rank))
+        return fail(CSA_ERR_UNSUPPORTED,
+                    "kv_cluster_build: n_clusters=%d rank=%d (rank in {4, 8, 16, 32}, n_clusters <= %d, "
+                    "n_clusters * rank <= %zu)",
+                    n_clusters, rank, csa::kClusterMaxClusters, csa::kClusterCentroidLds / sizeof(double));
+    if (!K || !V || !U || !seeds || !assign || !order || !offsets || !Kg || !Vg || !Kc || !Vc)
+        return fail(CSA_ERR_INVALID_ARG, "kv_cluster_build: NULL pointer");
+    if (!aligned16(K) || !aligned16(V) || !aligned16(Kg) || !aligned16(Vg) || !aligned16(Kc) || !aligned16(Vc) ||
+        !aligned4(U) || !aligned4(seeds) || !aligned4(assign) || !aligned4(order) || !aligned4(offsets))
+        return fail(CSA_ERR_INVALID_ARG, "kv_cluster_build: misaligned pointer");
+    if (int rc = check_ws(csa::cluster_build_ws_bytes(d, n_clusters, rank), ws, ws_bytes)) return rc;
+    if (index_checks_on())
+        if (int rc = check_device_indices("kv_cluster_build (seeds)", d, nullptr, 0, seeds, n_clusters, stream))
+            return rc;
+    csa::ClusterBuild cb{};
+    cb.K = K;
+    cb.V = V;
+    cb.U = U;
+    cb.seeds = seeds;
+    cb.C = n_clusters;
+    cb.r = rank;
+    cb.iters = iters;
+    cb.assign = assign;
+    cb.order = order;
+    cb.offsets = offsets;
+    cb.Kg = Kg;
+    cb.Vg = Vg;
+    cb.Kc = Kc;
+    cb.Vc = Vc;
+    cb.proj = static_cast<double*>(ws);
+    cb.cent = reinterpret_cast<double*>(static_cast<char*>(ws) +
+                                        align256((size_t)d.pairs() * d.n * rank * sizeof(double)));
+    const hipError_t e = csa::launch_cluster_build(d, cb, stream);
+    return e == hipSuccess ? CSA_OK : hip_fail(e, "kv_cluster_build");
+}
+
+int cluster_score(const csa_shape* shape, int32_t n_clusters, const void* q, const void* Kc,
+                  const int32_t* offsets, float* scores, void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    csa::Dims d;
+    if (int rc = make_dims(shape, &d)) return rc;
+    if (n_clusters < 1) return fail(CSA_ERR_INVALID_ARG, "cluster_score: n_clusters=%d", n_clusters);
+    if (!q || !Kc || !offsets || !scores) return fail(CSA_ERR_INVALID_ARG, "cluster_score: NULL pointer");
+    if (!aligned16(q) || !aligned16(Kc) || !aligned4(offsets) || !aligned4(scores))
+        return fail(CSA_ERR_INVALID_ARG, "cluster_score: misaligned pointer");
+    csa::Dims dc = d;  // the clusters take the place of blocks
+    dc.nb = n_clusters;
+    if (int rc = check_ws(block_score_ws(dc), ws, ws_bytes)) return rc;
+    float* lg = d.G == 1 ? scores : static_cast<float*>(ws);
+    hipError_t e = csa::launch_cluster_logits(d, n_clusters, q, Kc, offsets, lg, stream);
+    if (e != hipSuccess) return hip_fail(e, "cluster_score");
+    if (d.G > 1) {
+        e = csa::score_finish_ok(dc) ? csa::launch_score_finish(dc, lg, scores, nullptr, 0, stream)
+                                     : csa::launch_group_score(dc, lg, scores, stream);
+        if (e != hipSuccess) return hip_fail(e, "cluster_score (group score)");
+    }
+    return CSA_OK;
+}
+
+int cluster_decode_attn(const csa_shape* shape, int32_t n_clusters, const void* q, const void* Kg, const void* Vg,
+                        const void* Kc, const void* Vc, const int32_t* offsets, const int32_t* sel, int32_t k,
+                        csa_proxy_mode proxy_arg, float* out, float* lse, hipStream_t stream)
+{
+    const int proxy_mode = raw_enum(proxy_arg);
+    csa::Dims d;
+    if (int rc = make_dims(shape, &d)) return rc;
+    if (proxy_mode != CSA_PROXY_NONE && proxy_mode != CSA_PROXY_COMPLEMENT)
+        return fail(CSA_ERR_INVALID_ARG, "cluster_decode_attn: unknown proxy mode %d", proxy_mode);
+    const int proxies = proxy_mode == CSA_PROXY_COMPLEMENT;
+    if (n_clusters < 1 || n_clusters > csa::kClusterMaxClusters)
+        return fail(n_clusters < 1 ? CSA_ERR_INVALID_ARG : CSA_ERR_UNSUPPORTED,
+                    "cluster_decode_attn: n_clusters=%d (1 .. %d)", n_clusters, csa::kClusterMaxClusters);
+    if (k < 0 || k > n_clusters)
+        return fail(CSA_ERR_INVALID_ARG, "cluster_decode_attn: k=%d outside [0, %d]", k, n_clusters);
+    if (k > csa::kClusterMaxSel)
+        return fail(CSA_ERR_UNSUPPORTED, "cluster_decode_attn: k=%d above %d", k, csa::kClusterMaxSel);
+    if (k == 0 && !proxies)
+        return fail(CSA_ERR_INVALID_ARG, "cluster_decode_attn: empty virtual-token set (k = 0, no proxies)");
+    if (d.dtype != csa::DT_BF16) return fail(CSA_ERR_UNSUPPORTED, "cluster_decode_attn: bfloat16 caches only");
+    if (d.G > 8) return fail(CSA_ERR_UNSUPPORTED, "cluster_decode_attn: group size %d above 8", d.G);
+    if ((long long)d.n * d.d * 2 >= (1ll << 32))
+        return fail(CSA_ERR_UNSUPPORTED, "cluster_decode_attn: one KV head's cache must be below 4 GiB");
+    if (!q || !Kg || !Vg || !offsets || !out || (k > 0 && !sel) || (proxies && (!Kc || !Vc)))
+        return fail(CSA_ERR_INVALID_ARG, "cluster_decode_attn: NULL pointer");
+    if (!aligned16(q) || !aligned16(Kg) || !aligned16(Vg) || (proxies && (!aligned16(Kc) || !aligned16(Vc))) ||
+        !aligned4(offsets) || !aligned4(out) || (lse && !aligned4(lse)) || (sel && !aligned4(sel)))
+        return fail(CSA_ERR_INVALID_ARG, "cluster_decode_attn: misaligned pointer");
+    if (index_checks_on()) {
+        csa::Dims dc = d;
+        dc.nb = n_clusters;
+        if (int rc = check_device_indices("cluster_decode_attn", dc, sel, k, nullptr, 0, stream)) return rc;
+    }
+    csa::ClusterAttn ca{q, Kg, Vg, proxies ? Kc : Kg, proxies ? Vc : Vg, offsets, sel, n_clusters, k, proxies, out, lse};
+    const hipError_t e = csa::launch_cluster_attention(d, ca, stream);
+    return e == hipSuccess ? CSA_OK : hip_fail(e, "cluster_decode_attn");
+}
+
 size_t csa_workspace_size(const csa_shape* shape, csa_entry entry_arg, int32_t k, int32_t m)
 {
     const int entry = raw_enum(entry_arg);
@@ -570,6 +677,21 @@ size_t csa_workspace_size(const csa_shape* shape, csa_entry entry_arg, int32_t k
         const int kk = k < d.nb ? k : d.nb;
         if (attn_rows_ok(d, kk, m, 1, 0) != CSA_OK) return 0;
         return step_ws(d, kk, m).total;
+    }
+    case CSA_WS_KV_CLUSTER_BUILD:
+        if (!csa::cluster_build_ok(k, m)) {
+            fail(CSA_ERR_UNSUPPORTED, "csa_workspace_size: n_clusters=%d rank=%d unsupported", k, m);
+            return 0;
+        }
+        return csa::cluster_build_ws_bytes(d, k, m);
+    case CSA_WS_CLUSTER_SCORE: {
+        if (k < 1) {
+            fail(CSA_ERR_INVALID_ARG, "csa_workspace_size: n_clusters=%d", k);
+            return 0;
+        }
+        csa::Dims dc = d;
+        dc.nb = k;
+        return block_score_ws(dc);
     }
     }
     fail(CSA_ERR_INVALID_ARG, "csa_workspace_size: unknown entry %d", entry);

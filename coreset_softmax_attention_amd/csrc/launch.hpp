@@ -134,6 +134,47 @@ struct StepInputs {
     float* lse;     // may be null
 };
 
+// ---- query-guided clusters (cluster.hip) -----------------------------------
+constexpr int kClusterMaxClusters = 8192;  // clusters per KV head
+constexpr int kClusterMaxSel = 256;        // selected clusters per KV head
+constexpr size_t kClusterCentroidLds = 65536;  // C r fp64 centroids in one workgroup's LDS
+
+struct ClusterBuild {
+    const void* K;
+    const void* V;
+    const float* U;        // [B, Hkv, d, r]
+    const int32_t* seeds;  // [B, Hkv, C]
+    int C, r, iters;
+    int32_t* assign;   // [B, Hkv, n]
+    int32_t* order;    // [B, Hkv, n]
+    int32_t* offsets;  // [B, Hkv, C + 1]
+    void* Kg;          // [B, Hkv, n, d] in cluster order
+    void* Vg;
+    void* Kc;          // [B, Hkv, C, d] cluster means
+    void* Vc;
+    double* proj;      // workspace: [B, Hkv, n, r] projections
+    double* cent;      // workspace: [B, Hkv, C, r] centroids
+};
+bool cluster_build_ok(int C, int r);  // r in {4, 8, 16, 32}, C r doubles fit kClusterCentroidLds
+size_t cluster_build_ws_bytes(const Dims& s, int C, int r);
+hipError_t launch_cluster_build(const Dims& s, const ClusterBuild& cb, hipStream_t st);
+// Cluster logits [B, Hq, C] (the scores themselves when G == 1).
+hipError_t launch_cluster_logits(const Dims& s, int C, const void* q, const void* Kc, const int32_t* offsets,
+                                 float* logits, hipStream_t st);
+struct ClusterAttn {
+    const void* q;
+    const void* Kg;
+    const void* Vg;
+    const void* Kc;
+    const void* Vc;
+    const int32_t* offsets;
+    const int32_t* sel;
+    int C, k, proxies;
+    float* out;
+    float* lse;
+};
+hipError_t launch_cluster_attention(const Dims& s, const ClusterAttn& ca, hipStream_t st);
+
 bool fused_step_ok(const Dims& s, int k, int m, int proxies);
 hipError_t launch_decode_step(const Dims& s, const StepInputs& in, hipStream_t st);
 hipError_t launch_attention(const Dims& s, const AttnPlan& plan, const AttnInputs& in, void* ws,

@@ -99,7 +99,9 @@ typedef enum csa_entry {
     CSA_WS_BLOCK_SCORE_BOX = 5,
     CSA_WS_BLOCK_SCORE_COBS2 = 6,
     CSA_WS_BLOCK_SCORE_PROXY_ERROR = 7,
-    CSA_WS_BLOCK_SCORE_COBS2_FP4 = 8
+    CSA_WS_BLOCK_SCORE_COBS2_FP4 = 8,
+    CSA_WS_KV_CLUSTER_BUILD = 9, /* k = n_clusters, m = rank */
+    CSA_WS_CLUSTER_SCORE = 10    /* k = n_clusters, m unused */
 } csa_entry;
 
 typedef struct csa_shape {
@@ -307,6 +309,70 @@ int selective_decode_step_noalloc(const csa_shape* shape, csa_score_mode mode, c
                                   csa_proxy_mode proxy_mode, float* scores, int32_t* sel, float* out, float* lse,
                                   hipStream_t stream);
 
+/*
+ * Query-guided clusters ([OA] "Three helpers that make the proxy accurate":
+ * the cache is clustered once after prefill so that each proxy hides tokens
+ * with nearly equal logits -- keys are projected onto the top eigenvectors of
+ * the queries and clustered by k-means in that space; the proxies of
+ * "Skipping reviews..." then stand for clusters instead of fixed blocks).
+ *
+ * kv_cluster_build -- per KV head, with C = n_clusters and r = rank:
+ *   1. projections P_i = K_i U in fp64 (U [B, Hkv, d, r] float, the caller's
+ *      basis, e.g. the top r eigenvectors of the queries' second moment), the
+ *      d products of a coordinate summed in order;
+ *   2. centroids start at P of the seed tokens seeds [B, Hkv, C] (int32 in
+ *      [0, n); a seed outside gives a zero centroid);
+ *   3. `iters` rounds of: assign each token to the nearest centroid (squared
+ *      distance over the r coordinates summed in order, ties to the lower
+ *      index); move each centroid to the mean of its points summed in token
+ *      order (an empty cluster keeps its centroid); then a final assignment;
+ *   4. outputs: assign [B, Hkv, n] int32; order [B, Hkv, n] int32, the tokens
+ *      by cluster and, within one, by index; offsets [B, Hkv, C + 1] int32,
+ *      cluster c holding order[offsets[c] .. offsets[c + 1]); Kg, Vg
+ *      [B, Hkv, n, d] the cache rows in that order; Kc, Vc [B, Hkv, C, d] the
+ *      mean key and value of each cluster (fp64 sums in token order, one
+ *      rounding to the storage dtype, zero rows for an empty cluster).
+ * Every step is fp64 with products and sums rounded one by one, so the
+ * results are the bits of a plain sequential evaluation.  Supported: r in
+ * {4, 8, 16, 32}, 1 <= C <= 8192 and C r <= 8192 (else CSA_ERR_UNSUPPORTED),
+ * iters >= 0.  Workspace: csa_workspace_size(shape, CSA_WS_KV_CLUSTER_BUILD,
+ * C, r) bytes.  With index checks on (csa_set_index_checks) a seed outside
+ * [0, n) is CSA_ERR_INVALID_ARG.  Run once per cache (after prefill).
+ */
+int kv_cluster_build(const csa_shape* shape, int32_t n_clusters, int32_t rank, int32_t iters, const void* K,
+                     const void* V, const float* U, const int32_t* seeds, int32_t* assign, int32_t* order,
+                     int32_t* offsets, void* Kg, void* Vg, void* Kc, void* Vc, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/*
+ * cluster_score -- the score of each cluster, per KV head: the cluster logit
+ * l_hc = scale q_h . Kc_c + ln count_c (-inf for an empty cluster; the logit of
+ * the cluster's count-aware proxy, [OA] "Skipping reviews..."), combined over
+ * the query heads of a KV head by the rule of block_score (G = 1: l_hc;
+ * G > 1: ln sum_h exp(l_hc - ln sum_c' e^{l_hc'}), [COBS] Eq. (5)).
+ * offsets from kv_cluster_build; writes scores [B, Hkv, C].  Workspace:
+ * csa_workspace_size(shape, CSA_WS_CLUSTER_SCORE, C, 0) bytes (0 when G = 1).
+ * The clusters to read are then topk_select(B Hkv, C, k, scores, sel).
+ */
+int cluster_score(const csa_shape* shape, int32_t n_clusters, const void* q, const void* Kc,
+                  const int32_t* offsets, float* scores, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * cluster_decode_attn -- one online-softmax pass per KV head over every token of
+ * the k selected clusters sel [B, Hkv, k] (log-weight 0; rows of Kg, Vg) and,
+ * with CSA_PROXY_COMPLEMENT, one proxy per other non-empty cluster (key Kc_c,
+ * value Vc_c, log-weight ln count_c) ([OA] "Three helpers...": exact tokens and
+ * proxies in one pass).  out, lse as for sparse_decode_attn (lse may be NULL).
+ * bfloat16 only (else CSA_ERR_UNSUPPORTED); G <= 8; 0 <= k <= min(C, 256);
+ * k = 0 without proxies is CSA_ERR_INVALID_ARG.  A selection entry outside
+ * [0, C) is skipped, a repeated one read twice (index checks reject both); a
+ * KV head whose virtual-token set is empty (every selected cluster empty, no
+ * proxies) gets NaN rows and lse -inf.  No workspace.
+ */
+int cluster_decode_attn(const csa_shape* shape, int32_t n_clusters, const void* q, const void* Kg, const void* Vg,
+                        const void* Kc, const void* Vc, const int32_t* offsets, const int32_t* sel, int32_t k,
+                        csa_proxy_mode proxy_mode, float* out, float* lse, hipStream_t stream);
+
 /* Workspace bytes needed by an entry point for this shape (k, m as the call
  * will pass them).  Returns 0 for an invalid shape (see csa_last_error()). */
 size_t csa_workspace_size(const csa_shape* shape, csa_entry entry, int32_t k, int32_t m);
@@ -320,7 +386,8 @@ const char* csa_last_error(void);
 /*
  * csa_set_index_checks -- debugging aid for the index arrays that live in
  * device memory and are otherwise trusted: with checks on, sparse_decode_attn
- * (sel, tok_idx) and selective_decode_step (tok_idx) first copy them to the
+ * (sel, tok_idx), selective_decode_step (tok_idx), kv_cluster_build (seeds) and
+ * cluster_decode_attn (sel, against [0, C)) first copy them to the
  * host, which waits for the earlier work on their stream (so such calls
  * synchronise and cannot be captured in a graph), and return
  * CSA_ERR_INVALID_ARG, launching nothing, for a selection row that names a

@@ -333,3 +333,52 @@ def test_out_of_range_enum_values_are_rejected(L, value):
         assert rc in (csa.CSA_ERR_INVALID_ARG, csa.CSA_ERR_UNSUPPORTED)
     if value not in range(0, 9):
         assert L.csa_workspace_size(ctypes.byref(s), value, 0, 0) == 0 and b"entry" in L.csa_last_error()
+
+
+def cluster_build(L, s, C=64, r=16, iters=2, ptr=FAKE, U=FAKE, ws=FAKE, wsb=1 << 40):
+    p = ptr
+    return L.kv_cluster_build(ctypes.byref(s), C, r, iters, p, p, U, p, p, p, p, p, p, p, p, ws, wsb, None)
+
+
+def test_cluster_build_argument_checks(L):
+    s = shape()
+    assert cluster_build(L, s, r=5) == csa.CSA_ERR_UNSUPPORTED
+    assert cluster_build(L, s, r=64) == csa.CSA_ERR_UNSUPPORTED
+    assert cluster_build(L, s, C=8193, r=4) == csa.CSA_ERR_UNSUPPORTED
+    assert cluster_build(L, s, C=1024, r=16) == csa.CSA_ERR_UNSUPPORTED  # 1024 x 16 centroids over the LDS
+    assert cluster_build(L, s, C=0) == csa.CSA_ERR_INVALID_ARG
+    assert cluster_build(L, s, iters=-1) == csa.CSA_ERR_INVALID_ARG
+    assert cluster_build(L, s, ptr=None) == csa.CSA_ERR_INVALID_ARG
+    assert cluster_build(L, s, U=FAKE + 2) == csa.CSA_ERR_INVALID_ARG
+    assert cluster_build(L, s, ws=None, wsb=0) == csa.CSA_ERR_WORKSPACE
+    need = csa.workspace_size(s, csa.CSA_WS_KV_CLUSTER_BUILD, 64, 16)
+    # projections [B, Hkv, n, r] and centroids [B, Hkv, C, r], fp64
+    assert need == ((2 * 2 * 1024 * 16 * 8 + 255) // 256) * 256 + 2 * 2 * 64 * 16 * 8
+    assert cluster_build(L, s, wsb=need - 1) == csa.CSA_ERR_WORKSPACE
+    assert cluster_build(L, s, ws=FAKE + 16) == csa.CSA_ERR_WORKSPACE  # not 256-byte aligned
+    assert csa.workspace_size(s, csa.CSA_WS_KV_CLUSTER_BUILD, 64, 5) == 0
+
+
+def test_cluster_score_and_attention_argument_checks(L):
+    s = shape()
+    # G = 4: logits [B, Hq, C] in the workspace
+    assert csa.workspace_size(s, csa.CSA_WS_CLUSTER_SCORE, 100, 0) == 2 * 8 * 100 * 4
+    assert csa.workspace_size(shape(Hq=2), csa.CSA_WS_CLUSTER_SCORE, 100, 0) == 0
+    assert L.cluster_score(ctypes.byref(s), 100, FAKE, FAKE, FAKE, FAKE, None, 0, None) == csa.CSA_ERR_WORKSPACE
+    assert L.cluster_score(ctypes.byref(s), 0, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == csa.CSA_ERR_INVALID_ARG
+    assert L.cluster_score(ctypes.byref(s), 100, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == \
+        csa.CSA_ERR_INVALID_ARG
+
+    def attn(s, C=64, k=4, proxy=csa.CSA_PROXY_COMPLEMENT, sel=FAKE, kc=FAKE):
+        return L.cluster_decode_attn(ctypes.byref(s), C, FAKE, FAKE, FAKE, kc, kc, FAKE, sel, k, proxy, FAKE, FAKE,
+                                     None)
+
+    assert attn(shape(dtype=csa.CSA_F32)) == csa.CSA_ERR_UNSUPPORTED
+    assert attn(shape(Hq=18)) == csa.CSA_ERR_UNSUPPORTED  # G = 9
+    assert attn(s, k=65) == csa.CSA_ERR_INVALID_ARG
+    assert attn(s, C=1000, k=257) == csa.CSA_ERR_UNSUPPORTED
+    assert attn(s, C=9000) == csa.CSA_ERR_UNSUPPORTED
+    assert attn(s, k=0, proxy=csa.CSA_PROXY_NONE) == csa.CSA_ERR_INVALID_ARG
+    assert attn(s, proxy=2) == csa.CSA_ERR_INVALID_ARG
+    assert attn(s, sel=None) == csa.CSA_ERR_INVALID_ARG
+    assert attn(s, kc=None) == csa.CSA_ERR_INVALID_ARG
