@@ -67,7 +67,8 @@ def parse():
 HERE = os.path.dirname(os.path.abspath(__file__))
 COPY_PROBE_BYTES = 1 << 30
 # kernels whose HBM traffic is reported, by the name rocprofv3 records
-TRAFFIC_KERNELS = {"decode_step": "decode_step_kernel", "sparse_decode_attn": "attn_mfma_kernel"}
+TRAFFIC_KERNELS = {"decode_step": "decode_step_kernel", "sparse_decode_attn": "attn_mfma_kernel",
+                   "cluster_decode_attn": "cluster_attn_kernel", "cluster_logits": "cluster_logits_kernel"}
 
 
 def source_hash(csrc=None):
@@ -103,17 +104,21 @@ def counters_to_traffic(fetch_db, write_db, copy_fetch_db, copy_write_db, out_pa
         con.close()
         vals = [v for n, v in rows if name_part in n]
         if not vals:
-            raise SystemExit(f"{db}: no {counter} rows for a kernel named like {name_part!r}")
+            return None, 0
         return sum(vals) / len(vals), len(vals)
 
     copy_fetch, _ = per_dispatch(copy_fetch_db, "FETCH_SIZE", "copyBuffer")
     copy_write, _ = per_dispatch(copy_write_db, "WRITE_SIZE", "copyBuffer")
+    if copy_fetch is None or copy_write is None:
+        raise SystemExit("the copy-probe runs hold no copyBuffer dispatch")
     fetch_scale = COPY_PROBE_BYTES / (copy_fetch * 1024.0)
     write_scale = COPY_PROBE_BYTES / (copy_write * 1024.0)
     kernels = {}
     for key, name in TRAFFIC_KERNELS.items():
         f, nf = per_dispatch(fetch_db, "FETCH_SIZE", name)
         w, nw = per_dispatch(write_db, "WRITE_SIZE", name)
+        if f is None or w is None:  # not run by this workload
+            continue
         kernels[key] = {"kernel": name, "fetch_kib": f, "write_kib": w, "dispatches": [nf, nw],
                         "bytes": f * 1024.0 * fetch_scale + w * 1024.0 * write_scale}
     rec = {"workload": workload, "source_hash": source_hash(),
@@ -121,6 +126,8 @@ def counters_to_traffic(fetch_db, write_db, copy_fetch_db, copy_write_db, out_pa
                           "fetch_scale": fetch_scale, "write_scale": write_scale},
            "kernels": kernels,
            "bytes_per_launch": {k: v["bytes"] for k, v in kernels.items()}}
+    if not kernels:
+        raise SystemExit(f"{fetch_db}: none of the reported kernels ran")
     with open(out_path, "w") as fh:
         json.dump(rec, fh, indent=1)
         fh.write("\n")
@@ -209,6 +216,65 @@ def step_bytes(w, m=0):
     return pairs * per_read, pairs * per_write
 
 
+def graph_windows(g, steps, nwin):
+    """ms per step of `nwin` windows, each one replay of a graph of `steps` launches.  A GPU
+    sleep is queued before each window's start event, so the host has submitted the replay
+    before the GPU reaches it: the window holds the launches' GPU time only."""
+    import torch
+
+    out = []
+    for _ in range(nwin):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(200_000)  # about 0.1 ms at the GPU clock
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b) / steps)
+    return out
+
+
+def timed(fn, reps):
+    """ms of `reps` eager calls of fn(r), HIP events around the loop."""
+    import torch
+
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for r in range(reps):
+        fn(r)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b)
+
+
+def capture(fns, steps, nwin, warm):
+    """One HIP graph per named route holding exactly `steps` launches of fn(i); each is replayed
+    in `nwin` timed windows.  Returns {name: [ms per step of each window]}."""
+    import torch
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm the capture stream
+        for i in range(warm):
+            for fn in fns.values():
+                fn(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graphs = {}
+    for name, fn in fns.items():
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                fn(i)
+        graphs[name] = g
+    for g in graphs.values():
+        g.replay()
+    torch.cuda.synchronize()
+    return {name: graph_windows(g, steps, nwin) for name, g in graphs.items()}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -236,6 +302,9 @@ def main():
 
         build_lib.build()
     w = W.WORKLOADS[args.workload or W.HEADLINE]
+    if w.score_mode == "cluster":
+        cluster_main(args, w)
+        return
     t0 = time.time()
     data = W.generate(w)
     print(f"[bench] generated {w.name} in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
@@ -316,32 +385,6 @@ def main():
         csa.selective_decode_step(q, K, V, Kbar, Vbar, w.k, w.block_size, mode=w.score_mode, proxies=w.proxies,
                                   tok_idx=tok_idx, tok_logw=tok_logw, out=out, lse=lse, ws=ws_step)
 
-    def graph_windows(g, steps, nwin):
-        """ms per step of `nwin` windows, each one replay of a graph of `steps` launches.  A GPU
-        sleep is queued before each window's start event, so the host has submitted the replay
-        before the GPU reaches it: the window holds the launches' GPU time only."""
-        out = []
-        for _ in range(nwin):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            torch.cuda._sleep(200_000)  # about 0.1 ms at the GPU clock
-            a.record()
-            g.replay()
-            b.record()
-            torch.cuda.synchronize()
-            out.append(a.elapsed_time(b) / steps)
-        return out
-
-    def timed(fn, reps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record()
-        for r in range(reps):
-            fn(r)
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b)
-
     # eager
     for i in range(args.warmup):
         step(i)
@@ -355,28 +398,10 @@ def main():
     graph_ms = attn_ms = score_ms = modular_ms = None
     windows = None
     if not args.no_graph:
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):  # warm the capture stream
-            for i in range(NL):
-                step(i)
-                modular(i)
-        torch.cuda.current_stream().wait_stream(s)
-        torch.cuda.synchronize()
         # one graph per route holding exactly K launches (layers cycled); each timed window
         # replays it once, so a window times exactly K steps
-        graphs = {}
-        for name, fn in (("step", step), ("modular", modular), ("score", lambda i: score_select(layers[i % NL])),
-                         ("attn", lambda i: attend(layers[i % NL]))):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for i in range(args.steps):
-                    fn(i)
-            graphs[name] = g
-        for g in graphs.values():
-            g.replay()
-        torch.cuda.synchronize()
-        windows = {name: graph_windows(g, args.steps, args.windows) for name, g in graphs.items()}
+        windows = capture({"step": step, "modular": modular, "score": lambda i: score_select(layers[i % NL]),
+                           "attn": lambda i: attend(layers[i % NL])}, args.steps, args.windows, NL)
         per = {name: float(np.median(v)) for name, v in windows.items()}
         graph_ms, modular_ms, score_ms, attn_ms = per["step"], per["modular"], per["score"], per["attn"]
     else:
@@ -462,6 +487,203 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
+
+
+def cluster_bytes(w, sizes, sel):
+    """Bytes the cluster decode step must move (reads, writes), and those of its attention
+    kernel alone, from the selection actually made.  The step: every mean key once (it ranks
+    the clusters and gives the proxy logits), the cluster ranges, the mean values of the
+    unread non-empty clusters, the exact key/value rows of the selected clusters, the queries,
+    the selection, the outputs with their log-normalisers.  The attention kernel: the mean key
+    and value of each unread non-empty cluster, the exact rows, the ranges, the queries and
+    selection, the outputs."""
+    e, d, G, C = w.elem_bytes, w.head_dim, w.group, w.qgc
+    pairs = w.batch * w.n_kv_heads
+    sizes = sizes.reshape(pairs, C).astype(np.int64)
+    sel = sel.reshape(pairs, -1).astype(np.int64)
+    exact = int(np.take_along_axis(sizes, sel, axis=1).sum())
+    unread = int((sizes > 0).sum()) - int((np.take_along_axis(sizes, sel, axis=1) > 0).sum())
+    row = d * e
+    common = pairs * ((C + 1) * 4 + G * row + 4 * sel.shape[1]) + exact * 2 * row
+    writes = pairs * G * (d + 1) * 4
+    step_rd = common + pairs * C * row + unread * row
+    attn_rd = common + unread * 2 * row
+    return {"step": (step_rd, writes), "attn": (attn_rd, writes), "exact_tokens": int(exact),
+            "unread_clusters": unread}
+
+
+def cluster_main(args, w):
+    """The decode step over query-guided clusters: cluster_score -> topk_select ->
+    cluster_decode_attn over a cache clustered once beforehand (kv_cluster_build, timed once
+    for information).  Same timing scheme as the block path."""
+    import torch
+
+    sys.path.insert(0, os.path.join(HERE, "tests"))
+    import qgc_inputs as QI
+    from coreset_softmax_attention_amd import csa
+    from coreset_softmax_attention_amd import workloads as W
+
+    t0 = time.time()
+    data = W.generate(w)
+    U = QI.query_basis(W.prefill_queries(w, 256), w.qgc_rank)
+    seeds = QI.seed_tokens(w.batch, w.n_kv_heads, w.n_tokens, w.qgc)
+    print(f"[bench] generated {w.name} in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    NL = max(1, args.layers)
+    q = csa.to_device(data["q"], dev)
+    K0, V0 = csa.to_device(data["K"], dev), csa.to_device(data["V"], dev)
+    Ud, seedd = torch.from_numpy(U).to(dev), torch.from_numpy(seeds).to(dev)
+    del data
+    built = csa.kv_cluster_build(K0, V0, Ud, seedd, w.qgc_iters)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    csa.kv_cluster_build(K0, V0, Ud, seedd, w.qgc_iters, out=built)
+    e1.record()
+    torch.cuda.synchronize()
+    build_ms = e0.elapsed_time(e1)
+    del K0, V0
+    layer0 = (built["Kg"], built["Vg"], built["Kc"], built["Vc"], built["offsets"])
+    layers = [layer0] + [tuple(x.clone() for x in layer0) for _ in range(NL - 1)]
+    torch.cuda.synchronize()
+
+    B, Hq, Hkv, C = w.batch, w.n_q_heads, w.n_kv_heads, w.qgc
+    shape = csa.make_shape(q, layer0[0], w.n_tokens)
+    scores = torch.empty((B, Hkv, C), dtype=torch.float32, device=dev)
+    sel = torch.empty((B, Hkv, min(w.k, C)), dtype=torch.int32, device=dev)
+    out = torch.empty((B, Hq, w.head_dim), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, csa.workspace_size(shape, csa.CSA_WS_CLUSTER_SCORE, C, 0)), dtype=torch.uint8,
+                     device=dev)
+    ws_step = torch.empty(max(1, csa.workspace_size(shape, csa.CSA_WS_CLUSTER_DECODE_STEP, w.k, C)),
+                          dtype=torch.uint8, device=dev)
+
+    def score_select(i):
+        Kg, Vg, Kc, Vc, offs = layers[i % NL]
+        csa.cluster_score(q, Kc, offs, w.n_tokens, scores=scores, ws=ws)
+        csa.topk_select(scores, w.k, sel=sel)
+
+    def attend(i):
+        Kg, Vg, Kc, Vc, offs = layers[i % NL]
+        csa.cluster_decode_attn(q, Kg, Vg, Kc, Vc, offs, sel, proxies=w.proxies, out=out, lse=lse)
+
+    def modular(i):
+        score_select(i)
+        attend(i)
+
+    def step(i):
+        Kg, Vg, Kc, Vc, offs = layers[i % NL]
+        csa.cluster_decode_step(q, Kg, Vg, Kc, Vc, offs, w.k, proxies=w.proxies, sel=sel, out=out, lse=lse,
+                                ws=ws_step)
+
+    for i in range(args.warmup):
+        step(i)
+        modular(i)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    eager_ms = timed(step, args.steps) / args.steps
+    wall = time.perf_counter() - wall0
+    windows = None
+    modular_ms = None
+    if not args.no_graph:
+        windows = capture({"step": step, "modular": modular, "score": score_select, "attn": attend}, args.steps,
+                          args.windows, NL)
+        per = {name: float(np.median(v)) for name, v in windows.items()}
+        t_step, modular_ms, score_ms, attn_ms = per["step"], per["modular"], per["score"], per["attn"]
+    else:
+        t_step, score_ms = eager_ms, None
+        attn_ms = timed(attend, args.steps) / args.steps
+    step(0)
+    torch.cuda.synchronize()
+    sizes = torch.diff(layer0[4], dim=-1).cpu().numpy()
+    by = cluster_bytes(w, sizes, sel.cpu().numpy())
+    step_achieved = sum(by["step"]) / (t_step * 1e-3) / 1e9
+    attn_achieved = sum(by["attn"]) / (attn_ms * 1e-3) / 1e9
+    traffic = load_traffic(args.traffic or default_traffic_path(w.name))
+    cpu = None if args.no_cpu_baseline else cluster_cpu_baseline(w, args.cpu_seconds)
+    result = {
+        "metric": "selective decode attn: queries/s + achieved HBM GB/s, B=32, 32K ctx, 1% read",
+        "value": B / (t_step * 1e-3),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "timing_detail": timing_detail(args, windows),
+        "ms_per_step": t_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded generator; no dataset or weights)",
+        "config": {
+            "workload": w.name, "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": w.head_dim,
+            "context": w.n_tokens, "clusters": C, "cluster_rank": w.qgc_rank, "cluster_rounds": w.qgc_iters,
+            "k_clusters": w.k, "exact_read_fraction": by["exact_tokens"] / (B * Hkv * w.n_tokens),
+            "proxies": w.proxies, "layers_cycled": NL,
+            "timing": "HIP graph of the decode step replayed" if windows else "eager",
+            "entry_point": "cluster_decode_step",
+        },
+        "achieved_hbm_gb_s": step_achieved,
+        "eager_ms_per_step": eager_ms,
+        "eager_wall_s": wall,
+        "modular_ms_per_step": modular_ms,
+        "modular_breakdown_us": {"cluster_score+topk_select": score_ms * 1e3 if score_ms else None,
+                                 "cluster_decode_attn": attn_ms * 1e3},
+        "kv_cluster_build_ms": build_ms,
+        "roofline": {
+            "kernel": "cluster_decode_attn (cluster_attn_kernel)",
+            "bound": "hbm",
+            "achieved": attn_achieved,
+            "peak": 8000.0,
+            "unit": "GB/s",
+            "frac": attn_achieved / 8000.0,
+            "traffic": traffic.get("cluster_decode_attn") if isinstance(traffic, dict) else None,
+            "algorithmic_bytes": sum(by["attn"]),
+        },
+        "roofline_step": {
+            "kernel": "cluster_decode_step (score-and-select kernel, then cluster_attn_kernel)",
+            "bound": "hbm",
+            "achieved": step_achieved,
+            "peak": 8000.0,
+            "unit": "GB/s",
+            "frac": step_achieved / 8000.0,
+            "algorithmic_bytes": sum(by["step"]),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def cluster_cpu_baseline(w, budget_s):
+    """The fp64 oracle's cluster decode step (cluster scores, top-k, attention) on the host cores
+    for the first few sequences; their clustering (prefill state) is built before timing."""
+    sys.path.insert(0, HERE)
+    sys.path.insert(0, os.path.join(HERE, "tests"))
+    import qgc_inputs as QI
+    from coreset_softmax_attention_amd import workloads as W
+    from oracle import oracle as O
+
+    nseq = min(4, w.batch)
+    sub = W.generate(w, batches=range(nseq))
+    U = QI.query_basis(W.prefill_queries(w, 256, batches=range(nseq)), w.qgc_rank)
+    seeds = QI.seed_tokens(nseq, w.n_kv_heads, w.n_tokens, w.qgc)
+    shp = O.Shape(nseq, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_tokens, w.block_size, w.dtype)
+    cl = O.cluster_build(shp, sub["K"], sub["V"], U, seeds, w.qgc_iters)  # cache state, not timed
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        score = O.cluster_score(shp, sub["q"], cl["Kc"], cl["offsets"])
+        sel, _ = O.topk_select(score, w.k)
+        O.cluster_attend(shp, sub["q"], sub["K"], sub["V"], cl["Kc"], cl["Vc"], cl["order"], cl["offsets"], sel,
+                         w.proxies)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 100000:
+            break
+    cores = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
+    return {"value": nseq * reps / el, "unit": "queries/s", "cores": cores, "kind": "oracle",
+            "sample": f"{reps} repetitions of the cluster decode step for the first {nseq} of {w.batch} sequences "
+                      f"({el:.1f} s, fp64, OpenMP over query heads)", "cpu": cpu_model()}
 
 
 def timing_detail(args, windows):

@@ -25,7 +25,7 @@ CSA_WS_BLOCK_SCORE_SUMMARY, CSA_WS_BLOCK_SCORE_EXACT_MASS = 0, 1
 CSA_WS_SPARSE_DECODE_ATTN, CSA_WS_DENSE_DECODE_ATTN, CSA_WS_SELECTIVE_DECODE_STEP = 2, 3, 4
 CSA_WS_BLOCK_SCORE_BOX, CSA_WS_BLOCK_SCORE_COBS2, CSA_WS_BLOCK_SCORE_PROXY_ERROR = 5, 6, 7
 CSA_WS_BLOCK_SCORE_COBS2_FP4 = 8
-CSA_WS_KV_CLUSTER_BUILD, CSA_WS_CLUSTER_SCORE = 9, 10
+CSA_WS_KV_CLUSTER_BUILD, CSA_WS_CLUSTER_SCORE, CSA_WS_CLUSTER_DECODE_STEP = 9, 10, 11
 
 MODES = {"summary": CSA_SCORE_SUMMARY, "exact_mass": CSA_SCORE_EXACT_MASS, "box": CSA_SCORE_BOX,
          "cobs2": CSA_SCORE_COBS2, "proxy_error": CSA_SCORE_PROXY_ERROR, "cobs2_fp4": CSA_SCORE_COBS2_FP4}
@@ -87,6 +87,8 @@ _SIGS = {
     "cluster_score": [ctypes.POINTER(Shape), _I32, _P, _P, _P, _P, _P, _SZ, _P],
     "cluster_decode_attn": [ctypes.POINTER(Shape), _I32, _P, _P, _P, _P, _P, _P, _P, _I32, ctypes.c_int, _P, _P,
                             _P],
+    "cluster_decode_step": [ctypes.POINTER(Shape), _I32, _P, _P, _P, _P, _P, _P, _I32, ctypes.c_int, _P, _P, _P, _P,
+                            _P, _SZ, _P],
 }
 CSA_STEP_NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -407,6 +409,29 @@ def cluster_decode_attn(q, Kg, Vg, Kc, Vc, offsets, sel, proxies: bool = True, s
                                      CSA_PROXY_COMPLEMENT if proxies else CSA_PROXY_NONE, _ptr(out), _ptr(lse),
                                      _stream(dev)), "cluster_decode_attn")
     return out, lse
+
+
+def cluster_decode_step(q, Kg, Vg, Kc, Vc, offsets, k: int, proxies: bool = True, scale: float = 0.0, scores=None,
+                        sel=None, out=None, lse=None, ws=None, want_scores: bool = False, want_sel: bool = False):
+    """cluster_score -> topk_select -> cluster_decode_attn in one call.
+    Returns (out, lse, scores or None, sel or None)."""
+    dev = _dev(q, Kg, Vg, Kc, Vc, offsets)
+    shape = make_shape(q, Kg, Kg.shape[2], scale)
+    C = offsets.shape[-1] - 1
+    B, Hq, d = q.shape
+    Hkv = Kg.shape[1]
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev) if out is None else out
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if lse is None else lse
+    if want_scores and scores is None:
+        scores = torch.empty((B, Hkv, C), dtype=torch.float32, device=dev)
+    if want_sel and sel is None:
+        sel = torch.empty((B, Hkv, min(k, C)), dtype=torch.int32, device=dev)
+    ws, wsb = _workspace(shape, CSA_WS_CLUSTER_DECODE_STEP, k, C, ws, dev)
+    _check(lib().cluster_decode_step(ctypes.byref(shape), C, _ptr(q), _ptr(Kg), _ptr(Vg), _ptr(Kc), _ptr(Vc),
+                                     _ptr(offsets), k, CSA_PROXY_COMPLEMENT if proxies else CSA_PROXY_NONE,
+                                     _ptr(scores), _ptr(sel), _ptr(out), _ptr(lse), _ptr(ws), wsb, _stream(dev)),
+           "cluster_decode_step")
+    return out, lse, scores, sel
 
 
 def set_index_checks(enable: bool) -> bool:

@@ -196,6 +196,62 @@ StepWs step_ws(const csa::Dims& d, int k, int m)
     return w;
 }
 
+// ---- query-guided clusters ---------------------------------------------------
+
+// The cluster shape: clusters take the place of blocks.
+csa::Dims cluster_dims(const csa::Dims& d, int C)
+{
+    csa::Dims dc = d;
+    dc.nb = C;
+    return dc;
+}
+
+// Workspace of cluster_decode_step: scores | sel | per-head logits.
+struct ClusterStepWs {
+    size_t scores, sel, logits, total;
+};
+
+ClusterStepWs cluster_step_ws(const csa::Dims& d, int C, int k)
+{
+    ClusterStepWs w{};
+    const csa::Dims dc = cluster_dims(d, C);
+    w.scores = align256((size_t)d.pairs() * C * sizeof(float));
+    w.sel = align256((size_t)d.pairs() * (k > 0 ? k : 1) * sizeof(int32_t));
+    w.logits = align256(block_score_ws(dc));
+    w.total = w.scores + w.sel + w.logits;
+    return w;
+}
+
+// Cluster scores (and, when k > 0, the top-k to sel).  bfloat16 with G <= 8 and
+// G C <= 16384: the matrix-core summary-score kernels with count terms from the
+// ranges -- one workgroup per KV head (selecting too when k <= 32 and C <= 2048)
+// with 32 or more KV heads, else logits split over tiles; otherwise a scalar
+// logit kernel and the group score.  logits: [B, Hq, C] scratch (G > 1).
+hipError_t cluster_scores(const csa::Dims& d, int C, const void* q, const void* Kc, const int32_t* offsets,
+                          float* scores, int32_t* sel, int k, float* logits, hipStream_t st)
+{
+    const csa::Dims dc = cluster_dims(d, C);
+    hipError_t e;
+    bool selected = false;
+    if (csa::fused_summary_score_ok(dc)) {
+        selected = k > 0 && csa::split_select_ok(dc, k);
+        if (d.pairs() >= csa::kFusedStepMinPairs)
+            e = csa::launch_score_summary_fused(dc, q, Kc, scores, st, false, offsets, selected ? sel : nullptr,
+                                                selected ? k : 0);
+        else
+            e = csa::launch_score_summary_split(dc, q, Kc, d.G == 1 ? scores : logits, scores,
+                                                selected ? sel : nullptr, selected ? k : 0, st, false, offsets);
+    } else {
+        float* lg = d.G == 1 ? scores : logits;
+        e = csa::launch_cluster_logits(d, C, q, Kc, offsets, lg, st);
+        if (e == hipSuccess && d.G > 1)
+            e = csa::score_finish_ok(dc) ? csa::launch_score_finish(dc, lg, scores, nullptr, 0, st)
+                                         : csa::launch_group_score(dc, lg, scores, st);
+    }
+    if (e == hipSuccess && k > 0 && !selected) e = csa::launch_topk(d.pairs(), C, k, scores, sel, st);
+    return e;
+}
+
 // ---- the static scratch of selective_decode_step_noalloc ---------------------
 
 constexpr size_t kScratchBytes = (size_t)CSA_STEP_NOALLOC_SCRATCH_BYTES;
@@ -591,17 +647,41 @@ int cluster_score(const csa_shape* shape, int32_t n_clusters, const void* q, con
     if (!q || !Kc || !offsets || !scores) return fail(CSA_ERR_INVALID_ARG, "cluster_score: NULL pointer");
     if (!aligned16(q) || !aligned16(Kc) || !aligned4(offsets) || !aligned4(scores))
         return fail(CSA_ERR_INVALID_ARG, "cluster_score: misaligned pointer");
-    csa::Dims dc = d;  // the clusters take the place of blocks
-    dc.nb = n_clusters;
-    if (int rc = check_ws(block_score_ws(dc), ws, ws_bytes)) return rc;
-    float* lg = d.G == 1 ? scores : static_cast<float*>(ws);
-    hipError_t e = csa::launch_cluster_logits(d, n_clusters, q, Kc, offsets, lg, stream);
-    if (e != hipSuccess) return hip_fail(e, "cluster_score");
-    if (d.G > 1) {
-        e = csa::score_finish_ok(dc) ? csa::launch_score_finish(dc, lg, scores, nullptr, 0, stream)
-                                     : csa::launch_group_score(dc, lg, scores, stream);
-        if (e != hipSuccess) return hip_fail(e, "cluster_score (group score)");
-    }
+    if (n_clusters > csa::kClusterMaxClusters)
+        return fail(CSA_ERR_UNSUPPORTED, "cluster_score: n_clusters=%d above %d", n_clusters, csa::kClusterMaxClusters);
+    if ((long long)n_clusters * d.d * (d.dtype == csa::DT_F32 ? 4 : 2) >= (1ll << 32))
+        return fail(CSA_ERR_UNSUPPORTED, "cluster_score: one KV head's mean keys must be below 4 GiB");
+    if (int rc = check_ws(block_score_ws(cluster_dims(d, n_clusters)), ws, ws_bytes)) return rc;
+    const hipError_t e = cluster_scores(d, n_clusters, q, Kc, offsets, scores, nullptr, 0, static_cast<float*>(ws),
+                                        stream);
+    return e == hipSuccess ? CSA_OK : hip_fail(e, "cluster_score");
+}
+
+// Arguments of the cluster attention shared by cluster_decode_attn and
+// cluster_decode_step (sel is checked by the caller).
+int check_cluster_attn(const char* where, const csa::Dims& d, int n_clusters, int k, int proxy_mode, const void* q,
+                       const void* Kg, const void* Vg, const void* Kc, const void* Vc, const int32_t* offsets,
+                       const float* out, const float* lse)
+{
+    if (proxy_mode != CSA_PROXY_NONE && proxy_mode != CSA_PROXY_COMPLEMENT)
+        return fail(CSA_ERR_INVALID_ARG, "%s: unknown proxy mode %d", where, proxy_mode);
+    const int proxies = proxy_mode == CSA_PROXY_COMPLEMENT;
+    if (n_clusters < 1 || n_clusters > csa::kClusterMaxClusters)
+        return fail(n_clusters < 1 ? CSA_ERR_INVALID_ARG : CSA_ERR_UNSUPPORTED, "%s: n_clusters=%d (1 .. %d)", where,
+                    n_clusters, csa::kClusterMaxClusters);
+    if (k < 0 || k > n_clusters) return fail(CSA_ERR_INVALID_ARG, "%s: k=%d outside [0, %d]", where, k, n_clusters);
+    if (k > csa::kClusterMaxSel) return fail(CSA_ERR_UNSUPPORTED, "%s: k=%d above %d", where, k, csa::kClusterMaxSel);
+    if (k == 0 && !proxies)
+        return fail(CSA_ERR_INVALID_ARG, "%s: empty virtual-token set (k = 0, no proxies)", where);
+    if (d.dtype != csa::DT_BF16) return fail(CSA_ERR_UNSUPPORTED, "%s: bfloat16 caches only", where);
+    if (d.G > 8) return fail(CSA_ERR_UNSUPPORTED, "%s: group size %d above 8", where, d.G);
+    if ((long long)d.n * d.d * 2 >= (1ll << 32))
+        return fail(CSA_ERR_UNSUPPORTED, "%s: one KV head's cache must be below 4 GiB", where);
+    if (!q || !Kg || !Vg || !offsets || !out || (proxies && (!Kc || !Vc)))
+        return fail(CSA_ERR_INVALID_ARG, "%s: NULL pointer", where);
+    if (!aligned16(q) || !aligned16(Kg) || !aligned16(Vg) || (proxies && (!aligned16(Kc) || !aligned16(Vc))) ||
+        !aligned4(offsets) || !aligned4(out) || (lse && !aligned4(lse)))
+        return fail(CSA_ERR_INVALID_ARG, "%s: misaligned pointer", where);
     return CSA_OK;
 }
 
@@ -612,27 +692,12 @@ int cluster_decode_attn(const csa_shape* shape, int32_t n_clusters, const void* 
     const int proxy_mode = raw_enum(proxy_arg);
     csa::Dims d;
     if (int rc = make_dims(shape, &d)) return rc;
-    if (proxy_mode != CSA_PROXY_NONE && proxy_mode != CSA_PROXY_COMPLEMENT)
-        return fail(CSA_ERR_INVALID_ARG, "cluster_decode_attn: unknown proxy mode %d", proxy_mode);
+    if (int rc = check_cluster_attn("cluster_decode_attn", d, n_clusters, k, proxy_mode, q, Kg, Vg, Kc, Vc, offsets,
+                                    out, lse))
+        return rc;
     const int proxies = proxy_mode == CSA_PROXY_COMPLEMENT;
-    if (n_clusters < 1 || n_clusters > csa::kClusterMaxClusters)
-        return fail(n_clusters < 1 ? CSA_ERR_INVALID_ARG : CSA_ERR_UNSUPPORTED,
-                    "cluster_decode_attn: n_clusters=%d (1 .. %d)", n_clusters, csa::kClusterMaxClusters);
-    if (k < 0 || k > n_clusters)
-        return fail(CSA_ERR_INVALID_ARG, "cluster_decode_attn: k=%d outside [0, %d]", k, n_clusters);
-    if (k > csa::kClusterMaxSel)
-        return fail(CSA_ERR_UNSUPPORTED, "cluster_decode_attn: k=%d above %d", k, csa::kClusterMaxSel);
-    if (k == 0 && !proxies)
-        return fail(CSA_ERR_INVALID_ARG, "cluster_decode_attn: empty virtual-token set (k = 0, no proxies)");
-    if (d.dtype != csa::DT_BF16) return fail(CSA_ERR_UNSUPPORTED, "cluster_decode_attn: bfloat16 caches only");
-    if (d.G > 8) return fail(CSA_ERR_UNSUPPORTED, "cluster_decode_attn: group size %d above 8", d.G);
-    if ((long long)d.n * d.d * 2 >= (1ll << 32))
-        return fail(CSA_ERR_UNSUPPORTED, "cluster_decode_attn: one KV head's cache must be below 4 GiB");
-    if (!q || !Kg || !Vg || !offsets || !out || (k > 0 && !sel) || (proxies && (!Kc || !Vc)))
-        return fail(CSA_ERR_INVALID_ARG, "cluster_decode_attn: NULL pointer");
-    if (!aligned16(q) || !aligned16(Kg) || !aligned16(Vg) || (proxies && (!aligned16(Kc) || !aligned16(Vc))) ||
-        !aligned4(offsets) || !aligned4(out) || (lse && !aligned4(lse)) || (sel && !aligned4(sel)))
-        return fail(CSA_ERR_INVALID_ARG, "cluster_decode_attn: misaligned pointer");
+    if (k > 0 && !sel) return fail(CSA_ERR_INVALID_ARG, "cluster_decode_attn: NULL pointer");
+    if (sel && !aligned4(sel)) return fail(CSA_ERR_INVALID_ARG, "cluster_decode_attn: misaligned pointer");
     if (index_checks_on()) {
         csa::Dims dc = d;
         dc.nb = n_clusters;
@@ -641,6 +706,36 @@ int cluster_decode_attn(const csa_shape* shape, int32_t n_clusters, const void* 
     csa::ClusterAttn ca{q, Kg, Vg, proxies ? Kc : Kg, proxies ? Vc : Vg, offsets, sel, n_clusters, k, proxies, out, lse};
     const hipError_t e = csa::launch_cluster_attention(d, ca, stream);
     return e == hipSuccess ? CSA_OK : hip_fail(e, "cluster_decode_attn");
+}
+
+int cluster_decode_step(const csa_shape* shape, int32_t n_clusters, const void* q, const void* Kg, const void* Vg,
+                        const void* Kc, const void* Vc, const int32_t* offsets, int32_t k, csa_proxy_mode proxy_arg,
+                        float* scores, int32_t* sel, float* out, float* lse, void* ws, size_t ws_bytes,
+                        hipStream_t stream)
+{
+    const int proxy_mode = raw_enum(proxy_arg);
+    csa::Dims d;
+    if (int rc = make_dims(shape, &d)) return rc;
+    if (k < 0) return fail(CSA_ERR_INVALID_ARG, "cluster_decode_step: k=%d is negative", k);
+    const int kk = n_clusters >= 1 && k > n_clusters ? n_clusters : k;
+    if (int rc = check_cluster_attn("cluster_decode_step", d, n_clusters, kk, proxy_mode, q, Kg, Vg, Kc, Vc, offsets,
+                                    out, lse))
+        return rc;
+    if (!Kc) return fail(CSA_ERR_INVALID_ARG, "cluster_decode_step: Kc is NULL (it ranks the clusters)");
+    if (!aligned16(Kc) || (scores && !aligned4(scores)) || (sel && !aligned4(sel)))
+        return fail(CSA_ERR_INVALID_ARG, "cluster_decode_step: misaligned pointer");
+    const ClusterStepWs w = cluster_step_ws(d, n_clusters, kk);
+    if (int rc = check_ws(w.total, ws, ws_bytes)) return rc;
+    char* base = static_cast<char*>(ws);
+    float* sc = scores ? scores : reinterpret_cast<float*>(base);
+    int32_t* sl = sel ? sel : reinterpret_cast<int32_t*>(base + w.scores);
+    float* lg = reinterpret_cast<float*>(base + w.scores + w.sel);
+    hipError_t e = cluster_scores(d, n_clusters, q, Kc, offsets, sc, sl, kk, lg, stream);
+    if (e != hipSuccess) return hip_fail(e, "cluster_decode_step (scores)");
+    const int proxies = proxy_mode == CSA_PROXY_COMPLEMENT;
+    csa::ClusterAttn ca{q, Kg, Vg, proxies ? Kc : Kg, proxies ? Vc : Vg, offsets, sl, n_clusters, kk, proxies, out, lse};
+    e = csa::launch_cluster_attention(d, ca, stream);
+    return e == hipSuccess ? CSA_OK : hip_fail(e, "cluster_decode_step");
 }
 
 size_t csa_workspace_size(const csa_shape* shape, csa_entry entry_arg, int32_t k, int32_t m)
@@ -689,10 +784,14 @@ size_t csa_workspace_size(const csa_shape* shape, csa_entry entry_arg, int32_t k
             fail(CSA_ERR_INVALID_ARG, "csa_workspace_size: n_clusters=%d", k);
             return 0;
         }
-        csa::Dims dc = d;
-        dc.nb = k;
-        return block_score_ws(dc);
+        return block_score_ws(cluster_dims(d, k));
     }
+    case CSA_WS_CLUSTER_DECODE_STEP:
+        if (m < 1 || k < 0) {
+            fail(CSA_ERR_INVALID_ARG, "csa_workspace_size: n_clusters=%d (passed as m) or k=%d out of range", m, k);
+            return 0;
+        }
+        return cluster_step_ws(d, m, k < m ? k : m).total;
     }
     fail(CSA_ERR_INVALID_ARG, "csa_workspace_size: unknown entry %d", entry);
     return 0;

@@ -59,8 +59,12 @@ hipError_t launch_score_err(const Dims& s, const void* q, const void* Kvar, floa
 // (one workgroup per KV head); available when fused_summary_score_ok().
 bool fused_summary_score_ok(const Dims& s);
 // box = true: box scores from Kbox rows ([min | max], 2d wide) instead of Kbar.
+// offsets (clusters): per-row count terms ln(offsets[r + 1] - offsets[r]) from
+// the ranges [B, Hkv, nb + 1] instead of the block sizes.  k > 0 (at most 32,
+// nb <= 2048): the top-k of the scores to sel as well; scores may then be null.
 hipError_t launch_score_summary_fused(const Dims& s, const void* q, const void* Kbar, float* scores, hipStream_t st,
-                                      bool box = false);
+                                      bool box = false, const int32_t* offsets = nullptr, int32_t* sel = nullptr,
+                                      int k = 0);
 // The same in two kernels for few KV heads: logits over (KV head, tile chunk)
 // workgroups into `logits` ([B, Hq, nb]; may be `scores` when G == 1), then one
 // workgroup per KV head for the group scores (to `scores`, may be null) and,
@@ -71,7 +75,8 @@ bool split_select_ok(const Dims& s, int k);
 bool score_finish_ok(const Dims& s);
 hipError_t launch_score_finish(const Dims& s, const float* logits, float* scores, int32_t* sel, int k, hipStream_t st);
 hipError_t launch_score_summary_split(const Dims& s, const void* q, const void* Kbar, float* logits, float* scores,
-                                      int32_t* sel, int k, hipStream_t st, bool box = false);
+                                      int32_t* sel, int k, hipStream_t st, bool box = false,
+                                      const int32_t* offsets = nullptr);
 
 // ---- top-k -----------------------------------------------------------------
 hipError_t launch_topk(int rows, int nb, int k, const float* scores, int32_t* sel, hipStream_t st);

@@ -393,9 +393,21 @@ struct FusedScoreParams {
     float* logits;  // split: [B, Hq, nb] (the scores when G == 1)
     int32_t* sel;   // finish: selection [B, Hkv, k] when k > 0
     float* parts;   // proxy-error split: per (KV head, tile, head) log2 (max, sum) of the summary logits
+    const int32_t* offsets;  // clusters: ranges [B, Hkv, nb + 1] give the count terms (else blocks)
     int Hq, Hkv, G, nb, k, chunks;
     float scale, ln_L, ln_last;
 };
+
+// ln of the token count of row r: a block's (ln L, or the last block's), or a
+// cluster's from its range (-inf when empty).  off: this KV head's ranges or null.
+__device__ __forceinline__ float count_term(const FusedScoreParams& p, const int32_t* off, int r)
+{
+    if (off) {
+        const int c = off[r + 1] - off[r];
+        return c > 0 ? logf((float)c) : kNegInf;
+    }
+    return r == p.nb - 1 ? p.ln_last : p.ln_L;
+}
 
 // The mean keys of the tile of blocks [base, base + 32) in the A-operand layout
 // (lane (n16, g16): row n16 of each 16-row half, 16-byte chunks 4 s + g16).
@@ -421,7 +433,7 @@ __device__ __forceinline__ void load_key_tile(__amdgpu_buffer_rsrc_t kr, int bas
 template <int D>
 __device__ __forceinline__ void key_tile_logits(const FusedScoreParams& p, const KeyTile<D>& t,
                                                 const bf16x8_t (&bq)[D / 32], int base, float* dst, int stride,
-                                                int lane)
+                                                int lane, const int32_t* off)
 {
     constexpr int KS = D / 32;
     const int n16 = lane & 15, g16 = lane >> 4;
@@ -438,7 +450,7 @@ __device__ __forceinline__ void key_tile_logits(const FusedScoreParams& p, const
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = base + rb * 16 + 4 * g16 + i;
-                if (row < p.nb) dst[n16 * stride + row] = fmaf(c[rb][i], p.scale, row == p.nb - 1 ? p.ln_last : p.ln_L);
+                if (row < p.nb) dst[n16 * stride + row] = fmaf(c[rb][i], p.scale, count_term(p, off, row));
             }
     }
 }
@@ -494,6 +506,30 @@ __device__ __forceinline__ void load_score_q(const char* q_first_head, int nh, i
     }
 }
 
+// The top-k of the nb scores lsm[0 .. nb) of one KV head, by the whole
+// workgroup (NW waves), to out[0 .. k): the waves' maxima bound the search when
+// nb fits one value per thread, else one wave ranks them all.
+template <int NW>
+__device__ __forceinline__ void select_in_lds(const float* lsm, int nb, int k, int32_t* out, uint32_t* cand,
+                                              uint32_t* topk_sm)
+{
+    const int lane = threadIdx.x & 63;
+    auto emit = [&](int r, int idx) { out[r] = idx; };
+    auto one_wave_topk = [&]() {
+        auto load = [&](int i) { return lsm[i]; };
+        if (nb <= 8 * 64)
+            wave_topk<8>(load, nb, k, lane, cand, emit);
+        else
+            wave_topk<kFinishMaxBlocks / 64>(load, nb, k, lane, cand, emit);
+    };
+    if (nb <= NW * 64) {
+        uint32_t key[1] = {(int)threadIdx.x < nb ? order_key(lsm[threadIdx.x]) : 0u};
+        block_topk<NW, 1>(key, nb, k, topk_sm, one_wave_topk, emit);
+    } else if (threadIdx.x < 64) {
+        one_wave_topk();
+    }
+}
+
 template <int D, bool BOX>
 __global__ void __launch_bounds__(kFusedWaves * 64) score_summary_fused_kernel(const FusedScoreParams p)
 {
@@ -502,7 +538,10 @@ __global__ void __launch_bounds__(kFusedWaves * 64) score_summary_fused_kernel(c
     __shared__ float lse_h[8];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    __shared__ uint32_t cand[128];              // candidates of the one-wave ranking
+    __shared__ uint32_t topk_sm[2 * NW + 128];  // wave maxima, overflow flags, candidate slots
     const int pair = blockIdx.x, b = pair / p.Hkv, j = pair - b * p.Hkv;
+    const int32_t* off = p.offsets ? p.offsets + (size_t)pair * (p.nb + 1) : nullptr;
 
     bf16x8_t bq[KS];
     load_score_q<D, BOX>(p.q + ((size_t)b * p.Hq + (size_t)j * p.G) * QB, p.G, lane, bq);
@@ -512,11 +551,15 @@ __global__ void __launch_bounds__(kFusedWaves * 64) score_summary_fused_kernel(c
         const int base1 = base + NW * 32;
         load_key_tile<D>(kr, base, lane, t0);
         if (base1 < p.nb) load_key_tile<D>(kr, base1, lane, t1);
-        key_tile_logits<D>(p, t0, bq, base, lsm, p.nb, lane);
-        if (base1 < p.nb) key_tile_logits<D>(p, t1, bq, base1, lsm, p.nb, lane);
+        key_tile_logits<D>(p, t0, bq, base, lsm, p.nb, lane, off);
+        if (base1 < p.nb) key_tile_logits<D>(p, t1, bq, base1, lsm, p.nb, lane, off);
     }
     __syncthreads();
-    group_scores_in_lds<NW>(lsm, lse_h, p.G, p.nb, p.scores + (size_t)pair * p.nb);
+    group_scores_in_lds<NW>(lsm, lse_h, p.G, p.nb, p.scores ? p.scores + (size_t)pair * p.nb : nullptr);
+    if (p.k > 0) {
+        __syncthreads();
+        select_in_lds<NW>(lsm, p.nb, p.k, p.sel + (size_t)pair * p.k, cand, topk_sm);
+    }
 }
 
 // Split logits: workgroup (pair, chunk) computes tiles chunk * kSplitWaves + wave.
@@ -535,7 +578,8 @@ __global__ void __launch_bounds__(kSplitWaves * 64) score_logits_split_kernel(co
     const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(p.Kbar + (size_t)pair * p.nb * RB, (uint32_t)p.nb * RB);
     KeyTile<D> t;
     load_key_tile<D>(kr, base, lane, t);
-    key_tile_logits<D>(p, t, bq, base, p.logits + (size_t)pair * p.G * p.nb, p.nb, lane);
+    key_tile_logits<D>(p, t, bq, base, p.logits + (size_t)pair * p.G * p.nb, p.nb, lane,
+                       p.offsets ? p.offsets + (size_t)pair * (p.nb + 1) : nullptr);
 }
 
 // Second-order logits (COBS, cumulant expansion of ln m_b truncated at second
@@ -991,21 +1035,7 @@ __global__ void __launch_bounds__(kFusedWaves * 64) score_finish_kernel(const Fu
     group_scores_in_lds<NW>(lsm, lse_h, G, nb, p.scores ? p.scores + (size_t)pair * nb : nullptr, p.parts != nullptr);
     if (p.k > 0) {
         __syncthreads();
-        int32_t* out = p.sel + (size_t)pair * p.k;
-        auto emit = [&](int r, int idx) { out[r] = idx; };
-        auto one_wave_topk = [&]() {
-            auto load = [&](int i) { return lsm[i]; };
-            if (nb <= 8 * 64)
-                wave_topk<8>(load, nb, p.k, lane, cand, emit);
-            else
-                wave_topk<kFinishMaxBlocks / 64>(load, nb, p.k, lane, cand, emit);
-        };
-        if (nb <= NW * 64) {  // the bound from the waves' maxima; one wave over more blocks
-            uint32_t key[1] = {(int)threadIdx.x < nb ? order_key(lsm[threadIdx.x]) : 0u};
-            block_topk<NW, 1>(key, nb, p.k, topk_sm, one_wave_topk, emit);
-        } else if (threadIdx.x < 64) {
-            one_wave_topk();
-        }
+        select_in_lds<NW>(lsm, nb, p.k, p.sel + (size_t)pair * p.k, cand, topk_sm);
     }
 }
 
@@ -1032,10 +1062,13 @@ FusedScoreParams summary_params(const Dims& s, const void* q, const void* Kbar, 
 }
 
 hipError_t launch_score_summary_fused(const Dims& s, const void* q, const void* Kbar, float* scores, hipStream_t st,
-                                      bool box)
+                                      bool box, const int32_t* offsets, int32_t* sel, int k)
 {
     FusedScoreParams p = summary_params(s, q, Kbar, box);
     p.scores = scores;
+    p.offsets = offsets;
+    p.sel = sel;
+    p.k = k;
     const size_t shm = (size_t)s.G * s.nb * sizeof(float);
     const dim3 grid((unsigned)s.pairs()), block(kFusedWaves * 64);
     if (box) {
@@ -1058,9 +1091,10 @@ bool split_select_ok(const Dims& s, int k)
 }
 
 hipError_t launch_score_summary_split(const Dims& s, const void* q, const void* Kbar, float* logits, float* scores,
-                                      int32_t* sel, int k, hipStream_t st, bool box)
+                                      int32_t* sel, int k, hipStream_t st, bool box, const int32_t* offsets)
 {
     FusedScoreParams p = summary_params(s, q, Kbar, box);
+    p.offsets = offsets;
     p.logits = logits;
     p.scores = scores;
     p.sel = sel;

@@ -101,7 +101,8 @@ typedef enum csa_entry {
     CSA_WS_BLOCK_SCORE_PROXY_ERROR = 7,
     CSA_WS_BLOCK_SCORE_COBS2_FP4 = 8,
     CSA_WS_KV_CLUSTER_BUILD = 9, /* k = n_clusters, m = rank */
-    CSA_WS_CLUSTER_SCORE = 10    /* k = n_clusters, m unused */
+    CSA_WS_CLUSTER_SCORE = 10,      /* k = n_clusters, m unused */
+    CSA_WS_CLUSTER_DECODE_STEP = 11 /* k = clusters read exactly, m = n_clusters */
 } csa_entry;
 
 typedef struct csa_shape {
@@ -372,6 +373,23 @@ int cluster_score(const csa_shape* shape, int32_t n_clusters, const void* q, con
 int cluster_decode_attn(const csa_shape* shape, int32_t n_clusters, const void* q, const void* Kg, const void* Vg,
                         const void* Kc, const void* Vc, const int32_t* offsets, const int32_t* sel, int32_t k,
                         csa_proxy_mode proxy_mode, float* out, float* lse, hipStream_t stream);
+
+/*
+ * cluster_decode_step -- cluster_score, topk_select and cluster_decode_attn of one
+ * decode step in one call (same scores and selection bit for bit, outputs to
+ * rounding).  The cluster logit is the logit of the cluster's proxy, so the
+ * ranking reads each mean key once; where the shape allows (G C <= 16384, and
+ * k <= 32 with C <= 2048 for the selection) one kernel per KV head computes
+ * the logits on the matrix cores, combines the heads and selects, and a second
+ * kernel attends.  The conditions of cluster_decode_attn apply; k >= C reads
+ * every cluster exactly.  scores [B, Hkv, C] and sel [B, Hkv, min(k, C)] are
+ * written when not NULL.  Workspace: csa_workspace_size(shape,
+ * CSA_WS_CLUSTER_DECODE_STEP, k, C) bytes.
+ */
+int cluster_decode_step(const csa_shape* shape, int32_t n_clusters, const void* q, const void* Kg, const void* Vg,
+                        const void* Kc, const void* Vc, const int32_t* offsets, int32_t k, csa_proxy_mode proxy_mode,
+                        float* scores, int32_t* sel, float* out, float* lse, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
 
 /* Workspace bytes needed by an entry point for this shape (k, m as the call
  * will pass them).  Returns 0 for an invalid shape (see csa_last_error()). */

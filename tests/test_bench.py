@@ -73,3 +73,27 @@ def test_timing_detail_counts_what_was_timed():
 def test_cpu_model_names_family_and_affinity():
     s = bench.cpu_model()
     assert "family" in s and "logical CPUs" in s
+
+
+def test_cluster_bytes_counts_the_selection_actually_made():
+    """Two KV heads, four clusters of sizes (3, 0, 5, 2) and (1, 1, 1, 7), top-2 read exactly: the
+    step reads every mean key, the mean values of the unread non-empty clusters and the exact
+    rows of the selected ones; the attention kernel reads both mean rows of the unread ones."""
+    import json
+
+    import numpy as np
+
+    import bench
+    from coreset_softmax_attention_amd import workloads as W
+
+    w = W.WORKLOADS["llama3_8b_layer_b32_qgc"].with_(batch=1, n_q_heads=4, n_kv_heads=2, qgc=4, k=2)
+    sizes = np.array([[[3, 0, 5, 2], [1, 1, 1, 7]]])
+    sel = np.array([[[0, 2], [1, 3]]])
+    by = bench.cluster_bytes(w, sizes, sel)
+    row = 128 * 2
+    assert by["exact_tokens"] == 3 + 5 + 1 + 7
+    assert by["unread_clusters"] == 1 + 2  # cluster 3 of head 0; clusters 0 and 2 of head 1
+    common = 2 * (5 * 4 + 2 * row + 4 * 2) + 16 * 2 * row
+    assert by["step"] == (common + 2 * 4 * row + 3 * row, 2 * 2 * 129 * 4)
+    assert by["attn"] == (common + 3 * 2 * row, 2 * 2 * 129 * 4)
+    json.dumps(by)

@@ -109,13 +109,26 @@ def check_decode(w, data, o, what, k=None, proxies_list=(True, False)):
         return
     Kg = np.take_along_axis(data["K"], o["order"][..., None].astype(np.int64), axis=2)
     Vg = np.take_along_axis(data["V"], o["order"][..., None].astype(np.int64), axis=2)
+    Kgd, Vgd, Vcd = dev(Kg), dev(Vg), dev(o["Vc"])
     for proxies in proxies_list:
-        out, lse = csa.cluster_decode_attn(q, dev(Kg), dev(Vg), Kc, dev(o["Vc"]), offs,
+        out, lse = csa.cluster_decode_attn(q, Kgd, Vgd, Kc, Vcd, offs,
                                            torch.from_numpy(np.ascontiguousarray(ref_sel)).cuda(), proxies=proxies)
         torch.cuda.synchronize()
         ref_out, ref_lse = O.cluster_attend(shp, data["q"], data["K"], data["V"], o["Kc"], o["Vc"], o["order"],
                                             o["offsets"], ref_sel, proxies)
         assert_out(host(out), host(lse), ref_out, ref_lse, w.dtype, f"{what} proxies={proxies}")
+        # the one-call step: the same scores and selection as the entry points in turn, and
+        # the oracle's outputs for its selection
+        so, sl, ss, ssel = csa.cluster_decode_step(q, Kgd, Vgd, Kc, Vcd, offs, k, proxies=proxies, want_scores=True,
+                                                   want_sel=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(host(ss)), bits(host(scores))), f"{what}: step scores differ"
+        assert np.array_equal(host(ssel), host(sel)), f"{what}: step selection differs"
+        step_ref = (ref_out, ref_lse)
+        if not np.array_equal(host(sel), ref_sel):  # near-tied rows chose otherwise: attend to the GPU's choice
+            step_ref = O.cluster_attend(shp, data["q"], data["K"], data["V"], o["Kc"], o["Vc"], o["order"],
+                                        o["offsets"], host(sel), proxies)
+        assert_out(host(so), host(sl), *step_ref, w.dtype, f"{what} step proxies={proxies}")
 
 
 @pytest.mark.parametrize("w", CASES, ids=[c.name for c in CASES])
