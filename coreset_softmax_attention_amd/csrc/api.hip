@@ -154,9 +154,20 @@ int check_device_indices(const char* where, const csa::Dims& d, const int32_t* s
     return CSA_OK;
 }
 
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Block-score workspace (G > 1): per-head logits [B, Hq, nb], then the per-tile
+// log-sum-exp states of the split kernels.
+size_t block_logits_bytes(const csa::Dims& d) { return (size_t)d.B * d.Hq * d.nb * sizeof(float); }
+
 size_t block_score_ws(const csa::Dims& d)
 {
-    return d.G > 1 ? (size_t)d.B * d.Hq * d.nb * sizeof(float) : 0;
+    return d.G > 1 ? align256(block_logits_bytes(d)) + csa::score_err_parts_bytes(d) : 0;
+}
+
+float* score_parts(const csa::Dims& d, void* ws)
+{
+    return d.G > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + align256(block_logits_bytes(d))) : nullptr;
 }
 
 int attn_rows_ok(const csa::Dims& d, long long k, long long m, int proxies, int dense)
@@ -169,13 +180,8 @@ int attn_rows_ok(const csa::Dims& d, long long k, long long m, int proxies, int 
     return CSA_OK;
 }
 
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
 // Proxy-error scores: the log-errors, then the per-tile normaliser states.
-size_t error_score_ws(const csa::Dims& d)
-{
-    return d.G > 1 ? align256(block_score_ws(d)) + csa::score_err_parts_bytes(d) : 0;
-}
+size_t error_score_ws(const csa::Dims& d) { return block_score_ws(d); }
 
 // Workspace layout of the unfused decode step: scores | sel | block_score ws | attention ws.
 struct StepWs {
@@ -463,8 +469,7 @@ int block_score(const csa_shape* shape, csa_score_mode mode_arg, const void* q, 
     if (mode == CSA_SCORE_PROXY_ERROR) {
         if (int rc = check_ws(error_score_ws(d), ws, ws_bytes)) return rc;
         float* lg = d.G == 1 ? scores : static_cast<float*>(ws);
-        float* parts = d.G == 1 ? nullptr
-                                : reinterpret_cast<float*>(static_cast<char*>(ws) + align256(block_score_ws(d)));
+        float* parts = score_parts(d, ws);
         const hipError_t e = csa::launch_score_err(d, q, keys, lg, parts, scores, stream);
         return e == hipSuccess ? CSA_OK : hip_fail(e, "block_score");
     }

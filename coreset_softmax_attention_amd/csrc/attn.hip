@@ -49,6 +49,7 @@ constexpr int kTargetWorkgroups = 2048;
 constexpr int kMfmaWaves = 8;          // waves per workgroup
 constexpr int kMfmaMinWgs = 256;       // workgroups to cover every CU once
 constexpr int kMfmaTilesPerWave = 16;  // tiles a wave streams before the rows are split
+constexpr int kDirectMaxK = 32;        // selection held one block per lane in direct mode
 
 constexpr int unroll_for(int hg) { return hg <= 4 ? 8 : 4; }
 
@@ -68,6 +69,7 @@ struct AttnParams {
     int Hq, Hkv, G, n, L, nb;
     int rows, exact_rows, splits, rows_per_split;
     int pend, wbeg, ebeg;      // end of the proxy rows, first weighted row, first exact row
+    int direct;                // rows resolved from the global arrays, selection in registers (no LDS copies)
     float scale_log2;          // scale * log2(e)
     float log2_L, log2_last;   // log2 c_b of a full and of the last block
 };
@@ -298,20 +300,31 @@ struct RowSources {
     int tok_base;            // index of tok_idx[0] in the KV head's list
 };
 
+// Whether block r is among the k selected blocks held one per lane (lane s <
+// k: selv = sel[s]) by the wave.
+__device__ __forceinline__ bool in_selection(int r, int selv, int k)
+{
+    bool hit = false;
+    for (int s = 0; s < k; ++s) hit |= __builtin_amdgcn_readlane(selv, s) == r;
+    return hit;
+}
+
 // Virtual row r of KV head `pair` -> (row index in its source array, log2-
 // weight); -inf marks a row outside [.., r1), a padding row, a token outside
-// the cache, or (when `mask`) a proxy of a selected block.  Invalid rows keep
-// row 0, a valid address.
+// the cache, or (when `mask`) a proxy of a selected block (from the bitmap, or
+// in direct mode from the selection in the wave's registers).  Invalid rows
+// keep row 0, a valid address.
 __device__ __forceinline__ void resolve_row(const AttnParams& p, const RowSources& src, int r, int r1, int pb_lo,
-                                            const uint32_t* sel_bits, bool mask, uint32_t& row, float& lw)
+                                            const uint32_t* sel_bits, bool mask, int selv, uint32_t& row, float& lw)
 {
     row = 0;
     lw = kNegInf;
     if (r >= r1) return;
     if (r < p.pend) {
         row = (uint32_t)r;
-        if (!mask || !((sel_bits[(r - pb_lo) >> 5] >> ((r - pb_lo) & 31)) & 1u))
-            lw = r == p.nb - 1 ? p.log2_last : p.log2_L;
+        const bool selected = mask && (p.direct ? in_selection(r, selv, p.k)
+                                                : ((sel_bits[(r - pb_lo) >> 5] >> ((r - pb_lo) & 31)) & 1u) != 0);
+        if (!selected) lw = r == p.nb - 1 ? p.log2_last : p.log2_L;
     } else if (r >= p.wbeg && r < p.wbeg + p.m) {
         const int t = r - p.wbeg - src.tok_base;
         const int tok = src.tok_idx[t];
@@ -357,7 +370,8 @@ __global__ void __launch_bounds__(NW * 64) attn_mfma_kernel(const AttnParams p)
     // filled after the first tile's loads are in flight
     const int pb_lo = r0;
     const int pb_hi = min(r1, p.pend);
-    const int bitmap_words = pb_hi > pb_lo ? (pb_hi - pb_lo + 31) >> 5 : 0;
+    const bool direct = p.direct != 0;
+    const int bitmap_words = !direct && pb_hi > pb_lo ? (pb_hi - pb_lo + 31) >> 5 : 0;
     for (int w = threadIdx.x; w < bitmap_words; w += NW * 64) sel_bits[w] = 0;
 
     E eng(sm, p.q + (size_t)(b * p.Hq + h0) * RB, nh);
@@ -367,15 +381,18 @@ __global__ void __launch_bounds__(NW * 64) attn_mfma_kernel(const AttnParams p)
     // (when they fit) after the first tile is issued; until then, and when
     // they do not fit, rows are resolved from the global arrays.
     const int w_lo = max(r0, p.wbeg), w_hi = min(r1, p.wbeg + p.m);  // weighted rows of this range
-    const bool sel_in_lds = !p.dense && p.k > 0 && p.k <= kMaxSelLds;
-    const bool tok_in_lds = w_hi > w_lo && w_hi - w_lo <= kMaxTokLds;
+    const bool sel_in_lds = !direct && !p.dense && p.k > 0 && p.k <= kMaxSelLds;
+    const bool tok_in_lds = !direct && w_hi > w_lo && w_hi - w_lo <= kMaxTokLds;
     RowSources src{p.sel + (size_t)pair * p.k, p.tok_idx + (size_t)pair * p.m, p.tok_logw + (size_t)pair * p.m, 0};
+    // Direct mode (a tile or two per wave, k <= 32): no LDS copies and no barrier
+    // before the tiles; the selection sits one block per lane in every wave.
+    const int selv = direct && !p.dense && lane < p.k ? src.sel[lane] : -1;
 
     auto set_rows = [&](int base, int tb, bool masked) {
         if (lane < TR) {
             uint32_t row;
             float lw;
-            resolve_row(p, src, base + lane, r1, pb_lo, sel_bits, masked, row, lw);
+            resolve_row(p, src, base + lane, r1, pb_lo, sel_bits, masked, selv, row, lw);
             eng.set_row(tb, lane, row, lw);
         }
     };
@@ -436,6 +453,11 @@ __global__ void __launch_bounds__(NW * 64) attn_mfma_kernel(const AttnParams p)
     auto base_of = [&](int jt) { return jt < Tw ? row0(wave + jt * NW) : 0; };
     const int first = Tw > 0 ? row0(wave) : r1;
     issue(first, A, 0, false, Tw > 0);
+    if (direct && p.k > 0 && !p.dense) {  // mask the selected blocks among the first tile's proxy rows
+        const int r = first + lane;
+        if (lane < TR && r < pb_hi && in_selection(r, selv, p.k)) sm.tab_lw[0][wave][lane] = kNegInf;
+        wave_lds_fence();
+    }
     if (bitmap_words > 0 || sel_in_lds || tok_in_lds) {
         __syncthreads();  // bitmap cleared
         if (bitmap_words > 0 || sel_in_lds) {
@@ -648,6 +670,10 @@ AttnPlan plan_attention(const Dims& s, int k, int m, int proxies, int dense)
     pl.rows_per_split = per;
     pl.splits = (pl.rows + per - 1) / per;
     pl.ws_bytes = pl.splits > 1 ? (size_t)s.pairs() * pl.splits * s.G * (s.d + 2) * sizeof(float) : 0;
+    // a tile or two per wave: copying the selection and the weighted tokens to
+    // LDS first would cost a barrier and a memory round trip that the few tiles
+    // cannot amortise
+    pl.direct = s.dtype == DT_BF16 && !dense && k <= kDirectMaxK && pl.rows_per_split <= 2 * kMfmaWaves * kTileRows;
     return pl;
 }
 
@@ -680,6 +706,7 @@ hipError_t launch_attention(const Dims& s, const AttnPlan& pl, const AttnInputs&
     p.pend = pl.pend;
     p.wbeg = pl.wbeg;
     p.ebeg = pl.ebeg;
+    p.direct = pl.direct;
     p.splits = pl.splits;
     p.rows_per_split = pl.rows_per_split;
     p.scale_log2 = s.scale * kLog2e;

@@ -73,10 +73,18 @@ bool split_select_ok(const Dims& s, int k);
 // Group scores (and the top-k when k > 0) from per-head logits [B, Hq, nb], one
 // workgroup per KV head with the logits in LDS; when score_finish_ok().
 bool score_finish_ok(const Dims& s);
-hipError_t launch_score_finish(const Dims& s, const float* logits, float* scores, int32_t* sel, int k, hipStream_t st);
+// parts: per (KV head, tile of 32 rows, head) log-sum-exp states of the logits
+// (score_err_parts_bytes()), from which the per-head normalisers come; else
+// the normalisers are computed from the logits.
+hipError_t launch_score_finish(const Dims& s, const float* logits, float* scores, int32_t* sel, int k, hipStream_t st,
+                               const float* parts = nullptr);
+// parts (G > 1, may be null): the tiles' log-sum-exp states pass through it,
+// so the group-score kernel need not recompute the per-head normalisers.  Not
+// used by the summary and box routes: their normalisers must be the bits the
+// one-kernel step and the one-workgroup score kernel compute from the logits.
 hipError_t launch_score_summary_split(const Dims& s, const void* q, const void* Kbar, float* logits, float* scores,
                                       int32_t* sel, int k, hipStream_t st, bool box = false,
-                                      const int32_t* offsets = nullptr);
+                                      const int32_t* offsets = nullptr, float* parts = nullptr);
 
 // ---- top-k -----------------------------------------------------------------
 hipError_t launch_topk(int rows, int nb, int k, const float* scores, int32_t* sel, hipStream_t st);
@@ -90,6 +98,7 @@ struct AttnPlan {
     int hchunks;         // ceil(G / hg)
     int splits;          // workgroups per (KV head, head chunk)
     int rows_per_split;  // multiple of the wave tile
+    int direct;          // MFMA kernel: rows from the global arrays, no LDS copies (a tile or two per wave)
     size_t ws_bytes;     // partial states when splits > 1
 };
 

@@ -382,6 +382,7 @@ __global__ void __launch_bounds__(256) group_score_kernel(const float* logits, f
 
 constexpr int kFusedWaves = 8;
 constexpr int kFusedMaxLogits = 16384;  // G * nb floats in LDS
+static_assert(kFusedMaxLogits / 2 / 32 <= 4 * 64, "the group-score kernel merges up to 256 tile states per head");
 constexpr int kSplitWaves = 4;          // waves (one tile each) per workgroup of the split logits kernel
 constexpr int kFinishMaxK = 32;
 constexpr int kFinishMaxBlocks = 2048;  // top-k by one wave: up to 32 scores per lane
@@ -409,6 +410,21 @@ __device__ __forceinline__ float count_term(const FusedScoreParams& p, const int
     return r == p.nb - 1 ? p.ln_last : p.ln_L;
 }
 
+// Merge the online log-sum-exp states of the four lane groups holding one head:
+// lanes n16, n16 + 16, n16 + 32, n16 + 48.
+__device__ __forceinline__ void merge_lse_groups(float& m2, float& s2)
+{
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const LanePair pm = r == 0 ? swap16(__float_as_uint(m2)) : swap32(__float_as_uint(m2));
+        const LanePair ps = r == 0 ? swap16(__float_as_uint(s2)) : swap32(__float_as_uint(s2));
+        const float ma = __uint_as_float(pm.a), mb = __uint_as_float(pm.b);
+        const float mn = fmaxf(ma, mb);
+        s2 = __uint_as_float(ps.a) * rescale(ma, mn) + __uint_as_float(ps.b) * rescale(mb, mn);
+        m2 = mn;
+    }
+}
+
 // The mean keys of the tile of blocks [base, base + 32) in the A-operand layout
 // (lane (n16, g16): row n16 of each 16-row half, 16-byte chunks 4 s + g16).
 template <int D>
@@ -430,10 +446,12 @@ __device__ __forceinline__ void load_key_tile(__amdgpu_buffer_rsrc_t kr, int bas
 }
 
 // Logits of a loaded tile for every head of the group: dst[h * stride + b].
+// With `track`, each output lane also folds its logits (in log2 units) into an
+// online log-sum-exp state (m2, s2) of its head.
 template <int D>
 __device__ __forceinline__ void key_tile_logits(const FusedScoreParams& p, const KeyTile<D>& t,
                                                 const bf16x8_t (&bq)[D / 32], int base, float* dst, int stride,
-                                                int lane, const int32_t* off)
+                                                int lane, const int32_t* off, bool track, float& m2, float& s2)
 {
     constexpr int KS = D / 32;
     const int n16 = lane & 15, g16 = lane >> 4;
@@ -450,9 +468,27 @@ __device__ __forceinline__ void key_tile_logits(const FusedScoreParams& p, const
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = base + rb * 16 + 4 * g16 + i;
-                if (row < p.nb) dst[n16 * stride + row] = fmaf(c[rb][i], p.scale, count_term(p, off, row));
+                if (row < p.nb) {
+                    const float v = fmaf(c[rb][i], p.scale, count_term(p, off, row));
+                    dst[n16 * stride + row] = v;
+                    if (track && v > kNegInf) {
+                        const float t2 = v * kLog2e;
+                        const float mn = fmaxf(m2, t2);
+                        s2 = s2 * rescale(m2, mn) + exp2_(t2 - mn);
+                        m2 = mn;
+                    }
+                }
             }
     }
+}
+
+template <int D>
+__device__ __forceinline__ void key_tile_logits(const FusedScoreParams& p, const KeyTile<D>& t,
+                                                const bf16x8_t (&bq)[D / 32], int base, float* dst, int stride,
+                                                int lane, const int32_t* off)
+{
+    float m2 = kNegInf, s2 = 0.0f;
+    key_tile_logits<D>(p, t, bq, base, dst, stride, lane, off, false, m2, s2);
 }
 
 // Group scores of one KV head from its logits lsm[h * nb + b] in LDS, by the
@@ -506,28 +542,50 @@ __device__ __forceinline__ void load_score_q(const char* q_first_head, int nh, i
     }
 }
 
-// The top-k of the nb scores lsm[0 .. nb) of one KV head, by the whole
-// workgroup (NW waves), to out[0 .. k): the waves' maxima bound the search when
-// nb fits one value per thread, else one wave ranks them all.
+// LDS of the selection of one KV head by NW waves.
 template <int NW>
-__device__ __forceinline__ void select_in_lds(const float* lsm, int nb, int k, int32_t* out, uint32_t* cand,
-                                              uint32_t* topk_sm)
+struct SelectSmem {
+    uint32_t cand[NW][128];              // per-wave scratch of the one-wave ranking
+    uint32_t topk[2 * NW + 128];         // wave maxima, overflow flags, candidate slots
+    int32_t cidx[NW * kFinishMaxK];      // two-level: the waves' candidates, ascending block index
+};
+
+// The top-k (k <= 32) of the nb <= 2048 scores lsm[0 .. nb) of one KV head, by
+// the whole workgroup (NW waves), to out[0 .. k) in ascending index order.
+// Up to one score per thread, the waves' maxima bound the search.  Beyond, each
+// wave ranks its contiguous share of the blocks (its k best), then one wave
+// ranks the NW k candidates: they lie in ascending block order, so ranking by
+// position breaks ties towards the lower block like ranking by index, and the
+// k best of the union are the k best overall.
+template <int NW>
+__device__ __forceinline__ void select_in_lds(const float* lsm, int nb, int k, int32_t* out, SelectSmem<NW>& ss)
 {
     const int lane = threadIdx.x & 63;
     auto emit = [&](int r, int idx) { out[r] = idx; };
-    auto one_wave_topk = [&]() {
-        auto load = [&](int i) { return lsm[i]; };
-        if (nb <= 8 * 64)
-            wave_topk<8>(load, nb, k, lane, cand, emit);
-        else
-            wave_topk<kFinishMaxBlocks / 64>(load, nb, k, lane, cand, emit);
-    };
     if (nb <= NW * 64) {
+        auto one_wave_topk = [&]() { wave_topk<8>([&](int i) { return lsm[i]; }, nb, k, lane, ss.cand[0], emit); };
         uint32_t key[1] = {(int)threadIdx.x < nb ? order_key(lsm[threadIdx.x]) : 0u};
-        block_topk<NW, 1>(key, nb, k, topk_sm, one_wave_topk, emit);
-    } else if (threadIdx.x < 64) {
-        one_wave_topk();
+        block_topk<NW, 1>(key, nb, k, ss.topk, one_wave_topk, emit);
+        return;
     }
+    static_assert(kFinishMaxBlocks <= NW * 4 * 64 && NW * kFinishMaxK <= 4 * 64, "four scores per lane");
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int per = (nb + NW - 1) / NW;
+    auto share = [&](int w) { return min(per, max(0, nb - w * per)); };
+    int base = 0, total = 0;  // this wave's first candidate slot; all candidates
+    for (int w = 0; w < NW; ++w) {
+        const int c = min(k, share(w));
+        if (w < wave) base += c;
+        total += c;
+    }
+    const int lo = wave * per, kw = min(k, share(wave));
+    if (kw > 0)
+        wave_topk<4>([&](int i) { return lsm[lo + i]; }, share(wave), kw, lane, ss.cand[wave],
+                     [&](int r, int i) { ss.cidx[base + r] = lo + i; });
+    __syncthreads();
+    if (wave == 0)
+        wave_topk<4>([&](int i) { return lsm[ss.cidx[i]]; }, total, k, lane, ss.cand[0],
+                     [&](int r, int i) { out[r] = ss.cidx[i]; });
 }
 
 template <int D, bool BOX>
@@ -538,8 +596,7 @@ __global__ void __launch_bounds__(kFusedWaves * 64) score_summary_fused_kernel(c
     __shared__ float lse_h[8];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    __shared__ uint32_t cand[128];              // candidates of the one-wave ranking
-    __shared__ uint32_t topk_sm[2 * NW + 128];  // wave maxima, overflow flags, candidate slots
+    __shared__ SelectSmem<NW> ss;
     const int pair = blockIdx.x, b = pair / p.Hkv, j = pair - b * p.Hkv;
     const int32_t* off = p.offsets ? p.offsets + (size_t)pair * (p.nb + 1) : nullptr;
 
@@ -558,7 +615,7 @@ __global__ void __launch_bounds__(kFusedWaves * 64) score_summary_fused_kernel(c
     group_scores_in_lds<NW>(lsm, lse_h, p.G, p.nb, p.scores ? p.scores + (size_t)pair * p.nb : nullptr);
     if (p.k > 0) {
         __syncthreads();
-        select_in_lds<NW>(lsm, p.nb, p.k, p.sel + (size_t)pair * p.k, cand, topk_sm);
+        select_in_lds<NW>(lsm, p.nb, p.k, p.sel + (size_t)pair * p.k, ss);
     }
 }
 
@@ -578,8 +635,18 @@ __global__ void __launch_bounds__(kSplitWaves * 64) score_logits_split_kernel(co
     const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(p.Kbar + (size_t)pair * p.nb * RB, (uint32_t)p.nb * RB);
     KeyTile<D> t;
     load_key_tile<D>(kr, base, lane, t);
+    float m2 = kNegInf, s2 = 0.0f;
     key_tile_logits<D>(p, t, bq, base, p.logits + (size_t)pair * p.G * p.nb, p.nb, lane,
-                       p.offsets ? p.offsets + (size_t)pair * (p.nb + 1) : nullptr);
+                       p.offsets ? p.offsets + (size_t)pair * (p.nb + 1) : nullptr, p.parts != nullptr, m2, s2);
+    if (p.parts) {  // this tile's log-sum-exp state per head, for the group-score kernel's normalisers
+        merge_lse_groups(m2, s2);
+        if (lane < 8) {
+            const int tiles = (p.nb + 31) / 32;
+            float* dst = p.parts + (((size_t)pair * tiles + base / 32) * 8 + lane) * 2;
+            dst[0] = m2;
+            dst[1] = s2;
+        }
+    }
 }
 
 // Second-order logits (COBS, cumulant expansion of ln m_b truncated at second
@@ -918,21 +985,6 @@ __device__ __forceinline__ void square_q_operand(const bf16x8_t (&bq)[D / 32], b
     }
 }
 
-// Merge the online log-sum-exp states of the four lane groups holding one head:
-// lanes n16, n16 + 16, n16 + 32, n16 + 48.
-__device__ __forceinline__ void merge_lse_groups(float& m2, float& s2)
-{
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const LanePair pm = r == 0 ? swap16(__float_as_uint(m2)) : swap32(__float_as_uint(m2));
-        const LanePair ps = r == 0 ? swap16(__float_as_uint(s2)) : swap32(__float_as_uint(s2));
-        const float ma = __uint_as_float(pm.a), mb = __uint_as_float(pm.b);
-        const float mn = fmaxf(ma, mb);
-        s2 = __uint_as_float(ps.a) * rescale(ma, mn) + __uint_as_float(ps.b) * rescale(mb, mn);
-        m2 = mn;
-    }
-}
-
 template <int D>
 __global__ void __launch_bounds__(kFusedWaves * 64) score_err_fused_kernel(const FusedScoreParams p)
 {
@@ -1001,8 +1053,7 @@ __global__ void __launch_bounds__(kFusedWaves * 64) score_finish_kernel(const Fu
     constexpr int NW = kFusedWaves;
     extern __shared__ float lsm[];  // [G][nb] block logits, then the scores in row 0
     __shared__ float lse_h[8];
-    __shared__ uint32_t cand[128];               // candidates of the one-wave ranking
-    __shared__ uint32_t topk_sm[2 * NW + 128];  // wave maxima, overflow flags, candidate slots
+    __shared__ SelectSmem<NW> ss;
     const int lane = threadIdx.x & 63;
     const int pair = blockIdx.x, G = p.G, nb = p.nb;
     // copy the logits in (chunks of loads issued together: one memory round trip each;
@@ -1022,20 +1073,34 @@ __global__ void __launch_bounds__(kFusedWaves * 64) score_finish_kernel(const Fu
             if (i < G * nb) lsm[i] = v[c];
         }
     }
-    if (p.parts && threadIdx.x < (unsigned)G) {  // proxy-error scores: normalisers from the tile states
-        const int tiles = (nb + 31) / 32;
-        const float* st = p.parts + (size_t)pair * tiles * 16 + threadIdx.x * 2;
-        float M = kNegInf;
-        for (int t = 0; t < tiles; ++t) M = fmaxf(M, st[t * 16]);
-        float S = 0.0f;
-        for (int t = 0; t < tiles; ++t) S += st[t * 16 + 1] * rescale(st[t * 16], M);
-        lse_h[threadIdx.x] = (M + log2f(S)) * kLn2;
+    if (p.parts) {  // normalisers from the tiles' log-sum-exp states: wave h merges head h's
+        const int wave = threadIdx.x >> 6, tiles = (nb + 31) / 32;
+        if (wave < G) {
+            const float* st = p.parts + (size_t)pair * tiles * 16 + wave * 2;
+            constexpr int PT = 4;  // states per lane: up to 256 tiles (nb <= 8192)
+            float mv[PT], sv[PT];
+#pragma unroll
+            for (int j = 0; j < PT; ++j) {
+                const int t = lane + 64 * j;
+                mv[j] = t < tiles ? st[t * 16] : kNegInf;
+                sv[j] = t < tiles ? st[t * 16 + 1] : 0.0f;
+            }
+            float M = kNegInf;
+#pragma unroll
+            for (int j = 0; j < PT; ++j) M = fmaxf(M, mv[j]);
+            M = group_max<64>(M);
+            float S = 0.0f;
+#pragma unroll
+            for (int j = 0; j < PT; ++j) S += sv[j] * rescale(mv[j], M);
+            S = group_sum<64>(S);
+            if (lane == 0) lse_h[wave] = (M + log2f(S)) * kLn2;
+        }
     }
     __syncthreads();
     group_scores_in_lds<NW>(lsm, lse_h, G, nb, p.scores ? p.scores + (size_t)pair * nb : nullptr, p.parts != nullptr);
     if (p.k > 0) {
         __syncthreads();
-        select_in_lds<NW>(lsm, nb, p.k, p.sel + (size_t)pair * p.k, cand, topk_sm);
+        select_in_lds<NW>(lsm, nb, p.k, p.sel + (size_t)pair * p.k, ss);
     }
 }
 
@@ -1091,10 +1156,12 @@ bool split_select_ok(const Dims& s, int k)
 }
 
 hipError_t launch_score_summary_split(const Dims& s, const void* q, const void* Kbar, float* logits, float* scores,
-                                      int32_t* sel, int k, hipStream_t st, bool box, const int32_t* offsets)
+                                      int32_t* sel, int k, hipStream_t st, bool box, const int32_t* offsets,
+                                      float* parts)
 {
     FusedScoreParams p = summary_params(s, q, Kbar, box);
     p.offsets = offsets;
+    p.parts = s.G > 1 ? parts : nullptr;
     p.logits = logits;
     p.scores = scores;
     p.sel = sel;
@@ -1115,7 +1182,7 @@ hipError_t launch_score_summary_split(const Dims& s, const void* q, const void* 
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || (s.G == 1 && k == 0)) return e;  // G == 1: the logits are the scores
-    return launch_score_finish(s, logits, scores, sel, k, st);
+    return launch_score_finish(s, logits, scores, sel, k, st, p.parts);
 }
 
 template <bool FP4>
@@ -1204,10 +1271,12 @@ bool score_finish_ok(const Dims& s)
     return s.G <= 8 && s.G * s.nb <= kFusedMaxLogits;
 }
 
-hipError_t launch_score_finish(const Dims& s, const float* logits, float* scores, int32_t* sel, int k, hipStream_t st)
+hipError_t launch_score_finish(const Dims& s, const float* logits, float* scores, int32_t* sel, int k, hipStream_t st,
+                               const float* parts)
 {
     FusedScoreParams p{};
     p.logits = const_cast<float*>(logits);
+    p.parts = const_cast<float*>(parts);
     p.scores = scores;
     p.sel = sel;
     p.k = k;

@@ -123,7 +123,8 @@ def test_workspace_is_checked_before_launch(L):
     assert dneed > 0
     assert L.dense_decode_attn(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == csa.CSA_ERR_WORKSPACE
     bneed = L.csa_workspace_size(ctypes.byref(s), csa.CSA_WS_BLOCK_SCORE_SUMMARY, 0, 0)
-    assert bneed == 1 * 32 * 512 * 4
+    # logits [B, Hq, nb], 256-byte aligned, then (max, sum) per (KV head, tile of 32 blocks, 8 heads)
+    assert bneed == 1 * 32 * 512 * 4 + 8 * 16 * 16 * 4
     assert L.block_score(ctypes.byref(s), 0, FAKE, FAKE, FAKE, None, 0, None) == csa.CSA_ERR_WORKSPACE
     assert L.block_score(ctypes.byref(s), 9, FAKE, FAKE, FAKE, None, 0, None) == csa.CSA_ERR_INVALID_ARG
     assert L.csa_workspace_size(ctypes.byref(s), csa.CSA_WS_BLOCK_SCORE_BOX, 0, 0) == bneed
@@ -362,7 +363,7 @@ def test_cluster_build_argument_checks(L):
 def test_cluster_score_and_attention_argument_checks(L):
     s = shape()
     # G = 4: logits [B, Hq, C] in the workspace
-    assert csa.workspace_size(s, csa.CSA_WS_CLUSTER_SCORE, 100, 0) == 2 * 8 * 100 * 4
+    assert csa.workspace_size(s, csa.CSA_WS_CLUSTER_SCORE, 100, 0) == 2 * 8 * 100 * 4 + 2 * 2 * 4 * 16 * 4
     assert csa.workspace_size(shape(Hq=2), csa.CSA_WS_CLUSTER_SCORE, 100, 0) == 0
     assert L.cluster_score(ctypes.byref(s), 100, FAKE, FAKE, FAKE, FAKE, None, 0, None) == csa.CSA_ERR_WORKSPACE
     assert L.cluster_score(ctypes.byref(s), 0, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == csa.CSA_ERR_INVALID_ARG

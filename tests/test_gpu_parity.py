@@ -253,6 +253,45 @@ def test_sparse_edge_k(k):
         assert_out(g["out"], g["lse"], ref, ref_lse, "bf16", "all blocks + masked proxies vs dense")
 
 
+def topk_by_rule(scores, k):
+    """The k largest scores per row, ties to the lower index, ascending (the selection rule)."""
+    s2 = scores.reshape(-1, scores.shape[-1])
+    out = np.empty((s2.shape[0], k), np.int32)
+    for r, row in enumerate(s2):
+        order = np.lexsort((np.arange(row.size), -row.astype(np.float64)))
+        out[r] = np.sort(order[:k])
+    return out.reshape(scores.shape[:-1] + (k,))
+
+
+@pytest.mark.parametrize("n,k", [(65536, 8), (131072, 32), (40000, 5)])
+def test_selection_ties_across_waves(n, k):
+    """Equal block scores far apart: the cache repeats every 256 blocks, so each score occurs
+    several times, in the shares of different waves of the two-level top-k.  The selection
+    must follow the rule on the GPU's own scores exactly: the k largest, ties to the lower
+    index (few KV heads: the split score kernels and the group-score kernel select)."""
+    B, Hkv, G, d, L = 1, 2, 4, 128, 64
+    rng = np.random.default_rng(n + k)
+    period = 256 * L
+    base = rng.standard_normal((B, Hkv, period, d)).astype(np.float32)
+    K = np.concatenate([base] * (-(-n // period)), axis=2)[:, :, :n]
+    data = {"q": W.to_bf16_bits(2.0 * rng.standard_normal((B, G * Hkv, d)).astype(np.float32)),
+            "K": W.to_bf16_bits(K), "V": W.to_bf16_bits(rng.standard_normal((B, Hkv, n, d)).astype(np.float32))}
+    q, Kd, Vd = dev(data["q"]), dev(data["K"]), dev(data["V"])
+    Kbar, Vbar = csa.kv_summary_build(Kd, Vd, L)
+    _, _, sc, sel = csa.selective_decode_step(q, Kd, Vd, Kbar, Vbar, k, L, want_scores=True, want_sel=True)
+    sc2 = csa.block_score(q, Kbar, "summary", L, n_tokens=n)
+    sel2 = csa.topk_select(sc2, k)
+    torch.cuda.synchronize()
+    sc, sel, sc2, sel2 = host(sc), host(sel), host(sc2), host(sel2)
+    assert np.array_equal(bits(sc), bits(sc2))
+    nb = sc.shape[-1]
+    full = nb // 256 * 256
+    assert (sc[..., :full].reshape(B, Hkv, -1, 256) == sc[..., None, :256]).all(), "repeated blocks score alike"
+    want = topk_by_rule(sc, k)
+    assert np.array_equal(sel, want), f"step selection {sel} != rule {want}"
+    assert np.array_equal(sel2, want), f"topk_select {sel2} != rule {want}"
+
+
 def test_weighted_tokens_only_and_duplicates():
     """A weighted token list alone (k = 0, no proxies), with repeated indices."""
     B, Hkv, G, d, n, L, m = 2, 2, 4, 128, 2048, 64, 700
