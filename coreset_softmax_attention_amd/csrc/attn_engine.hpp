@@ -15,8 +15,12 @@
 //   3. logits for up to 8 query heads come from two 16x16x32 MFMA chains (rows
 //      x heads, heads padded to 16 columns), or from LDS when the caller has
 //      them already; the online-softmax update runs once per (row, head) on the
-//      MFMA output lanes and the probabilities go through LDS to the value lanes;
-//   4. the value lanes accumulate P V in fp32.
+//      MFMA output lanes, which keep the probabilities;
+//   4. P V on the matrix cores: the probabilities, split into two bfloat16
+//      terms (hi + lo equals the fp32 value to about 2^-17), are the A operand
+//      as they lie in the lanes; the value rows go through the wave's LDS slot
+//      and come back transposed (ds_read_b64_tr_b16) as the B operand; the
+//      output of all heads x d columns accumulates in D / 16 fp32 MFMA tiles.
 // All lane groups of a wave share one running maximum per head, so their
 // partial sums add directly; waves are merged through LDS at the end.
 #pragma once
@@ -36,7 +40,6 @@ struct MfmaEngine {
     static constexpr int RPV = 64 / LPV;        // value rows per wave-wide load
     static constexpr int NVI = TR / RPV;        // value loads per lane per tile
     static constexpr int NI = TR / RPV;         // key loads per lane per tile (rows RPV j + gv)
-    static constexpr int HP = HG <= 4 ? 4 : 8;  // padded heads per probability row
     static_assert(KS * 32 == D && HG <= 8 && (LPV == 8 || LPV == 16), "unsupported geometry");
     static_assert(NI == 2 * KS && RPV * NI / 2 == 16, "a half tile of key loads covers one 16-row MFMA block");
     // Key rows go through LDS (coalesced non-temporal loads, then the layout
@@ -47,15 +50,23 @@ struct MfmaEngine {
 
     static constexpr int NTAB = 4;  // row tables per wave (tiles in flight or pending)
 
+    // Per-wave LDS slot: 16 key rows padded to LPV + 1 chunks (layout change of
+    // the keys), or the tile's 32 value rows padded by 32 bytes (the transposed
+    // reads of a 16-lane group then cover four rows on disjoint banks).
+    static constexpr int VRS = RB + 32;  // value row stride in the slot (bytes)
+    static constexpr int SLOT = (TR * VRS > 16 * (LPV + 1) * 16 ? TR * VRS : 16 * (LPV + 1) * 16);
+    static_assert(SLOT % 16 == 0 && VRS % 16 == 0, "16-byte aligned slot rows");
+
     struct Smem {
         uint32_t tab_row[NTAB][NW][TR];
         float tab_lw[NTAB][NW][TR] __attribute__((aligned(16)));
-        float p[NW][TR][HP] __attribute__((aligned(16)));
-        float alpha[NW][HP] __attribute__((aligned(16)));
+        float alpha[NW][16] __attribute__((aligned(16)));
         float m[NW][HG];
         float l[NW][HG];
-        float acc[NW][HG][D];
-        uint4 kt[kLdsKeys ? NW : 1][16 * (LPV + 1)];  // per-wave staging of 16 key rows (layout change)
+        union {
+            uint4 slot[NW][SLOT / 16];  // while tiles stream
+            float acc[NW][HG][D];       // the waves' outputs, at the end
+        } u;
     };
 
     // One tile's rows in registers, as loaded: kr[j] and vr[j] hold 16-byte
@@ -69,8 +80,9 @@ struct MfmaEngine {
     Smem& sm;
     const int lane, wave, n16, g16, gv, cv;
     bf16x8_t bq[KS];
-    float m_run, l_part;  // MFMA lanes: head n16
-    float acc[HG][8];     // value lanes: chunk cv of the rows RPV j + gv
+    float m_run, l_part;     // MFMA lanes: head n16
+    bf16x8_t pa_hi, pa_lo;   // the tile's probabilities, head n16, rows of k-slots 8 g16 .. 8 g16 + 7
+    f32x4_t oacc[D / 16];    // output: heads 4 g16 + i, column 16 c + n16
 
     __device__ __forceinline__ MfmaEngine(Smem& s, const char* q_first_head, int nh)
         : sm(s),
@@ -85,9 +97,7 @@ struct MfmaEngine {
     {
         load_q_operand<D>(q_first_head, nh, lane, bq);
 #pragma unroll
-        for (int g = 0; g < HG; ++g)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[g][e] = 0.0f;
+        for (int c = 0; c < D / 16; ++c) oacc[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
 
     // Row table entry (lanes 0..31 of the wave) of table `tb` (0 or 1).
@@ -155,7 +165,7 @@ struct MfmaEngine {
             for (int s = 0; s < KS; ++s) a[s] = kr[KS * rb + s];
             return;
         }
-        uint4* slot = sm.kt[wave];
+        uint4* slot = sm.u.slot[wave];
 #pragma unroll
         for (int j = 0; j < NI / 2; ++j) slot[(RPV * j + gv) * (LPV + 1) + cv] = kr[rb * (NI / 2) + j];
         wave_lds_fence();
@@ -216,7 +226,11 @@ struct MfmaEngine {
         for (int i = 0; i < 8; ++i) x[i] = lws[i] == kNegInf ? kNegInf : vs[i] * kLog2e;
     }
 
-    // Online-softmax update with the tile's logits; probabilities to LDS.
+    // Online-softmax update with the tile's logits.  The probabilities stay in
+    // the lanes as the A operand of P V: lane (n16, g16) holds head n16 at rows
+    // 4 g16 + i and 16 + 4 g16 + i, which become its k-slots 0..3 and 4..7 (the
+    // value rows are read in the same order).  The rescale factor of each head
+    // goes to LDS for the output lanes.
     __device__ __forceinline__ void softmax(float (&x)[8])
     {
         float mx = x[0];
@@ -227,19 +241,27 @@ struct MfmaEngine {
         const float alpha = rescale(m_run, m_new);
         m_run = m_new;
         l_part *= alpha;
+        uint32_t hw[4], lw[4];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             x[i] = x[i] == kNegInf ? 0.0f : exp2_(x[i] - m_new);
             l_part += x[i];
-        }
-        if (n16 < HG) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                sm.p[wave][4 * g16 + i][n16] = x[i];
-                sm.p[wave][16 + 4 * g16 + i][n16] = x[4 + i];
+            // x = hi + lo: hi its leading 8 significant bits, lo the rest rounded to bfloat16
+            const uint32_t hb = __float_as_uint(x[i]) >> 16;
+            const float r = x[i] - __uint_as_float(hb << 16);
+            const uint32_t ru = __float_as_uint(r);
+            const uint32_t lb = (ru + 0x7fffu + ((ru >> 16) & 1u)) >> 16;
+            if (i & 1) {
+                hw[i >> 1] |= hb << 16;
+                lw[i >> 1] |= lb << 16;
+            } else {
+                hw[i >> 1] = hb;
+                lw[i >> 1] = lb;
             }
-            if (g16 == 0) sm.alpha[wave][n16] = alpha;
         }
+        pa_hi = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+        pa_lo = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+        if (g16 == 0) sm.alpha[wave][n16] = alpha;
         wave_lds_fence();
     }
 
@@ -248,27 +270,40 @@ struct MfmaEngine {
 
     __device__ __forceinline__ void accumulate_values(const uint4 (&vr)[NVI])
     {
-        float al[HP];
-        *reinterpret_cast<float4*>(&al[0]) = *reinterpret_cast<const float4*>(&sm.alpha[wave][0]);
-        if constexpr (HP == 8) *reinterpret_cast<float4*>(&al[4]) = *reinterpret_cast<const float4*>(&sm.alpha[wave][4]);
+        // rescale: lane (n16, g16) holds heads 4 g16 + i
+        const float4 al = *reinterpret_cast<const float4*>(&sm.alpha[wave][4 * g16]);
 #pragma unroll
-        for (int g = 0; g < HG; ++g)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[g][e] *= al[g];
-#pragma unroll
-        for (int u = 0; u < NVI; ++u) {
-            float pr[HP];
-            *reinterpret_cast<float4*>(&pr[0]) = *reinterpret_cast<const float4*>(&sm.p[wave][RPV * u + gv][0]);
-            if constexpr (HP == 8)
-                *reinterpret_cast<float4*>(&pr[4]) = *reinterpret_cast<const float4*>(&sm.p[wave][RPV * u + gv][4]);
-            float vf[8];
-            unpack<DT_BF16>(vr[u], vf);
-#pragma unroll
-            for (int g = 0; g < HG; ++g)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(pr[g], vf[e], acc[g][e]);
+        for (int c = 0; c < D / 16; ++c) {
+            oacc[c][0] *= al.x;
+            oacc[c][1] *= al.y;
+            oacc[c][2] *= al.z;
+            oacc[c][3] *= al.w;
         }
-        wave_lds_fence();  // p / alpha are rewritten by the next tile
+        // the value rows into the slot, as loaded (row RPV u + gv, chunk cv)
+        char* slot = reinterpret_cast<char*>(sm.u.slot[wave]);
+#pragma unroll
+        for (int u = 0; u < NVI; ++u) *reinterpret_cast<uint4*>(slot + (RPV * u + gv) * VRS + cv * 16) = vr[u];
+        wave_lds_fence();
+        // B operand of column block c: lane (t, g16), t = lane % 16, k-slots 0..3 are
+        // rows 4 g16 + 0..3 and 4..7 rows 16 + 4 g16 + 0..3, column 16 c + t.  A
+        // transposed read over a 16-lane group gives lane 4 a + b element b of the
+        // chunks addressed by lanes 4 j + a (j = 0..3): lane 4 j + a addresses row
+        // j of the four, columns 16 c + 4 a .. + 3.
+        const int t = lane & 15;
+        const char* b0 = slot + (4 * g16 + (t >> 2)) * VRS + (t & 3) * 8;
+        const char* b1 = b0 + 16 * VRS;
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+            typedef short v4i16_t __attribute__((ext_vector_type(4)));
+            typedef __attribute__((address_space(3))) v4i16_t* lds_v4i16_ptr;
+            const v4i16_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(b0 + c * 32));
+            const v4i16_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(b1 + c * 32));
+            const uint2 l2 = __builtin_bit_cast(uint2, lo4), h2 = __builtin_bit_cast(uint2, hi4);
+            const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
+            oacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, bv, oacc[c], 0, 0, 0);
+            oacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, bv, oacc[c], 0, 0, 0);
+        }
+        wave_lds_fence();  // the slot and alpha are rewritten by the next tile
     }
 
     // Merge the waves (the whole workgroup must call this).  Writes, for each
@@ -278,21 +313,15 @@ struct MfmaEngine {
     __device__ __forceinline__ void finish(int nh, float* out, float* lse, float* part)
     {
         l_part = add_xor32(add_xor16(l_part));
-        // sum the lane groups holding the same value columns (lanes l ^ LPV, ...)
+        __syncthreads();  // every wave is done with its slot: the outputs take its place
+        // output lanes: heads 4 g16 + i, column 16 c + n16
 #pragma unroll
-        for (int g = 0; g < HG; ++g)
+        for (int i = 0; i < 4; ++i) {
+            const int g = 4 * g16 + i;
+            if (g < HG) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float a = acc[g][e];
-                if constexpr (LPV == 8) a += dpp<DPP_ROW_ROR8>(a);
-                a = add_xor32(add_xor16(a));
-                acc[g][e] = a;
+                for (int c = 0; c < D / 16; ++c) sm.u.acc[wave][g][16 * c + n16] = oacc[c][i];
             }
-        if (gv == 0) {
-#pragma unroll
-            for (int g = 0; g < HG; ++g)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) sm.acc[wave][g][cv * 8 + e] = acc[g][e];
         }
         if (lane < HG) {
             sm.m[wave][lane] = m_run;
@@ -310,7 +339,7 @@ struct MfmaEngine {
             for (int w = 0; w < NW; ++w) {
                 const float a = rescale(sm.m[w][g], M);
                 Ls += sm.l[w][g] * a;
-                A += sm.acc[w][g][e] * a;
+                A += sm.u.acc[w][g][e] * a;
             }
             if (part == nullptr) {
                 out[(size_t)g * D + e] = A / Ls;

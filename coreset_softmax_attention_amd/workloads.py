@@ -85,6 +85,9 @@ WORKLOADS = {
                  description="Llama-3.1-8B-shaped layer, one sequence, 1% read + proxies"),
         Workload("llama3_8b_layer_b32", 1002, 32, 32, 8, 128, 32768, 64, "bf16", 5, "summary", True, "clusters",
                  description="Llama-3.1-8B-shaped layer, batch 32, 32K context, 1% read + proxies"),
+        Workload("g8_layer_b32", 1006, 32, 64, 8, 128, 32768, 64, "bf16", 5, "summary", True, "clusters",
+                 description="the headline cache read by 64 query heads (G = 8, a 70B-class layer), batch 32, "
+                             "32K context, 1% read + proxies"),
         Workload("exact_mass_mha_b8", 1003, 8, 32, 32, 128, 32768, 64, "bf16", 16, "exact_mass", False, "clusters",
                  description="exact block masses (MHA), values read for the top-16 blocks only"),
         Workload("exact_mass_gqa_b8", 1013, 8, 32, 8, 128, 32768, 64, "bf16", 16, "exact_mass", False, "clusters",

@@ -436,7 +436,7 @@ def test_invalid_arguments_raise():
 # ---------------------------------------------------------------------------
 
 FULL = ["llama3_8b_layer_b1", "llama3_8b_layer_b32", "exact_mass_mha_b8", "exact_mass_gqa_b8",
-        "weighted_coreset_128k", "llama3_8b_layer_b32_box", "llama3_8b_layer_b32_err"]
+        "weighted_coreset_128k", "llama3_8b_layer_b32_box", "llama3_8b_layer_b32_err", "g8_layer_b32"]
 
 
 @pytest.mark.parametrize("name", FULL)
