@@ -43,10 +43,12 @@ struct MfmaEngine {
     static_assert(KS * 32 == D && HG <= 8 && (LPV == 8 || LPV == 16), "unsupported geometry");
     static_assert(NI == 2 * KS && RPV * NI / 2 == 16, "a half tile of key loads covers one 16-row MFMA block");
     // Key rows go through LDS (coalesced non-temporal loads, then the layout
-    // change) up to six heads; with seven or eight the value accumulators leave
-    // no room for it, and the keys are loaded in the operand layout directly
-    // (kr[KS rb + s] = operand s of block rb).
-    static constexpr bool kLdsKeys = HG <= 6;
+    // change).  The other form, keys loaded in the operand layout directly
+    // (kr[KS rb + s] = operand s of block rb), stays for comparison: with P V on
+    // the matrix cores every head count has the registers for the LDS route,
+    // which took the 64-head step from 23.6 to 23.0 us (the 7-head weighted-
+    // coreset step, latency-bound, from 30.4 to 30.8 us).
+    static constexpr bool kLdsKeys = true;
 
     static constexpr int NTAB = 4;  // row tables per wave (tiles in flight or pending)
 
