@@ -380,6 +380,89 @@ def cobs2_fp4_logits(shape: Shape, q, packed):
     return out
 
 
+def sub_padded(s_dim: int) -> int:
+    """Stored length of a query-subspace eigenvector: s rounded up to whole 16-byte chunks of
+    bfloat16 (8 elements), the padding zero."""
+    return -(-s_dim // 8) * 8
+
+
+def cov_sub_factors(shape: Shape, K, U, rank: int = COBS_RANK):
+    """Query-subspace covariance factors of "COBS: Cumulant Order Block Sparse Attention"
+    (section on keeping the covariance only within the query subspace): U [Hkv, d, s] holds
+    the top s eigenvectors of the queries' second moment for each KV head (the caller's
+    basis); per block B_b = U^T Sigma_b U (s x s), Sigma_b the within-block key covariance
+    (1/c) sum_i (k_i - kbar)(k_i - kbar)^T, and its top `rank` scaled eigenvectors
+    xi_i = sqrt(mu_i) v_i, largest first, each signed so that its largest-magnitude
+    coordinate is positive.  fp64, unrounded: [B, Hkv, nb, rank, s]."""
+    B, Hkv, n, d, L, nb = shape.batch, shape.n_kv_heads, shape.n_tokens, shape.head_dim, shape.block_size, \
+        shape.n_blocks
+    Kf = widen(shape, _stored(shape, K, (B, Hkv, n, d)))
+    U = np.asarray(U, np.float64)
+    s_dim = U.shape[-1]
+    assert U.shape == (Hkv, d, s_dim)
+    xi = np.zeros((B, Hkv, nb, rank, s_dim), np.float64)
+    for b in range(B):
+        for j in range(Hkv):
+            for blk in range(nb):
+                X = Kf[b, j, blk * L:min(n, (blk + 1) * L)]
+                Y = (X - X.mean(axis=0)) @ U[j]  # centred keys in the query subspace
+                mu, V = np.linalg.eigh(Y.T @ Y / X.shape[0])  # ascending
+                for i in range(min(rank, s_dim)):
+                    v = V[:, s_dim - 1 - i]
+                    v = v if v[np.argmax(np.abs(v))] > 0 else -v
+                    xi[b, j, blk, i] = math.sqrt(max(mu[s_dim - 1 - i], 0.0)) * v
+    return xi
+
+
+def cov_sub_build(shape: Shape, K, U, Kbar=None, rank: int = COBS_RANK):
+    """Stored query-subspace descriptor [B, Hkv, nb, d + rank * sub_padded(s)] in the storage
+    dtype: the mean key (the bits of kv_summary_build), then the `rank` factors of
+    cov_sub_factors, each rounded once and zero-padded to sub_padded(s) elements."""
+    B, Hkv, nb, d = shape.batch, shape.n_kv_heads, shape.n_blocks, shape.head_dim
+    if Kbar is None:
+        Kbar, _ = kv_summary_build(shape, K, K)
+    xi = cov_sub_factors(shape, K, U, rank)
+    s_dim = xi.shape[-1]
+    sp = sub_padded(s_dim)
+    out = np.zeros((B, Hkv, nb, d + rank * sp), shape.np_dtype)
+    out[..., :d] = np.asarray(Kbar).reshape(B, Hkv, nb, d)
+    padded = np.zeros((B, Hkv, nb, rank, sp), np.float64)
+    padded[..., :s_dim] = xi
+    out[..., d:] = store_array(shape, padded).reshape(B, Hkv, nb, rank * sp)
+    return out
+
+
+def cov_sub_unpack(shape: Shape, Kcs, s_dim: int, rank: int = COBS_RANK):
+    """Mean keys [B, Hkv, nb, d] and factors [B, Hkv, nb, rank, s] (fp64) of a stored
+    query-subspace descriptor."""
+    B, Hkv, nb, d = shape.batch, shape.n_kv_heads, shape.n_blocks, shape.head_dim
+    sp = sub_padded(s_dim)
+    C = widen(shape, np.asarray(Kcs).reshape(B, Hkv, nb, d + rank * sp))
+    return C[..., :d], C[..., d:].reshape(B, Hkv, nb, rank, sp)[..., :s_dim]
+
+
+def cobs2_sub_logits(shape: Shape, q, Kcs, U):
+    """Second-order block logits [B, Hq, nb] from query-subspace descriptors: the cumulant
+    estimate truncated at second order with the covariance kept in the subspace,
+    scale q.kbar_b + ln c_b + (1/2) scale^2 sum_i (qt . xi_i)^2 with qt = U^T q the query's
+    coordinates in the subspace of its KV head."""
+    B, Hq, Hkv, d, nb = shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.n_blocks
+    G = Hq // Hkv
+    U = np.asarray(U, np.float64)
+    s_dim = U.shape[-1]
+    qf = widen(shape, _stored(shape, q, (B, Hq, d)))
+    mean, xi = cov_sub_unpack(shape, Kcs, s_dim)
+    scale = shape.scale if shape.scale else 1.0 / math.sqrt(d)
+    counts = np.array([min(shape.block_size, shape.n_tokens - i * shape.block_size) for i in range(nb)], np.float64)
+    out = np.empty((B, Hq, nb), np.float64)
+    for h in range(Hq):
+        qt = qf[:, h] @ U[h // G]  # [B, s]
+        m1 = np.einsum("bd,bkd->bk", qf[:, h], mean[:, h // G])
+        m2 = np.einsum("bs,bkrs->bkr", qt, xi[:, h // G])
+        out[:, h] = scale * m1 + np.log(counts) + 0.5 * scale * scale * (m2 ** 2).sum(-1)
+    return out
+
+
 def block_logits(shape: Shape, mode: int, q, keys):
     """Per-query-head block logits [B, Hq, nb]: first-order summary score, exact ln m_b, or the
     largest logit over the block's key box."""

@@ -127,6 +127,14 @@ PY_MUTANTS = {
     "FP4 nibbles swapped": ("codes[2 * t] | (codes[2 * t + 1] << 4)", "codes[2 * t + 1] | (codes[2 * t] << 4)"),
     "FP4 sign dropped": ("return best | (8 if (float(r) < 0 and best) else 0)", "return best"),
     "FP4 decoded without the scale": ("return mean, scales[..., None] * val", "return mean, val"),
+    "subspace covariance not centred": ("Y = (X - X.mean(axis=0)) @ U[j]", "Y = X @ U[j]"),
+    "subspace covariance with the sample divisor": ("Y.T @ Y / X.shape[0]", "Y.T @ Y / (X.shape[0] - 1)"),
+    "subspace factors not scaled by the root eigenvalue": ("math.sqrt(max(mu[s_dim - 1 - i], 0.0)) * v",
+                                                           "max(mu[s_dim - 1 - i], 0.0) * v"),
+    "smallest subspace directions kept": ("v = V[:, s_dim - 1 - i]", "v = V[:, i]"),
+    "query projected with another KV head's basis": ("qt = qf[:, h] @ U[h // G]", "qt = qf[:, h] @ U[(h + 1) % Hkv]"),
+    "subspace term without the one half": ("(m2 ** 2).sum(-1)\n    return out\n\n\ndef block_logits",
+                                           "(m2 ** 2).sum(-1) * 2.0\n    return out\n\n\ndef block_logits"),
 }
 PY_BATTERY = [
     P.test_cov_descriptor_is_the_top_eigen_truncation,
@@ -141,6 +149,12 @@ PY_BATTERY = [
     P.test_fp4_pack_layout_by_hand,
     P.test_fp4_decode_error_is_within_half_a_grid_step,
     P.test_fp4_score_equals_bf16_score_on_grid_exact_descriptors,
+    P.test_subspace_storage_is_the_pages_figure,
+    P.test_subspace_factors_are_the_top_eigen_truncation_of_the_projected_covariance,
+    P.test_subspace_of_full_dimension_scores_like_the_full_space_descriptor,
+    P.test_subspace_score_is_exact_when_query_and_spread_live_in_the_subspace,
+    P.test_subspace_term_at_full_rank_is_the_projected_quadratic_form,
+    P.test_subspace_basis_of_coordinate_axes_keeps_the_leading_block,
 ]
 
 

@@ -1024,3 +1024,120 @@ def test_equal_distances_go_to_the_lower_cluster():
     assert np.all(res["Kc"][:, :, 1] == 0) and np.all(res["Vc"][:, :, 1] == 0)
     lg = O.cluster_logits(shp, data["q"], res["Kc"], res["offsets"])
     assert np.all(lg[:, :, 1] == -np.inf)
+
+
+# ---------------------------------------------------------------------------
+# query-subspace second-order descriptors ("COBS: Cumulant Order Block Sparse
+# Attention", section on keeping the covariance only within the query subspace)
+# ---------------------------------------------------------------------------
+
+def orthonormal(rng, d, s_dim):
+    """d x s matrix with orthonormal columns (QR of a Gaussian matrix), fp64."""
+    Q, _ = np.linalg.qr(rng.standard_normal((d, s_dim)))
+    return Q
+
+
+def test_subspace_storage_is_the_pages_figure():
+    """At rank 4 and s = 85 the factors are r s = 340 floats per block against r d = 512 for the
+    full-space descriptor at d = 128 (the page's figures); stored, each factor is padded to 88
+    elements (whole 16-byte chunks of bfloat16) after the d-element mean key."""
+    assert O.COBS_RANK * 85 == 340 and O.COBS_RANK * 128 == 512
+    assert O.sub_padded(85) == 88 and O.sub_padded(8) == 8 and O.sub_padded(1) == 8
+    n, L, d, s_dim = 128, 64, 128, 85
+    shp = O.Shape(1, 1, 1, d, n, L, "bf16")
+    rng = np.random.default_rng(60)
+    _, K, _ = rand_case(60, 1, 1, 1, d, n, "bf16")
+    U = orthonormal(rng, d, s_dim)[None].astype(np.float32)
+    C = O.cov_sub_build(shp, K, U)
+    assert C.shape == (1, 1, 2, d + 4 * 88) and C.dtype == np.uint16
+    assert np.all(C[..., d:].reshape(1, 1, 2, 4, 88)[..., 85:] == 0)  # the padding is zero
+    Kbar, _ = O.kv_summary_build(shp, K, K)
+    assert np.array_equal(C[..., :d], Kbar)
+
+
+def test_subspace_factors_are_the_top_eigen_truncation_of_the_projected_covariance():
+    """sum_i xi_i xi_i^T equals the best rank-r approximation of U^T Sigma_b U, with Sigma_b
+    from an explicit loop over the tokens and the truncation by an SVD; the factors come
+    ordered by decreasing norm with their largest-magnitude coordinate positive."""
+    n, L, d, s_dim = 96, 32, 24, 10
+    shp = O.Shape(1, 1, 2, d, n, L, "f32")
+    rng = np.random.default_rng(61)
+    _, K, _ = rand_case(61, 1, 2, 2, d, n, "f32")
+    U = np.stack([orthonormal(rng, d, s_dim) for _ in range(2)]).astype(np.float32)
+    xi = O.cov_sub_factors(shp, K, U)
+    for j in range(2):
+        Uj = U[j].astype(np.float64)
+        for blk in range(shp.n_blocks):
+            Bm = Uj.T @ explicit_covariance(K[0, j, blk * L:(blk + 1) * L]) @ Uj
+            W, sv, _ = np.linalg.svd(Bm)
+            best = (W[:, :O.COBS_RANK] * sv[:O.COBS_RANK]) @ W[:, :O.COBS_RANK].T
+            x = xi[0, j, blk]
+            assert np.linalg.norm(x.T @ x - best) <= 1e-9 * np.linalg.norm(best)
+            norms = np.linalg.norm(x, axis=1)
+            assert np.all(np.diff(norms) <= 1e-9 * norms[0])
+            assert all(v[np.argmax(np.abs(v))] > 0 for v in x)
+
+
+def test_subspace_of_full_dimension_scores_like_the_full_space_descriptor():
+    """With s = d and any orthonormal basis the projected covariance is similar to Sigma_b, so
+    the subspace and full-space second-order logits agree (binary32 storage)."""
+    n, L, d = 128, 32, 32
+    shp = O.Shape(1, 4, 2, d, n, L, "f32")
+    rng = np.random.default_rng(62)
+    q, K, _ = rand_case(62, 1, 4, 2, d, n, "f32", qscale=2.0)
+    U = np.stack([orthonormal(rng, d, d) for _ in range(2)]).astype(np.float32)
+    U = np.stack([np.linalg.qr(u.astype(np.float64))[0] for u in U])  # orthonormal in fp64 too
+    sub = O.cobs2_sub_logits(shp, q, O.cov_sub_build(shp, K, U), U)
+    full = O.block_logits(shp, O.COBS2, q, O.cov_build(shp, K))
+    assert np.abs(sub - full).max() <= 1e-5 * (1 + np.abs(full).max())
+
+
+def test_subspace_score_is_exact_when_query_and_spread_live_in_the_subspace():
+    """Keys whose deviations from a common point lie in span(U) and queries in span(U) (Pi q = q):
+    the covariance lives in the subspace, so at s < d the subspace logits equal the full-space
+    ones."""
+    n, L, d, s_dim = 128, 32, 48, 6
+    shp = O.Shape(1, 2, 1, d, n, L, "f32")
+    rng = np.random.default_rng(63)
+    Uj = orthonormal(rng, d, s_dim)
+    K = (rng.standard_normal(d)[None] + rng.standard_normal((n, s_dim)) @ Uj.T).astype(np.float32)[None, None]
+    q = (2.0 * rng.standard_normal((2, s_dim)) @ Uj.T).astype(np.float32)[None]
+    U = Uj[None]
+    sub = O.cobs2_sub_logits(shp, q, O.cov_sub_build(shp, K, U), U)
+    full = O.block_logits(shp, O.COBS2, q, O.cov_build(shp, K))
+    assert np.abs(sub - full).max() <= 1e-5 * (1 + np.abs(full).max())
+
+
+def test_subspace_term_at_full_rank_is_the_projected_quadratic_form():
+    """s = r = 4: the factors hold all of B_b, so the second-order term is (1/2) scale^2
+    qt^T (U^T Sigma_b U) qt with qt = U^T q, Sigma_b from an explicit loop."""
+    n, L, d, s_dim = 64, 16, 20, 4
+    shp = O.Shape(1, 3, 1, d, n, L, "f32")
+    rng = np.random.default_rng(64)
+    q, K, _ = rand_case(64, 1, 3, 1, d, n, "f32", qscale=2.0)
+    U = orthonormal(rng, d, s_dim)[None].astype(np.float32)
+    C = O.cov_sub_build(shp, K, U)
+    second = O.cobs2_sub_logits(shp, q, C, U) - O.block_logits(shp, O.SUMMARY, q, C[..., :d])
+    Uj = U[0].astype(np.float64)
+    for h in range(3):
+        qt = q[0, h].astype(np.float64) @ Uj
+        for blk in range(shp.n_blocks):
+            Bm = Uj.T @ explicit_covariance(K[0, 0, blk * L:(blk + 1) * L]) @ Uj
+            want = 0.5 * (qt @ Bm @ qt) / d
+            assert abs(second[0, h, blk] - want) <= 1e-5 * (1 + abs(want))
+
+
+def test_subspace_basis_of_coordinate_axes_keeps_the_leading_block():
+    """U = the first s coordinate axes: B_b is the leading s x s block of Sigma_b, so the
+    factors reconstruct its best rank-r approximation (explicit loop, SVD)."""
+    n, L, d, s_dim = 64, 32, 16, 7
+    shp = O.Shape(1, 1, 1, d, n, L, "f32")
+    _, K, _ = rand_case(65, 1, 1, 1, d, n, "f32")
+    U = np.eye(d)[:, :s_dim][None].astype(np.float32)
+    xi = O.cov_sub_factors(shp, K, U)
+    for blk in range(shp.n_blocks):
+        Bm = explicit_covariance(K[0, 0, blk * L:(blk + 1) * L])[:s_dim, :s_dim]
+        W, sv, _ = np.linalg.svd(Bm)
+        best = (W[:, :O.COBS_RANK] * sv[:O.COBS_RANK]) @ W[:, :O.COBS_RANK].T
+        x = xi[0, 0, blk]
+        assert np.linalg.norm(x.T @ x - best) <= 1e-9 * np.linalg.norm(best)
