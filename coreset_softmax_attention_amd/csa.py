@@ -26,6 +26,7 @@ CSA_WS_SPARSE_DECODE_ATTN, CSA_WS_DENSE_DECODE_ATTN, CSA_WS_SELECTIVE_DECODE_STE
 CSA_WS_BLOCK_SCORE_BOX, CSA_WS_BLOCK_SCORE_COBS2, CSA_WS_BLOCK_SCORE_PROXY_ERROR = 5, 6, 7
 CSA_WS_BLOCK_SCORE_COBS2_FP4 = 8
 CSA_WS_KV_CLUSTER_BUILD, CSA_WS_CLUSTER_SCORE, CSA_WS_CLUSTER_DECODE_STEP = 9, 10, 11
+CSA_WS_BLOCK_SCORE_COBS2_SUB = 12
 
 MODES = {"summary": CSA_SCORE_SUMMARY, "exact_mass": CSA_SCORE_EXACT_MASS, "box": CSA_SCORE_BOX,
          "cobs2": CSA_SCORE_COBS2, "proxy_error": CSA_SCORE_PROXY_ERROR, "cobs2_fp4": CSA_SCORE_COBS2_FP4}
@@ -87,6 +88,8 @@ _SIGS = {
     "cluster_score": [ctypes.POINTER(Shape), _I32, _P, _P, _P, _P, _P, _SZ, _P],
     "cluster_decode_attn": [ctypes.POINTER(Shape), _I32, _P, _P, _P, _P, _P, _P, _P, _I32, ctypes.c_int, _P, _P,
                             _P],
+    "kv_cov_sub_build": [ctypes.POINTER(Shape), _I32, _P, _P, _P, _P],
+    "block_score_cobs2_sub": [ctypes.POINTER(Shape), _I32, _P, _P, _P, _P, _P, _SZ, _P],
     "cluster_decode_step": [ctypes.POINTER(Shape), _I32, _P, _P, _P, _P, _P, _P, _I32, ctypes.c_int, _P, _P, _P, _P,
                             _P, _SZ, _P],
 }
@@ -221,6 +224,40 @@ def kv_cov4_build(K: torch.Tensor, block_size: int, Kcov4=None):
         Kcov4 = torch.empty((B, Hkv, shape.n_blocks, cov4_block_bytes(d)), dtype=torch.uint8, device=dev)
     _check(lib().kv_cov4_build(ctypes.byref(shape), _ptr(K), _ptr(Kcov4), _stream(dev)), "kv_cov4_build")
     return Kcov4
+
+
+def cov_sub_block_elems(d: int, s_dim: int) -> int:
+    """Elements per block of the query-subspace descriptor (CSA_COV_SUB_BLOCK_ELEMS)."""
+    return d + CSA_COBS_RANK * (-(-s_dim // 8) * 8)
+
+
+def kv_cov_sub_build(K: torch.Tensor, U: torch.Tensor, block_size: int, Kcs=None):
+    """Query-subspace second-order descriptors [B, Hkv, nb, cov_sub_block_elems(d, s)] from the
+    basis U [Hkv, d, s] (float32)."""
+    dev = _dev(K, U, Kcs)
+    B, Hkv, n, d = K.shape
+    s_dim = U.shape[-1]
+    shape = Shape(B, Hkv, Hkv, d, n, block_size, _dtype_code(K), 0.0)
+    nb = shape.n_blocks
+    Kcs = torch.empty((B, Hkv, nb, cov_sub_block_elems(d, s_dim)), dtype=K.dtype, device=dev) if Kcs is None else Kcs
+    _check(lib().kv_cov_sub_build(ctypes.byref(shape), s_dim, _ptr(K), _ptr(U), _ptr(Kcs), _stream(dev)),
+           "kv_cov_sub_build")
+    return Kcs
+
+
+def block_score_cobs2_sub(q: torch.Tensor, Kcs: torch.Tensor, U: torch.Tensor, block_size: int, n_tokens: int,
+                          scale: float = 0.0, scores=None, ws=None):
+    """Second-order block scores [B, Hkv, nb] from query-subspace descriptors."""
+    dev = _dev(q, Kcs, U)
+    B, Hq, d = q.shape
+    Hkv, nb = Kcs.shape[1], Kcs.shape[2]
+    s_dim = U.shape[-1]
+    shape = Shape(B, Hq, Hkv, d, n_tokens, block_size, _dtype_code(q), float(scale))
+    scores = torch.empty((B, Hkv, nb), dtype=torch.float32, device=dev) if scores is None else scores
+    ws, wsb = _workspace(shape, CSA_WS_BLOCK_SCORE_COBS2_SUB, 0, 0, ws, dev)
+    _check(lib().block_score_cobs2_sub(ctypes.byref(shape), s_dim, _ptr(q), _ptr(Kcs), _ptr(U), _ptr(scores),
+                                       _ptr(ws), wsb, _stream(dev)), "block_score_cobs2_sub")
+    return scores
 
 
 def kv_var_build(K: torch.Tensor, block_size: int, Kvar=None):

@@ -428,6 +428,46 @@ int kv_cov4_build(const csa_shape* shape, const void* K, void* Kcov4, hipStream_
     return e == hipSuccess ? CSA_OK : hip_fail(e, "kv_cov4_build");
 }
 
+int kv_cov_sub_build(const csa_shape* shape, int32_t s_dim, const void* K, const float* U, void* Kcs,
+                     hipStream_t stream)
+{
+    csa::Dims d;
+    if (int rc = make_dims(shape, &d)) return rc;
+    if (!K || !U || !Kcs) return fail(CSA_ERR_INVALID_ARG, "kv_cov_sub_build: NULL pointer");
+    if (!aligned16(K) || !aligned16(Kcs) || !aligned4(U))
+        return fail(CSA_ERR_INVALID_ARG, "kv_cov_sub_build: misaligned pointer");
+    if (s_dim < 1 || s_dim > d.d)
+        return fail(CSA_ERR_INVALID_ARG, "kv_cov_sub_build: s=%d outside [1, d=%d]", s_dim, d.d);
+    if (!csa::cov_sub_ok(d, s_dim))
+        return fail(CSA_ERR_UNSUPPORTED, "kv_cov_sub_build: blocks of %d tokens (at most 64) or s=%d above 128", d.L,
+                    s_dim);
+    const hipError_t e = csa::launch_cov_sub(d, s_dim, K, U, Kcs, stream);
+    return e == hipSuccess ? CSA_OK : hip_fail(e, "kv_cov_sub_build");
+}
+
+int block_score_cobs2_sub(const csa_shape* shape, int32_t s_dim, const void* q, const void* Kcs, const float* U,
+                          float* scores, void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    csa::Dims d;
+    if (int rc = make_dims(shape, &d)) return rc;
+    if (!q || !Kcs || !U || !scores) return fail(CSA_ERR_INVALID_ARG, "block_score_cobs2_sub: NULL pointer");
+    if (!aligned16(q) || !aligned16(Kcs) || !aligned4(U) || !aligned4(scores))
+        return fail(CSA_ERR_INVALID_ARG, "block_score_cobs2_sub: misaligned pointer");
+    if (s_dim < 1 || s_dim > d.d)
+        return fail(CSA_ERR_INVALID_ARG, "block_score_cobs2_sub: s=%d outside [1, d=%d]", s_dim, d.d);
+    if (d.dtype != csa::DT_BF16 || d.G > 8)
+        return fail(CSA_ERR_UNSUPPORTED, "block_score_cobs2_sub: needs bfloat16 and G <= 8");
+    {
+        const long long bb = 2ll * d.d + 2ll * CSA_COBS_RANK * ((s_dim + 7) / 8 * 8);
+        if ((long long)d.nb * bb >= (1ll << 32))
+            return fail(CSA_ERR_UNSUPPORTED, "block_score_cobs2_sub: one KV head's descriptors must be below 4 GiB");
+    }
+    if (int rc = check_ws(block_score_ws(d), ws, ws_bytes)) return rc;
+    const hipError_t e = csa::launch_score_cobs2_sub(d, s_dim, q, Kcs, U, d.G == 1 ? scores : static_cast<float*>(ws),
+                                                     scores, stream);
+    return e == hipSuccess ? CSA_OK : hip_fail(e, "block_score_cobs2_sub");
+}
+
 int kv_var_build(const csa_shape* shape, const void* K, void* Kvar, hipStream_t stream)
 {
     csa::Dims d;
@@ -753,7 +793,8 @@ size_t csa_workspace_size(const csa_shape* shape, csa_entry entry_arg, int32_t k
     case CSA_WS_BLOCK_SCORE_EXACT_MASS:
     case CSA_WS_BLOCK_SCORE_BOX:
     case CSA_WS_BLOCK_SCORE_COBS2:
-    case CSA_WS_BLOCK_SCORE_COBS2_FP4: return block_score_ws(d);
+    case CSA_WS_BLOCK_SCORE_COBS2_FP4:
+    case CSA_WS_BLOCK_SCORE_COBS2_SUB: return block_score_ws(d);
     case CSA_WS_BLOCK_SCORE_PROXY_ERROR: return error_score_ws(d);
     case CSA_WS_SPARSE_DECODE_ATTN: {
         if (k < 0 || k > d.nb || m < 0) {

@@ -29,6 +29,7 @@ namespace {
 
 constexpr int kCovMaxRows = 64; // tokens per block
 constexpr int kLanczos = 64;    // Lanczos steps: the whole Krylov space of a 64-token block
+constexpr int kSubMax = 128;    // query-subspace dimensions held per block (two columns per lane)
 
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 
@@ -36,7 +37,7 @@ __device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 // to form the Gram matrix; their space then holds the Lanczos vectors.  Rows
 // are padded to a multiple of 4 floats plus 4, so that 16-byte row reads by 16
 // lanes at once fall on distinct banks.
-template <int D>
+template <int D, bool SUB>
 struct CovSmem {
     union {
         float x[kCovMaxRows][D + 4];  // centred keys
@@ -51,6 +52,9 @@ struct CovSmem {
     float y[4][kLanczos];                    // their eigenvectors of the tridiagonal matrix
     float cp[4][kLanczos], dp[4][kLanczos];  // tridiagonal elimination
     float z[4][kCovMaxRows];                 // Ritz vectors over the block's rows
+    // query subspace: the centred keys' coordinates in it, row per token (kept
+    // to the end: the factors are formed from them)
+    float ys[SUB ? kCovMaxRows : 1][SUB ? kSubMax + 4 : 4];
 };
 
 // E2M1 code of r: nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6 by magnitude, ties to the
@@ -67,14 +71,22 @@ __device__ __forceinline__ uint32_t e2m1_code(float r)
 // E2M1 codes] per block (bfloat16 caches): each eigenvector, rounded to bfloat16 as
 // in the plain descriptor, is divided by its scale max_t |xi_t| / 6 and rounded to
 // E2M1; byte t of a row holds coordinates 2t (low nibble) and 2t + 1 (high nibble).
-template <int DT, int D, int R, bool FP4>
-__global__ void __launch_bounds__(64) cov_kernel(const char* K, char* Kcov, int n, int L, int nb)
+//
+// SUB (the query-subspace descriptor of the same page: the covariance kept only
+// within the span of the caller's basis U [Hkv, d, s], the top eigenvectors of the
+// queries' second moment): the centred keys are projected on U first (Y = X U,
+// fp32, the d products of a coordinate in order), the Gram matrix is Y Y^T, and
+// the factors xi = Y^T v / sqrt(c) are the scaled eigenvectors of U^T Sigma U.
+// Stored as [mean: d][R x sps] per block, sps = s rounded up to 8 (zeros after s).
+template <int DT, int D, int R, bool FP4, bool SUB>
+__global__ void __launch_bounds__(64) cov_kernel(const char* K, char* Kcov, int n, int L, int nb, const float* U,
+                                                 int s_dim, int Hkv)
 {
     constexpr int EB = Elem<DT>::bytes;
     constexpr int RB = D * EB;      // bytes per key row
     constexpr int CPL = D / 64;     // columns per lane: lane owns CPL lane .. CPL lane + CPL - 1
     static_assert(R <= 4, "at most four descriptors");
-    __shared__ CovSmem<D> sm;
+    __shared__ CovSmem<D, SUB> sm;
     const int lane = threadIdx.x;
     const long long gblk = blockIdx.x;
     const long long pair = gblk / nb;
@@ -82,7 +94,8 @@ __global__ void __launch_bounds__(64) cov_kernel(const char* K, char* Kcov, int 
     const int t0 = blk * L, c = min(L, n - t0);
     const char* kp = K + ((size_t)pair * n + t0) * RB;
     static_assert(!FP4 || (DT == DT_BF16 && (D == 128 || D == 64)), "FP4 descriptors are for bfloat16 caches");
-    constexpr int BB = FP4 ? 2 * D + 4 * R + R * D / 2 : (1 + R) * RB;  // bytes per block
+    const int sps = SUB ? (s_dim + 7) / 8 * 8 : 0;  // stored subspace row length
+    const int BB = FP4 ? 2 * D + 4 * R + R * D / 2 : SUB ? RB + R * sps * EB : (1 + R) * RB;  // bytes per block
     char* out = Kcov + ((size_t)pair * nb + blk) * BB;
 
     // ---- keys -> LDS (row per lane), mean of this lane's columns (fp64, token
@@ -125,21 +138,49 @@ __global__ void __launch_bounds__(64) cov_kernel(const char* K, char* Kcov, int 
     }
     wave_lds_fence();
 
-    // ---- Gram matrix row of this lane: g[j] = x_lane . x_j (16-byte LDS reads)
+    // ---- query subspace: this lane's row of Y = X U, eight columns at a time
+    // (U's rows are the same for every lane: scalar loads), zero past s
+    const int syp = SUB ? (s_dim + 3) / 4 * 4 : 0;  // Y columns the Gram matrix reads
+    if constexpr (SUB) {
+        const float* Uj = U + (size_t)(pair % Hkv) * D * s_dim;
+        for (int c0 = 0; c0 < syp; c0 += 8) {
+            float acc[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+            for (int t = 0; t < D; ++t) {
+                const float xv = sm.x[lane][t];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] = fmaf(xv, c0 + e < s_dim ? Uj[(size_t)t * s_dim + c0 + e] : 0.0f, acc[e]);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (c0 + e < syp) sm.ys[lane][c0 + e] = acc[e];
+        }
+        wave_lds_fence();
+    }
+
+    // ---- Gram matrix row of this lane: g[j] = x_lane . x_j (16-byte LDS reads;
+    // of the subspace coordinates y with SUB)
     float g[kCovMaxRows];
 #pragma unroll
     for (int j = 0; j < kCovMaxRows; ++j) g[j] = 0.0f;
-    for (int t = 0; t < D; t += 4) {
-        const float4 xl = *reinterpret_cast<const float4*>(&sm.x[lane][t]);
+    auto gram = [&](const float* rows, int stride, int cols) {
+        for (int t = 0; t < cols; t += 4) {
+            const float4 xl = *reinterpret_cast<const float4*>(rows + lane * stride + t);
 #pragma unroll
-        for (int j = 0; j < kCovMaxRows; ++j) {
-            const float4 xj = *reinterpret_cast<const float4*>(&sm.x[j][t]);
-            g[j] = fmaf(xl.x, xj.x, g[j]);
-            g[j] = fmaf(xl.y, xj.y, g[j]);
-            g[j] = fmaf(xl.z, xj.z, g[j]);
-            g[j] = fmaf(xl.w, xj.w, g[j]);
+            for (int j = 0; j < kCovMaxRows; ++j) {
+                const float4 xj = *reinterpret_cast<const float4*>(rows + j * stride + t);
+                g[j] = fmaf(xl.x, xj.x, g[j]);
+                g[j] = fmaf(xl.y, xj.y, g[j]);
+                g[j] = fmaf(xl.z, xj.z, g[j]);
+                g[j] = fmaf(xl.w, xj.w, g[j]);
+            }
         }
-    }
+    };
+    if constexpr (SUB)
+        gram(&sm.ys[0][0], kSubMax + 4, syp);
+    else
+        gram(&sm.x[0][0], D + 4, D);
     if (lane >= c) {
 #pragma unroll
         for (int j = 0; j < kCovMaxRows; ++j) g[j] = 0.0f;
@@ -329,13 +370,29 @@ __global__ void __launch_bounds__(64) cov_kernel(const char* K, char* Kcov, int 
     wave_lds_fence();
 
     // ---- xi_i = X^T z_i / sqrt(c), the centred keys read again from memory (the
-    // same fp32 values as in LDS before); sign: largest-magnitude coordinate positive
-    float xi[R][CPL];
+    // same fp32 values as in LDS before); sign: largest-magnitude coordinate positive.
+    // SUB: xi_i = Y^T z_i / sqrt(c) from the subspace coordinates in LDS, columns
+    // 2 lane and 2 lane + 1 of each lane.
+    constexpr int XC = SUB ? kSubMax / 64 : CPL;  // coordinates per lane
+    float xi[R][XC];
 #pragma unroll
     for (int i = 0; i < R; ++i)
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) xi[i][e] = 0.0f;
-    for (int l = 0; l < c; ++l) {
+        for (int e = 0; e < XC; ++e) xi[i][e] = 0.0f;
+    if constexpr (SUB) {
+        for (int l = 0; l < c; ++l) {
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                const float zi = sm.z[i][l];
+#pragma unroll
+                for (int e = 0; e < XC; ++e) {
+                    const int col = XC * lane + e;
+                    xi[i][e] = fmaf(col < s_dim ? sm.ys[l][col] : 0.0f, zi, xi[i][e]);
+                }
+            }
+        }
+    }
+    for (int l = 0; l < (SUB ? 0 : c); ++l) {
         float f[CPL];
         const char* row = kp + (size_t)l * RB + CPL * lane * EB;
         if constexpr (DT == DT_F32) {
@@ -364,18 +421,19 @@ __global__ void __launch_bounds__(64) cov_kernel(const char* K, char* Kcov, int 
             for (int e = 0; e < CPL; ++e) xi[i][e] = fmaf(f[e], zi, xi[i][e]);
         }
     }
+    (void)syp;
     const float inv_sqrt_c = 1.0f / sqrtf((float)c);
 #pragma unroll
     for (int i = 0; i < R; ++i) {
         float best = -1.0f;
         int bt = 0;
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) {
+        for (int e = 0; e < XC; ++e) {
             xi[i][e] *= inv_sqrt_c;
             const float a = fabsf(xi[i][e]);
             if (a > best) {
                 best = a;
-                bt = CPL * lane + e;
+                bt = XC * lane + e;
             }
         }
         // wave-wide (magnitude, -index) maximum: the first coordinate of largest magnitude
@@ -384,10 +442,23 @@ __global__ void __launch_bounds__(64) cov_kernel(const char* K, char* Kcov, int 
         const int at = (int)~lkey;
         float sgn_src = 0.0f;
 #pragma unroll
-        for (int e = 0; e < CPL; ++e)
-            if (CPL * lane + e == at) sgn_src = xi[i][e];
-        const float sgn = __shfl(sgn_src, at / CPL) < 0.0f ? -1.0f : 1.0f;
-        if constexpr (FP4) {
+        for (int e = 0; e < XC; ++e)
+            if (XC * lane + e == at) sgn_src = xi[i][e];
+        const float sgn = __shfl(sgn_src, at / XC) < 0.0f ? -1.0f : 1.0f;
+        if constexpr (SUB) {
+#pragma unroll
+            for (int e = 0; e < XC; ++e) {
+                const int col = XC * lane + e;
+                if (col < sps) {
+                    const float val = col < s_dim ? xi[i][e] * sgn : 0.0f;
+                    char* row = out + RB + (size_t)i * sps * EB;
+                    if constexpr (DT == DT_F32)
+                        reinterpret_cast<float*>(row)[col] = val;
+                    else
+                        reinterpret_cast<uint16_t*>(row)[col] = bf16_from_f64((double)val);
+                }
+            }
+        } else if constexpr (FP4) {
             float vb[CPL];  // the bfloat16-rounded coordinates, widened exactly
             float amax = 0.0f;
 #pragma unroll
@@ -423,12 +494,13 @@ __global__ void __launch_bounds__(64) cov_kernel(const char* K, char* Kcov, int 
     }
 }
 
-template <int DT, int D, bool FP4>
-hipError_t launch_cov_dtd(const Dims& s, const void* K, void* Kcov, hipStream_t st)
+template <int DT, int D, bool FP4, bool SUB = false>
+hipError_t launch_cov_dtd(const Dims& s, const void* K, void* Kcov, hipStream_t st, const float* U = nullptr,
+                          int s_dim = 0)
 {
     const long long total = (long long)s.pairs() * s.nb;  // one workgroup (one wave) per block
-    cov_kernel<DT, D, kCobsRank, FP4><<<dim3((unsigned)total), dim3(64), 0, st>>>(
-        static_cast<const char*>(K), static_cast<char*>(Kcov), s.n, s.L, s.nb);
+    cov_kernel<DT, D, kCobsRank, FP4, SUB><<<dim3((unsigned)total), dim3(64), 0, st>>>(
+        static_cast<const char*>(K), static_cast<char*>(Kcov), s.n, s.L, s.nb, U, s_dim, s.Hkv);
     return hipGetLastError();
 }
 
@@ -447,6 +519,23 @@ hipError_t launch_cov(const Dims& s, const void* K, void* Kcov, hipStream_t st)
     } else {
         if (s.d == 128) return launch_cov_dtd<DT_F32, 128, false>(s, K, Kcov, st);
         if (s.d == 64) return launch_cov_dtd<DT_F32, 64, false>(s, K, Kcov, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+bool cov_sub_ok(const Dims& s, int s_dim)
+{
+    return cov_build_ok(s) && s_dim >= 1 && s_dim <= s.d && s_dim <= kSubMax;
+}
+
+hipError_t launch_cov_sub(const Dims& s, int s_dim, const void* K, const float* U, void* Kcs, hipStream_t st)
+{
+    if (s.dtype == DT_BF16) {
+        if (s.d == 128) return launch_cov_dtd<DT_BF16, 128, false, true>(s, K, Kcs, st, U, s_dim);
+        if (s.d == 64) return launch_cov_dtd<DT_BF16, 64, false, true>(s, K, Kcs, st, U, s_dim);
+    } else {
+        if (s.d == 128) return launch_cov_dtd<DT_F32, 128, false, true>(s, K, Kcs, st, U, s_dim);
+        if (s.d == 64) return launch_cov_dtd<DT_F32, 64, false, true>(s, K, Kcs, st, U, s_dim);
     }
     return hipErrorInvalidValue;
 }

@@ -395,6 +395,8 @@ struct FusedScoreParams {
     int32_t* sel;   // finish: selection [B, Hkv, k] when k > 0
     float* parts;   // proxy-error split: per (KV head, tile, head) log2 (max, sum) of the summary logits
     const int32_t* offsets;  // clusters: ranges [B, Hkv, nb + 1] give the count terms (else blocks)
+    const float* U;          // query-subspace descriptors: the basis [Hkv, d, s]
+    int s_dim, sps;          // its dimension s and the stored factor length (s rounded up to 8)
     int Hq, Hkv, G, nb, k, chunks;
     float scale, ln_L, ln_last;
 };
@@ -726,6 +728,142 @@ __device__ __forceinline__ void cobs2_tile_logits(const FusedScoreParams& p, __a
     wave_lds_fence();  // tmp is reused by the next tile
 }
 
+// Query-subspace descriptors, per block [mean: d bfloat16][4 x sps bfloat16]
+// (kv_cov_sub_build).  The query's coordinates in the subspace, qt = U^T q, are
+// not bfloat16: each enters the MFMA as two bfloat16 terms (hi + lo, within about
+// 2^-17 of the fp32 value), two chains into one accumulator.  Otherwise the tile
+// of cobs2_tile_logits, the factor rows KSS k-steps of 32 long (chunks past the
+// stored length read as zero).
+template <int D, int KSS>
+__device__ __forceinline__ void cobs2_sub_tile_logits(const FusedScoreParams& p, __amdgpu_buffer_rsrc_t kr,
+                                                      const bf16x8_t (&bq)[D / 32], const bf16x8_t (&bh)[KSS],
+                                                      const bf16x8_t (&bl)[KSS], int base, float* dst, int stride,
+                                                      int lane, float (*tmp)[32])
+{
+    constexpr int RB = D * 2, KS = D / 32;
+    static_assert(kCobsRank == 4, "one output lane holds one block's four factor products");
+    const int n16 = lane & 15, g16 = lane >> 4;
+    const uint32_t BB = (uint32_t)(RB + kCobsRank * p.sps * 2), nch = (uint32_t)(p.sps / 8);
+    uint4 am[2][KS], ax[4][2][KSS];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int tr = rb * 16 + n16;
+        const uint32_t om = (uint32_t)(base + tr) * BB + g16 * 16;  // past nb: zeros
+#pragma unroll
+        for (int s = 0; s < KS; ++s) am[rb][s] = buffer_ld16(kr, om + s * 64);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t ox = (uint32_t)(base + 8 * u + tr / 4) * BB + RB + (uint32_t)(tr % 4) * p.sps * 2;
+#pragma unroll
+            for (int s = 0; s < KSS; ++s) {
+                const uint32_t c = 4 * s + g16;
+                ax[u][rb][s] = c < nch ? buffer_ld16(kr, ox + c * 16) : make_uint4(0, 0, 0, 0);
+            }
+        }
+    }
+    f32x4_t cm[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+            cm[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, am[rb][s]), bq[s], cm[rb], 0, 0,
+                                                             0);
+    float sq[4][2];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        f32x4_t cx[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+        for (int s = 0; s < KSS; ++s)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, ax[u][rb][s]);
+                cx[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh[s], cx[rb], 0, 0, 0);
+                cx[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl[s], cx[rb], 0, 0, 0);
+            }
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+            sq[u][rb] = (cx[rb][0] * cx[rb][0] + cx[rb][1] * cx[rb][1]) + (cx[rb][2] * cx[rb][2] + cx[rb][3] * cx[rb][3]);
+    }
+    if (n16 < p.G) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int tr = rb * 16 + 4 * g16 + i;
+                tmp[n16][tr] = fmaf(cm[rb][i], p.scale, base + tr == p.nb - 1 ? p.ln_last : p.ln_L);
+            }
+    }
+    wave_lds_fence();
+    const float half_s2 = 0.5f * p.scale * p.scale;
+    if (n16 < p.G) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) tmp[n16][8 * u + 4 * rb + g16] += half_s2 * sq[u][rb];
+    }
+    wave_lds_fence();
+    for (int e = lane; e < p.G * 32; e += 64) {
+        const int h = e >> 5, b = e & 31;
+        if (base + b < p.nb) dst[h * stride + base + b] = tmp[h][b];
+    }
+    wave_lds_fence();  // tmp is reused by the next tile
+}
+
+// qt = U^T q for the G heads of KV head j, by the whole workgroup, into
+// qt_sm[h][0 .. 32 KSS) (zeros past s), fp32: a thread per (head, coordinate), the
+// d products in four interleaved partial sums with every load of a row of q and
+// of a column of U issued together.  The caller synchronises before reading it.
+template <int D, int KSS>
+__device__ __forceinline__ void subspace_query(const FusedScoreParams& p, const char* q_first_head, int j,
+                                               float (*qt_sm)[128])
+{
+    const float* Uj = p.U + (size_t)j * D * p.s_dim;
+    const int sd = p.s_dim;
+    for (int e = threadIdx.x; e < p.G * 32 * KSS; e += blockDim.x) {
+        const int h = e / (32 * KSS), c = e - h * (32 * KSS);
+        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (c < sd) {
+            const uint4* q8 = reinterpret_cast<const uint4*>(q_first_head + (size_t)h * D * 2);
+            const float* uc = Uj + c;
+#pragma unroll
+            for (int t8 = 0; t8 < D / 8; ++t8) {
+                float qf[8];
+                unpack<DT_BF16>(q8[t8], qf);
+#pragma unroll
+                for (int e8 = 0; e8 < 8; ++e8) acc[e8 & 3] = fmaf(qf[e8], uc[(size_t)(8 * t8 + e8) * sd], acc[e8 & 3]);
+            }
+        }
+        qt_sm[h][c] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    }
+}
+
+// The B operands of qt (lane (n16, g16): head n16, elements 8 (4 s + g16) .. + 7)
+// as hi + lo bfloat16 terms.
+template <int KSS>
+__device__ __forceinline__ void subspace_operands(const float (*qt_sm)[128], int G, int lane, bf16x8_t (&bh)[KSS],
+                                                  bf16x8_t (&bl)[KSS])
+{
+    const int n16 = lane & 15, g16 = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < KSS; ++s) {
+        uint32_t hw[4] = {0, 0, 0, 0}, lw[4] = {0, 0, 0, 0};
+        if (n16 < G) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = qt_sm[n16][8 * (4 * s + g16) + e];
+                const uint32_t hb = __float_as_uint(x) >> 16;  // the leading 8 significant bits
+                const float r = x - __uint_as_float(hb << 16);
+                const uint32_t ru = __float_as_uint(r);
+                const uint32_t lb = (ru + 0x7fffu + ((ru >> 16) & 1u)) >> 16;
+                hw[e >> 1] |= hb << (16 * (e & 1));
+                lw[e >> 1] |= lb << (16 * (e & 1));
+            }
+        }
+        bh[s] = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+        bl[s] = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+    }
+}
+
 // FP4 descriptors, per block [mean: d bfloat16][4 fp32 scales][4 x d/2 bytes of E2M1
 // codes] (kv_cov4_build).  The same tile as cobs2_tile_logits: the mean rows
 // against q, and the eigenvector rows, their codes widened to bfloat16 by the
@@ -889,6 +1027,59 @@ __global__ void __launch_bounds__(kSplitWaves * 64) score_cobs2_split_kernel(con
     } else {
         cobs2_tile_logits<D>(p, kr, bq, base, p.logits + (size_t)pair * p.G * p.nb, p.nb, lane, tmp[wave]);
     }
+}
+
+// Query-subspace second-order logits, split form: workgroup (pair, chunk), one tile
+// per wave, the subspace query computed by the workgroup first.
+template <int D, int KSS>
+__global__ void __launch_bounds__(kSplitWaves * 64) score_cobs2_sub_split_kernel(const FusedScoreParams p)
+{
+    constexpr int RB = D * 2, KS = D / 32;
+    __shared__ float tmp[kSplitWaves][8][32];
+    __shared__ float qt_sm[8][128];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int pair = blockIdx.x / p.chunks, chunk = blockIdx.x - pair * p.chunks;
+    const int b = pair / p.Hkv, j = pair - b * p.Hkv;
+    const int base = (chunk * kSplitWaves + wave) * 32;
+    const char* q0 = p.q + ((size_t)b * p.Hq + (size_t)j * p.G) * RB;
+    subspace_query<D, KSS>(p, q0, j, qt_sm);
+    __syncthreads();
+    if (base >= p.nb) return;  // whole wave; no barrier after this point
+    bf16x8_t bq[KS], bh[KSS], bl[KSS];
+    load_q_operand<D>(q0, p.G, lane, bq);
+    subspace_operands<KSS>(qt_sm, p.G, lane, bh, bl);
+    const uint32_t BB = (uint32_t)(RB + kCobsRank * p.sps * 2);
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(p.Kbar + (size_t)pair * p.nb * BB, (uint32_t)p.nb * BB);
+    cobs2_sub_tile_logits<D, KSS>(p, kr, bq, bh, bl, base, p.logits + (size_t)pair * p.G * p.nb, p.nb, lane,
+                                  tmp[wave]);
+}
+
+// Query-subspace second-order scores, one workgroup per KV head: the subspace
+// query once, the tiles by the eight waves, the group scores in LDS.
+template <int D, int KSS>
+__global__ void __launch_bounds__(kFusedWaves * 64) score_cobs2_sub_fused_kernel(const FusedScoreParams p)
+{
+    constexpr int RB = D * 2, KS = D / 32, NW = kFusedWaves;
+    extern __shared__ float lsm[];  // [G][nb] block logits
+    __shared__ float lse_h[8];
+    __shared__ float tmp[NW][8][32];
+    __shared__ float qt_sm[8][128];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int pair = blockIdx.x, b = pair / p.Hkv, j = pair - b * p.Hkv;
+    const char* q0 = p.q + ((size_t)b * p.Hq + (size_t)j * p.G) * RB;
+    subspace_query<D, KSS>(p, q0, j, qt_sm);
+    __syncthreads();
+    bf16x8_t bq[KS], bh[KSS], bl[KSS];
+    load_q_operand<D>(q0, p.G, lane, bq);
+    subspace_operands<KSS>(qt_sm, p.G, lane, bh, bl);
+    const uint32_t BB = (uint32_t)(RB + kCobsRank * p.sps * 2);
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(p.Kbar + (size_t)pair * p.nb * BB, (uint32_t)p.nb * BB);
+    for (int base = wave * 32; base < p.nb; base += NW * 32)
+        cobs2_sub_tile_logits<D, KSS>(p, kr, bq, bh, bl, base, lsm, p.nb, lane, tmp[wave]);
+    __syncthreads();
+    group_scores_in_lds<NW>(lsm, lse_h, p.G, p.nb, p.scores + (size_t)pair * p.nb);
 }
 
 // Proxy-error logits ("OpenAttention reads 1% of the KV cache -- Count-aware
@@ -1215,6 +1406,49 @@ hipError_t launch_score_cobs2_t(const Dims& s, const void* q, const void* Kcov, 
         score_cobs2_split_kernel<64, FP4><<<grid, block, 0, st>>>(p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || s.G == 1) return e;  // G == 1: the logits are the scores
+    return launch_score_finish(s, logits, scores, nullptr, 0, st);
+}
+
+hipError_t launch_score_cobs2_sub(const Dims& s, int s_dim, const void* q, const void* Kcs, const float* U,
+                                  float* logits, float* scores, hipStream_t st)
+{
+    FusedScoreParams p = summary_params(s, q, Kcs, false);
+    p.scores = scores;
+    p.logits = logits;
+    p.U = U;
+    p.s_dim = s_dim;
+    p.sps = (s_dim + 7) / 8 * 8;
+    const int kss = (p.sps + 31) / 32;
+    const int tiles = (s.nb + 31) / 32;
+    // one workgroup per KV head when there are enough of them and the logits fit LDS
+    const bool fused = s.pairs() >= kFusedStepMinPairs && fused_summary_score_ok(s);
+    p.chunks = (tiles + kSplitWaves - 1) / kSplitWaves;
+    const dim3 grid((unsigned)(fused ? s.pairs() : s.pairs() * p.chunks)),
+        block(fused ? kFusedWaves * 64 : kSplitWaves * 64);
+    const size_t shm = fused ? (size_t)s.G * s.nb * sizeof(float) : 0;
+#define CSA_SUB_CASE(D, KSS)                                                                 \
+    if (fused)                                                                               \
+        score_cobs2_sub_fused_kernel<D, KSS><<<grid, block, shm, st>>>(p);                   \
+    else                                                                                     \
+        score_cobs2_sub_split_kernel<D, KSS><<<grid, block, 0, st>>>(p)
+    if (s.d == 128) {
+        switch (kss) {
+        case 1: CSA_SUB_CASE(128, 1); break;
+        case 2: CSA_SUB_CASE(128, 2); break;
+        case 3: CSA_SUB_CASE(128, 3); break;
+        case 4: CSA_SUB_CASE(128, 4); break;
+        default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (kss) {
+        case 1: CSA_SUB_CASE(64, 1); break;
+        case 2: CSA_SUB_CASE(64, 2); break;
+        default: return hipErrorInvalidValue;
+        }
+    }
+#undef CSA_SUB_CASE
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || fused || s.G == 1) return e;  // G == 1: the logits are the scores
     return launch_score_finish(s, logits, scores, nullptr, 0, st);
 }
 

@@ -50,7 +50,7 @@ class Workload:
     block_size: int
     dtype: str  # "f32" or "bf16"
     k: int  # blocks read exactly per KV head
-    score_mode: str  # "summary", "exact_mass", "box", "cobs2", "cobs2_fp4", "proxy_error" or "cluster"
+    score_mode: str  # "summary", "exact_mass", "box", "cobs2", "cobs2_fp4", "cobs2_sub", "proxy_error" or "cluster"
     proxies: bool  # one count-aware proxy per unread block
     keys: str  # "heavy_hitters" or "clusters"
     n_clusters: int = 64
@@ -59,6 +59,7 @@ class Workload:
     qgc: int = 0  # query-guided clusters per KV head (score_mode "cluster"), 0 = blocks
     qgc_iters: int = 8  # Lloyd rounds of the cluster build
     qgc_rank: int = 16  # dimensions of the projection the clusters are found in
+    sub_dim: int = 0  # query-subspace dimension s of the "cobs2_sub" descriptors
 
     @property
     def group(self) -> int:
@@ -101,6 +102,10 @@ WORKLOADS = {
                  "clusters", description="the headline layer with second-order (mean + rank-4 covariance) scores"),
         Workload("llama3_8b_layer_b32_cobs2_fp4", 1002, 32, 32, 8, 128, 32768, 64, "bf16", 5, "cobs2_fp4", True,
                  "clusters", description="the headline layer with second-order scores from FP4 (E2M1) eigenvectors"),
+        Workload("llama3_8b_layer_b32_cobs2_sub", 1002, 32, 32, 8, 128, 32768, 64, "bf16", 5, "cobs2_sub", True,
+                 "clusters", sub_dim=85,
+                 description="the headline layer with second-order scores whose covariance is kept in an "
+                             "85-dimensional query subspace (340 instead of 512 factor floats per block)"),
         Workload("llama3_8b_layer_b32_err", 1002, 32, 32, 8, 128, 32768, 64, "bf16", 5, "proxy_error", True,
                  "clusters", description="the headline layer with exact reads spent on the largest estimated "
                                          "proxy errors (mean and variance tokens)"),

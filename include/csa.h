@@ -102,7 +102,8 @@ typedef enum csa_entry {
     CSA_WS_BLOCK_SCORE_COBS2_FP4 = 8,
     CSA_WS_KV_CLUSTER_BUILD = 9, /* k = n_clusters, m = rank */
     CSA_WS_CLUSTER_SCORE = 10,      /* k = n_clusters, m unused */
-    CSA_WS_CLUSTER_DECODE_STEP = 11 /* k = clusters read exactly, m = n_clusters */
+    CSA_WS_CLUSTER_DECODE_STEP = 11, /* k = clusters read exactly, m = n_clusters */
+    CSA_WS_BLOCK_SCORE_COBS2_SUB = 12 /* block_score_cobs2_sub                       */
 } csa_entry;
 
 typedef struct csa_shape {
@@ -168,6 +169,39 @@ int kv_cov_build(const csa_shape* shape, const void* K, void* Kcov, hipStream_t 
  */
 #define CSA_COV4_BLOCK_BYTES(d) (2 * (d) + 4 * CSA_COBS_RANK + CSA_COBS_RANK * (d) / 2)
 int kv_cov4_build(const csa_shape* shape, const void* K, void* Kcov4, hipStream_t stream);
+
+/*
+ * kv_cov_sub_build -- the query-subspace form of the second-order descriptor
+ * ([COBS] section on keeping the covariance only within the query subspace:
+ * ranking needs Sigma_b only through q^T Sigma_b q, so the covariance is kept
+ * within the span of U, the top s eigenvectors of the queries' second moment).
+ * U [Hkv, d, s] float (orthonormal columns, the caller's query statistics per KV
+ * head, shared by the batch).  Per block: the mean key (the bits of
+ * kv_summary_build's Kbar), then the top CSA_COBS_RANK scaled eigenvectors
+ * xi_i = sqrt(mu_i) v_i of B_b = U^T Sigma_b U (s x s), largest first, each
+ * signed so that its largest-magnitude coordinate is positive, rounded once to
+ * the storage dtype and zero-padded to sps = s rounded up to 8 elements.  Writes
+ * Kcs [B, Hkv, nb, CSA_COV_SUB_BLOCK_ELEMS(d, s)] elements of the cache dtype (at
+ * d = 128, s = 85: the factors take 4 x 88 stored elements for the page's 340
+ * against 512 of the full-space descriptor).  fp32 projection Y = X U of the
+ * centred keys, then the Gram-matrix eigen-solve of kv_cov_build on Y.
+ * 1 <= s <= d (CSA_ERR_INVALID_ARG otherwise); blocks of at most 64 tokens
+ * (else CSA_ERR_UNSUPPORTED).  Run once per cache; no workspace.
+ */
+#define CSA_COV_SUB_BLOCK_ELEMS(d, s) ((d) + CSA_COBS_RANK * (((s) + 7) / 8 * 8))
+int kv_cov_sub_build(const csa_shape* shape, int32_t s_dim, const void* K, const float* U, void* Kcs,
+                     hipStream_t stream);
+
+/*
+ * block_score_cobs2_sub -- block scores from query-subspace descriptors: the block
+ * logit scale q_h . Kbar_b + ln c_b + (1/2) scale^2 sum_i (qt_h . xi_bi)^2 with
+ * qt_h = U^T q_h (fp32) the query's coordinates in its KV head's subspace, and the
+ * group rule of block_score.  Kcs from kv_cov_sub_build with the same U and s.
+ * bfloat16 and G <= 8 (else CSA_ERR_UNSUPPORTED).  Writes scores [B, Hkv, nb].
+ * Workspace: csa_workspace_size(shape, CSA_WS_BLOCK_SCORE_COBS2_SUB, 0, 0) bytes.
+ */
+int block_score_cobs2_sub(const csa_shape* shape, int32_t s_dim, const void* q, const void* Kcs, const float* U,
+                          float* scores, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * kv_var_build -- per block, the mean and the variance tokens that the

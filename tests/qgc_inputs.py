@@ -1,8 +1,10 @@
-"""Caller-side inputs of the query-guided cluster build ("OpenAttention reads 1% of the KV cache
--- Count-aware tail proxy", section "Three helpers that make the proxy accurate": keys are
-projected onto the top eigenvectors of the queries).  The library takes the projection basis
-and the seed tokens as inputs; the tests and the benchmark make them here, from the seeded
-prefill queries of the workload generator."""
+"""Caller-side query statistics: the basis of the query-guided cluster build ("OpenAttention
+reads 1% of the KV cache -- Count-aware tail proxy", section "Three helpers that make the proxy
+accurate": keys are projected onto the top eigenvectors of the queries) and of the
+query-subspace descriptors ("COBS: Cumulant Order Block Sparse Attention", section on keeping
+the covariance within the query subspace), and the cluster seeds.  The library takes them as
+inputs; the tests and the benchmark make them here, from the seeded prefill queries of the
+workload generator."""
 import numpy as np
 
 
@@ -27,3 +29,12 @@ def query_basis(queries: np.ndarray, r: int) -> np.ndarray:
 def seed_tokens(B: int, Hkv: int, n: int, C: int) -> np.ndarray:
     """The tokens whose projections start the C centroids: evenly spaced, c n / C."""
     return np.broadcast_to((np.arange(C, dtype=np.int64) * n // C).astype(np.int32), (B, Hkv, C)).copy()
+
+
+def pooled_query_basis(queries: np.ndarray, s_dim: int) -> np.ndarray:
+    """[B, Hkv, N, d] prefill queries -> [Hkv, d, s] float32: per KV head the query basis of
+    its queries pooled over the batch (the query statistics of a layer's KV head, shared by
+    every sequence)."""
+    B, Hkv, N, d = queries.shape
+    pooled = np.ascontiguousarray(np.transpose(queries, (1, 0, 2, 3)).reshape(Hkv, B * N, d))
+    return query_basis(pooled, s_dim)

@@ -381,3 +381,22 @@ def test_cluster_score_and_attention_argument_checks(L):
     assert attn(s, proxy=2) == csa.CSA_ERR_INVALID_ARG
     assert attn(s, sel=None) == csa.CSA_ERR_INVALID_ARG
     assert attn(s, kc=None) == csa.CSA_ERR_INVALID_ARG
+
+
+def test_cov_sub_argument_checks(L):
+    s = shape()  # d = 128, L = 64
+    assert L.kv_cov_sub_build(ctypes.byref(s), 85, None, FAKE, FAKE, None) == csa.CSA_ERR_INVALID_ARG
+    assert L.kv_cov_sub_build(ctypes.byref(s), 0, FAKE, FAKE, FAKE, None) == csa.CSA_ERR_INVALID_ARG
+    assert L.kv_cov_sub_build(ctypes.byref(s), 129, FAKE, FAKE, FAKE, None) == csa.CSA_ERR_INVALID_ARG
+    assert L.kv_cov_sub_build(ctypes.byref(s), 85, FAKE, FAKE + 2, FAKE, None) == csa.CSA_ERR_INVALID_ARG
+    big = shape(L=128)
+    assert L.kv_cov_sub_build(ctypes.byref(big), 85, FAKE, FAKE, FAKE, None) == csa.CSA_ERR_UNSUPPORTED
+    assert csa.cov_sub_block_elems(128, 85) == 128 + 4 * 88
+    f32 = shape(dtype=csa.CSA_F32)
+    assert L.block_score_cobs2_sub(ctypes.byref(f32), 85, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20,
+                                   None) == csa.CSA_ERR_UNSUPPORTED
+    assert L.block_score_cobs2_sub(ctypes.byref(shape(Hq=18)), 85, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20,
+                                   None) == csa.CSA_ERR_UNSUPPORTED  # G = 9
+    assert L.block_score_cobs2_sub(ctypes.byref(s), 85, FAKE, FAKE, FAKE, FAKE, None, 0,
+                                   None) == csa.CSA_ERR_WORKSPACE
+    assert csa.workspace_size(s, csa.CSA_WS_BLOCK_SCORE_COBS2_SUB) == csa.workspace_size(s, csa.CSA_WS_BLOCK_SCORE_COBS2)
