@@ -68,19 +68,35 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 COPY_PROBE_BYTES = 1 << 30
 # kernels whose HBM traffic is reported, by the name rocprofv3 records
 TRAFFIC_KERNELS = {"decode_step": "decode_step_kernel", "sparse_decode_attn": "attn_mfma_kernel",
-                   "cluster_decode_attn": "cluster_attn_kernel", "cluster_logits": "cluster_logits_kernel"}
+                   "cluster_decode_attn": "cluster_attn_kernel", "cluster_logits": "cluster_logits_kernel",
+                   "block_score_exact": "logits_exact_mfma_kernel", "block_score_exact_valu": "logits_exact_kernel",
+                   "score_logits_split": "score_logits_split_kernel", "score_finish": "score_finish_kernel",
+                   "attn_merge": "attn_merge_kernel", "topk": "topk_"}
 
 
-def source_hash(csrc=None):
-    """Hash of the HIP sources' code (comments and whitespace dropped): a traffic file
-    measured on other code is stale."""
+# The device sources each counted kernel is compiled from (its traffic is stale once any of
+# them changes; the host-side declarations in launch.hpp and api.hip do not count).
+_DEVICE_COMMON = ["device.hpp", "select.hpp", "attn_engine.hpp"]
+KERNEL_SOURCES = {"decode_step": ["step.hip"], "sparse_decode_attn": ["attn.hip"],
+                  "cluster_decode_attn": ["cluster.hip"], "cluster_logits": ["cluster.hip"],
+                  "block_score_exact": ["score.hip"], "block_score_exact_valu": ["score.hip"],
+                  "score_logits_split": ["score.hip"], "score_finish": ["score.hip"], "attn_merge": ["attn.hip"],
+                  "topk": ["topk.hip"]}
+
+
+def source_hash(csrc=None, files=None):
+    """Hash of the HIP sources' code (comments and whitespace dropped), of the files named
+    (else of all of them): a traffic figure measured on other code is stale."""
     import glob
     import hashlib
     import re
 
     h = hashlib.sha256()
     csrc = csrc or os.path.join(HERE, "coreset_softmax_attention_amd", "csrc")
-    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.hpp"))):
+    names = sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.hpp")))
+    if files is not None:
+        names = [os.path.join(csrc, f) for f in sorted(set(files) | set(_DEVICE_COMMON))]
+    for f in names:
         h.update(os.path.basename(f).encode())
         with open(f, encoding="utf-8") as fh:
             code = re.sub(r"/\*.*?\*/", " ", fh.read(), flags=re.S)
@@ -120,7 +136,8 @@ def counters_to_traffic(fetch_db, write_db, copy_fetch_db, copy_write_db, out_pa
         if f is None or w is None:  # not run by this workload
             continue
         kernels[key] = {"kernel": name, "fetch_kib": f, "write_kib": w, "dispatches": [nf, nw],
-                        "bytes": f * 1024.0 * fetch_scale + w * 1024.0 * write_scale}
+                        "bytes": f * 1024.0 * fetch_scale + w * 1024.0 * write_scale,
+                        "source_hash": source_hash(files=KERNEL_SOURCES[key])}
     rec = {"workload": workload, "source_hash": source_hash(),
            "copy_probe": {"bytes": COPY_PROBE_BYTES, "fetch_kib": copy_fetch, "write_kib": copy_write,
                           "fetch_scale": fetch_scale, "write_scale": write_scale},
@@ -135,14 +152,19 @@ def counters_to_traffic(fetch_db, write_db, copy_fetch_db, copy_write_db, out_pa
 
 
 def load_traffic(path):
-    """Measured bytes per launch, or None when absent or measured on other kernel sources."""
+    """Measured bytes per launch of the kernels whose device sources are unchanged since (the
+    others are left out, reported as null), or None when there is no record."""
     if not path or not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("source_hash") != source_hash():
-        print(f"[bench] {path} was measured on other kernel sources: traffic not reported", file=sys.stderr)
-        return None
-    return rec.get("bytes_per_launch")
+    out = {}
+    for key, k in rec.get("kernels", {}).items():
+        if key in KERNEL_SOURCES and k.get("source_hash") == source_hash(files=KERNEL_SOURCES[key]):
+            out[key] = k["bytes"]
+        else:
+            print(f"[bench] {path}: {key} was measured on other kernel sources: traffic not reported",
+                  file=sys.stderr)
+    return out
 
 
 def copy_probe(nbytes):

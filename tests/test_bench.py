@@ -97,3 +97,24 @@ def test_cluster_bytes_counts_the_selection_actually_made():
     assert by["step"] == (common + 2 * 4 * row + 3 * row, 2 * 2 * 129 * 4)
     assert by["attn"] == (common + 3 * 2 * row, 2 * 2 * 129 * 4)
     json.dumps(by)
+
+
+def test_kernel_source_hash_follows_only_its_own_files(tmp_path):
+    """A kernel's traffic stays valid when another kernel's source or a host declaration
+    changes, and goes stale when its own source or a shared device header does."""
+    src = os.path.join(ROOT, "coreset_softmax_attention_amd", "csrc")
+    dst = tmp_path / "csrc"
+    shutil.copytree(src, dst)
+    files = bench.KERNEL_SOURCES["decode_step"]
+    h0 = bench.source_hash(str(dst), files)
+    for other in ("cluster.hip", "launch.hpp"):
+        f = dst / other
+        f.write_text(f.read_text() + "\nstatic int unused_marker = 1;\n")
+    assert bench.source_hash(str(dst), files) == h0
+    for own in ("step.hip", "attn_engine.hpp"):
+        f = dst / own
+        text = f.read_text()
+        f.write_text(text + "\nstatic int unused_marker = 1;\n")
+        assert bench.source_hash(str(dst), files) != h0
+        f.write_text(text)
+    assert bench.source_hash(str(dst), files) == h0
