@@ -463,6 +463,77 @@ def cobs2_sub_logits(shape: Shape, q, Kcs, U):
     return out
 
 
+def sub4_padded(s_dim: int) -> int:
+    """Coordinates per FP4 query-subspace factor: s rounded up to 32 (16 bytes of codes)."""
+    return -(-s_dim // 32) * 32
+
+
+def sub4_block_bytes(d: int, s_dim: int, rank: int = COBS_RANK) -> int:
+    """Bytes per block of the FP4 query-subspace descriptor: the bfloat16 mean key, one fp32
+    scale per factor, then the factors' 4-bit codes (two per byte, zero codes past s)."""
+    return 2 * d + 4 * rank + rank * sub4_padded(s_dim) // 2
+
+
+def cov_sub4_pack(shape: Shape, Kcs, s_dim: int):
+    """FP4 storage of query-subspace descriptors (the FP4 quantisation of the COBS page applied
+    to the subspace factors), from the stored bfloat16 descriptors Kcs: per block the mean row
+    (its bits), the scales s_i = max_t |xi_it| / 6 (binary32), then for each factor the codes
+    of xi_it / s_i (binary32 quotient) for t < s and zero codes up to sub4_padded(s), coordinate
+    2t in the low and 2t + 1 in the high nibble of byte t.  Returns uint8
+    [B, Hkv, nb, sub4_block_bytes(d, s)]."""
+    assert shape.dtype == "bf16"
+    B, Hkv, nb, d, r = shape.batch, shape.n_kv_heads, shape.n_blocks, shape.head_dim, COBS_RANK
+    sp, sf = sub_padded(s_dim), sub4_padded(s_dim)
+    C = np.asarray(Kcs, np.uint16).reshape(B, Hkv, nb, d + r * sp)
+    out = np.zeros((B, Hkv, nb, sub4_block_bytes(d, s_dim)), np.uint8)
+    out[..., :2 * d] = C[..., :d].copy().view(np.uint8).reshape(B, Hkv, nb, 2 * d)
+    xi = widen("bf16", C[..., d:].reshape(B, Hkv, nb, r, sp)[..., :s_dim]).astype(np.float32)  # exact
+    for b in range(B):
+        for j in range(Hkv):
+            for blk in range(nb):
+                for i in range(r):
+                    x = xi[b, j, blk, i]
+                    sc = np.float32(np.abs(x).max()) / np.float32(6.0)
+                    out[b, j, blk, 2 * d + 4 * i:2 * d + 4 * i + 4] = np.frombuffer(np.float32(sc).tobytes(), np.uint8)
+                    codes = [e2m1_code(np.float32(v) / sc) if sc > 0 else 0 for v in x] + [0] * (sf - s_dim)
+                    base = 2 * d + 4 * r + i * sf // 2
+                    for t in range(sf // 2):
+                        out[b, j, blk, base + t] = codes[2 * t] | (codes[2 * t + 1] << 4)
+    return out
+
+
+def cov_sub4_unpack(shape: Shape, packed, s_dim: int):
+    """Mean keys (fp64) [B, Hkv, nb, d] and decoded factors s_i x E2M1(code) (fp64)
+    [B, Hkv, nb, r, s] of FP4 query-subspace descriptors."""
+    B, Hkv, nb, d, r = shape.batch, shape.n_kv_heads, shape.n_blocks, shape.head_dim, COBS_RANK
+    sf = sub4_padded(s_dim)
+    P = np.asarray(packed, np.uint8).reshape(B, Hkv, nb, sub4_block_bytes(d, s_dim))
+    mean = widen("bf16", P[..., :2 * d].copy().view(np.uint16))
+    scales = P[..., 2 * d:2 * d + 4 * r].copy().view(np.float32).astype(np.float64)
+    codes = P[..., 2 * d + 4 * r:].reshape(B, Hkv, nb, r, sf // 2)
+    nib = np.stack([codes & 15, codes >> 4], axis=-1).reshape(B, Hkv, nb, r, sf)[..., :s_dim]
+    mag = np.asarray(E2M1)[nib & 7]
+    return mean, scales[..., None] * np.where(nib & 8, -mag, mag)
+
+
+def cobs2_sub4_logits(shape: Shape, q, packed, U):
+    """The logits of cobs2_sub_logits from FP4 query-subspace descriptors (decoded factors)."""
+    B, Hq, Hkv, d, nb = shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.n_blocks
+    G = Hq // Hkv
+    U = np.asarray(U, np.float64)
+    qf = widen(shape, _stored(shape, q, (B, Hq, d)))
+    mean, xi = cov_sub4_unpack(shape, packed, U.shape[-1])
+    scale = shape.scale if shape.scale else 1.0 / math.sqrt(d)
+    counts = np.array([min(shape.block_size, shape.n_tokens - i * shape.block_size) for i in range(nb)], np.float64)
+    out = np.empty((B, Hq, nb), np.float64)
+    for h in range(Hq):
+        qt = qf[:, h] @ U[h // G]
+        m1 = np.einsum("bd,bkd->bk", qf[:, h], mean[:, h // G])
+        m2 = np.einsum("bs,bkrs->bkr", qt, xi[:, h // G])
+        out[:, h] = scale * m1 + np.log(counts) + 0.5 * scale * scale * (m2 ** 2).sum(-1)
+    return out
+
+
 def block_logits(shape: Shape, mode: int, q, keys):
     """Per-query-head block logits [B, Hq, nb]: first-order summary score, exact ln m_b, or the
     largest logit over the block's key box."""

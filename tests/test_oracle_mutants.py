@@ -133,6 +133,9 @@ PY_MUTANTS = {
                                                            "max(mu[s_dim - 1 - i], 0.0) * v"),
     "smallest subspace directions kept": ("v = V[:, s_dim - 1 - i]", "v = V[:, i]"),
     "query projected with another KV head's basis": ("qt = qf[:, h] @ U[h // G]", "qt = qf[:, h] @ U[(h + 1) % Hkv]"),
+    "FP4 subspace padding codes not zero": ("+ [0] * (sf - s_dim)", "+ [1] * (sf - s_dim)"),
+    "FP4 subspace factors decoded without the scale": ("return mean, scales[..., None] * np.where(nib & 8, -mag, mag)",
+                                                       "return mean, np.where(nib & 8, -mag, mag)"),
     "subspace term without the one half": ("(m2 ** 2).sum(-1)\n    return out\n\n\ndef block_logits",
                                            "(m2 ** 2).sum(-1) * 2.0\n    return out\n\n\ndef block_logits"),
 }
@@ -155,6 +158,8 @@ PY_BATTERY = [
     P.test_subspace_score_is_exact_when_query_and_spread_live_in_the_subspace,
     P.test_subspace_term_at_full_rank_is_the_projected_quadratic_form,
     P.test_subspace_basis_of_coordinate_axes_keeps_the_leading_block,
+    P.test_sub_fp4_size_and_layout_by_hand,
+    P.test_sub_fp4_score_equals_bf16_score_on_grid_exact_factors,
 ]
 
 

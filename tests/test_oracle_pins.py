@@ -1141,3 +1141,54 @@ def test_subspace_basis_of_coordinate_axes_keeps_the_leading_block():
         best = (W[:, :O.COBS_RANK] * sv[:O.COBS_RANK]) @ W[:, :O.COBS_RANK].T
         x = xi[0, 0, blk]
         assert np.linalg.norm(x.T @ x - best) <= 1e-9 * np.linalg.norm(best)
+
+
+def test_sub_fp4_size_and_layout_by_hand():
+    """FP4 query-subspace descriptors: s = 85 takes 96 coordinates (48 bytes of codes) per factor,
+    464 bytes per block at d = 128; on a hand-made descriptor every byte is where the layout puts
+    it (mean bits, binary32 scales max|xi|/6, coordinate 2t low and 2t + 1 high, zero codes past s)."""
+    assert O.sub4_padded(85) == 96 and O.sub4_block_bytes(128, 85) == 256 + 16 + 4 * 48
+    d, s_dim = 16, 5
+    shp = O.Shape(1, 1, 1, d, 4, 4, "bf16")
+    mean = np.arange(1, d + 1, dtype=np.float32) / 8
+    fac = np.zeros((4, O.sub_padded(s_dim)), np.float32)
+    fac[0, :5] = [3.0, -1.5, 0.75, 0.0, 6.0]   # scale 1: codes 5, 8|3, 2, 0, 7
+    fac[1, :5] = [0.5, 0.5, -0.25, 1.0, 2.0]    # scale 1/3: 1.5, 1.5, -0.75, 3, 6 -> 3, 3, 8|2 (tie to even), 5, 7
+    Kcs = np.concatenate([W.to_bf16_bits(mean), W.to_bf16_bits(fac.reshape(-1))])[None, None, None]
+    P = O.cov_sub4_pack(shp, Kcs, s_dim)[0, 0, 0]
+    assert P.size == 2 * d + 16 + 4 * 16
+    assert np.array_equal(P[:2 * d].view(np.uint16), Kcs[0, 0, 0, :d])
+    sc = P[2 * d:2 * d + 16].view(np.float32)
+    assert sc[0] == np.float32(1.0) and sc[1] == np.float32(2.0) / np.float32(6.0) and sc[2] == 0 and sc[3] == 0
+    c0 = P[2 * d + 16:2 * d + 32]
+    assert list(c0[:3]) == [5 | (11 << 4), 2 | (0 << 4), 7 | (0 << 4)] and not c0[3:].any()
+    c1 = P[2 * d + 32:2 * d + 48]
+    assert list(c1[:3]) == [3 | (3 << 4), 10 | (5 << 4), 7] and not c1[3:].any()
+
+
+def test_sub_fp4_score_equals_bf16_score_on_grid_exact_factors():
+    """Factors that are already scale x E2M1 values (largest coordinate 6 x scale) survive FP4
+    storage, so the FP4 and bfloat16 query-subspace scores agree exactly; on general factors the
+    decoded values lie within half a grid step of the stored ones."""
+    n, L, d, s_dim = 128, 32, 64, 21
+    shp = O.Shape(1, 2, 1, d, n, L, "bf16")
+    rng = np.random.default_rng(66)
+    q, K, _ = rand_case(66, 1, 2, 1, d, n, "bf16", qscale=2.0)
+    U = orthonormal(rng, d, s_dim)[None].astype(np.float32)
+    C = O.cov_sub_build(shp, K, U)
+    sp = O.sub_padded(s_dim)
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    fac = (rng.choice(grid, size=(1, 1, shp.n_blocks, 4, s_dim)) * rng.choice([-1, 1], size=(1, 1, shp.n_blocks, 4, s_dim))
+           * 0.125)
+    fac[..., 0] = 6.0 * 0.125
+    G = C.copy()
+    full = np.zeros((1, 1, shp.n_blocks, 4, sp))
+    full[..., :s_dim] = fac
+    G[..., d:] = W.to_bf16_bits(full.astype(np.float32)).reshape(1, 1, shp.n_blocks, 4 * sp)
+    a = O.cobs2_sub4_logits(shp, q, O.cov_sub4_pack(shp, G, s_dim), U)
+    b = O.cobs2_sub_logits(shp, q, G, U)
+    assert np.array_equal(a, b)
+    mean, dec = O.cov_sub4_unpack(shp, O.cov_sub4_pack(shp, C, s_dim), s_dim)
+    _, stored = O.cov_sub_unpack(shp, C, s_dim)
+    step = np.abs(stored).max(axis=-1, keepdims=True) / 6.0 * 2.0  # the widest grid step
+    assert np.all(np.abs(dec - stored) <= 0.5 * step + 1e-12)
