@@ -233,12 +233,15 @@ def step_bytes(w, m=0):
     elif w.score_mode == "cobs2_sub":  # mean key and four padded subspace factors of every block
         sps = -(-w.sub_dim // 8) * 8
         per_read = nb * (d + 4 * sps) * e + unread * d * e + k * L * 2 * d * e
+    elif w.score_mode == "cobs2_sub_fp4":  # mean key, four scales and four rows of FP4 codes of every block
+        spf = -(-w.sub_dim // 32) * 32
+        per_read = nb * (2 * d + 16 + 2 * spf) + unread * d * e + k * L * 2 * d * e
     else:  # second-order: the mean key and four eigenvector rows of every block
         per_read = 5 * nb * d * e + unread * d * e + k * L * 2 * d * e
     per_read += m * (2 * d * e + 8) + G * d * e
     per_write = G * (d + 1) * 4
     pairs = w.batch * w.n_kv_heads
-    basis = w.n_kv_heads * d * w.sub_dim * 4 if w.score_mode == "cobs2_sub" else 0  # U, once per step
+    basis = w.n_kv_heads * d * w.sub_dim * 4 if w.score_mode.startswith("cobs2_sub") else 0  # U, once per step
     return pairs * per_read + basis, pairs * per_write
 
 
@@ -354,11 +357,12 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     summary_ms = e0.elapsed_time(e1)
-    box = w.score_mode in ("box", "cobs2", "proxy_error", "cobs2_fp4", "cobs2_sub")  # extra per-block summaries
+    box = w.score_mode in ("box", "cobs2", "proxy_error", "cobs2_fp4", "cobs2_sub", "cobs2_sub_fp4")  # extra summaries
     Kbox0 = None
     extra_ms = None
     Usub = None
-    if w.score_mode == "cobs2_sub":  # the query basis of each KV head, from the seeded prefill queries
+    sub_fp4 = w.score_mode == "cobs2_sub_fp4"
+    if w.score_mode.startswith("cobs2_sub"):  # the query basis of each KV head, from the seeded prefill queries
         sys.path.insert(0, os.path.join(HERE, "tests"))
         import qgc_inputs as QI
 
@@ -366,7 +370,8 @@ def main():
     if box:
         build = {"box": csa.kv_box_build, "cobs2": csa.kv_cov_build, "proxy_error": csa.kv_var_build,
                  "cobs2_fp4": csa.kv_cov4_build,
-                 "cobs2_sub": lambda K, L, out=None: csa.kv_cov_sub_build(K, Usub, L, out)}[w.score_mode]
+                 "cobs2_sub": lambda K, L, out=None: csa.kv_cov_sub_build(K, Usub, L, out),
+                 "cobs2_sub_fp4": lambda K, L, out=None: csa.kv_cov_sub_build(K, Usub, L, out, fp4=True)}[w.score_mode]
         Kbox0 = build(K0, w.block_size)
         torch.cuda.synchronize()
         e0.record()
@@ -389,7 +394,8 @@ def main():
                   "box": csa.CSA_WS_BLOCK_SCORE_BOX, "cobs2": csa.CSA_WS_BLOCK_SCORE_COBS2,
                   "proxy_error": csa.CSA_WS_BLOCK_SCORE_PROXY_ERROR,
                   "cobs2_fp4": csa.CSA_WS_BLOCK_SCORE_COBS2_FP4,
-                  "cobs2_sub": csa.CSA_WS_BLOCK_SCORE_COBS2_SUB}[w.score_mode]
+                  "cobs2_sub": csa.CSA_WS_BLOCK_SCORE_COBS2_SUB,
+                  "cobs2_sub_fp4": csa.CSA_WS_BLOCK_SCORE_COBS2_SUB}[w.score_mode]
     ws_score = torch.empty(max(1, csa.workspace_size(shape, mode_entry)), dtype=torch.uint8, device=dev)
     ws_attn = torch.empty(max(1, csa.workspace_size(shape, csa.CSA_WS_SPARSE_DECODE_ATTN, w.k, m)),
                           dtype=torch.uint8, device=dev)
@@ -399,8 +405,8 @@ def main():
     def score_select(layer):
         K, V, Kbar, Vbar, Kbox = layer
         keys = Kbar if w.score_mode == "summary" else K if w.score_mode == "exact_mass" else Kbox
-        if w.score_mode == "cobs2_sub":
-            csa.block_score_cobs2_sub(q, keys, Usub, w.block_size, w.n_tokens, scores=scores, ws=ws_score)
+        if w.score_mode.startswith("cobs2_sub"):
+            csa.block_score_cobs2_sub(q, keys, Usub, w.block_size, w.n_tokens, scores=scores, ws=ws_score, fp4=sub_fp4)
         else:
             csa.block_score(q, keys, w.score_mode, w.block_size, n_tokens=w.n_tokens, scores=scores, ws=ws_score)
         csa.topk_select(scores, w.k, sel=sel)
@@ -496,7 +502,7 @@ def main():
         "modular_breakdown_us": {"block_score+topk_select": score_ms * 1e3 if score_ms else None,
                                  "sparse_decode_attn": attn_ms * 1e3},
         "kv_summary_build_ms": summary_ms,
-        **({f"kv_{ {'box': 'box', 'cobs2': 'cov', 'proxy_error': 'var', 'cobs2_fp4': 'cov4', 'cobs2_sub': 'cov_sub'}[w.score_mode]}_build_ms": extra_ms}
+        **({f"kv_{ {'box': 'box', 'cobs2': 'cov', 'proxy_error': 'var', 'cobs2_fp4': 'cov4', 'cobs2_sub': 'cov_sub', 'cobs2_sub_fp4': 'cov_sub4'}[w.score_mode]}_build_ms": extra_ms}
            if extra_ms is not None else {}),
         "dense_decode_attn_ms": dense_ms,
         "step_vs_dense_speedup": (dense_ms / t_step) if dense_ms else None,

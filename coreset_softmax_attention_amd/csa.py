@@ -90,6 +90,8 @@ _SIGS = {
                             _P],
     "kv_cov_sub_build": [ctypes.POINTER(Shape), _I32, _P, _P, _P, _P],
     "block_score_cobs2_sub": [ctypes.POINTER(Shape), _I32, _P, _P, _P, _P, _P, _SZ, _P],
+    "kv_cov_sub4_build": [ctypes.POINTER(Shape), _I32, _P, _P, _P, _P],
+    "block_score_cobs2_sub4": [ctypes.POINTER(Shape), _I32, _P, _P, _P, _P, _P, _SZ, _P],
     "cluster_decode_step": [ctypes.POINTER(Shape), _I32, _P, _P, _P, _P, _P, _P, _I32, ctypes.c_int, _P, _P, _P, _P,
                             _P, _SZ, _P],
 }
@@ -231,23 +233,31 @@ def cov_sub_block_elems(d: int, s_dim: int) -> int:
     return d + CSA_COBS_RANK * (-(-s_dim // 8) * 8)
 
 
-def kv_cov_sub_build(K: torch.Tensor, U: torch.Tensor, block_size: int, Kcs=None):
-    """Query-subspace second-order descriptors [B, Hkv, nb, cov_sub_block_elems(d, s)] from the
-    basis U [Hkv, d, s] (float32)."""
+def cov_sub4_block_bytes(d: int, s_dim: int) -> int:
+    """Bytes per block of the FP4 query-subspace descriptor (CSA_COV_SUB4_BLOCK_BYTES)."""
+    return 2 * d + 4 * CSA_COBS_RANK + CSA_COBS_RANK * (-(-s_dim // 32) * 32) // 2
+
+
+def kv_cov_sub_build(K: torch.Tensor, U: torch.Tensor, block_size: int, Kcs=None, fp4: bool = False):
+    """Query-subspace second-order descriptors from the basis U [Hkv, d, s] (float32):
+    [B, Hkv, nb, cov_sub_block_elems(d, s)] in the cache dtype, or with fp4
+    [B, Hkv, nb, cov_sub4_block_bytes(d, s)] bytes."""
     dev = _dev(K, U, Kcs)
     B, Hkv, n, d = K.shape
     s_dim = U.shape[-1]
     shape = Shape(B, Hkv, Hkv, d, n, block_size, _dtype_code(K), 0.0)
     nb = shape.n_blocks
-    Kcs = torch.empty((B, Hkv, nb, cov_sub_block_elems(d, s_dim)), dtype=K.dtype, device=dev) if Kcs is None else Kcs
-    _check(lib().kv_cov_sub_build(ctypes.byref(shape), s_dim, _ptr(K), _ptr(U), _ptr(Kcs), _stream(dev)),
-           "kv_cov_sub_build")
+    if Kcs is None:
+        Kcs = (torch.empty((B, Hkv, nb, cov_sub4_block_bytes(d, s_dim)), dtype=torch.uint8, device=dev) if fp4 else
+               torch.empty((B, Hkv, nb, cov_sub_block_elems(d, s_dim)), dtype=K.dtype, device=dev))
+    name = "kv_cov_sub4_build" if fp4 else "kv_cov_sub_build"
+    _check(getattr(lib(), name)(ctypes.byref(shape), s_dim, _ptr(K), _ptr(U), _ptr(Kcs), _stream(dev)), name)
     return Kcs
 
 
 def block_score_cobs2_sub(q: torch.Tensor, Kcs: torch.Tensor, U: torch.Tensor, block_size: int, n_tokens: int,
-                          scale: float = 0.0, scores=None, ws=None):
-    """Second-order block scores [B, Hkv, nb] from query-subspace descriptors."""
+                          scale: float = 0.0, scores=None, ws=None, fp4: bool = False):
+    """Second-order block scores [B, Hkv, nb] from query-subspace descriptors (FP4 ones with fp4)."""
     dev = _dev(q, Kcs, U)
     B, Hq, d = q.shape
     Hkv, nb = Kcs.shape[1], Kcs.shape[2]
@@ -255,8 +265,9 @@ def block_score_cobs2_sub(q: torch.Tensor, Kcs: torch.Tensor, U: torch.Tensor, b
     shape = Shape(B, Hq, Hkv, d, n_tokens, block_size, _dtype_code(q), float(scale))
     scores = torch.empty((B, Hkv, nb), dtype=torch.float32, device=dev) if scores is None else scores
     ws, wsb = _workspace(shape, CSA_WS_BLOCK_SCORE_COBS2_SUB, 0, 0, ws, dev)
-    _check(lib().block_score_cobs2_sub(ctypes.byref(shape), s_dim, _ptr(q), _ptr(Kcs), _ptr(U), _ptr(scores),
-                                       _ptr(ws), wsb, _stream(dev)), "block_score_cobs2_sub")
+    name = "block_score_cobs2_sub4" if fp4 else "block_score_cobs2_sub"
+    _check(getattr(lib(), name)(ctypes.byref(shape), s_dim, _ptr(q), _ptr(Kcs), _ptr(U), _ptr(scores), _ptr(ws), wsb,
+                                _stream(dev)), name)
     return scores
 
 

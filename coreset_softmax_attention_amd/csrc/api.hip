@@ -428,44 +428,71 @@ int kv_cov4_build(const csa_shape* shape, const void* K, void* Kcov4, hipStream_
     return e == hipSuccess ? CSA_OK : hip_fail(e, "kv_cov4_build");
 }
 
-int kv_cov_sub_build(const csa_shape* shape, int32_t s_dim, const void* K, const float* U, void* Kcs,
-                     hipStream_t stream)
+namespace {
+
+int cov_sub_build_impl(const char* where, bool fp4, const csa_shape* shape, int32_t s_dim, const void* K,
+                       const float* U, void* Kcs, hipStream_t stream)
 {
     csa::Dims d;
     if (int rc = make_dims(shape, &d)) return rc;
-    if (!K || !U || !Kcs) return fail(CSA_ERR_INVALID_ARG, "kv_cov_sub_build: NULL pointer");
-    if (!aligned16(K) || !aligned16(Kcs) || !aligned4(U))
-        return fail(CSA_ERR_INVALID_ARG, "kv_cov_sub_build: misaligned pointer");
-    if (s_dim < 1 || s_dim > d.d)
-        return fail(CSA_ERR_INVALID_ARG, "kv_cov_sub_build: s=%d outside [1, d=%d]", s_dim, d.d);
+    if (!K || !U || !Kcs) return fail(CSA_ERR_INVALID_ARG, "%s: NULL pointer", where);
+    if (!aligned16(K) || !aligned16(Kcs) || !aligned4(U)) return fail(CSA_ERR_INVALID_ARG, "%s: misaligned pointer", where);
+    if (s_dim < 1 || s_dim > d.d) return fail(CSA_ERR_INVALID_ARG, "%s: s=%d outside [1, d=%d]", where, s_dim, d.d);
+    if (fp4 && d.dtype != csa::DT_BF16)
+        return fail(CSA_ERR_UNSUPPORTED, "%s: FP4 descriptors need a bfloat16 cache", where);
     if (!csa::cov_sub_ok(d, s_dim))
-        return fail(CSA_ERR_UNSUPPORTED, "kv_cov_sub_build: blocks of %d tokens (at most 64) or s=%d above 128", d.L,
-                    s_dim);
-    const hipError_t e = csa::launch_cov_sub(d, s_dim, K, U, Kcs, stream);
-    return e == hipSuccess ? CSA_OK : hip_fail(e, "kv_cov_sub_build");
+        return fail(CSA_ERR_UNSUPPORTED, "%s: blocks of %d tokens (at most 64) or s=%d above 128", where, d.L, s_dim);
+    const hipError_t e = fp4 ? csa::launch_cov_sub4(d, s_dim, K, U, Kcs, stream)
+                             : csa::launch_cov_sub(d, s_dim, K, U, Kcs, stream);
+    return e == hipSuccess ? CSA_OK : hip_fail(e, where);
+}
+
+int score_sub_impl(const char* where, bool fp4, const csa_shape* shape, int32_t s_dim, const void* q, const void* Kcs,
+                   const float* U, float* scores, void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    csa::Dims d;
+    if (int rc = make_dims(shape, &d)) return rc;
+    if (!q || !Kcs || !U || !scores) return fail(CSA_ERR_INVALID_ARG, "%s: NULL pointer", where);
+    if (!aligned16(q) || !aligned16(Kcs) || !aligned4(U) || !aligned4(scores))
+        return fail(CSA_ERR_INVALID_ARG, "%s: misaligned pointer", where);
+    if (s_dim < 1 || s_dim > d.d) return fail(CSA_ERR_INVALID_ARG, "%s: s=%d outside [1, d=%d]", where, s_dim, d.d);
+    if (d.dtype != csa::DT_BF16 || d.G > 8) return fail(CSA_ERR_UNSUPPORTED, "%s: needs bfloat16 and G <= 8", where);
+    {
+        const long long bb = fp4 ? (long long)CSA_COV_SUB4_BLOCK_BYTES(d.d, s_dim)
+                                 : 2ll * CSA_COV_SUB_BLOCK_ELEMS((long long)d.d, (long long)s_dim);
+        if ((long long)d.nb * bb >= (1ll << 32))
+            return fail(CSA_ERR_UNSUPPORTED, "%s: one KV head's descriptors must be below 4 GiB", where);
+    }
+    if (int rc = check_ws(block_score_ws(d), ws, ws_bytes)) return rc;
+    const hipError_t e = csa::launch_score_cobs2_sub(d, s_dim, q, Kcs, U, d.G == 1 ? scores : static_cast<float*>(ws),
+                                                     scores, stream, fp4);
+    return e == hipSuccess ? CSA_OK : hip_fail(e, where);
+}
+
+}  // namespace
+
+int kv_cov_sub_build(const csa_shape* shape, int32_t s_dim, const void* K, const float* U, void* Kcs,
+                     hipStream_t stream)
+{
+    return cov_sub_build_impl("kv_cov_sub_build", false, shape, s_dim, K, U, Kcs, stream);
+}
+
+int kv_cov_sub4_build(const csa_shape* shape, int32_t s_dim, const void* K, const float* U, void* Kcs4,
+                      hipStream_t stream)
+{
+    return cov_sub_build_impl("kv_cov_sub4_build", true, shape, s_dim, K, U, Kcs4, stream);
 }
 
 int block_score_cobs2_sub(const csa_shape* shape, int32_t s_dim, const void* q, const void* Kcs, const float* U,
                           float* scores, void* ws, size_t ws_bytes, hipStream_t stream)
 {
-    csa::Dims d;
-    if (int rc = make_dims(shape, &d)) return rc;
-    if (!q || !Kcs || !U || !scores) return fail(CSA_ERR_INVALID_ARG, "block_score_cobs2_sub: NULL pointer");
-    if (!aligned16(q) || !aligned16(Kcs) || !aligned4(U) || !aligned4(scores))
-        return fail(CSA_ERR_INVALID_ARG, "block_score_cobs2_sub: misaligned pointer");
-    if (s_dim < 1 || s_dim > d.d)
-        return fail(CSA_ERR_INVALID_ARG, "block_score_cobs2_sub: s=%d outside [1, d=%d]", s_dim, d.d);
-    if (d.dtype != csa::DT_BF16 || d.G > 8)
-        return fail(CSA_ERR_UNSUPPORTED, "block_score_cobs2_sub: needs bfloat16 and G <= 8");
-    {
-        const long long bb = 2ll * d.d + 2ll * CSA_COBS_RANK * ((s_dim + 7) / 8 * 8);
-        if ((long long)d.nb * bb >= (1ll << 32))
-            return fail(CSA_ERR_UNSUPPORTED, "block_score_cobs2_sub: one KV head's descriptors must be below 4 GiB");
-    }
-    if (int rc = check_ws(block_score_ws(d), ws, ws_bytes)) return rc;
-    const hipError_t e = csa::launch_score_cobs2_sub(d, s_dim, q, Kcs, U, d.G == 1 ? scores : static_cast<float*>(ws),
-                                                     scores, stream);
-    return e == hipSuccess ? CSA_OK : hip_fail(e, "block_score_cobs2_sub");
+    return score_sub_impl("block_score_cobs2_sub", false, shape, s_dim, q, Kcs, U, scores, ws, ws_bytes, stream);
+}
+
+int block_score_cobs2_sub4(const csa_shape* shape, int32_t s_dim, const void* q, const void* Kcs4, const float* U,
+                           float* scores, void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    return score_sub_impl("block_score_cobs2_sub4", true, shape, s_dim, q, Kcs4, U, scores, ws, ws_bytes, stream);
 }
 
 int kv_var_build(const csa_shape* shape, const void* K, void* Kvar, hipStream_t stream)

@@ -94,8 +94,11 @@ __global__ void __launch_bounds__(64) cov_kernel(const char* K, char* Kcov, int 
     const int t0 = blk * L, c = min(L, n - t0);
     const char* kp = K + ((size_t)pair * n + t0) * RB;
     static_assert(!FP4 || (DT == DT_BF16 && (D == 128 || D == 64)), "FP4 descriptors are for bfloat16 caches");
-    const int sps = SUB ? (s_dim + 7) / 8 * 8 : 0;  // stored subspace row length
-    const int BB = FP4 ? 2 * D + 4 * R + R * D / 2 : SUB ? RB + R * sps * EB : (1 + R) * RB;  // bytes per block
+    static_assert(!(SUB && FP4) || kSubMax == 128, "two subspace coordinates per lane");
+    const int sps = SUB ? (s_dim + 7) / 8 * 8 : 0;     // stored subspace row length
+    const int spf = SUB ? (s_dim + 31) / 32 * 32 : 0;  // FP4 subspace factor: coordinates with codes
+    const int BB = FP4 ? (SUB ? 2 * D + 4 * R + R * spf / 2 : 2 * D + 4 * R + R * D / 2)
+                       : SUB ? RB + R * sps * EB : (1 + R) * RB;  // bytes per block
     char* out = Kcov + ((size_t)pair * nb + blk) * BB;
 
     // ---- keys -> LDS (row per lane), mean of this lane's columns (fp64, token
@@ -445,7 +448,27 @@ __global__ void __launch_bounds__(64) cov_kernel(const char* K, char* Kcov, int 
         for (int e = 0; e < XC; ++e)
             if (XC * lane + e == at) sgn_src = xi[i][e];
         const float sgn = __shfl(sgn_src, at / XC) < 0.0f ? -1.0f : 1.0f;
-        if constexpr (SUB) {
+        if constexpr (SUB && FP4) {
+            // the bfloat16-rounded coordinates (zero past s), the scale from their largest
+            // magnitude, one byte of two codes per lane (coordinates 2 lane, 2 lane + 1)
+            float vb[XC];
+            float amax = 0.0f;
+#pragma unroll
+            for (int e = 0; e < XC; ++e) {
+                const int col = XC * lane + e;
+                vb[e] = col < s_dim ? __uint_as_float((uint32_t)bf16_from_f64((double)(xi[i][e] * sgn)) << 16) : 0.0f;
+                amax = fmaxf(amax, fabsf(vb[e]));
+            }
+            amax = __uint_as_float(wave_max_u32(__float_as_uint(amax)));
+            const float sc = amax / 6.0f;
+            if (lane == 0) *reinterpret_cast<float*>(out + 2 * D + 4 * i) = sc;
+            uint32_t code[XC];
+#pragma unroll
+            for (int e = 0; e < XC; ++e) code[e] = sc > 0.0f ? e2m1_code(vb[e] / sc) : 0u;
+            static_assert(XC == 2, "two coordinates, one byte of codes per lane");
+            if (2 * lane < spf)
+                reinterpret_cast<uint8_t*>(out + 2 * D + 4 * R + i * (spf / 2))[lane] = (uint8_t)(code[0] | (code[1] << 4));
+        } else if constexpr (SUB) {
 #pragma unroll
             for (int e = 0; e < XC; ++e) {
                 const int col = XC * lane + e;
@@ -537,6 +560,14 @@ hipError_t launch_cov_sub(const Dims& s, int s_dim, const void* K, const float* 
         if (s.d == 128) return launch_cov_dtd<DT_F32, 128, false, true>(s, K, Kcs, st, U, s_dim);
         if (s.d == 64) return launch_cov_dtd<DT_F32, 64, false, true>(s, K, Kcs, st, U, s_dim);
     }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_cov_sub4(const Dims& s, int s_dim, const void* K, const float* U, void* Kcs4, hipStream_t st)
+{
+    if (s.dtype != DT_BF16) return hipErrorInvalidValue;
+    if (s.d == 128) return launch_cov_dtd<DT_BF16, 128, true, true>(s, K, Kcs4, st, U, s_dim);
+    if (s.d == 64) return launch_cov_dtd<DT_BF16, 64, true, true>(s, K, Kcs4, st, U, s_dim);
     return hipErrorInvalidValue;
 }
 

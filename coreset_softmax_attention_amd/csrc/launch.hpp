@@ -42,6 +42,9 @@ hipError_t launch_cov(const Dims& s, const void* K, void* Kcov, hipStream_t st);
 // U^T Sigma_b U for the caller's basis U [Hkv, d, s] (fp32).
 bool cov_sub_ok(const Dims& s, int s_dim);  // cov_build_ok and 1 <= s <= min(d, 128)
 hipError_t launch_cov_sub(const Dims& s, int s_dim, const void* K, const float* U, void* Kcs, hipStream_t st);
+// The same with FP4 factors (bfloat16 caches): per block the mean key, kCobsRank fp32
+// scales and kCobsRank x spf/2 bytes of E2M1 codes, spf = s rounded up to 32.
+hipError_t launch_cov_sub4(const Dims& s, int s_dim, const void* K, const float* U, void* Kcs4, hipStream_t st);
 // The same with FP4 eigenvectors (bfloat16 caches): per block the mean key,
 // kCobsRank fp32 scales and kCobsRank x d/2 bytes of E2M1 codes.
 hipError_t launch_cov4(const Dims& s, const void* K, void* Kcov4, hipStream_t st);
@@ -54,8 +57,9 @@ hipError_t launch_score_cobs2(const Dims& s, const void* q, const void* Kcov, fl
 // Second-order scores from query-subspace descriptors (bfloat16, G <= 8): split
 // kernels (logits to `logits`, the scores themselves when G == 1) and the
 // group-score kernel.
+// fp4: the descriptors of launch_cov_sub4.
 hipError_t launch_score_cobs2_sub(const Dims& s, int s_dim, const void* q, const void* Kcs, const float* U,
-                                  float* logits, float* scores, hipStream_t st);
+                                  float* logits, float* scores, hipStream_t st, bool fp4 = false);
 // Mean and variance tokens Kvar [B, Hkv, nb, 2, d] of the proxy-error scores.
 hipError_t launch_var(const Dims& s, const void* K, void* Kvar, hipStream_t st);
 // Proxy-error block scores from Kvar (bfloat16, fused_summary_score_ok()); with

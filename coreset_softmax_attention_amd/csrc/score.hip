@@ -809,6 +809,97 @@ __device__ __forceinline__ void cobs2_sub_tile_logits(const FusedScoreParams& p,
     wave_lds_fence();  // tmp is reused by the next tile
 }
 
+// FP4 query-subspace descriptors, per block [mean: d bfloat16][4 fp32 scales][4 x
+// spf/2 bytes of E2M1 codes] (spf = s rounded up to 32): the tile of
+// cobs2_fp4_tile_logits with factor rows of spf coordinates (KSS = spf / 32 code
+// words per lane) against qt as two bfloat16 terms in the code words' order.
+template <int D, int KSS>
+__device__ __forceinline__ void cobs2_sub4_tile_logits(const FusedScoreParams& p, __amdgpu_buffer_rsrc_t kr,
+                                                       const bf16x8_t (&bq)[D / 32], const bf16x8_t (&bh)[KSS],
+                                                       const bf16x8_t (&bl)[KSS], int base, float* dst, int stride,
+                                                       int lane, float (*tmp)[32])
+{
+    constexpr int KS = D / 32, SPF = 32 * KSS;
+    constexpr uint32_t BB = 2 * D + 16 + 4 * SPF / 2;
+    static_assert(kCobsRank == 4, "one output lane holds one block's four factor products");
+    const int n16 = lane & 15, g16 = lane >> 4;
+    uint4 am[2][KS];
+    uint32_t ac[4][2][KSS];  // the lane's code words: coordinates 8 (KSS g16 + s) .. + 7
+    float4 scl[4][2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int tr = rb * 16 + n16;
+        const uint32_t om = (uint32_t)(base + tr) * BB + g16 * 16;  // past nb: zeros
+#pragma unroll
+        for (int s = 0; s < KS; ++s) am[rb][s] = buffer_ld16(kr, om + s * 64);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t oc = (uint32_t)(base + 8 * u + tr / 4) * BB + 2 * D + 16 + (tr % 4) * (SPF / 2) + g16 * 4 * KSS;
+#pragma unroll
+            for (int s = 0; s < KSS; ++s) ac[u][rb][s] = buffer_ld4(kr, oc + 4 * s);
+            const uint32_t os = (uint32_t)(base + 8 * u + 4 * rb + g16) * BB + 2 * D;
+            scl[u][rb] = __builtin_bit_cast(float4, buffer_ld16(kr, os));
+        }
+    }
+    f32x4_t cm[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+            cm[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, am[rb][s]), bq[s], cm[rb], 0, 0,
+                                                             0);
+    float sq[4][2];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        f32x4_t cx[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+        for (int s = 0; s < KSS; ++s)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                const uint32_t w = ac[u][rb][s];
+                typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+                const bf16x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0);
+                const bf16x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1);
+                const bf16x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2);
+                const bf16x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3);
+                const bf16x8_t a = __builtin_bit_cast(
+                    bf16x8_t, make_uint4(__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1),
+                                         __builtin_bit_cast(uint32_t, v2), __builtin_bit_cast(uint32_t, v3)));
+                cx[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh[s], cx[rb], 0, 0, 0);
+                cx[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl[s], cx[rb], 0, 0, 0);
+            }
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            const float e0 = cx[rb][0] * scl[u][rb].x, e1 = cx[rb][1] * scl[u][rb].y;
+            const float e2 = cx[rb][2] * scl[u][rb].z, e3 = cx[rb][3] * scl[u][rb].w;
+            sq[u][rb] = (e0 * e0 + e1 * e1) + (e2 * e2 + e3 * e3);
+        }
+    }
+    if (n16 < p.G) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int tr = rb * 16 + 4 * g16 + i;
+                tmp[n16][tr] = fmaf(cm[rb][i], p.scale, base + tr == p.nb - 1 ? p.ln_last : p.ln_L);
+            }
+    }
+    wave_lds_fence();
+    const float half_s2 = 0.5f * p.scale * p.scale;
+    if (n16 < p.G) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) tmp[n16][8 * u + 4 * rb + g16] += half_s2 * sq[u][rb];
+    }
+    wave_lds_fence();
+    for (int e = lane; e < p.G * 32; e += 64) {
+        const int h = e >> 5, b = e & 31;
+        if (base + b < p.nb) dst[h * stride + base + b] = tmp[h][b];
+    }
+    wave_lds_fence();  // tmp is reused by the next tile
+}
+
 // qt = U^T q for the G heads of KV head j, by the whole workgroup, into
 // qt_sm[h][0 .. 32 KSS) (zeros past s), fp32: a thread per (head, coordinate), the
 // d products in four interleaved partial sums with every load of a row of q and
@@ -837,9 +928,10 @@ __device__ __forceinline__ void subspace_query(const FusedScoreParams& p, const 
     }
 }
 
-// The B operands of qt (lane (n16, g16): head n16, elements 8 (4 s + g16) .. + 7)
-// as hi + lo bfloat16 terms.
-template <int KSS>
+// The B operands of qt as hi + lo bfloat16 terms: lane (n16, g16) holds head n16,
+// elements 8 c .. 8 c + 7 at k-step s with c = 4 s + g16, or (BY_LANE, the order
+// of the FP4 code words a lane loads) c = KSS g16 + s.
+template <int KSS, bool BY_LANE = false>
 __device__ __forceinline__ void subspace_operands(const float (*qt_sm)[128], int G, int lane, bf16x8_t (&bh)[KSS],
                                                   bf16x8_t (&bl)[KSS])
 {
@@ -847,10 +939,11 @@ __device__ __forceinline__ void subspace_operands(const float (*qt_sm)[128], int
 #pragma unroll
     for (int s = 0; s < KSS; ++s) {
         uint32_t hw[4] = {0, 0, 0, 0}, lw[4] = {0, 0, 0, 0};
+        const int c = BY_LANE ? KSS * g16 + s : 4 * s + g16;
         if (n16 < G) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float x = qt_sm[n16][8 * (4 * s + g16) + e];
+                const float x = qt_sm[n16][8 * c + e];
                 const uint32_t hb = __float_as_uint(x) >> 16;  // the leading 8 significant bits
                 const float r = x - __uint_as_float(hb << 16);
                 const uint32_t ru = __float_as_uint(r);
@@ -1031,7 +1124,7 @@ __global__ void __launch_bounds__(kSplitWaves * 64) score_cobs2_split_kernel(con
 
 // Query-subspace second-order logits, split form: workgroup (pair, chunk), one tile
 // per wave, the subspace query computed by the workgroup first.
-template <int D, int KSS>
+template <int D, int KSS, bool FP4>
 __global__ void __launch_bounds__(kSplitWaves * 64) score_cobs2_sub_split_kernel(const FusedScoreParams p)
 {
     constexpr int RB = D * 2, KS = D / 32;
@@ -1048,16 +1141,19 @@ __global__ void __launch_bounds__(kSplitWaves * 64) score_cobs2_sub_split_kernel
     if (base >= p.nb) return;  // whole wave; no barrier after this point
     bf16x8_t bq[KS], bh[KSS], bl[KSS];
     load_q_operand<D>(q0, p.G, lane, bq);
-    subspace_operands<KSS>(qt_sm, p.G, lane, bh, bl);
-    const uint32_t BB = (uint32_t)(RB + kCobsRank * p.sps * 2);
+    subspace_operands<KSS, FP4>(qt_sm, p.G, lane, bh, bl);
+    const uint32_t BB = FP4 ? (uint32_t)(2 * D + 16 + 64 * KSS) : (uint32_t)(RB + kCobsRank * p.sps * 2);
     const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(p.Kbar + (size_t)pair * p.nb * BB, (uint32_t)p.nb * BB);
-    cobs2_sub_tile_logits<D, KSS>(p, kr, bq, bh, bl, base, p.logits + (size_t)pair * p.G * p.nb, p.nb, lane,
-                                  tmp[wave]);
+    float* dst = p.logits + (size_t)pair * p.G * p.nb;
+    if constexpr (FP4)
+        cobs2_sub4_tile_logits<D, KSS>(p, kr, bq, bh, bl, base, dst, p.nb, lane, tmp[wave]);
+    else
+        cobs2_sub_tile_logits<D, KSS>(p, kr, bq, bh, bl, base, dst, p.nb, lane, tmp[wave]);
 }
 
 // Query-subspace second-order scores, one workgroup per KV head: the subspace
 // query once, the tiles by the eight waves, the group scores in LDS.
-template <int D, int KSS>
+template <int D, int KSS, bool FP4>
 __global__ void __launch_bounds__(kFusedWaves * 64) score_cobs2_sub_fused_kernel(const FusedScoreParams p)
 {
     constexpr int RB = D * 2, KS = D / 32, NW = kFusedWaves;
@@ -1073,11 +1169,15 @@ __global__ void __launch_bounds__(kFusedWaves * 64) score_cobs2_sub_fused_kernel
     __syncthreads();
     bf16x8_t bq[KS], bh[KSS], bl[KSS];
     load_q_operand<D>(q0, p.G, lane, bq);
-    subspace_operands<KSS>(qt_sm, p.G, lane, bh, bl);
-    const uint32_t BB = (uint32_t)(RB + kCobsRank * p.sps * 2);
+    subspace_operands<KSS, FP4>(qt_sm, p.G, lane, bh, bl);
+    const uint32_t BB = FP4 ? (uint32_t)(2 * D + 16 + 64 * KSS) : (uint32_t)(RB + kCobsRank * p.sps * 2);
     const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(p.Kbar + (size_t)pair * p.nb * BB, (uint32_t)p.nb * BB);
-    for (int base = wave * 32; base < p.nb; base += NW * 32)
-        cobs2_sub_tile_logits<D, KSS>(p, kr, bq, bh, bl, base, lsm, p.nb, lane, tmp[wave]);
+    for (int base = wave * 32; base < p.nb; base += NW * 32) {
+        if constexpr (FP4)
+            cobs2_sub4_tile_logits<D, KSS>(p, kr, bq, bh, bl, base, lsm, p.nb, lane, tmp[wave]);
+        else
+            cobs2_sub_tile_logits<D, KSS>(p, kr, bq, bh, bl, base, lsm, p.nb, lane, tmp[wave]);
+    }
     __syncthreads();
     group_scores_in_lds<NW>(lsm, lse_h, p.G, p.nb, p.scores + (size_t)pair * p.nb);
 }
@@ -1410,7 +1510,7 @@ hipError_t launch_score_cobs2_t(const Dims& s, const void* q, const void* Kcov, 
 }
 
 hipError_t launch_score_cobs2_sub(const Dims& s, int s_dim, const void* q, const void* Kcs, const float* U,
-                                  float* logits, float* scores, hipStream_t st)
+                                  float* logits, float* scores, hipStream_t st, bool fp4)
 {
     FusedScoreParams p = summary_params(s, q, Kcs, false);
     p.scores = scores;
@@ -1418,7 +1518,7 @@ hipError_t launch_score_cobs2_sub(const Dims& s, int s_dim, const void* q, const
     p.U = U;
     p.s_dim = s_dim;
     p.sps = (s_dim + 7) / 8 * 8;
-    const int kss = (p.sps + 31) / 32;
+    const int kss = (p.sps + 31) / 32;  // also the FP4 code words per lane: spf / 32
     const int tiles = (s.nb + 31) / 32;
     // one workgroup per KV head when there are enough of them and the logits fit LDS
     const bool fused = s.pairs() >= kFusedStepMinPairs && fused_summary_score_ok(s);
@@ -1427,10 +1527,14 @@ hipError_t launch_score_cobs2_sub(const Dims& s, int s_dim, const void* q, const
         block(fused ? kFusedWaves * 64 : kSplitWaves * 64);
     const size_t shm = fused ? (size_t)s.G * s.nb * sizeof(float) : 0;
 #define CSA_SUB_CASE(D, KSS)                                                                 \
-    if (fused)                                                                               \
-        score_cobs2_sub_fused_kernel<D, KSS><<<grid, block, shm, st>>>(p);                   \
+    if (fused && fp4)                                                                        \
+        score_cobs2_sub_fused_kernel<D, KSS, true><<<grid, block, shm, st>>>(p);             \
+    else if (fused)                                                                          \
+        score_cobs2_sub_fused_kernel<D, KSS, false><<<grid, block, shm, st>>>(p);            \
+    else if (fp4)                                                                            \
+        score_cobs2_sub_split_kernel<D, KSS, true><<<grid, block, 0, st>>>(p);               \
     else                                                                                     \
-        score_cobs2_sub_split_kernel<D, KSS><<<grid, block, 0, st>>>(p)
+        score_cobs2_sub_split_kernel<D, KSS, false><<<grid, block, 0, st>>>(p)
     if (s.d == 128) {
         switch (kss) {
         case 1: CSA_SUB_CASE(128, 1); break;

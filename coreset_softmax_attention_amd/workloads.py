@@ -50,7 +50,7 @@ class Workload:
     block_size: int
     dtype: str  # "f32" or "bf16"
     k: int  # blocks read exactly per KV head
-    score_mode: str  # "summary", "exact_mass", "box", "cobs2", "cobs2_fp4", "cobs2_sub", "proxy_error" or "cluster"
+    score_mode: str  # "summary", "exact_mass", "box", "cobs2", "cobs2_fp4", "cobs2_sub", "cobs2_sub_fp4", "proxy_error" or "cluster"
     proxies: bool  # one count-aware proxy per unread block
     keys: str  # "heavy_hitters" or "clusters"
     n_clusters: int = 64
@@ -106,6 +106,10 @@ WORKLOADS = {
                  "clusters", sub_dim=85,
                  description="the headline layer with second-order scores whose covariance is kept in an "
                              "85-dimensional query subspace (340 instead of 512 factor floats per block)"),
+        Workload("llama3_8b_layer_b32_cobs2_sub_fp4", 1002, 32, 32, 8, 128, 32768, 64, "bf16", 5, "cobs2_sub_fp4",
+                 True, "clusters", sub_dim=85,
+                 description="the headline layer with second-order scores from 85-dimensional query-subspace "
+                             "factors stored in FP4 (464 bytes per block)"),
         Workload("llama3_8b_layer_b32_err", 1002, 32, 32, 8, 128, 32768, 64, "bf16", 5, "proxy_error", True,
                  "clusters", description="the headline layer with exact reads spent on the largest estimated "
                                          "proxy errors (mean and variance tokens)"),

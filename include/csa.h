@@ -204,6 +204,27 @@ int block_score_cobs2_sub(const csa_shape* shape, int32_t s_dim, const void* q, 
                           float* scores, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * kv_cov_sub4_build, block_score_cobs2_sub4 -- the query-subspace descriptor with its
+ * factors in E2M1 FP4, one fp32 scale each, the mean key in bfloat16 ([COBS]
+ * section on quantising the stored factors, applied to the subspace factors).
+ * Per block CSA_COV_SUB4_BLOCK_BYTES(d, s) bytes: the mean key (d bfloat16, the
+ * bits of Kbar), the CSA_COBS_RANK scales s_i = max_t |xi_it| / 6 (binary32), then
+ * for each factor spf/2 bytes of codes, spf = s rounded up to 32: coordinate 2t
+ * in the low and 2t + 1 in the high nibble of byte t, zero codes past s.  xi_it is
+ * the bfloat16 value kv_cov_sub_build stores; its code is xi_it / s_i (binary32)
+ * rounded to the nearest of +-{0, 0.5, 1, 1.5, 2, 3, 4, 6}, ties to the even
+ * mantissa, zero as +0.  At d = 128, s = 85: 464 bytes per block (the factors
+ * 208 of them, against 704 in bfloat16).  bfloat16 caches only (else
+ * CSA_ERR_UNSUPPORTED); otherwise as kv_cov_sub_build and block_score_cobs2_sub
+ * (same workspace entry).
+ */
+#define CSA_COV_SUB4_BLOCK_BYTES(d, s) (2 * (d) + 4 * CSA_COBS_RANK + CSA_COBS_RANK * (((s) + 31) / 32 * 32) / 2)
+int kv_cov_sub4_build(const csa_shape* shape, int32_t s_dim, const void* K, const float* U, void* Kcs4,
+                      hipStream_t stream);
+int block_score_cobs2_sub4(const csa_shape* shape, int32_t s_dim, const void* q, const void* Kcs4, const float* U,
+                           float* scores, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * kv_var_build -- per block, the mean and the variance tokens that the
  * proxy-error ranking of [OA] reads (section "Three helpers that make the
  * proxy accurate": mean and variance tokens cached per group of tokens, the

@@ -400,3 +400,13 @@ def test_cov_sub_argument_checks(L):
     assert L.block_score_cobs2_sub(ctypes.byref(s), 85, FAKE, FAKE, FAKE, FAKE, None, 0,
                                    None) == csa.CSA_ERR_WORKSPACE
     assert csa.workspace_size(s, csa.CSA_WS_BLOCK_SCORE_COBS2_SUB) == csa.workspace_size(s, csa.CSA_WS_BLOCK_SCORE_COBS2)
+
+
+def test_cov_sub4_argument_checks(L):
+    s = shape()
+    f32 = shape(dtype=csa.CSA_F32)
+    assert L.kv_cov_sub4_build(ctypes.byref(f32), 85, FAKE, FAKE, FAKE, None) == csa.CSA_ERR_UNSUPPORTED
+    assert L.kv_cov_sub4_build(ctypes.byref(s), 0, FAKE, FAKE, FAKE, None) == csa.CSA_ERR_INVALID_ARG
+    assert L.block_score_cobs2_sub4(ctypes.byref(s), 85, FAKE, FAKE, FAKE, FAKE, None, 0,
+                                    None) == csa.CSA_ERR_WORKSPACE
+    assert csa.cov_sub4_block_bytes(128, 85) == 464 and csa.cov_sub4_block_bytes(64, 30) == 128 + 16 + 4 * 16

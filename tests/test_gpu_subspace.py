@@ -149,3 +149,51 @@ def test_sub_end_to_end_selection_agreement():
     assert len(differ) <= sel.shape[0] // 4
     print(f"query-subspace ranking end to end (descriptors built on each side): "
           f"{sel.shape[0] - len(differ)} of {sel.shape[0]} rows select the same blocks")
+
+
+# ---------------------------------------------------------------------------
+# FP4 factors
+# ---------------------------------------------------------------------------
+
+FP4_CASES = [c for c in CASES if c[8] == "bf16"]
+
+
+@pytest.mark.parametrize("name,B,Hkv,G,d,n,L,s_dim,dtype,tol", FP4_CASES, ids=[c[0] for c in FP4_CASES])
+def test_sub_fp4_descriptors_are_the_fp4_storage_of_the_bf16_ones(name, B, Hkv, G, d, n, L, s_dim, dtype, tol):
+    """kv_cov_sub4_build writes, bit for bit, what the oracle's FP4 packing makes of the bfloat16
+    subspace descriptors (which match the oracle's solve, above), and its scores match the
+    oracle's FP4 scores of those bytes."""
+    w = W.Workload(name, 4200 + n, B, G * Hkv, Hkv, d, n, L, dtype, 5, "cobs2_sub", True, "clusters", sub_dim=s_dim)
+    data = rand_inputs(4200 + n + s_dim, B, G * Hkv, Hkv, d, n, dtype)
+    U = basis(w, s_dim)
+    q, K, Ud = dev(data["q"]), dev(data["K"]), torch.from_numpy(U).cuda()
+    kc = csa.kv_cov_sub_build(K, Ud, L)
+    k4 = csa.kv_cov_sub_build(K, Ud, L, fp4=True)
+    sc = csa.block_score_cobs2_sub(q, k4, Ud, L, n, fp4=True)
+    sel = csa.topk_select(sc, w.k)
+    torch.cuda.synchronize()
+    shp = oshape(w)
+    kc, k4, sc, sel = host(kc), host(k4), host(sc), host(sel)
+    assert np.array_equal(k4, O.cov_sub4_pack(shp, kc, s_dim)), f"{name}: FP4 bytes differ"
+    ref = O.group_score(shp, O.cobs2_sub4_logits(shp, data["q"], k4, U))
+    ref_sel, margin = O.topk_select(ref, w.k)
+    err = assert_scores(sc, ref, f"{name} fp4")
+    assert_selection(sel, ref_sel, ref, margin, f"{name} fp4", err)
+
+
+def test_sub_fp4_full_size_all_pairs():
+    w = W.WORKLOADS["llama3_8b_layer_b32_cobs2_sub_fp4"]
+    data = W.generate(w)
+    U = basis(w, w.sub_dim)
+    q, K, Ud = dev(data["q"]), dev(data["K"]), torch.from_numpy(U).cuda()
+    k4 = csa.kv_cov_sub_build(K, Ud, w.block_size, fp4=True)
+    sc = csa.block_score_cobs2_sub(q, k4, Ud, w.block_size, w.n_tokens, fp4=True)
+    sel = csa.topk_select(sc, w.k)
+    torch.cuda.synchronize()
+    shp = oshape(w)
+    k4, sc, sel = host(k4), host(sc), host(sel)
+    assert k4.shape[-1] == 464
+    ref = O.group_score(shp, O.cobs2_sub4_logits(shp, data["q"], k4, U))
+    ref_sel, margin = O.topk_select(ref, w.k)
+    err = assert_scores(sc, ref, w.name)
+    assert_selection(sel, ref_sel, ref, margin, w.name, err)
