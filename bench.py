@@ -193,6 +193,19 @@ def step_kernels(w):
             "selective_decode_step (the block_score, topk_select and sparse_decode_attn kernels in turn)")
 
 
+def cluster_step_kernels(w):
+    """Which kernels cluster_decode_step runs for workload w: one kernel per KV head in bfloat16
+    with G <= 8, k <= 32, at least 32 KV heads and the logits, scores, selection bits and ranges
+    of C clusters within 64 KiB of LDS, else cluster_score, topk_select and cluster_decode_attn
+    in turn.  Used for the roofline label only."""
+    C, G, k = w.qgc, w.group, min(w.k, w.qgc)
+    ls = (C + 31) // 32 * 32
+    lds = (G + 1) * ls * 4 + ls // 32 * 4 + (ls + 1) * 4
+    one = w.dtype == "bf16" and G <= 8 and k <= 32 and C <= 2048 and w.batch * w.n_kv_heads >= 32 and lds <= 65536
+    return ("cluster_decode_step (decode_step_kernel over clusters)" if one else
+            "cluster_decode_step (the cluster_score, topk_select and cluster_decode_attn kernels in turn)")
+
+
 def algorithmic_bytes(w, m=0):
     """Bytes the sparse attention must move per launch (reads, writes), following the read
     accounting of the OpenAttention explainer (exact rows, proxy rows and query-side data):
@@ -556,9 +569,10 @@ def cluster_bytes(w, sizes, sel):
 
 
 def cluster_main(args, w):
-    """The decode step over query-guided clusters: cluster_score -> topk_select ->
-    cluster_decode_attn over a cache clustered once beforehand (kv_cluster_build, timed once
-    for information).  Same timing scheme as the block path."""
+    """The decode step over query-guided clusters (cluster_decode_step: cluster scores, top-k
+    and attention) over a cache clustered once beforehand (kv_cluster_build, timed once for
+    information), beside the three entry points in turn.  Same timing scheme as the block
+    path."""
     import torch
 
     sys.path.insert(0, os.path.join(HERE, "tests"))
@@ -675,6 +689,16 @@ def cluster_main(args, w):
                                  "cluster_decode_attn": attn_ms * 1e3},
         "kv_cluster_build_ms": build_ms,
         "roofline": {
+            "kernel": cluster_step_kernels(w),
+            "bound": "hbm",
+            "achieved": step_achieved,
+            "peak": 8000.0,
+            "unit": "GB/s",
+            "frac": step_achieved / 8000.0,
+            "traffic": traffic.get("decode_step") if isinstance(traffic, dict) else None,
+            "algorithmic_bytes": sum(by["step"]),
+        },
+        "roofline_cluster_decode_attn": {
             "kernel": "cluster_decode_attn (cluster_attn_kernel)",
             "bound": "hbm",
             "achieved": attn_achieved,
@@ -683,15 +707,6 @@ def cluster_main(args, w):
             "frac": attn_achieved / 8000.0,
             "traffic": traffic.get("cluster_decode_attn") if isinstance(traffic, dict) else None,
             "algorithmic_bytes": sum(by["attn"]),
-        },
-        "roofline_step": {
-            "kernel": "cluster_decode_step (score-and-select kernel, then cluster_attn_kernel)",
-            "bound": "hbm",
-            "achieved": step_achieved,
-            "peak": 8000.0,
-            "unit": "GB/s",
-            "frac": step_achieved / 8000.0,
-            "algorithmic_bytes": sum(by["step"]),
         },
         "cpu_baseline": cpu,
     }

@@ -798,13 +798,19 @@ int cluster_decode_step(const csa_shape* shape, int32_t n_clusters, const void* 
         return fail(CSA_ERR_INVALID_ARG, "cluster_decode_step: misaligned pointer");
     const ClusterStepWs w = cluster_step_ws(d, n_clusters, kk);
     if (int rc = check_ws(w.total, ws, ws_bytes)) return rc;
+    const int proxies = proxy_mode == CSA_PROXY_COMPLEMENT;
+    const csa::Dims dc = cluster_dims(d, n_clusters);
+    if (csa::cluster_step_ok(dc, kk)) {  // one kernel per KV head; the workspace stays unused
+        const csa::ClusterStepInputs in{q, Kg, Vg, Kc, proxies ? Vc : Vg, offsets, kk, proxies, scores, sel, out, lse};
+        const hipError_t e = csa::launch_cluster_step(dc, in, stream);
+        return e == hipSuccess ? CSA_OK : hip_fail(e, "cluster_decode_step");
+    }
     char* base = static_cast<char*>(ws);
     float* sc = scores ? scores : reinterpret_cast<float*>(base);
     int32_t* sl = sel ? sel : reinterpret_cast<int32_t*>(base + w.scores);
     float* lg = reinterpret_cast<float*>(base + w.scores + w.sel);
     hipError_t e = cluster_scores(d, n_clusters, q, Kc, offsets, sc, sl, kk, lg, stream);
     if (e != hipSuccess) return hip_fail(e, "cluster_decode_step (scores)");
-    const int proxies = proxy_mode == CSA_PROXY_COMPLEMENT;
     csa::ClusterAttn ca{q, Kg, Vg, proxies ? Kc : Kg, proxies ? Vc : Vg, offsets, sl, n_clusters, kk, proxies, out, lse};
     e = csa::launch_cluster_attention(d, ca, stream);
     return e == hipSuccess ? CSA_OK : hip_fail(e, "cluster_decode_step");

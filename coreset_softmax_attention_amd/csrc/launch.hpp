@@ -204,6 +204,27 @@ struct ClusterAttn {
 hipError_t launch_cluster_attention(const Dims& s, const ClusterAttn& ca, hipStream_t st);
 
 bool fused_step_ok(const Dims& s, int k, int m, int proxies);
+
+// The decode step over query-guided clusters in one kernel per KV head (Dims
+// with nb = the cluster count): cluster logits from the mean keys with count
+// terms from the ranges, group scores, the top-k, then attention over the
+// proxies (logits from LDS) and the selected clusters' rows of Kg / Vg.
+struct ClusterStepInputs {
+    const void* q;
+    const void* Kg;
+    const void* Vg;
+    const void* Kc;
+    const void* Vc;
+    const int32_t* offsets;
+    int k;
+    int proxies;
+    float* scores;  // may be null
+    int32_t* sel;   // may be null
+    float* out;
+    float* lse;     // may be null
+};
+bool cluster_step_ok(const Dims& s, int k);  // bf16, G <= 8, k <= 32, nb <= 2048, >= 32 KV heads
+hipError_t launch_cluster_step(const Dims& s, const ClusterStepInputs& in, hipStream_t st);
 hipError_t launch_decode_step(const Dims& s, const StepInputs& in, hipStream_t st);
 hipError_t launch_attention(const Dims& s, const AttnPlan& plan, const AttnInputs& in, void* ws,
                             hipStream_t st);

@@ -21,6 +21,15 @@
 //   3. attention tiles: proxy rows (values only, logits from LDS, selected
 //      blocks masked), weighted rows, exact rows of the selected blocks (keys
 //      and values, MFMA logits), in the engine of attn_engine.hpp.
+//
+// CLUSTER: the same step over query-guided clusters ("OpenAttention reads 1%
+// of the KV cache -- Count-aware tail proxy", section "Three helpers that make
+// the proxy accurate"): the rows of Kbar / Vbar are the clusters' mean keys and
+// values, the count term of a row is ln of its cluster's size (from the ranges
+// offsets[c] .. offsets[c + 1]; -inf for an empty cluster), and the exact rows
+// are the selected clusters' ranges of K / V (the cache in cluster order), whose
+// number is known only after the selection: each wave then forms the running
+// row counts of the selected clusters and plans its exact tiles.
 #include <type_traits>
 
 #include "attn_engine.hpp"
@@ -48,6 +57,7 @@ struct StepParams {
     int32_t* sel;   // optional
     float* out;
     float* lse;     // optional
+    const int32_t* offsets;  // CLUSTER: cluster ranges [B, Hkv, nb + 1]
     int Hq, Hkv, G, n, L, nb, k, m, proxies;
     int pend;    // proxy rows [0, pend): one per block (0 without proxies)
     int cr;      // cache rows: the m weighted tokens, then the k L exact rows
@@ -56,7 +66,7 @@ struct StepParams {
     float scale, ln_L, ln_last, scale_log2;
 };
 
-template <int D, int HG>
+template <int D, int HG, bool CLUSTER>
 __global__ void __launch_bounds__(kStepWaves * 64) decode_step_kernel(const StepParams p)
 {
     constexpr int NW = kStepWaves, TR = kTileRows;
@@ -68,12 +78,16 @@ __global__ void __launch_bounds__(kStepWaves * 64) decode_step_kernel(const Step
     __shared__ int32_t sel_sm[kStepMaxK];
     __shared__ uint32_t cand_sm[128];          // top-k candidates of the one-wave ranking
     __shared__ __attribute__((aligned(16))) uint32_t topk_sm[2 * NW + 128];  // wave maxima, counts, candidates
+    // CLUSTER: each wave's copy of the selected clusters' first rows and running row counts
+    __shared__ int32_t cl_start[CLUSTER ? NW : 1][kStepMaxK], cl_cum[CLUSTER ? NW : 1][kStepMaxK + 1];
 
     const int LS = p.lstride, G = p.G, nb = p.nb;
     float* lsm = dyn;                                              // [G][LS] block logits (natural log)
     float* ssm = dyn + G * LS;                                     // [LS] group scores
     uint32_t* bits = reinterpret_cast<uint32_t*>(ssm + LS);        // [LS / 32] selected blocks
+    int32_t* off_sm = reinterpret_cast<int32_t*>(bits + LS / 32);  // CLUSTER: [nb + 1] cluster ranges
     const int pair = blockIdx.x, b = pair / p.Hkv, j = pair - b * p.Hkv;
+    const int32_t* off = CLUSTER ? p.offsets + (size_t)pair * (nb + 1) : nullptr;
     const int h0 = j * G;
 
     E eng(sm, p.q + (size_t)(b * p.Hq + h0) * RB, G);
@@ -105,15 +119,15 @@ __global__ void __launch_bounds__(kStepWaves * 64) decode_step_kernel(const Step
     const int nK = (nb + TR - 1) / TR;                                  // mean-key tiles
     const int rotK = (int)((hsh >> 4) % (uint32_t)nK);
     const int nP = (p.pend + TR - 1) / TR;  // proxy tiles
-    const int nC = p.nc;                    // cache tiles of p.rt rows
-    const int nT = nP + nC;
+    int nC = p.nc;                          // cache tiles of p.rt rows (CLUSTER: set after the selection)
+    int nT = nP + nC;
     const int rotP = nP ? (int)((hsh >> 8) % (uint32_t)nP) : 0;
-    const int rotC = nC ? (int)((hsh >> 16) % (uint32_t)nC) : 0;
+    int rotC = nC ? (int)((hsh >> 16) % (uint32_t)nC) : 0;
     // first row of tile t: a proxy row, or a cache row (index into the cache rows)
     auto row0 = [&](int t) { return t < nP ? (t + rotP) % nP * TR : (t - nP + rotC) % nC * p.rt; };
     // this wave's tiles are t = wave + j NW: first Pw proxy tiles, then cache tiles
     const int Pw = wave < nP ? (nP - wave + NW - 1) / NW : 0;
-    const int Tw = wave < nT ? (nT - wave + NW - 1) / NW : 0;
+    int Tw = wave < nT ? (nT - wave + NW - 1) / NW : 0;
     auto tile_of = [&](int jj) { return wave + jj * NW; };
 
     // Proxy tiles hold only mean values (their logits are the block logits of
@@ -132,7 +146,20 @@ __global__ void __launch_bounds__(kStepWaves * 64) decode_step_kernel(const Step
     };
 
     // ---- phase 1: block logits of every head -> LDS ---------------------------
-    auto logits_to_lds = [&](int base, const uint4 (&kr)[E::NI]) {
+    // CLUSTER: the range starts of the rows this lane writes logits for (rows
+    // base + 16 rb + 4 g16 + i, and the next one), loaded with the tile's keys
+    auto load_ranges = [&](int base, int (&o)[2][5]) {
+        if constexpr (CLUSTER) {
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int i = 0; i < 5; ++i) {
+                    const int row = base + rb * 16 + 4 * g16 + i;
+                    o[rb][i] = row <= nb ? off[row] : 0;
+                }
+        }
+    };
+    auto logits_to_lds = [&](int base, const uint4 (&kr)[E::NI], const int (&o)[2][5]) {
         f32x4_t c[2];
         eng.qk_tile(kr, c);
         if (n16 < G) {
@@ -141,7 +168,14 @@ __global__ void __launch_bounds__(kStepWaves * 64) decode_step_kernel(const Step
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int row = base + rb * 16 + 4 * g16 + i;
-                    if (row < nb) lsm[n16 * LS + row] = fmaf(c[rb][i], p.scale, row == nb - 1 ? p.ln_last : p.ln_L);
+                    float lnc = row == nb - 1 ? p.ln_last : p.ln_L;
+                    if constexpr (CLUSTER) {
+                        const int cnt = o[rb][i + 1] - o[rb][i];
+                        lnc = cnt > 0 ? logf((float)cnt) : kNegInf;
+                        if (row < nb && n16 == 0) off_sm[row] = o[rb][i];
+                        if (row == nb - 1 && n16 == 0) off_sm[nb] = o[rb][i + 1];
+                    }
+                    if (row < nb) lsm[n16 * LS + row] = fmaf(c[rb][i], p.scale, lnc);
                 }
         }
     };
@@ -164,12 +198,15 @@ __global__ void __launch_bounds__(kStepWaves * 64) decode_step_kernel(const Step
     // have arrived, and stream in while the selection is made.
     for (int t = wave; t < nK; t += 2 * NW) {  // two tiles in flight
         uint4 k0[E::NI], k1[E::NI];
+        int o0[2][5], o1[2][5];
         const int b0 = (t + rotK) % nK * TR, b1 = (t + NW + rotK) % nK * TR;
         const bool two = t + NW < nK;
         load_keys(b0, k0, true);
         load_keys(b1, k1, two);
-        logits_to_lds(b0, k0);
-        if (two) logits_to_lds(b1, k1);
+        load_ranges(b0, o0);
+        if (two) load_ranges(b1, o1);
+        logits_to_lds(b0, k0, o0);
+        if (two) logits_to_lds(b1, k1, o1);
     }
     // The first proxy value tile goes out before the barrier, the second after
     // it, and from the waves that compute the head log-normalisers only once
@@ -244,6 +281,34 @@ __global__ void __launch_bounds__(kStepWaves * 64) decode_step_kernel(const Step
 
     if (lse_wave) issue_second_proxies();
 
+    if constexpr (CLUSTER) {
+        // the selected clusters' ranges: lane r < kk holds cluster sel_sm[r]; running
+        // row counts by an inclusive scan over the lanes (each wave its own copy)
+        int cnt = 0, st = 0;
+        if (lane < kk) {
+            const int c = sel_sm[lane];
+            st = off_sm[c];
+            cnt = off_sm[c + 1] - st;
+        }
+        int inc = cnt;
+#pragma unroll
+        for (int d2 = 1; d2 < 32; d2 <<= 1) {
+            const int o = __shfl_up(inc, d2);
+            if (lane >= d2) inc += o;
+        }
+        if (lane < kk) {
+            cl_start[wave][lane] = st;
+            cl_cum[wave][lane] = inc - cnt;
+        }
+        const int exact = __builtin_amdgcn_readfirstlane(__shfl(inc, kk > 0 ? kk - 1 : 0) * (kk > 0 ? 1 : 0));
+        if (lane == 0) cl_cum[wave][kk] = exact;
+        wave_lds_fence();
+        nC = (exact + TR - 1) / TR;
+        nT = nP + nC;
+        rotC = nC ? (int)((hsh >> 16) % (uint32_t)nC) : 0;
+        Tw = wave < nT ? (nT - wave + NW - 1) / NW : 0;
+    }
+
     // ---- phase 3: attention ------------------------------------------------------
     // Cache row c: weighted token c (c < m), else exact row c - m of the
     // selected blocks.  Rows that do not count point past the cache buffers
@@ -251,13 +316,20 @@ __global__ void __launch_bounds__(kStepWaves * 64) decode_step_kernel(const Step
     auto resolve_cache = [&](int c, bool valid, uint32_t& row, float& lw) {
         row = (uint32_t)p.n;
         lw = kNegInf;
-        if (!valid || c >= p.cr) return;
+        if (!valid || c >= (CLUSTER ? p.m + cl_cum[wave][kk] : p.cr)) return;
         if (c < p.m) {
             const int tok = p.tok_idx[(size_t)pair * p.m + c];
             if (tok >= 0 && tok < p.n) {
                 row = (uint32_t)tok;
                 lw = p.tok_logw[(size_t)pair * p.m + c] * kLog2e;
             }
+        } else if constexpr (CLUSTER) {  // exact row e: the last selected cluster starting at or before it
+            const int e = c - p.m;
+            int slot = 0;
+            for (int s2 = 1; s2 < kk; ++s2)
+                if (cl_cum[wave][s2] <= e) slot = s2;
+            row = (uint32_t)(cl_start[wave][slot] + (e - cl_cum[wave][slot]));
+            lw = 0.0f;
         } else {
             const int e = c - p.m;
             const int slot = e / p.L;
@@ -342,25 +414,26 @@ __global__ void __launch_bounds__(kStepWaves * 64) decode_step_kernel(const Step
     eng.finish(G, p.out + ((size_t)b * p.Hq + h0) * D, p.lse ? p.lse + (size_t)b * p.Hq + h0 : nullptr, nullptr);
 }
 
-size_t step_lds_bytes(const Dims& s)
+size_t step_lds_bytes(const Dims& s, bool cluster = false)
 {
     const int ls = (s.nb + kTileRows - 1) / kTileRows * kTileRows;
-    return (size_t)(s.G + 1) * ls * sizeof(float) + (size_t)(ls / 32) * sizeof(uint32_t);
+    return (size_t)(s.G + 1) * ls * sizeof(float) + (size_t)(ls / 32) * sizeof(uint32_t) +
+           (cluster ? (size_t)(ls + 1) * sizeof(int32_t) : 0);
 }
 
-template <int D>
+template <int D, bool CLUSTER>
 hipError_t launch_step_d(const StepParams& p, int pairs, size_t shm, hipStream_t st)
 {
     const dim3 grid((unsigned)pairs), block(kStepWaves * 64);
     switch (p.G) {
-    case 1: decode_step_kernel<D, 1><<<grid, block, shm, st>>>(p); break;
-    case 2: decode_step_kernel<D, 2><<<grid, block, shm, st>>>(p); break;
-    case 3: decode_step_kernel<D, 3><<<grid, block, shm, st>>>(p); break;
-    case 4: decode_step_kernel<D, 4><<<grid, block, shm, st>>>(p); break;
-    case 5: decode_step_kernel<D, 5><<<grid, block, shm, st>>>(p); break;
-    case 6: decode_step_kernel<D, 6><<<grid, block, shm, st>>>(p); break;
-    case 7: decode_step_kernel<D, 7><<<grid, block, shm, st>>>(p); break;
-    case 8: decode_step_kernel<D, 8><<<grid, block, shm, st>>>(p); break;
+    case 1: decode_step_kernel<D, 1, CLUSTER><<<grid, block, shm, st>>>(p); break;
+    case 2: decode_step_kernel<D, 2, CLUSTER><<<grid, block, shm, st>>>(p); break;
+    case 3: decode_step_kernel<D, 3, CLUSTER><<<grid, block, shm, st>>>(p); break;
+    case 4: decode_step_kernel<D, 4, CLUSTER><<<grid, block, shm, st>>>(p); break;
+    case 5: decode_step_kernel<D, 5, CLUSTER><<<grid, block, shm, st>>>(p); break;
+    case 6: decode_step_kernel<D, 6, CLUSTER><<<grid, block, shm, st>>>(p); break;
+    case 7: decode_step_kernel<D, 7, CLUSTER><<<grid, block, shm, st>>>(p); break;
+    case 8: decode_step_kernel<D, 8, CLUSTER><<<grid, block, shm, st>>>(p); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -413,8 +486,49 @@ hipError_t launch_decode_step(const Dims& s, const StepInputs& in, hipStream_t s
     p.ln_last = s.ln_last;
     p.scale_log2 = s.scale * kLog2e;
     const size_t shm = step_lds_bytes(s);
-    if (s.d == 128) return launch_step_d<128>(p, s.pairs(), shm, st);
-    if (s.d == 64) return launch_step_d<64>(p, s.pairs(), shm, st);
+    if (s.d == 128) return launch_step_d<128, false>(p, s.pairs(), shm, st);
+    if (s.d == 64) return launch_step_d<64, false>(p, s.pairs(), shm, st);
+    return hipErrorInvalidValue;
+}
+
+bool cluster_step_ok(const Dims& s, int k)
+{
+    return s.dtype == DT_BF16 && s.G <= 8 && k >= 0 && k <= kStepMaxK && s.nb <= kStepMaxBlocks &&
+           s.pairs() >= kFusedStepMinPairs && step_lds_bytes(s, true) <= (size_t)kStepMaxLdsBytes;
+}
+
+hipError_t launch_cluster_step(const Dims& s, const ClusterStepInputs& in, hipStream_t st)
+{
+    StepParams p{};
+    p.q = static_cast<const char*>(in.q);
+    p.K = static_cast<const char*>(in.Kg);
+    p.V = static_cast<const char*>(in.Vg);
+    p.Kbar = static_cast<const char*>(in.Kc);
+    p.Vbar = static_cast<const char*>(in.Vc);
+    p.offsets = in.offsets;
+    p.scores = in.scores;
+    p.sel = in.sel;
+    p.out = in.out;
+    p.lse = in.lse;
+    p.Hq = s.Hq;
+    p.Hkv = s.Hkv;
+    p.G = s.G;
+    p.n = s.n;
+    p.L = 1;
+    p.nb = s.nb;
+    p.k = in.k < s.nb ? in.k : s.nb;
+    p.m = 0;
+    p.proxies = in.proxies;
+    p.pend = in.proxies ? s.nb : 0;
+    p.cr = 0;
+    p.rt = kTileRows;
+    p.nc = 0;  // the exact tiles are planned after the selection
+    p.lstride = (s.nb + kTileRows - 1) / kTileRows * kTileRows;
+    p.scale = s.scale;
+    p.scale_log2 = s.scale * kLog2e;
+    const size_t shm = step_lds_bytes(s, true);
+    if (s.d == 128) return launch_step_d<128, true>(p, s.pairs(), shm, st);
+    if (s.d == 64) return launch_step_d<64, true>(p, s.pairs(), shm, st);
     return hipErrorInvalidValue;
 }
 

@@ -164,6 +164,63 @@ def test_cluster_decode_edges():
     check_decode(one, d1, o1, "C=1 proxy only", k=0, proxies_list=(True,))
 
 
+# 32 or more KV heads, k <= 32, C <= 2048: cluster_decode_step runs as one kernel per KV head
+STEP_CASES = [
+    case("step_g4_d128", 3101, 8, 4, 4, 128, 1024, 48, 8, k=5, iters=2),
+    case("step_g8_d64_k32", 3102, 4, 8, 8, 64, 768, 100, 4, k=32, iters=1),
+    case("step_g1_c600", 3103, 16, 2, 1, 128, 2048, 600, 8, k=3, iters=1),
+    case("step_g3_d128", 3104, 32, 1, 3, 128, 640, 37, 16, k=7, iters=2),
+]
+
+
+def fused_step_runs(w, data, o, k, proxies=True):
+    """The one-kernel route leaves the workspace alone (the kernels in turn keep their scores
+    and selection there when the caller passes no buffers for them)."""
+    q, Kc, offs = dev(data["q"]), dev(o["Kc"]), torch.from_numpy(o["offsets"]).cuda()
+    Kg = np.take_along_axis(data["K"], o["order"][..., None].astype(np.int64), axis=2)
+    Vg = np.take_along_axis(data["V"], o["order"][..., None].astype(np.int64), axis=2)
+    shape = csa.make_shape(q, dev(Kg), w.n_tokens, 0.0)
+    need = csa.workspace_size(shape, csa.CSA_WS_CLUSTER_DECODE_STEP, k, w.qgc)
+    ws = torch.full((need,), 0xAB, dtype=torch.uint8, device="cuda")
+    csa.cluster_decode_step(q, dev(Kg), dev(Vg), Kc, dev(o["Vc"]), offs, k, proxies=proxies, ws=ws)
+    torch.cuda.synchronize()
+    return bool((ws == 0xAB).all().item())
+
+
+@pytest.mark.parametrize("w", STEP_CASES, ids=[c.name for c in STEP_CASES])
+def test_cluster_step_one_kernel(w):
+    data, U, seeds = inputs(w)
+    o = O.cluster_build(oshape(w), data["K"], data["V"], U, seeds, w.qgc_iters)
+    assert fused_step_runs(w, data, o, w.k), f"{w.name}: not the one-kernel route"
+    check_decode(w, data, o, w.name)
+
+
+def test_cluster_step_one_kernel_edges():
+    """The one-kernel route with empty clusters (count term -inf: never a proxy, last in the
+    ranking), k = 0 (proxies only) and k = C (every cluster exact: dense attention)."""
+    w = case("step_edges", 3110, 8, 4, 2, 128, 1024, 24, 8, iters=0)
+    seeds = QI.seed_tokens(w.batch, w.n_kv_heads, w.n_tokens, w.qgc)
+    seeds[..., 7] = seeds[..., 3]
+    seeds[..., 23] = seeds[..., 0]
+    data, U, _ = inputs(w)
+    o = O.cluster_build(oshape(w), data["K"], data["V"], U, seeds, w.qgc_iters)
+    cnt = np.diff(o["offsets"], axis=-1)
+    assert (cnt[..., 7] == 0).all() and (cnt[..., 23] == 0).all()
+    for k in (0, 4, 22, 24):
+        assert fused_step_runs(w, data, o, k), f"k={k}: not the one-kernel route"
+    check_decode(w, data, o, "step empty clusters", k=4)
+    check_decode(w, data, o, "step k=22 (with empty ones)", k=22)
+    check_decode(w, data, o, "step k=0", k=0, proxies_list=(True,))
+    check_decode(w, data, o, "step k=C", k=w.qgc)
+    Kg = np.take_along_axis(data["K"], o["order"][..., None].astype(np.int64), axis=2)
+    Vg = np.take_along_axis(data["V"], o["order"][..., None].astype(np.int64), axis=2)
+    out, lse, _, _ = csa.cluster_decode_step(dev(data["q"]), dev(Kg), dev(Vg), dev(o["Kc"]), dev(o["Vc"]),
+                                             torch.from_numpy(o["offsets"]).cuda(), w.qgc, proxies=False)
+    torch.cuda.synchronize()
+    ref, ref_lse = O.dense_decode_attn(oshape(w), data["q"], data["K"], data["V"])
+    assert_out(host(out), host(lse), ref, ref_lse, "bf16", "one-kernel step, all clusters vs dense")
+
+
 def test_cluster_index_checks_reject_what_the_oracle_rejects():
     w = case("checks", 3030, 1, 2, 2, 64, 1024, 16, 8, iters=1)
     data, U, seeds = inputs(w)
