@@ -71,7 +71,7 @@ TRAFFIC_KERNELS = {"decode_step": "decode_step_kernel", "sparse_decode_attn": "a
                    "cluster_decode_attn": "cluster_attn_kernel", "cluster_logits": "cluster_logits_kernel",
                    "block_score_exact": "logits_exact_mfma_kernel", "block_score_exact_valu": "logits_exact_kernel",
                    "score_logits_split": "score_logits_split_kernel", "score_finish": "score_finish_kernel",
-                   "attn_merge": "attn_merge_kernel", "topk": "topk_"}
+                   "attn_merge": "attn_merge_kernel", "topk": "topk_", "score_group_chunk": "score_group_chunk_kernel"}
 
 
 # The device sources each counted kernel is compiled from (its traffic is stale once any of
@@ -81,7 +81,7 @@ KERNEL_SOURCES = {"decode_step": ["step.hip"], "sparse_decode_attn": ["attn.hip"
                   "cluster_decode_attn": ["cluster.hip"], "cluster_logits": ["cluster.hip"],
                   "block_score_exact": ["score.hip"], "block_score_exact_valu": ["score.hip"],
                   "score_logits_split": ["score.hip"], "score_finish": ["score.hip"], "attn_merge": ["attn.hip"],
-                  "topk": ["topk.hip"]}
+                  "topk": ["topk.hip"], "score_group_chunk": ["score.hip"]}
 
 
 def source_hash(csrc=None, files=None):
@@ -183,14 +183,18 @@ def copy_probe(nbytes):
 def step_kernels(w):
     """Which kernels selective_decode_step runs for workload w: the library takes one kernel per
     KV head for summary scores in bfloat16 with G <= 8, k <= 32 and nb <= 2048 when there are at
-    least 32 KV heads or each one's share is small ((proxies + k L + m) G <= 4096), else the
-    split kernels.  Used for the label of the roofline entry only."""
+    least 32 KV heads or each one's share is small ((proxies + k L + m) G <= 4096 with nb <= 512),
+    else the split kernels.  Used for the label of the roofline entry only."""
     nb, k = w.n_blocks, min(w.k, w.n_blocks)
     rows = (nb - k if w.proxies else 0) + k * w.block_size + w.coreset
     one = (w.score_mode == "summary" and w.dtype == "bf16" and w.group <= 8 and k <= 32 and nb <= 2048
-           and (w.batch * w.n_kv_heads >= 32 or rows * w.group <= 4096))
-    return ("selective_decode_step (decode_step_kernel)" if one else
-            "selective_decode_step (the block_score, topk_select and sparse_decode_attn kernels in turn)")
+           and (w.batch * w.n_kv_heads >= 32 or (rows * w.group <= 4096 and nb <= 512)))
+    if one:
+        return "selective_decode_step (decode_step_kernel)"
+    if w.score_mode == "summary" and w.dtype == "bf16" and w.group <= 8 and nb > 512 and 1 <= k <= 32:
+        return ("selective_decode_step (split logits, chunk group scores and candidates, attention ranking the "
+                "candidates, merge)")
+    return "selective_decode_step (the block_score, topk_select and sparse_decode_attn kernels in turn)"
 
 
 def cluster_step_kernels(w):

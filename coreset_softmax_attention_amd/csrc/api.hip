@@ -185,7 +185,7 @@ size_t error_score_ws(const csa::Dims& d) { return block_score_ws(d); }
 
 // Workspace layout of the unfused decode step: scores | sel | block_score ws | attention ws.
 struct StepWs {
-    size_t scores, sel, score_ws, attn_ws, total;
+    size_t scores, sel, score_ws, attn_ws, cand, total;
 };
 
 StepWs step_ws(const csa::Dims& d, int k, int m)
@@ -198,7 +198,11 @@ StepWs step_ws(const csa::Dims& d, int k, int m)
     const size_t a = csa::plan_attention(d, kk, m, 1, 0).ws_bytes;
     const size_t b = (kk > 0 || m > 0) ? csa::plan_attention(d, kk, m, 0, 0).ws_bytes : 0;
     w.attn_ws = align256(a > b ? a : b);
-    w.total = w.scores + w.sel + w.score_ws + w.attn_ws;
+    // chunk candidates (score and index) of the split route beyond kLseFromLogitsMaxBlocks blocks
+    w.cand = d.nb > csa::kLseFromLogitsMaxBlocks && kk > 0
+                 ? align256((size_t)d.pairs() * ((d.nb + csa::kCandChunk - 1) / csa::kCandChunk) * kk * 8)
+                 : 0;
+    w.total = w.scores + w.sel + w.score_ws + w.attn_ws + w.cand;
     return w;
 }
 
@@ -232,7 +236,8 @@ ClusterStepWs cluster_step_ws(const csa::Dims& d, int C, int k)
 // G C <= 16384: the matrix-core summary-score kernels with count terms from the
 // ranges -- one workgroup per KV head (selecting too when k <= 32 and C <= 2048)
 // with 32 or more KV heads, else logits split over tiles; otherwise a scalar
-// logit kernel and the group score.  logits: [B, Hq, C] scratch (G > 1).
+// logit kernel and the group score.  logits: block_score_ws() bytes of scratch
+// (G > 1): the logits [B, Hq, C], then the tiles' log-sum-exp states.
 hipError_t cluster_scores(const csa::Dims& d, int C, const void* q, const void* Kc, const int32_t* offsets,
                           float* scores, int32_t* sel, int k, float* logits, hipStream_t st)
 {
@@ -246,7 +251,8 @@ hipError_t cluster_scores(const csa::Dims& d, int C, const void* q, const void* 
                                                 selected ? k : 0);
         else
             e = csa::launch_score_summary_split(dc, q, Kc, d.G == 1 ? scores : logits, scores,
-                                                selected ? sel : nullptr, selected ? k : 0, st, false, offsets);
+                                                selected ? sel : nullptr, selected ? k : 0, st, false, offsets,
+                                                score_parts(dc, logits));
     } else {
         float* lg = d.G == 1 ? scores : logits;
         e = csa::launch_cluster_logits(d, C, q, Kc, offsets, lg, st);
@@ -356,10 +362,36 @@ int step_impl(const csa_shape* shape, int mode, const void* q, const void* K, co
     void* sws = base + w.scores + w.sel;
     void* aws = base + w.scores + w.sel + w.score_ws;
     if (mode == CSA_SCORE_SUMMARY && csa::fused_summary_score_ok(d) && d.pairs() < csa::kFusedStepMinPairs &&
+        csa::split_select_ok(d, kk) && d.nb > csa::kLseFromLogitsMaxBlocks && kk > 0 &&
+        csa::plan_attention(d, kk, m, proxies, 0).direct) {
+        // split logits with their tiles' log-sum-exp states, group scores and each
+        // chunk's top-k candidates, then the attention kernel ranks the candidates
+        float* lg = d.G == 1 ? sc : static_cast<float*>(sws);
+        float* parts = score_parts(d, sws);
+        float* cand_score = reinterpret_cast<float*>(base + w.scores + w.sel + w.score_ws + w.attn_ws);
+        const int nchunks = (d.nb + csa::kCandChunk - 1) / csa::kCandChunk;
+        int32_t* cand_idx = reinterpret_cast<int32_t*>(cand_score + (size_t)d.pairs() * nchunks * kk);
+        const int last = d.nb - (nchunks - 1) * csa::kCandChunk;
+        const int ncand = (nchunks - 1) * kk + (last < kk ? last : kk);
+        hipError_t e = csa::launch_score_summary_split(d, q, Kbar, lg, sc, nullptr, -1, stream, false, nullptr, parts);
+        if (e == hipSuccess) e = csa::launch_score_group_chunks(d, lg, parts, sc, kk, cand_score, cand_idx, stream);
+        if (e != hipSuccess) return hip_fail(e, "selective_decode_step (score)");
+        const csa::AttnPlan plan = csa::plan_attention(d, kk, m, proxies, 0);
+        if (int rc = check_ws(plan.ws_bytes, aws, w.attn_ws)) return rc;
+        csa::AttnInputs in{q, K, V, Kbar, Vbar, nullptr, kk, tok_idx, tok_logw, m, proxies, 0, out, lse};
+        in.cand_score = cand_score;
+        in.cand_idx = cand_idx;
+        in.ncand = ncand;
+        in.sel_out = sel;
+        in.plog = lg;
+        e = csa::launch_attention(d, plan, in, aws, stream);
+        return e == hipSuccess ? CSA_OK : hip_fail(e, "selective_decode_step");
+    }
+    if (mode == CSA_SCORE_SUMMARY && csa::fused_summary_score_ok(d) && d.pairs() < csa::kFusedStepMinPairs &&
         csa::split_select_ok(d, kk)) {
         // scores and selection from the split kernels (the top-k rides on the group-score kernel)
         const hipError_t e = csa::launch_score_summary_split(d, q, Kbar, d.G == 1 ? sc : static_cast<float*>(sws),
-                                                             sc, sl, kk, stream);
+                                                             sc, sl, kk, stream, false, nullptr, score_parts(d, sws));
         if (e != hipSuccess) return hip_fail(e, "selective_decode_step (score)");
     } else if (mode == CSA_SCORE_EXACT_MASS && d.G > 1 && csa::score_finish_ok(d) && csa::split_select_ok(d, kk)) {
         // exact masses, then group scores and selection in one kernel
@@ -553,7 +585,7 @@ int block_score(const csa_shape* shape, csa_score_mode mode_arg, const void* q, 
             d.pairs() >= csa::kFusedStepMinPairs
                 ? csa::launch_score_summary_fused(d, q, keys, scores, stream, box)
                 : csa::launch_score_summary_split(d, q, keys, d.G == 1 ? scores : static_cast<float*>(ws), scores,
-                                                  nullptr, 0, stream, box);
+                                                  nullptr, 0, stream, box, nullptr, score_parts(d, ws));
         return e == hipSuccess ? CSA_OK : hip_fail(e, "block_score");
     }
     float* dst = d.G == 1 ? scores : static_cast<float*>(ws);

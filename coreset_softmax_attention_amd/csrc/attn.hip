@@ -35,6 +35,7 @@
 #include "attn_engine.hpp"
 #include "device.hpp"
 #include "launch.hpp"
+#include "select.hpp"
 
 namespace csa {
 namespace {
@@ -65,6 +66,11 @@ struct AttnParams {
     float* out;
     float* lse;
     float* part;
+    const float* cand_score;   // direct mode: candidates to rank instead of sel (may be null)
+    const int32_t* cand_idx;
+    int32_t* sel_out;          // with candidates: the ranked selection (may be null)
+    const float* plog;         // direct mode: the proxy rows' logits [B, Hq, nb], natural log (may be null)
+    int ncand;
     int k, m, proxies, dense;
     int Hq, Hkv, G, n, L, nb;
     int rows, exact_rows, splits, rows_per_split;
@@ -358,6 +364,7 @@ __global__ void __launch_bounds__(NW * 64) attn_mfma_kernel(const AttnParams p)
     __shared__ int32_t tok_sm[kMaxTokLds];
     __shared__ float logw_sm[kMaxTokLds];
     __shared__ typename E::Smem sm;
+    static_assert(kMaxTokLds >= NW * 128 && kMaxSelLds >= NW * kDirectMaxK, "ranked mode's per-wave LDS");
 
     const int pair = blockIdx.x / p.splits, split = blockIdx.x - pair * p.splits;
     const int b = pair / p.Hkv, j = pair - b * p.Hkv;
@@ -383,10 +390,13 @@ __global__ void __launch_bounds__(NW * 64) attn_mfma_kernel(const AttnParams p)
     const int w_lo = max(r0, p.wbeg), w_hi = min(r1, p.wbeg + p.m);  // weighted rows of this range
     const bool sel_in_lds = !direct && !p.dense && p.k > 0 && p.k <= kMaxSelLds;
     const bool tok_in_lds = !direct && w_hi > w_lo && w_hi - w_lo <= kMaxTokLds;
-    RowSources src{p.sel + (size_t)pair * p.k, p.tok_idx + (size_t)pair * p.m, p.tok_logw + (size_t)pair * p.m, 0};
+    // Ranked mode (direct only): each wave ranks the KV head's candidates itself.
+    const bool ranked = direct && p.cand_score != nullptr;
+    RowSources src{ranked ? nullptr : p.sel + (size_t)pair * p.k, p.tok_idx + (size_t)pair * p.m,
+                   p.tok_logw + (size_t)pair * p.m, 0};
     // Direct mode (a tile or two per wave, k <= 32): no LDS copies and no barrier
     // before the tiles; the selection sits one block per lane in every wave.
-    const int selv = direct && !p.dense && lane < p.k ? src.sel[lane] : -1;
+    int selv = direct && !ranked && !p.dense && lane < p.k ? src.sel[lane] : -1;
 
     auto set_rows = [&](int base, int tb, bool masked) {
         if (lane < TR) {
@@ -413,20 +423,48 @@ __global__ void __launch_bounds__(NW * 64) attn_mfma_kernel(const AttnParams p)
         const uint32_t bytes = (uint32_t)__builtin_amdgcn_readfirstlane((int)(live ? (summ ? sbytes : cbytes) : 0u));
         return buffer_rsrc(summ ? (keys ? ks : vs) : (keys ? kc : vc), bytes);
     };
+    // Proxy tiles whose logits are given (the split scores' logits of the KV
+    // head's query heads): the lane's logits of head n16 ride in the tile's key
+    // registers instead of the mean keys.  A row past the blocks reads the next
+    // head's logits or nothing; it is masked.
+    // (five to eight heads: with fewer, the extra path would push the kernel's
+    // registers into scratch)
+    const bool given = HG > 4 && direct && p.plog != nullptr;
+    const float* const lg = given ? p.plog + ((size_t)b * p.Hq + h0) * p.nb : nullptr;
+    const int lg_head = min(eng.n16, nh - 1);
+    auto given_tile = [&](int base) { return given && base < p.wbeg; };  // uniform over the wave
+    auto load_given = [&](int base, typename E::Tile& t, bool live) {
+        const __amdgpu_buffer_rsrc_t r =
+            buffer_rsrc(lg, (uint32_t)__builtin_amdgcn_readfirstlane((int)(live ? nh * p.nb * 4 : 0)));
+        const uint32_t off = (uint32_t)(lg_head * p.nb + base + 4 * eng.g16) * 4;
+        t.kr[0] = buffer_ld16(r, off);
+        t.kr[1] = buffer_ld16(r, off + 64);
+    };
     auto issue = [&](int base, typename E::Tile& t, int tb, bool masked, bool live) {
         if (live) set_rows(base, tb, masked);
-        eng.issue(t, tb, rsrc(base, live, true), rsrc(base, live, false), true);
+        if (given_tile(base)) {
+            load_given(base, t, live);
+            eng.issue(t, tb, rsrc(base, live, true), rsrc(base, live, false), false);
+        } else {
+            eng.issue(t, tb, rsrc(base, live, true), rsrc(base, live, false), true);
+        }
     };
     auto issue_keys = [&](int base, typename E::Tile& t, int tb, bool live) {
         if (live) set_rows(base, tb, true);
-        eng.issue_keys(t, tb, rsrc(base, live, true));
+        if (given_tile(base))
+            load_given(base, t, live);
+        else
+            eng.issue_keys(t, tb, rsrc(base, live, true));
     };
     auto issue_values = [&](int base, typename E::Tile& t, int tb, bool live) {
         eng.issue_values(t.vr, tb, rsrc(base, live, false));
     };
-    auto compute = [&](const typename E::Tile& t, int tb) {
+    auto compute = [&](const typename E::Tile& t, int tb, int base) {
         float x[8];
-        eng.logits_mfma(t, tb, p.scale_log2, x);
+        if (given_tile(base))
+            eng.logits_given(tb, __builtin_bit_cast(float4, t.kr[0]), __builtin_bit_cast(float4, t.kr[1]), x);
+        else
+            eng.logits_mfma(t, tb, p.scale_log2, x);
         eng.softmax(x);
     };
 
@@ -452,7 +490,30 @@ __global__ void __launch_bounds__(NW * 64) attn_mfma_kernel(const AttnParams p)
     const int Tw = wave < nT ? (nT - wave + NW - 1) / NW : 0;
     auto base_of = [&](int jt) { return jt < Tw ? row0(wave + jt * NW) : 0; };
     const int first = Tw > 0 ? row0(wave) : r1;
-    issue(first, A, 0, false, Tw > 0);
+    // In ranked mode a first tile of exact rows waits for the ranking; any other
+    // goes out before it.
+    const bool first_waits = ranked && Tw > 0 && first >= p.ebeg;
+    if (!first_waits) issue(first, A, 0, false, Tw > 0);
+    if (ranked) {
+        // the candidates lie in ascending block order, so ranking by position
+        // breaks ties towards the lower block; the wave's scratch and its copy of
+        // the selection use the LDS of the non-direct modes
+        uint32_t* scratch = reinterpret_cast<uint32_t*>(tok_sm) + wave * 128;
+        int32_t* mine = sel_sm + wave * kDirectMaxK;
+        const size_t cbase = (size_t)pair * ((p.nb + kCandChunk - 1) / kCandChunk) * p.k;
+        const float* cs = p.cand_score + cbase;
+        const int32_t* ci = p.cand_idx + cbase;
+        auto emit = [&](int r, int i) { mine[r] = ci[i]; };
+        if (p.ncand <= 128)
+            wave_topk<2>([&](int i) { return cs[i]; }, p.ncand, p.k, lane, scratch, emit);
+        else
+            wave_topk<8>([&](int i) { return cs[i]; }, p.ncand, p.k, lane, scratch, emit);
+        wave_lds_fence();
+        selv = lane < p.k ? mine[lane] : -1;
+        src.sel = mine;
+        if (p.sel_out && split == 0 && wave == 0 && lane < p.k) p.sel_out[(size_t)pair * p.k + lane] = selv;
+        if (first_waits) issue(first, A, 0, false, true);
+    }
     if (direct && p.k > 0 && !p.dense) {  // mask the selected blocks among the first tile's proxy rows
         const int r = first + lane;
         if (lane < TR && r < pb_hi && in_selection(r, selv, p.k)) sm.tab_lw[0][wave][lane] = kNegInf;
@@ -493,11 +554,11 @@ __global__ void __launch_bounds__(NW * 64) attn_mfma_kernel(const AttnParams p)
         // values right after them
         issue_keys(base_of(1), B, 1, 1 < Tw);
         for (; jt + 1 < Tw; jt += 2) {
-            compute(A, 0);
+            compute(A, 0, base_of(jt));
             issue_values(base_of(jt + 1), B, 1, true);
             eng.accumulate(A);
             issue_keys(base_of(jt + 2), A, 0, jt + 2 < Tw);
-            compute(B, 1);
+            compute(B, 1, base_of(jt + 1));
             issue_values(base_of(jt + 2), A, 0, jt + 2 < Tw);
             eng.accumulate(B);
             issue_keys(base_of(jt + 3), B, 1, jt + 3 < Tw);
@@ -505,16 +566,16 @@ __global__ void __launch_bounds__(NW * 64) attn_mfma_kernel(const AttnParams p)
     } else {
         // tile jt+1's loads go out once tile jt's keys are consumed
         for (; jt + 1 < Tw; jt += 2) {
-            compute(A, 0);
+            compute(A, 0, base_of(jt));
             issue(base_of(jt + 1), B, 1, true, true);
             eng.accumulate(A);
-            compute(B, 1);
+            compute(B, 1, base_of(jt + 1));
             issue(base_of(jt + 2), A, 0, true, jt + 2 < Tw);
             eng.accumulate(B);
         }
     }
     if (jt < Tw) {  // odd tile count: the last tile is in A
-        compute(A, 0);
+        compute(A, 0, base_of(jt));
         eng.accumulate(A);
     }
     float* part = p.splits == 1 ? nullptr : p.part + (((size_t)pair * p.splits + split) * p.G + g0) * (D + 2);
@@ -688,6 +749,13 @@ hipError_t launch_attention(const Dims& s, const AttnPlan& pl, const AttnInputs&
     p.sel = in.sel;
     p.tok_idx = in.tok_idx;
     p.tok_logw = in.tok_logw;
+    if (pl.direct && in.cand_score) {
+        p.cand_score = in.cand_score;
+        p.cand_idx = in.cand_idx;
+        p.ncand = in.ncand;
+        p.sel_out = in.sel_out;
+    }
+    if (pl.direct && in.proxies && s.nb % 4 == 0 && pl.hg > 4 && s.G <= 8) p.plog = in.plog;
     p.out = in.out;
     p.lse = in.lse;
     p.part = static_cast<float*>(ws);

@@ -218,10 +218,16 @@ struct MfmaEngine {
     // table log-weight of -inf masks the row, any other value is ignored.
     __device__ __forceinline__ void logits_lds(int tb, const float* row_logits, float (&x)[8])
     {
+        logits_given(tb, *reinterpret_cast<const float4*>(row_logits + 4 * g16),
+                     *reinterpret_cast<const float4*>(row_logits + 16 + 4 * g16), x);
+    }
+
+    // The same from the lane's own natural-log logits: v0 rows 4 g16 + i, v1 rows
+    // 16 + 4 g16 + i of head n16.
+    __device__ __forceinline__ void logits_given(int tb, float4 v0, float4 v1, float (&x)[8])
+    {
         const float4 lw0 = *reinterpret_cast<const float4*>(&sm.tab_lw[tb][wave][4 * g16]);
         const float4 lw1 = *reinterpret_cast<const float4*>(&sm.tab_lw[tb][wave][16 + 4 * g16]);
-        const float4 v0 = *reinterpret_cast<const float4*>(row_logits + 4 * g16);
-        const float4 v1 = *reinterpret_cast<const float4*>(row_logits + 16 + 4 * g16);
         const float lws[8] = {lw0.x, lw0.y, lw0.z, lw0.w, lw1.x, lw1.y, lw1.z, lw1.w};
         const float vs[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll

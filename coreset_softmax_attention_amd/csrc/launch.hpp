@@ -92,13 +92,20 @@ bool score_finish_ok(const Dims& s);
 // the normalisers are computed from the logits.
 hipError_t launch_score_finish(const Dims& s, const float* logits, float* scores, int32_t* sel, int k, hipStream_t st,
                                const float* parts = nullptr);
-// parts (G > 1, may be null): the tiles' log-sum-exp states pass through it,
-// so the group-score kernel need not recompute the per-head normalisers.  Not
-// used by the summary and box routes: their normalisers must be the bits the
-// one-kernel step and the one-workgroup score kernel compute from the logits.
+// parts (G > 1, may be null; score_err_parts_bytes()): above
+// kLseFromLogitsMaxBlocks blocks the tiles' log-sum-exp states pass through it
+// and the group-score kernel takes the per-head normalisers from them; up to
+// that many it computes them from the logits, as the one-workgroup kernels do.
+// k < 0: the logits (and tile states) only, for launch_score_group_chunks.
 hipError_t launch_score_summary_split(const Dims& s, const void* q, const void* Kbar, float* logits, float* scores,
                                       int32_t* sel, int k, hipStream_t st, bool box = false,
                                       const int32_t* offsets = nullptr, float* parts = nullptr);
+// Group scores of the split logits (G > 1: to scores, with the normalisers from
+// the tile states `parts`; G == 1: logits are the scores) and each chunk's top-k
+// candidates, cand_score / cand_idx [B, Hkv, ceil(nb / kCandChunk), k]: nb above
+// kLseFromLogitsMaxBlocks, 1 <= k <= 32, G <= 8.
+hipError_t launch_score_group_chunks(const Dims& s, const float* logits, const float* parts, float* scores, int k,
+                                     float* cand_score, int32_t* cand_idx, hipStream_t st);
 
 // ---- top-k -----------------------------------------------------------------
 hipError_t launch_topk(int rows, int nb, int k, const float* scores, int32_t* sel, hipStream_t st);
@@ -131,6 +138,18 @@ struct AttnInputs {
     int dense;
     float* out;
     float* lse;
+    // Direct-mode plans only (AttnPlan::direct): with cand_score set, sel is not
+    // read; every wave ranks the ncand candidates [B, Hkv, ncand] of
+    // launch_score_group_chunks (ascending block order) for its k blocks, and
+    // the first workgroup of each KV head writes them to sel_out when given.
+    const float* cand_score = nullptr;
+    const int32_t* cand_idx = nullptr;
+    int ncand = 0;
+    int32_t* sel_out = nullptr;
+    // Direct-mode plans with proxies, nb a multiple of 4, 5 <= G <= 8 (else ignored):
+    // the logits [B, Hq, nb] (natural log, count terms included) of the summary
+    // scores, which the proxy rows then use instead of reading the mean keys.
+    const float* plog = nullptr;
 };
 
 AttnPlan plan_attention(const Dims& s, int k, int m, int proxies, int dense);
@@ -144,6 +163,23 @@ constexpr int kFusedStepMinPairs = 32;  // below this, the split kernels use the
 // 14.2 against 19.3 us at 8K tokens, 16.6 against 19.2 us at 32K; from 64K
 // tokens (5376) and at G = 7 over 32K tokens (7168) the split kernels win.
 constexpr long kFusedStepSmallWork = 4096;
+
+// Up to this many blocks per KV head the per-head normalisers of the summary,
+// box and cluster scores are computed from the logits in LDS, the same way in
+// the one-workgroup kernels and in the group-score kernel of the split route.
+// Beyond it the split route takes them from the tiles' log-sum-exp states,
+// which its logit kernel forms in parallel (at 2048 blocks the pass over the
+// logits cost the group-score kernel 2.5 us of its chain), and the one-kernel
+// step with fewer than kFusedStepMinPairs KV heads is not taken: every shape
+// keeps one arithmetic for its scores whichever entry point computes them.
+constexpr int kLseFromLogitsMaxBlocks = 512;
+
+// Beyond kLseFromLogitsMaxBlocks blocks the split route of the decode step
+// ranks in two levels: one wave per chunk of kCandChunk blocks forms their group
+// scores and its k best (launch_score_group_chunks), and the attention kernel
+// ranks those candidates itself (AttnInputs::cand_*), so that no workgroup runs
+// the whole KV head's group scores and top-k as one chain.
+constexpr int kCandChunk = 128;
 
 struct StepInputs {
     const void* q;

@@ -386,6 +386,7 @@ static_assert(kFusedMaxLogits / 2 / 32 <= 4 * 64, "the group-score kernel merges
 constexpr int kSplitWaves = 4;          // waves (one tile each) per workgroup of the split logits kernel
 constexpr int kFinishMaxK = 32;
 constexpr int kFinishMaxBlocks = 2048;  // top-k by one wave: up to 32 scores per lane
+static_assert(kCandChunk % 64 == 0 && kCandChunk <= 128, "candidate chunks of one or two blocks per lane");
 
 struct FusedScoreParams {
     const char* q;
@@ -508,10 +509,23 @@ __device__ __forceinline__ void group_scores_in_lds(float* lsm, float* lse_h, in
         }
         __syncthreads();
     }
-    for (int i = threadIdx.x; i < nb; i += NW * 64) {
-        const float v = G == 1 ? lsm[i] : group_score<8>(lsm + i, nb, lse_h, G);
-        lsm[i] = v;
-        if (scores) scores[i] = v;
+    // four blocks per thread at a time, their reads issued together
+    constexpr int U = 4;
+    for (int i0 = threadIdx.x; i0 < nb; i0 += U * NW * 64) {
+        float v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = min(i0 + u * NW * 64, nb - 1);
+            v[u] = G == 1 ? lsm[i] : group_score<8>(lsm + i, nb, lse_h, G);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + u * NW * 64;
+            if (i < nb) {
+                lsm[i] = v[u];
+                if (scores) scores[i] = v[u];
+            }
+        }
     }
 }
 
@@ -1338,6 +1352,121 @@ __global__ void __launch_bounds__(kSplitWaves * 64) score_err_split_kernel(const
     }
 }
 
+// Normaliser (natural log) of one head from its tiles' log-sum-exp states,
+// lane t holding those of tiles t, t + 64, ... (absent ones (-inf, 0)): the
+// maximum, then the rescaled sum, over the wave.  Every lane returns lane 0's
+// value.  States (-inf, 0) change neither the maximum nor the sum, so the
+// result does not depend on PT.
+template <int PT>
+__device__ __forceinline__ float lse_merge(const float (&mv)[PT], const float (&sv)[PT])
+{
+#pragma clang fp contract(off)  // the same bits wherever it is inlined
+    float M = kNegInf;
+#pragma unroll
+    for (int j = 0; j < PT; ++j) M = fmaxf(M, mv[j]);
+    M = group_max<64>(M);
+    float S = 0.0f;
+#pragma unroll
+    for (int j = 0; j < PT; ++j) S += sv[j] * rescale(mv[j], M);
+    S = group_sum<64>(S);
+    const float lse = (M + log2f(S)) * kLn2;
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, lse)));
+}
+
+// The normaliser of one head from its tiles' states st[16 t], st[16 t + 1]
+// (t < tiles <= 256).
+__device__ __forceinline__ float lse_from_parts(const float* st, int tiles, int lane)
+{
+    constexpr int PT = 4;
+    float mv[PT], sv[PT];
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+        const int t = lane + 64 * j;
+        mv[j] = t < tiles ? st[t * 16] : kNegInf;
+        sv[j] = t < tiles ? st[t * 16 + 1] : 0.0f;
+    }
+    return lse_merge<PT>(mv, sv);
+}
+
+// The normalisers of every head h < G of one KV head (st: its states
+// [tiles][8][2], tiles <= 64 PT), all loads first; lse[h] for h >= G is lse[0].
+template <int PT>
+__device__ __forceinline__ void lse_from_parts_heads(const float* st, int tiles, int G, int lane, float (&lse)[8])
+{
+    float mv[8][PT], sv[8][PT];
+#pragma unroll
+    for (int h = 0; h < 8; ++h)
+#pragma unroll
+        for (int j = 0; j < PT; ++j) {
+            const int t = lane + 64 * j;
+            const bool ok = t < tiles && h < G;
+            const float* s = st + (size_t)(ok ? t : 0) * 16 + (h < G ? h : 0) * 2;
+            const float a = s[0], c = s[1];
+            mv[h][j] = ok ? a : kNegInf;
+            sv[h][j] = ok ? c : 0.0f;
+        }
+#pragma unroll
+    for (int h = 0; h < 8; ++h) lse[h] = h < G ? lse_merge<PT>(mv[h], sv[h]) : 0.0f;
+#pragma unroll
+    for (int h = 1; h < 8; ++h)
+        if (h >= G) lse[h] = lse[0];
+}
+
+// Group scores and top-k candidates of the split route beyond
+// kLseFromLogitsMaxBlocks blocks: one wave per (KV head, chunk of kCandChunk
+// blocks).  The normalisers come from the tiles' log-sum-exp states and the group
+// scores from the logits, by the same functions as in score_finish_kernel (the
+// same bits); the scores go to p.scores (G > 1; with one head the logits are the
+// scores) and the chunk's min(k, chunk blocks) best, in ascending block order, to
+// cand_score / cand_idx [pair][chunk][k].  The k best blocks of the KV head are
+// the k best of the candidates, ties to the lower block as by position.
+__global__ void __launch_bounds__(64) score_group_chunk_kernel(const FusedScoreParams p, float* cand_score,
+                                                               int32_t* cand_idx)
+{
+    __shared__ uint32_t cand_sm[128];
+    __shared__ float sc_sm[kCandChunk];
+    const int lane = threadIdx.x, G = p.G, nb = p.nb, k = p.k;
+    const int nchunks = (nb + kCandChunk - 1) / kCandChunk;
+    const int pair = blockIdx.x / nchunks, chunk = blockIdx.x - pair * nchunks;
+    const int lo = chunk * kCandChunk, len = min(kCandChunk, nb - lo);
+    constexpr int PER = kCandChunk / 64;
+    float v[PER];
+    if (G > 1) {
+        // the chunk's logits and every head's tile states go out together
+        const int tiles = (nb + 31) / 32;
+        const float* lg = p.logits + (size_t)pair * G * nb;
+        float lv[PER][8];
+#pragma unroll
+        for (int u = 0; u < PER; ++u)
+#pragma unroll
+            for (int h = 0; h < 8; ++h) lv[u][h] = lg[(size_t)(h < G ? h : 0) * nb + lo + min(lane + 64 * u, len - 1)];
+        float lse_h[8];
+        const float* st = p.parts + (size_t)pair * tiles * 16;
+        if (tiles <= 64)
+            lse_from_parts_heads<1>(st, tiles, G, lane, lse_h);
+        else
+            lse_from_parts_heads<4>(st, tiles, G, lane, lse_h);
+#pragma unroll
+        for (int u = 0; u < PER; ++u) v[u] = group_score_v<8>(lv[u], lse_h, G);
+        if (p.scores) {
+#pragma unroll
+            for (int u = 0; u < PER; ++u)
+                if (lane + 64 * u < len) p.scores[(size_t)pair * nb + lo + lane + 64 * u] = v[u];
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < PER; ++u) v[u] = p.logits[(size_t)pair * nb + lo + min(lane + 64 * u, len - 1)];
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) sc_sm[lane + 64 * u] = v[u];
+    wave_lds_fence();
+    const size_t base = ((size_t)pair * nchunks + chunk) * k;
+    wave_topk<PER>([&](int i) { return sc_sm[i]; }, len, min(k, len), lane, cand_sm, [&](int r, int i) {
+        cand_score[base + r] = sc_sm[i];
+        cand_idx[base + r] = lo + i;
+    });
+}
+
 // Group scores (and the top-k when p.k > 0) of one KV head from split logits.
 __global__ void __launch_bounds__(kFusedWaves * 64) score_finish_kernel(const FusedScoreParams p)
 {
@@ -1367,24 +1496,8 @@ __global__ void __launch_bounds__(kFusedWaves * 64) score_finish_kernel(const Fu
     if (p.parts) {  // normalisers from the tiles' log-sum-exp states: wave h merges head h's
         const int wave = threadIdx.x >> 6, tiles = (nb + 31) / 32;
         if (wave < G) {
-            const float* st = p.parts + (size_t)pair * tiles * 16 + wave * 2;
-            constexpr int PT = 4;  // states per lane: up to 256 tiles (nb <= 8192)
-            float mv[PT], sv[PT];
-#pragma unroll
-            for (int j = 0; j < PT; ++j) {
-                const int t = lane + 64 * j;
-                mv[j] = t < tiles ? st[t * 16] : kNegInf;
-                sv[j] = t < tiles ? st[t * 16 + 1] : 0.0f;
-            }
-            float M = kNegInf;
-#pragma unroll
-            for (int j = 0; j < PT; ++j) M = fmaxf(M, mv[j]);
-            M = group_max<64>(M);
-            float S = 0.0f;
-#pragma unroll
-            for (int j = 0; j < PT; ++j) S += sv[j] * rescale(mv[j], M);
-            S = group_sum<64>(S);
-            if (lane == 0) lse_h[wave] = (M + log2f(S)) * kLn2;
+            const float lse = lse_from_parts(p.parts + (size_t)pair * tiles * 16 + wave * 2, tiles, lane);
+            if (lane == 0) lse_h[wave] = lse;
         }
     }
     __syncthreads();
@@ -1452,7 +1565,7 @@ hipError_t launch_score_summary_split(const Dims& s, const void* q, const void* 
 {
     FusedScoreParams p = summary_params(s, q, Kbar, box);
     p.offsets = offsets;
-    p.parts = s.G > 1 ? parts : nullptr;
+    p.parts = s.G > 1 && s.nb > kLseFromLogitsMaxBlocks ? parts : nullptr;
     p.logits = logits;
     p.scores = scores;
     p.sel = sel;
@@ -1472,8 +1585,25 @@ hipError_t launch_score_summary_split(const Dims& s, const void* q, const void* 
             score_logits_split_kernel<64, false><<<grid, block, 0, st>>>(p);
     }
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || (s.G == 1 && k == 0)) return e;  // G == 1: the logits are the scores
+    if (e != hipSuccess || (s.G == 1 && k == 0) || k < 0) return e;  // G == 1: the logits are the scores
     return launch_score_finish(s, logits, scores, sel, k, st, p.parts);
+}
+
+hipError_t launch_score_group_chunks(const Dims& s, const float* logits, const float* parts, float* scores, int k,
+                                     float* cand_score, int32_t* cand_idx, hipStream_t st)
+{
+    if (s.nb <= kLseFromLogitsMaxBlocks || k < 1 || k > kFinishMaxK || (s.G > 1 && !parts) || s.G > 8)
+        return hipErrorInvalidValue;
+    FusedScoreParams p{};
+    p.logits = const_cast<float*>(logits);
+    p.parts = const_cast<float*>(parts);
+    p.scores = s.G > 1 ? scores : nullptr;
+    p.G = s.G;
+    p.nb = s.nb;
+    p.k = k;
+    const int nchunks = (s.nb + kCandChunk - 1) / kCandChunk;
+    score_group_chunk_kernel<<<dim3((unsigned)(s.pairs() * nchunks)), dim3(64), 0, st>>>(p, cand_score, cand_idx);
+    return hipGetLastError();
 }
 
 template <bool FP4>

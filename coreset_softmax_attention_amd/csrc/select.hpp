@@ -32,6 +32,7 @@ __device__ __forceinline__ uint32_t order_key(float f)
 template <int CH = 8>
 __device__ __forceinline__ float head_lse(const float* row, int nb, int lane)
 {
+#pragma clang fp contract(off)  // the same bits wherever it is inlined
     auto load_chunk = [&](int base, float (&v)[CH]) {
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
@@ -69,13 +70,15 @@ __device__ __forceinline__ float head_lse(const float* row, int nb, int lane)
     return mx + logf(sum);
 }
 
-// Group score of one block from its G <= MAXG head logits l[h * stride].
+// Group score of one block from its head logits lv[h] and normalisers ls[h]
+// (entries h >= G are ignored).
 template <int MAXG>
-__device__ __forceinline__ float group_score(const float* l, int stride, const float* lse_h, int G)
+__device__ __forceinline__ float group_score_v(const float (&lv)[MAXG], const float (&ls)[MAXG], int G)
 {
+#pragma clang fp contract(off)  // the same bits wherever it is inlined
     float x[MAXG];
 #pragma unroll
-    for (int h = 0; h < MAXG; ++h) x[h] = l[(h < G ? h : 0) * stride] - lse_h[h < G ? h : 0];
+    for (int h = 0; h < MAXG; ++h) x[h] = lv[h] - ls[h];
     float mx = kNegInf;
 #pragma unroll
     for (int h = 0; h < MAXG; ++h)
@@ -86,6 +89,19 @@ __device__ __forceinline__ float group_score(const float* l, int stride, const f
     for (int h = 0; h < MAXG; ++h)
         if (h < G) sum += exp2_((x[h] - mx) * kLog2e);
     return mx + logf(sum);
+}
+
+// Group score of one block from its G <= MAXG head logits l[h * stride].
+template <int MAXG>
+__device__ __forceinline__ float group_score(const float* l, int stride, const float* lse_h, int G)
+{
+    float lv[MAXG], ls[MAXG];
+#pragma unroll
+    for (int h = 0; h < MAXG; ++h) {
+        lv[h] = l[(h < G ? h : 0) * stride];
+        ls[h] = lse_h[h < G ? h : 0];
+    }
+    return group_score_v<MAXG>(lv, ls, G);
 }
 
 // Key (hi, lo) = (order_key(score), ~index): larger key = larger score, then

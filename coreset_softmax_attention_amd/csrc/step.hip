@@ -444,7 +444,8 @@ hipError_t launch_step_d(const StepParams& p, int pairs, size_t shm, hipStream_t
 bool fused_step_ok(const Dims& s, int k, int m, int proxies)
 {
     const long rows = (proxies ? (long)(s.nb - k) : 0L) + (long)k * s.L + m;  // virtual rows per KV head
-    const bool enough = s.pairs() >= kFusedStepMinPairs || rows * s.G <= kFusedStepSmallWork;
+    const bool enough = s.pairs() >= kFusedStepMinPairs ||
+                        (rows * s.G <= kFusedStepSmallWork && s.nb <= kLseFromLogitsMaxBlocks);
     return s.dtype == DT_BF16 && s.G <= 8 && k <= kStepMaxK && s.nb <= kStepMaxBlocks && enough &&
            step_lds_bytes(s) <= (size_t)kStepMaxLdsBytes;
 }

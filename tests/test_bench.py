@@ -33,11 +33,13 @@ def test_weighted_tokens_add_their_rows():
 
 
 def test_route_label_follows_the_step_rule():
-    one, split = "decode_step_kernel", "in turn"
+    one, split, ranked = "decode_step_kernel", "in turn", "ranking the candidates"
     assert one in bench.step_kernels(W.WORKLOADS["llama3_8b_layer_b32"])   # 256 KV heads
     assert one in bench.step_kernels(W.WORKLOADS["llama3_8b_layer_b1"])    # 8, small share each
-    assert split in bench.step_kernels(W.WORKLOADS["weighted_coreset_128k"])  # (2040+512+2048) x 7
+    assert ranked in bench.step_kernels(W.WORKLOADS["weighted_coreset_128k"])  # 16 KV heads, 2048 blocks
     assert split in bench.step_kernels(W.WORKLOADS["exact_mass_gqa_b8"])   # exact-mass scores
+    # a small share over more than 512 blocks takes the split kernels
+    assert ranked in bench.step_kernels(W.WORKLOADS["llama3_8b_layer_b1"].with_(n_tokens=40000, proxies=False))
 
 
 def test_source_hash_ignores_comments_but_not_code(tmp_path):

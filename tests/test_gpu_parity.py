@@ -597,6 +597,31 @@ def test_split_step_selection_beyond_512_blocks(nb, k, keys):
     compare_pipelines(w, g, oracle_pipeline(w, data), f"split step nb={nb} k={k} {keys}")
 
 
+# The same route at other shapes: one query head per KV head over a ragged last chunk of
+# candidates, the weighted-coreset recipe scaled down (G = 7, weighted tokens, k = 32: a
+# chunk's whole candidate list), and no proxies (only exact rows: every first tile waits for
+# the ranking)
+RANKED_CASES = [
+    ("g1_nb700", W.Workload("ranked_g1", 0, 2, 3, 3, 128, 700 * 16, 16, "bf16", 4, "summary", True, "clusters"), {}),
+    ("coreset_g7_nb1500_k32",
+     small("weighted_coreset_128k", batch=2, n_tokens=1500 * 64, n_kv_heads=2).with_(coreset=300, k=32), {}),
+    ("g4_nb2048_no_proxies", W.Workload("ranked_g4", 0, 1, 8, 2, 128, 2048 * 32, 32, "bf16", 6, "summary", False,
+                                        "clusters"), {}),
+]
+
+
+@pytest.mark.parametrize("name,w,kw", RANKED_CASES, ids=[c[0] for c in RANKED_CASES])
+def test_split_step_ranked_shapes(name, w, kw):
+    """More than 512 blocks and fewer than 32 KV heads: chunk candidates ranked by the attention
+    kernel.  Scores and selection bit for bit against block_score + topk_select, and against the
+    oracle."""
+    data = W.generate(w)
+    g, m = gpu_step(w, data, **kw), gpu_pipeline(w, data, **kw)
+    assert np.array_equal(bits(g["score"]), bits(m["score"])), f"{name}: scores differ from block_score"
+    assert np.array_equal(g["sel"], m["sel"]), f"{name}: selection differs from topk_select"
+    compare_pipelines(w, g, oracle_pipeline(w, data, **kw), name)
+
+
 @pytest.mark.parametrize("dtype,G,d,n,L", [("bf16", 3, 128, 1000, 64), ("bf16", 8, 64, 2000, 32),
                                            ("bf16", 1, 128, 700, 16)])
 def test_decode_step_shapes(dtype, G, d, n, L):
