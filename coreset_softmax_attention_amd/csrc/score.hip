@@ -509,6 +509,15 @@ __device__ __forceinline__ void group_scores_in_lds(float* lsm, float* lse_h, in
         }
         __syncthreads();
     }
+    if (nb <= NW * 64) {  // a block per thread at most
+        const int i = threadIdx.x;
+        if (i < nb) {
+            const float v = G == 1 ? lsm[i] : group_score<8>(lsm + i, nb, lse_h, G);
+            lsm[i] = v;
+            if (scores) scores[i] = v;
+        }
+        return;
+    }
     // four blocks per thread at a time, their reads issued together
     constexpr int U = 4;
     for (int i0 = threadIdx.x; i0 < nb; i0 += U * NW * 64) {
