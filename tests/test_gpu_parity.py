@@ -607,6 +607,8 @@ RANKED_CASES = [
      small("weighted_coreset_128k", batch=2, n_tokens=1500 * 64, n_kv_heads=2).with_(coreset=300, k=32), {}),
     ("g4_nb2048_no_proxies", W.Workload("ranked_g4", 0, 1, 8, 2, 128, 2048 * 32, 32, "bf16", 6, "summary", False,
                                         "clusters"), {}),
+    # six heads over 1001 blocks (not a multiple of 4): the proxy rows read their mean keys
+    ("g6_nb1001", W.Workload("ranked_g6", 0, 1, 12, 2, 64, 1001 * 64, 64, "bf16", 5, "summary", True, "clusters"), {}),
 ]
 
 

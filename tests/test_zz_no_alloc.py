@@ -56,13 +56,30 @@ CASES = [
 ]
 
 
+# the split route beyond 512 blocks (chunk candidates ranked by the attention kernel), whose
+# candidates also live in the scratch
+RANKED_CASES = [
+    W.scaled_down(W.WORKLOADS["weighted_coreset_128k"], batch=1, n_tokens=65536, n_kv_heads=2).with_(coreset=300),
+    W.scaled_down(W.WORKLOADS["weighted_coreset_128k"], batch=1, n_tokens=40960, n_kv_heads=2).with_(coreset=200),
+]
+
+
 def test_noalloc_step_matches_the_step_with_a_workspace_twice_in_a_row():
-    shape0 = csa.Shape(CASES[0].batch, CASES[0].n_q_heads, CASES[0].n_kv_heads, CASES[0].head_dim,
-                       CASES[0].n_tokens, CASES[0].block_size, csa.CSA_BF16, 0.0)
-    need = csa.lib().csa_workspace_size(ctypes.byref(shape0), csa.CSA_WS_SELECTIVE_DECODE_STEP, CASES[0].k,
-                                        CASES[0].coreset)
+    check_twice(CASES)
+
+
+def test_noalloc_ranked_route_matches_the_step_with_a_workspace_twice_in_a_row():
+    assert all(w.n_blocks > 512 for w in RANKED_CASES)
+    check_twice(RANKED_CASES)
+
+
+def check_twice(cases):
+    shape0 = csa.Shape(cases[0].batch, cases[0].n_q_heads, cases[0].n_kv_heads, cases[0].head_dim,
+                       cases[0].n_tokens, cases[0].block_size, csa.CSA_BF16, 0.0)
+    need = csa.lib().csa_workspace_size(ctypes.byref(shape0), csa.CSA_WS_SELECTIVE_DECODE_STEP, cases[0].k,
+                                        cases[0].coreset)
     assert 0 < need <= csa.CSA_STEP_NOALLOC_SCRATCH_BYTES  # this route does use the scratch
-    for i, w in enumerate(CASES):
+    for i, w in enumerate(cases):
         print(f"noalloc call {i}: B={w.batch} Hkv={w.n_kv_heads} n={w.n_tokens} m={w.coreset}", flush=True)
         data = W.generate(w)
         q, K, V = (csa.to_device(data[x]) for x in ("q", "K", "V"))
