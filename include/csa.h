@@ -323,10 +323,15 @@ int dense_decode_attn(const csa_shape* shape, const void* q, const void* K, cons
  * ([COBS] Eq. (18)) is also the logit of the block's count-aware proxy ([OA]
  * "Skipping reviews...": mean logit + ln count), so where the shape allows
  * (bfloat16, G <= 8, k <= 32, nb <= 2048, and either B * Hkv >= 32 or a small
- * share per KV head: (proxies + k L + m) G <= 4096 virtual rows times query
- * heads) one kernel per KV head reads Kbar once, keeps the logits on chip for
- * both uses, selects the blocks and attends; otherwise the three entry points
- * run in turn.
+ * share per KV head over at most 512 blocks: (proxies + k L + m) G <= 4096
+ * virtual rows times query heads) one kernel per KV head reads Kbar once, keeps
+ * the logits on chip for both uses, selects the blocks and attends.  With fewer
+ * KV heads the kernels are split over workgroups: beyond 512 blocks (and
+ * 1 <= k <= 32) the logits, then each 128-block chunk's group scores and k best,
+ * then the attention, whose workgroups rank those candidates themselves (and
+ * with 5 to 8 heads take the proxies' logits from the split logits rather than
+ * reading Kbar again), then the merge of the splits; otherwise the three entry
+ * points run in turn.
  * keys = Kbar (SUMMARY) or K (EXACT_MASS) as for block_score (BOX, COBS2,
  * COBS2_FP4 and PROXY_ERROR scores are CSA_ERR_UNSUPPORTED here: they need Kbox, Kcov, Kcov4 or Kvar
  * besides Kbar; use the three entry points); Kbar may be NULL in EXACT_MASS
@@ -433,13 +438,16 @@ int cluster_decode_attn(const csa_shape* shape, int32_t n_clusters, const void* 
  * cluster_decode_step -- cluster_score, topk_select and cluster_decode_attn of one
  * decode step in one call (same scores and selection bit for bit, outputs to
  * rounding).  The cluster logit is the logit of the cluster's proxy, so the
- * ranking reads each mean key once; where the shape allows (G C <= 16384, and
- * k <= 32 with C <= 2048 for the selection) one kernel per KV head computes
- * the logits on the matrix cores, combines the heads and selects, and a second
- * kernel attends.  The conditions of cluster_decode_attn apply; k >= C reads
- * every cluster exactly.  scores [B, Hkv, C] and sel [B, Hkv, min(k, C)] are
- * written when not NULL.  Workspace: csa_workspace_size(shape,
- * CSA_WS_CLUSTER_DECODE_STEP, k, C) bytes.
+ * ranking and the proxies share it: with 32 or more KV heads, k <= 32 and the
+ * logits of C clusters within 64 KiB of on-chip memory, one kernel per KV head
+ * ranks, selects and attends (the mean keys read once); otherwise, where the
+ * shape allows (G C <= 16384, and k <= 32 with C <= 2048 for the selection),
+ * one kernel per KV head computes the logits on the matrix cores, combines the
+ * heads and selects, and a second kernel attends.  The conditions of
+ * cluster_decode_attn apply; k >= C reads every cluster exactly.  scores
+ * [B, Hkv, C] and sel [B, Hkv, min(k, C)] are written when not NULL.
+ * Workspace: csa_workspace_size(shape, CSA_WS_CLUSTER_DECODE_STEP, k, C) bytes
+ * (unused on the one-kernel route).
  */
 int cluster_decode_step(const csa_shape* shape, int32_t n_clusters, const void* q, const void* Kg, const void* Vg,
                         const void* Kc, const void* Vc, const int32_t* offsets, int32_t k, csa_proxy_mode proxy_mode,
