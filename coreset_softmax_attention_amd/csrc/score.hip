@@ -394,7 +394,7 @@ struct FusedScoreParams {
     float* scores;
     float* logits;  // split: [B, Hq, nb] (the scores when G == 1)
     int32_t* sel;   // finish: selection [B, Hkv, k] when k > 0
-    float* parts;   // proxy-error split: per (KV head, tile, head) log2 (max, sum) of the summary logits
+    float* parts;   // split kernels: per (KV head, tile, head) log2 (max, sum) of the logits (may be null)
     const int32_t* offsets;  // clusters: ranges [B, Hkv, nb + 1] give the count terms (else blocks)
     const float* U;          // query-subspace descriptors: the basis [Hkv, d, s]
     int s_dim, sps;          // its dimension s and the stored factor length (s rounded up to 8)
