@@ -180,7 +180,7 @@ __global__ void __launch_bounds__(kNW * 64) logits_exact_kernel(const LogitParam
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int t = min(base + u * RPW + gi, t1 - 1);
-                kr[u] = ld16(base_ptr + (size_t)t * RB);
+                kr[u] = ld16_nt(base_ptr + (size_t)t * RB);
             }
             float x[U][HG];
 #pragma unroll
@@ -233,7 +233,9 @@ __global__ void __launch_bounds__(kNW * 64) logits_exact_kernel(const LogitParam
 
 // Exact-mass logits on the matrix cores (bfloat16, G <= 16, L a multiple of
 // 32): ln m_{h,b} = log-sum-exp over the block's tokens of scale * q_h . K_i.
-// A wave streams the 32-token key tiles of its blocks (two tiles in flight),
+// A wave streams the 32-token key tiles of its blocks (two tiles in flight;
+// whole rows with the non-temporal hint, 102.8 against 110.0 us per GQA
+// exact-mass step with the keys loaded in the operand layout),
 // q K^T of a tile is two 16x16x32 MFMA chains (tokens x heads), and each
 // output lane keeps an online (max, sum) for its head over its rows; at the
 // end of a block the four row groups of a head are merged with lane swaps.
@@ -265,24 +267,36 @@ __global__ void __launch_bounds__(kExactWaves * 64) logits_exact_mfma_kernel(con
     // has no exit between its two halves, so that the compiler's wait before a
     // tile's MFMAs covers that tile's loads only, not the next tile's too.
     const __amdgpu_buffer_rsrc_t none = buffer_rsrc(p.keys, 0u);
-    auto load = [&](int t, uint4 (&ak)[2][KS]) {
+    // Key rows are loaded whole (LPV lanes per row, RPV rows per instruction)
+    // with the non-temporal hint, then moved into the MFMA operand layout
+    // through a per-wave LDS slot of 16 rows padded to LPV + 1 chunks.
+    constexpr int LPV = RB / 16, RPV = 64 / LPV, NI = 32 / RPV;
+    static_assert(RPV * NI / 2 == 16, "half a tile's loads cover one 16-row MFMA block");
+    __shared__ uint4 slot_all[kExactWaves][16 * (LPV + 1)];
+    uint4* const slot = slot_all[wave];
+    const int gv = lane / LPV, cv = lane % LPV;
+    auto load = [&](int t, uint4 (&ak)[NI]) {
         const __amdgpu_buffer_rsrc_t r = t < t1 ? kr : none;
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-            const uint32_t off = (uint32_t)(t * 32 + rb * 16 + n16) * RB + g16 * 16;  // past n: zeros
-#pragma unroll
-            for (int s = 0; s < KS; ++s) ak[rb][s] = buffer_ld16(r, off + s * 64);
-        }
+        for (int jj = 0; jj < NI; ++jj)
+            ak[jj] = buffer_ld16_nt(r, (uint32_t)(t * 32 + RPV * jj + gv) * RB + cv * 16);  // past n: zeros
     };
     float m_run = kNegInf, l_run = 0.0f;  // this lane's head n16, its rows of the current block
-    auto consume = [&](int t, const uint4 (&ak)[2][KS]) {
+    auto consume = [&](int t, const uint4 (&ak)[NI]) {
         f32x4_t c[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
+        for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-                c[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ak[rb][s]), bq[s], c[rb], 0,
-                                                                0, 0);
+            for (int jj = 0; jj < NI / 2; ++jj) slot[(RPV * jj + gv) * (LPV + 1) + cv] = ak[rb * (NI / 2) + jj];
+            wave_lds_fence();
+            uint4 a[KS];
+#pragma unroll
+            for (int s = 0; s < KS; ++s) a[s] = slot[n16 * (LPV + 1) + 4 * s + g16];
+            wave_lds_fence();  // the slot is rewritten next
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                c[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[s]), bq[s], c[rb], 0, 0, 0);
+        }
         float x[8];
         float mx = m_run;
 #pragma unroll
@@ -317,7 +331,7 @@ __global__ void __launch_bounds__(kExactWaves * 64) logits_exact_mfma_kernel(con
             l_run = 0.0f;
         }
     };
-    uint4 A[2][KS], B[2][KS];
+    uint4 A[NI], B[NI];
     load(t0, A);
     load(t0 + 1, B);
     int t = t0;
@@ -1797,7 +1811,10 @@ hipError_t launch_logits_dtd(const LogitParams& p, int hg, int pairs, int hchunk
 // whole 32-token tiles per block.
 bool exact_mfma_ok(const Dims& s)
 {
-    return s.dtype == DT_BF16 && s.G >= 2 && s.G <= 16 && s.L % 32 == 0;
+    // one head per KV head too: the matrix cores waste 15 of 16 columns, but the
+    // kernel's whole-row loads stream faster than the VALU kernel's (350.7
+    // against 389.8 us per MHA exact-mass step at 32 KV heads x 8 sequences)
+    return s.dtype == DT_BF16 && s.G >= 1 && s.G <= 16 && s.L % 32 == 0;
 }
 
 template <bool EXACT>
