@@ -442,24 +442,45 @@ __device__ __forceinline__ void merge_lse_groups(float& m2, float& s2)
     }
 }
 
-// The mean keys of the tile of blocks [base, base + 32) in the A-operand layout
-// (lane (n16, g16): row n16 of each 16-row half, 16-byte chunks 4 s + g16).
+// The mean keys of the tile of blocks [base, base + 32), loaded whole (LPV
+// lanes per row, RPV rows per load) with the non-temporal hint: kr[j] holds
+// chunk lane % LPV of row RPV j + lane / LPV.  Rows past nb read as zeros.
 template <int D>
 struct KeyTile {
-    uint4 ak[2][D / 32];
+    static constexpr int RB = D * 2, LPV = RB / 16, RPV = 64 / LPV, NI = 32 / RPV;
+    static_assert(RPV * NI / 2 == 16, "half a tile's loads cover one 16-row MFMA block");
+    uint4 kr[NI];
 };
+
+// A wave's LDS slot for the layout change of a key tile: 16 rows padded to
+// LPV + 1 chunks (the lanes of a whole-row write and of an operand read hit
+// different banks).
+template <int D>
+constexpr int kKeySlot = 16 * (D * 2 / 16 + 1);
 
 template <int D>
 __device__ __forceinline__ void load_key_tile(__amdgpu_buffer_rsrc_t kr, int base, int lane, KeyTile<D>& t)
 {
-    constexpr int RB = D * 2, KS = D / 32;
-    const int n16 = lane & 15, g16 = lane >> 4;
+    using T = KeyTile<D>;
+    const int gv = lane / T::LPV, cv = lane % T::LPV;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        const uint32_t off = (uint32_t)(base + rb * 16 + n16) * RB + g16 * 16;  // past nb: zeros
+    for (int jj = 0; jj < T::NI; ++jj)
+        t.kr[jj] = buffer_ld16_nt(kr, (uint32_t)(base + T::RPV * jj + gv) * T::RB + cv * 16);
+}
+
+// The tile's 16-row block rb in the A-operand layout (lane (n16, g16): row n16,
+// 16-byte chunks 4 s + g16), through the wave's slot.
+template <int D>
+__device__ __forceinline__ void key_tile_operand(const KeyTile<D>& t, int rb, int lane, uint4* slot, uint4 (&a)[D / 32])
+{
+    using T = KeyTile<D>;
+    const int gv = lane / T::LPV, cv = lane % T::LPV, n16 = lane & 15, g16 = lane >> 4;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) t.ak[rb][s] = buffer_ld16(kr, off + s * 64);
-    }
+    for (int jj = 0; jj < T::NI / 2; ++jj) slot[(T::RPV * jj + gv) * (T::LPV + 1) + cv] = t.kr[rb * (T::NI / 2) + jj];
+    wave_lds_fence();
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) a[s] = slot[n16 * (T::LPV + 1) + 4 * s + g16];
+    wave_lds_fence();  // the slot is rewritten next
 }
 
 // Logits of a loaded tile for every head of the group: dst[h * stride + b].
@@ -468,17 +489,20 @@ __device__ __forceinline__ void load_key_tile(__amdgpu_buffer_rsrc_t kr, int bas
 template <int D>
 __device__ __forceinline__ void key_tile_logits(const FusedScoreParams& p, const KeyTile<D>& t,
                                                 const bf16x8_t (&bq)[D / 32], int base, float* dst, int stride,
-                                                int lane, const int32_t* off, bool track, float& m2, float& s2)
+                                                int lane, const int32_t* off, bool track, float& m2, float& s2,
+                                                uint4* slot)
 {
     constexpr int KS = D / 32;
     const int n16 = lane & 15, g16 = lane >> 4;
     f32x4_t c[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
+    for (int rb = 0; rb < 2; ++rb) {
+        uint4 a[KS];
+        key_tile_operand<D>(t, rb, lane, slot, a);
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-            c[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, t.ak[rb][s]), bq[s], c[rb], 0, 0,
-                                                            0);
+        for (int s = 0; s < KS; ++s)
+            c[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[s]), bq[s], c[rb], 0, 0, 0);
+    }
     if (n16 < p.G) {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
@@ -502,10 +526,10 @@ __device__ __forceinline__ void key_tile_logits(const FusedScoreParams& p, const
 template <int D>
 __device__ __forceinline__ void key_tile_logits(const FusedScoreParams& p, const KeyTile<D>& t,
                                                 const bf16x8_t (&bq)[D / 32], int base, float* dst, int stride,
-                                                int lane, const int32_t* off)
+                                                int lane, const int32_t* off, uint4* slot)
 {
     float m2 = kNegInf, s2 = 0.0f;
-    key_tile_logits<D>(p, t, bq, base, dst, stride, lane, off, false, m2, s2);
+    key_tile_logits<D>(p, t, bq, base, dst, stride, lane, off, false, m2, s2, slot);
 }
 
 // Group scores of one KV head from its logits lsm[h * nb + b] in LDS, by the
@@ -636,6 +660,7 @@ __global__ void __launch_bounds__(kFusedWaves * 64) score_summary_fused_kernel(c
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     __shared__ SelectSmem<NW> ss;
+    __shared__ uint4 kslot[NW][kKeySlot<D>];
     const int pair = blockIdx.x, b = pair / p.Hkv, j = pair - b * p.Hkv;
     const int32_t* off = p.offsets ? p.offsets + (size_t)pair * (p.nb + 1) : nullptr;
 
@@ -646,9 +671,9 @@ __global__ void __launch_bounds__(kFusedWaves * 64) score_summary_fused_kernel(c
         KeyTile<D> t0, t1;
         const int base1 = base + NW * 32;
         load_key_tile<D>(kr, base, lane, t0);
-        if (base1 < p.nb) load_key_tile<D>(kr, base1, lane, t1);
-        key_tile_logits<D>(p, t0, bq, base, lsm, p.nb, lane, off);
-        if (base1 < p.nb) key_tile_logits<D>(p, t1, bq, base1, lsm, p.nb, lane, off);
+        load_key_tile<D>(kr, base1, lane, t1);  // past nb: zeros, no memory traffic
+        key_tile_logits<D>(p, t0, bq, base, lsm, p.nb, lane, off, kslot[wave]);
+        if (base1 < p.nb) key_tile_logits<D>(p, t1, bq, base1, lsm, p.nb, lane, off, kslot[wave]);
     }
     __syncthreads();
     group_scores_in_lds<NW>(lsm, lse_h, p.G, p.nb, p.scores ? p.scores + (size_t)pair * p.nb : nullptr);
@@ -669,6 +694,7 @@ __global__ void __launch_bounds__(kSplitWaves * 64) score_logits_split_kernel(co
     const int b = pair / p.Hkv, j = pair - b * p.Hkv;
     const int base = (chunk * kSplitWaves + wave) * 32;
     if (base >= p.nb) return;  // whole wave; no barrier in this kernel
+    __shared__ uint4 kslot[kSplitWaves][kKeySlot<D>];
     bf16x8_t bq[KS];
     load_score_q<D, BOX>(p.q + ((size_t)b * p.Hq + (size_t)j * p.G) * QB, p.G, lane, bq);
     const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(p.Kbar + (size_t)pair * p.nb * RB, (uint32_t)p.nb * RB);
@@ -676,7 +702,8 @@ __global__ void __launch_bounds__(kSplitWaves * 64) score_logits_split_kernel(co
     load_key_tile<D>(kr, base, lane, t);
     float m2 = kNegInf, s2 = 0.0f;
     key_tile_logits<D>(p, t, bq, base, p.logits + (size_t)pair * p.G * p.nb, p.nb, lane,
-                       p.offsets ? p.offsets + (size_t)pair * (p.nb + 1) : nullptr, p.parts != nullptr, m2, s2);
+                       p.offsets ? p.offsets + (size_t)pair * (p.nb + 1) : nullptr, p.parts != nullptr, m2, s2,
+                       kslot[wave]);
     if (p.parts) {  // this tile's log-sum-exp state per head, for the group-score kernel's normalisers
         merge_lse_groups(m2, s2);
         if (lane < 8) {
