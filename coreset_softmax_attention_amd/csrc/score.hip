@@ -1263,19 +1263,34 @@ template <int D>
 __device__ __forceinline__ void err_tile_logits(const FusedScoreParams& p, __amdgpu_buffer_rsrc_t kr,
                                                 const bf16x8_t (&bq)[D / 32], const bf16x8_t (&bqh)[D / 32],
                                                 const bf16x8_t (&bql)[D / 32], int base, float* dst, int stride,
-                                                int lane, float& m2, float& s2)
+                                                int lane, float& m2, float& s2, uint4* slot)
 {
     constexpr int RB = D * 2, KS = D / 32;
-    const int n16 = lane & 15, g16 = lane >> 4;
+    // The tile's 64 rows (mean and variance row of 32 blocks, contiguous) are
+    // loaded whole with the non-temporal hint (LPV lanes per row, RPV rows per
+    // load), then each 16-block half goes through the wave's LDS slot into the
+    // operand layout: slot rows 0..15 the mean rows, 16..31 the variance rows.
+    constexpr int LPV = RB / 16, RPV = 64 / LPV, NI = 64 / RPV;
+    const int n16 = lane & 15, g16 = lane >> 4, gv = lane / LPV, ck = lane % LPV;
+    uint4 rows[NI];
+#pragma unroll
+    for (int jj = 0; jj < NI; ++jj)  // past nb: zeros
+        rows[jj] = buffer_ld16_nt(kr, (uint32_t)(2 * base + RPV * jj + gv) * RB + ck * 16);
     uint4 am[2][KS], av[2][KS];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-        const uint32_t om = (uint32_t)(base + rb * 16 + n16) * 2 * RB + g16 * 16;  // past nb: zeros
+#pragma unroll
+        for (int jj = 0; jj < NI / 2; ++jj) {
+            const int lr = RPV * jj + gv;  // row of this half: block lr / 2, mean (even) or variance (odd)
+            slot[((lr & 1) * 16 + (lr >> 1)) * (LPV + 1) + ck] = rows[rb * (NI / 2) + jj];
+        }
+        wave_lds_fence();
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            am[rb][s] = buffer_ld16(kr, om + s * 64);
-            av[rb][s] = buffer_ld16(kr, om + RB + s * 64);
+            am[rb][s] = slot[n16 * (LPV + 1) + 4 * s + g16];
+            av[rb][s] = slot[(16 + n16) * (LPV + 1) + 4 * s + g16];
         }
+        wave_lds_fence();  // the slot is rewritten next
     }
     f32x4_t cm[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
     f32x4_t cv[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
@@ -1354,9 +1369,10 @@ __global__ void __launch_bounds__(kFusedWaves * 64) score_err_fused_kernel(const
     load_q_operand<D>(p.q + ((size_t)b * p.Hq + (size_t)j * p.G) * RB, p.G, lane, bq);
     square_q_operand<D>(bq, bqh, bql);
     const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(p.Kbar + (size_t)pair * p.nb * 2 * RB, (uint32_t)p.nb * 2 * RB);
+    __shared__ uint4 eslot[NW][32 * (RB / 16 + 1)];
     float m2 = kNegInf, s2 = 0.0f;
     for (int base = wave * 32; base < p.nb; base += NW * 32)
-        err_tile_logits<D>(p, kr, bq, bqh, bql, base, lsm, p.nb, lane, m2, s2);
+        err_tile_logits<D>(p, kr, bq, bqh, bql, base, lsm, p.nb, lane, m2, s2, eslot[wave]);
     merge_lse_groups(m2, s2);
     if (lane < 8) {
         pm[wave][lane] = m2;
@@ -1391,8 +1407,10 @@ __global__ void __launch_bounds__(kSplitWaves * 64) score_err_split_kernel(const
     load_q_operand<D>(p.q + ((size_t)b * p.Hq + (size_t)j * p.G) * RB, p.G, lane, bq);
     square_q_operand<D>(bq, bqh, bql);
     const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(p.Kbar + (size_t)pair * p.nb * 2 * RB, (uint32_t)p.nb * 2 * RB);
+    __shared__ uint4 eslot[kSplitWaves][32 * (RB / 16 + 1)];
     float m2 = kNegInf, s2 = 0.0f;
-    err_tile_logits<D>(p, kr, bq, bqh, bql, base, p.logits + (size_t)pair * p.G * p.nb, p.nb, lane, m2, s2);
+    err_tile_logits<D>(p, kr, bq, bqh, bql, base, p.logits + (size_t)pair * p.G * p.nb, p.nb, lane, m2, s2,
+                       eslot[wave]);
     merge_lse_groups(m2, s2);
     if (p.parts && lane < 8) {
         const int tiles = (p.nb + 31) / 32;
