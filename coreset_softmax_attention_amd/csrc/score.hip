@@ -727,24 +727,57 @@ __global__ void __launch_bounds__(kSplitWaves * 64) score_logits_split_kernel(co
 template <int D>
 __device__ __forceinline__ void cobs2_tile_logits(const FusedScoreParams& p, __amdgpu_buffer_rsrc_t kr,
                                                   const bf16x8_t (&bq)[D / 32], int base, float* dst, int stride,
-                                                  int lane, float (*tmp)[32])
+                                                  int lane, float (*tmp)[32], uint4* slot)
 {
     constexpr int RB = D * 2, KS = D / 32, NR = 1 + kCobsRank;
     static_assert(kCobsRank == 4, "one output lane holds one block's four eigenvector products");
-    const int n16 = lane & 15, g16 = lane >> 4;
-    uint4 am[2][KS], ax[4][2][KS];
+    // The tile's 32 NR rows are contiguous: they are loaded whole with the
+    // non-temporal hint (LPV lanes per row, RPV rows per load), and each group
+    // of 8 blocks goes through the wave's LDS slot (kCobsSlot rows: the 32
+    // eigenvector rows in sub-tile order, then the 8 mean rows) into the
+    // operand layout.
+    constexpr int LPV = RB / 16, RPV = 64 / LPV, NG = 8 * NR / RPV;
+    static_assert(8 * NR % RPV == 0, "whole loads per group of 8 blocks");
+    const int n16 = lane & 15, g16 = lane >> 4, gv = lane / LPV, ck = lane % LPV;
+    uint4 rows[4][NG];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        const int tr = rb * 16 + n16;
-        const uint32_t om = (uint32_t)(base + tr) * NR * RB + g16 * 16;  // past nb: zeros
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int s = 0; s < KS; ++s) am[rb][s] = buffer_ld16(kr, om + s * 64);
+        for (int jj = 0; jj < NG; ++jj)  // past nb: zeros
+            rows[u][jj] = buffer_ld16_nt(kr, (uint32_t)((base + 8 * u) * NR + RPV * jj + gv) * RB + ck * 16);
+    uint4 am[2][KS];
+    float sq[4][2];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const uint32_t ox = ((uint32_t)(base + 8 * u + tr / 4) * NR + 1 + tr % 4) * RB + g16 * 16;
+    for (int u = 0; u < 4; ++u) {
 #pragma unroll
-            for (int s = 0; s < KS; ++s) ax[u][rb][s] = buffer_ld16(kr, ox + s * 64);
+        for (int jj = 0; jj < NG; ++jj) {
+            const int lr = RPV * jj + gv, bl = lr / NR, kind = lr - bl * NR;
+            const int pos = kind == 0 ? 32 + bl : 4 * bl + kind - 1;
+            slot[pos * (LPV + 1) + ck] = rows[u][jj];
         }
+        wave_lds_fence();
+        uint4 ax[2][KS];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int s = 0; s < KS; ++s) ax[rb][s] = slot[(rb * 16 + n16) * (LPV + 1) + 4 * s + g16];
+        // the mean rows of blocks 8 u .. 8 u + 7: lanes n16 = 8 (u % 2) + i of mean block u / 2
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const uint4 v = slot[(32 + (n16 & 7)) * (LPV + 1) + 4 * s + g16];
+            if ((n16 >> 3) == (u & 1)) am[u >> 1][s] = v;
+        }
+        wave_lds_fence();  // the slot is rewritten next
+        f32x4_t cx[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+                cx[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ax[rb][s]), bq[s], cx[rb], 0,
+                                                                 0, 0);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+            sq[u][rb] = (cx[rb][0] * cx[rb][0] + cx[rb][1] * cx[rb][1]) + (cx[rb][2] * cx[rb][2] + cx[rb][3] * cx[rb][3]);
     }
     f32x4_t cm[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
@@ -753,20 +786,6 @@ __device__ __forceinline__ void cobs2_tile_logits(const FusedScoreParams& p, __a
         for (int rb = 0; rb < 2; ++rb)
             cm[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, am[rb][s]), bq[s], cm[rb], 0, 0,
                                                              0);
-    float sq[4][2];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        f32x4_t cx[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-                cx[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ax[u][rb][s]), bq[s],
-                                                                 cx[rb], 0, 0, 0);
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-            sq[u][rb] = (cx[rb][0] * cx[rb][0] + cx[rb][1] * cx[rb][1]) + (cx[rb][2] * cx[rb][2] + cx[rb][3] * cx[rb][3]);
-    }
     if (n16 < p.G) {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
@@ -1153,12 +1172,9 @@ __global__ void __launch_bounds__(kFusedWaves * 64) score_cobs2_fused_kernel(con
     load_q_operand<D>(p.q + ((size_t)b * p.Hq + (size_t)j * p.G) * RB, p.G, lane, bq);
     if constexpr (FP4) load_q_operand_by_lane_chunks<D>(p.q + ((size_t)b * p.Hq + (size_t)j * p.G) * RB, p.G, lane, bqp);
     const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(p.Kbar + (size_t)pair * p.nb * BB, (uint32_t)p.nb * BB);
-    for (int base = wave * 32; base < p.nb; base += NW * 32) {
-        if constexpr (FP4)
-            cobs2_fp4_tile_logits<D>(p, kr, bq, bqp, base, lsm, p.nb, lane, tmp[wave]);
-        else
-            cobs2_tile_logits<D>(p, kr, bq, base, lsm, p.nb, lane, tmp[wave]);
-    }
+    static_assert(FP4, "bfloat16 descriptors go through the split kernel");
+    for (int base = wave * 32; base < p.nb; base += NW * 32)
+        cobs2_fp4_tile_logits<D>(p, kr, bq, bqp, base, lsm, p.nb, lane, tmp[wave]);
     __syncthreads();
     group_scores_in_lds<NW>(lsm, lse_h, p.G, p.nb, p.scores + (size_t)pair * p.nb);
 }
@@ -1182,7 +1198,9 @@ __global__ void __launch_bounds__(kSplitWaves * 64) score_cobs2_split_kernel(con
         load_q_operand_by_lane_chunks<D>(p.q + ((size_t)b * p.Hq + (size_t)j * p.G) * RB, p.G, lane, bqp);
         cobs2_fp4_tile_logits<D>(p, kr, bq, bqp, base, p.logits + (size_t)pair * p.G * p.nb, p.nb, lane, tmp[wave]);
     } else {
-        cobs2_tile_logits<D>(p, kr, bq, base, p.logits + (size_t)pair * p.G * p.nb, p.nb, lane, tmp[wave]);
+        __shared__ uint4 cslot[kSplitWaves][40 * (RB / 16 + 1)];
+        cobs2_tile_logits<D>(p, kr, bq, base, p.logits + (size_t)pair * p.G * p.nb, p.nb, lane, tmp[wave],
+                             cslot[wave]);
     }
 }
 
@@ -1686,14 +1704,16 @@ hipError_t launch_score_cobs2_t(const Dims& s, const void* q, const void* Kcov, 
     // split kernels and the finishing kernel, whose many workgroups stream the
     // rows faster (41.8 against 44.8 us with one workgroup per KV head at 256 KV
     // heads over 512 blocks).
-    if (FP4 && s.pairs() >= kFusedStepMinPairs) {
-        const size_t shm = (size_t)s.G * s.nb * sizeof(float);
-        const dim3 grid((unsigned)s.pairs()), block(kFusedWaves * 64);
-        if (s.d == 128)
-            score_cobs2_fused_kernel<128, FP4><<<grid, block, shm, st>>>(p);
-        else
-            score_cobs2_fused_kernel<64, FP4><<<grid, block, shm, st>>>(p);
-        return hipGetLastError();
+    if constexpr (FP4) {
+        if (s.pairs() >= kFusedStepMinPairs) {
+            const size_t shm = (size_t)s.G * s.nb * sizeof(float);
+            const dim3 grid((unsigned)s.pairs()), block(kFusedWaves * 64);
+            if (s.d == 128)
+                score_cobs2_fused_kernel<128, FP4><<<grid, block, shm, st>>>(p);
+            else
+                score_cobs2_fused_kernel<64, FP4><<<grid, block, shm, st>>>(p);
+            return hipGetLastError();
+        }
     }
     const int tiles = (s.nb + 31) / 32;
     p.chunks = (tiles + kSplitWaves - 1) / kSplitWaves;
