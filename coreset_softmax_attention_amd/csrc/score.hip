@@ -900,29 +900,51 @@ template <int D, int KSS>
 __device__ __forceinline__ void cobs2_sub4_tile_logits(const FusedScoreParams& p, __amdgpu_buffer_rsrc_t kr,
                                                        const bf16x8_t (&bq)[D / 32], const bf16x8_t (&bh)[KSS],
                                                        const bf16x8_t (&bl)[KSS], int base, float* dst, int stride,
-                                                       int lane, float (*tmp)[32])
+                                                       int lane, float (*tmp)[32], uint4* gslot)
 {
     constexpr int KS = D / 32, SPF = 32 * KSS;
     constexpr uint32_t BB = 2 * D + 16 + 4 * SPF / 2;
     static_assert(kCobsRank == 4, "one output lane holds one block's four factor products");
+    // The tile's 32 BB bytes are contiguous: they are loaded 16 bytes per lane (a
+    // KiB per load, non-temporal; chunks past the tile or past nb read as zeros)
+    // and each group of 8 blocks is copied to the wave's LDS slot, from which the
+    // lanes take their mean-row chunks, code words and scales.
+    constexpr int GC = 8 * BB / 16, NJ = (4 * GC + 63) / 64;  // chunks per group; loads per lane
+    static_assert(8 * BB % 16 == 0, "groups of whole 16-byte chunks");
     const int n16 = lane & 15, g16 = lane >> 4;
+    uint4 v[NJ];
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) {
+        const int ci = 64 * jj + lane;
+        v[jj] = buffer_ld16_nt(kr, ci < 4 * GC ? (uint32_t)base * BB + (uint32_t)ci * 16 : 0xfffffff0u);
+    }
+    const char* const g = reinterpret_cast<const char*>(gslot);
     uint4 am[2][KS];
     uint32_t ac[4][2][KSS];  // the lane's code words: coordinates 8 (KSS g16 + s) .. + 7
     float4 scl[4][2];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        const int tr = rb * 16 + n16;
-        const uint32_t om = (uint32_t)(base + tr) * BB + g16 * 16;  // past nb: zeros
+    for (int u = 0; u < 4; ++u) {
 #pragma unroll
-        for (int s = 0; s < KS; ++s) am[rb][s] = buffer_ld16(kr, om + s * 64);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const uint32_t oc = (uint32_t)(base + 8 * u + tr / 4) * BB + 2 * D + 16 + (tr % 4) * (SPF / 2) + g16 * 4 * KSS;
-#pragma unroll
-            for (int s = 0; s < KSS; ++s) ac[u][rb][s] = buffer_ld4(kr, oc + 4 * s);
-            const uint32_t os = (uint32_t)(base + 8 * u + 4 * rb + g16) * BB + 2 * D;
-            scl[u][rb] = __builtin_bit_cast(float4, buffer_ld16(kr, os));
+        for (int jj = u * GC / 64; jj <= ((u + 1) * GC - 1) / 64; ++jj) {
+            const int ci = 64 * jj + lane;
+            if (ci >= u * GC && ci < (u + 1) * GC) gslot[ci - u * GC] = v[jj];
         }
+        wave_lds_fence();
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            const int tr = rb * 16 + n16;
+            const char* c = g + (tr / 4) * BB + 2 * D + 16 + (tr % 4) * (SPF / 2) + g16 * 4 * KSS;
+#pragma unroll
+            for (int s = 0; s < KSS; ++s) ac[u][rb][s] = *reinterpret_cast<const uint32_t*>(c + 4 * s);
+            scl[u][rb] = *reinterpret_cast<const float4*>(g + (4 * rb + g16) * BB + 2 * D);
+        }
+        // the mean rows of blocks 8 u .. 8 u + 7: lanes n16 = 8 (u % 2) + i of mean block u / 2
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const uint4 m = *reinterpret_cast<const uint4*>(g + (n16 & 7) * BB + g16 * 16 + s * 64);
+            if ((n16 >> 3) == (u & 1)) am[u >> 1][s] = m;
+        }
+        wave_lds_fence();  // the slot is rewritten next
     }
     f32x4_t cm[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
@@ -1227,8 +1249,9 @@ __global__ void __launch_bounds__(kSplitWaves * 64) score_cobs2_sub_split_kernel
     const uint32_t BB = FP4 ? (uint32_t)(2 * D + 16 + 64 * KSS) : (uint32_t)(RB + kCobsRank * p.sps * 2);
     const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(p.Kbar + (size_t)pair * p.nb * BB, (uint32_t)p.nb * BB);
     float* dst = p.logits + (size_t)pair * p.G * p.nb;
+    __shared__ uint4 gslot[kSplitWaves][FP4 ? (2 * D + 16 + 64 * KSS) / 2 : 1];
     if constexpr (FP4)
-        cobs2_sub4_tile_logits<D, KSS>(p, kr, bq, bh, bl, base, dst, p.nb, lane, tmp[wave]);
+        cobs2_sub4_tile_logits<D, KSS>(p, kr, bq, bh, bl, base, dst, p.nb, lane, tmp[wave], gslot[wave]);
     else
         cobs2_sub_tile_logits<D, KSS>(p, kr, bq, bh, bl, base, dst, p.nb, lane, tmp[wave]);
 }
@@ -1254,9 +1277,10 @@ __global__ void __launch_bounds__(kFusedWaves * 64) score_cobs2_sub_fused_kernel
     subspace_operands<KSS, FP4>(qt_sm, p.G, lane, bh, bl);
     const uint32_t BB = FP4 ? (uint32_t)(2 * D + 16 + 64 * KSS) : (uint32_t)(RB + kCobsRank * p.sps * 2);
     const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(p.Kbar + (size_t)pair * p.nb * BB, (uint32_t)p.nb * BB);
+    __shared__ uint4 gslot[NW][FP4 ? (2 * D + 16 + 64 * KSS) / 2 : 1];
     for (int base = wave * 32; base < p.nb; base += NW * 32) {
         if constexpr (FP4)
-            cobs2_sub4_tile_logits<D, KSS>(p, kr, bq, bh, bl, base, lsm, p.nb, lane, tmp[wave]);
+            cobs2_sub4_tile_logits<D, KSS>(p, kr, bq, bh, bl, base, lsm, p.nb, lane, tmp[wave], gslot[wave]);
         else
             cobs2_sub_tile_logits<D, KSS>(p, kr, bq, bh, bl, base, lsm, p.nb, lane, tmp[wave]);
     }
