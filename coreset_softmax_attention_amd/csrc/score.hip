@@ -1075,36 +1075,59 @@ constexpr int fp4_block_bytes(int d) { return 2 * d + 4 * kCobsRank + kCobsRank 
 template <int D>
 __device__ __forceinline__ void cobs2_fp4_tile_logits(const FusedScoreParams& p, __amdgpu_buffer_rsrc_t kr,
                                                       const bf16x8_t (&bq)[D / 32], const bf16x8_t (&bqp)[D / 32],
-                                                      int base, float* dst, int stride, int lane, float (*tmp)[32])
+                                                      int base, float* dst, int stride, int lane, float (*tmp)[32],
+                                                      uint4* gslot)
 {
     constexpr int KS = D / 32, BB = fp4_block_bytes(D), CB = D / 8;  // code bytes per lane and row
     static_assert(kCobsRank == 4, "one output lane holds one block's four eigenvector products");
+    // The tile's 32 BB bytes are contiguous: loaded 16 bytes per lane (a KiB per
+    // load, non-temporal; chunks past the tile or past nb read as zeros), each
+    // group of 8 blocks copied to the wave's LDS slot, the lanes' mean chunks,
+    // code words and scales taken from there.
+    constexpr int GC = 8 * BB / 16, NJ = (4 * GC + 63) / 64;  // chunks per group; loads per lane
+    static_assert(8 * BB % 16 == 0, "groups of whole 16-byte chunks");
     const int n16 = lane & 15, g16 = lane >> 4;
+    uint4 v[NJ];
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) {
+        const int ci = 64 * jj + lane;
+        v[jj] = buffer_ld16_nt(kr, ci < 4 * GC ? (uint32_t)base * BB + (uint32_t)ci * 16 : 0xfffffff0u);
+    }
+    const char* const g = reinterpret_cast<const char*>(gslot);
     uint4 am[2][KS];
     uint32_t ac[4][2][KS];  // four code bytes per k-step
     float4 scl[4][2];       // the four scales of the block an output lane holds
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        const int tr = rb * 16 + n16;
-        const uint32_t om = (uint32_t)(base + tr) * BB + g16 * 16;  // past nb: zeros
+    for (int u = 0; u < 4; ++u) {
 #pragma unroll
-        for (int s = 0; s < KS; ++s) am[rb][s] = buffer_ld16(kr, om + s * 64);
+        for (int jj = u * GC / 64; jj <= ((u + 1) * GC - 1) / 64; ++jj) {
+            const int ci = 64 * jj + lane;
+            if (ci >= u * GC && ci < (u + 1) * GC) gslot[ci - u * GC] = v[jj];
+        }
+        wave_lds_fence();
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const uint32_t oc = (uint32_t)(base + 8 * u + tr / 4) * BB + 2 * D + 16 + (tr % 4) * (D / 2) + g16 * CB;
+        for (int rb = 0; rb < 2; ++rb) {
+            const int tr = rb * 16 + n16;
+            const char* c = g + (tr / 4) * BB + 2 * D + 16 + (tr % 4) * (D / 2) + g16 * CB;
             if constexpr (KS == 4) {
-                const uint4 c4 = buffer_ld16(kr, oc);
+                const uint4 c4 = *reinterpret_cast<const uint4*>(c);
                 ac[u][rb][0] = c4.x;
                 ac[u][rb][1] = c4.y;
                 ac[u][rb][2] = c4.z;
                 ac[u][rb][3] = c4.w;
             } else {
-                ac[u][rb][0] = buffer_ld4(kr, oc);
-                ac[u][rb][1] = buffer_ld4(kr, oc + 4);
+                ac[u][rb][0] = *reinterpret_cast<const uint32_t*>(c);
+                ac[u][rb][1] = *reinterpret_cast<const uint32_t*>(c + 4);
             }
-            const uint32_t os = (uint32_t)(base + 8 * u + 4 * rb + g16) * BB + 2 * D;
-            scl[u][rb] = __builtin_bit_cast(float4, buffer_ld16(kr, os));
+            scl[u][rb] = *reinterpret_cast<const float4*>(g + (4 * rb + g16) * BB + 2 * D);
         }
+        // the mean rows of blocks 8 u .. 8 u + 7: lanes n16 = 8 (u % 2) + i of mean block u / 2
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const uint4 m = *reinterpret_cast<const uint4*>(g + (n16 & 7) * BB + g16 * 16 + s * 64);
+            if ((n16 >> 3) == (u & 1)) am[u >> 1][s] = m;
+        }
+        wave_lds_fence();  // the slot is rewritten next
     }
     f32x4_t cm[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
@@ -1195,8 +1218,9 @@ __global__ void __launch_bounds__(kFusedWaves * 64) score_cobs2_fused_kernel(con
     if constexpr (FP4) load_q_operand_by_lane_chunks<D>(p.q + ((size_t)b * p.Hq + (size_t)j * p.G) * RB, p.G, lane, bqp);
     const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(p.Kbar + (size_t)pair * p.nb * BB, (uint32_t)p.nb * BB);
     static_assert(FP4, "bfloat16 descriptors go through the split kernel");
+    __shared__ uint4 gslot[NW][8 * BB / 16];
     for (int base = wave * 32; base < p.nb; base += NW * 32)
-        cobs2_fp4_tile_logits<D>(p, kr, bq, bqp, base, lsm, p.nb, lane, tmp[wave]);
+        cobs2_fp4_tile_logits<D>(p, kr, bq, bqp, base, lsm, p.nb, lane, tmp[wave], gslot[wave]);
     __syncthreads();
     group_scores_in_lds<NW>(lsm, lse_h, p.G, p.nb, p.scores + (size_t)pair * p.nb);
 }
@@ -1217,8 +1241,10 @@ __global__ void __launch_bounds__(kSplitWaves * 64) score_cobs2_split_kernel(con
     load_q_operand<D>(p.q + ((size_t)b * p.Hq + (size_t)j * p.G) * RB, p.G, lane, bq);
     const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(p.Kbar + (size_t)pair * p.nb * BB, (uint32_t)p.nb * BB);
     if constexpr (FP4) {
+        __shared__ uint4 gslot[kSplitWaves][8 * BB / 16];
         load_q_operand_by_lane_chunks<D>(p.q + ((size_t)b * p.Hq + (size_t)j * p.G) * RB, p.G, lane, bqp);
-        cobs2_fp4_tile_logits<D>(p, kr, bq, bqp, base, p.logits + (size_t)pair * p.G * p.nb, p.nb, lane, tmp[wave]);
+        cobs2_fp4_tile_logits<D>(p, kr, bq, bqp, base, p.logits + (size_t)pair * p.G * p.nb, p.nb, lane, tmp[wave],
+                                 gslot[wave]);
     } else {
         __shared__ uint4 cslot[kSplitWaves][40 * (RB / 16 + 1)];
         cobs2_tile_logits<D>(p, kr, bq, base, p.logits + (size_t)pair * p.G * p.nb, p.nb, lane, tmp[wave],
