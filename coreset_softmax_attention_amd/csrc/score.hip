@@ -821,28 +821,70 @@ template <int D, int KSS>
 __device__ __forceinline__ void cobs2_sub_tile_logits(const FusedScoreParams& p, __amdgpu_buffer_rsrc_t kr,
                                                       const bf16x8_t (&bq)[D / 32], const bf16x8_t (&bh)[KSS],
                                                       const bf16x8_t (&bl)[KSS], int base, float* dst, int stride,
-                                                      int lane, float (*tmp)[32])
+                                                      int lane, float (*tmp)[32], uint4* gslot)
 {
     constexpr int RB = D * 2, KS = D / 32;
     static_assert(kCobsRank == 4, "one output lane holds one block's four factor products");
     const int n16 = lane & 15, g16 = lane >> 4;
     const uint32_t BB = (uint32_t)(RB + kCobsRank * p.sps * 2), nch = (uint32_t)(p.sps / 8);
-    uint4 am[2][KS], ax[4][2][KSS];
+    // The tile's 32 BB bytes are contiguous (BB a multiple of 64).  Group by group
+    // of 8 blocks (two groups in flight), they are loaded 16 bytes per lane (a
+    // KiB per load, non-temporal; chunks past the group or past nb read as zeros),
+    // copied to the wave's LDS slot, and the lanes' operand chunks taken from there.
+    constexpr int NJG = ((RB + kCobsRank * 32 * KSS * 2) * 8 / 16 + 63) / 64;  // loads per lane per group, at most
+    const int GC = (int)(8 * BB / 16);  // 16-byte chunks of a group of 8 blocks
+    uint4 vg[2][NJG];
+    auto load_group = [&](int u, uint4 (&dstv)[NJG]) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        const int tr = rb * 16 + n16;
-        const uint32_t om = (uint32_t)(base + tr) * BB + g16 * 16;  // past nb: zeros
+        for (int jj = 0; jj < NJG; ++jj) {
+            const int cl = 64 * jj + lane;
+            dstv[jj] = buffer_ld16_nt(kr, cl < GC ? (uint32_t)base * BB + (uint32_t)(u * GC + cl) * 16 : 0xfffffff0u);
+        }
+    };
+    load_group(0, vg[0]);
+    load_group(1, vg[1]);
+    const char* const g = reinterpret_cast<const char*>(gslot);
+    uint4 am[2][KS];
+    float sq[4][2];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) am[rb][s] = buffer_ld16(kr, om + s * 64);
+    for (int u = 0; u < 4; ++u) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const uint32_t ox = (uint32_t)(base + 8 * u + tr / 4) * BB + RB + (uint32_t)(tr % 4) * p.sps * 2;
+        for (int jj = 0; jj < NJG; ++jj) {
+            const int cl = 64 * jj + lane;
+            if (cl < GC) gslot[cl] = vg[u & 1][jj];
+        }
+        wave_lds_fence();
+        uint4 ax[2][KSS];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            const int tr = rb * 16 + n16;
+            const char* x = g + (tr / 4) * BB + RB + (uint32_t)(tr % 4) * p.sps * 2;
 #pragma unroll
             for (int s = 0; s < KSS; ++s) {
                 const uint32_t c = 4 * s + g16;
-                ax[u][rb][s] = c < nch ? buffer_ld16(kr, ox + c * 16) : make_uint4(0, 0, 0, 0);
+                ax[rb][s] = c < nch ? *reinterpret_cast<const uint4*>(x + c * 16) : make_uint4(0, 0, 0, 0);
             }
         }
+        // the mean rows of blocks 8 u .. 8 u + 7: lanes n16 = 8 (u % 2) + i of mean block u / 2
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const uint4 m = *reinterpret_cast<const uint4*>(g + (n16 & 7) * BB + g16 * 16 + s * 64);
+            if ((n16 >> 3) == (u & 1)) am[u >> 1][s] = m;
+        }
+        wave_lds_fence();  // the slot is rewritten next
+        if (u + 2 < 4) load_group(u + 2, vg[u & 1]);
+        f32x4_t cx[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+        for (int s = 0; s < KSS; ++s)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, ax[rb][s]);
+                cx[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh[s], cx[rb], 0, 0, 0);
+                cx[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl[s], cx[rb], 0, 0, 0);
+            }
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+            sq[u][rb] = (cx[rb][0] * cx[rb][0] + cx[rb][1] * cx[rb][1]) + (cx[rb][2] * cx[rb][2] + cx[rb][3] * cx[rb][3]);
     }
     f32x4_t cm[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
@@ -851,22 +893,6 @@ __device__ __forceinline__ void cobs2_sub_tile_logits(const FusedScoreParams& p,
         for (int rb = 0; rb < 2; ++rb)
             cm[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, am[rb][s]), bq[s], cm[rb], 0, 0,
                                                              0);
-    float sq[4][2];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        f32x4_t cx[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
-#pragma unroll
-        for (int s = 0; s < KSS; ++s)
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, ax[u][rb][s]);
-                cx[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh[s], cx[rb], 0, 0, 0);
-                cx[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl[s], cx[rb], 0, 0, 0);
-            }
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-            sq[u][rb] = (cx[rb][0] * cx[rb][0] + cx[rb][1] * cx[rb][1]) + (cx[rb][2] * cx[rb][2] + cx[rb][3] * cx[rb][3]);
-    }
     if (n16 < p.G) {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
@@ -1275,11 +1301,11 @@ __global__ void __launch_bounds__(kSplitWaves * 64) score_cobs2_sub_split_kernel
     const uint32_t BB = FP4 ? (uint32_t)(2 * D + 16 + 64 * KSS) : (uint32_t)(RB + kCobsRank * p.sps * 2);
     const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(p.Kbar + (size_t)pair * p.nb * BB, (uint32_t)p.nb * BB);
     float* dst = p.logits + (size_t)pair * p.G * p.nb;
-    __shared__ uint4 gslot[kSplitWaves][FP4 ? (2 * D + 16 + 64 * KSS) / 2 : 1];
+    __shared__ uint4 gslot[kSplitWaves][FP4 ? (2 * D + 16 + 64 * KSS) / 2 : (RB + kCobsRank * 32 * KSS * 2) / 2];
     if constexpr (FP4)
         cobs2_sub4_tile_logits<D, KSS>(p, kr, bq, bh, bl, base, dst, p.nb, lane, tmp[wave], gslot[wave]);
     else
-        cobs2_sub_tile_logits<D, KSS>(p, kr, bq, bh, bl, base, dst, p.nb, lane, tmp[wave]);
+        cobs2_sub_tile_logits<D, KSS>(p, kr, bq, bh, bl, base, dst, p.nb, lane, tmp[wave], gslot[wave]);
 }
 
 // Query-subspace second-order scores, one workgroup per KV head: the subspace
@@ -1303,12 +1329,12 @@ __global__ void __launch_bounds__(kFusedWaves * 64) score_cobs2_sub_fused_kernel
     subspace_operands<KSS, FP4>(qt_sm, p.G, lane, bh, bl);
     const uint32_t BB = FP4 ? (uint32_t)(2 * D + 16 + 64 * KSS) : (uint32_t)(RB + kCobsRank * p.sps * 2);
     const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(p.Kbar + (size_t)pair * p.nb * BB, (uint32_t)p.nb * BB);
-    __shared__ uint4 gslot[NW][FP4 ? (2 * D + 16 + 64 * KSS) / 2 : 1];
+    __shared__ uint4 gslot[NW][FP4 ? (2 * D + 16 + 64 * KSS) / 2 : (RB + kCobsRank * 32 * KSS * 2) / 2];
     for (int base = wave * 32; base < p.nb; base += NW * 32) {
         if constexpr (FP4)
             cobs2_sub4_tile_logits<D, KSS>(p, kr, bq, bh, bl, base, lsm, p.nb, lane, tmp[wave], gslot[wave]);
         else
-            cobs2_sub_tile_logits<D, KSS>(p, kr, bq, bh, bl, base, lsm, p.nb, lane, tmp[wave]);
+            cobs2_sub_tile_logits<D, KSS>(p, kr, bq, bh, bl, base, lsm, p.nb, lane, tmp[wave], gslot[wave]);
     }
     __syncthreads();
     group_scores_in_lds<NW>(lsm, lse_h, p.G, p.nb, p.scores + (size_t)pair * p.nb);
