@@ -726,6 +726,18 @@ def test_cobs2_pipeline_matches_oracle(B, Hkv, G, n, L, k):
     compare_pipelines(w, g, o, f"cobs2 B={B} Hkv={Hkv} G={G} n={n} L={L}")
 
 
+@pytest.mark.parametrize("B,Hkv,G,n,L,k", [
+    (2, 2, 4, 2048, 32, 4),     # d = 64, split scoring path
+    (2, 1, 1, 1000, 16, 3),     # d = 64, one head per KV head, ragged
+])
+def test_cobs2_pipeline_d64_matches_oracle(B, Hkv, G, n, L, k):
+    """The second-order split kernel at d = 64 (eight lanes per descriptor row in its loads)."""
+    w = W.Workload("cobs2_d64", 0, B, G * Hkv, Hkv, 64, n, L, "bf16", k, "cobs2", True, "clusters")
+    data = rand_inputs(310 + B + G + n, B, G * Hkv, Hkv, 64, n, "bf16")
+    g, o = cobs2_case(w, data)
+    compare_pipelines(w, g, o, f"cobs2 d=64 B={B} Hkv={Hkv} G={G} n={n} L={L}")
+
+
 def test_cov4_descriptors_are_the_fp4_storage_of_the_bf16_ones():
     """kv_cov4_build stores exactly what the oracle's FP4 packing makes of kv_cov_build's
     bfloat16 descriptors (same eigen-solve on the GPU): bit for bit, d = 128 and 64, ragged."""
@@ -937,6 +949,17 @@ def test_proxy_error_pipeline_matches_oracle(B, Hkv, G, n, L, k):
     w = W.Workload("err_case", 0, B, G * Hkv, Hkv, 128, n, L, "bf16", k, "proxy_error", True, "clusters")
     data = rand_inputs(600 + B + G + n, B, G * Hkv, Hkv, 128, n, "bf16")
     compare_pipelines(w, gpu_pipeline(w, data), oracle_pipeline(w, data), f"proxy error B={B} Hkv={Hkv} G={G}")
+
+
+@pytest.mark.parametrize("B,Hkv,G,n,L,k", [
+    (8, 4, 4, 2048, 32, 4),     # d = 64, one workgroup per KV head
+    (2, 2, 2, 1000, 16, 3),     # d = 64, split kernels, ragged
+])
+def test_proxy_error_pipeline_d64_matches_oracle(B, Hkv, G, n, L, k):
+    """The proxy-error kernels at d = 64 (eight lanes per mean or variance row in their loads)."""
+    w = W.Workload("err_d64", 0, B, G * Hkv, Hkv, 64, n, L, "bf16", k, "proxy_error", True, "clusters")
+    data = rand_inputs(610 + B + G + n, B, G * Hkv, Hkv, 64, n, "bf16")
+    compare_pipelines(w, gpu_pipeline(w, data), oracle_pipeline(w, data), f"proxy error d=64 B={B} Hkv={Hkv} G={G}")
 
 
 @pytest.mark.parametrize("B,Hkv", [(1, 2), (8, 4)])
