@@ -833,12 +833,13 @@ __device__ __forceinline__ void cobs2_sub_tile_logits(const FusedScoreParams& p,
     // copied to the wave's LDS slot, and the lanes' operand chunks taken from there.
     constexpr int NJG = ((RB + kCobsRank * 32 * KSS * 2) * 8 / 16 + 63) / 64;  // loads per lane per group, at most
     const int GC = (int)(8 * BB / 16);  // 16-byte chunks of a group of 8 blocks
+    const uint32_t oob = (uint32_t)p.nb * BB;  // the buffer's size: a load there reads zeros
     uint4 vg[2][NJG];
     auto load_group = [&](int u, uint4 (&dstv)[NJG]) {
 #pragma unroll
         for (int jj = 0; jj < NJG; ++jj) {
             const int cl = 64 * jj + lane;
-            dstv[jj] = buffer_ld16_nt(kr, cl < GC ? (uint32_t)base * BB + (uint32_t)(u * GC + cl) * 16 : 0xfffffff0u);
+            dstv[jj] = buffer_ld16_nt(kr, cl < GC ? (uint32_t)base * BB + (uint32_t)(u * GC + cl) * 16 : oob);
         }
     };
     load_group(0, vg[0]);
@@ -938,11 +939,12 @@ __device__ __forceinline__ void cobs2_sub4_tile_logits(const FusedScoreParams& p
     constexpr int GC = 8 * BB / 16, NJ = (4 * GC + 63) / 64;  // chunks per group; loads per lane
     static_assert(8 * BB % 16 == 0, "groups of whole 16-byte chunks");
     const int n16 = lane & 15, g16 = lane >> 4;
+    const uint32_t oob = (uint32_t)p.nb * BB;  // the buffer's size: a load there reads zeros
     uint4 v[NJ];
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj) {
         const int ci = 64 * jj + lane;
-        v[jj] = buffer_ld16_nt(kr, ci < 4 * GC ? (uint32_t)base * BB + (uint32_t)ci * 16 : 0xfffffff0u);
+        v[jj] = buffer_ld16_nt(kr, ci < 4 * GC ? (uint32_t)base * BB + (uint32_t)ci * 16 : oob);
     }
     const char* const g = reinterpret_cast<const char*>(gslot);
     uint4 am[2][KS];
@@ -1113,11 +1115,12 @@ __device__ __forceinline__ void cobs2_fp4_tile_logits(const FusedScoreParams& p,
     constexpr int GC = 8 * BB / 16, NJ = (4 * GC + 63) / 64;  // chunks per group; loads per lane
     static_assert(8 * BB % 16 == 0, "groups of whole 16-byte chunks");
     const int n16 = lane & 15, g16 = lane >> 4;
+    const uint32_t oob = (uint32_t)p.nb * BB;  // the buffer's size: a load there reads zeros
     uint4 v[NJ];
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj) {
         const int ci = 64 * jj + lane;
-        v[jj] = buffer_ld16_nt(kr, ci < 4 * GC ? (uint32_t)base * BB + (uint32_t)ci * 16 : 0xfffffff0u);
+        v[jj] = buffer_ld16_nt(kr, ci < 4 * GC ? (uint32_t)base * BB + (uint32_t)ci * 16 : oob);
     }
     const char* const g = reinterpret_cast<const char*>(gslot);
     uint4 am[2][KS];
