@@ -201,10 +201,10 @@ __global__ void __launch_bounds__(kStepWaves * 64) decode_step_kernel(const Step
         int o0[2][5], o1[2][5];
         const int b0 = (t + rotK) % nK * TR, b1 = (t + NW + rotK) % nK * TR;
         const bool two = t + NW < nK;
+        load_ranges(b0, o0);  // the few range words ahead of the key tiles, not behind them
+        if (two) load_ranges(b1, o1);
         load_keys(b0, k0, true);
         load_keys(b1, k1, two);
-        load_ranges(b0, o0);
-        if (two) load_ranges(b1, o1);
         logits_to_lds(b0, k0, o0);
         if (two) logits_to_lds(b1, k1, o1);
     }
