@@ -58,6 +58,7 @@ struct MfmaEngine {
     static constexpr int VRS = RB + 32;  // value row stride in the slot (bytes)
     static constexpr int SLOT = (TR * VRS > 16 * (LPV + 1) * 16 ? TR * VRS : 16 * (LPV + 1) * 16);
     static_assert(SLOT % 16 == 0 && VRS % 16 == 0, "16-byte aligned slot rows");
+    static_assert(SLOT >= HG * D * 4, "a wave's output fits in its own slot");
 
     struct Smem {
         uint32_t tab_row[NTAB][NW][TR];
@@ -66,8 +67,7 @@ struct MfmaEngine {
         float m[NW][HG];
         float l[NW][HG];
         union {
-            uint4 slot[NW][SLOT / 16];  // while tiles stream
-            float acc[NW][HG][D];       // the waves' outputs, at the end
+            uint4 slot[NW][SLOT / 16];  // while tiles stream; then the wave's output [HG][D] at its start
         } u;
     };
 
@@ -321,14 +321,15 @@ struct MfmaEngine {
     __device__ __forceinline__ void finish(int nh, float* out, float* lse, float* part)
     {
         l_part = add_xor32(add_xor16(l_part));
-        __syncthreads();  // every wave is done with its slot: the outputs take its place
+        // the wave's output takes the place of its own slot (no other wave reads it)
+        float* mine = reinterpret_cast<float*>(sm.u.slot[wave]);
         // output lanes: heads 4 g16 + i, column 16 c + n16
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int g = 4 * g16 + i;
             if (g < HG) {
 #pragma unroll
-                for (int c = 0; c < D / 16; ++c) sm.u.acc[wave][g][16 * c + n16] = oacc[c][i];
+                for (int c = 0; c < D / 16; ++c) mine[g * D + 16 * c + n16] = oacc[c][i];
             }
         }
         if (lane < HG) {
@@ -347,7 +348,7 @@ struct MfmaEngine {
             for (int w = 0; w < NW; ++w) {
                 const float a = rescale(sm.m[w][g], M);
                 Ls += sm.l[w][g] * a;
-                A += sm.u.acc[w][g][e] * a;
+                A += reinterpret_cast<const float*>(sm.u.slot[w])[g * D + e] * a;
             }
             if (part == nullptr) {
                 out[(size_t)g * D + e] = A / Ls;
