@@ -71,7 +71,15 @@ TRAFFIC_KERNELS = {"decode_step": "decode_step_kernel", "sparse_decode_attn": "a
                    "cluster_decode_attn": "cluster_attn_kernel", "cluster_logits": "cluster_logits_kernel",
                    "block_score_exact": "logits_exact_mfma_kernel", "block_score_exact_valu": "logits_exact_kernel",
                    "score_logits_split": "score_logits_split_kernel", "score_finish": "score_finish_kernel",
-                   "attn_merge": "attn_merge_kernel", "topk": "topk_", "score_group_chunk": "score_group_chunk_kernel"}
+                   "attn_merge": "attn_merge_kernel", "topk": "topk_", "score_group_chunk": "score_group_chunk_kernel",
+                   "block_score_box": "score_summary_fused_kernel<256, true>",
+                   "block_score_cobs2_split": "score_cobs2_split_kernel",
+                   "block_score_cobs2_fused": "score_cobs2_fused_kernel",
+                   "block_score_cobs2_sub": "score_cobs2_sub_fused_kernel", "block_score_err": "score_err_fused_kernel"}
+# the kernels of the three-call route (block_score, topk_select, sparse_decode_attn) whose
+# measured bytes add up to a step's traffic
+THREE_CALL_KERNELS = ("block_score_box", "block_score_cobs2_split", "block_score_cobs2_fused", "block_score_cobs2_sub",
+                      "block_score_err", "score_finish", "topk", "sparse_decode_attn")
 
 
 # The device sources each counted kernel is compiled from (its traffic is stale once any of
@@ -81,7 +89,9 @@ KERNEL_SOURCES = {"decode_step": ["step.hip"], "sparse_decode_attn": ["attn.hip"
                   "cluster_decode_attn": ["cluster.hip"], "cluster_logits": ["cluster.hip"],
                   "block_score_exact": ["score.hip"], "block_score_exact_valu": ["score.hip"],
                   "score_logits_split": ["score.hip"], "score_finish": ["score.hip"], "attn_merge": ["attn.hip"],
-                  "topk": ["topk.hip"], "score_group_chunk": ["score.hip"]}
+                  "topk": ["topk.hip"], "score_group_chunk": ["score.hip"], "block_score_box": ["score.hip"],
+                  "block_score_cobs2_split": ["score.hip"], "block_score_cobs2_fused": ["score.hip"],
+                  "block_score_cobs2_sub": ["score.hip"], "block_score_err": ["score.hip"]}
 
 
 def source_hash(csrc=None, files=None):
@@ -165,6 +175,18 @@ def load_traffic(path):
             print(f"[bench] {path}: {key} was measured on other kernel sources: traffic not reported",
                   file=sys.stderr)
     return out
+
+
+def three_call_traffic(traffic):
+    """HBM bytes of one step through block_score, topk_select and sparse_decode_attn: the sum
+    of the measured bytes per launch of the kernels of that route (null unless the score
+    kernel, the top-k and the attention were all measured on the current sources)."""
+    if not isinstance(traffic, dict):
+        return None
+    keys = [k for k in THREE_CALL_KERNELS if k in traffic]
+    if "sparse_decode_attn" not in keys or "topk" not in keys or not any(k.startswith("block_score_") for k in keys):
+        return None
+    return sum(traffic[k] for k in keys)
 
 
 def copy_probe(nbytes):
@@ -531,7 +553,8 @@ def main():
             "peak": 8000.0,
             "unit": "GB/s",
             "frac": step_achieved / 8000.0,
-            "traffic": traffic.get("decode_step") if isinstance(traffic, dict) else None,
+            "traffic": (three_call_traffic(traffic) if box else
+                        traffic.get("decode_step") if isinstance(traffic, dict) else None),
             "algorithmic_bytes": srd + swr,
         },
         "roofline_sparse_decode_attn": {

@@ -120,3 +120,19 @@ def test_kernel_source_hash_follows_only_its_own_files(tmp_path):
         assert bench.source_hash(str(dst), files) != h0
         f.write_text(text)
     assert bench.source_hash(str(dst), files) == h0
+
+
+def test_three_call_traffic_sums_the_route_kernels():
+    """The step traffic of the three-call route is the sum of its kernels' measured bytes per
+    launch, and null when the score kernel, the top-k or the attention is missing (not
+    measured, or measured on other sources)."""
+    t = {"block_score_cobs2_split": 100.0, "score_finish": 10.0, "topk": 1.0, "sparse_decode_attn": 1000.0,
+         "decode_step": 5.0}
+    assert bench.three_call_traffic(t) == 1111.0
+    assert bench.three_call_traffic({"block_score_box": 7.0, "topk": 1.0, "sparse_decode_attn": 2.0}) == 10.0
+    for drop in ("block_score_cobs2_split", "topk", "sparse_decode_attn"):
+        assert bench.three_call_traffic({k: v for k, v in t.items() if k != drop}) is None
+    assert bench.three_call_traffic(None) is None
+    # every counted kernel has its device sources listed
+    assert set(bench.TRAFFIC_KERNELS) == set(bench.KERNEL_SOURCES)
+    assert set(bench.THREE_CALL_KERNELS) <= set(bench.TRAFFIC_KERNELS)
