@@ -590,13 +590,41 @@ template <int D>
 __global__ void __launch_bounds__(D) attn_merge_kernel(const float* part, int splits, int G, int Hq, int Hkv,
                                                        float* out, float* lse)
 {
-    constexpr int CH = 8;
+    constexpr int CH = 16;
     const int pair = blockIdx.x / G, g = blockIdx.x - pair * G;
     const int b = pair / Hkv, j = pair - b * Hkv;
     const int e = threadIdx.x;
     const size_t stride = (size_t)G * (D + 2);
     const float* st = part + ((size_t)pair * splits * G + g) * (D + 2);
     float M = kNegInf;
+    float Ls = 0.0f, A = 0.0f;
+    if (splits <= CH) {
+        // every state's loads go out together (one memory round trip); the
+        // maximum, then the rescaled sums, in split order as below
+        float m[CH], l[CH], a[CH];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const bool in = c < splits;
+            const float* sc = st + (in ? c : 0) * stride;
+            m[c] = in ? sc[0] : kNegInf;
+            l[c] = sc[1];
+            a[c] = sc[2 + e];
+        }
+#pragma unroll
+        for (int c = 0; c < CH; ++c) M = fmaxf(M, m[c]);
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            if (c < splits) {
+                const float w = rescale(m[c], M);
+                Ls += l[c] * w;
+                A += a[c] * w;
+            }
+        }
+        const int h = j * G + g;
+        out[((size_t)b * Hq + h) * D + e] = A / Ls;
+        if (e == 0 && lse) lse[(size_t)b * Hq + h] = (M + log2f(Ls)) * kLn2;
+        return;
+    }
     for (int s0 = 0; s0 < splits; s0 += CH) {
         float m[CH];
 #pragma unroll
@@ -604,7 +632,6 @@ __global__ void __launch_bounds__(D) attn_merge_kernel(const float* part, int sp
 #pragma unroll
         for (int c = 0; c < CH; ++c) M = fmaxf(M, m[c]);
     }
-    float Ls = 0.0f, A = 0.0f;
     for (int s0 = 0; s0 < splits; s0 += CH) {
         float m[CH], l[CH], a[CH];
 #pragma unroll
