@@ -527,9 +527,9 @@ hipError_t launch_cluster_attention(const Dims& s, const ClusterAttn& ca, hipStr
     p.k = ca.k;
     p.proxies = ca.proxies;
     p.scale_log2 = s.scale * kLog2e;
-    // up to 7 heads share a workgroup; 8 go as two of 4 (eight heads' states
-    // and a tile in flight do not fit the registers)
-    const int hg = s.G <= 7 ? s.G : 4;
+    // all heads of a KV head (up to 8) share a workgroup, so its cluster rows are
+    // read once (with P V on the matrix cores eight heads fit two waves per SIMD)
+    const int hg = s.G;
     const dim3 grid((unsigned)s.pairs(), (unsigned)((s.G + hg - 1) / hg)), block(kClusterWaves * 64);
 #define CSA_CLUSTER_ATTN(D)                                                                \
     switch (hg) {                                                                          \
@@ -540,6 +540,7 @@ hipError_t launch_cluster_attention(const Dims& s, const ClusterAttn& ca, hipStr
     case 5: cluster_attn_kernel<D, 5><<<grid, block, 0, st>>>(p); break;                   \
     case 6: cluster_attn_kernel<D, 6><<<grid, block, 0, st>>>(p); break;                   \
     case 7: cluster_attn_kernel<D, 7><<<grid, block, 0, st>>>(p); break;                   \
+    case 8: cluster_attn_kernel<D, 8><<<grid, block, 0, st>>>(p); break;                   \
     default: return hipErrorInvalidValue;                                                  \
     }
     if (s.d == 128) {
