@@ -366,7 +366,13 @@ __global__ void __launch_bounds__(NW * 64) attn_mfma_kernel(const AttnParams p)
     __shared__ typename E::Smem sm;
     static_assert(kMaxTokLds >= NW * 128 && kMaxSelLds >= NW * kDirectMaxK, "ranked mode's per-wave LDS");
 
-    const int pair = blockIdx.x / p.splits, split = blockIdx.x - pair * p.splits;
+    // workgroup w (on XCD w mod 8) takes item (w mod 8) N / 8 + w / 8: each XCD
+    // streams a contiguous eighth of the (pair, split) items (sparse_decode_attn
+    // over the 32-sequence layer 20.98 -> 20.70 us, the 128K weighted-coreset step
+    // 25.90 -> 25.65 us)
+    const int wg = gridDim.x % 8 == 0 ? (int)(blockIdx.x % 8) * (int)(gridDim.x / 8) + (int)(blockIdx.x / 8)
+                                      : (int)blockIdx.x;
+    const int pair = wg / p.splits, split = wg - pair * p.splits;
     const int b = pair / p.Hkv, j = pair - b * p.Hkv;
     const int g0 = blockIdx.y * HG;
     const int nh = min(HG, p.G - g0);
