@@ -248,7 +248,12 @@ __global__ void __launch_bounds__(kExactWaves * 64) logits_exact_mfma_kernel(con
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n16 = lane & 15, g16 = lane >> 4;
-    const int pair = blockIdx.x / p.chunks, chunk = blockIdx.x - pair * p.chunks;
+    // workgroup w (on XCD w mod 8) takes item (w mod 8) N / 8 + w / 8: each XCD
+    // scans a contiguous eighth of the keys (exact-mass step over 32 KV heads of 8
+    // sequences 348.4 -> 340.3 us; no change over 8 KV heads)
+    const int wg = gridDim.x % 8 == 0 ? (int)(blockIdx.x % 8) * (int)(gridDim.x / 8) + (int)(blockIdx.x / 8)
+                                      : (int)blockIdx.x;
+    const int pair = wg / p.chunks, chunk = wg - pair * p.chunks;
     const int b = pair / p.Hkv, j = pair - b * p.Hkv;
     // this wave's blocks: a contiguous share of the chunk's
     const int blk0 = chunk * p.items_per_wg, blk1 = min(p.nb, blk0 + p.items_per_wg);
