@@ -598,7 +598,10 @@ __global__ void __launch_bounds__(D) attn_merge_kernel(const float* part, int sp
                                                        float* out, float* lse)
 {
     constexpr int CH = 16;
-    const int pair = blockIdx.x / G, g = blockIdx.x - pair * G;
+    // each XCD merges a contiguous eighth of the (pair, head) items
+    const int wg = gridDim.x % 8 == 0 ? (int)(blockIdx.x % 8) * (int)(gridDim.x / 8) + (int)(blockIdx.x / 8)
+                                      : (int)blockIdx.x;
+    const int pair = wg / G, g = wg - pair * G;
     const int b = pair / Hkv, j = pair - b * Hkv;
     const int e = threadIdx.x;
     const size_t stride = (size_t)G * (D + 2);

@@ -1601,7 +1601,11 @@ __global__ void __launch_bounds__(64) score_group_chunk_kernel(const FusedScoreP
     __shared__ float sc_sm[kCandChunk];
     const int lane = threadIdx.x, G = p.G, nb = p.nb, k = p.k;
     const int nchunks = (nb + kCandChunk - 1) / kCandChunk;
-    const int pair = blockIdx.x / nchunks, chunk = blockIdx.x - pair * nchunks;
+    // each XCD takes a contiguous eighth of the (pair, chunk) items (with the
+    // merge likewise: 128K weighted-coreset step 25.11 -> 23.87 us)
+    const int wg = gridDim.x % 8 == 0 ? (int)(blockIdx.x % 8) * (int)(gridDim.x / 8) + (int)(blockIdx.x / 8)
+                                      : (int)blockIdx.x;
+    const int pair = wg / nchunks, chunk = wg - pair * nchunks;
     const int lo = chunk * kCandChunk, len = min(kCandChunk, nb - lo);
     constexpr int PER = kCandChunk / 64;
     float v[PER];
