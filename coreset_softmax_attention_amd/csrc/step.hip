@@ -200,11 +200,13 @@ __global__ void __launch_bounds__(kStepWaves * 64) decode_step_kernel(const Step
     // The mean keys decide the selection: they have the memory system to
     // themselves.  The wave's first two proxy value tiles go out once its keys
     // have arrived, and stream in while the selection is made.
-    for (int t = wave; t < nK; t += 2 * NW) {  // two tiles in flight
+    // two adjacent tiles in flight per wave (tiles w and w + NW instead: 19.89 ->
+    // 20.13 us per step at 32 sequences, 21.38 -> 21.67 at 64 query heads)
+    for (int t = 2 * wave; t < nK; t += 2 * NW) {
         uint4 k0[E::NI], k1[E::NI];
         int o0[2][5], o1[2][5];
-        const int b0 = t * TR, b1 = (t + NW) * TR;
-        const bool two = t + NW < nK;
+        const int b0 = t * TR, b1 = (t + 1) * TR;
+        const bool two = t + 1 < nK;
         load_ranges(b0, o0);  // the few range words ahead of the key tiles, not behind them
         if (two) load_ranges(b1, o1);
         load_keys(b0, k0, true);
